@@ -1,0 +1,87 @@
+"""ctypes binding of libdet_attn.so (argument marshalling only).
+
+Every computation happens in the HIP kernels behind the C ABI declared in
+include/det_attn.h; this module converts torch tensors to descriptors, takes
+the current HIP stream, allocates the workspace the library asks for, and
+raises on a nonzero return code.  If the shared library is missing the import
+fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdet_attn.so")
+
+DET_F32, DET_BF16 = 0, 1
+NUM_DIGITS, NUM_ELO, DEN_DIGITS, DEN_ELO = 14, -298, 9, -149
+
+ERRORS = {-1: "DET_E_NULL", -2: "DET_E_SHAPE", -3: "DET_E_DTYPE", -4: "DET_E_STRIDE", -5: "DET_E_WORKSPACE",
+          -6: "DET_E_HIP", -7: "DET_E_VALUE"}
+
+
+class DetError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Tensor(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("dtype", C.c_int32), ("B", C.c_int64), ("H", C.c_int64),
+                ("S", C.c_int64), ("D", C.c_int64), ("sB", C.c_int64), ("sH", C.c_int64), ("sS", C.c_int64)]
+
+
+class Out(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("sB", C.c_int64), ("sH", C.c_int64), ("sS", C.c_int64)]
+
+
+# name -> (restype, argtypes); mirrors include/det_attn.h
+_P, _I32, _I64, _D, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_double, C.c_size_t
+_T, _O = C.POINTER(Tensor), C.POINTER(Out)
+SIGNATURES = {
+    "det_digit_format": (C.c_int, [_I32, C.POINTER(_I32), C.POINTER(_I32)]),
+    "det_last_error": (C.c_char_p, []),
+    "det_attn_workspace_size": (_SZ, [_T, _T, _T, _I32]),
+    "det_attn": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _SZ, _P]),
+    "det_attn_rowmax_workspace_size": (_SZ, [_T, _T, _I64, _I64]),
+    "det_attn_rowmax": (C.c_int, [_T, _T, _I64, _I64, _I32, _D, _P, _P, _SZ, _P]),
+    "det_attn_accumulate_workspace_size": (_SZ, [_T, _T, _T, _I64, _I64]),
+    "det_attn_accumulate": (C.c_int, [_T, _T, _T, _P, _I64, _I64, _I32, _D, _P, _P, _I32, _P, _SZ, _P]),
+    "det_rowmax_combine": (C.c_int, [_P, _P, _I64, _P]),
+    "det_digits_combine": (C.c_int, [_P, _P, _I64, _I32, _P]),
+    "det_attn_finalize": (C.c_int, [_P, _P, _I64, _I64, _I64, _I64, _O, _P]),
+    "det_attn_sharded_workspace_size": (_SZ, [_T, _T, _T, _P, _I32, _I32]),
+    "det_attn_sharded": (C.c_int, [_T, _T, _T, _P, _I32, _P, _I32, _D, _O, _P, _SZ, _P]),
+    "det_ce_rowmax": (C.c_int, [_P, _I32, _I64, _I64, _I64, _I64, _P, _P]),
+    "det_ce_denom_digits": (C.c_int, [_P, _I32, _I64, _I64, _P, _I64, _I64, _P, _I32, _P]),
+    "det_ce_finalize": (C.c_int, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "det_ce_forward_workspace_size": (_SZ, [_I64]),
+    "det_ce_forward": (C.c_int, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "det_ce_reduce_workspace_size": (_SZ, [_I64]),
+    "det_ce_reduce": (C.c_int, [_P, _I64, _I32, _P, _P, _SZ, _P]),
+    "det_ce_backward": (C.c_int, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I64, _P]),
+}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libdet_attn.so (raises ImportError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m bitwise_deterministic_exact_pass1_amd.build`")
+        h = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def check(rc: int) -> None:
+    if rc != 0:
+        raise DetError(rc, lib().det_last_error().decode())

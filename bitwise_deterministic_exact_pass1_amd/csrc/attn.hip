@@ -1,0 +1,413 @@
+// attn.hip -- attention kernels for gfx950.
+//
+// Pass 1 (det-attn page, "Method": the global row max) and the score rule:
+//   s_ij = RN32(RN64(scale * dot_ij)), dot_ij = fp64 fma chain over d ascending.
+// One lane owns one key j and keeps kRowTile chains (one per query row) in
+// VGPRs; the query rows come in through scalar loads of a widened fp64 copy of
+// Q, so every FMA takes its q operand from an SGPR pair and its k operand from
+// a VGPR.  Scores are stored for pass 2 (the chain is not recomputed).
+//
+// Pass 2 ("exact Kulisch long-accumulator sums"): w = RN32(exp_det(s - m)),
+// then NUM_id = sum_j w_ij V_jd and DEN_i = sum_j w_ij exactly.  The deposit
+// keeps, per (i,d), one binary64 window whose terms all lie on a common grid
+// 2^g with |window| < 2^(g+53), so every addition in it is exact whatever the
+// order; when a term would break either bound the window is flushed into the
+// int64 radix-2^32 digit planes with integer atomics (integer addition is
+// associative, so the digit planes hold the same value whatever the flush
+// order).  The digits are then carried to canonical form.
+#include "dev_math.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+#include <climits>
+
+namespace det {
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t score_scratch_bytes(const AttnGeom &g, int64_t rows_i, int64_t kv_len) {
+    const int64_t bh = g.B * g.Hq;
+    return align256((size_t)bh * padded_rows(rows_i) * g.Dp * sizeof(double)) +  // widened Q rows
+           align256((size_t)bh * rows_i * sizeof(uint32_t)) +       // rowmax keys
+           align256((size_t)bh * rows_i * kv_len * sizeof(float));  // scores / weights
+}
+
+// ---------------------------------------------------------------- small kernels
+
+__global__ void k_fill_u32(uint32_t *p, int64_t n, uint32_t v) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x)
+        p[t] = v;
+}
+__global__ void k_fill_i64(int64_t *p, int64_t n, int64_t v) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x)
+        p[t] = v;
+}
+
+static dim3 grid_for(int64_t n, int block = 256) {
+    int64_t g = (n + block - 1) / block;
+    return dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>(g, 1 << 20)));
+}
+
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_u32, grid_for(n), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+hipError_t launch_fill_i64(int64_t *p, int64_t n, int64_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_i64, grid_for(n), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+// Widen query rows [i0,i1) of every (b,hq) to fp64, rows padded with zeros to
+// Dp (a zero k and zero q add exactly +0 to a chain that is never -0).
+template <typename T>
+__global__ void k_widen_q(const T *__restrict__ q, int64_t sB, int64_t sH, int64_t sS, int64_t Hq, int64_t D,
+                          int64_t Dp, int64_t i0, int64_t ni, int64_t ni_pad, int64_t total,
+                          double *__restrict__ out) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t d = t % Dp;
+        const int64_t r = t / Dp;
+        const int64_t ii = r % ni_pad;
+        const int64_t bh = r / ni_pad;
+        const int64_t b = bh / Hq, h = bh % Hq;
+        double x = 0.0;
+        if (d < D && ii < ni) x = (double)elem<T>::to_f32(q[b * sB + h * sH + (i0 + ii) * sS + d]);
+        out[t] = x;
+    }
+}
+
+hipError_t launch_widen_q(const Tensor &q, const AttnGeom &g, int64_t i0, int64_t i1, double *q64,
+                          hipStream_t s) {
+    const int64_t ni = i1 - i0, ni_pad = padded_rows(ni), total = g.B * g.Hq * ni_pad * g.Dp;
+    if (total <= 0) return hipSuccess;
+    if (q.dtype == 0)
+        hipLaunchKernelGGL(k_widen_q<float>, grid_for(total), dim3(256), 0, s, (const float *)q.data, q.sB, q.sH,
+                           q.sS, g.Hq, g.D, g.Dp, i0, ni, ni_pad, total, q64);
+    else
+        hipLaunchKernelGGL(k_widen_q<bf16_t>, grid_for(total), dim3(256), 0, s, (const bf16_t *)q.data, q.sB,
+                           q.sH, q.sS, g.Hq, g.D, g.Dp, i0, ni, ni_pad, total, q64);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pass 1: scores
+
+// Query rows of a tile are read at compile-time offsets r*DP*8 from one scalar
+// base address (DP = the padded head dim), so each row's slice arrives with a
+// single s_load_dwordx16 and the row loop is branch-free: the widened Q chunk
+// is padded with zero rows up to a multiple of kRowTile.
+template <typename TK, int DP>
+__global__ __launch_bounds__(256) void k_scores(const double *__restrict__ q64, const TK *__restrict__ kp,
+                                                int64_t ksB, int64_t ksH, int64_t ksS, int64_t Hq, int64_t group,
+                                                int64_t D, int causal, double scale, int64_t i0, int64_t i1,
+                                                int64_t ni_pad, int64_t kv_lo, int64_t kv_hi,
+                                                float *__restrict__ scores, uint32_t *__restrict__ rowmax_keys,
+                                                int64_t key_rows, int64_t key_row0) {
+    constexpr int RT = kRowTile;
+    constexpr int DC = 8;  // head-dim slice per step: one s_load_dwordx16 per row
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t bh = blockIdx.z;
+    const int64_t b = bh / Hq, hq = bh % Hq, hk = hq / group;
+    const int64_t ni = i1 - i0;
+    const int64_t ir0 = i0 + (int64_t)blockIdx.y * RT;
+    if (ir0 >= i1) return;
+    const int nrows = (int)std::min<int64_t>(RT, i1 - ir0);
+    const int64_t W = kv_hi - kv_lo;
+    const double *qtile = q64 + (bh * ni_pad + (ir0 - i0)) * DP;
+    const TK *kbase = kp + b * ksB + hk * ksH;
+
+    uint32_t mkey[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) mkey[r] = kKeyNegInf;
+
+    for (int64_t tile = blockIdx.x;; tile += gridDim.x) {
+        const int64_t jt0 = kv_lo + tile * kKeyTile;
+        if (jt0 >= kv_hi) break;
+        if (causal && jt0 > ir0 + nrows - 1) break;  // this and later tiles are masked
+        const int64_t j = jt0 + wave * 64 + lane;
+        const bool jv = j < kv_hi;
+        const TK *krow = kbase + (jv ? j : kv_lo) * ksS;
+        double acc[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = 0.0;
+        for (int dc = 0; dc < DP; dc += DC) {
+            double kv[DC];
+#pragma unroll
+            for (int u = 0; u < DC; ++u)
+                kv[u] = (jv && dc + u < D) ? (double)elem<TK>::to_f32(krow[dc + u]) : 0.0;
+            const double *qd = qtile + dc;
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+#pragma unroll
+                for (int u = 0; u < DC; ++u) acc[r] = fma(qd[r * DP + u], kv[u], acc[r]);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            if (r < nrows) {
+                const int64_t i = ir0 + r;
+                const float sc = (float)(scale * acc[r]);
+                if (scores && jv) scores[(bh * ni + (i - i0)) * W + (j - kv_lo)] = sc;
+                if (jv && (!causal || j <= i)) mkey[r] = std::max(mkey[r], order_key(sc));
+            }
+        }
+    }
+    if (!rowmax_keys) return;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        if (r < nrows) {
+            uint32_t m = mkey[r];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) m = std::max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+            if (lane == 0) atomicMax(&rowmax_keys[bh * key_rows + (ir0 + r - key_row0)], m);
+        }
+    }
+}
+
+template <typename TK, int DP>
+static void launch_scores_dp(dim3 grid, const Tensor &k, const AttnGeom &g, const double *q64, int64_t i0,
+                             int64_t i1, int64_t kv_lo, int64_t kv_hi, float *scores, uint32_t *rowmax_keys,
+                             int64_t key_rows, int64_t key_row0, hipStream_t s) {
+    hipLaunchKernelGGL((k_scores<TK, DP>), grid, dim3(256), 0, s, q64, (const TK *)k.data, k.sB, k.sH, k.sS, g.Hq,
+                       g.Hq / g.Hkv, g.D, g.causal, g.scale, i0, i1, padded_rows(i1 - i0), kv_lo, kv_hi, scores,
+                       rowmax_keys, key_rows, key_row0);
+}
+
+template <typename TK>
+static void launch_scores_t(dim3 grid, const Tensor &k, const AttnGeom &g, const double *q64, int64_t i0,
+                            int64_t i1, int64_t kv_lo, int64_t kv_hi, float *scores, uint32_t *rowmax_keys,
+                            int64_t key_rows, int64_t key_row0, hipStream_t s) {
+    switch (g.Dp) {
+    case 16: launch_scores_dp<TK, 16>(grid, k, g, q64, i0, i1, kv_lo, kv_hi, scores, rowmax_keys, key_rows, key_row0, s); break;
+    case 32: launch_scores_dp<TK, 32>(grid, k, g, q64, i0, i1, kv_lo, kv_hi, scores, rowmax_keys, key_rows, key_row0, s); break;
+    case 64: launch_scores_dp<TK, 64>(grid, k, g, q64, i0, i1, kv_lo, kv_hi, scores, rowmax_keys, key_rows, key_row0, s); break;
+    case 128: launch_scores_dp<TK, 128>(grid, k, g, q64, i0, i1, kv_lo, kv_hi, scores, rowmax_keys, key_rows, key_row0, s); break;
+    default: launch_scores_dp<TK, 256>(grid, k, g, q64, i0, i1, kv_lo, kv_hi, scores, rowmax_keys, key_rows, key_row0, s); break;
+    }
+}
+
+hipError_t launch_scores(const Tensor &k, const AttnGeom &g, const double *q64, int64_t i0, int64_t i1,
+                         int64_t kv_lo, int64_t kv_hi, float *scores, uint32_t *rowmax_keys, int64_t key_rows,
+                         int64_t key_row0, hipStream_t s) {
+    const int64_t ni = i1 - i0;
+    if (ni <= 0 || kv_hi <= kv_lo) return hipSuccess;
+    const int64_t ktiles = (kv_hi - kv_lo + kKeyTile - 1) / kKeyTile;
+    const int64_t parts = std::min<int64_t>(ktiles, 8);
+    dim3 grid((unsigned)parts, (unsigned)((ni + kRowTile - 1) / kRowTile), (unsigned)(g.B * g.Hq));
+    if (k.dtype == 0)
+        launch_scores_t<float>(grid, k, g, q64, i0, i1, kv_lo, kv_hi, scores, rowmax_keys, key_rows, key_row0, s);
+    else
+        launch_scores_t<bf16_t>(grid, k, g, q64, i0, i1, kv_lo, kv_hi, scores, rowmax_keys, key_rows, key_row0, s);
+    return hipGetLastError();
+}
+
+__global__ void k_keys_to_f32(const uint32_t *__restrict__ keys, float *__restrict__ out, int64_t BHq, int64_t rows,
+                              int64_t out_rows, int64_t out_row0) {
+    const int64_t n = BHq * rows;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t bh = t / rows, r = t % rows;
+        out[bh * out_rows + out_row0 + r] = key_value(keys[t]);
+    }
+}
+
+hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t BHq, int64_t rows, int64_t out_rows,
+                              int64_t out_row0, hipStream_t s) {
+    if (BHq * rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_keys_to_f32, grid_for(BHq * rows), dim3(256), 0, s, keys, out, BHq, rows, out_rows,
+                       out_row0);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pass 2: weights
+
+__global__ void k_weights(float *__restrict__ sc, const float *__restrict__ rowmax, int64_t rm_rows,
+                          int64_t rm_row0, int64_t i0, int64_t ni, int64_t kv_lo, int64_t W, int causal,
+                          int64_t total) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t jj = t % W;
+        const int64_t r = t / W;
+        const int64_t ii = r % ni, bh = r / ni;
+        const int64_t i = i0 + ii, j = kv_lo + jj;
+        float w = 0.0f;
+        if (!causal || j <= i) w = weight(sc[t], rowmax[bh * rm_rows + (i - rm_row0)]);
+        sc[t] = w;
+    }
+}
+
+hipError_t launch_weights(const AttnGeom &g, float *scores, const float *rowmax, int64_t rm_rows, int64_t rm_row0,
+                          int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, hipStream_t s) {
+    const int64_t ni = i1 - i0, W = kv_hi - kv_lo, total = g.B * g.Hq * ni * W;
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_weights, grid_for(total), dim3(256), 0, s, scores, rowmax, rm_rows, rm_row0, i0, ni,
+                       kv_lo, W, g.causal, total);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pass 2: exact deposit
+
+template <typename TV>
+__global__ __launch_bounds__(256) void k_deposit(const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
+                                                 int64_t Hq, int64_t group, int64_t D, int causal,
+                                                 const float *__restrict__ wts, int64_t i0, int64_t ni,
+                                                 int64_t kv_lo, int64_t kv_hi, int64_t nDB, int64_t total_waves,
+                                                 int64_t *__restrict__ num, int64_t *__restrict__ den,
+                                                 int64_t plane_rows, int64_t rows_per_bh, int64_t row0) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wid >= total_waves) return;
+    const int64_t rl = wid / nDB, db = wid % nDB;
+    const int64_t bh = rl / ni, ii = rl % ni;
+    const int64_t i = i0 + ii;
+    const int64_t b = bh / Hq, hq = bh % Hq, hk = hq / group;
+    const int64_t d = db * 64 + lane;
+    const bool dv = d < D;
+    const int64_t W = kv_hi - kv_lo;
+    const int64_t jend = causal ? std::min<int64_t>(kv_hi, i + 1) : kv_hi;
+    const float *wrow = wts + rl * W;
+    const TV *vcol = vp + b * vsB + hk * vsH + (dv ? d : 0);
+    const int64_t prow = bh * rows_per_bh + (i - row0);  // row in the digit planes
+    constexpr int VMB = elem<TV>::mant_bits;
+    const bool den_lane = (db == 0) && (lane == 0);
+
+    Window nw, dw;
+    nw.init();
+    dw.init();
+    int64_t *ndig = num + prow * D + d;
+    int64_t *ddig = den + prow;
+    const int64_t nplane = plane_rows * D;
+
+    for (int64_t j = kv_lo; j < jend; ++j) {
+        const float w = wrow[j - kv_lo];
+        if (w == 0.0f) continue;
+        const int ew = f32_exp(w);
+        const int lw = max(ew, -126) - 23;  // w is a multiple of 2^lw
+        if (dv) {
+            const float vf = elem<TV>::to_f32(vcol[j * vsS]);
+            if (vf != 0.0f) {
+                const int ev = f32_exp(vf);
+                const double p = (double)w * (double)vf;  // exact: at most 48 significant bits
+                nw.add<kNumDigits>(p, lw + max(ev, -126) - VMB, ew + ev + 2, kNumGcap, kNumElo, ndig, nplane);
+            }
+        }
+        if (den_lane) dw.add<kDenDigits>((double)w, lw, ew + 1, kDenGcap, kDenElo, ddig, plane_rows);
+    }
+    if (dv) nw.flush<kNumDigits>(kNumElo, ndig, nplane);
+    if (den_lane) dw.flush<kDenDigits>(kDenElo, ddig, plane_rows);
+}
+
+hipError_t launch_deposit(const Tensor &v, const AttnGeom &g, const float *weights, int64_t i0, int64_t i1,
+                          int64_t kv_lo, int64_t kv_hi, int64_t *num, int64_t *den, int64_t plane_rows,
+                          int64_t rows_per_bh, int64_t row0, hipStream_t s) {
+    const int64_t ni = i1 - i0;
+    if (ni <= 0 || kv_hi <= kv_lo) return hipSuccess;
+    const int64_t nDB = (g.D + 63) / 64;
+    const int64_t waves = g.B * g.Hq * ni * nDB;
+    const unsigned blocks = (unsigned)((waves + 3) / 4);
+    const int64_t group = g.Hq / g.Hkv;
+    if (v.dtype == 0)
+        hipLaunchKernelGGL(k_deposit<float>, dim3(blocks), dim3(256), 0, s, (const float *)v.data, v.sB, v.sH,
+                           v.sS, g.Hq, group, g.D, g.causal, weights, i0, ni, kv_lo, kv_hi, nDB, waves, num, den,
+                           plane_rows, rows_per_bh, row0);
+    else
+        hipLaunchKernelGGL(k_deposit<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t *)v.data, v.sB, v.sH,
+                           v.sS, g.Hq, group, g.D, g.causal, weights, i0, ni, kv_lo, kv_hi, nDB, waves, num, den,
+                           plane_rows, rows_per_bh, row0);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- digits
+
+template <int K>
+__global__ void k_normalize(int64_t *__restrict__ dg, int64_t n) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+        int64_t d[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) d[k] = dg[k * n + t];
+        canonicalize<K>(d);
+#pragma unroll
+        for (int k = 0; k < K; ++k) dg[k * n + t] = d[k];
+    }
+}
+
+template <int K>
+__global__ void k_digits_combine(int64_t *__restrict__ acc, const int64_t *__restrict__ part, int64_t n) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+        int64_t d[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) d[k] = acc[k * n + t] + part[k * n + t];
+        canonicalize<K>(d);
+#pragma unroll
+        for (int k = 0; k < K; ++k) acc[k * n + t] = d[k];
+    }
+}
+
+hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hipStream_t s) {
+    if (n_values <= 0) return hipSuccess;
+    if (n_digits == kNumDigits)
+        hipLaunchKernelGGL(k_normalize<kNumDigits>, grid_for(n_values), dim3(256), 0, s, digits, n_values);
+    else
+        hipLaunchKernelGGL(k_normalize<kDenDigits>, grid_for(n_values), dim3(256), 0, s, digits, n_values);
+    return hipGetLastError();
+}
+
+hipError_t launch_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int n_digits,
+                                 hipStream_t s) {
+    if (n_values <= 0) return hipSuccess;
+    if (n_digits == kNumDigits)
+        hipLaunchKernelGGL(k_digits_combine<kNumDigits>, grid_for(n_values), dim3(256), 0, s, acc, part,
+                           n_values);
+    else
+        hipLaunchKernelGGL(k_digits_combine<kDenDigits>, grid_for(n_values), dim3(256), 0, s, acc, part,
+                           n_values);
+    return hipGetLastError();
+}
+
+__global__ void k_rowmax_combine(float *__restrict__ acc, const float *__restrict__ part, int64_t n) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x)
+        acc[t] = key_value(max(order_key(acc[t]), order_key(part[t])));
+}
+
+hipError_t launch_rowmax_combine(float *acc, const float *part, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rowmax_combine, grid_for(n), dim3(256), 0, s, acc, part, n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- finalize
+
+__global__ void k_finalize(const int64_t *__restrict__ num, const int64_t *__restrict__ den, int64_t plane_rows,
+                           int64_t rows_per_bh, int64_t row0, int64_t Hq, int64_t i0, int64_t ni, int64_t D,
+                           float *__restrict__ o, int64_t osB, int64_t osH, int64_t osS, int64_t total) {
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t d = t % D;
+        const int64_t r = t / D;
+        const int64_t ii = r % ni, bh = r / ni;
+        const int64_t i = i0 + ii;
+        const int64_t prow = bh * rows_per_bh + (i - row0);
+        int64_t nd[kNumDigits], dd[kDenDigits];
+        const int64_t nplane = plane_rows * D;
+#pragma unroll
+        for (int k = 0; k < kNumDigits; ++k) nd[k] = num[k * nplane + prow * D + d];
+#pragma unroll
+        for (int k = 0; k < kDenDigits; ++k) dd[k] = den[k * plane_rows + prow];
+        canonicalize<kNumDigits>(nd);
+        canonicalize<kDenDigits>(dd);
+        const double n64 = digits_to_f64<kNumDigits>(nd, kNumElo);
+        const double d64 = digits_to_f64<kDenDigits>(dd, kDenElo);
+        const int64_t b = bh / Hq, h = bh % Hq;
+        o[b * osB + h * osH + i * osS + d] = (float)(n64 / d64);
+    }
+}
+
+hipError_t launch_finalize(const int64_t *num, const int64_t *den, int64_t plane_rows, int64_t rows_per_bh,
+                           int64_t row0, int64_t B_Hq, int64_t Hq, int64_t i0, int64_t i1, int64_t D,
+                           const OutView &o, hipStream_t s) {
+    const int64_t ni = i1 - i0, total = B_Hq * ni * D;
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_finalize, grid_for(total), dim3(256), 0, s, num, den, plane_rows, rows_per_bh, row0, Hq,
+                       i0, ni, D, o.data, o.sB, o.sH, o.sS, total);
+    return hipGetLastError();
+}
+
+}  // namespace det

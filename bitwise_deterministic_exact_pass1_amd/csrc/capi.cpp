@@ -1,0 +1,549 @@
+// capi.cpp -- the extern "C" entry points declared in include/det_attn.h.
+//
+// Every entry point validates its arguments on the host before the first HIP
+// call (so the checks run without a GPU), then enqueues a fixed sequence of
+// kernels on the caller's stream.  Work is split into query-row chunks sized by
+// the caller's workspace; rows are independent, so the chunking never changes
+// a result bit.
+#include "det_attn.h"
+#include "kernels.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+using namespace det;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return DET_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(DET_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                        \
+    do {                                           \
+        hipError_t _e = (expr);                    \
+        if (_e != hipSuccess) return hip_fail(_e, what); \
+    } while (0)
+
+constexpr size_t kDefaultBudget = (size_t)8 << 30;  // default workspace per call
+
+Tensor to_t(const det_tensor *t) { return Tensor{t->data, t->dtype, t->B, t->H, t->S, t->D, t->sB, t->sH, t->sS}; }
+
+int check_tensor(const det_tensor *t, const char *name) {
+    if (!t) return fail(DET_E_NULL, "%s descriptor is NULL", name);
+    if (t->dtype != DET_F32 && t->dtype != DET_BF16) return fail(DET_E_DTYPE, "%s dtype %d is not f32/bf16", name, t->dtype);
+    if (t->B < 1 || t->H < 1 || t->S < 0) return fail(DET_E_SHAPE, "%s has B=%lld H=%lld S=%lld", name,
+                                                      (long long)t->B, (long long)t->H, (long long)t->S);
+    if (t->D < 1 || t->D > 256) return fail(DET_E_SHAPE, "%s head dim D=%lld outside [1,256]", name, (long long)t->D);
+    if (t->sB < 0 || t->sH < 0 || t->sS < 0) return fail(DET_E_STRIDE, "%s has a negative stride", name);
+    if (!t->data && t->S > 0) return fail(DET_E_NULL, "%s data is NULL", name);
+    return DET_OK;
+}
+
+int check_qk(const det_tensor *q, const det_tensor *k, int causal) {
+    int rc;
+    if ((rc = check_tensor(q, "q")) || (rc = check_tensor(k, "k"))) return rc;
+    if (q->dtype != k->dtype) return fail(DET_E_DTYPE, "q and k dtypes differ");
+    if (q->B != k->B) return fail(DET_E_SHAPE, "q and k batch sizes differ");
+    if (q->D != k->D) return fail(DET_E_SHAPE, "q and k head dims differ");
+    if (q->H % k->H) return fail(DET_E_SHAPE, "Hq=%lld is not a multiple of Hkv=%lld", (long long)q->H, (long long)k->H);
+    if (causal && q->S != k->S) return fail(DET_E_SHAPE, "causal attention needs Sq == Skv");
+    return DET_OK;
+}
+
+int check_qkv(const det_tensor *q, const det_tensor *k, const det_tensor *v, int causal) {
+    int rc;
+    if ((rc = check_qk(q, k, causal)) || (rc = check_tensor(v, "v"))) return rc;
+    if (v->dtype != k->dtype) return fail(DET_E_DTYPE, "v and k dtypes differ");
+    if (v->B != k->B || v->H != k->H || v->S != k->S || v->D != k->D)
+        return fail(DET_E_SHAPE, "v shape differs from k");
+    return DET_OK;
+}
+
+int check_range(const det_tensor *k, int64_t lo, int64_t hi) {
+    if (lo < 0 || hi < lo || hi > k->S)
+        return fail(DET_E_SHAPE, "key range [%lld,%lld) outside [0,%lld]", (long long)lo, (long long)hi, (long long)k->S);
+    return DET_OK;
+}
+
+int check_out(const det_out *o) {
+    if (!o) return fail(DET_E_NULL, "output descriptor is NULL");
+    if (!o->data) return fail(DET_E_NULL, "output data is NULL");
+    if (o->sB < 0 || o->sH < 0 || o->sS < 0) return fail(DET_E_STRIDE, "output has a negative stride");
+    return DET_OK;
+}
+
+AttnGeom geom(const det_tensor *q, const det_tensor *k, int causal, double scale) {
+    AttnGeom g;
+    g.B = q->B;
+    g.Hq = q->H;
+    g.Hkv = k->H;
+    g.Sq = q->S;
+    g.Skv = k->S;
+    g.D = q->D;
+    g.Dp = padded_dim(q->D);
+    g.causal = causal;
+    g.scale = scale;
+    return g;
+}
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+    char *p;
+    size_t used = 0;
+    template <typename T> T *take(size_t count) {
+        T *r = (T *)(p + used);
+        used += align256(count * sizeof(T));
+        return r;
+    }
+};
+
+// ---- per-chunk workspace needs of each entry point (ni = query rows per chunk)
+
+size_t bytes_rowmax(const AttnGeom &g, int64_t ni) {
+    const int64_t bh = g.B * g.Hq;
+    return align256((size_t)bh * padded_rows(ni) * g.Dp * 8) + align256((size_t)bh * ni * 4);
+}
+
+size_t bytes_accumulate(const AttnGeom &g, int64_t ni, int64_t W) {
+    const int64_t bh = g.B * g.Hq;
+    return align256((size_t)bh * padded_rows(ni) * g.Dp * 8) + align256((size_t)bh * ni * W * 4);
+}
+
+size_t bytes_fused(const AttnGeom &g, int64_t ni) {
+    const int64_t bh = g.B * g.Hq, rows = bh * ni;
+    return score_scratch_bytes(g, ni, g.Skv) + align256((size_t)rows * 4) +
+           align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8);
+}
+
+size_t bytes_sharded(const AttnGeom &g, int64_t ni, int64_t maxlen) {
+    const int64_t bh = g.B * g.Hq, rows = bh * ni;
+    return score_scratch_bytes(g, ni, maxlen) + 2 * align256((size_t)rows * 4) +
+           2 * (align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8));
+}
+
+// Largest chunk (a multiple of kRowTile, or all Sq rows) whose need fits `budget`;
+// 0 if even one tile does not fit.
+template <typename F> int64_t choose_chunk(int64_t Sq, size_t budget, F need) {
+    if (Sq <= 0) return 0;
+    if (need(Sq) <= budget) return Sq;
+    int64_t lo = 0, hi = (Sq - 1) / kRowTile;  // in tiles
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) / 2;
+        if (need(mid * kRowTile) <= budget) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo * kRowTile;
+}
+
+template <typename F> size_t default_size(int64_t Sq, F need) {
+    if (Sq <= 0) return 256;
+    const int64_t ni = std::max<int64_t>(std::min<int64_t>(Sq, kRowTile), choose_chunk(Sq, kDefaultBudget, need));
+    return need(ni);
+}
+
+int check_ws(void *ws, size_t have, size_t need_min) {
+    if (need_min == 0) return DET_OK;
+    if (!ws) return fail(DET_E_WORKSPACE, "workspace is NULL (need %zu bytes)", need_min);
+    if (((uintptr_t)ws) & 255) return fail(DET_E_WORKSPACE, "workspace is not 256-byte aligned");
+    if (have < need_min) return fail(DET_E_WORKSPACE, "workspace has %zu bytes, need at least %zu", have, need_min);
+    return DET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *det_last_error(void) { return g_err.c_str(); }
+
+int det_digit_format(int32_t which, int32_t *n_digits, int32_t *lsb_exp2) {
+    if (!n_digits || !lsb_exp2) return fail(DET_E_NULL, "output pointer is NULL");
+    if (which == 0) {
+        *n_digits = kNumDigits;
+        *lsb_exp2 = kNumElo;
+    } else if (which == 1) {
+        *n_digits = kDenDigits;
+        *lsb_exp2 = kDenElo;
+    } else {
+        return fail(DET_E_VALUE, "digit format %d is neither 0 (NUM) nor 1 (DEN)", which);
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------ rowmax
+
+size_t det_attn_rowmax_workspace_size(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi) {
+    if (check_qk(q, k, 0) || check_range(k, kv_lo, kv_hi)) return 0;
+    const AttnGeom g = geom(q, k, 0, 1.0);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_rowmax(g, ni); });
+}
+
+int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi, int32_t causal,
+                    double scale, float *rowmax, void *workspace, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_qk(q, k, causal)) || (rc = check_range(k, kv_lo, kv_hi))) return rc;
+    if (!rowmax && q->S > 0) return fail(DET_E_NULL, "rowmax is NULL");
+    const AttnGeom g = geom(q, k, causal, scale);
+    auto need = [&](int64_t ni) { return bytes_rowmax(g, ni); };
+    if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
+    if (g.Sq == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    const Tensor tq = to_t(q), tk = to_t(k);
+    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
+    for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
+        const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
+        Carver c{(char *)workspace};
+        double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
+        uint32_t *keys = c.take<uint32_t>(bh * ni);
+        HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
+        HIP_TRY(launch_fill_u32(keys, bh * ni, kKeyNegInf, s), "fill");
+        HIP_TRY(launch_scores(tk, g, q64, i0, i1, kv_lo, kv_hi, nullptr, keys, ni, i0, s), "scores");
+        HIP_TRY(launch_keys_to_f32(keys, rowmax, bh, ni, g.Sq, i0, s), "rowmax");
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------ accumulate
+
+size_t det_attn_accumulate_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
+                                          int64_t kv_lo, int64_t kv_hi) {
+    if (check_qkv(q, k, v, 0) || check_range(k, kv_lo, kv_hi)) return 0;
+    const AttnGeom g = geom(q, k, 0, 1.0);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_accumulate(g, ni, kv_hi - kv_lo); });
+}
+
+int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tensor *v, const float *rowmax,
+                        int64_t kv_lo, int64_t kv_hi, int32_t causal, double scale, int64_t *num, int64_t *den,
+                        int32_t add_into, void *workspace, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_qkv(q, k, v, causal)) || (rc = check_range(k, kv_lo, kv_hi))) return rc;
+    if (q->S > 0 && (!rowmax || !num || !den)) return fail(DET_E_NULL, "rowmax, num or den is NULL");
+    const AttnGeom g = geom(q, k, causal, scale);
+    const int64_t W = kv_hi - kv_lo;
+    auto need = [&](int64_t ni) { return bytes_accumulate(g, ni, W); };
+    if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
+    if (g.Sq == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    const Tensor tq = to_t(q), tk = to_t(k), tv = to_t(v);
+    const int64_t bh = g.B * g.Hq, rows = bh * g.Sq;
+    if (!add_into) {
+        HIP_TRY(launch_fill_i64(num, kNumDigits * rows * g.D, 0, s), "fill num");
+        HIP_TRY(launch_fill_i64(den, kDenDigits * rows, 0, s), "fill den");
+    }
+    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need);
+    for (int64_t i0 = 0; i0 < g.Sq && W > 0; i0 += chunk) {
+        const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
+        Carver c{(char *)workspace};
+        double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
+        float *sc = c.take<float>(bh * ni * W);
+        HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
+        HIP_TRY(launch_scores(tk, g, q64, i0, i1, kv_lo, kv_hi, sc, nullptr, 0, 0, s), "scores");
+        HIP_TRY(launch_weights(g, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, s), "weights");
+        HIP_TRY(launch_deposit(tv, g, sc, i0, i1, kv_lo, kv_hi, num, den, rows, g.Sq, 0, s), "deposit");
+    }
+    HIP_TRY(launch_normalize(num, rows * g.D, kNumDigits, s), "normalize num");
+    HIP_TRY(launch_normalize(den, rows, kDenDigits, s), "normalize den");
+    return ok();
+}
+
+// ------------------------------------------------------------------ composition
+
+int det_rowmax_combine(float *acc, const float *part, int64_t n, void *stream) {
+    if (n < 0) return fail(DET_E_SHAPE, "negative count");
+    if (n > 0 && (!acc || !part)) return fail(DET_E_NULL, "acc or part is NULL");
+    HIP_TRY(launch_rowmax_combine(acc, part, n, (hipStream_t)stream), "rowmax combine");
+    return ok();
+}
+
+int det_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int32_t n_digits, void *stream) {
+    if (n_values < 0) return fail(DET_E_SHAPE, "negative count");
+    if (n_digits != kNumDigits && n_digits != kDenDigits)
+        return fail(DET_E_VALUE, "n_digits must be %d or %d", kNumDigits, kDenDigits);
+    if (n_values > 0 && (!acc || !part)) return fail(DET_E_NULL, "acc or part is NULL");
+    HIP_TRY(launch_digits_combine(acc, part, n_values, n_digits, (hipStream_t)stream), "digits combine");
+    return ok();
+}
+
+// ------------------------------------------------------------------ finalize
+
+int det_attn_finalize(const int64_t *num, const int64_t *den, int64_t B, int64_t Hq, int64_t Sq, int64_t D,
+                      const det_out *o, void *stream) {
+    if (B < 1 || Hq < 1 || Sq < 0 || D < 1 || D > 256) return fail(DET_E_SHAPE, "bad finalize shape");
+    int rc;
+    if (Sq == 0) return ok();
+    if ((rc = check_out(o))) return rc;
+    if (!num || !den) return fail(DET_E_NULL, "num or den is NULL");
+    const int64_t rows = B * Hq * Sq;
+    HIP_TRY(launch_finalize(num, den, rows, Sq, 0, B * Hq, Hq, 0, Sq, D, OutView{o->data, o->sB, o->sH, o->sS},
+                            (hipStream_t)stream),
+            "finalize");
+    return ok();
+}
+
+// ------------------------------------------------------------------ fused
+
+size_t det_attn_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal) {
+    if (check_qkv(q, k, v, causal)) return 0;
+    const AttnGeom g = geom(q, k, causal, 1.0);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_fused(g, ni); });
+}
+
+int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
+             const det_out *o, void *workspace, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_qkv(q, k, v, causal))) return rc;
+    if (q->S > 0 && (rc = check_out(o))) return rc;
+    const AttnGeom g = geom(q, k, causal, scale);
+    auto need = [&](int64_t ni) { return bytes_fused(g, ni); };
+    if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
+    if (g.Sq == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    const Tensor tq = to_t(q), tk = to_t(k), tv = to_t(v);
+    const OutView ov{o->data, o->sB, o->sH, o->sS};
+    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
+    for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
+        const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
+        Carver c{(char *)workspace};
+        double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
+        uint32_t *keys = c.take<uint32_t>(rows);
+        float *sc = c.take<float>(rows * g.Skv);
+        float *rm = c.take<float>(rows);
+        int64_t *num = c.take<int64_t>(kNumDigits * rows * g.D);
+        int64_t *den = c.take<int64_t>(kDenDigits * rows);
+        HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
+        HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
+        HIP_TRY(launch_scores(tk, g, q64, i0, i1, 0, g.Skv, sc, keys, ni, i0, s), "scores");
+        HIP_TRY(launch_keys_to_f32(keys, rm, bh, ni, ni, 0, s), "rowmax");
+        HIP_TRY(launch_weights(g, sc, rm, ni, i0, i0, i1, 0, g.Skv, s), "weights");
+        HIP_TRY(launch_fill_i64(num, kNumDigits * rows * g.D, 0, s), "fill num");
+        HIP_TRY(launch_fill_i64(den, kDenDigits * rows, 0, s), "fill den");
+        HIP_TRY(launch_deposit(tv, g, sc, i0, i1, 0, g.Skv, num, den, rows, ni, i0, s), "deposit");
+        HIP_TRY(launch_finalize(num, den, rows, ni, i0, bh, g.Hq, i0, i1, g.D, ov, s), "finalize");
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------ sharded
+
+namespace {
+int check_splits(const det_tensor *k, const int64_t *splits, int32_t n, const int32_t *order) {
+    if (n < 1) return fail(DET_E_VALUE, "need at least one KV split");
+    if (!splits) return fail(DET_E_NULL, "kv_splits is NULL");
+    int64_t sum = 0;
+    for (int32_t a = 0; a < n; ++a) {
+        if (splits[a] < 0) return fail(DET_E_VALUE, "negative split length");
+        sum += splits[a];
+    }
+    if (sum != k->S) return fail(DET_E_VALUE, "kv_splits sum to %lld, Skv is %lld", (long long)sum, (long long)k->S);
+    if (order) {
+        std::vector<char> seen(n, 0);
+        for (int32_t a = 0; a < n; ++a) {
+            if (order[a] < 0 || order[a] >= n || seen[order[a]]) return fail(DET_E_VALUE, "order is not a permutation");
+            seen[order[a]] = 1;
+        }
+    }
+    return DET_OK;
+}
+int64_t max_split(const int64_t *splits, int32_t n) {
+    int64_t m = 0;
+    for (int32_t a = 0; a < n; ++a) m = std::max(m, splits[a]);
+    return m;
+}
+}  // namespace
+
+size_t det_attn_sharded_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
+                                       const int64_t *kv_splits, int32_t n_splits, int32_t causal) {
+    if (check_qkv(q, k, v, causal) || check_splits(k, kv_splits, n_splits, nullptr)) return 0;
+    const AttnGeom g = geom(q, k, causal, 1.0);
+    const int64_t ml = max_split(kv_splits, n_splits);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_sharded(g, ni, ml); });
+}
+
+int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor *v, const int64_t *kv_splits,
+                     int32_t n_splits, const int32_t *order, int32_t causal, double scale, const det_out *o,
+                     void *workspace, size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_qkv(q, k, v, causal)) || (rc = check_splits(k, kv_splits, n_splits, order))) return rc;
+    if (q->S > 0 && (rc = check_out(o))) return rc;
+    const AttnGeom g = geom(q, k, causal, scale);
+    const int64_t ml = max_split(kv_splits, n_splits);
+    auto need = [&](int64_t ni) { return bytes_sharded(g, ni, ml); };
+    if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
+    if (g.Sq == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    const Tensor tq = to_t(q), tk = to_t(k), tv = to_t(v);
+    const OutView ov{o->data, o->sB, o->sH, o->sS};
+    std::vector<int64_t> lo(n_splits);
+    int64_t run = 0;
+    for (int32_t a = 0; a < n_splits; ++a) {
+        lo[a] = run;
+        run += kv_splits[a];
+    }
+    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
+    for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
+        const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
+        Carver c{(char *)workspace};
+        double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
+        uint32_t *keys = c.take<uint32_t>(rows);
+        float *sc = c.take<float>(rows * ml);
+        float *rm_acc = c.take<float>(rows);
+        float *rm_part = c.take<float>(rows);
+        int64_t *num_acc = c.take<int64_t>(kNumDigits * rows * g.D);
+        int64_t *den_acc = c.take<int64_t>(kDenDigits * rows);
+        int64_t *num_part = c.take<int64_t>(kNumDigits * rows * g.D);
+        int64_t *den_part = c.take<int64_t>(kDenDigits * rows);
+        HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
+        // pass 1: rowmax of each shard, composed by max
+        HIP_TRY(launch_fill_u32((uint32_t *)rm_acc, rows, 0xff800000u, s), "fill rowmax");  // -inf
+        for (int32_t a = 0; a < n_splits; ++a) {
+            const int32_t sh = order ? order[a] : a;
+            const int64_t l = lo[sh], h = l + kv_splits[sh];
+            HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
+            HIP_TRY(launch_scores(tk, g, q64, i0, i1, l, h, nullptr, keys, ni, i0, s), "scores");
+            HIP_TRY(launch_keys_to_f32(keys, rm_part, bh, ni, ni, 0, s), "rowmax");
+            HIP_TRY(launch_rowmax_combine(rm_acc, rm_part, rows, s), "rowmax combine");
+        }
+        // pass 2: canonical digits of each shard against the global max, composed by int64 add
+        HIP_TRY(launch_fill_i64(num_acc, kNumDigits * rows * g.D, 0, s), "fill num");
+        HIP_TRY(launch_fill_i64(den_acc, kDenDigits * rows, 0, s), "fill den");
+        for (int32_t a = 0; a < n_splits; ++a) {
+            const int32_t sh = order ? order[a] : a;
+            const int64_t l = lo[sh], h = l + kv_splits[sh];
+            HIP_TRY(launch_fill_i64(num_part, kNumDigits * rows * g.D, 0, s), "fill num");
+            HIP_TRY(launch_fill_i64(den_part, kDenDigits * rows, 0, s), "fill den");
+            if (h > l) {
+                HIP_TRY(launch_scores(tk, g, q64, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
+                HIP_TRY(launch_weights(g, sc, rm_acc, ni, i0, i0, i1, l, h, s), "weights");
+                HIP_TRY(launch_deposit(tv, g, sc, i0, i1, l, h, num_part, den_part, rows, ni, i0, s), "deposit");
+            }
+            HIP_TRY(launch_normalize(num_part, rows * g.D, kNumDigits, s), "normalize");
+            HIP_TRY(launch_normalize(den_part, rows, kDenDigits, s), "normalize");
+            HIP_TRY(launch_digits_combine(num_acc, num_part, rows * g.D, kNumDigits, s), "combine");
+            HIP_TRY(launch_digits_combine(den_acc, den_part, rows, kDenDigits, s), "combine");
+        }
+        HIP_TRY(launch_finalize(num_acc, den_acc, rows, ni, i0, bh, g.Hq, i0, i1, g.D, ov, s), "finalize");
+    }
+    return ok();
+}
+
+// ------------------------------------------------------------------ cross-entropy
+
+namespace {
+int check_logits(const void *x, int32_t dtype, int64_t N, int64_t V, int64_t ld) {
+    if (dtype != DET_F32 && dtype != DET_BF16) return fail(DET_E_DTYPE, "logits dtype %d is not f32/bf16", dtype);
+    if (N < 0 || V < 1) return fail(DET_E_SHAPE, "bad logits shape N=%lld V=%lld", (long long)N, (long long)V);
+    if (ld < V) return fail(DET_E_STRIDE, "row stride %lld < V=%lld", (long long)ld, (long long)V);
+    if (N > 0 && !x) return fail(DET_E_NULL, "logits is NULL");
+    return DET_OK;
+}
+// Range form used by rowmax / denom_digits, where V itself is not passed.
+int check_logits_range(const void *x, int32_t dtype, int64_t N, int64_t ld, int64_t lo, int64_t hi) {
+    if (dtype != DET_F32 && dtype != DET_BF16) return fail(DET_E_DTYPE, "logits dtype %d is not f32/bf16", dtype);
+    if (N < 0 || ld < 1) return fail(DET_E_SHAPE, "bad logits shape N=%lld ld=%lld", (long long)N, (long long)ld);
+    if (lo < 0 || hi < lo || hi > ld)
+        return fail(DET_E_SHAPE, "vocab range [%lld,%lld) outside the row of %lld", (long long)lo, (long long)hi,
+                    (long long)ld);
+    if (N > 0 && !x) return fail(DET_E_NULL, "logits is NULL");
+    return DET_OK;
+}
+int check_vrange(int64_t V, int64_t lo, int64_t hi) {
+    if (lo < 0 || hi < lo || hi > V) return fail(DET_E_SHAPE, "vocab range [%lld,%lld) outside [0,%lld]", (long long)lo,
+                                                 (long long)hi, (long long)V);
+    return DET_OK;
+}
+}  // namespace
+
+int det_ce_rowmax(const void *logits, int32_t dtype, int64_t N, int64_t ld, int64_t v_lo, int64_t v_hi,
+                  float *rowmax, void *stream) {
+    int rc;
+    if ((rc = check_logits_range(logits, dtype, N, ld, v_lo, v_hi))) return rc;
+    if (N > 0 && !rowmax) return fail(DET_E_NULL, "rowmax is NULL");
+    HIP_TRY(launch_ce_rowmax(logits, dtype, N, ld, v_lo, v_hi, rowmax, (hipStream_t)stream), "ce rowmax");
+    return ok();
+}
+
+int det_ce_denom_digits(const void *logits, int32_t dtype, int64_t N, int64_t ld, const float *rowmax,
+                        int64_t v_lo, int64_t v_hi, int64_t *den, int32_t add_into, void *stream) {
+    int rc;
+    if ((rc = check_logits_range(logits, dtype, N, ld, v_lo, v_hi))) return rc;
+    if (N > 0 && (!rowmax || !den)) return fail(DET_E_NULL, "rowmax or den is NULL");
+    HIP_TRY(launch_ce_denom(logits, dtype, N, ld, rowmax, v_lo, v_hi, den, add_into, (hipStream_t)stream),
+            "ce denom");
+    return ok();
+}
+
+int det_ce_finalize(const int64_t *den, const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld,
+                    const int64_t *targets, const float *rowmax, float *loss, double *denom, void *stream) {
+    int rc;
+    if ((rc = check_logits(logits, dtype, N, V, ld))) return rc;
+    if (N > 0 && (!den || !targets || !rowmax || !loss || !denom)) return fail(DET_E_NULL, "a required pointer is NULL");
+    HIP_TRY(launch_ce_finalize(den, logits, dtype, N, ld, targets, rowmax, loss, denom, (hipStream_t)stream),
+            "ce finalize");
+    return ok();
+}
+
+size_t det_ce_forward_workspace_size(int64_t) { return 0; }
+
+int det_ce_forward(const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
+                   float *loss, float *rowmax, double *denom, void *, size_t, void *stream) {
+    int rc;
+    if ((rc = check_logits(logits, dtype, N, V, ld))) return rc;
+    if (N > 0 && (!targets || !loss || !rowmax || !denom)) return fail(DET_E_NULL, "a required pointer is NULL");
+    HIP_TRY(launch_ce_forward(logits, dtype, N, V, ld, targets, loss, rowmax, denom, (hipStream_t)stream),
+            "ce forward");
+    return ok();
+}
+
+size_t det_ce_reduce_workspace_size(int64_t) { return 0; }
+
+int det_ce_reduce(const float *loss, int64_t N, int32_t reduction, float *out, void *, size_t, void *stream) {
+    if (N < 0) return fail(DET_E_SHAPE, "negative N");
+    if (reduction < 0 || reduction > 2) return fail(DET_E_VALUE, "reduction %d is not 0/1/2", reduction);
+    if (!out || (N > 0 && !loss)) return fail(DET_E_NULL, "loss or out is NULL");
+    hipStream_t s = (hipStream_t)stream;
+    if (reduction == 0) {
+        if (N > 0) HIP_TRY(hipMemcpyAsync(out, loss, N * sizeof(float), hipMemcpyDeviceToDevice, s), "copy");
+        return ok();
+    }
+    HIP_TRY(launch_ce_reduce(loss, N, reduction, out, nullptr, s), "ce reduce");
+    return ok();
+}
+
+int det_ce_backward(const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
+                    const float *rowmax, const double *denom, const float *grad_loss, int32_t reduction,
+                    float *grad, int64_t grad_ld, void *stream) {
+    int rc;
+    if ((rc = check_logits(logits, dtype, N, V, ld))) return rc;
+    if (reduction < 0 || reduction > 2) return fail(DET_E_VALUE, "reduction %d is not 0/1/2", reduction);
+    if (grad_ld < V) return fail(DET_E_STRIDE, "grad row stride %lld < V", (long long)grad_ld);
+    if (N > 0 && (!targets || !rowmax || !denom || !grad_loss || !grad))
+        return fail(DET_E_NULL, "a required pointer is NULL");
+    HIP_TRY(launch_ce_backward(logits, dtype, N, V, ld, targets, rowmax, denom, grad_loss, reduction, grad, grad_ld,
+                               (hipStream_t)stream),
+            "ce backward");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// kernels.hpp -- host-side launchers shared by the C ABI (capi.cpp) and the
+// kernel translation units.  Argument checking happens in capi.cpp before any
+// of these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dev_math.hpp"
+
+namespace det {
+
+struct Tensor {  // mirrors det_tensor
+    const void *data;
+    int dtype;  // 0 f32, 1 bf16
+    int64_t B, H, S, D;
+    int64_t sB, sH, sS;
+};
+
+struct OutView {
+    float *data;
+    int64_t sB, sH, sS;
+};
+
+// Geometry shared by the attention launchers.
+struct AttnGeom {
+    int64_t B, Hq, Hkv, Sq, Skv, D;
+    int64_t Dp;  // widened Q row length: D rounded up to 16, 32, 64, 128 or 256
+    int causal;
+    double scale;
+};
+
+constexpr int kRowTile = 32;    // query rows per score tile
+constexpr int kKeyTile = 256;   // keys per score tile (4 waves x 64 lanes)
+
+// Query rows of a chunk, padded to whole row tiles (padding rows are zero).
+inline int64_t padded_rows(int64_t ni) { return (ni + kRowTile - 1) / kRowTile * kRowTile; }
+inline int64_t padded_dim(int64_t D) {
+    int64_t p = 16;
+    while (p < D) p *= 2;
+    return p;
+}
+
+// ---- workspace carving (all offsets 256-byte aligned)
+size_t align256(size_t n);
+
+// Per-chunk scratch of the score path: widened Q rows, rowmax keys, scores.
+size_t score_scratch_bytes(const AttnGeom &g, int64_t rows_i, int64_t kv_len);
+
+// Launchers (return hipError_t of the first failing launch).
+hipError_t launch_widen_q(const Tensor &q, const AttnGeom &g, int64_t i0, int64_t i1, double *q64,
+                          hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
+hipError_t launch_fill_i64(int64_t *p, int64_t n, int64_t v, hipStream_t s);
+
+// Scores of query rows [i0,i1) (all b,hq) against keys [kv_lo,kv_hi); writes
+// scores[bh][i-i0][j-kv_lo] when `scores` is non-null and folds the visible
+// scores into rowmax_keys[bh*key_rows + (i - key_row0)] by atomic max.
+hipError_t launch_scores(const Tensor &k, const AttnGeom &g, const double *q64, int64_t i0, int64_t i1,
+                         int64_t kv_lo, int64_t kv_hi, float *scores, uint32_t *rowmax_keys, int64_t key_rows,
+                         int64_t key_row0, hipStream_t s);
+
+hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t B_Hq, int64_t rows, int64_t out_rows,
+                              int64_t out_row0, hipStream_t s);
+
+// scores -> weights in place, against rowmax f32 at rowmax[bh*rm_rows + i - rm_row0].
+hipError_t launch_weights(const AttnGeom &g, float *scores, const float *rowmax, int64_t rm_rows, int64_t rm_row0,
+                          int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, hipStream_t s);
+
+// Exact deposit of weights x V into num/den digit planes (atomics, int64):
+// num [14][plane_rows][D] at row (bh*rows_per_bh + i - row0), den [9][plane_rows].
+hipError_t launch_deposit(const Tensor &v, const AttnGeom &g, const float *weights, int64_t i0, int64_t i1,
+                          int64_t kv_lo, int64_t kv_hi, int64_t *num, int64_t *den, int64_t plane_rows,
+                          int64_t rows_per_bh, int64_t row0, hipStream_t s);
+
+hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hipStream_t s);
+hipError_t launch_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int n_digits,
+                                 hipStream_t s);
+hipError_t launch_rowmax_combine(float *acc, const float *part, int64_t n, hipStream_t s);
+
+// out[b][hq][i][d] for rows i0..i1 from planes num [14][plane_rows][D], den [9][plane_rows].
+hipError_t launch_finalize(const int64_t *num, const int64_t *den, int64_t plane_rows, int64_t rows_per_bh,
+                           int64_t row0, int64_t B_Hq, int64_t Hq, int64_t i0, int64_t i1, int64_t D,
+                           const OutView &o, hipStream_t s);
+
+// ---- cross-entropy
+hipError_t launch_ce_rowmax(const void *x, int dtype, int64_t N, int64_t ld, int64_t v_lo, int64_t v_hi,
+                            float *rowmax, hipStream_t s);
+hipError_t launch_ce_denom(const void *x, int dtype, int64_t N, int64_t ld, const float *rowmax, int64_t v_lo,
+                           int64_t v_hi, int64_t *den, int add_into, hipStream_t s);
+hipError_t launch_ce_finalize(const int64_t *den, const void *x, int dtype, int64_t N, int64_t ld,
+                              const int64_t *targets, const float *rowmax, float *loss, double *denom,
+                              hipStream_t s);
+hipError_t launch_ce_forward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
+                             float *loss, float *rowmax, double *denom, hipStream_t s);
+hipError_t launch_ce_reduce(const float *loss, int64_t N, int reduction, float *out, int64_t *scratch,
+                            hipStream_t s);
+hipError_t launch_ce_backward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
+                              const float *rowmax, const double *denom, const float *grad_loss, int reduction,
+                              float *grad, int64_t grad_ld, hipStream_t s);
+
+}  // namespace det

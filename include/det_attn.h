@@ -1,0 +1,196 @@
+/*
+ * det_attn.h -- C ABI of the MI355X (gfx950) library for shard-invariant exact
+ * softmax attention and deterministic cross-entropy.
+ *
+ * The operation follows the det-attn page, section "Method": a global row max
+ *     rowmax_i = max_j s_ij,   s_ij = scale * Q_i . K_j,
+ * then exact long-accumulator sums
+ *     NUM_id = sum_j w_ij V_jd,   DEN_i = sum_j w_ij,   w_ij = exp(s_ij - rowmax_i),
+ * where KV shards compose by an elementwise max (rowmax) and an int64 add of
+ * digit arrays (NUM/DEN), and "finalize" turns digits into the f32 output
+ * (same page, "API" table: det_attn, rowmax, accumulate, finalize,
+ * det_attn_sharded).  The det-cross-entropy page, section "Method", applies
+ * the same two reductions over a vocabulary axis (API table: forward, rowmax,
+ * denom_digits, finalize).
+ *
+ * Rounding points (the pages leave them open; every result below is a fixed
+ * function of the inputs, bit for bit):
+ *   s    = RN32(RN64(scale * dot)), dot = fp64 fma chain over d = 0..D-1 from +0
+ *   max  = IEEE totalOrder max (-0 < +0); a row with no visible key: -inf
+ *   w    = RN32(exp_det(RN64(s - m))), exp_det = Cody-Waite reduction with
+ *          n = rint(t/ln2), then the degree-13 Taylor polynomial in Horner
+ *          form, times 2^n; exactly 0 for t < -104
+ *   sums = exact (every w*V product is exact in binary64 and no sum rounds)
+ *   out  = RN32(RN64(NUM) / RN64(DEN))    (a row with no visible key: NaN)
+ *
+ * Digit arrays ("Kulisch long accumulators"): X = sum_k d_k 2^(32k + E_lo),
+ * int64 digits in radix 2^32, digit-major planes.
+ *   NUM  : 14 digits, E_lo = -298, layout [14][B][Hq][Sq][D]
+ *   DEN  :  9 digits, E_lo = -149, layout [9][B][Hq][Sq]
+ *   CE den:  9 digits, E_lo = -149, layout [9][N]
+ * Every array the library writes is canonical: digits 0..K-2 in [0, 2^32), the
+ * top digit signed.  Inputs to combine/finalize may be any sum of up to 2^30
+ * canonical arrays (for example an elementwise int64 add done by the caller).
+ *
+ * Conventions for every entry point:
+ *   - Returns DET_OK (0) or a negative DET_E_* code; det_last_error() gives a
+ *     thread-local message.  Argument checks run on the host before any HIP
+ *     call, so they are testable without a GPU.
+ *   - Pointers marked (device) are device memory; the caller owns every buffer.
+ *     Nothing is allocated by the library except where a workspace size query
+ *     says so; the caller passes that workspace (device, 256-byte aligned).
+ *   - `stream` is a hipStream_t (NULL = default stream); all work is enqueued
+ *     on it asynchronously, in a fixed launch configuration, so repeated calls
+ *     give identical bits.
+ *   - Q, K, V share one dtype (DET_F32 or DET_BF16); D <= 256; Hq % Hkv == 0;
+ *     query head h reads KV head h / (Hq/Hkv).  Causal means key j is visible
+ *     to query i iff j <= i (absolute indices) and requires Sq == Skv.
+ *   - Inputs must be finite.  Debug checks are not performed.
+ */
+#ifndef DET_ATTN_H
+#define DET_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { DET_F32 = 0, DET_BF16 = 1 };
+
+enum {
+    DET_OK = 0,
+    DET_E_NULL = -1,      /* a required pointer is NULL */
+    DET_E_SHAPE = -2,     /* sizes disagree, D outside [1,256], Hq % Hkv != 0, bad range, causal with Sq != Skv */
+    DET_E_DTYPE = -3,     /* dtype not DET_F32/DET_BF16, or operands differ */
+    DET_E_STRIDE = -4,    /* negative stride or an unsupported layout */
+    DET_E_WORKSPACE = -5, /* workspace missing, too small, or misaligned */
+    DET_E_HIP = -6,       /* a HIP runtime call or launch failed */
+    DET_E_VALUE = -7      /* other invalid argument (reduction code, split list) */
+};
+
+enum { DET_NUM_DIGITS = 14, DET_NUM_ELO = -298, DET_DEN_DIGITS = 9, DET_DEN_ELO = -149 };
+
+/* An attention operand [B, H, S, D]: element (b,h,s,d) at
+ * data + (b*sB + h*sH + s*sS + d) elements (device memory, D stride 1).
+ * The interleaved NHD layout of a fused QKV projection is expressed with
+ * strides (sB, sH, sS) = (S*row, D, row). */
+typedef struct {
+    const void *data;
+    int32_t dtype;
+    int64_t B, H, S, D;
+    int64_t sB, sH, sS;
+} det_tensor;
+
+/* f32 output [B, Hq, Sq, D] with D stride 1 (device memory). */
+typedef struct {
+    float *data;
+    int64_t sB, sH, sS;
+} det_out;
+
+/* Digit format of NUM (which = 0) or DEN / CE den (which = 1). */
+int det_digit_format(int32_t which, int32_t *n_digits, int32_t *lsb_exp2);
+
+const char *det_last_error(void);
+
+/* ---------------------------------------------------------------- attention */
+
+/* det-attn page, "API": det_attn(Q, K, V, causal, scale) -- the whole path
+ * (global rowmax, exact NUM/DEN over all keys, finalize) in one call.
+ * Workspace: det_attn_workspace_size() bytes, or more; a larger workspace
+ * lets the library process more query rows per launch (never changes bits). */
+size_t det_attn_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal);
+int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
+             const det_out *o, void *workspace, size_t ws_bytes, void *stream);
+
+/* det-attn page, "API": rowmax(Q, K, ..., kv_lo, kv_hi) -- per-query max
+ * score over keys [kv_lo, kv_hi) (combine shards by max).
+ * rowmax: (device) f32 [B][Hq][Sq].  Workspace: det_attn_rowmax_workspace_size(). */
+size_t det_attn_rowmax_workspace_size(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi);
+int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi, int32_t causal,
+                    double scale, float *rowmax, void *workspace, size_t ws_bytes, void *stream);
+
+/* det-attn page, "API": accumulate(Q, K, V, rowmax, ...) -- exact NUM/DEN
+ * digits of keys [kv_lo, kv_hi) weighted against `rowmax` (which must be
+ * >= every visible score, normally the composed global max).
+ * num: (device) int64 [14][B][Hq][Sq][D]; den: (device) int64 [9][B][Hq][Sq].
+ * add_into = 0 overwrites them; 1 adds this shard to what they hold.  The
+ * result is canonical either way. */
+size_t det_attn_accumulate_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
+                                          int64_t kv_lo, int64_t kv_hi);
+int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tensor *v, const float *rowmax,
+                        int64_t kv_lo, int64_t kv_hi, int32_t causal, double scale, int64_t *num, int64_t *den,
+                        int32_t add_into, void *workspace, size_t ws_bytes, void *stream);
+
+/* Shard composition (det-attn page, "Method": max and int64 add).
+ * det_rowmax_combine: acc[i] = totalOrder max(acc[i], part[i]), n values (device).
+ * det_digits_combine: acc = canonical(acc + part) for n_values values of
+ * n_digits digits each, planes [n_digits][n_values] (device). */
+int det_rowmax_combine(float *acc, const float *part, int64_t n, void *stream);
+int det_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int32_t n_digits, void *stream);
+
+/* det-attn page, "API": finalize(NUM, DEN, shape) -- out = RN32(RN64(NUM)/RN64(DEN)).
+ * num [14][B][Hq][Sq][D], den [9][B][Hq][Sq] (device). */
+int det_attn_finalize(const int64_t *num, const int64_t *den, int64_t B, int64_t Hq, int64_t Sq, int64_t D,
+                      const det_out *o, void *stream);
+
+/* det-attn page, "API": det_attn_sharded(Q, K, V, kv_splits, ...) -- the
+ * KV-shard composition: rowmax per shard, combined by max; digits per shard
+ * against the global max, combined by int64 add in `order` (NULL = 0,1,..);
+ * finalize.  Bit-identical to det_attn for every split and order.
+ * kv_splits: (host) n_splits shard lengths summing to Skv; order: (host)
+ * permutation of 0..n_splits-1 or NULL. */
+size_t det_attn_sharded_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
+                                       const int64_t *kv_splits, int32_t n_splits, int32_t causal);
+int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor *v, const int64_t *kv_splits,
+                     int32_t n_splits, const int32_t *order, int32_t causal, double scale, const det_out *o,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------ cross-entropy */
+/* det-cross-entropy page.  logits: (device) [N][V] of dtype DET_F32 or
+ * DET_BF16, row i at logits + i*ld elements; targets: (device) int64 [N] in
+ * [0, V).  Reduction codes: 0 none, 1 mean, 2 sum. */
+
+/* "API": rowmax(logits, v_lo, v_hi) -- per-token max over [v_lo, v_hi). rowmax: (device) f32 [N]. */
+int det_ce_rowmax(const void *logits, int32_t dtype, int64_t N, int64_t ld, int64_t v_lo, int64_t v_hi,
+                  float *rowmax, void *stream);
+
+/* "API": denom_digits(logits, global_rowmax, v_lo, v_hi) -- exact
+ * den_i = sum_v RN32(exp_det(x_iv - m_i)) over [v_lo, v_hi).
+ * den: (device) int64 [9][N]; add_into as for det_attn_accumulate. */
+int det_ce_denom_digits(const void *logits, int32_t dtype, int64_t N, int64_t ld, const float *rowmax,
+                        int64_t v_lo, int64_t v_hi, int64_t *den, int32_t add_into, void *stream);
+
+/* "API": finalize(den_digits, logits, targets, global_rowmax) -> (loss, denom):
+ * denom_i = RN64(den_i); loss_i = RN32(RN64(RN64(m_i + log_det(denom_i)) - x_{i,t_i})),
+ * log_det = 2*atanh((f-1)/(f+1)) series on f in (sqrt2/2, sqrt2] plus e*ln2.
+ * loss: (device) f32 [N]; denom: (device) f64 [N]. */
+int det_ce_finalize(const int64_t *den, const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld,
+                    const int64_t *targets, const float *rowmax, float *loss, double *denom, void *stream);
+
+/* "API": forward(logits, targets) -> (loss [N], rowmax [N], denom [N]) over the
+ * whole vocabulary.  Workspace: det_ce_forward_workspace_size() bytes. */
+size_t det_ce_forward_workspace_size(int64_t N);
+int det_ce_forward(const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
+                   float *loss, float *rowmax, double *denom, void *workspace, size_t ws_bytes, void *stream);
+
+/* Loss reduction ("reduction is mean, sum, or none"): none copies loss to out[N];
+ * sum = RN32(RN64(S)), mean = RN32(RN64(RN64(S)/N)), S = exact sum of the f32
+ * losses; out[0].  Workspace: det_ce_reduce_workspace_size() bytes. */
+size_t det_ce_reduce_workspace_size(int64_t N);
+int det_ce_reduce(const float *loss, int64_t N, int32_t reduction, float *out, void *workspace, size_t ws_bytes,
+                  void *stream);
+
+/* Gradient "softmax(x_i) - onehot(t_i)" scaled by the upstream gradient:
+ * grad_iv = RN32(RN64(RN64(RN64(w_iv / denom_i) - [v == t_i]) * c_i)),
+ * c_i = grad_loss[i] (none), grad_loss[0] (sum), RN64(grad_loss[0]/N) (mean).
+ * grad_loss: (device) f32 [N] or [1]; grad: (device) f32, row i at grad + i*grad_ld. */
+int det_ce_backward(const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
+                    const float *rowmax, const double *denom, const float *grad_loss, int32_t reduction,
+                    float *grad, int64_t grad_ld, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,282 @@
+"""GPU parity of the attention path against the CPU oracle (bit-exact), plus
+the shard-invariance properties of the det-attn page ("Correctness": every KV
+split and block permutation, and repeated runs, are torch.equal to the fused
+result).  Inputs come from the seeded generators in workloads.py."""
+import itertools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from bitwise_deterministic_exact_pass1_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    from bitwise_deterministic_exact_pass1_amd import attention
+    return attention
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def u32(x):
+    """Bit pattern of an f32 array/tensor (NaN-safe equality)."""
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+def assert_bits_equal(a, b, what=""):
+    ua, ub = u32(a), u32(b)
+    if not np.array_equal(ua, ub):
+        bad = np.argwhere(ua != ub)
+        raise AssertionError(f"{what}: {len(bad)} of {ua.size} differ; first at {bad[0].tolist()}")
+
+
+def gpu(*ts):
+    return [t.cuda() for t in ts]
+
+
+# ---------------------------------------------------------------- tiny MHA f32 (S=128, D=64)
+
+def test_tiny_fused_and_primitives_bit_exact(A, oracle):
+    wl = W.attn_workload("tiny_mha_f32")
+    q, k, v, scale = wl["q"], wl["k"], wl["v"], wl["scale"]
+    say("tiny: oracle")
+    ref, m, num, den = oracle.det_attn(q, k, v, False, scale, return_parts=True)
+    Q, K, V = gpu(q, k, v)
+    say("tiny: det_attn")
+    out = A.det_attn(Q, K, V, False, scale)
+    assert_bits_equal(out, ref, "det_attn")
+    say("tiny: rowmax")
+    gm = A.rowmax(Q, K, 0, 128, False, scale)
+    assert_bits_equal(gm, m, "rowmax")
+    say("tiny: accumulate")
+    gn, gd = A.accumulate(Q, K, V, gm, 0, 128, False, scale)
+    assert np.array_equal(gn.cpu().numpy(), num) and np.array_equal(gd.cpu().numpy(), den)
+    assert_bits_equal(A.finalize(gn, gd), ref, "finalize")
+
+
+def test_tiny_all_24_shard_orders(A):
+    wl = W.attn_workload("tiny_mha_f32")
+    Q, K, V = gpu(wl["q"], wl["k"], wl["v"])
+    ref = A.det_attn(Q, K, V, False, wl["scale"])
+    for order in itertools.permutations(range(4)):
+        out = A.det_attn_sharded(Q, K, V, [32] * 4, False, wl["scale"], order=order)
+        assert torch.equal(out, ref), order
+    for order in list(itertools.permutations(range(4)))[::6]:
+        out = A.det_attn_composed(Q, K, V, [32] * 4, False, wl["scale"], order=order)
+        assert torch.equal(out, ref), order
+
+
+def test_tiny_physical_block_permutations(A):
+    """Non-causal: permuting whole 32-key blocks of K and V together."""
+    wl = W.attn_workload("tiny_mha_f32")
+    Q, K, V = gpu(wl["q"], wl["k"], wl["v"])
+    ref = A.det_attn(Q, K, V, False, wl["scale"])
+    for perm in itertools.permutations(range(4)):
+        idx = torch.cat([torch.arange(32 * p, 32 * p + 32) for p in perm]).cuda()
+        out = A.det_attn(Q, K[:, :, idx], V[:, :, idx], False, wl["scale"])
+        assert torch.equal(out, ref), perm
+
+
+# ---------------------------------------------------------------- causal GQA bf16 (B=2, Hq=8, Hkv=2, S=1024, D=128)
+
+@pytest.fixture(scope="module")
+def gqa(A):
+    wl = W.attn_workload("gqa_causal_bf16")
+    Q, K, V = gpu(wl["q"], wl["k"], wl["v"])
+    say("gqa: det_attn")
+    out = A.det_attn(Q, K, V, True, wl["scale"])
+    torch.cuda.synchronize()
+    return wl, Q, K, V, out
+
+
+def test_gqa_causal_fused_bit_exact(gqa, oracle):
+    wl, Q, K, V, out = gqa
+    say("gqa: oracle (full)")
+    ref = oracle.det_attn(wl["q"], wl["k"], wl["v"], True, wl["scale"])
+    assert_bits_equal(out, ref, "det_attn gqa")
+
+
+def test_gqa_causal_rowmax_and_digits_bit_exact(A, gqa, oracle):
+    wl, Q, K, V, out = gqa
+    gm = A.rowmax(Q, K, 0, 1024, True, wl["scale"])
+    gn, gd = A.accumulate(Q, K, V, gm, 0, 1024, True, wl["scale"])
+    rng = np.random.default_rng(20)
+    rows = np.stack([rng.integers(0, 2, 48), rng.integers(0, 8, 48), rng.integers(0, 1024, 48)], 1)
+    rows = np.concatenate([rows, [[0, 0, 0], [1, 7, 1023], [0, 3, 1], [1, 4, 511]]]).astype(np.int64)
+    say("gqa: oracle rows")
+    m = oracle.attn_rowmax(wl["q"], wl["k"], 0, 1024, True, wl["scale"], rows=rows)
+    num, den = oracle.attn_accumulate(wl["q"], wl["k"], wl["v"], m, 0, 1024, True, wl["scale"], rows=rows)
+    b, h, i = rows.T
+    assert_bits_equal(gm.cpu().numpy()[b, h, i], m, "rowmax")
+    gnc, gdc = gn.cpu().numpy(), gd.cpu().numpy()
+    assert np.array_equal(gnc[:, b, h, i, :], num)
+    assert np.array_equal(gdc[:, b, h, i], den)
+    assert gnc[:13].min() >= 0 and gnc[:13].max() < 2 ** 32  # canonical
+
+
+@pytest.mark.parametrize("splits", [[256] * 4, [64] * 16])
+def test_gqa_causal_shard_invariance(A, gqa, splits):
+    wl, Q, K, V, ref = gqa
+    n = len(splits)
+    for s in range(8):
+        order = W.shard_order(1000 + 2 + 100 * n + s, n)
+        out = A.det_attn_sharded(Q, K, V, splits, True, wl["scale"], order=order)
+        assert torch.equal(out, ref), (splits[0], order)
+    out = A.det_attn_composed(Q, K, V, splits, True, wl["scale"], order=W.shard_order(77 + n, n))
+    assert torch.equal(out, ref)
+
+
+def test_gqa_repeat_runs_identical(A, gqa):
+    wl, Q, K, V, ref = gqa
+    for _ in range(3):
+        assert torch.equal(A.det_attn(Q, K, V, True, wl["scale"]), ref)
+
+
+# ---------------------------------------------------------------- context-parallel share (sampled rows)
+
+def _sample_rows(B, H, S, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.stack([rng.integers(0, B, n), rng.integers(0, H, n), rng.integers(0, S, n)], 1)
+    edge = [[0, 0, 0], [B - 1, H - 1, S - 1], [0, H - 1, 1], [B - 1, 0, S // 2]]
+    return np.concatenate([rows, edge]).astype(np.int64)
+
+
+@pytest.mark.parametrize("name,nrows", [("cp_share_bf16", 20), ("cp_share_d256_bf16", 40)])
+def test_cp_share_sampled_rows_bit_exact(A, oracle, name, nrows):
+    wl = W.attn_workload(name)
+    Q, K, V = gpu(wl["q"], wl["k"], wl["v"])
+    say(f"{name}: det_attn")
+    out = A.det_attn(Q, K, V, True, wl["scale"])
+    B, Hq, S, D = wl["q"].shape
+    rows = _sample_rows(B, Hq, S, nrows, 31)
+    say(f"{name}: oracle rows")
+    ref = oracle.det_attn(wl["q"], wl["k"], wl["v"], True, wl["scale"], rows=rows)
+    b, h, i = rows.T
+    assert_bits_equal(out.cpu().numpy()[b, h, i], ref, name)
+    if name == "cp_share_bf16":
+        say(f"{name}: 8 x 1024 shards")
+        sh = A.det_attn_sharded(Q, K, V, [1024] * 8, True, wl["scale"], order=W.shard_order(1003, 8))
+        assert torch.equal(sh, out)
+
+
+# ---------------------------------------------------------------- long non-causal strided NHD
+
+@pytest.fixture(scope="module")
+def long_nhd(A):
+    say("long: building the interleaved QKV buffer")
+    buf = W.long_nhd_buffer()
+    return buf, buf.cuda()
+
+
+def test_long_nhd_sampled_rows_bit_exact(A, oracle, long_nhd):
+    buf, dbuf = long_nhd
+    q, k, v = W.long_nhd_views(buf)
+    Q, K, V = W.long_nhd_views(dbuf)
+    scale = W.default_scale(128)
+    say("long: det_attn (full)")
+    out = A.det_attn(Q, K, V, False, scale)
+    torch.cuda.synchronize()
+    rows = _sample_rows(1, 56, W.LONG_S, 12, 55)
+    say("long: oracle rows")
+    ref = oracle.det_attn(q, k, v, False, scale, rows=rows)
+    b, h, i = rows.T
+    assert_bits_equal(out.cpu().numpy()[b, h, i], ref, "long nhd")
+
+
+def test_long_nhd_591_blocks_on_row_subset(A, long_nhd):
+    """KV split into 590 blocks of 64 plus 50, composed in two seeded orders, on
+    the first 64 query positions (all 56 heads): equal to the fused result."""
+    buf, dbuf = long_nhd
+    Q, K, V = W.long_nhd_views(dbuf)
+    Qs = Q[:, :, :64]
+    scale = W.default_scale(128)
+    ref = A.det_attn(Qs, K, V, False, scale)
+    splits = [64] * 590 + [50]
+    for seed in (1005, 2005):
+        say(f"long: 591 shards order seed {seed}")
+        out = A.det_attn_sharded(Qs, K, V, splits, False, scale, order=W.shard_order(seed, 591))
+        assert torch.equal(out, ref)
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("D", [1, 3, 17, 100, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims_and_ragged_tails(A, oracle, D, causal):
+    q, k, v = W.attn_inputs(300 + D, 1, 4, 2, 45, 45, D, torch.bfloat16)
+    scale = W.default_scale(D)
+    ref = oracle.det_attn(q, k, v, causal, scale)
+    out = A.det_attn(*gpu(q, k, v), causal, scale)
+    assert_bits_equal(out, ref, f"D={D}")
+
+
+def test_noncausal_rectangular_and_one_key(A, oracle):
+    q, k, v = W.attn_inputs(401, 2, 3, 1, 70, 300, 32, torch.float32)
+    ref = oracle.det_attn(q, k, v, False, 0.2)
+    assert_bits_equal(A.det_attn(*gpu(q, k, v), False, 0.2), ref, "rect")
+    q, k, v = W.attn_inputs(402, 1, 2, 2, 5, 1, 16, torch.float32)
+    out = A.det_attn(*gpu(q, k, v), False, 0.25)
+    assert torch.equal(out.cpu(), v.expand(1, 2, 5, 16))
+
+
+def test_wide_score_spread_tiny_and_subnormal_weights(A, oracle):
+    """Large scores make most weights tiny or subnormal in f32, exercising every
+    window flush; tiny V entries put products far below the others."""
+    q, k, v = W.attn_inputs(403, 1, 2, 1, 64, 64, 16, torch.float32, std=6.0)
+    v[0, 0, ::7, ::3] *= 1e-30
+    v[0, 0, 5, :] = 0.0
+    for scale in (1.0, 3.0):
+        ref = oracle.det_attn(q, k, v, False, scale)
+        out = A.det_attn(*gpu(q, k, v), False, scale)
+        assert_bits_equal(out, ref, f"spread scale={scale}")
+        assert np.isfinite(ref).all()
+
+
+def test_special_values(A, oracle):
+    q, k, v = W.attn_inputs(404, 1, 1, 1, 9, 9, 8, torch.float32)
+    kz = torch.zeros_like(k)
+    assert_bits_equal(A.det_attn(*gpu(q, kz, v), False, 0.5), oracle.det_attn(q, kz, v, False, 0.5), "K=0")
+    vz = torch.zeros_like(v)
+    out = A.det_attn(*gpu(q, k, vz), False, 0.5)
+    assert torch.equal(out.cpu(), torch.zeros_like(out.cpu())) and not torch.signbit(out).any()
+
+
+def test_empty_key_range_gives_neg_inf_and_nan(A):
+    q, k, v = gpu(*W.attn_inputs(405, 1, 2, 2, 8, 8, 16, torch.float32))
+    m = A.rowmax(q, k, 4, 4)
+    assert torch.isneginf(m).all()
+    num, den = A.accumulate(q, k, v, m, 4, 4)
+    assert not num.any() and not den.any()
+    assert torch.isnan(A.finalize(num, den)).all()
+
+
+def test_accumulate_add_into_equals_combine(A):
+    q, k, v = gpu(*W.attn_inputs(406, 1, 2, 1, 50, 50, 24, torch.bfloat16))
+    m = A.rowmax(q, k, 0, 50, True)
+    n1, d1 = A.accumulate(q, k, v, m, 0, 20, True)
+    n2, d2 = A.accumulate(q, k, v, m, 20, 50, True)
+    nall, dall = A.accumulate(q, k, v, m, 0, 50, True)
+    na, da = n1.clone(), d1.clone()
+    A.accumulate(q, k, v, m, 20, 50, True, num=na, den=da)
+    assert torch.equal(na, nall) and torch.equal(da, dall)
+    A.combine_digits(n1, n2)
+    A.combine_digits(d1, d2)
+    assert torch.equal(n1, nall) and torch.equal(d1, dall)
+    # a caller-side int64 add (non-canonical) finalizes to the same output
+    n3, d3 = A.accumulate(q, k, v, m, 0, 20, True)
+    assert torch.equal(A.finalize(n3 + n2, d3 + d2), A.finalize(nall, dall))
+
+
+def test_empty_query_rows(A):
+    q, k, v = gpu(*W.attn_inputs(407, 1, 2, 2, 0, 16, 16, torch.float32))
+    out = A.det_attn(q, k, v, False)
+    assert out.shape == (1, 2, 0, 16)
