@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact two-pass attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one fused det_attn call (global rowmax, exact NUM/DEN digits over
+every key, finalize) on the causal GQA workload B=2, Hq=8, Hkv=2, S=1024,
+D=128, bf16 N(0,1) inputs resident in HBM.  The metric is unmasked (i,j)
+pairs per second.  Alongside it the script reports, for the kernel that takes
+the most time, its algorithmic fp64 work per launch divided by its average
+launch time (HIP events recorded by the library on the launch stream), and
+the CPU oracle's throughput on a bounded row sample of the same workload.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "exact-attention (i,j) pairs/sec + % of FP64-vector roofline, bit-exact"
+FP64_PEAK_TFLOPS = 78.6   # MI355X vector fp64 (256 CUs x 2.4 GHz x 128 flops/clk)
+HBM_PEAK_GBS = 8000.0
+
+
+def visible_pairs(B, Hq, Sq, Skv, causal):
+    if causal:
+        return B * Hq * Sq * (Sq + 1) // 2
+    return B * Hq * Sq * Skv
+
+
+def kernel_work(name, pairs, rows, D):
+    """(amount, unit, bound) of algorithmic work of one launch of `name`:
+    fp64 flops for the compute kernels, HBM bytes for the data-movement ones."""
+    if name == "scores":      # one fp64 fma chain of length D per pair
+        return 2.0 * D * pairs, "flop", "alu"
+    if name == "weights":     # exp_det: 2 mul + 15 fma
+        return 32.0 * pairs, "flop", "alu"
+    if name == "deposit":     # D exact product-accumulates per pair, one fma each
+        return 2.0 * D * pairs, "flop", "alu"
+    if name == "finalize":    # read 14+9/D digits, write one f32 per output
+        return rows * D * (112 + 72.0 / D + 4), "byte", "hbm"
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gqa_causal_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the sharded / cross-entropy side measurements")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    from bitwise_deterministic_exact_pass1_amd import _lib, attention, workloads as W
+
+    wl = W.attn_workload(args.workload)
+    q, k, v, causal, scale = wl["q"], wl["k"], wl["v"], wl["causal"], wl["scale"]
+    B, Hq, Sq, D = q.shape
+    Skv = k.shape[2]
+    Q, K, V = q.cuda(), k.cuda(), v.cuda()
+    pairs = visible_pairs(B, Hq, Sq, Skv, causal)
+    rows = B * Hq * Sq
+
+    for _ in range(args.warmup):
+        out = attention.det_attn(Q, K, V, causal, scale)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, events on torch's current stream (the library's stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        out = attention.det_attn(Q, K, V, causal, scale)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    value = pairs * args.steps / (ms_total / 1e3)
+
+    # the same K steps again with per-kernel events recorded by the library
+    _lib.profile_begin()
+    for _ in range(args.steps):
+        out2 = attention.det_attn(Q, K, V, causal, scale)
+    torch.cuda.synchronize()
+    prof = _lib.profile_end()
+    assert torch.equal(out, out2), "repeat runs differ"
+    kernels = {n: {"launches": c, "avg_ms": t / c, "share": 0.0} for n, (c, t) in prof.items()}
+    total_k = sum(t for c, t in prof.values())
+    for n in kernels:
+        kernels[n]["share"] = prof[n][1] / total_k
+    dominant = max(prof, key=lambda n: prof[n][1])
+    per_step_launches = prof[dominant][0] / args.steps
+    work = kernel_work(dominant, pairs / per_step_launches, rows / per_step_launches, D)
+    avg_s = prof[dominant][1] / prof[dominant][0] / 1e3
+    if work is not None:
+        amount, unit, bound = work
+        if unit == "flop":
+            achieved, peak, runit = amount / avg_s / 1e12, FP64_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            achieved, peak, runit = amount / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+        roofline = {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": runit,
+                    "frac": achieved / peak, "traffic": None}
+    else:
+        roofline = {"bound": "alu", "kernel": dominant, "achieved": None, "peak": FP64_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": None, "traffic": None}
+    path_flops = pairs * (6 * D + 32)
+    path = {"flop_per_pair": 6 * D + 32, "achieved_tflops": path_flops / (ms_step / 1e3) / 1e12,
+            "frac_of_fp64_peak": path_flops / (ms_step / 1e3) / 1e12 / FP64_PEAK_TFLOPS}
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64+int64", "data": "synthetic",
+        "config": {"workload": f"fused det_attn, {wl['desc']}", "B": B, "Hq": Hq, "Hkv": k.shape[1],
+                   "S": Sq, "D": D, "causal": causal, "pairs_per_step": pairs},
+        "roofline": roofline, "path_roofline": path, "kernels": kernels,
+    }
+
+    if not args.no_extra:
+        result["extra"] = extra_measurements(attention, W, Q, K, V, causal, scale, out, pairs)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, causal, scale, out, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
+    """Side numbers: the sharded composition (16 x 64 keys) on the same inputs,
+    and cross-entropy forward/backward on N=4096, V=128256 bf16."""
+    from bitwise_deterministic_exact_pass1_amd import cross_entropy as CE
+    res = {}
+    splits = [64] * (K.shape[2] // 64)
+    order = W.shard_order(1002, len(splits))
+    out = attention.det_attn_sharded(Q, K, V, splits, causal, scale, order=order)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = attention.det_attn_sharded(Q, K, V, splits, causal, scale, order=order)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3
+    res["sharded_16x64"] = {"ms": ms, "pairs_per_s": pairs / (ms / 1e3), "equal_to_fused": bool(torch.equal(out, ref))}
+
+    x, t = W.ce_inputs()
+    X, T = x.cuda(), t.cuda()
+    del x
+    loss, m, den = CE.forward(X, T)
+    g = torch.ones(1, device=X.device)
+    grad = CE.backward(X, T, m, den, g, "mean")
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    e[0].record()
+    loss, m, den = CE.forward(X, T)
+    e[1].record()
+    grad = CE.backward(X, T, m, den, g, "mean")
+    e[2].record()
+    torch.cuda.synchronize()
+    N, Vv = X.shape
+    fwd_ms, bwd_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+    res["cross_entropy"] = {"workload": "N=4096 V=128256 bf16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
+                            "forward_token_vocab_per_s": N * Vv / (fwd_ms / 1e3),
+                            "backward_hbm_GBps": N * Vv * 6 / (bwd_ms / 1e3) / 1e9}
+    return res
+
+
+def cpu_baseline(q, k, v, causal, scale, gpu_out, seconds):
+    """The CPU oracle (untuned) on a row sample of the same workload, sized to
+    about `seconds` of work; also checks the GPU output on those rows."""
+    from oracle import oracle
+    B, Hq, Sq, D = q.shape
+    rng = np.random.default_rng(12345)
+    allrows = oracle.all_rows(B, Hq, Sq)
+
+    def run(n):
+        sel = allrows[np.sort(rng.choice(len(allrows), n, replace=False))]
+        t0 = time.perf_counter()
+        ref = oracle.det_attn(q, k, v, causal, scale, rows=sel)
+        dt = time.perf_counter() - t0
+        npairs = int(np.sum(sel[:, 2] + 1)) if causal else n * k.shape[2]
+        return sel, ref, dt, npairs
+
+    sel, ref, dt, npairs = run(64)
+    n = int(min(len(allrows), max(64, 64 * seconds / max(dt, 1e-3))))
+    if n > 64:
+        sel, ref, dt, npairs = run(n)
+    got = gpu_out.cpu().numpy()[sel[:, 0], sel[:, 1], sel[:, 2]]
+    exact = bool(np.array_equal(got.view(np.uint32), np.ascontiguousarray(ref).view(np.uint32)))
+    return {"value": npairs / dt, "unit": "pairs/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{len(sel)} random query rows of the same workload ({npairs} pairs), {dt:.1f} s",
+            "gpu_bit_exact_on_sample": exact}
+
+
+if __name__ == "__main__":
+    main()

@@ -42,6 +42,8 @@ _T, _O = C.POINTER(Tensor), C.POINTER(Out)
 SIGNATURES = {
     "det_digit_format": (C.c_int, [_I32, C.POINTER(_I32), C.POINTER(_I32)]),
     "det_last_error": (C.c_char_p, []),
+    "det_profile_begin": (C.c_int, []),
+    "det_profile_end": (_SZ, [C.c_char_p, _SZ]),
     "det_attn_workspace_size": (_SZ, [_T, _T, _T, _I32]),
     "det_attn": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _SZ, _P]),
     "det_attn_rowmax_workspace_size": (_SZ, [_T, _T, _I64, _I64]),
@@ -80,6 +82,25 @@ def lib() -> C.CDLL:
             fn.argtypes = args
         _lib = h
     return _lib
+
+
+def profile_begin() -> None:
+    check(lib().det_profile_begin())
+
+
+def profile_end() -> dict:
+    """{kernel: (launches, total_ms)} for the launches since profile_begin()."""
+    buf = C.create_string_buffer(1 << 16)
+    lib().det_profile_end(buf, len(buf))
+    return _parse(buf.value.decode())
+
+
+def _parse(text: str) -> dict:
+    out = {}
+    for line in text.splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out
 
 
 def check(rc: int) -> None:

@@ -20,10 +20,98 @@
 
 #include <algorithm>
 #include <climits>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
 
 namespace det {
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------- per-kernel timing
+
+namespace {
+struct ProfRec {
+    const char *name;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+ProfScope::ProfScope(const char *name, hipStream_t s) : slot(-1), stream(s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    ProfRec r{name, pooled_event(), pooled_event()};
+    if (!r.a || !r.b) return;
+    hipEventRecord(r.a, s);
+    slot = (int)g_prof.size();
+    g_prof.push_back(r);
+}
+
+ProfScope::~ProfScope() {
+    if (slot < 0) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEventRecord(g_prof[slot].b, stream);
+}
+
+void prof_enable(bool on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto &r : g_prof) {
+        g_event_pool.push_back(r.a);
+        g_event_pool.push_back(r.b);
+    }
+    g_prof.clear();
+    g_prof_on = on;
+}
+
+size_t prof_report(char *buf, size_t len) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    std::vector<std::string> names;
+    std::vector<double> tot;
+    std::vector<long> cnt;
+    for (auto &r : g_prof) {
+        hipEventSynchronize(r.b);
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) continue;
+        size_t k = 0;
+        while (k < names.size() && names[k] != r.name) ++k;
+        if (k == names.size()) {
+            names.push_back(r.name);
+            tot.push_back(0.0);
+            cnt.push_back(0);
+        }
+        tot[k] += ms;
+        cnt[k] += 1;
+    }
+    std::string out;
+    for (size_t k = 0; k < names.size(); ++k) {
+        char line[160];
+        snprintf(line, sizeof line, "%s %ld %.6f\n", names[k].c_str(), cnt[k], tot[k]);
+        out += line;
+    }
+    if (buf && len) {
+        const size_t n = std::min(len - 1, out.size());
+        memcpy(buf, out.data(), n);
+        buf[n] = 0;
+    }
+    return out.size() + 1;
+}
 
 size_t score_scratch_bytes(const AttnGeom &g, int64_t rows_i, int64_t kv_len) {
     const int64_t bh = g.B * g.Hq;
@@ -49,11 +137,13 @@ static dim3 grid_for(int64_t n, int block = 256) {
 }
 
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) {
+    ProfScope prof_("fill", s);
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_fill_u32, grid_for(n), dim3(256), 0, s, p, n, v);
     return hipGetLastError();
 }
 hipError_t launch_fill_i64(int64_t *p, int64_t n, int64_t v, hipStream_t s) {
+    ProfScope prof_("fill", s);
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_fill_i64, grid_for(n), dim3(256), 0, s, p, n, v);
     return hipGetLastError();
@@ -79,6 +169,7 @@ __global__ void k_widen_q(const T *__restrict__ q, int64_t sB, int64_t sH, int64
 
 hipError_t launch_widen_q(const Tensor &q, const AttnGeom &g, int64_t i0, int64_t i1, double *q64,
                           hipStream_t s) {
+    ProfScope prof_("widen_q", s);
     const int64_t ni = i1 - i0, ni_pad = padded_rows(ni), total = g.B * g.Hq * ni_pad * g.Dp;
     if (total <= 0) return hipSuccess;
     if (q.dtype == 0)
@@ -190,6 +281,7 @@ static void launch_scores_t(dim3 grid, const Tensor &k, const AttnGeom &g, const
 hipError_t launch_scores(const Tensor &k, const AttnGeom &g, const double *q64, int64_t i0, int64_t i1,
                          int64_t kv_lo, int64_t kv_hi, float *scores, uint32_t *rowmax_keys, int64_t key_rows,
                          int64_t key_row0, hipStream_t s) {
+    ProfScope prof_("scores", s);
     const int64_t ni = i1 - i0;
     if (ni <= 0 || kv_hi <= kv_lo) return hipSuccess;
     const int64_t ktiles = (kv_hi - kv_lo + kKeyTile - 1) / kKeyTile;
@@ -213,6 +305,7 @@ __global__ void k_keys_to_f32(const uint32_t *__restrict__ keys, float *__restri
 
 hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t BHq, int64_t rows, int64_t out_rows,
                               int64_t out_row0, hipStream_t s) {
+    ProfScope prof_("keys_to_f32", s);
     if (BHq * rows <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_keys_to_f32, grid_for(BHq * rows), dim3(256), 0, s, keys, out, BHq, rows, out_rows,
                        out_row0);
@@ -237,6 +330,7 @@ __global__ void k_weights(float *__restrict__ sc, const float *__restrict__ rowm
 
 hipError_t launch_weights(const AttnGeom &g, float *scores, const float *rowmax, int64_t rm_rows, int64_t rm_row0,
                           int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, hipStream_t s) {
+    ProfScope prof_("weights", s);
     const int64_t ni = i1 - i0, W = kv_hi - kv_lo, total = g.B * g.Hq * ni * W;
     if (total <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_weights, grid_for(total), dim3(256), 0, s, scores, rowmax, rm_rows, rm_row0, i0, ni,
@@ -299,6 +393,7 @@ __global__ __launch_bounds__(256) void k_deposit(const TV *__restrict__ vp, int6
 hipError_t launch_deposit(const Tensor &v, const AttnGeom &g, const float *weights, int64_t i0, int64_t i1,
                           int64_t kv_lo, int64_t kv_hi, int64_t *num, int64_t *den, int64_t plane_rows,
                           int64_t rows_per_bh, int64_t row0, hipStream_t s) {
+    ProfScope prof_("deposit", s);
     const int64_t ni = i1 - i0;
     if (ni <= 0 || kv_hi <= kv_lo) return hipSuccess;
     const int64_t nDB = (g.D + 63) / 64;
@@ -343,6 +438,7 @@ __global__ void k_digits_combine(int64_t *__restrict__ acc, const int64_t *__res
 }
 
 hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hipStream_t s) {
+    ProfScope prof_("normalize", s);
     if (n_values <= 0) return hipSuccess;
     if (n_digits == kNumDigits)
         hipLaunchKernelGGL(k_normalize<kNumDigits>, grid_for(n_values), dim3(256), 0, s, digits, n_values);
@@ -353,6 +449,7 @@ hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hip
 
 hipError_t launch_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int n_digits,
                                  hipStream_t s) {
+    ProfScope prof_("digits_combine", s);
     if (n_values <= 0) return hipSuccess;
     if (n_digits == kNumDigits)
         hipLaunchKernelGGL(k_digits_combine<kNumDigits>, grid_for(n_values), dim3(256), 0, s, acc, part,
@@ -369,6 +466,7 @@ __global__ void k_rowmax_combine(float *__restrict__ acc, const float *__restric
 }
 
 hipError_t launch_rowmax_combine(float *acc, const float *part, int64_t n, hipStream_t s) {
+    ProfScope prof_("rowmax_combine", s);
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_rowmax_combine, grid_for(n), dim3(256), 0, s, acc, part, n);
     return hipGetLastError();
@@ -403,6 +501,7 @@ __global__ void k_finalize(const int64_t *__restrict__ num, const int64_t *__res
 hipError_t launch_finalize(const int64_t *num, const int64_t *den, int64_t plane_rows, int64_t rows_per_bh,
                            int64_t row0, int64_t B_Hq, int64_t Hq, int64_t i0, int64_t i1, int64_t D,
                            const OutView &o, hipStream_t s) {
+    ProfScope prof_("finalize", s);
     const int64_t ni = i1 - i0, total = B_Hq * ni * D;
     if (total <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_finalize, grid_for(total), dim3(256), 0, s, num, den, plane_rows, rows_per_bh, row0, Hq,

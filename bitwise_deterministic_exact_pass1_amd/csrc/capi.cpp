@@ -178,6 +178,17 @@ extern "C" {
 
 const char *det_last_error(void) { return g_err.c_str(); }
 
+int det_profile_begin(void) {
+    prof_enable(true);
+    return ok();
+}
+
+size_t det_profile_end(char *buf, size_t len) {
+    const size_t n = prof_report(buf, len);
+    prof_enable(false);
+    return n;
+}
+
 int det_digit_format(int32_t which, int32_t *n_digits, int32_t *lsb_exp2) {
     if (!n_digits || !lsb_exp2) return fail(DET_E_NULL, "output pointer is NULL");
     if (which == 0) {

@@ -181,6 +181,7 @@ __global__ void k_ce_backward(const void *x, int64_t N, int64_t V, int64_t ld, c
 
 hipError_t launch_ce_rowmax(const void *x, int dtype, int64_t N, int64_t ld, int64_t v_lo, int64_t v_hi,
                             float *rowmax, hipStream_t s) {
+    ProfScope prof_("ce_rowmax", s);
     if (N <= 0) return hipSuccess;
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_rowmax<float>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, ld, v_lo, v_hi, rowmax);
@@ -192,6 +193,7 @@ hipError_t launch_ce_rowmax(const void *x, int dtype, int64_t N, int64_t ld, int
 
 hipError_t launch_ce_denom(const void *x, int dtype, int64_t N, int64_t ld, const float *rowmax, int64_t v_lo,
                            int64_t v_hi, int64_t *den, int add_into, hipStream_t s) {
+    ProfScope prof_("ce_denom", s);
     if (N <= 0) return hipSuccess;
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_denom<float>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, N, ld, rowmax, v_lo,
@@ -205,6 +207,7 @@ hipError_t launch_ce_denom(const void *x, int dtype, int64_t N, int64_t ld, cons
 hipError_t launch_ce_finalize(const int64_t *den, const void *x, int dtype, int64_t N, int64_t ld,
                               const int64_t *targets, const float *rowmax, float *loss, double *denom,
                               hipStream_t s) {
+    ProfScope prof_("ce_finalize", s);
     if (N <= 0) return hipSuccess;
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_finalize<float>, ce_grid(N), dim3(256), 0, s, den, x, N, ld, targets, rowmax, loss,
@@ -217,6 +220,7 @@ hipError_t launch_ce_finalize(const int64_t *den, const void *x, int dtype, int6
 
 hipError_t launch_ce_forward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
                              float *loss, float *rowmax, double *denom, hipStream_t s) {
+    ProfScope prof_("ce_forward", s);
     if (N <= 0) return hipSuccess;
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_forward<float>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, V, ld, targets, loss,
@@ -228,6 +232,7 @@ hipError_t launch_ce_forward(const void *x, int dtype, int64_t N, int64_t V, int
 }
 
 hipError_t launch_ce_reduce(const float *loss, int64_t N, int reduction, float *out, int64_t *, hipStream_t s) {
+    ProfScope prof_("ce_reduce", s);
     hipLaunchKernelGGL(k_ce_reduce, dim3(1), dim3(1024), 0, s, loss, N, reduction, out);
     return hipGetLastError();
 }
@@ -235,6 +240,7 @@ hipError_t launch_ce_reduce(const float *loss, int64_t N, int reduction, float *
 hipError_t launch_ce_backward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
                               const float *rowmax, const double *denom, const float *grad_loss, int reduction,
                               float *grad, int64_t grad_ld, hipStream_t s) {
+    ProfScope prof_("ce_backward", s);
     if (N * V <= 0) return hipSuccess;
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_backward<float>, ce_grid(N * V), dim3(256), 0, s, x, N, V, ld, targets, rowmax,

@@ -42,6 +42,18 @@ inline int64_t padded_dim(int64_t D) {
     return p;
 }
 
+// ---- per-kernel timing (tracing aid): when enabled, every launch below is
+// bracketed by two HIP events on its own stream.
+struct ProfScope {
+    ProfScope(const char *name, hipStream_t s);
+    ~ProfScope();
+    int slot;
+    hipStream_t stream;
+};
+void prof_enable(bool on);
+// "name count total_ms" lines for the launches since prof_enable(true).
+size_t prof_report(char *buf, size_t len);
+
 // ---- workspace carving (all offsets 256-byte aligned)
 size_t align256(size_t n);
 

@@ -94,6 +94,17 @@ int det_digit_format(int32_t which, int32_t *n_digits, int32_t *lsb_exp2);
 
 const char *det_last_error(void);
 
+/* Per-kernel timing (a tracing aid; results never depend on it).
+ * det_profile_begin(): from now on every kernel the library launches is
+ * bracketed by two HIP events recorded on the stream it runs on.
+ * det_profile_end(buf, len): waits for those events, writes one line
+ * "kernel_name launches total_ms" per kernel into buf (NUL-terminated,
+ * truncated to len), switches recording off and returns the full length
+ * needed (including the NUL).  Not meant to be called while other threads
+ * launch work through the library. */
+int det_profile_begin(void);
+size_t det_profile_end(char *buf, size_t len);
+
 /* ---------------------------------------------------------------- attention */
 
 /* det-attn page, "API": det_attn(Q, K, V, causal, scale) -- the whole path

@@ -17,7 +17,19 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 int32_t ora_version(void) { return 1; }
+
+int32_t ora_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* Exact integer accumulator                                                 */

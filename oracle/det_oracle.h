@@ -55,6 +55,9 @@ enum { ORA_NUM_DIGITS = 14, ORA_NUM_ELO = -298, ORA_DEN_DIGITS = 9, ORA_DEN_ELO 
 
 int32_t ora_version(void);
 
+/* Threads the row loops run on (OpenMP). */
+int32_t ora_threads(void);
+
 /* The two elementary routines, exported so tests can pin them. */
 double ora_exp_det(double t);
 double ora_log_det(double x);

@@ -52,6 +52,7 @@ def lib():
         T = C.POINTER(_Tensor)
         sig = {
             "ora_version": (I32, []),
+            "ora_threads": (I32, []),
             "ora_exp_det": (D, [D]),
             "ora_log_det": (D, [D]),
             "ora_score": (C.c_float, [P, P, I64, D]),
@@ -110,6 +111,11 @@ def all_rows(B: int, H: int, S: int) -> np.ndarray:
 def default_scale(D: int) -> float:
     """RN64(1 / RN64(sqrt(D))), computed on the host."""
     return 1.0 / float(np.sqrt(np.float64(D)))
+
+
+def threads() -> int:
+    """Number of host threads the oracle's row loops use."""
+    return int(lib().ora_threads())
 
 
 def exp_det(t: float) -> float:
