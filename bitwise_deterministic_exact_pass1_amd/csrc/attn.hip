@@ -7,14 +7,8 @@
 // Q, so every FMA takes its q operand from an SGPR pair and its k operand from
 // a VGPR.  Scores are stored for pass 2 (the chain is not recomputed).
 //
-// Pass 2 ("exact Kulisch long-accumulator sums"): w = RN32(exp_det(s - m)),
-// then NUM_id = sum_j w_ij V_jd and DEN_i = sum_j w_ij exactly.  The deposit
-// keeps, per (i,d), one binary64 window whose terms all lie on a common grid
-// 2^g with |window| < 2^(g+53), so every addition in it is exact whatever the
-// order; when a term would break either bound the window is flushed into the
-// int64 radix-2^32 digit planes with integer atomics (integer addition is
-// associative, so the digit planes hold the same value whatever the flush
-// order).  The digits are then carried to canonical form.
+// Pass 2 lives in pv.hip; this file also holds the digit compose, carry and
+// finalize kernels.
 #include "dev_math.hpp"
 #include "kernels.hpp"
 
@@ -309,105 +303,6 @@ hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t BHq, int
     if (BHq * rows <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_keys_to_f32, grid_for(BHq * rows), dim3(256), 0, s, keys, out, BHq, rows, out_rows,
                        out_row0);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- pass 2: weights
-
-__global__ void k_weights(float *__restrict__ sc, const float *__restrict__ rowmax, int64_t rm_rows,
-                          int64_t rm_row0, int64_t i0, int64_t ni, int64_t kv_lo, int64_t W, int causal,
-                          int64_t total) {
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t jj = t % W;
-        const int64_t r = t / W;
-        const int64_t ii = r % ni, bh = r / ni;
-        const int64_t i = i0 + ii, j = kv_lo + jj;
-        float w = 0.0f;
-        if (!causal || j <= i) w = weight(sc[t], rowmax[bh * rm_rows + (i - rm_row0)]);
-        sc[t] = w;
-    }
-}
-
-hipError_t launch_weights(const AttnGeom &g, float *scores, const float *rowmax, int64_t rm_rows, int64_t rm_row0,
-                          int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, hipStream_t s) {
-    ProfScope prof_("weights", s);
-    const int64_t ni = i1 - i0, W = kv_hi - kv_lo, total = g.B * g.Hq * ni * W;
-    if (total <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_weights, grid_for(total), dim3(256), 0, s, scores, rowmax, rm_rows, rm_row0, i0, ni,
-                       kv_lo, W, g.causal, total);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- pass 2: exact deposit
-
-template <typename TV>
-__global__ __launch_bounds__(256) void k_deposit(const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
-                                                 int64_t Hq, int64_t group, int64_t D, int causal,
-                                                 const float *__restrict__ wts, int64_t i0, int64_t ni,
-                                                 int64_t kv_lo, int64_t kv_hi, int64_t nDB, int64_t total_waves,
-                                                 int64_t *__restrict__ num, int64_t *__restrict__ den,
-                                                 int64_t plane_rows, int64_t rows_per_bh, int64_t row0) {
-    const int lane = threadIdx.x & 63;
-    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wid >= total_waves) return;
-    const int64_t rl = wid / nDB, db = wid % nDB;
-    const int64_t bh = rl / ni, ii = rl % ni;
-    const int64_t i = i0 + ii;
-    const int64_t b = bh / Hq, hq = bh % Hq, hk = hq / group;
-    const int64_t d = db * 64 + lane;
-    const bool dv = d < D;
-    const int64_t W = kv_hi - kv_lo;
-    const int64_t jend = causal ? std::min<int64_t>(kv_hi, i + 1) : kv_hi;
-    const float *wrow = wts + rl * W;
-    const TV *vcol = vp + b * vsB + hk * vsH + (dv ? d : 0);
-    const int64_t prow = bh * rows_per_bh + (i - row0);  // row in the digit planes
-    constexpr int VMB = elem<TV>::mant_bits;
-    const bool den_lane = (db == 0) && (lane == 0);
-
-    Window nw, dw;
-    nw.init();
-    dw.init();
-    int64_t *ndig = num + prow * D + d;
-    int64_t *ddig = den + prow;
-    const int64_t nplane = plane_rows * D;
-
-    for (int64_t j = kv_lo; j < jend; ++j) {
-        const float w = wrow[j - kv_lo];
-        if (w == 0.0f) continue;
-        const int ew = f32_exp(w);
-        const int lw = max(ew, -126) - 23;  // w is a multiple of 2^lw
-        if (dv) {
-            const float vf = elem<TV>::to_f32(vcol[j * vsS]);
-            if (vf != 0.0f) {
-                const int ev = f32_exp(vf);
-                const double p = (double)w * (double)vf;  // exact: at most 48 significant bits
-                nw.add<kNumDigits>(p, lw + max(ev, -126) - VMB, ew + ev + 2, kNumGcap, kNumElo, ndig, nplane);
-            }
-        }
-        if (den_lane) dw.add<kDenDigits>((double)w, lw, ew + 1, kDenGcap, kDenElo, ddig, plane_rows);
-    }
-    if (dv) nw.flush<kNumDigits>(kNumElo, ndig, nplane);
-    if (den_lane) dw.flush<kDenDigits>(kDenElo, ddig, plane_rows);
-}
-
-hipError_t launch_deposit(const Tensor &v, const AttnGeom &g, const float *weights, int64_t i0, int64_t i1,
-                          int64_t kv_lo, int64_t kv_hi, int64_t *num, int64_t *den, int64_t plane_rows,
-                          int64_t rows_per_bh, int64_t row0, hipStream_t s) {
-    ProfScope prof_("deposit", s);
-    const int64_t ni = i1 - i0;
-    if (ni <= 0 || kv_hi <= kv_lo) return hipSuccess;
-    const int64_t nDB = (g.D + 63) / 64;
-    const int64_t waves = g.B * g.Hq * ni * nDB;
-    const unsigned blocks = (unsigned)((waves + 3) / 4);
-    const int64_t group = g.Hq / g.Hkv;
-    if (v.dtype == 0)
-        hipLaunchKernelGGL(k_deposit<float>, dim3(blocks), dim3(256), 0, s, (const float *)v.data, v.sB, v.sH,
-                           v.sS, g.Hq, group, g.D, g.causal, weights, i0, ni, kv_lo, kv_hi, nDB, waves, num, den,
-                           plane_rows, rows_per_bh, row0);
-    else
-        hipLaunchKernelGGL(k_deposit<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t *)v.data, v.sB, v.sH,
-                           v.sS, g.Hq, group, g.D, g.causal, weights, i0, ni, kv_lo, kv_hi, nDB, waves, num, den,
-                           plane_rows, rows_per_bh, row0);
     return hipGetLastError();
 }
 

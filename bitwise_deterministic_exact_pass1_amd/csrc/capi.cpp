@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -129,19 +130,42 @@ size_t bytes_rowmax(const AttnGeom &g, int64_t ni) {
 
 size_t bytes_accumulate(const AttnGeom &g, int64_t ni, int64_t W) {
     const int64_t bh = g.B * g.Hq;
-    return align256((size_t)bh * padded_rows(ni) * g.Dp * 8) + align256((size_t)bh * ni * W * 4);
+    return vprep_bytes(g, W) + align256((size_t)bh * padded_rows(ni) * g.Dp * 8) +
+           align256((size_t)bh * ni * W * 4) + pv_fallback_bytes(g, 0);
 }
 
 size_t bytes_fused(const AttnGeom &g, int64_t ni) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
-    return score_scratch_bytes(g, ni, g.Skv) + align256((size_t)rows * 4) +
-           align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8);
+    return vprep_bytes(g, g.Skv) + score_scratch_bytes(g, ni, g.Skv) + align256((size_t)rows * 4) +
+           pv_fallback_bytes(g, ni);
 }
 
 size_t bytes_sharded(const AttnGeom &g, int64_t ni, int64_t maxlen) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
-    return score_scratch_bytes(g, ni, maxlen) + 2 * align256((size_t)rows * 4) +
+    return vprep_bytes(g, maxlen) + score_scratch_bytes(g, ni, maxlen) + 2 * align256((size_t)rows * 4) +
+           pv_fallback_bytes(g, 0) +
            2 * (align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8));
+}
+
+VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
+    const int64_t bhk = g.B * g.Hkv, Dp32 = (g.D + 31) / 32 * 32, nG = Dp32 / 32;
+    const int64_t nKB = std::max<int64_t>((kv_len + 31) / 32, 1);
+    VPrep v;
+    v.colmax = c.take<int>(bhk * Dp32);
+    v.colmin = c.take<int>(bhk * Dp32);
+    v.colgrid = c.take<int>(bhk * Dp32);
+    v.grpB = c.take<int>(bhk * nG);
+    v.slices = c.take<char>(bhk * nG * nKB * 6 * 1024);
+    v.Dp32 = Dp32;
+    v.nKB = nKB;
+    return v;
+}
+
+// DET_FORCE_FALLBACK=1 sends every tile through the generic exact path (tests
+// use it to check that both paths give the same bits).
+int force_fallback() {
+    const char *e = getenv("DET_FORCE_FALLBACK");
+    return e && e[0] == '1';
 }
 
 // Largest chunk (a multiple of kRowTile, or all Sq rows) whose need fits `budget`;
@@ -264,15 +288,21 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
         HIP_TRY(launch_fill_i64(den, kDenDigits * rows, 0, s), "fill den");
     }
     const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need);
+    Carver c0{(char *)workspace};
+    VPrep vp = carve_vprep(c0, g, W);
+    if (W > 0) HIP_TRY(launch_vprep(tv, g, kv_lo, kv_hi, vp, s), "prepare v");
+    const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq && W > 0; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        Carver c{(char *)workspace};
+        Carver c = c0;
         double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
         float *sc = c.take<float>(bh * ni * W);
+        int *flags = c.take<int>(bh * ((ni + 31) / 32));
         HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
         HIP_TRY(launch_scores(tk, g, q64, i0, i1, kv_lo, kv_hi, sc, nullptr, 0, 0, s), "scores");
-        HIP_TRY(launch_weights(g, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, s), "weights");
-        HIP_TRY(launch_deposit(tv, g, sc, i0, i1, kv_lo, kv_hi, num, den, rows, g.Sq, 0, s), "deposit");
+        HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr, nullptr,
+                          num, den, rows, g.Sq, 0, ff, s),
+                "deposit");
     }
     HIP_TRY(launch_normalize(num, rows * g.D, kNumDigits, s), "normalize num");
     HIP_TRY(launch_normalize(den, rows, kDenDigits, s), "normalize den");
@@ -334,24 +364,28 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     const Tensor tq = to_t(q), tk = to_t(k), tv = to_t(v);
     const OutView ov{o->data, o->sB, o->sH, o->sS};
     const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
+    Carver c0{(char *)workspace};
+    VPrep vp = carve_vprep(c0, g, g.Skv);
+    HIP_TRY(launch_vprep(tv, g, 0, g.Skv, vp, s), "prepare v");
+    const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
-        Carver c{(char *)workspace};
+        const int64_t tiles = (ni + 31) / 32;
+        Carver c = c0;
         double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
         uint32_t *keys = c.take<uint32_t>(rows);
         float *sc = c.take<float>(rows * g.Skv);
         float *rm = c.take<float>(rows);
-        int64_t *num = c.take<int64_t>(kNumDigits * rows * g.D);
-        int64_t *den = c.take<int64_t>(kDenDigits * rows);
+        int *flags = c.take<int>(bh * tiles);
+        int64_t *fnum = c.take<int64_t>(kNumDigits * bh * tiles * 32 * g.D);
+        int64_t *fden = c.take<int64_t>(kDenDigits * bh * tiles * 32);
         HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
         HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
         HIP_TRY(launch_scores(tk, g, q64, i0, i1, 0, g.Skv, sc, keys, ni, i0, s), "scores");
         HIP_TRY(launch_keys_to_f32(keys, rm, bh, ni, ni, 0, s), "rowmax");
-        HIP_TRY(launch_weights(g, sc, rm, ni, i0, i0, i1, 0, g.Skv, s), "weights");
-        HIP_TRY(launch_fill_i64(num, kNumDigits * rows * g.D, 0, s), "fill num");
-        HIP_TRY(launch_fill_i64(den, kDenDigits * rows, 0, s), "fill den");
-        HIP_TRY(launch_deposit(tv, g, sc, i0, i1, 0, g.Skv, num, den, rows, ni, i0, s), "deposit");
-        HIP_TRY(launch_finalize(num, den, rows, ni, i0, bh, g.Hq, i0, i1, g.D, ov, s), "finalize");
+        HIP_TRY(launch_pv(tv, g, vp, sc, rm, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr, nullptr, 0, 0,
+                          0, ff, s),
+                "deposit");
     }
     return ok();
 }
@@ -413,14 +447,17 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         run += kv_splits[a];
     }
     const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
+    const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
         Carver c{(char *)workspace};
+        VPrep vp = carve_vprep(c, g, ml);
         double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
         uint32_t *keys = c.take<uint32_t>(rows);
         float *sc = c.take<float>(rows * ml);
         float *rm_acc = c.take<float>(rows);
         float *rm_part = c.take<float>(rows);
+        int *flags = c.take<int>(bh * ((ni + 31) / 32));
         int64_t *num_acc = c.take<int64_t>(kNumDigits * rows * g.D);
         int64_t *den_acc = c.take<int64_t>(kDenDigits * rows);
         int64_t *num_part = c.take<int64_t>(kNumDigits * rows * g.D);
@@ -445,9 +482,11 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
             HIP_TRY(launch_fill_i64(num_part, kNumDigits * rows * g.D, 0, s), "fill num");
             HIP_TRY(launch_fill_i64(den_part, kDenDigits * rows, 0, s), "fill den");
             if (h > l) {
+                HIP_TRY(launch_vprep(tv, g, l, h, vp, s), "prepare v");
                 HIP_TRY(launch_scores(tk, g, q64, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
-                HIP_TRY(launch_weights(g, sc, rm_acc, ni, i0, i0, i1, l, h, s), "weights");
-                HIP_TRY(launch_deposit(tv, g, sc, i0, i1, l, h, num_part, den_part, rows, ni, i0, s), "deposit");
+                HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
+                                  num_part, den_part, rows, ni, i0, ff, s),
+                        "deposit");
             }
             HIP_TRY(launch_normalize(num_part, rows * g.D, kNumDigits, s), "normalize");
             HIP_TRY(launch_normalize(den_part, rows, kDenDigits, s), "normalize");

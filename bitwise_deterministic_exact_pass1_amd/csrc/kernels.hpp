@@ -76,15 +76,28 @@ hipError_t launch_scores(const Tensor &k, const AttnGeom &g, const double *q64, 
 hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t B_Hq, int64_t rows, int64_t out_rows,
                               int64_t out_row0, hipStream_t s);
 
-// scores -> weights in place, against rowmax f32 at rowmax[bh*rm_rows + i - rm_row0].
-hipError_t launch_weights(const AttnGeom &g, float *scores, const float *rowmax, int64_t rm_rows, int64_t rm_row0,
-                          int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, hipStream_t s);
+// ---- pass 2 on the matrix cores (pv.hip)
 
-// Exact deposit of weights x V into num/den digit planes (atomics, int64):
-// num [14][plane_rows][D] at row (bh*rows_per_bh + i - row0), den [9][plane_rows].
-hipError_t launch_deposit(const Tensor &v, const AttnGeom &g, const float *weights, int64_t i0, int64_t i1,
-                          int64_t kv_lo, int64_t kv_hi, int64_t *num, int64_t *den, int64_t plane_rows,
-                          int64_t rows_per_bh, int64_t row0, hipStream_t s);
+// Prepared V of one key range: per-column grid exponents and balanced int8
+// digits in MFMA lane order.
+struct VPrep {
+    int *colmax, *colmin, *colgrid, *grpB;
+    void *slices;
+    int64_t Dp32, nKB;
+};
+size_t vprep_bytes(const AttnGeom &g, int64_t kv_len);
+size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i);
+hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
+                        hipStream_t s);
+// Exact NUM/DEN of query rows [i0,i1) against keys [kv_lo,kv_hi) from stored
+// scores (chunk layout [bh][i-i0][j-kv_lo]) and rowmax[bh*rm_rows + i - rm_row0].
+// With `o` the tile is finalized into o; otherwise its exact values are added
+// into the digit planes num/den (rows bh*rows_per_bh + i - row0).  Tiles the
+// matrix-core path cannot represent exactly are redone by the generic path.
+hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
+                     int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
+                     int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
+                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s);
 
 hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hipStream_t s);
 hipError_t launch_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int n_digits,

@@ -1,0 +1,542 @@
+// pv.hip -- pass 2 of the exact softmax on the matrix cores.
+//
+// The det-attn page ("Method") needs NUM_id = sum_j w_ij V_jd and
+// DEN_i = sum_j w_ij exactly.  Both factors are turned into integers on fixed
+// grids, split into balanced base-256 digits, and multiplied on the int8
+// matrix cores, which add exactly in int32:
+//
+//   W_ij = w_ij * 2^46                 (an integer when w >= 2^-23: 24-bit mantissa)
+//   Vi_jd = V_jd * 2^-g_d              (g_d = the smallest lsb exponent in column d)
+//   W = sum_a c_a 256^a,  Vi = sum_b e_b 256^b,  c, e in [-128, 127]
+//   NUM_id = 2^(g_d - 46) * sum_s 256^s * C_s[i][d],  C_s = sum_{a+b=s} sum_j c_a(W_ij) e_b(Vi_jd)
+//
+// v_mfma_i32_32x32x32_i8 computes one C_s update for a 32-row x 32-dim tile
+// over 32 keys.  Every int32 partial sum is exact (|c e| <= 2^14 per key and
+// pair; the classes are carried into each other every 8192 keys), so the
+// result is the exact NUM whatever the order of keys, blocks or instructions.
+// DEN is the exact int64 sum of the W_ij.  A tile whose weights do not fit the
+// grid (w < 2^-23, or w > 1 from a rowmax below the scores) or whose V columns
+// need more than six digits is flagged and redone by the generic exact kernel
+// (k_tile_fallback): results never depend on which path ran.
+#include "dev_math.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace det {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kAw = 6;                  // digits of W
+constexpr int kSw = 8 * kAw - 2;        // W = w * 2^46, |W| <= 2^46 fits six balanced digits
+constexpr int kBmax = 6;                // at most six digits of a V column (48-bit integers)
+constexpr int kNC = kAw + kBmax - 1;    // shift classes s = a + b
+constexpr int kKB = 32;                 // keys per block (the MFMA K)
+constexpr int kCarryEvery = 256;        // blocks (8192 keys) between carry passes
+constexpr int kBvFallback = 99;         // "needs the generic path" marker
+
+// ---------------------------------------------------------------- V preparation
+
+// Column statistics over keys [kv_lo, kv_hi): max exponent and min lsb exponent
+// of the nonzero entries, folded into per-column int32 by atomic max/min.
+template <typename TV>
+__global__ __launch_bounds__(256) void k_vstats(const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
+                                                int64_t Hkv, int64_t D, int64_t Dp32, int64_t kv_lo, int64_t kv_hi,
+                                                int *__restrict__ colmax, int *__restrict__ colmin) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t bhk = blockIdx.z, b = bhk / Hkv, hk = bhk % Hkv;
+    const int64_t d = (int64_t)blockIdx.y * 64 + lane;
+    const int64_t j0 = kv_lo + (int64_t)blockIdx.x * 512;
+    const int64_t j1 = std::min<int64_t>(kv_hi, j0 + 512);
+    int emax = INT_MIN, lmin = INT_MAX;
+    if (d < D) {
+        const TV *col = vp + b * vsB + hk * vsH + d;
+        for (int64_t j = j0 + wave; j < j1; j += 4) {
+            const float x = elem<TV>::to_f32(col[j * vsS]);
+            if (x != 0.0f) {
+                const int e = f32_exp(x);
+                emax = max(emax, e);
+                lmin = min(lmin, max(e, -126) - elem<TV>::mant_bits);
+            }
+        }
+    }
+    __shared__ int smax[256], smin[256];
+    smax[threadIdx.x] = emax;
+    smin[threadIdx.x] = lmin;
+    __syncthreads();
+    if (wave == 0 && d < Dp32) {
+        for (int w = 1; w < 4; ++w) {
+            emax = max(emax, smax[w * 64 + lane]);
+            lmin = min(lmin, smin[w * 64 + lane]);
+        }
+        if (emax != INT_MIN) atomicMax(&colmax[bhk * Dp32 + d], emax);
+        if (lmin != INT_MAX) atomicMin(&colmin[bhk * Dp32 + d], lmin);
+    }
+}
+
+// Digits of Vi = V * 2^-g_d in MFMA lane order: block (bhk, G, kb, b) holds
+// 64 lanes x 16 bytes, lane l byte p = e_b(Vi[key kv_lo + 32kb + 16(l/32) + p][dim 32G + l%32]).
+// Also writes the per-column grid g_d and the per-group digit count.
+template <typename TV>
+__global__ __launch_bounds__(64) void k_vslice(const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
+                                               int64_t Hkv, int64_t D, int64_t Dp32, int64_t kv_lo, int64_t kv_hi,
+                                               int64_t nKB, const int *__restrict__ colmax,
+                                               const int *__restrict__ colmin, int *__restrict__ colgrid,
+                                               int *__restrict__ grpB, v4i *__restrict__ vsl) {
+    const int lane = threadIdx.x;
+    const int64_t kb = blockIdx.x, G = blockIdx.y, bhk = blockIdx.z;
+    const int64_t b = bhk / Hkv, hk = bhk % Hkv;
+    const int64_t nG = Dp32 / 32;
+    const int64_t d = G * 32 + (lane & 31);
+    const int cmax = colmax[bhk * Dp32 + d], cmin = colmin[bhk * Dp32 + d];
+    const bool nonzero = cmax != INT_MIN;
+    const int g = nonzero ? cmin : 0;
+    // digits needed: |Vi| < 2^(cmax + 1 - g); balanced digits hold |x| <= 2^(8B-2)
+    int need = nonzero ? (cmax + 1 - g + 2 + 7) / 8 : 0;
+    int bg = need;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) bg = max(bg, __shfl_xor(bg, off, 64));
+    bg = max(bg, 1);
+    if (bg > kBmax) bg = kBvFallback;
+    if (kb == 0 && lane < 32) colgrid[bhk * Dp32 + d] = g;
+    if (kb == 0 && lane == 0) grpB[bhk * nG + G] = bg;
+    const TV *col = vp + b * vsB + hk * vsH + (d < D ? d : 0);
+    int64_t vi[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const int64_t j = kv_lo + kb * kKB + 16 * (lane >> 5) + p;
+        double x = 0.0;
+        if (d < D && j < kv_hi && bg != kBvFallback) x = (double)elem<TV>::to_f32(col[j * vsS]);
+        vi[p] = (int64_t)ldexp(x, -g);  // exact: x is a multiple of 2^g and |x/2^g| < 2^48
+    }
+    v4i *out = vsl + ((bhk * nG + G) * nKB + kb) * kBmax * 64;
+#pragma unroll
+    for (int s = 0; s < kBmax; ++s) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t pack = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t x = vi[4 * q + u];
+                const int64_t c = ((x & 255) ^ 128) - 128;  // balanced low digit
+                vi[4 * q + u] = (x - c) >> 8;
+                pack |= ((uint32_t)(c & 255)) << (8 * u);
+            }
+            wv[q] = pack;
+        }
+        out[s * 64 + lane] = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+    }
+}
+
+// ---------------------------------------------------------------- exact int128 helpers
+
+__device__ __forceinline__ int clz128(unsigned __int128 u) {
+    const uint64_t hi = (uint64_t)(u >> 64), lo = (uint64_t)u;
+    return hi ? __clzll((long long)hi) : 64 + __clzll((long long)lo);
+}
+
+// Correctly rounded (ties to even) binary64 of x * 2^e.
+__device__ __forceinline__ double i128_to_f64(__int128 x, int e) {
+    if (x == 0) return 0.0;
+    const bool neg = x < 0;
+    const unsigned __int128 u = neg ? (unsigned __int128)(-x) : (unsigned __int128)x;
+    const int nb = 128 - clz128(u);
+    double r;
+    if (nb <= 53) {
+        r = ldexp((double)(uint64_t)u, e);
+    } else {
+        const int sh = nb - 53;
+        uint64_t mant = (uint64_t)(u >> sh);
+        const unsigned __int128 rem = u & ((((unsigned __int128)1) << sh) - 1);
+        const unsigned __int128 half = ((unsigned __int128)1) << (sh - 1);
+        if (rem > half || (rem == half && (mant & 1))) mant += 1;
+        r = ldexp((double)mant, e + sh);
+    }
+    return neg ? -r : r;
+}
+
+// Add x * 2^pos (pos >= 0, in units of the digit lsb) to K radix-2^32 digits.
+template <int K>
+__device__ __forceinline__ void add_i128_digits(__int128 x, int pos, int64_t *dg, int64_t plane) {
+    if (x == 0) return;
+    const bool neg = x < 0;
+    unsigned __int128 u = neg ? (unsigned __int128)(-x) : (unsigned __int128)x;
+    int k = pos >> 5;
+    const int sh = pos & 31;
+    // u * 2^sh < 2^(128+31): emit limbs of (u << sh) without losing the top bits
+    const uint64_t top = sh ? (uint64_t)(u >> (128 - sh)) : 0;  // bits above 128 after the shift
+    u <<= sh;
+    unsigned long long *d = (unsigned long long *)dg;
+    for (int t = 0; t < 5; ++t, ++k) {
+        int64_t limb = t < 4 ? (int64_t)(uint32_t)(u >> (32 * t)) : (int64_t)top;
+        if (!limb) continue;
+        if (neg) limb = -limb;
+        if (k < K) {
+            atomicAdd(d + (int64_t)k * plane, (unsigned long long)limb);
+        } else {  // fold into the signed top digit (only reached by values near the format's ceiling)
+            atomicAdd(d + (int64_t)(K - 1) * plane, (unsigned long long)(limb << (32 * (k - (K - 1)))));
+        }
+    }
+}
+
+// ---------------------------------------------------------------- the MFMA kernel
+
+struct PvArgs {
+    const float *scores;  // [bh][ni][W] chunk scores
+    const float *rowmax;  // rowmax[bh*rm_rows + i - rm_row0]
+    int64_t rm_rows, rm_row0;
+    int64_t ni, W, i0, kv_lo, kv_hi;
+    int64_t Hq, Hkv, group, D, Dp32, nKB;
+    int causal;
+    const v4i *vsl;
+    const int *colgrid, *grpB;
+    int *flags;  // [bh][ntiles]
+    int64_t ntiles;
+    int force_fallback;
+    // fused output
+    float *o;
+    int64_t osB, osH, osS;
+    // digit output (accumulate): num [14][plane_rows][D], den [9][plane_rows]
+    int64_t *num, *den;
+    int64_t plane_rows, rows_per_bh, row0;
+};
+
+template <int NW, bool FUSED>
+__global__ __launch_bounds__(64 * NW) void k_pv_mfma(PvArgs A) {
+    constexpr int NT = 64 * NW;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t bh = blockIdx.y, tile = blockIdx.x;
+    const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
+    const int64_t it0 = A.i0 + tile * 32;     // first query row of the tile
+    const int64_t i_end = A.i0 + A.ni;         // rows of the chunk
+    const int64_t nG = A.Dp32 / 32;
+    const int64_t jlo = A.kv_lo;
+    const int64_t jhi = A.causal ? std::min<int64_t>(A.kv_hi, it0 + 32) : A.kv_hi;
+    const int64_t nblk = jhi > jlo ? (jhi - jlo + kKB - 1) / kKB : 0;
+
+    __shared__ __attribute__((aligned(16))) uint8_t abuf[2][kAw][64 * 16];
+    __shared__ int64_t den_s[32];
+    __shared__ int bad_s;
+
+    if (tid < 32) den_s[tid] = 0;
+    if (tid == 0) bad_s = A.force_fallback;
+    // any group needing more than kBmax digits sends the whole tile to the generic path
+    int Bv = 1;
+    for (int64_t g = 0; g < nG; ++g) {
+        const int x = A.grpB[bhk * nG + g];
+        if (x > kBmax && tid == 0) bad_s = 1;
+        if (g == wave) Bv = x;
+    }
+    __syncthreads();
+    if (bad_s) {
+        if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
+        return;
+    }
+    const v4i *vblk = A.vsl + ((bhk * nG + wave) * A.nKB) * kBmax * 64;
+
+    v16i C[kNC];
+#pragma unroll
+    for (int s = 0; s < kNC; ++s) C[s] = v16i{0};
+    bool bad = false;
+
+    for (int64_t kb = 0; kb < nblk; ++kb) {
+        const int buf = (int)(kb & 1);
+        const int64_t j0 = jlo + kb * kKB;
+        // weights of 32 rows x 32 keys -> balanced digits of W in LDS
+        for (int p = tid; p < 256; p += NT) {
+            const int r = p >> 3, q = p & 7;
+            const int64_t i = it0 + r;
+            int64_t Wq[4];
+            int64_t wsum = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t j = j0 + 4 * q + u;
+                float w = 0.0f;
+                if (i < i_end && j < jhi && (!A.causal || j <= i)) {
+                    const int64_t row = bh * A.ni + (i - A.i0);
+                    w = weight(A.scores[row * A.W + (j - A.kv_lo)], A.rowmax[bh * A.rm_rows + (i - A.rm_row0)]);
+                }
+                const double ws = ldexp((double)w, kSw);
+                const int64_t Wi = (int64_t)ws;
+                if ((double)Wi != ws || Wi > (1ll << kSw)) bad = true;
+                Wq[u] = Wi;
+                wsum += Wi;
+            }
+            if (wsum) atomicAdd((unsigned long long *)&den_s[r], (unsigned long long)wsum);
+            const int lrow = r + 32 * (q >> 2), boff = (q & 3) * 4;
+#pragma unroll
+            for (int a = 0; a < kAw; ++a) {
+                uint32_t pack = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int64_t c = ((Wq[u] & 255) ^ 128) - 128;
+                    Wq[u] = (Wq[u] - c) >> 8;
+                    pack |= ((uint32_t)(c & 255)) << (8 * u);
+                }
+                *(uint32_t *)&abuf[buf][a][lrow * 16 + boff] = pack;
+            }
+        }
+        __syncthreads();
+        // exact products on the matrix cores
+        v4i Bd[kBmax];
+#pragma unroll
+        for (int s = 0; s < kBmax; ++s)
+            if (s < Bv) Bd[s] = vblk[(kb * kBmax + s) * 64 + lane];
+#pragma unroll
+        for (int a = 0; a < kAw; ++a) {
+            const v4i Aa = *(const v4i *)&abuf[buf][a][lane * 16];
+            const bool nz = (Aa.x | Aa.y | Aa.z | Aa.w) != 0;
+            if (__any(nz)) {
+#pragma unroll
+                for (int s = 0; s < kBmax; ++s)
+                    if (s < Bv) C[a + s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aa, Bd[s], C[a + s], 0, 0, 0);
+            }
+        }
+        if ((kb % kCarryEvery) == kCarryEvery - 1) {
+            // carry each class into the next so every partial sum stays far below 2^31
+#pragma unroll
+            for (int s = 0; s < kNC - 1; ++s) {
+                const v16i c = C[s] >> 8;
+                C[s] -= c << 8;
+                C[s + 1] += c;
+            }
+        }
+    }
+    if (bad) bad_s = 1;  // benign race: every writer stores 1
+    __syncthreads();
+    if (bad_s) {
+        if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
+        return;
+    }
+
+    const int64_t d = wave * 32 + (lane & 31);
+    const int g = A.colgrid[bhk * A.Dp32 + d];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t i = it0 + row;
+        if (i >= i_end || d >= A.D) continue;
+        __int128 num = 0;
+#pragma unroll
+        for (int s = kNC - 1; s >= 0; --s) num = num * 256 + (__int128)C[s][r];
+        const int64_t dsum = den_s[row];
+        if (FUSED) {
+            const double n64 = i128_to_f64(num, g - kSw);
+            const double d64 = i128_to_f64((__int128)dsum, -kSw);
+            A.o[b * A.osB + hq * A.osH + i * A.osS + d] = (float)(n64 / d64);
+        } else {
+            const int64_t prow = bh * A.rows_per_bh + (i - A.row0);
+            add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, A.num + prow * A.D + d, A.plane_rows * A.D);
+            if (wave == 0 && (lane & 31) == 0)
+                add_i128_digits<kDenDigits>((__int128)dsum, -kSw - kDenElo, A.den + prow, A.plane_rows);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- generic exact fallback
+
+// One workgroup per flagged tile: the windowed exact deposit of the general
+// path over all keys of the tile's rows, then (fused) an in-kernel finalize.
+template <typename TV, bool FUSED>
+__global__ __launch_bounds__(256) void k_tile_fallback(PvArgs A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH,
+                                                       int64_t vsS, int64_t *__restrict__ num_ws,
+                                                       int64_t *__restrict__ den_ws) {
+    const int64_t bh = blockIdx.y, tile = blockIdx.x;
+    if (!A.flags[bh * A.ntiles + tile]) return;
+    const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group;
+    const int64_t it0 = A.i0 + tile * 32, i_end = A.i0 + A.ni;
+    const int64_t D = A.D;
+    constexpr int VMB = elem<TV>::mant_bits;
+    // digit target: fused -> 32-row scratch of this tile (zeroed here); digits -> caller planes
+    int64_t *num = FUSED ? num_ws : A.num;
+    int64_t *den = FUSED ? den_ws : A.den;
+    const int64_t nplane_rows = FUSED ? A.ntiles * 32 * (int64_t)gridDim.y : A.plane_rows;
+    auto prow_of = [&](int64_t i) -> int64_t {
+        return FUSED ? (bh * A.ntiles + tile) * 32 + (i - it0) : bh * A.rows_per_bh + (i - A.row0);
+    };
+    if (FUSED) {
+        for (int64_t t = threadIdx.x; t < 32 * D * kNumDigits; t += blockDim.x) {
+            const int64_t k = t / (32 * D), rem = t % (32 * D);
+            num[k * nplane_rows * D + prow_of(it0) * D + rem] = 0;
+        }
+        for (int64_t t = threadIdx.x; t < 32 * kDenDigits; t += blockDim.x)
+            den[(t / 32) * nplane_rows + prow_of(it0) + (t % 32)] = 0;
+        __threadfence();
+        __syncthreads();
+    }
+    for (int64_t t = threadIdx.x; t < 32 * (D + 1); t += blockDim.x) {
+        const int64_t r = t / (D + 1), d = t % (D + 1);  // d == D: the DEN window of row r
+        const int64_t i = it0 + r;
+        if (i >= i_end) continue;
+        const int64_t row = bh * A.ni + (i - A.i0);
+        const float m = A.rowmax[bh * A.rm_rows + (i - A.rm_row0)];
+        const int64_t jend = A.causal ? std::min<int64_t>(A.kv_hi, i + 1) : A.kv_hi;
+        const TV *vcol = vp + b * vsB + hk * vsH + (d < D ? d : 0);
+        const int64_t prow = prow_of(i);
+        Window win;
+        win.init();
+        for (int64_t j = A.kv_lo; j < jend; ++j) {
+            const float w = weight(A.scores[row * A.W + (j - A.kv_lo)], m);
+            if (w == 0.0f) continue;
+            const int ew = f32_exp(w);
+            const int lw = max(ew, -126) - 23;
+            if (d == D) {
+                win.add<kDenDigits>((double)w, lw, ew + 1, kDenGcap, kDenElo, den + prow, nplane_rows);
+            } else {
+                const float vf = elem<TV>::to_f32(vcol[j * vsS]);
+                if (vf == 0.0f) continue;
+                const int ev = f32_exp(vf);
+                win.add<kNumDigits>((double)w * (double)vf, lw + max(ev, -126) - VMB, ew + ev + 2, kNumGcap,
+                                    kNumElo, num + prow * D + d, nplane_rows * D);
+            }
+        }
+        if (d == D) win.flush<kDenDigits>(kDenElo, den + prow, nplane_rows);
+        else win.flush<kNumDigits>(kNumElo, num + prow * D + d, nplane_rows * D);
+    }
+    if (!FUSED) return;
+    __threadfence();
+    __syncthreads();
+    for (int64_t t = threadIdx.x; t < 32 * D; t += blockDim.x) {
+        const int64_t r = t / D, d = t % D, i = it0 + r;
+        if (i >= i_end) continue;
+        const int64_t prow = prow_of(i);
+        int64_t nd[kNumDigits], dd[kDenDigits];
+        unsigned long long *np = (unsigned long long *)num, *dp = (unsigned long long *)den;
+#pragma unroll
+        for (int k = 0; k < kNumDigits; ++k) nd[k] = (int64_t)atomicAdd(np + k * nplane_rows * D + prow * D + d, 0ull);
+#pragma unroll
+        for (int k = 0; k < kDenDigits; ++k) dd[k] = (int64_t)atomicAdd(dp + k * nplane_rows + prow, 0ull);
+        canonicalize<kNumDigits>(nd);
+        canonicalize<kDenDigits>(dd);
+        const double n64 = digits_to_f64<kNumDigits>(nd, kNumElo);
+        const double d64 = digits_to_f64<kDenDigits>(dd, kDenElo);
+        A.o[b * A.osB + hq * A.osH + i * A.osS + d] = (float)(n64 / d64);
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+size_t vprep_bytes(const AttnGeom &g, int64_t kv_len) {
+    const int64_t bhk = g.B * g.Hkv, Dp32 = (g.D + 31) / 32 * 32, nG = Dp32 / 32;
+    const int64_t nKB = (kv_len + kKB - 1) / kKB;
+    return 3 * align256((size_t)bhk * Dp32 * 4) + align256((size_t)bhk * nG * 4) +
+           align256((size_t)bhk * nG * std::max<int64_t>(nKB, 1) * kBmax * 1024);
+}
+
+size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i) {
+    const int64_t tiles = (rows_i + 31) / 32, bh = g.B * g.Hq;
+    return align256((size_t)bh * tiles * 4) +                                   // flags
+           align256((size_t)kNumDigits * bh * tiles * 32 * g.D * 8) +           // fused scratch NUM
+           align256((size_t)kDenDigits * bh * tiles * 32 * 8);                  // fused scratch DEN
+}
+
+hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
+                        hipStream_t s) {
+    ProfScope prof_("vprep", s);
+    const int64_t bhk = g.B * g.Hkv, Dp32 = (g.D + 31) / 32 * 32, nG = Dp32 / 32;
+    const int64_t len = kv_hi - kv_lo, nKB = std::max<int64_t>((len + kKB - 1) / kKB, 1);
+    vp.Dp32 = Dp32;
+    vp.nKB = nKB;
+    hipError_t e;
+    if ((e = launch_fill_u32((uint32_t *)vp.colmax, bhk * Dp32, (uint32_t)INT_MIN, s)) != hipSuccess) return e;
+    if ((e = launch_fill_u32((uint32_t *)vp.colmin, bhk * Dp32, (uint32_t)INT_MAX, s)) != hipSuccess) return e;
+    if (len > 0) {
+        dim3 gs((unsigned)((len + 511) / 512), (unsigned)((Dp32 + 63) / 64), (unsigned)bhk);
+        if (v.dtype == 0)
+            hipLaunchKernelGGL(k_vstats<float>, gs, dim3(256), 0, s, (const float *)v.data, v.sB, v.sH, v.sS, g.Hkv,
+                               g.D, Dp32, kv_lo, kv_hi, vp.colmax, vp.colmin);
+        else
+            hipLaunchKernelGGL(k_vstats<bf16_t>, gs, dim3(256), 0, s, (const bf16_t *)v.data, v.sB, v.sH, v.sS,
+                               g.Hkv, g.D, Dp32, kv_lo, kv_hi, vp.colmax, vp.colmin);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    dim3 gsl((unsigned)nKB, (unsigned)nG, (unsigned)bhk);
+    if (v.dtype == 0)
+        hipLaunchKernelGGL(k_vslice<float>, gsl, dim3(64), 0, s, (const float *)v.data, v.sB, v.sH, v.sS, g.Hkv, g.D,
+                           Dp32, kv_lo, kv_hi, nKB, vp.colmax, vp.colmin, vp.colgrid, vp.grpB, (v4i *)vp.slices);
+    else
+        hipLaunchKernelGGL(k_vslice<bf16_t>, gsl, dim3(64), 0, s, (const bf16_t *)v.data, v.sB, v.sH, v.sS, g.Hkv,
+                           g.D, Dp32, kv_lo, kv_hi, nKB, vp.colmax, vp.colmin, vp.colgrid, vp.grpB,
+                           (v4i *)vp.slices);
+    return hipGetLastError();
+}
+
+template <bool FUSED>
+static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &vp, PvArgs &a, dim3 grid,
+                              int64_t *num_ws, int64_t *den_ws, hipStream_t s) {
+    {
+        ProfScope prof_("pv_mfma", s);
+        switch (vp.Dp32 / 32) {
+        case 1: hipLaunchKernelGGL((k_pv_mfma<1, FUSED>), grid, dim3(64), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_pv_mfma<2, FUSED>), grid, dim3(128), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((k_pv_mfma<3, FUSED>), grid, dim3(192), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((k_pv_mfma<4, FUSED>), grid, dim3(256), 0, s, a); break;
+        case 5: hipLaunchKernelGGL((k_pv_mfma<5, FUSED>), grid, dim3(320), 0, s, a); break;
+        case 6: hipLaunchKernelGGL((k_pv_mfma<6, FUSED>), grid, dim3(384), 0, s, a); break;
+        case 7: hipLaunchKernelGGL((k_pv_mfma<7, FUSED>), grid, dim3(448), 0, s, a); break;
+        default: hipLaunchKernelGGL((k_pv_mfma<8, FUSED>), grid, dim3(512), 0, s, a); break;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    ProfScope prof_("pv_fallback", s);
+    if (v.dtype == 0)
+        hipLaunchKernelGGL((k_tile_fallback<float, FUSED>), grid, dim3(256), 0, s, a, (const float *)v.data, v.sB,
+                           v.sH, v.sS, num_ws, den_ws);
+    else
+        hipLaunchKernelGGL((k_tile_fallback<bf16_t, FUSED>), grid, dim3(256), 0, s, a, (const bf16_t *)v.data, v.sB,
+                           v.sH, v.sS, num_ws, den_ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
+                     int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
+                     int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
+                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s) {
+    const int64_t ni = i1 - i0;
+    if (ni <= 0) return hipSuccess;
+    const int64_t ntiles = (ni + 31) / 32, bh = g.B * g.Hq;
+    hipError_t e = launch_fill_u32((uint32_t *)flags, bh * ntiles, 0u, s);
+    if (e != hipSuccess) return e;
+    PvArgs a{};
+    a.scores = scores;
+    a.rowmax = rowmax;
+    a.rm_rows = rm_rows;
+    a.rm_row0 = rm_row0;
+    a.ni = ni;
+    a.W = kv_hi - kv_lo;
+    a.i0 = i0;
+    a.kv_lo = kv_lo;
+    a.kv_hi = kv_hi;
+    a.Hq = g.Hq;
+    a.Hkv = g.Hkv;
+    a.group = g.Hq / g.Hkv;
+    a.D = g.D;
+    a.Dp32 = vp.Dp32;
+    a.nKB = vp.nKB;
+    a.causal = g.causal;
+    a.vsl = (const v4i *)vp.slices;
+    a.colgrid = vp.colgrid;
+    a.grpB = vp.grpB;
+    a.flags = flags;
+    a.ntiles = ntiles;
+    a.force_fallback = force_fallback;
+    if (o) {
+        a.o = o->data;
+        a.osB = o->sB;
+        a.osH = o->sH;
+        a.osS = o->sS;
+    }
+    a.num = num;
+    a.den = den;
+    a.plane_rows = plane_rows;
+    a.rows_per_bh = rows_per_bh;
+    a.row0 = row0;
+    dim3 grid((unsigned)ntiles, (unsigned)bh);
+    return o ? launch_pv_t<true>(v, g, vp, a, grid, fb_num, fb_den, s)
+             : launch_pv_t<false>(v, g, vp, a, grid, fb_num, fb_den, s);
+}
+
+}  // namespace det

@@ -2,7 +2,9 @@
 the shard-invariance properties of the det-attn page ("Correctness": every KV
 split and block permutation, and repeated runs, are torch.equal to the fused
 result).  Inputs come from the seeded generators in workloads.py."""
+import contextlib
 import itertools
+import os
 import sys
 
 import numpy as np
@@ -280,3 +282,45 @@ def test_empty_query_rows(A):
     q, k, v = gpu(*W.attn_inputs(407, 1, 2, 2, 0, 16, 16, torch.float32))
     out = A.det_attn(q, k, v, False)
     assert out.shape == (1, 2, 0, 16)
+
+
+# ---------------------------------------------------------------- both deposit paths
+
+@contextlib.contextmanager
+def generic_path():
+    """Send every tile through the generic exact deposit instead of the
+    matrix-core one (DET_FORCE_FALLBACK is read on each call)."""
+    os.environ["DET_FORCE_FALLBACK"] = "1"
+    try:
+        yield
+    finally:
+        os.environ.pop("DET_FORCE_FALLBACK", None)
+
+
+@pytest.mark.parametrize("case", ["tiny", "gqa_small", "d3", "d256", "rect"])
+def test_matrix_core_and_generic_paths_bit_identical(A, oracle, case):
+    if case == "tiny":
+        wl = W.attn_workload("tiny_mha_f32")
+        q, k, v, causal, scale = wl["q"], wl["k"], wl["v"], False, wl["scale"]
+    elif case == "gqa_small":
+        q, k, v = W.attn_inputs(501, 2, 4, 2, 200, 200, 128, torch.bfloat16)
+        causal, scale = True, W.default_scale(128)
+    elif case == "d3":
+        q, k, v = W.attn_inputs(502, 1, 2, 1, 70, 70, 3, torch.bfloat16)
+        causal, scale = True, W.default_scale(3)
+    elif case == "d256":
+        q, k, v = W.attn_inputs(503, 1, 2, 2, 96, 96, 256, torch.bfloat16)
+        causal, scale = False, W.default_scale(256)
+    else:
+        q, k, v = W.attn_inputs(504, 1, 3, 3, 33, 131, 64, torch.float32)
+        causal, scale = False, 0.15
+    Q, K, V = gpu(q, k, v)
+    fast = A.det_attn(Q, K, V, causal, scale)
+    m = A.rowmax(Q, K, 0, K.shape[2], causal, scale)
+    nf, df = A.accumulate(Q, K, V, m, 0, K.shape[2], causal, scale)
+    with generic_path():
+        gen = A.det_attn(Q, K, V, causal, scale)
+        ng, dg = A.accumulate(Q, K, V, m, 0, K.shape[2], causal, scale)
+    assert torch.equal(fast, gen)
+    assert torch.equal(nf, ng) and torch.equal(df, dg)
+    assert_bits_equal(fast, oracle.det_attn(q, k, v, causal, scale), case)
