@@ -53,7 +53,7 @@ ProfScope::ProfScope(const char *name, hipStream_t s) : slot(-1), stream(s) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     ProfRec r{name, pooled_event(), pooled_event()};
     if (!r.a || !r.b) return;
-    hipEventRecord(r.a, s);
+    (void)hipEventRecord(r.a, s);
     slot = (int)g_prof.size();
     g_prof.push_back(r);
 }
@@ -61,7 +61,7 @@ ProfScope::ProfScope(const char *name, hipStream_t s) : slot(-1), stream(s) {
 ProfScope::~ProfScope() {
     if (slot < 0) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    hipEventRecord(g_prof[slot].b, stream);
+    (void)hipEventRecord(g_prof[slot].b, stream);
 }
 
 void prof_enable(bool on) {
@@ -80,7 +80,7 @@ size_t prof_report(char *buf, size_t len) {
     std::vector<double> tot;
     std::vector<long> cnt;
     for (auto &r : g_prof) {
-        hipEventSynchronize(r.b);
+        (void)hipEventSynchronize(r.b);
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) continue;
         size_t k = 0;

@@ -131,19 +131,20 @@ size_t bytes_rowmax(const AttnGeom &g, int64_t ni) {
 size_t bytes_accumulate(const AttnGeom &g, int64_t ni, int64_t W) {
     const int64_t bh = g.B * g.Hq;
     return vprep_bytes(g, W) + align256((size_t)bh * padded_rows(ni) * g.Dp * 8) +
-           align256((size_t)bh * ni * W * 4) + pv_fallback_bytes(g, 0);
+           align256((size_t)bh * ni * W * 4) + align256((size_t)bh * ((ni + 31) / 32) * 4) +
+           pv_digit_bytes(g, ni, W);
 }
 
 size_t bytes_fused(const AttnGeom &g, int64_t ni) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, g.Skv) + score_scratch_bytes(g, ni, g.Skv) + align256((size_t)rows * 4) +
-           pv_fallback_bytes(g, ni);
+           pv_fallback_bytes(g, ni) + pv_digit_bytes(g, ni, g.Skv);
 }
 
 size_t bytes_sharded(const AttnGeom &g, int64_t ni, int64_t maxlen) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, maxlen) + score_scratch_bytes(g, ni, maxlen) + 2 * align256((size_t)rows * 4) +
-           pv_fallback_bytes(g, 0) +
+           align256((size_t)bh * ((ni + 31) / 32) * 4) + pv_digit_bytes(g, ni, maxlen) +
            2 * (align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8));
 }
 
@@ -298,10 +299,11 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
         double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
         float *sc = c.take<float>(bh * ni * W);
         int *flags = c.take<int>(bh * ((ni + 31) / 32));
+        char *dws = c.take<char>(pv_digit_bytes(g, ni, W));
         HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
         HIP_TRY(launch_scores(tk, g, q64, i0, i1, kv_lo, kv_hi, sc, nullptr, 0, 0, s), "scores");
-        HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr, nullptr,
-                          num, den, rows, g.Sq, 0, ff, s),
+        HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, dws, nullptr, nullptr,
+                          nullptr, num, den, rows, g.Sq, 0, ff, s),
                 "deposit");
     }
     HIP_TRY(launch_normalize(num, rows * g.D, kNumDigits, s), "normalize num");
@@ -379,12 +381,13 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
         int *flags = c.take<int>(bh * tiles);
         int64_t *fnum = c.take<int64_t>(kNumDigits * bh * tiles * 32 * g.D);
         int64_t *fden = c.take<int64_t>(kDenDigits * bh * tiles * 32);
+        char *dws = c.take<char>(pv_digit_bytes(g, ni, g.Skv));
         HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
         HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
         HIP_TRY(launch_scores(tk, g, q64, i0, i1, 0, g.Skv, sc, keys, ni, i0, s), "scores");
         HIP_TRY(launch_keys_to_f32(keys, rm, bh, ni, ni, 0, s), "rowmax");
-        HIP_TRY(launch_pv(tv, g, vp, sc, rm, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr, nullptr, 0, 0,
-                          0, ff, s),
+        HIP_TRY(launch_pv(tv, g, vp, sc, rm, ni, i0, i0, i1, 0, g.Skv, flags, dws, fnum, fden, &ov, nullptr, nullptr,
+                          0, 0, 0, ff, s),
                 "deposit");
     }
     return ok();
@@ -458,6 +461,7 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         float *rm_acc = c.take<float>(rows);
         float *rm_part = c.take<float>(rows);
         int *flags = c.take<int>(bh * ((ni + 31) / 32));
+        char *dws = c.take<char>(pv_digit_bytes(g, ni, ml));
         int64_t *num_acc = c.take<int64_t>(kNumDigits * rows * g.D);
         int64_t *den_acc = c.take<int64_t>(kDenDigits * rows);
         int64_t *num_part = c.take<int64_t>(kNumDigits * rows * g.D);
@@ -484,7 +488,7 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
             if (h > l) {
                 HIP_TRY(launch_vprep(tv, g, l, h, vp, s), "prepare v");
                 HIP_TRY(launch_scores(tk, g, q64, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
-                HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
+                HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, ni, i0, i0, i1, l, h, flags, dws, nullptr, nullptr, nullptr,
                                   num_part, den_part, rows, ni, i0, ff, s),
                         "deposit");
             }

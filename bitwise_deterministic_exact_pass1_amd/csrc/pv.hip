@@ -35,6 +35,7 @@ constexpr int kNC = kAw + kBmax - 1;    // shift classes s = a + b
 constexpr int kKB = 32;                 // keys per block (the MFMA K)
 constexpr int kCarryEvery = 256;        // blocks (8192 keys) between carry passes
 constexpr int kBvFallback = 99;         // "needs the generic path" marker
+constexpr int kStatKeys = 64;           // keys per workgroup of the column statistics
 
 // ---------------------------------------------------------------- V preparation
 
@@ -47,8 +48,8 @@ __global__ __launch_bounds__(256) void k_vstats(const TV *__restrict__ vp, int64
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t bhk = blockIdx.z, b = bhk / Hkv, hk = bhk % Hkv;
     const int64_t d = (int64_t)blockIdx.y * 64 + lane;
-    const int64_t j0 = kv_lo + (int64_t)blockIdx.x * 512;
-    const int64_t j1 = std::min<int64_t>(kv_hi, j0 + 512);
+    const int64_t j0 = kv_lo + (int64_t)blockIdx.x * kStatKeys;
+    const int64_t j1 = std::min<int64_t>(kv_hi, j0 + kStatKeys);
     int emax = INT_MIN, lmin = INT_MAX;
     if (d < D) {
         const TV *col = vp + b * vsB + hk * vsH + d;
@@ -181,7 +182,7 @@ __device__ __forceinline__ void add_i128_digits(__int128 x, int pos, int64_t *dg
     }
 }
 
-// ---------------------------------------------------------------- the MFMA kernel
+// ---------------------------------------------------------------- the MFMA kernels
 
 struct PvArgs {
     const float *scores;  // [bh][ni][W] chunk scores
@@ -195,6 +196,9 @@ struct PvArgs {
     int *flags;  // [bh][ntiles]
     int64_t ntiles;
     int force_fallback;
+    v4i *wdig;          // [bh][ntiles][nKB][kAw][64] digit blocks of W
+    uint32_t *wmask;    // [bh][ntiles][nKB] nonzero-digit masks
+    int64_t *den_rows;  // [bh][ntiles*32] exact sum of W per row
     // fused output
     float *o;
     int64_t osB, osH, osS;
@@ -203,92 +207,106 @@ struct PvArgs {
     int64_t plane_rows, rows_per_bh, row0;
 };
 
-template <int NW, bool FUSED>
-__global__ __launch_bounds__(64 * NW) void k_pv_mfma(PvArgs A) {
-    constexpr int NT = 64 * NW;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t bh = blockIdx.y, tile = blockIdx.x;
-    const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
-    const int64_t it0 = A.i0 + tile * 32;     // first query row of the tile
-    const int64_t i_end = A.i0 + A.ni;         // rows of the chunk
-    const int64_t nG = A.Dp32 / 32;
-    const int64_t jlo = A.kv_lo;
+// Weights of one 32-row x 32-key block: w = RN32(exp_det(s - m)), W = w 2^46,
+// its six balanced digits written in MFMA lane order (lane l byte p holds
+// key 16(l/32)+p of row l%32), the nonzero-digit mask of the block, and the
+// exact row sums of W.  A weight the grid cannot hold flags the tile.
+__global__ __launch_bounds__(256) void k_wdigits(PvArgs A) {
+    const int tid = threadIdx.x;
+    const int64_t kb = blockIdx.x, tile = blockIdx.y, bh = blockIdx.z;
+    const int64_t it0 = A.i0 + tile * 32, i_end = A.i0 + A.ni;
+    const int64_t jlo = A.kv_lo + kb * kKB;
     const int64_t jhi = A.causal ? std::min<int64_t>(A.kv_hi, it0 + 32) : A.kv_hi;
-    const int64_t nblk = jhi > jlo ? (jhi - jlo + kKB - 1) / kKB : 0;
-
-    __shared__ __attribute__((aligned(16))) uint8_t abuf[2][kAw][64 * 16];
-    __shared__ int64_t den_s[32];
-    __shared__ int bad_s;
-
-    if (tid < 32) den_s[tid] = 0;
-    if (tid == 0) bad_s = A.force_fallback;
-    // any group needing more than kBmax digits sends the whole tile to the generic path
-    int Bv = 1;
-    for (int64_t g = 0; g < nG; ++g) {
-        const int x = A.grpB[bhk * nG + g];
-        if (x > kBmax && tid == 0) bad_s = 1;
-        if (g == wave) Bv = x;
-    }
+    if (jlo >= jhi) return;  // block above the causal diagonal: never read
+    __shared__ uint32_t smask;
+    if (tid == 0) smask = 0;
     __syncthreads();
-    if (bad_s) {
-        if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
+    const int r = tid >> 3, q = tid & 7;
+    const int64_t i = it0 + r;
+    const bool rowok = i < i_end;
+    float m = 0.0f;
+    const float *srow = A.scores;
+    if (rowok) {
+        m = A.rowmax[bh * A.rm_rows + (i - A.rm_row0)];
+        srow = A.scores + (bh * A.ni + (i - A.i0)) * A.W - A.kv_lo;
+    }
+    int64_t Wq[4];
+    int64_t wsum = 0;
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t j = jlo + 4 * q + u;
+        float w = 0.0f;
+        if (rowok && j < jhi && (!A.causal || j <= i)) w = weight(srow[j], m);
+        const double ws = ldexp((double)w, kSw);
+        const int64_t Wi = (int64_t)ws;
+        if ((double)Wi != ws || Wi > (1ll << kSw)) bad = true;
+        Wq[u] = Wi;
+        wsum += Wi;
+    }
+    // row sums: the 8 threads of a row are 8 consecutive lanes
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) wsum += __shfl_xor(wsum, off, 64);
+    if (q == 0 && wsum) atomicAdd((unsigned long long *)&A.den_rows[bh * A.ntiles * 32 + tile * 32 + r],
+                                  (unsigned long long)wsum);
+    if (bad) A.flags[bh * A.ntiles + tile] = 1;
+    uint8_t *blk = (uint8_t *)(A.wdig + ((bh * A.ntiles + tile) * A.nKB + kb) * kAw * 64);
+    const int lrow = r + 32 * (q >> 2), boff = (q & 3) * 4;
+    uint32_t nzm = 0;
+#pragma unroll
+    for (int a = 0; a < kAw; ++a) {
+        uint32_t pack = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t c = ((Wq[u] & 255) ^ 128) - 128;
+            Wq[u] = (Wq[u] - c) >> 8;
+            pack |= ((uint32_t)(c & 255)) << (8 * u);
+        }
+        if (pack) nzm |= 1u << a;
+        *(uint32_t *)(blk + (a * 64 + lrow) * 16 + boff) = pack;
+    }
+    if (nzm) atomicOr(&smask, nzm);
+    __syncthreads();
+    if (tid == 0) A.wmask[(bh * A.ntiles + tile) * A.nKB + kb] = smask;
+}
+
+// One wave per (row tile, 32-dim group): C_s += digits(W) x digits(V) on the
+// matrix cores over the tile's keys, then the exact value is finalized (o) or
+// added into digit planes.  Tiles flagged by k_wdigits or by a V group that
+// needs more than kBmax digits are left to the generic path.
+template <bool FUSED>
+__global__ __launch_bounds__(64, 2) void k_pv_mfma(PvArgs A) {
+    const int lane = threadIdx.x;
+    const int64_t tile = blockIdx.x, G = blockIdx.y, bh = blockIdx.z;
+    const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
+    const int64_t it0 = A.i0 + tile * 32, i_end = A.i0 + A.ni;
+    const int64_t nG = A.Dp32 / 32;
+    const int64_t jhi = A.causal ? std::min<int64_t>(A.kv_hi, it0 + 32) : A.kv_hi;
+    const int64_t nblk = jhi > A.kv_lo ? (jhi - A.kv_lo + kKB - 1) / kKB : 0;
+    int badtile = A.force_fallback || A.flags[bh * A.ntiles + tile];
+    for (int64_t g = 0; g < nG; ++g) badtile |= A.grpB[bhk * nG + g] > kBmax;
+    if (badtile) {
+        if (lane == 0 && G == 0) A.flags[bh * A.ntiles + tile] = 1;
         return;
     }
-    const v4i *vblk = A.vsl + ((bhk * nG + wave) * A.nKB) * kBmax * 64;
+    const int Bv = A.grpB[bhk * nG + G];
+    const v4i *vblk = A.vsl + ((bhk * nG + G) * A.nKB) * kBmax * 64 + lane;
+    const v4i *wblk = A.wdig + ((bh * A.ntiles + tile) * A.nKB) * kAw * 64 + lane;
+    const uint32_t *wm = A.wmask + (bh * A.ntiles + tile) * A.nKB;
 
     v16i C[kNC];
 #pragma unroll
     for (int s = 0; s < kNC; ++s) C[s] = v16i{0};
-    bool bad = false;
-
     for (int64_t kb = 0; kb < nblk; ++kb) {
-        const int buf = (int)(kb & 1);
-        const int64_t j0 = jlo + kb * kKB;
-        // weights of 32 rows x 32 keys -> balanced digits of W in LDS
-        for (int p = tid; p < 256; p += NT) {
-            const int r = p >> 3, q = p & 7;
-            const int64_t i = it0 + r;
-            int64_t Wq[4];
-            int64_t wsum = 0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t j = j0 + 4 * q + u;
-                float w = 0.0f;
-                if (i < i_end && j < jhi && (!A.causal || j <= i)) {
-                    const int64_t row = bh * A.ni + (i - A.i0);
-                    w = weight(A.scores[row * A.W + (j - A.kv_lo)], A.rowmax[bh * A.rm_rows + (i - A.rm_row0)]);
-                }
-                const double ws = ldexp((double)w, kSw);
-                const int64_t Wi = (int64_t)ws;
-                if ((double)Wi != ws || Wi > (1ll << kSw)) bad = true;
-                Wq[u] = Wi;
-                wsum += Wi;
-            }
-            if (wsum) atomicAdd((unsigned long long *)&den_s[r], (unsigned long long)wsum);
-            const int lrow = r + 32 * (q >> 2), boff = (q & 3) * 4;
-#pragma unroll
-            for (int a = 0; a < kAw; ++a) {
-                uint32_t pack = 0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int64_t c = ((Wq[u] & 255) ^ 128) - 128;
-                    Wq[u] = (Wq[u] - c) >> 8;
-                    pack |= ((uint32_t)(c & 255)) << (8 * u);
-                }
-                *(uint32_t *)&abuf[buf][a][lrow * 16 + boff] = pack;
-            }
-        }
-        __syncthreads();
-        // exact products on the matrix cores
+        const uint32_t mask = wm[kb];
         v4i Bd[kBmax];
 #pragma unroll
         for (int s = 0; s < kBmax; ++s)
-            if (s < Bv) Bd[s] = vblk[(kb * kBmax + s) * 64 + lane];
+            if (s < Bv) Bd[s] = vblk[(kb * kBmax + s) * 64];
 #pragma unroll
         for (int a = 0; a < kAw; ++a) {
-            const v4i Aa = *(const v4i *)&abuf[buf][a][lane * 16];
-            const bool nz = (Aa.x | Aa.y | Aa.z | Aa.w) != 0;
-            if (__any(nz)) {
+            if (mask & (1u << a)) {
+                const v4i Aa = wblk[(kb * kAw + a) * 64];
 #pragma unroll
                 for (int s = 0; s < kBmax; ++s)
                     if (s < Bv) C[a + s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aa, Bd[s], C[a + s], 0, 0, 0);
@@ -304,15 +322,10 @@ __global__ __launch_bounds__(64 * NW) void k_pv_mfma(PvArgs A) {
             }
         }
     }
-    if (bad) bad_s = 1;  // benign race: every writer stores 1
-    __syncthreads();
-    if (bad_s) {
-        if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
-        return;
-    }
 
-    const int64_t d = wave * 32 + (lane & 31);
+    const int64_t d = G * 32 + (lane & 31);
     const int g = A.colgrid[bhk * A.Dp32 + d];
+    const int64_t *dsum_row = A.den_rows + bh * A.ntiles * 32 + tile * 32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(64 * NW) void k_pv_mfma(PvArgs A) {
         __int128 num = 0;
 #pragma unroll
         for (int s = kNC - 1; s >= 0; --s) num = num * 256 + (__int128)C[s][r];
-        const int64_t dsum = den_s[row];
+        const int64_t dsum = dsum_row[row];
         if (FUSED) {
             const double n64 = i128_to_f64(num, g - kSw);
             const double d64 = i128_to_f64((__int128)dsum, -kSw);
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(64 * NW) void k_pv_mfma(PvArgs A) {
         } else {
             const int64_t prow = bh * A.rows_per_bh + (i - A.row0);
             add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, A.num + prow * A.D + d, A.plane_rows * A.D);
-            if (wave == 0 && (lane & 31) == 0)
+            if (G == 0 && (lane & 31) == 0)
                 add_i128_digits<kDenDigits>((__int128)dsum, -kSw - kDenElo, A.den + prow, A.plane_rows);
         }
     }
@@ -432,6 +445,14 @@ size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i) {
            align256((size_t)kDenDigits * bh * tiles * 32 * 8);                  // fused scratch DEN
 }
 
+size_t pv_digit_bytes(const AttnGeom &g, int64_t rows_i, int64_t kv_len) {
+    const int64_t tiles = (rows_i + 31) / 32, bh = g.B * g.Hq;
+    const int64_t nKB = std::max<int64_t>((kv_len + kKB - 1) / kKB, 1);
+    return align256((size_t)bh * tiles * nKB * kAw * 1024) +  // W digit blocks
+           align256((size_t)bh * tiles * nKB * 4) +            // nonzero masks
+           align256((size_t)bh * tiles * 32 * 8);              // row sums of W
+}
+
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
                         hipStream_t s) {
     ProfScope prof_("vprep", s);
@@ -443,7 +464,7 @@ hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64
     if ((e = launch_fill_u32((uint32_t *)vp.colmax, bhk * Dp32, (uint32_t)INT_MIN, s)) != hipSuccess) return e;
     if ((e = launch_fill_u32((uint32_t *)vp.colmin, bhk * Dp32, (uint32_t)INT_MAX, s)) != hipSuccess) return e;
     if (len > 0) {
-        dim3 gs((unsigned)((len + 511) / 512), (unsigned)((Dp32 + 63) / 64), (unsigned)bhk);
+        dim3 gs((unsigned)((len + kStatKeys - 1) / kStatKeys), (unsigned)((Dp32 + 63) / 64), (unsigned)bhk);
         if (v.dtype == 0)
             hipLaunchKernelGGL(k_vstats<float>, gs, dim3(256), 0, s, (const float *)v.data, v.sB, v.sH, v.sS, g.Hkv,
                                g.D, Dp32, kv_lo, kv_hi, vp.colmax, vp.colmin);
@@ -464,24 +485,23 @@ hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64
 }
 
 template <bool FUSED>
-static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &vp, PvArgs &a, dim3 grid,
+static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &vp, PvArgs &a, int64_t bh,
                               int64_t *num_ws, int64_t *den_ws, hipStream_t s) {
+    hipError_t e;
+    {
+        ProfScope prof_("wdigits", s);
+        dim3 grid((unsigned)vp.nKB, (unsigned)a.ntiles, (unsigned)bh);
+        hipLaunchKernelGGL(k_wdigits, grid, dim3(256), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     {
         ProfScope prof_("pv_mfma", s);
-        switch (vp.Dp32 / 32) {
-        case 1: hipLaunchKernelGGL((k_pv_mfma<1, FUSED>), grid, dim3(64), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_pv_mfma<2, FUSED>), grid, dim3(128), 0, s, a); break;
-        case 3: hipLaunchKernelGGL((k_pv_mfma<3, FUSED>), grid, dim3(192), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((k_pv_mfma<4, FUSED>), grid, dim3(256), 0, s, a); break;
-        case 5: hipLaunchKernelGGL((k_pv_mfma<5, FUSED>), grid, dim3(320), 0, s, a); break;
-        case 6: hipLaunchKernelGGL((k_pv_mfma<6, FUSED>), grid, dim3(384), 0, s, a); break;
-        case 7: hipLaunchKernelGGL((k_pv_mfma<7, FUSED>), grid, dim3(448), 0, s, a); break;
-        default: hipLaunchKernelGGL((k_pv_mfma<8, FUSED>), grid, dim3(512), 0, s, a); break;
-        }
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        dim3 grid((unsigned)a.ntiles, (unsigned)(vp.Dp32 / 32), (unsigned)bh);
+        hipLaunchKernelGGL((k_pv_mfma<FUSED>), grid, dim3(64), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     ProfScope prof_("pv_fallback", s);
+    dim3 grid((unsigned)a.ntiles, (unsigned)bh);
     if (v.dtype == 0)
         hipLaunchKernelGGL((k_tile_fallback<float, FUSED>), grid, dim3(256), 0, s, a, (const float *)v.data, v.sB,
                            v.sH, v.sS, num_ws, den_ws);
@@ -493,13 +513,21 @@ static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &v
 
 hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
                      int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
-                     int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
-                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s) {
+                     int *flags, void *digit_ws, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num,
+                     int64_t *den, int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback,
+                     hipStream_t s) {
     const int64_t ni = i1 - i0;
     if (ni <= 0) return hipSuccess;
     const int64_t ntiles = (ni + 31) / 32, bh = g.B * g.Hq;
     hipError_t e = launch_fill_u32((uint32_t *)flags, bh * ntiles, 0u, s);
     if (e != hipSuccess) return e;
+    char *dw = (char *)digit_ws;
+    v4i *wdig = (v4i *)dw;
+    dw += align256((size_t)bh * ntiles * vp.nKB * kAw * 1024);
+    uint32_t *wmask = (uint32_t *)dw;
+    dw += align256((size_t)bh * ntiles * vp.nKB * 4);
+    int64_t *den_rows = (int64_t *)dw;
+    if ((e = launch_fill_i64(den_rows, bh * ntiles * 32, 0, s)) != hipSuccess) return e;
     PvArgs a{};
     a.scores = scores;
     a.rowmax = rowmax;
@@ -523,6 +551,9 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     a.flags = flags;
     a.ntiles = ntiles;
     a.force_fallback = force_fallback;
+    a.wdig = wdig;
+    a.wmask = wmask;
+    a.den_rows = den_rows;
     if (o) {
         a.o = o->data;
         a.osB = o->sB;
@@ -534,9 +565,8 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     a.plane_rows = plane_rows;
     a.rows_per_bh = rows_per_bh;
     a.row0 = row0;
-    dim3 grid((unsigned)ntiles, (unsigned)bh);
-    return o ? launch_pv_t<true>(v, g, vp, a, grid, fb_num, fb_den, s)
-             : launch_pv_t<false>(v, g, vp, a, grid, fb_num, fb_den, s);
+    return o ? launch_pv_t<true>(v, g, vp, a, bh, fb_num, fb_den, s)
+             : launch_pv_t<false>(v, g, vp, a, bh, fb_num, fb_den, s);
 }
 
 }  // namespace det
