@@ -123,27 +123,57 @@ struct Carver {
 
 // ---- per-chunk workspace needs of each entry point (ni = query rows per chunk)
 
-size_t bytes_rowmax(const AttnGeom &g, int64_t ni) {
-    const int64_t bh = g.B * g.Hq;
-    return align256((size_t)bh * padded_rows(ni) * g.Dp * 8) + align256((size_t)bh * ni * 4);
+// ---- scores: bf16 on the matrix cores (qk.hip), f32 by the fp64 VALU chain (attn.hip)
+
+size_t score_fixed_bytes(const AttnGeom &g, bool mfma, int64_t kv_len) {
+    return mfma ? qk_kprep_bytes(g, kv_len) : 0;
 }
 
-size_t bytes_accumulate(const AttnGeom &g, int64_t ni, int64_t W) {
+size_t score_chunk_bytes(const AttnGeom &g, bool mfma, int64_t ni, int64_t kv_len) {
+    return mfma ? qk_chunk_bytes(g, ni, kv_len) : align256((size_t)g.B * g.Hq * padded_rows(ni) * g.Dp * 8);
+}
+
+hipError_t prep_keys(const Tensor &tk, const AttnGeom &g, bool mfma, void *kprep, int64_t lo, int64_t hi,
+                     hipStream_t s) {
+    if (!mfma || hi <= lo) return hipSuccess;
+    return launch_qk_kprep(tk, g, lo, hi, kprep, s);
+}
+
+hipError_t run_scores(const Tensor &tq, const Tensor &tk, const AttnGeom &g, bool mfma, const void *kprep,
+                      void *chunk_ws, int64_t i0, int64_t i1, int64_t lo, int64_t hi, float *scores, uint32_t *keys,
+                      int64_t key_rows, int64_t key_row0, hipStream_t s) {
+    if (mfma)
+        return launch_scores_qk(tq, tk, g, kprep, chunk_ws, i0, i1, lo, hi, scores, keys, key_rows, key_row0, s);
+    hipError_t e = launch_widen_q(tq, g, i0, i1, (double *)chunk_ws, s);
+    if (e != hipSuccess) return e;
+    return launch_scores(tk, g, (const double *)chunk_ws, i0, i1, lo, hi, scores, keys, key_rows, key_row0, s);
+}
+
+bool use_mfma_scores(const det_tensor *q) { return q->dtype == DET_BF16; }
+
+size_t bytes_rowmax(const AttnGeom &g, bool mfma, int64_t ni, int64_t kv_len) {
     const int64_t bh = g.B * g.Hq;
-    return vprep_bytes(g, W) + align256((size_t)bh * padded_rows(ni) * g.Dp * 8) +
+    return score_fixed_bytes(g, mfma, kv_len) + score_chunk_bytes(g, mfma, ni, kv_len) + align256((size_t)bh * ni * 4);
+}
+
+size_t bytes_accumulate(const AttnGeom &g, bool mfma, int64_t ni, int64_t W) {
+    const int64_t bh = g.B * g.Hq;
+    return vprep_bytes(g, W) + score_fixed_bytes(g, mfma, W) + score_chunk_bytes(g, mfma, ni, W) +
            align256((size_t)bh * ni * W * 4) + align256((size_t)bh * ((ni + 31) / 32) * 4) +
            pv_digit_bytes(g, ni, W);
 }
 
-size_t bytes_fused(const AttnGeom &g, int64_t ni) {
+size_t bytes_fused(const AttnGeom &g, bool mfma, int64_t ni) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
-    return vprep_bytes(g, g.Skv) + score_scratch_bytes(g, ni, g.Skv) + align256((size_t)rows * 4) +
+    return vprep_bytes(g, g.Skv) + score_fixed_bytes(g, mfma, g.Skv) + score_chunk_bytes(g, mfma, ni, g.Skv) +
+           align256((size_t)rows * 4) + align256((size_t)rows * g.Skv * 4) + align256((size_t)rows * 4) +
            pv_fallback_bytes(g, ni) + pv_digit_bytes(g, ni, g.Skv);
 }
 
-size_t bytes_sharded(const AttnGeom &g, int64_t ni, int64_t maxlen) {
+size_t bytes_sharded(const AttnGeom &g, bool mfma, int64_t ni, int64_t maxlen) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
-    return vprep_bytes(g, maxlen) + score_scratch_bytes(g, ni, maxlen) + 2 * align256((size_t)rows * 4) +
+    return vprep_bytes(g, maxlen) + score_fixed_bytes(g, mfma, maxlen) + score_chunk_bytes(g, mfma, ni, maxlen) +
+           align256((size_t)rows * 4) + align256((size_t)rows * maxlen * 4) + 2 * align256((size_t)rows * 4) +
            align256((size_t)bh * ((ni + 31) / 32) * 4) + pv_digit_bytes(g, ni, maxlen) +
            2 * (align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8));
 }
@@ -233,7 +263,8 @@ int det_digit_format(int32_t which, int32_t *n_digits, int32_t *lsb_exp2) {
 size_t det_attn_rowmax_workspace_size(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi) {
     if (check_qk(q, k, 0) || check_range(k, kv_lo, kv_hi)) return 0;
     const AttnGeom g = geom(q, k, 0, 1.0);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_rowmax(g, ni); });
+    const bool mf = use_mfma_scores(q);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_rowmax(g, mf, ni, kv_hi - kv_lo); });
 }
 
 int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi, int32_t causal,
@@ -242,20 +273,24 @@ int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int
     if ((rc = check_qk(q, k, causal)) || (rc = check_range(k, kv_lo, kv_hi))) return rc;
     if (!rowmax && q->S > 0) return fail(DET_E_NULL, "rowmax is NULL");
     const AttnGeom g = geom(q, k, causal, scale);
-    auto need = [&](int64_t ni) { return bytes_rowmax(g, ni); };
+    const bool mf = use_mfma_scores(q);
+    const int64_t W = kv_hi - kv_lo;
+    auto need = [&](int64_t ni) { return bytes_rowmax(g, mf, ni, W); };
     if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
     if (g.Sq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
     const Tensor tq = to_t(q), tk = to_t(k);
     const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
+    Carver c0{(char *)workspace};
+    void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
+    HIP_TRY(prep_keys(tk, g, mf, kprep, kv_lo, kv_hi, s), "prepare k");
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        Carver c{(char *)workspace};
-        double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
+        Carver c = c0;
+        void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, W));
         uint32_t *keys = c.take<uint32_t>(bh * ni);
-        HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
         HIP_TRY(launch_fill_u32(keys, bh * ni, kKeyNegInf, s), "fill");
-        HIP_TRY(launch_scores(tk, g, q64, i0, i1, kv_lo, kv_hi, nullptr, keys, ni, i0, s), "scores");
+        HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, kv_lo, kv_hi, nullptr, keys, ni, i0, s), "scores");
         HIP_TRY(launch_keys_to_f32(keys, rowmax, bh, ni, g.Sq, i0, s), "rowmax");
     }
     return ok();
@@ -267,7 +302,8 @@ size_t det_attn_accumulate_workspace_size(const det_tensor *q, const det_tensor 
                                           int64_t kv_lo, int64_t kv_hi) {
     if (check_qkv(q, k, v, 0) || check_range(k, kv_lo, kv_hi)) return 0;
     const AttnGeom g = geom(q, k, 0, 1.0);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_accumulate(g, ni, kv_hi - kv_lo); });
+    const bool mf = use_mfma_scores(q);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_accumulate(g, mf, ni, kv_hi - kv_lo); });
 }
 
 int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tensor *v, const float *rowmax,
@@ -277,8 +313,9 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     if ((rc = check_qkv(q, k, v, causal)) || (rc = check_range(k, kv_lo, kv_hi))) return rc;
     if (q->S > 0 && (!rowmax || !num || !den)) return fail(DET_E_NULL, "rowmax, num or den is NULL");
     const AttnGeom g = geom(q, k, causal, scale);
+    const bool mf = use_mfma_scores(q);
     const int64_t W = kv_hi - kv_lo;
-    auto need = [&](int64_t ni) { return bytes_accumulate(g, ni, W); };
+    auto need = [&](int64_t ni) { return bytes_accumulate(g, mf, ni, W); };
     if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
     if (g.Sq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
@@ -291,17 +328,20 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need);
     Carver c0{(char *)workspace};
     VPrep vp = carve_vprep(c0, g, W);
-    if (W > 0) HIP_TRY(launch_vprep(tv, g, kv_lo, kv_hi, vp, s), "prepare v");
+    void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
+    if (W > 0) {
+        HIP_TRY(launch_vprep(tv, g, kv_lo, kv_hi, vp, s), "prepare v");
+        HIP_TRY(prep_keys(tk, g, mf, kprep, kv_lo, kv_hi, s), "prepare k");
+    }
     const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq && W > 0; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
         Carver c = c0;
-        double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
+        void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, W));
         float *sc = c.take<float>(bh * ni * W);
         int *flags = c.take<int>(bh * ((ni + 31) / 32));
         char *dws = c.take<char>(pv_digit_bytes(g, ni, W));
-        HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
-        HIP_TRY(launch_scores(tk, g, q64, i0, i1, kv_lo, kv_hi, sc, nullptr, 0, 0, s), "scores");
+        HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, kv_lo, kv_hi, sc, nullptr, 0, 0, s), "scores");
         HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, dws, nullptr, nullptr,
                           nullptr, num, den, rows, g.Sq, 0, ff, s),
                 "deposit");
@@ -350,7 +390,8 @@ int det_attn_finalize(const int64_t *num, const int64_t *den, int64_t B, int64_t
 size_t det_attn_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal) {
     if (check_qkv(q, k, v, causal)) return 0;
     const AttnGeom g = geom(q, k, causal, 1.0);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_fused(g, ni); });
+    const bool mf = use_mfma_scores(q);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_fused(g, mf, ni); });
 }
 
 int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
@@ -359,7 +400,8 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     if ((rc = check_qkv(q, k, v, causal))) return rc;
     if (q->S > 0 && (rc = check_out(o))) return rc;
     const AttnGeom g = geom(q, k, causal, scale);
-    auto need = [&](int64_t ni) { return bytes_fused(g, ni); };
+    const bool mf = use_mfma_scores(q);
+    auto need = [&](int64_t ni) { return bytes_fused(g, mf, ni); };
     if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
     if (g.Sq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
@@ -368,13 +410,15 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
     Carver c0{(char *)workspace};
     VPrep vp = carve_vprep(c0, g, g.Skv);
+    void *kprep = c0.take<char>(score_fixed_bytes(g, mf, g.Skv));
     HIP_TRY(launch_vprep(tv, g, 0, g.Skv, vp, s), "prepare v");
+    HIP_TRY(prep_keys(tk, g, mf, kprep, 0, g.Skv, s), "prepare k");
     const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
         const int64_t tiles = (ni + 31) / 32;
         Carver c = c0;
-        double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
+        void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, g.Skv));
         uint32_t *keys = c.take<uint32_t>(rows);
         float *sc = c.take<float>(rows * g.Skv);
         float *rm = c.take<float>(rows);
@@ -382,9 +426,8 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
         int64_t *fnum = c.take<int64_t>(kNumDigits * bh * tiles * 32 * g.D);
         int64_t *fden = c.take<int64_t>(kDenDigits * bh * tiles * 32);
         char *dws = c.take<char>(pv_digit_bytes(g, ni, g.Skv));
-        HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
         HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
-        HIP_TRY(launch_scores(tk, g, q64, i0, i1, 0, g.Skv, sc, keys, ni, i0, s), "scores");
+        HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, 0, g.Skv, sc, keys, ni, i0, s), "scores");
         HIP_TRY(launch_keys_to_f32(keys, rm, bh, ni, ni, 0, s), "rowmax");
         HIP_TRY(launch_pv(tv, g, vp, sc, rm, ni, i0, i0, i1, 0, g.Skv, flags, dws, fnum, fden, &ov, nullptr, nullptr,
                           0, 0, 0, ff, s),
@@ -425,8 +468,9 @@ size_t det_attn_sharded_workspace_size(const det_tensor *q, const det_tensor *k,
                                        const int64_t *kv_splits, int32_t n_splits, int32_t causal) {
     if (check_qkv(q, k, v, causal) || check_splits(k, kv_splits, n_splits, nullptr)) return 0;
     const AttnGeom g = geom(q, k, causal, 1.0);
+    const bool mf = use_mfma_scores(q);
     const int64_t ml = max_split(kv_splits, n_splits);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_sharded(g, ni, ml); });
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_sharded(g, mf, ni, ml); });
 }
 
 int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor *v, const int64_t *kv_splits,
@@ -436,8 +480,9 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
     if ((rc = check_qkv(q, k, v, causal)) || (rc = check_splits(k, kv_splits, n_splits, order))) return rc;
     if (q->S > 0 && (rc = check_out(o))) return rc;
     const AttnGeom g = geom(q, k, causal, scale);
+    const bool mf = use_mfma_scores(q);
     const int64_t ml = max_split(kv_splits, n_splits);
-    auto need = [&](int64_t ni) { return bytes_sharded(g, ni, ml); };
+    auto need = [&](int64_t ni) { return bytes_sharded(g, mf, ni, ml); };
     if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
     if (g.Sq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
@@ -455,7 +500,8 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
         Carver c{(char *)workspace};
         VPrep vp = carve_vprep(c, g, ml);
-        double *q64 = c.take<double>(bh * padded_rows(ni) * g.Dp);
+        void *kprep = c.take<char>(score_fixed_bytes(g, mf, ml));
+        void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, ml));
         uint32_t *keys = c.take<uint32_t>(rows);
         float *sc = c.take<float>(rows * ml);
         float *rm_acc = c.take<float>(rows);
@@ -466,14 +512,14 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         int64_t *den_acc = c.take<int64_t>(kDenDigits * rows);
         int64_t *num_part = c.take<int64_t>(kNumDigits * rows * g.D);
         int64_t *den_part = c.take<int64_t>(kDenDigits * rows);
-        HIP_TRY(launch_widen_q(tq, g, i0, i1, q64, s), "widen q");
         // pass 1: rowmax of each shard, composed by max
         HIP_TRY(launch_fill_u32((uint32_t *)rm_acc, rows, 0xff800000u, s), "fill rowmax");  // -inf
         for (int32_t a = 0; a < n_splits; ++a) {
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
             HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
-            HIP_TRY(launch_scores(tk, g, q64, i0, i1, l, h, nullptr, keys, ni, i0, s), "scores");
+            HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
+            HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, nullptr, keys, ni, i0, s), "scores");
             HIP_TRY(launch_keys_to_f32(keys, rm_part, bh, ni, ni, 0, s), "rowmax");
             HIP_TRY(launch_rowmax_combine(rm_acc, rm_part, rows, s), "rowmax combine");
         }
@@ -487,7 +533,8 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
             HIP_TRY(launch_fill_i64(den_part, kDenDigits * rows, 0, s), "fill den");
             if (h > l) {
                 HIP_TRY(launch_vprep(tv, g, l, h, vp, s), "prepare v");
-                HIP_TRY(launch_scores(tk, g, q64, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
+                HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
+                HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
                 HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, ni, i0, i0, i1, l, h, flags, dws, nullptr, nullptr, nullptr,
                                   num_part, den_part, rows, ni, i0, ff, s),
                         "deposit");

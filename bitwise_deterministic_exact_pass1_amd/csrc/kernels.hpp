@@ -76,6 +76,16 @@ hipError_t launch_scores(const Tensor &k, const AttnGeom &g, const double *q64, 
 hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t B_Hq, int64_t rows, int64_t out_rows,
                               int64_t out_row0, hipStream_t s);
 
+// ---- pass-1 scores of bf16 inputs on the matrix cores (qk.hip)
+bool qk_uses_mfma(const Tensor &q);
+size_t qk_kprep_bytes(const AttnGeom &g, int64_t kv_len);
+size_t qk_chunk_bytes(const AttnGeom &g, int64_t ni, int64_t kv_len);
+hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws,
+                           hipStream_t s);
+hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g, const void *kprep, void *chunk_ws,
+                            int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, float *scores,
+                            uint32_t *rowmax_keys, int64_t key_rows, int64_t key_row0, hipStream_t s);
+
 // ---- pass 2 on the matrix cores (pv.hip)
 
 // Prepared V of one key range: per-column grid exponents and balanced int8

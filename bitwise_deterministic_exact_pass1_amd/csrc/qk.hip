@@ -1,0 +1,364 @@
+// qk.hip -- pass-1 scores of bf16 inputs on the int8 matrix cores.
+//
+// The score rule is the fp64 fma chain over d = 0..D-1 (then RN64(scale*dot),
+// RN32).  For bf16 operands every product q_d k_d has at most 16 significant
+// bits, and with q = Qi * 2^gq, k = Ki * 2^gk (gq, gk = the smallest lsb
+// exponent of the row; Qi, Ki integers) every partial sum of the chain is an
+// integer times 2^(gq+gk).  When sum_d |Qi_d| |Ki_d| < 2^53 every partial sum
+// is exactly representable in binary64, so the chain's result IS the exact
+// integer dot product, whatever order it is summed in.  That integer is
+// computed here from balanced int8 digits of Qi and Ki with
+// v_mfma_i32_16x16x64_i8 (exact int32 sums).  The bound is checked per
+// 16-row x 16-key item from per-row max|Qi| and per-key sum|Ki|; an item that
+// fails it (or whose rows need more than kQKmax digits) is recomputed by the
+// plain fp64 chain in k_qk_fix, so the scores are the chain's bits either way.
+#include "dev_math.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace det {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kQKmax = 4;              // digits per Q or K row (32-bit integers)
+constexpr int kQKC = 2 * kQKmax - 1;   // shift classes of the product
+constexpr int kQKbad = 99;             // row needs more digits than kQKmax
+
+// Per-row statistics and digits.  One wave per row: grid exponent g (smallest
+// lsb), digit count, log2 bound of max|Xi| (Q) or of sum|Xi| (K); digits in
+// [row][kQKmax][Dp64] bytes, zero padded to a multiple of 64 dims.
+template <bool IS_K>
+__global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, int64_t sB, int64_t sH, int64_t sS,
+                                                int64_t H, int64_t D, int64_t Dp64, int64_t s0, int64_t ns,
+                                                int64_t ns_pad, int64_t nrows, int4 *__restrict__ info,
+                                                int8_t *__restrict__ dig) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= nrows) return;
+    const int64_t bh = row / ns_pad, ii = row % ns_pad;
+    const int64_t b = bh / H, h = bh % H;
+    const bool live = ii < ns;
+    const bf16_t *xr = x + b * sB + h * sH + (s0 + (live ? ii : 0)) * sS;
+    float v[4];
+    int emax = INT_MIN, lmin = INT_MAX;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t d = lane + 64 * t;
+        v[t] = (live && d < D) ? elem<bf16_t>::to_f32(xr[d]) : 0.0f;
+        if (v[t] != 0.0f) {
+            const int e = f32_exp(v[t]);
+            emax = max(emax, e);
+            lmin = min(lmin, max(e, -126) - 7);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        emax = max(emax, __shfl_xor(emax, off, 64));
+        lmin = min(lmin, __shfl_xor(lmin, off, 64));
+    }
+    const bool zero = emax == INT_MIN;
+    const int g = zero ? 0 : lmin;
+    const int mbits = zero ? 0 : emax + 1 - g;  // |Xi| < 2^mbits
+    int nd = zero ? 1 : (mbits + 2 + 7) / 8;
+    if (nd > kQKmax) nd = kQKbad;
+    int64_t xi[4];
+    int64_t l1 = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        xi[t] = nd == kQKbad ? 0 : (int64_t)ldexp((double)v[t], -g);
+        l1 += xi[t] < 0 ? -xi[t] : xi[t];
+    }
+    int bound = mbits;
+    if (IS_K) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) l1 += __shfl_xor(l1, off, 64);
+        bound = l1 ? 64 - __clzll((long long)l1) : 0;  // sum|Ki| < 2^bound
+    }
+    if (lane == 0) info[row] = int4{g, nd, bound, 0};
+    int8_t *out = dig + row * kQKmax * Dp64;
+#pragma unroll
+    for (int a = 0; a < kQKmax; ++a) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t d = lane + 64 * t;
+            if (d < Dp64) {
+                const int64_t c = ((xi[t] & 255) ^ 128) - 128;
+                xi[t] = (xi[t] - c) >> 8;
+                out[a * Dp64 + d] = (int8_t)c;
+            }
+        }
+    }
+}
+
+constexpr int kQkT = 16;     // rows and keys per matrix-core item
+constexpr int kQkWaves = 4;  // waves per workgroup
+
+struct QkArgs {
+    const int8_t *qdig, *kdig;  // [row][kQKmax][Dp64]
+    const int4 *qinfo, *kinfo;
+    int64_t Dp64, ni, ni_pad, i0, kv_lo, kv_hi, kv_pad;
+    int64_t Hq, Hkv, group;
+    int causal;
+    double scale;
+    float *scores;  // [bh][ni][W] or null
+    int64_t W;
+    uint32_t *keys;  // rowmax keys, [bh*key_rows + i - key_row0], or null
+    int64_t key_rows, key_row0;
+    int *nfix;       // number of items left to the fp64 chain
+    int4 *fixlist;   // their (kb, tile, bh)
+    int64_t nKB;
+};
+
+// One workgroup per (16-row tile, key partition); its waves take the tile's
+// 16-key blocks round robin.  A wave keeps its rows' digits in registers for
+// all of its blocks.  Per block: the item bound, the digit products on the
+// matrix cores, the exact integer dot per pair turned into the score, and a
+// running per-lane max of each row.  Items that fail the bound go to a list.
+// All kQKmax digit products are issued: digits above a row's count are zero,
+// and branching per product would cost more registers than the products do.
+// Operand layout of v_mfma_i32_16x16x64_i8: lane l supplies row (A) or column
+// (B) l%16 with k = 16*(l/16) + 0..15; result register r of lane l holds
+// row 4*(l/16) + r, column l%16.
+template <int ND>
+__global__ __launch_bounds__(64 * kQkWaves) void k_qk_mfma(QkArgs A) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lr = lane & 15, lq = lane >> 4;
+    const int64_t tile = blockIdx.y, bh = blockIdx.z;
+    const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
+    const int64_t it0 = A.i0 + tile * kQkT, i_end = A.i0 + A.ni;
+    const int4 qi = A.qinfo[bh * A.ni_pad + tile * kQkT + lr];
+    int aq = qi.y, qbt = qi.z;
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+        aq = max(aq, __shfl_xor(aq, off, 64));
+        qbt = max(qbt, __shfl_xor(qbt, off, 64));
+    }
+    aq = __builtin_amdgcn_readfirstlane(aq);  // wave-uniform after the reduction
+    qbt = __builtin_amdgcn_readfirstlane(qbt);
+    v4i Aq[kQKmax][ND];
+    {
+        const int8_t *qrow = A.qdig + (bh * A.ni_pad + tile * kQkT + lr) * kQKmax * A.Dp64 + 16 * lq;
+#pragma unroll
+        for (int a = 0; a < kQKmax; ++a)
+#pragma unroll
+            for (int n = 0; n < ND; ++n) Aq[a][n] = *(const v4i *)(qrow + a * A.Dp64 + 64 * n);
+    }
+    int gq[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) gq[r] = __shfl(qi.x, 4 * lq + r, 64);
+    uint32_t mkey[4] = {kKeyNegInf, kKeyNegInf, kKeyNegInf, kKeyNegInf};
+    float *srow = A.scores ? A.scores + (bh * A.ni + (it0 + 4 * lq - A.i0)) * A.W : nullptr;
+    const int64_t stride = (int64_t)gridDim.x * kQkWaves;
+    for (int64_t kb = (int64_t)blockIdx.x * kQkWaves + wave; kb < A.nKB; kb += stride) {
+        const int64_t j0 = A.kv_lo + kb * kQkT;
+        if (A.causal && j0 > it0 + kQkT - 1) break;  // this and later blocks lie above the diagonal
+        const int4 ki = A.kinfo[bhk * A.kv_pad + kb * kQkT + lr];
+        int bk = ki.y, kbnd = ki.z;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+            bk = max(bk, __shfl_xor(bk, off, 64));
+            kbnd = max(kbnd, __shfl_xor(kbnd, off, 64));
+        }
+        bk = __builtin_amdgcn_readfirstlane(bk);
+        kbnd = __builtin_amdgcn_readfirstlane(kbnd);
+        if (aq > kQKmax || bk > kQKmax || qbt + kbnd > 53) {
+            if (lane == 0) {
+                const int at = atomicAdd(A.nfix, 1);
+                A.fixlist[at] = int4{(int)kb, (int)tile, (int)bh, 0};
+            }
+            continue;
+        }
+        const int8_t *krow = A.kdig + (bhk * A.kv_pad + kb * kQkT + lr) * kQKmax * A.Dp64 + 16 * lq;
+        v4i C[kQKC];
+#pragma unroll
+        for (int c = 0; c < kQKC; ++c) C[c] = v4i{0, 0, 0, 0};
+#pragma unroll
+        for (int n = 0; n < ND; ++n) {
+            v4i Bk[kQKmax];
+#pragma unroll
+            for (int c = 0; c < kQKmax; ++c)
+                Bk[c] = *(const v4i *)(krow + c * A.Dp64 + 64 * n);
+#pragma unroll
+            for (int a = 0; a < kQKmax; ++a)
+#pragma unroll
+                for (int c = 0; c < kQKmax; ++c)
+                        C[a + c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[a][n], Bk[c], C[a + c], 0, 0, 0);
+        }
+        const int64_t j = j0 + lr;
+        const bool jv = j < A.kv_hi;
+        const int gk = ki.x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t i = it0 + 4 * lq + r;
+            int64_t dot = 0;
+#pragma unroll
+            for (int c = kQKC - 1; c >= 0; --c) dot = dot * 256 + (int64_t)C[c][r];
+            const double d64 = ldexp((double)dot, gq[r] + gk);  // exact: |dot| < 2^53
+            const float sc = (float)(A.scale * d64);
+            if (jv && i < i_end) {
+                if (srow) srow[r * A.W + (j - A.kv_lo)] = sc;
+                if (!A.causal || j <= i) mkey[r] = max(mkey[r], order_key(sc));
+            }
+        }
+    }
+    if (!A.keys) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        uint32_t m = mkey[r];
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+        const int64_t i = it0 + 4 * lq + r;
+        if (lr == 0 && i < i_end && m != kKeyNegInf) atomicMax(&A.keys[bh * A.key_rows + (i - A.key_row0)], m);
+    }
+}
+
+// The fp64 chain for the items k_qk_mfma left.  A persistent grid walks the
+// item list; per item the 16 query rows and 16 key rows are staged in LDS as
+// binary64, 64 dims at a time, and each thread runs the chain of one
+// (row, key) pair in ascending d.
+constexpr int kFixDC = 64;
+__global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restrict__ q, int64_t qsB, int64_t qsH,
+                                                int64_t qsS, const bf16_t *__restrict__ k, int64_t ksB, int64_t ksH,
+                                                int64_t ksS, int64_t D) {
+    __shared__ double sq[kQkT][kFixDC + 1], sk[kQkT][kFixDC + 1];
+    const int tid = threadIdx.x;
+    const int r = tid >> 4, c = tid & 15;
+    const int n = *A.nfix;
+    for (int it = blockIdx.x; it < n; it += gridDim.x) {
+        const int4 item = A.fixlist[it];
+        const int64_t kb = item.x, tile = item.y, bh = item.z;
+        const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group;
+        const int64_t it0 = A.i0 + tile * kQkT, i_end = A.i0 + A.ni;
+        const int64_t j0 = A.kv_lo + kb * kQkT;
+        double acc = 0.0;
+        for (int64_t d0 = 0; d0 < D; d0 += kFixDC) {
+            __syncthreads();
+            for (int t = tid; t < kQkT * kFixDC; t += 256) {
+                const int rr = t / kFixDC, dd = t % kFixDC;
+                const int64_t d = d0 + dd, i = it0 + rr, j = j0 + rr;
+                sq[rr][dd] = (d < D && i < i_end) ? (double)elem<bf16_t>::to_f32(q[b * qsB + hq * qsH + i * qsS + d]) : 0.0;
+                sk[rr][dd] = (d < D && j < A.kv_hi) ? (double)elem<bf16_t>::to_f32(k[b * ksB + hk * ksH + j * ksS + d]) : 0.0;
+            }
+            __syncthreads();
+            const int dn = (int)std::min<int64_t>(kFixDC, D - d0);
+            for (int dd = 0; dd < dn; ++dd) acc = fma(sq[r][dd], sk[c][dd], acc);
+        }
+        const int64_t i = it0 + r, j = j0 + c;
+        uint32_t m = kKeyNegInf;
+        if (i < i_end && j < A.kv_hi) {
+            const float sc = (float)(A.scale * acc);
+            if (A.scores) A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)] = sc;
+            if (!A.causal || j <= i) m = order_key(sc);
+        }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+        if (A.keys && c == 0 && i < i_end && m != kKeyNegInf) atomicMax(&A.keys[bh * A.key_rows + (i - A.key_row0)], m);
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+
+static int64_t qk_dp64(const AttnGeom &g) { return (g.D + 63) / 64 * 64; }
+static int64_t qk_pad(int64_t len) { return std::max<int64_t>((len + kQkT - 1) / kQkT, 1) * kQkT; }
+
+size_t qk_kprep_bytes(const AttnGeom &g, int64_t kv_len) {
+    const int64_t rows = g.B * g.Hkv * qk_pad(kv_len);
+    return align256((size_t)rows * 16) + align256((size_t)rows * kQKmax * qk_dp64(g));
+}
+
+size_t qk_chunk_bytes(const AttnGeom &g, int64_t ni, int64_t kv_len) {
+    const int64_t ni_pad = padded_rows(ni), bh = g.B * g.Hq;
+    const int64_t nKB = qk_pad(kv_len) / kQkT;
+    return align256((size_t)bh * ni_pad * 16) + align256((size_t)bh * ni_pad * kQKmax * qk_dp64(g)) + 256 +
+           align256((size_t)bh * (ni_pad / kQkT) * nKB * 16);
+}
+
+bool qk_uses_mfma(const Tensor &q) { return q.dtype == 1; }
+
+hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws,
+                           hipStream_t s) {
+    ProfScope prof_("qk_prep", s);
+    const int64_t Dp64 = qk_dp64(g), len = kv_hi - kv_lo;
+    const int64_t kv_pad = qk_pad(len), rows = g.B * g.Hkv * kv_pad;
+    int4 *info = (int4 *)ws;
+    int8_t *dig = (int8_t *)ws + align256((size_t)rows * 16);
+    hipLaunchKernelGGL(k_qkprep<true>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const bf16_t *)k.data,
+                       k.sB, k.sH, k.sS, g.Hkv, g.D, Dp64, kv_lo, len, kv_pad, rows, info, dig);
+    return hipGetLastError();
+}
+
+hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g, const void *kprep, void *chunk_ws,
+                            int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, float *scores,
+                            uint32_t *rowmax_keys, int64_t key_rows, int64_t key_row0, hipStream_t s) {
+    const int64_t ni = i1 - i0;
+    if (ni <= 0 || kv_hi <= kv_lo) return hipSuccess;
+    if (g.D > 256) return hipErrorInvalidValue;
+    const int64_t Dp64 = qk_dp64(g), ni_pad = padded_rows(ni), bh = g.B * g.Hq;
+    const int64_t len = kv_hi - kv_lo, kv_pad = qk_pad(len);
+    const int64_t ntiles = ni_pad / kQkT, nKB = kv_pad / kQkT;
+    char *c = (char *)chunk_ws;
+    int4 *qinfo = (int4 *)c;
+    c += align256((size_t)bh * ni_pad * 16);
+    int8_t *qdig = (int8_t *)c;
+    c += align256((size_t)bh * ni_pad * kQKmax * Dp64);
+    int *nfix = (int *)c;
+    c += 256;
+    int4 *fixlist = (int4 *)c;
+    const int64_t krows = g.B * g.Hkv * kv_pad;
+    hipError_t e;
+    {
+        ProfScope prof_("qk_prep", s);
+        hipLaunchKernelGGL(k_qkprep<false>, dim3((unsigned)((bh * ni_pad + 3) / 4)), dim3(256), 0, s,
+                           (const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad, bh * ni_pad,
+                           qinfo, qdig);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_fill_u32((uint32_t *)nfix, 1, 0u, s)) != hipSuccess) return e;
+    }
+    QkArgs a{};
+    a.qdig = qdig;
+    a.kdig = (const int8_t *)kprep + align256((size_t)krows * 16);
+    a.qinfo = qinfo;
+    a.kinfo = (const int4 *)kprep;
+    a.Dp64 = Dp64;
+    a.ni = ni;
+    a.ni_pad = ni_pad;
+    a.i0 = i0;
+    a.kv_lo = kv_lo;
+    a.kv_hi = kv_hi;
+    a.kv_pad = kv_pad;
+    a.Hq = g.Hq;
+    a.Hkv = g.Hkv;
+    a.group = g.Hq / g.Hkv;
+    a.causal = g.causal;
+    a.scale = g.scale;
+    a.scores = scores;
+    a.W = kv_hi - kv_lo;
+    a.keys = rowmax_keys;
+    a.key_rows = key_rows;
+    a.key_row0 = key_row0;
+    a.nfix = nfix;
+    a.fixlist = fixlist;
+    a.nKB = nKB;
+    {
+        ProfScope prof_("scores", s);
+        // a tile's key blocks spread over up to 64 workgroups, at least 4 blocks per wave
+        const int64_t per_wg = 4 * kQkWaves;
+        const int64_t parts = std::max<int64_t>(1, std::min<int64_t>((nKB + per_wg - 1) / per_wg, 64));
+        dim3 grid((unsigned)parts, (unsigned)ntiles, (unsigned)bh);
+        switch (Dp64 / 64) {
+            case 1: hipLaunchKernelGGL(k_qk_mfma<1>, grid, dim3(64 * kQkWaves), 0, s, a); break;
+            case 2: hipLaunchKernelGGL(k_qk_mfma<2>, grid, dim3(64 * kQkWaves), 0, s, a); break;
+            case 3: hipLaunchKernelGGL(k_qk_mfma<3>, grid, dim3(64 * kQkWaves), 0, s, a); break;
+            default: hipLaunchKernelGGL(k_qk_mfma<4>, grid, dim3(64 * kQkWaves), 0, s, a); break;
+        }
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    ProfScope prof_("scores_fix", s);
+    const int64_t items = bh * ntiles * nKB;
+    hipLaunchKernelGGL(k_qk_fix, dim3((unsigned)std::min<int64_t>(items, 4096)), dim3(256), 0, s, a,
+                       (const bf16_t *)q.data, q.sB, q.sH, q.sS, (const bf16_t *)k.data, k.sB, k.sH, k.sS, g.D);
+    return hipGetLastError();
+}
+
+}  // namespace det

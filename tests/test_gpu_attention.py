@@ -324,3 +324,22 @@ def test_matrix_core_and_generic_paths_bit_identical(A, oracle, case):
     assert torch.equal(fast, gen)
     assert torch.equal(nf, ng) and torch.equal(df, dg)
     assert_bits_equal(fast, oracle.det_attn(q, k, v, causal, scale), case)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_scores_outlier_rows_take_the_fp64_chain(A, oracle, causal):
+    """Rows whose entries span many binades break the matrix-core exactness
+    bound (or need more than four int8 digits); those items are recomputed by
+    the fp64 chain and must still match the oracle bit for bit."""
+    q, k, v = W.attn_inputs(601, 1, 4, 2, 96, 96, 128, torch.float32)
+    q[0, 1, 3, 5] = 1e-9
+    q[0, 2, 40, :7] = 3e-12
+    k[0, 0, 7, 9] = 2e-10
+    k[0, 1, 50, 100] = 5e-13
+    k[0, 1, 51, :] *= 1e6
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    ref = oracle.det_attn(q, k, v, causal, 0.02)
+    out = A.det_attn(*gpu(q, k, v), causal, 0.02)
+    assert_bits_equal(out, ref, "outliers")
+    m = A.rowmax(*gpu(q, k), 0, 96, causal, 0.02)
+    assert_bits_equal(m, oracle.attn_rowmax(q, k, 0, 96, causal, 0.02), "rowmax")
