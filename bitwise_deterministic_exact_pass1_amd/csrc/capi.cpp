@@ -111,12 +111,18 @@ AttnGeom geom(const det_tensor *q, const det_tensor *k, int causal, double scale
 }
 
 // Bump allocator over the caller's workspace.
+// Bump allocator over the caller's workspace.  Every region is checked
+// against the workspace size on the host: a layout that outgrows the size the
+// byte functions computed is reported (over) before any kernel could touch it.
 struct Carver {
     char *p;
+    size_t cap;
     size_t used = 0;
+    bool over = false;
     template <typename T> T *take(size_t count) {
         T *r = (T *)(p + used);
         used += align256(count * sizeof(T));
+        if (used > cap) over = true;
         return r;
     }
 };
@@ -159,22 +165,21 @@ size_t bytes_rowmax(const AttnGeom &g, bool mfma, int64_t ni, int64_t kv_len) {
 size_t bytes_accumulate(const AttnGeom &g, bool mfma, int64_t ni, int64_t W) {
     const int64_t bh = g.B * g.Hq;
     return vprep_bytes(g, W) + score_fixed_bytes(g, mfma, W) + score_chunk_bytes(g, mfma, ni, W) +
-           align256((size_t)bh * ni * W * 4) + align256((size_t)bh * ((ni + 31) / 32) * 4) +
-           pv_digit_bytes(g, ni, W);
+           align256((size_t)bh * ni * W * 4) + align256((size_t)bh * ((ni + 31) / 32) * 4);
 }
 
 size_t bytes_fused(const AttnGeom &g, bool mfma, int64_t ni) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, g.Skv) + score_fixed_bytes(g, mfma, g.Skv) + score_chunk_bytes(g, mfma, ni, g.Skv) +
            align256((size_t)rows * 4) + align256((size_t)rows * g.Skv * 4) + align256((size_t)rows * 4) +
-           pv_fallback_bytes(g, ni) + pv_digit_bytes(g, ni, g.Skv);
+           pv_fallback_bytes(g, ni);
 }
 
 size_t bytes_sharded(const AttnGeom &g, bool mfma, int64_t ni, int64_t maxlen) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, maxlen) + score_fixed_bytes(g, mfma, maxlen) + score_chunk_bytes(g, mfma, ni, maxlen) +
            align256((size_t)rows * 4) + align256((size_t)rows * maxlen * 4) + 2 * align256((size_t)rows * 4) +
-           align256((size_t)bh * ((ni + 31) / 32) * 4) + pv_digit_bytes(g, ni, maxlen) +
+           align256((size_t)bh * ((ni + 31) / 32) * 4) +
            2 * (align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8));
 }
 
@@ -186,7 +191,7 @@ VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
     v.colmin = c.take<int>(bhk * Dp32);
     v.colgrid = c.take<int>(bhk * Dp32);
     v.grpB = c.take<int>(bhk * nG);
-    v.slices = c.take<char>(bhk * nG * nKB * 6 * 1024);
+    v.slices = c.take<char>(vslice_bytes(g, kv_len));
     v.Dp32 = Dp32;
     v.nKB = nKB;
     return v;
@@ -281,14 +286,15 @@ int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int
     hipStream_t s = (hipStream_t)stream;
     const Tensor tq = to_t(q), tk = to_t(k);
     const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
-    Carver c0{(char *)workspace};
+    Carver c0{(char *)workspace, ws_bytes};
     void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
+    // per-chunk regions, sized for the largest chunk and reused by every chunk
+    void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, W));
+    uint32_t *keys = c0.take<uint32_t>(bh * chunk);
+    if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
     HIP_TRY(prep_keys(tk, g, mf, kprep, kv_lo, kv_hi, s), "prepare k");
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        Carver c = c0;
-        void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, W));
-        uint32_t *keys = c.take<uint32_t>(bh * ni);
         HIP_TRY(launch_fill_u32(keys, bh * ni, kKeyNegInf, s), "fill");
         HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, kv_lo, kv_hi, nullptr, keys, ni, i0, s), "scores");
         HIP_TRY(launch_keys_to_f32(keys, rowmax, bh, ni, g.Sq, i0, s), "rowmax");
@@ -321,28 +327,28 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     hipStream_t s = (hipStream_t)stream;
     const Tensor tq = to_t(q), tk = to_t(k), tv = to_t(v);
     const int64_t bh = g.B * g.Hq, rows = bh * g.Sq;
+    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need);
+    Carver c0{(char *)workspace, ws_bytes};
+    VPrep vp = carve_vprep(c0, g, W);
+    void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
+    // per-chunk regions, sized for the largest chunk and reused by every chunk
+    void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, W));
+    float *sc = c0.take<float>(bh * chunk * W);
+    int *flags = c0.take<int>(bh * ((chunk + 31) / 32));
+    if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
     if (!add_into) {
         HIP_TRY(launch_fill_i64(num, kNumDigits * rows * g.D, 0, s), "fill num");
         HIP_TRY(launch_fill_i64(den, kDenDigits * rows, 0, s), "fill den");
     }
-    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need);
-    Carver c0{(char *)workspace};
-    VPrep vp = carve_vprep(c0, g, W);
-    void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
     if (W > 0) {
         HIP_TRY(launch_vprep(tv, g, kv_lo, kv_hi, vp, s), "prepare v");
         HIP_TRY(prep_keys(tk, g, mf, kprep, kv_lo, kv_hi, s), "prepare k");
     }
     const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq && W > 0; i0 += chunk) {
-        const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        Carver c = c0;
-        void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, W));
-        float *sc = c.take<float>(bh * ni * W);
-        int *flags = c.take<int>(bh * ((ni + 31) / 32));
-        char *dws = c.take<char>(pv_digit_bytes(g, ni, W));
+        const int64_t i1 = std::min(g.Sq, i0 + chunk);
         HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, kv_lo, kv_hi, sc, nullptr, 0, 0, s), "scores");
-        HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, dws, nullptr, nullptr,
+        HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr,
                           nullptr, num, den, rows, g.Sq, 0, ff, s),
                 "deposit");
     }
@@ -408,28 +414,28 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     const Tensor tq = to_t(q), tk = to_t(k), tv = to_t(v);
     const OutView ov{o->data, o->sB, o->sH, o->sS};
     const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
-    Carver c0{(char *)workspace};
+    Carver c0{(char *)workspace, ws_bytes};
     VPrep vp = carve_vprep(c0, g, g.Skv);
     void *kprep = c0.take<char>(score_fixed_bytes(g, mf, g.Skv));
+    // per-chunk regions, sized for the largest chunk and reused by every chunk
+    const int64_t crows = bh * chunk, ctiles = (chunk + 31) / 32;
+    void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, g.Skv));
+    uint32_t *keys = c0.take<uint32_t>(crows);
+    float *sc = c0.take<float>(crows * g.Skv);
+    float *rm = c0.take<float>(crows);
+    int *flags = c0.take<int>(bh * ctiles);
+    int64_t *fnum = c0.take<int64_t>(kNumDigits * bh * ctiles * 32 * g.D);
+    int64_t *fden = c0.take<int64_t>(kDenDigits * bh * ctiles * 32);
+    if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
     HIP_TRY(launch_vprep(tv, g, 0, g.Skv, vp, s), "prepare v");
     HIP_TRY(prep_keys(tk, g, mf, kprep, 0, g.Skv, s), "prepare k");
     const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
-        const int64_t tiles = (ni + 31) / 32;
-        Carver c = c0;
-        void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, g.Skv));
-        uint32_t *keys = c.take<uint32_t>(rows);
-        float *sc = c.take<float>(rows * g.Skv);
-        float *rm = c.take<float>(rows);
-        int *flags = c.take<int>(bh * tiles);
-        int64_t *fnum = c.take<int64_t>(kNumDigits * bh * tiles * 32 * g.D);
-        int64_t *fden = c.take<int64_t>(kDenDigits * bh * tiles * 32);
-        char *dws = c.take<char>(pv_digit_bytes(g, ni, g.Skv));
         HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
         HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, 0, g.Skv, sc, keys, ni, i0, s), "scores");
         HIP_TRY(launch_keys_to_f32(keys, rm, bh, ni, ni, 0, s), "rowmax");
-        HIP_TRY(launch_pv(tv, g, vp, sc, rm, ni, i0, i0, i1, 0, g.Skv, flags, dws, fnum, fden, &ov, nullptr, nullptr,
+        HIP_TRY(launch_pv(tv, g, vp, sc, rm, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr, nullptr,
                           0, 0, 0, ff, s),
                 "deposit");
     }
@@ -498,7 +504,7 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
     const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
-        Carver c{(char *)workspace};
+        Carver c{(char *)workspace, ws_bytes};
         VPrep vp = carve_vprep(c, g, ml);
         void *kprep = c.take<char>(score_fixed_bytes(g, mf, ml));
         void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, ml));
@@ -507,11 +513,11 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         float *rm_acc = c.take<float>(rows);
         float *rm_part = c.take<float>(rows);
         int *flags = c.take<int>(bh * ((ni + 31) / 32));
-        char *dws = c.take<char>(pv_digit_bytes(g, ni, ml));
         int64_t *num_acc = c.take<int64_t>(kNumDigits * rows * g.D);
         int64_t *den_acc = c.take<int64_t>(kDenDigits * rows);
         int64_t *num_part = c.take<int64_t>(kNumDigits * rows * g.D);
         int64_t *den_part = c.take<int64_t>(kDenDigits * rows);
+        if (c.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
         // pass 1: rowmax of each shard, composed by max
         HIP_TRY(launch_fill_u32((uint32_t *)rm_acc, rows, 0xff800000u, s), "fill rowmax");  // -inf
         for (int32_t a = 0; a < n_splits; ++a) {
@@ -535,7 +541,7 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
                 HIP_TRY(launch_vprep(tv, g, l, h, vp, s), "prepare v");
                 HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
                 HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
-                HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, ni, i0, i0, i1, l, h, flags, dws, nullptr, nullptr, nullptr,
+                HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
                                   num_part, den_part, rows, ni, i0, ff, s),
                         "deposit");
             }

@@ -26,32 +26,52 @@ constexpr double kSqrt2 = 0x1.6a09e667f3bcdp+0;
 // exp_det(t), t <= 0: t = n*ln2 + r with n = rint(t/ln2) (ties to even) and r
 // from two fma steps against the split ln2; e^r by its Taylor series to r^13
 // (coefficients RN64(1/k!)) in Horner form; times 2^n.  Zero below -104,
-// where the f32 weight underflows to zero anyway.
-__device__ __forceinline__ double exp_det(double t) {
+// where the f32 weight underflows to zero anyway.  FMA performs the Horner
+// steps: any correctly rounded binary64 fused multiply-add.
+template <class FMA>
+__device__ __forceinline__ double exp_det_with(double t, FMA fma_step) {
     if (t < -104.0) return 0.0;
     const double n = rint(t * kInvLn2);
     double r = fma(-n, kLn2Hi, t);
     r = fma(-n, kLn2Lo, r);
-    double p = 0x1.6124613a86d09p-33;      // 1/13!
-    p = fma(p, r, 0x1.1eed8eff8d898p-29);  // 1/12!
-    p = fma(p, r, 0x1.ae64567f544e4p-26);  // 1/11!
-    p = fma(p, r, 0x1.27e4fb7789f5cp-22);  // 1/10!
-    p = fma(p, r, 0x1.71de3a556c734p-19);  // 1/9!
-    p = fma(p, r, 0x1.a01a01a01a01ap-16);  // 1/8!
-    p = fma(p, r, 0x1.a01a01a01a01ap-13);  // 1/7!
-    p = fma(p, r, 0x1.6c16c16c16c17p-10);  // 1/6!
-    p = fma(p, r, 0x1.1111111111111p-7);   // 1/5!
-    p = fma(p, r, 0x1.5555555555555p-5);   // 1/4!
-    p = fma(p, r, 0x1.5555555555555p-3);   // 1/3!
-    p = fma(p, r, 0.5);                    // 1/2!
-    p = fma(p, r, 1.0);                    // 1/1!
-    p = fma(p, r, 1.0);                    // 1/0!
+    double p = 0x1.6124613a86d09p-33;             // 1/13!
+    p = fma_step(p, r, 0x1.1eed8eff8d898p-29);  // 1/12!
+    p = fma_step(p, r, 0x1.ae64567f544e4p-26);  // 1/11!
+    p = fma_step(p, r, 0x1.27e4fb7789f5cp-22);  // 1/10!
+    p = fma_step(p, r, 0x1.71de3a556c734p-19);  // 1/9!
+    p = fma_step(p, r, 0x1.a01a01a01a01ap-16);  // 1/8!
+    p = fma_step(p, r, 0x1.a01a01a01a01ap-13);  // 1/7!
+    p = fma_step(p, r, 0x1.6c16c16c16c17p-10);  // 1/6!
+    p = fma_step(p, r, 0x1.1111111111111p-7);   // 1/5!
+    p = fma_step(p, r, 0x1.5555555555555p-5);   // 1/4!
+    p = fma_step(p, r, 0x1.5555555555555p-3);   // 1/3!
+    p = fma_step(p, r, 0.5);                    // 1/2!
+    p = fma_step(p, r, 1.0);                    // 1/1!
+    p = fma_step(p, r, 1.0);                    // 1/0!
     return ldexp(p, (int)n);
 }
 
+struct FmaPlain {
+    __device__ __forceinline__ double operator()(double a, double b, double c) const { return fma(a, b, c); }
+};
+
+// v_fma_f64 with three vector-register sources: the same IEEE operation as
+// fma().  In a loop the constant addends then stay in registers hoisted out
+// of it; plain fma() pairs each v_fmac_f64 with a copy of the constant.
+struct FmaVreg {
+    __device__ __forceinline__ double operator()(double a, double b, double c) const {
+        double d;
+        asm("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+        return d;
+    }
+};
+
+__device__ __forceinline__ double exp_det(double t) { return exp_det_with(t, FmaPlain{}); }
+
 // w = RN32(exp_det(RN64(s - m))).
-__device__ __forceinline__ float weight(float s, float m) {
-    return (float)exp_det((double)s - (double)m);
+template <class FMA = FmaPlain>
+__device__ __forceinline__ float weight(float s, float m, FMA f = FMA{}) {
+    return (float)exp_det_with((double)s - (double)m, f);
 }
 
 // log_det(x), x >= 1: x = f 2^e with f folded into (sqrt2/2, sqrt2];

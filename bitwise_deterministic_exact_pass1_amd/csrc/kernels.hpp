@@ -96,9 +96,9 @@ struct VPrep {
     int64_t Dp32, nKB;
 };
 size_t vprep_bytes(const AttnGeom &g, int64_t kv_len);
+// bytes of the V digit slices within vprep_bytes
+size_t vslice_bytes(const AttnGeom &g, int64_t kv_len);
 size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i);
-// W digit blocks, their nonzero masks and the exact row sums of one chunk.
-size_t pv_digit_bytes(const AttnGeom &g, int64_t rows_i, int64_t kv_len);
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
                         hipStream_t s);
 // Exact NUM/DEN of query rows [i0,i1) against keys [kv_lo,kv_hi) from stored
@@ -108,9 +108,8 @@ hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64
 // matrix-core path cannot represent exactly are redone by the generic path.
 hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
                      int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
-                     int *flags, void *digit_ws, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num,
-                     int64_t *den, int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback,
-                     hipStream_t s);
+                     int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
+                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s);
 
 hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hipStream_t s);
 hipError_t launch_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int n_digits,

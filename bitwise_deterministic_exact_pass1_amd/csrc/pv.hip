@@ -30,7 +30,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kAw = 6;                  // digits of W
 constexpr int kSw = 8 * kAw - 2;        // W = w * 2^46, |W| <= 2^46 fits six balanced digits
-constexpr int kBmax = 6;                // at most six digits of a V column (48-bit integers)
+constexpr int kBmax = 5;                // at most five digits of a V column (40-bit integers)
 constexpr int kNC = kAw + kBmax - 1;    // shift classes s = a + b
 constexpr int kKB = 32;                 // keys per block (the MFMA K)
 constexpr int kCarryEvery = 256;        // blocks (8192 keys) between carry passes
@@ -193,12 +193,9 @@ struct PvArgs {
     int causal;
     const v4i *vsl;
     const int *colgrid, *grpB;
-    int *flags;  // [bh][ntiles]
+    int *flags;  // [bh][ntiles]: 1 = the tile is left to the generic path
     int64_t ntiles;
     int force_fallback;
-    v4i *wdig;          // [bh][ntiles][nKB][kAw][64] digit blocks of W
-    uint32_t *wmask;    // [bh][ntiles][nKB] nonzero-digit masks
-    int64_t *den_rows;  // [bh][ntiles*32] exact sum of W per row
     // fused output
     float *o;
     int64_t osB, osH, osS;
@@ -207,143 +204,282 @@ struct PvArgs {
     int64_t plane_rows, rows_per_bh, row0;
 };
 
-// Weights of one 32-row x 32-key block: w = RN32(exp_det(s - m)), W = w 2^46,
-// its six balanced digits written in MFMA lane order (lane l byte p holds
-// key 16(l/32)+p of row l%32), the nonzero-digit mask of the block, and the
-// exact row sums of W.  A weight the grid cannot hold flags the tile.
-__global__ __launch_bounds__(256) void k_wdigits(PvArgs A) {
-    const int tid = threadIdx.x;
-    const int64_t kb = blockIdx.x, tile = blockIdx.y, bh = blockIdx.z;
-    const int64_t it0 = A.i0 + tile * 32, i_end = A.i0 + A.ni;
-    const int64_t jlo = A.kv_lo + kb * kKB;
-    const int64_t jhi = A.causal ? std::min<int64_t>(A.kv_hi, it0 + 32) : A.kv_hi;
-    if (jlo >= jhi) return;  // block above the causal diagonal: never read
-    __shared__ uint32_t smask;
-    if (tid == 0) smask = 0;
-    __syncthreads();
-    const int r = tid >> 3, q = tid & 7;
-    const int64_t i = it0 + r;
-    const bool rowok = i < i_end;
-    float m = 0.0f;
-    const float *srow = A.scores;
-    if (rowok) {
-        m = A.rowmax[bh * A.rm_rows + (i - A.rm_row0)];
-        srow = A.scores + (bh * A.ni + (i - A.i0)) * A.W - A.kv_lo;
-    }
-    int64_t Wq[4];
-    int64_t wsum = 0;
-    bool bad = false;
+// Weights of one 32-key block for the calling thread: KPT consecutive keys of
+// one row with scores sc[]; the first nv of them are visible.  w =
+// RN32(exp_det(s - m)) and W = w 2^46 = M << (E + 23) for the f32 w =
+// M 2^(E-23), an integer for 2^-23 <= w <= 1 (other nonzero weights set bad).
+// The six balanced base-256 digits of W are the bytes of W + 0x808080808080
+// with their top bit flipped (digit set [-128, 127], the unique such
+// representation).  Digit a of the KPT keys goes to dst + a*1024 (MFMA lane
+// order, set up by the caller).  Returns the mask of digits nonzero for this
+// thread and adds W to wsum.
+template <int KPT>
+__device__ __forceinline__ uint32_t block_weights(const float (&sc)[KPT], float m, int nv, uint8_t *dst,
+                                                  int64_t &wsum, bool &bad) {
+    uint64_t U[KPT];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t j = jlo + 4 * q + u;
-        float w = 0.0f;
-        if (rowok && j < jhi && (!A.causal || j <= i)) w = weight(srow[j], m);
-        const double ws = ldexp((double)w, kSw);
-        const int64_t Wi = (int64_t)ws;
-        if ((double)Wi != ws || Wi > (1ll << kSw)) bad = true;
-        Wq[u] = Wi;
-        wsum += Wi;
+    for (int u = 0; u < KPT; ++u) {
+        const float w = u < nv ? weight(sc[u], m, FmaVreg{}) : 0.0f;
+        const uint32_t bits = __float_as_uint(w);
+        // 0x34000000 = 2^-23, 0x3f800000 = 1
+        if (bits != 0 && (bits < 0x34000000u || bits > 0x3f800000u)) bad = true;
+        const uint64_t Wi =
+            bits ? ((uint64_t)((bits & 0x7fffffu) | 0x800000u)) << (((bits >> 23) - 104u) & 63u) : 0ull;
+        wsum += (int64_t)Wi;
+        U[u] = Wi + 0x808080808080ull;
     }
-    // row sums: the 8 threads of a row are 8 consecutive lanes
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) wsum += __shfl_xor(wsum, off, 64);
-    if (q == 0 && wsum) atomicAdd((unsigned long long *)&A.den_rows[bh * A.ntiles * 32 + tile * 32 + r],
-                                  (unsigned long long)wsum);
-    if (bad) A.flags[bh * A.ntiles + tile] = 1;
-    uint8_t *blk = (uint8_t *)(A.wdig + ((bh * A.ntiles + tile) * A.nKB + kb) * kAw * 64);
-    const int lrow = r + 32 * (q >> 2), boff = (q & 3) * 4;
     uint32_t nzm = 0;
 #pragma unroll
     for (int a = 0; a < kAw; ++a) {
-        uint32_t pack = 0;
+        uint32_t word[KPT / 4] = {};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t c = ((Wq[u] & 255) ^ 128) - 128;
-            Wq[u] = (Wq[u] - c) >> 8;
-            pack |= ((uint32_t)(c & 255)) << (8 * u);
+        for (int u = 0; u < KPT; ++u) word[u / 4] |= ((uint32_t)(U[u] >> (8 * a)) & 255u) << (8 * (u % 4));
+        uint32_t any = 0;
+#pragma unroll
+        for (int t = 0; t < KPT / 4; ++t) {
+            word[t] ^= 0x80808080u;
+            any |= word[t];
+            ((uint32_t *)(dst + a * 64 * 16))[t] = word[t];
         }
-        if (pack) nzm |= 1u << a;
-        *(uint32_t *)(blk + (a * 64 + lrow) * 16 + boff) = pack;
+        if (any) nzm |= 1u << a;
     }
-    if (nzm) atomicOr(&smask, nzm);
-    __syncthreads();
-    if (tid == 0) A.wmask[(bh * A.ntiles + tile) * A.nKB + kb] = smask;
+    return nzm;
 }
 
-// One wave per (row tile, 32-dim group): C_s += digits(W) x digits(V) on the
-// matrix cores over the tile's keys, then the exact value is finalized (o) or
-// added into digit planes.  Tiles flagged by k_wdigits or by a V group that
-// needs more than kBmax digits are left to the generic path.
-template <bool FUSED>
-__global__ __launch_bounds__(64, 2) void k_pv_mfma(PvArgs A) {
-    const int lane = threadIdx.x;
-    const int64_t tile = blockIdx.x, G = blockIdx.y, bh = blockIdx.z;
-    const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
-    const int64_t it0 = A.i0 + tile * 32, i_end = A.i0 + A.ni;
-    const int64_t nG = A.Dp32 / 32;
-    const int64_t jhi = A.causal ? std::min<int64_t>(A.kv_hi, it0 + 32) : A.kv_hi;
-    const int64_t nblk = jhi > A.kv_lo ? (jhi - A.kv_lo + kKB - 1) / kKB : 0;
-    int badtile = A.force_fallback || A.flags[bh * A.ntiles + tile];
-    for (int64_t g = 0; g < nG; ++g) badtile |= A.grpB[bhk * nG + g] > kBmax;
-    if (badtile) {
-        if (lane == 0 && G == 0) A.flags[bh * A.ntiles + tile] = 1;
+constexpr int kPW = 4;  // producer waves of the pass-2 kernel
+
+// OR of a kAw-bit mask over the wave, by one ballot per bit (no LDS traffic).
+__device__ __forceinline__ uint32_t wave_or_mask(uint32_t nz) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int a = 0; a < kAw; ++a)
+        if (__ballot((nz >> a) & 1u)) r |= 1u << a;
+    return r;
+}
+
+// LDS of the pass-2 kernel: W digits of two key blocks, the producers'
+// staged scores of two blocks, digit masks, row sums, the bad-tile flag.
+struct PvShared {
+    uint8_t dig[2][kAw * 1024];
+    float sc[2][32][32];
+    uint32_t mask[2][kPW];
+    int64_t den[32];
+    int bad;
+};
+
+// Pass 2 of a 32-row tile for the 32-dim groups G0 .. G0+NG-1.
+//
+// NG consumer waves, one per group, run C_s += W_a x V_b (s = a + b) on the
+// matrix cores, with their V digits fetched from global memory one block
+// ahead; kPW producer waves turn the next 32-key block's scores into W
+// digits in LDS meanwhile (double buffered, one barrier per block).  The two
+// roles run separate code with the same barriers, so the weight arithmetic on
+// the vector ALUs overlaps the matrix-core work and neither role's registers
+// are held in the other.  Producers stage the scores of the block after next
+// in LDS, so every global load has a whole block of arithmetic to arrive in.
+// DEN (the exact sum of W per row) stays in the producers' registers.  At the
+// end the consumers finalize the exact NUM and DEN to o or add them into
+// digit planes.  A tile whose weights or V columns do not fit the grids is
+// flagged for the generic path and produces no output here.
+
+struct PvTile {
+    int64_t b, hq, bhk, it0, i_end, nG, jhi;
+    int nblk;
+    bool badv;  // a V group the grid cannot hold: the whole tile takes the generic path
+};
+
+__device__ __forceinline__ PvTile pv_tile_of(const PvArgs &A, int64_t bh, int64_t tile) {
+    PvTile T;
+    T.b = bh / A.Hq;
+    T.hq = bh % A.Hq;
+    T.bhk = T.b * A.Hkv + T.hq / A.group;
+    T.it0 = A.i0 + tile * 32;
+    T.i_end = A.i0 + A.ni;
+    T.nG = A.Dp32 / 32;
+    T.jhi = A.causal ? std::min<int64_t>(A.kv_hi, T.it0 + 32) : A.kv_hi;
+    T.nblk = T.jhi > A.kv_lo ? (int)((T.jhi - A.kv_lo + kKB - 1) / kKB) : 0;
+    int bad = A.force_fallback;
+    for (int64_t g = 0; g < T.nG; ++g) bad |= A.grpB[T.bhk * T.nG + g] > kBmax;
+    T.badv = bad;
+    return T;
+}
+
+// Producer side of one tile: thread ptid of the kPW producer waves.
+template <int NG>
+__device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t tile, int ptid, PvShared &S) {
+    constexpr int NPT = 64 * kPW;  // producer threads
+    constexpr int TPR = NPT / 32;  // producer threads per row
+    constexpr int KPT = 32 / TPR;  // keys per producer thread and block
+    const PvTile T = pv_tile_of(A, bh, tile);
+    if (T.badv) return;
+    const int lane = ptid & 63, pw = ptid >> 6;
+    const int r = ptid / TPR, k0 = (ptid % TPR) * KPT;
+    const int dofs = ((r + 32 * (k0 >> 4)) * 16) + (k0 & 15);
+    const int64_t i = T.it0 + r;
+    const bool rowok = i < T.i_end;
+    const float m = rowok ? A.rowmax[bh * A.rm_rows + (i - A.rm_row0)] : 0.0f;
+    const float *srow = A.scores + (bh * A.ni + (rowok ? i - A.i0 : 0)) * A.W - A.kv_lo;
+    // keys this row sees: [kv_lo, jend)
+    const int64_t jend = rowok ? (A.causal ? std::min<int64_t>(T.jhi, i + 1) : T.jhi) : A.kv_lo;
+    auto nvis = [&](int kb) {  // visible keys among this thread's KPT keys of block kb
+        const int64_t n = jend - (A.kv_lo + (int64_t)kb * kKB + k0);
+        return (int)std::max<int64_t>(0, std::min<int64_t>(KPT, n));
+    };
+    // the KPT scores of block kb; every load reads an in-range key (kv_hi > kv_lo
+    // whenever there is a block), the invisible ones are not used
+    const int64_t jlast = A.kv_hi - 1;
+    auto load_scores = [&](int kb, float (&x)[KPT]) {
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) x[u] = srow[std::min<int64_t>(A.kv_lo + (int64_t)kb * kKB + k0 + u, jlast)];
+    };
+    float *my0 = &S.sc[0][r][k0], *my1 = &S.sc[1][r][k0];
+    int64_t wsum = 0;
+    bool bad = false;
+    if (T.nblk > 0) {
+        float sc[KPT], s1[KPT];
+        load_scores(0, sc);
+        load_scores(1, s1);
+        const uint32_t nz = wave_or_mask(block_weights<KPT>(sc, m, nvis(0), S.dig[0] + dofs, wsum, bad));
+        if (lane == 0) S.mask[0][pw] = nz;
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) my1[u] = s1[u];
+    }
+    __syncthreads();
+    for (int kb = 0; kb < T.nblk; ++kb) {
+        const int nb = (kb & 1) ^ 1;
+        if (kb + 1 < T.nblk) {
+            float s2[KPT], sc[KPT];
+            load_scores(kb + 2, s2);
+            const float *cur = nb ? my1 : my0;
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) sc[u] = cur[u];
+            const uint32_t nz = wave_or_mask(block_weights<KPT>(sc, m, nvis(kb + 1), S.dig[nb] + dofs, wsum, bad));
+            if (lane == 0) S.mask[nb][pw] = nz;
+            float *nxt = nb ? my0 : my1;  // block kb+2 uses buffer (kb+2)&1
+#pragma unroll
+            for (int u = 0; u < KPT; ++u) nxt[u] = s2[u];
+        }
+        __syncthreads();
+    }
+    // exact row sums of W: the TPR threads of a row are consecutive lanes
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) wsum += __shfl_xor(wsum, off, 64);
+    if (ptid % TPR == 0) S.den[r] = wsum;
+    if (bad) S.bad = 1;
+    __syncthreads();
+}
+
+// Consumer side of one tile: wave `wave` (< NG) owns 32-dim group G0 + wave.
+template <bool FUSED, int NG>
+__device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, int64_t tile, int wave, PvShared &S) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const PvTile T = pv_tile_of(A, bh, tile);
+    if (T.badv) {
+        if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
         return;
     }
-    const int Bv = A.grpB[bhk * nG + G];
-    const v4i *vblk = A.vsl + ((bhk * nG + G) * A.nKB) * kBmax * 64 + lane;
-    const v4i *wblk = A.wdig + ((bh * A.ntiles + tile) * A.nKB) * kAw * 64 + lane;
-    const uint32_t *wm = A.wmask + (bh * A.ntiles + tile) * A.nKB;
-
+    if (tid == 0) S.bad = 0;
+    const int64_t G = G0 + wave;
+    const bool mine = G < T.nG;
+    const int Bv = mine ? A.grpB[T.bhk * T.nG + G] : 0;
+    const v4i *vb = A.vsl + ((T.bhk * T.nG + (mine ? G : 0)) * A.nKB) * kBmax * 64 + lane;
     v16i C[kNC];
 #pragma unroll
     for (int s = 0; s < kNC; ++s) C[s] = v16i{0};
-    for (int64_t kb = 0; kb < nblk; ++kb) {
-        const uint32_t mask = wm[kb];
-        v4i Bd[kBmax];
+    v4i Bn[kBmax];
 #pragma unroll
-        for (int s = 0; s < kBmax; ++s)
-            if (s < Bv) Bd[s] = vblk[(kb * kBmax + s) * 64];
+    for (int s = 0; s < kBmax; ++s)
+        if (s < Bv && T.nblk > 0) Bn[s] = vb[s * 64];
+    __syncthreads();
+    for (int kb = 0; kb < T.nblk; ++kb) {
+        const int buf = kb & 1;
+        if (mine) {
+            // this block's V digits (fetched one block earlier), then the next block's
+            v4i Bd[kBmax];
 #pragma unroll
-        for (int a = 0; a < kAw; ++a) {
-            if (mask & (1u << a)) {
-                const v4i Aa = wblk[(kb * kAw + a) * 64];
+            for (int s = 0; s < kBmax; ++s) Bd[s] = Bn[s];
+            __builtin_amdgcn_sched_barrier(0);
+            if (kb + 1 < T.nblk) {
 #pragma unroll
                 for (int s = 0; s < kBmax; ++s)
-                    if (s < Bv) C[a + s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aa, Bd[s], C[a + s], 0, 0, 0);
+                    if (s < Bv) Bn[s] = vb[((int64_t)(kb + 1) * kBmax + s) * 64];
             }
-        }
-        if ((kb % kCarryEvery) == kCarryEvery - 1) {
-            // carry each class into the next so every partial sum stays far below 2^31
+            uint32_t mask = 0;
 #pragma unroll
-            for (int s = 0; s < kNC - 1; ++s) {
-                const v16i c = C[s] >> 8;
-                C[s] -= c << 8;
-                C[s + 1] += c;
+            for (int w = 0; w < kPW; ++w) mask |= S.mask[buf][w];
+            mask = __builtin_amdgcn_readfirstlane(mask);
+#pragma unroll
+            for (int a = 0; a < kAw; ++a) {
+                if (mask & (1u << a)) {
+                    const v4i Aa = *(const v4i *)(S.dig[buf] + (a * 64 + lane) * 16);
+#pragma unroll
+                    for (int s = 0; s < kBmax; ++s)
+                        if (s < Bv) C[a + s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aa, Bd[s], C[a + s], 0, 0, 0);
+                }
+            }
+            if ((kb % kCarryEvery) == kCarryEvery - 1) {
+                // carry each class into the next so every partial sum stays far below 2^31
+#pragma unroll
+                for (int s = 0; s < kNC - 1; ++s) {
+                    const v16i c = C[s] >> 8;
+                    C[s] -= c << 8;
+                    C[s + 1] += c;
+                }
             }
         }
+        __syncthreads();
     }
+    __syncthreads();
+    if (S.bad) {
+        if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
+        return;
+    }
+    if (tid == 0) A.flags[bh * A.ntiles + tile] = 0;
+    if (!mine) return;
 
     const int64_t d = G * 32 + (lane & 31);
-    const int g = A.colgrid[bhk * A.Dp32 + d];
-    const int64_t *dsum_row = A.den_rows + bh * A.ntiles * 32 + tile * 32;
+    const int g = A.colgrid[T.bhk * A.Dp32 + d];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t i = it0 + row;
-        if (i >= i_end || d >= A.D) continue;
+    for (int rr = 0; rr < 16; ++rr) {
+        const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+        const int64_t io = T.it0 + row;
+        if (io >= T.i_end || d >= A.D) continue;
         __int128 num = 0;
 #pragma unroll
-        for (int s = kNC - 1; s >= 0; --s) num = num * 256 + (__int128)C[s][r];
-        const int64_t dsum = dsum_row[row];
+        for (int s = kNC - 1; s >= 0; --s) num = num * 256 + (__int128)C[s][rr];
+        const int64_t dsum = S.den[row];
         if (FUSED) {
             const double n64 = i128_to_f64(num, g - kSw);
             const double d64 = i128_to_f64((__int128)dsum, -kSw);
-            A.o[b * A.osB + hq * A.osH + i * A.osS + d] = (float)(n64 / d64);
+            A.o[T.b * A.osB + T.hq * A.osH + io * A.osS + d] = (float)(n64 / d64);
         } else {
-            const int64_t prow = bh * A.rows_per_bh + (i - A.row0);
+            const int64_t prow = bh * A.rows_per_bh + (io - A.row0);
             add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, A.num + prow * A.D + d, A.plane_rows * A.D);
             if (G == 0 && (lane & 31) == 0)
                 add_i128_digits<kDenDigits>((__int128)dsum, -kSw - kDenElo, A.den + prow, A.plane_rows);
+        }
+    }
+}
+
+// One workgroup per tile, or for causal attention per pair of tiles (x,
+// ntiles-1-x), whose key counts add up to the same total for every pair: the
+// whole grid then runs in one balanced round.  Both roles walk the same tiles
+// and meet at the same barriers.
+template <bool FUSED, int NG>
+__global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
+    __shared__ __align__(16) PvShared S;
+    const int64_t bh = blockIdx.y, x = blockIdx.x;
+    const int npass = (A.causal && x != A.ntiles - 1 - x) ? 2 : 1;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave >= NG) {
+        for (int pass = 0; pass < npass; ++pass) {
+            if (pass) __syncthreads();  // the LDS of the first tile is free again
+            pv_produce<NG>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, threadIdx.x - 64 * NG, S);
+        }
+    } else {
+        for (int pass = 0; pass < npass; ++pass) {
+            if (pass) __syncthreads();
+            pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave, S);
         }
     }
 }
@@ -431,11 +567,15 @@ __global__ __launch_bounds__(256) void k_tile_fallback(PvArgs A, const TV *__res
 
 // ---------------------------------------------------------------- launchers
 
+size_t vslice_bytes(const AttnGeom &g, int64_t kv_len) {
+    const int64_t bhk = g.B * g.Hkv, nG = (g.D + 31) / 32;
+    const int64_t nKB = std::max<int64_t>((kv_len + kKB - 1) / kKB, 1);
+    return align256((size_t)bhk * nG * nKB * kBmax * 1024);
+}
+
 size_t vprep_bytes(const AttnGeom &g, int64_t kv_len) {
     const int64_t bhk = g.B * g.Hkv, Dp32 = (g.D + 31) / 32 * 32, nG = Dp32 / 32;
-    const int64_t nKB = (kv_len + kKB - 1) / kKB;
-    return 3 * align256((size_t)bhk * Dp32 * 4) + align256((size_t)bhk * nG * 4) +
-           align256((size_t)bhk * nG * std::max<int64_t>(nKB, 1) * kBmax * 1024);
+    return 3 * align256((size_t)bhk * Dp32 * 4) + align256((size_t)bhk * nG * 4) + vslice_bytes(g, kv_len);
 }
 
 size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i) {
@@ -443,14 +583,6 @@ size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i) {
     return align256((size_t)bh * tiles * 4) +                                   // flags
            align256((size_t)kNumDigits * bh * tiles * 32 * g.D * 8) +           // fused scratch NUM
            align256((size_t)kDenDigits * bh * tiles * 32 * 8);                  // fused scratch DEN
-}
-
-size_t pv_digit_bytes(const AttnGeom &g, int64_t rows_i, int64_t kv_len) {
-    const int64_t tiles = (rows_i + 31) / 32, bh = g.B * g.Hq;
-    const int64_t nKB = std::max<int64_t>((kv_len + kKB - 1) / kKB, 1);
-    return align256((size_t)bh * tiles * nKB * kAw * 1024) +  // W digit blocks
-           align256((size_t)bh * tiles * nKB * 4) +            // nonzero masks
-           align256((size_t)bh * tiles * 32 * 8);              // row sums of W
 }
 
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
@@ -489,15 +621,17 @@ static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &v
                               int64_t *num_ws, int64_t *den_ws, hipStream_t s) {
     hipError_t e;
     {
-        ProfScope prof_("wdigits", s);
-        dim3 grid((unsigned)vp.nKB, (unsigned)a.ntiles, (unsigned)bh);
-        hipLaunchKernelGGL(k_wdigits, grid, dim3(256), 0, s, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    {
         ProfScope prof_("pv_mfma", s);
-        dim3 grid((unsigned)a.ntiles, (unsigned)(vp.Dp32 / 32), (unsigned)bh);
-        hipLaunchKernelGGL((k_pv_mfma<FUSED>), grid, dim3(64), 0, s, a);
+        const int64_t nG = vp.Dp32 / 32;
+        dim3 grid((unsigned)(a.causal ? (a.ntiles + 1) / 2 : a.ntiles), (unsigned)bh);
+        // at most four groups per launch; wider heads take several launches over
+        // the same tiles (the weights are recomputed, the digits are not shared)
+        for (int G0 = 0; G0 < nG; G0 += 4) {
+            if (nG == 1) hipLaunchKernelGGL((k_pv<FUSED, 1>), grid, dim3(64 * (1 + kPW)), 0, s, a, G0);
+            else if (nG == 2) hipLaunchKernelGGL((k_pv<FUSED, 2>), grid, dim3(64 * (2 + kPW)), 0, s, a, G0);
+            else hipLaunchKernelGGL((k_pv<FUSED, 4>), grid, dim3(64 * (4 + kPW)), 0, s, a, G0);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     ProfScope prof_("pv_fallback", s);
@@ -513,21 +647,12 @@ static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &v
 
 hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
                      int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
-                     int *flags, void *digit_ws, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num,
-                     int64_t *den, int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback,
-                     hipStream_t s) {
+                     int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
+                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s) {
     const int64_t ni = i1 - i0;
     if (ni <= 0) return hipSuccess;
+    if (vp.Dp32 > 256) return hipErrorInvalidValue;
     const int64_t ntiles = (ni + 31) / 32, bh = g.B * g.Hq;
-    hipError_t e = launch_fill_u32((uint32_t *)flags, bh * ntiles, 0u, s);
-    if (e != hipSuccess) return e;
-    char *dw = (char *)digit_ws;
-    v4i *wdig = (v4i *)dw;
-    dw += align256((size_t)bh * ntiles * vp.nKB * kAw * 1024);
-    uint32_t *wmask = (uint32_t *)dw;
-    dw += align256((size_t)bh * ntiles * vp.nKB * 4);
-    int64_t *den_rows = (int64_t *)dw;
-    if ((e = launch_fill_i64(den_rows, bh * ntiles * 32, 0, s)) != hipSuccess) return e;
     PvArgs a{};
     a.scores = scores;
     a.rowmax = rowmax;
@@ -551,9 +676,6 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     a.flags = flags;
     a.ntiles = ntiles;
     a.force_fallback = force_fallback;
-    a.wdig = wdig;
-    a.wmask = wmask;
-    a.den_rows = den_rows;
     if (o) {
         a.o = o->data;
         a.osB = o->sB;

@@ -112,3 +112,50 @@ def test_cross_entropy_argument_errors(lib):
     assert lib.det_ce_reduce(0x1000, 4, 3, 0x2000, None, 0, None) == -7
     assert lib.det_ce_backward(0x1000, 1, 4, 10, 10, 0x1, 0x2, 0x3, 0x4, 1, 0x5, 9, None) == -4
     assert lib.det_ce_backward(0x1000, 1, 4, 10, 10, 0x1, 0x2, 0x3, 0x4, 5, 0x5, 10, None) == -7
+
+
+def _no_device():
+    import torch
+    return torch.cuda.device_count() == 0  # counts devices without initialising one
+
+
+# (B, Hq, Hkv, S, D, causal) of the workloads; the key splits used with them
+_LAYOUT_CASES = [
+    (1, 2, 2, 128, 64, 0, [32] * 4),
+    (2, 8, 2, 1024, 128, 1, [64] * 16),
+    (1, 32, 8, 8192, 128, 1, [1024] * 8),
+    (1, 32, 8, 2048, 256, 1, [256] * 8),
+    (1, 56, 56, 37810, 128, 0, [64] * 590 + [50]),
+]
+
+
+@pytest.mark.skipif(not _no_device(), reason="passes dummy device pointers: only where no device exists")
+@pytest.mark.parametrize("dtype", [L.DET_F32, L.DET_BF16])
+@pytest.mark.parametrize("case", _LAYOUT_CASES, ids=lambda c: "x".join(map(str, c[:5])))
+def test_workspace_layout_fits_the_reported_size(lib, case, dtype):
+    """Each entry point carves its workspace on the host before it launches
+    anything; given exactly the size its *_workspace_size reports, it must get
+    past that (and then fail at its first HIP call, there being no device)
+    rather than report that its layout outgrew the workspace."""
+    B, Hq, Hkv, S, D, causal, splits = case
+    q = _t(B=B, H=Hq, S=S, D=D, dtype=dtype, data=0x100000)
+    k = _t(B=B, H=Hkv, S=S, D=D, dtype=dtype, data=0x200000)
+    v = _t(B=B, H=Hkv, S=S, D=D, dtype=dtype, data=0x300000)
+    o = L.Out(0x400000, Hq * S * D, S * D, D)
+    ws = 0x10000000
+    n = lib.det_attn_workspace_size(C.byref(q), C.byref(k), C.byref(v), causal)
+    rc = lib.det_attn(C.byref(q), C.byref(k), C.byref(v), causal, 0.125, C.byref(o), ws, n, None)
+    assert rc == -6, (rc, lib.det_last_error())
+    sp = (C.c_int64 * len(splits))(*splits)
+    n = lib.det_attn_sharded_workspace_size(C.byref(q), C.byref(k), C.byref(v), sp, len(splits), causal)
+    rc = lib.det_attn_sharded(C.byref(q), C.byref(k), C.byref(v), sp, len(splits), None, causal, 0.125,
+                              C.byref(o), ws, n, None)
+    assert rc == -6, (rc, lib.det_last_error())
+    lo, hi = S // 4, S // 4 + splits[0]
+    n = lib.det_attn_rowmax_workspace_size(C.byref(q), C.byref(k), lo, hi)
+    rc = lib.det_attn_rowmax(C.byref(q), C.byref(k), lo, hi, causal, 0.125, 0x500000, ws, n, None)
+    assert rc == -6, (rc, lib.det_last_error())
+    n = lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), lo, hi)
+    rc = lib.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), 0x500000, lo, hi, causal, 0.125, 0x600000,
+                                 0x700000, 0, ws, n, None)
+    assert rc == -6, (rc, lib.det_last_error())
