@@ -37,15 +37,21 @@ def visible_pairs(B, Hq, Sq, Skv, causal):
     return B * Hq * Sq * Skv
 
 
-def kernel_work(name, pairs, rows, D):
-    """(amount, unit, bound) of algorithmic work of one launch of `name`:
-    fp64 flops for the compute kernels, HBM bytes for the data-movement ones."""
-    if name == "scores":      # one fp64 fma chain of length D per pair
+def kernel_work(name, pairs, rows, D, kv_elems=0, q_elems=0):
+    """(amount, unit, bound) of algorithmic work of one launch of `name`: fp64
+    flops of the method's steps for the compute kernels (whatever units run
+    them), HBM bytes for the data-movement ones.  kv_elems / q_elems: elements
+    of one of K, V / of Q (bf16 or f32 inputs, counted at 2 bytes)."""
+    if name == "scores":      # pass 1: one fp64 fma chain of length D per pair
         return 2.0 * D * pairs, "flop", "alu"
+    if name == "pv_mfma":     # pass 2: exp_det (2 mul + 15 fma) and D exact product-accumulates
+        return (2.0 * D + 32.0) * pairs, "flop", "alu"
     if name == "weights":     # exp_det: 2 mul + 15 fma
         return 32.0 * pairs, "flop", "alu"
     if name == "deposit":     # D exact product-accumulates per pair, one fma each
         return 2.0 * D * pairs, "flop", "alu"
+    if name == "vprep":       # read V twice (statistics, digits), write five digit bytes per element
+        return kv_elems * (2 + 2 + 5), "byte", "hbm"
     if name == "finalize":    # read 14+9/D digits, write one f32 per output
         return rows * D * (112 + 72.0 / D + 4), "byte", "hbm"
     return None
@@ -107,7 +113,8 @@ def main():
         kernels[n]["share"] = prof[n][1] / total_k
     dominant = max(prof, key=lambda n: prof[n][1])
     per_step_launches = prof[dominant][0] / args.steps
-    work = kernel_work(dominant, pairs / per_step_launches, rows / per_step_launches, D)
+    work = kernel_work(dominant, pairs / per_step_launches, rows / per_step_launches, D,
+                       kv_elems=B * k.shape[1] * Skv * D / per_step_launches)
     avg_s = prof[dominant][1] / prof[dominant][0] / 1e3
     if work is not None:
         amount, unit, bound = work

@@ -138,22 +138,26 @@ __device__ __forceinline__ int clz128(unsigned __int128 u) {
     return hi ? __clzll((long long)hi) : 64 + __clzll((long long)lo);
 }
 
-// Correctly rounded (ties to even) binary64 of x * 2^e.
-__device__ __forceinline__ double i128_to_f64(__int128 x, int e) {
-    if (x == 0) return 0.0;
-    const bool neg = x < 0;
-    const unsigned __int128 u = neg ? (unsigned __int128)(-x) : (unsigned __int128)x;
-    const int nb = 128 - clz128(u);
+// Correctly rounded (ties to even) binary64 of N * 2^e for the 128-bit
+// integer N = hi * 2^64 + lo (hi signed, lo unsigned); N * 2^e must lie in
+// the normal range.  The top 64 bits of |N| are rounded by the (correctly
+// rounded) uint64 conversion, with every lower bit folded into bit 0 as a
+// sticky bit: bit 0 lies below the rounding position of a 64-bit value.
+__device__ __forceinline__ double i128_to_f64(int64_t hi, uint64_t lo, int e) {
+    const bool neg = hi < 0;
+    uint64_t mh = (uint64_t)hi, ml = lo;
+    if (neg) {  // |N|: two's complement negation over both words
+        ml = ~ml + 1;
+        mh = ~mh + (ml == 0 ? 1 : 0);
+    }
     double r;
-    if (nb <= 53) {
-        r = ldexp((double)(uint64_t)u, e);
+    if (mh == 0) {
+        r = ldexp((double)ml, e);
     } else {
-        const int sh = nb - 53;
-        uint64_t mant = (uint64_t)(u >> sh);
-        const unsigned __int128 rem = u & ((((unsigned __int128)1) << sh) - 1);
-        const unsigned __int128 half = ((unsigned __int128)1) << (sh - 1);
-        if (rem > half || (rem == half && (mant & 1))) mant += 1;
-        r = ldexp((double)mant, e + sh);
+        const int k = __clzll((long long)mh);
+        const uint64_t top = k ? (mh << k) | (ml >> (64 - k)) : mh;
+        const uint64_t rest = ml << k;
+        r = ldexp((double)(top | (rest != 0 ? 1ull : 0ull)), e + 64 - k);
     }
     return neg ? -r : r;
 }
@@ -263,8 +267,10 @@ struct PvShared {
     uint8_t dig[2][kAw * 1024];
     float sc[2][32][32];
     uint32_t mask[2][kPW];
-    int64_t den[32];
-    int bad;
+    // per tile parity, so that a tile's finalize overlaps the next tile's start
+    int64_t den[2][32];  // exact sum of W per row
+    double d64[2][32];   // RN64(DEN) of the row
+    int bad[2];
 };
 
 // Pass 2 of a 32-row tile for the 32-dim groups G0 .. G0+NG-1.
@@ -306,7 +312,8 @@ __device__ __forceinline__ PvTile pv_tile_of(const PvArgs &A, int64_t bh, int64_
 
 // Producer side of one tile: thread ptid of the kPW producer waves.
 template <int NG>
-__device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t tile, int ptid, PvShared &S) {
+__device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t tile, int ptid, int par,
+                                           PvShared &S) {
     constexpr int NPT = 64 * kPW;  // producer threads
     constexpr int TPR = NPT / 32;  // producer threads per row
     constexpr int KPT = 32 / TPR;  // keys per producer thread and block
@@ -364,21 +371,25 @@ __device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t 
     // exact row sums of W: the TPR threads of a row are consecutive lanes
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) wsum += __shfl_xor(wsum, off, 64);
-    if (ptid % TPR == 0) S.den[r] = wsum;
-    if (bad) S.bad = 1;
+    if (ptid % TPR == 0) {
+        S.den[par][r] = wsum;
+        S.d64[par][r] = ldexp((double)wsum, -kSw);  // exact scaling of the correctly rounded conversion
+    }
+    if (bad) S.bad[par] = 1;
     __syncthreads();
 }
 
 // Consumer side of one tile: wave `wave` (< NG) owns 32-dim group G0 + wave.
 template <bool FUSED, int NG>
-__device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, int64_t tile, int wave, PvShared &S) {
+__device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, int64_t tile, int wave, int par,
+                                           PvShared &S) {
     const int tid = threadIdx.x, lane = tid & 63;
     const PvTile T = pv_tile_of(A, bh, tile);
     if (T.badv) {
         if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
         return;
     }
-    if (tid == 0) S.bad = 0;
+    if (tid == 0) S.bad[par] = 0;
     const int64_t G = G0 + wave;
     const bool mine = G < T.nG;
     const int Bv = mine ? A.grpB[T.bhk * T.nG + G] : 0;
@@ -430,13 +441,21 @@ __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, 
         __syncthreads();
     }
     __syncthreads();
-    if (S.bad) {
+    if (S.bad[par]) {
         if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
         return;
     }
     if (tid == 0) A.flags[bh * A.ntiles + tile] = 0;
     if (!mine) return;
 
+    // carry the classes into bytes: C_0..C_8 in [0, 256), C_9 signed, so that
+    // NUM = C_9 2^72 + sum_{s<9} C_s 2^(8s) = hi 2^64 + lo
+#pragma unroll
+    for (int s = 0; s < kNC - 1; ++s) {
+        const v16i c = C[s] >> 8;
+        C[s] &= 255;
+        C[s + 1] += c;
+    }
     const int64_t d = G * 32 + (lane & 31);
     const int g = A.colgrid[T.bhk * A.Dp32 + d];
 #pragma unroll
@@ -444,19 +463,21 @@ __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, 
         const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
         const int64_t io = T.it0 + row;
         if (io >= T.i_end || d >= A.D) continue;
-        __int128 num = 0;
-#pragma unroll
-        for (int s = kNC - 1; s >= 0; --s) num = num * 256 + (__int128)C[s][rr];
-        const int64_t dsum = S.den[row];
+        const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) | ((uint32_t)C[2][rr] << 16) |
+                            ((uint32_t)C[3][rr] << 24);
+        const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) | ((uint32_t)C[6][rr] << 16) |
+                            ((uint32_t)C[7][rr] << 24);
+        const uint64_t lo = ((uint64_t)l1 << 32) | l0;
+        const int64_t hi = (int64_t)C[kNC - 1][rr] * 256 + C[kNC - 2][rr];
         if (FUSED) {
-            const double n64 = i128_to_f64(num, g - kSw);
-            const double d64 = i128_to_f64((__int128)dsum, -kSw);
-            A.o[T.b * A.osB + T.hq * A.osH + io * A.osS + d] = (float)(n64 / d64);
+            const double n64 = i128_to_f64(hi, lo, g - kSw);
+            A.o[T.b * A.osB + T.hq * A.osH + io * A.osS + d] = (float)(n64 / S.d64[par][row]);
         } else {
+            const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
             const int64_t prow = bh * A.rows_per_bh + (io - A.row0);
             add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, A.num + prow * A.D + d, A.plane_rows * A.D);
             if (G == 0 && (lane & 31) == 0)
-                add_i128_digits<kDenDigits>((__int128)dsum, -kSw - kDenElo, A.den + prow, A.plane_rows);
+                add_i128_digits<kDenDigits>((__int128)S.den[par][row], -kSw - kDenElo, A.den + prow, A.plane_rows);
         }
     }
 }
@@ -471,16 +492,14 @@ __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
     const int64_t bh = blockIdx.y, x = blockIdx.x;
     const int npass = (A.causal && x != A.ntiles - 1 - x) ? 2 : 1;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // No barrier between the tiles: the producers start the second tile while
+    // the consumers finalize the first (row sums and flags are kept per tile).
     if (wave >= NG) {
-        for (int pass = 0; pass < npass; ++pass) {
-            if (pass) __syncthreads();  // the LDS of the first tile is free again
-            pv_produce<NG>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, threadIdx.x - 64 * NG, S);
-        }
+        for (int pass = 0; pass < npass; ++pass)
+            pv_produce<NG>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, threadIdx.x - 64 * NG, pass, S);
     } else {
-        for (int pass = 0; pass < npass; ++pass) {
-            if (pass) __syncthreads();
-            pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave, S);
-        }
+        for (int pass = 0; pass < npass; ++pass)
+            pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave, pass, S);
     }
 }
 
