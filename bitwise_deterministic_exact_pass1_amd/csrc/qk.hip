@@ -92,43 +92,86 @@ __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, in
 }
 
 constexpr int kQkT = 16;     // rows and keys per matrix-core item
-constexpr int kQkWaves = 4;  // waves per workgroup
+constexpr int kQkWaves = 4;  // waves per workgroup, one 16-row tile each: 64-row groups
 
+// Extents are 32-bit (the launcher rejects larger ones); offsets are formed
+// in 64 bits.  Fewer 64-bit scalars keep the kernel's scalar registers in
+// bounds.
 struct QkArgs {
     const int8_t *qdig, *kdig;  // [row][kQKmax][Dp64]
     const int4 *qinfo, *kinfo;
-    int64_t Dp64, ni, ni_pad, i0, kv_lo, kv_hi, kv_pad;
-    int64_t Hq, Hkv, group;
-    int causal;
-    double scale;
     float *scores;  // [bh][ni][W] or null
-    int64_t W;
     uint32_t *keys;  // rowmax keys, [bh*key_rows + i - key_row0], or null
-    int64_t key_rows, key_row0;
     int *nfix;       // number of items left to the fp64 chain
     int4 *fixlist;   // their (kb, tile, bh)
-    int64_t nKB;
+    double scale;
+    int Dp64, ni, ni_pad, i0, kv_lo, kv_hi, kv_pad;
+    int Hq, Hkv, group;
+    int causal;
+    int W, key_rows, key_row0;
+    int nKB, ntiles, ngroups;
 };
 
-// One workgroup per (16-row tile, key partition); its waves take the tile's
-// 16-key blocks round robin.  A wave keeps its rows' digits in registers for
-// all of its blocks.  Per block: the item bound, the digit products on the
-// matrix cores, the exact integer dot per pair turned into the score, and a
-// running per-lane max of each row.  Items that fail the bound go to a list.
-// All kQKmax digit products are issued: digits above a row's count are zero,
-// and branching per product would cost more registers than the products do.
-// Operand layout of v_mfma_i32_16x16x64_i8: lane l supplies row (A) or column
-// (B) l%16 with k = 16*(l/16) + 0..15; result register r of lane l holds
-// row 4*(l/16) + r, column l%16.
+// LDS of the score kernel: the digits and statistics of two 16-key blocks.
+// Each key's row is padded by 16 bytes: the 16 lanes of a read pass then
+// fetch 16 different keys from 16 disjoint sets of four banks.
 template <int ND>
-__global__ __launch_bounds__(64 * kQkWaves) void k_qk_mfma(QkArgs A) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+struct QkShared {
+    static constexpr int kRow = kQKmax * 64 * ND + 16;
+    uint8_t k[2][kQkT * kRow];
+    int4 info[2][kQkT];
+};
+
+// One 64-row group of one head: wave w owns 16-row tile 4*group + w and keeps
+// its digits in registers; the workgroup walks key blocks part, part + P, ...
+// (P = gridDim.x) up to the last block the group can see.  The digits of the
+// next block are loaded from global memory while the current one is
+// multiplied and are stored to LDS only afterwards, so the loads overlap the
+// matrix-core work and the epilogue.  Per block and wave: the item bound, the
+// digit products, the exact integer dot per pair turned into the score, and a
+// running per-lane max of each row.  Items that fail the bound go to a list
+// for the fp64 chain.  All kQKmax digit products are issued: digits above a
+// row's count are zero, and branching per product costs more registers than
+// the products do.  Operand layout of v_mfma_i32_16x16x64_i8: lane l supplies
+// row (A) or column (B) l%16 with k = 16*(l/16) + 0..15; result register r of
+// lane l holds row 4*(l/16) + r, column l%16.
+template <int ND>
+__device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t group, QkShared<ND> &S) {
+    constexpr int RB = kQKmax * 64 * ND;  // digit bytes of one key (or row) in global memory
+    constexpr int KROW = QkShared<ND>::kRow;
+    constexpr int NCH = kQkT * RB / 16;   // 16-byte chunks of one block
+    constexpr int CPT = (NCH + 255) / 256;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;
-    const int64_t tile = blockIdx.y, bh = blockIdx.z;
+    const int P = gridDim.x, part = blockIdx.x;
     const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
-    const int64_t it0 = A.i0 + tile * kQkT, i_end = A.i0 + A.ni;
-    const int4 qi = A.qinfo[bh * A.ni_pad + tile * kQkT + lr];
-    int aq = qi.y, qbt = qi.z;
+    const int tile = (int)group * kQkWaves + wave;
+    const bool live = tile < A.ntiles;
+    const int it0 = A.i0 + tile * kQkT, i_end = A.i0 + A.ni;
+
+    // key blocks of this workgroup: part, part + P, ... below kb_end
+    int kb_end = A.nKB;
+    if (A.causal) {
+        const int last = A.i0 + min(((int)group + 1) * kQkWaves * kQkT, A.ni) - 1;
+        kb_end = last >= A.kv_lo ? min(kb_end, (last - A.kv_lo) / kQkT + 1) : 0;
+    }
+    const int nb = kb_end > part ? (kb_end - (int)part + (int)P - 1) / (int)P : 0;
+
+    // this wave's rows: digits, digit count and bound (max over the 16 rows), grids
+    int aq = 0, qbt = 0;
+    int4 qi = int4{0, 0, 0, 0};
+    v4i Aq[kQKmax][ND];
+    if (live) {
+        qi = A.qinfo[bh * A.ni_pad + tile * kQkT + lr];
+        const int8_t *qrow = A.qdig + (bh * A.ni_pad + (int64_t)(tile * kQkT + lr)) * RB + 16 * lq;
+#pragma unroll
+        for (int a = 0; a < kQKmax; ++a)
+#pragma unroll
+            for (int n = 0; n < ND; ++n) Aq[a][n] = *(const v4i *)(qrow + a * 64 * ND + 64 * n);
+    }
+    aq = qi.y;
+    qbt = qi.z;
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) {
         aq = max(aq, __shfl_xor(aq, off, 64));
@@ -136,80 +179,119 @@ __global__ __launch_bounds__(64 * kQkWaves) void k_qk_mfma(QkArgs A) {
     }
     aq = __builtin_amdgcn_readfirstlane(aq);  // wave-uniform after the reduction
     qbt = __builtin_amdgcn_readfirstlane(qbt);
-    v4i Aq[kQKmax][ND];
-    {
-        const int8_t *qrow = A.qdig + (bh * A.ni_pad + tile * kQkT + lr) * kQKmax * A.Dp64 + 16 * lq;
-#pragma unroll
-        for (int a = 0; a < kQKmax; ++a)
-#pragma unroll
-            for (int n = 0; n < ND; ++n) Aq[a][n] = *(const v4i *)(qrow + a * A.Dp64 + 64 * n);
-    }
     int gq[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) gq[r] = __shfl(qi.x, 4 * lq + r, 64);
     uint32_t mkey[4] = {kKeyNegInf, kKeyNegInf, kKeyNegInf, kKeyNegInf};
-    float *srow = A.scores ? A.scores + (bh * A.ni + (it0 + 4 * lq - A.i0)) * A.W : nullptr;
-    const int64_t stride = (int64_t)gridDim.x * kQkWaves;
-    for (int64_t kb = (int64_t)blockIdx.x * kQkWaves + wave; kb < A.nKB; kb += stride) {
-        const int64_t j0 = A.kv_lo + kb * kQkT;
-        if (A.causal && j0 > it0 + kQkT - 1) break;  // this and later blocks lie above the diagonal
-        const int4 ki = A.kinfo[bhk * A.kv_pad + kb * kQkT + lr];
-        int bk = ki.y, kbnd = ki.z;
+    float *srow = (A.scores && live) ? A.scores + (bh * A.ni + (it0 + 4 * lq - A.i0)) * (int64_t)A.W : nullptr;
+
+    // staging of a block's digits: chunk c = tid + 256 t is bytes 16*(c % (RB/16)) of key c / (RB/16)
+    const int8_t *kbase = A.kdig + bhk * A.kv_pad * (int64_t)RB;
+    const int4 *ibase = A.kinfo + bhk * A.kv_pad;
+    auto block_src = [&](int n) { return kbase + (int64_t)((part + n * P) * kQkT) * RB; };
+    v4i stage[CPT];
+    int4 sinfo = int4{0, 0, 0, 0};
+    auto load_block = [&](int n) {
+        const int8_t *src = block_src(n);
 #pragma unroll
-        for (int off = 8; off > 0; off >>= 1) {
-            bk = max(bk, __shfl_xor(bk, off, 64));
-            kbnd = max(kbnd, __shfl_xor(kbnd, off, 64));
+        for (int t = 0; t < CPT; ++t) {
+            const int c = tid + 256 * t;
+            if (c < NCH) stage[t] = *(const v4i *)(src + (int64_t)c * 16);
         }
-        bk = __builtin_amdgcn_readfirstlane(bk);
-        kbnd = __builtin_amdgcn_readfirstlane(kbnd);
-        if (aq > kQKmax || bk > kQKmax || qbt + kbnd > 53) {
-            if (lane == 0) {
-                const int at = atomicAdd(A.nfix, 1);
-                A.fixlist[at] = int4{(int)kb, (int)tile, (int)bh, 0};
-            }
-            continue;
+        if (tid < kQkT) sinfo = ibase[(part + n * P) * kQkT + tid];
+    };
+    auto store_block = [&](int buf) {
+#pragma unroll
+        for (int t = 0; t < CPT; ++t) {
+            const int c = tid + 256 * t;
+            if (c < NCH) *(v4i *)(S.k[buf] + (c / (RB / 16)) * KROW + (c % (RB / 16)) * 16) = stage[t];
         }
-        const int8_t *krow = A.kdig + (bhk * A.kv_pad + kb * kQkT + lr) * kQKmax * A.Dp64 + 16 * lq;
-        v4i C[kQKC];
-#pragma unroll
-        for (int c = 0; c < kQKC; ++c) C[c] = v4i{0, 0, 0, 0};
-#pragma unroll
-        for (int n = 0; n < ND; ++n) {
-            v4i Bk[kQKmax];
-#pragma unroll
-            for (int c = 0; c < kQKmax; ++c)
-                Bk[c] = *(const v4i *)(krow + c * A.Dp64 + 64 * n);
-#pragma unroll
-            for (int a = 0; a < kQKmax; ++a)
-#pragma unroll
-                for (int c = 0; c < kQKmax; ++c)
-                        C[a + c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[a][n], Bk[c], C[a + c], 0, 0, 0);
-        }
-        const int64_t j = j0 + lr;
-        const bool jv = j < A.kv_hi;
-        const int gk = ki.x;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t i = it0 + 4 * lq + r;
-            int64_t dot = 0;
-#pragma unroll
-            for (int c = kQKC - 1; c >= 0; --c) dot = dot * 256 + (int64_t)C[c][r];
-            const double d64 = ldexp((double)dot, gq[r] + gk);  // exact: |dot| < 2^53
-            const float sc = (float)(A.scale * d64);
-            if (jv && i < i_end) {
-                if (srow) srow[r * A.W + (j - A.kv_lo)] = sc;
-                if (!A.causal || j <= i) mkey[r] = max(mkey[r], order_key(sc));
-            }
-        }
+        if (tid < kQkT) S.info[buf][tid] = sinfo;
+    };
+    if (nb > 0) {
+        load_block(0);
+        store_block(0);
     }
-    if (!A.keys) return;
+    __syncthreads();
+    for (int n = 0; n < nb; ++n) {
+        const int buf = n & 1;
+        const int kb = part + n * P;
+        if (n + 1 < nb) load_block(n + 1);
+        const int j0 = A.kv_lo + kb * kQkT;
+        if (live && !(A.causal && j0 > it0 + kQkT - 1)) {
+            const int4 ki = S.info[buf][lr];
+            int bk = ki.y, kbnd = ki.z;
+#pragma unroll
+            for (int off = 8; off > 0; off >>= 1) {
+                bk = max(bk, __shfl_xor(bk, off, 64));
+                kbnd = max(kbnd, __shfl_xor(kbnd, off, 64));
+            }
+            bk = __builtin_amdgcn_readfirstlane(bk);
+            kbnd = __builtin_amdgcn_readfirstlane(kbnd);
+            if (aq > kQKmax || bk > kQKmax || qbt + kbnd > 53) {
+                if (lane == 0) {
+                    const int at = atomicAdd(A.nfix, 1);
+                    A.fixlist[at] = int4{kb, tile, (int)bh, 0};
+                }
+            } else {
+                const uint8_t *krow = S.k[buf] + lr * KROW + 16 * lq;
+                v4i C[kQKC];
+#pragma unroll
+                for (int c = 0; c < kQKC; ++c) C[c] = v4i{0, 0, 0, 0};
+#pragma unroll
+                for (int nn = 0; nn < ND; ++nn) {
+                    v4i Bk[kQKmax];
+#pragma unroll
+                    for (int c = 0; c < kQKmax; ++c) Bk[c] = *(const v4i *)(krow + c * 64 * ND + 64 * nn);
+#pragma unroll
+                    for (int a = 0; a < kQKmax; ++a)
+#pragma unroll
+                        for (int c = 0; c < kQKmax; ++c)
+                            C[a + c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[a][nn], Bk[c], C[a + c], 0, 0, 0);
+                }
+                const int j = j0 + lr;
+                const bool jv = j < A.kv_hi;
+                const int gk = ki.x;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = it0 + 4 * lq + r;
+                    int64_t dot = 0;
+#pragma unroll
+                    for (int c = kQKC - 1; c >= 0; --c) dot = dot * 256 + (int64_t)C[c][r];
+                    const double d64 = ldexp((double)dot, gq[r] + gk);  // exact: |dot| < 2^53
+                    const float sc = (float)(A.scale * d64);
+                    if (jv && i < i_end) {
+                        if (srow) srow[(int64_t)r * A.W + (j - A.kv_lo)] = sc;
+                        if (!A.causal || j <= i) mkey[r] = max(mkey[r], order_key(sc));
+                    }
+                }
+            }
+        }
+        if (n + 1 < nb) store_block(buf ^ 1);
+        __syncthreads();
+    }
+    if (!A.keys || !live) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         uint32_t m = mkey[r];
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-        const int64_t i = it0 + 4 * lq + r;
+        const int i = it0 + 4 * lq + r;
         if (lr == 0 && i < i_end && m != kKeyNegInf) atomicMax(&A.keys[bh * A.key_rows + (i - A.key_row0)], m);
+    }
+}
+
+// Grid (P parts, groups or causal pairs of groups, heads).  A causal
+// workgroup takes group ngroups-1-y and then group y, whose visible key
+// counts add up alike for every y.
+template <int ND>
+__global__ __launch_bounds__(64 * kQkWaves) void k_qk_mfma(QkArgs A) {
+    __shared__ __align__(16) QkShared<ND> S;
+    const int64_t bh = blockIdx.z, y = blockIdx.y;
+    const int npass = (A.causal && y != A.ngroups - 1 - y) ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        if (pass) __syncthreads();  // the LDS of the first group is free again
+        qk_group<ND>(A, bh, (A.causal && pass == 0) ? A.ngroups - 1 - y : y, S);
     }
 }
 
@@ -315,37 +397,43 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_fill_u32((uint32_t *)nfix, 1, 0u, s)) != hipSuccess) return e;
     }
+    // every extent the kernels see must fit 32 bits (offsets are formed in 64)
+    const int64_t lim = INT32_MAX;
+    if (ni_pad > lim || kv_pad > lim || i0 + ni_pad > lim || kv_hi > lim || key_rows > lim || g.Hq > lim)
+        return hipErrorInvalidValue;
     QkArgs a{};
     a.qdig = qdig;
     a.kdig = (const int8_t *)kprep + align256((size_t)krows * 16);
     a.qinfo = qinfo;
     a.kinfo = (const int4 *)kprep;
-    a.Dp64 = Dp64;
-    a.ni = ni;
-    a.ni_pad = ni_pad;
-    a.i0 = i0;
-    a.kv_lo = kv_lo;
-    a.kv_hi = kv_hi;
-    a.kv_pad = kv_pad;
-    a.Hq = g.Hq;
-    a.Hkv = g.Hkv;
-    a.group = g.Hq / g.Hkv;
-    a.causal = g.causal;
-    a.scale = g.scale;
     a.scores = scores;
-    a.W = kv_hi - kv_lo;
     a.keys = rowmax_keys;
-    a.key_rows = key_rows;
-    a.key_row0 = key_row0;
     a.nfix = nfix;
     a.fixlist = fixlist;
-    a.nKB = nKB;
+    a.scale = g.scale;
+    a.Dp64 = (int)Dp64;
+    a.ni = (int)ni;
+    a.ni_pad = (int)ni_pad;
+    a.i0 = (int)i0;
+    a.kv_lo = (int)kv_lo;
+    a.kv_hi = (int)kv_hi;
+    a.kv_pad = (int)kv_pad;
+    a.Hq = (int)g.Hq;
+    a.Hkv = (int)g.Hkv;
+    a.group = (int)(g.Hq / g.Hkv);
+    a.causal = g.causal;
+    a.W = (int)(kv_hi - kv_lo);
+    a.key_rows = (int)key_rows;
+    a.key_row0 = (int)key_row0;
+    a.nKB = (int)nKB;
+    a.ntiles = (int)ntiles;
+    a.ngroups = (int)((ntiles + kQkWaves - 1) / kQkWaves);
     {
         ProfScope prof_("scores", s);
-        // a tile's key blocks spread over up to 64 workgroups, at least 4 blocks per wave
-        const int64_t per_wg = 4 * kQkWaves;
-        const int64_t parts = std::max<int64_t>(1, std::min<int64_t>((nKB + per_wg - 1) / per_wg, 64));
-        dim3 grid((unsigned)parts, (unsigned)ntiles, (unsigned)bh);
+        // causal launches pair groups; parts of the key range spread the rest over the chip
+        const int64_t gy = g.causal ? (a.ngroups + 1) / 2 : a.ngroups;
+        const int64_t parts = std::max<int64_t>(1, std::min<int64_t>(8, (768 + gy * bh - 1) / (gy * bh)));
+        dim3 grid((unsigned)parts, (unsigned)gy, (unsigned)bh);
         switch (Dp64 / 64) {
             case 1: hipLaunchKernelGGL(k_qk_mfma<1>, grid, dim3(64 * kQkWaves), 0, s, a); break;
             case 2: hipLaunchKernelGGL(k_qk_mfma<2>, grid, dim3(64 * kQkWaves), 0, s, a); break;
