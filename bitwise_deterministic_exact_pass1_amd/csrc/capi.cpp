@@ -148,10 +148,19 @@ hipError_t prep_keys(const Tensor &tk, const AttnGeom &g, bool mfma, void *kprep
 hipError_t run_scores(const Tensor &tq, const Tensor &tk, const AttnGeom &g, bool mfma, const void *kprep,
                       void *chunk_ws, int64_t i0, int64_t i1, int64_t lo, int64_t hi, float *scores, uint32_t *keys,
                       int64_t key_rows, int64_t key_row0, hipStream_t s) {
+    // both paths start the rowmax keys of rows [i0, i1) at "empty" themselves
     if (mfma)
         return launch_scores_qk(tq, tk, g, kprep, chunk_ws, i0, i1, lo, hi, scores, keys, key_rows, key_row0, s);
-    hipError_t e = launch_widen_q(tq, g, i0, i1, (double *)chunk_ws, s);
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (keys) {  // keys[h * key_rows + i - key_row0]: one run per head, or one in all when contiguous
+        const int64_t bh = g.B * g.Hq, n = i1 - i0;
+        const bool whole = key_rows == n && key_row0 == i0;
+        for (int64_t h = 0; h < (whole ? 1 : bh); ++h)
+            if ((e = launch_fill_u32(keys + h * key_rows + (i0 - key_row0), whole ? bh * n : n, kKeyNegInf, s)) !=
+                hipSuccess)
+                return e;
+    }
+    if ((e = launch_widen_q(tq, g, i0, i1, (double *)chunk_ws, s)) != hipSuccess) return e;
     return launch_scores(tk, g, (const double *)chunk_ws, i0, i1, lo, hi, scores, keys, key_rows, key_row0, s);
 }
 
@@ -171,8 +180,7 @@ size_t bytes_accumulate(const AttnGeom &g, bool mfma, int64_t ni, int64_t W) {
 size_t bytes_fused(const AttnGeom &g, bool mfma, int64_t ni) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, g.Skv) + score_fixed_bytes(g, mfma, g.Skv) + score_chunk_bytes(g, mfma, ni, g.Skv) +
-           align256((size_t)rows * 4) + align256((size_t)rows * g.Skv * 4) + align256((size_t)rows * 4) +
-           pv_fallback_bytes(g, ni);
+           align256((size_t)rows * 4) + align256((size_t)rows * g.Skv * 4) + pv_fallback_bytes(g, ni);
 }
 
 size_t bytes_sharded(const AttnGeom &g, bool mfma, int64_t ni, int64_t maxlen) {
@@ -187,8 +195,7 @@ VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
     const int64_t bhk = g.B * g.Hkv, Dp32 = (g.D + 31) / 32 * 32, nG = Dp32 / 32;
     const int64_t nKB = std::max<int64_t>((kv_len + 31) / 32, 1);
     VPrep v;
-    v.colmax = c.take<int>(bhk * Dp32);
-    v.colmin = c.take<int>(bhk * Dp32);
+    v.stats = c.take<char>(vstats_bytes(g));
     v.colgrid = c.take<int>(bhk * Dp32);
     v.grpB = c.take<int>(bhk * nG);
     v.slices = c.take<char>(vslice_bytes(g, kv_len));
@@ -295,7 +302,6 @@ int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int
     HIP_TRY(prep_keys(tk, g, mf, kprep, kv_lo, kv_hi, s), "prepare k");
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        HIP_TRY(launch_fill_u32(keys, bh * ni, kKeyNegInf, s), "fill");
         HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, kv_lo, kv_hi, nullptr, keys, ni, i0, s), "scores");
         HIP_TRY(launch_keys_to_f32(keys, rowmax, bh, ni, g.Sq, i0, s), "rowmax");
     }
@@ -348,7 +354,7 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     for (int64_t i0 = 0; i0 < g.Sq && W > 0; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk);
         HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, kv_lo, kv_hi, sc, nullptr, 0, 0, s), "scores");
-        HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr,
+        HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, nullptr, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr,
                           nullptr, num, den, rows, g.Sq, 0, ff, s),
                 "deposit");
     }
@@ -422,7 +428,6 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, g.Skv));
     uint32_t *keys = c0.take<uint32_t>(crows);
     float *sc = c0.take<float>(crows * g.Skv);
-    float *rm = c0.take<float>(crows);
     int *flags = c0.take<int>(bh * ctiles);
     int64_t *fnum = c0.take<int64_t>(kNumDigits * bh * ctiles * 32 * g.D);
     int64_t *fden = c0.take<int64_t>(kDenDigits * bh * ctiles * 32);
@@ -431,12 +436,10 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     HIP_TRY(prep_keys(tk, g, mf, kprep, 0, g.Skv, s), "prepare k");
     const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
-        const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0, rows = bh * ni;
-        HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
+        const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
         HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, 0, g.Skv, sc, keys, ni, i0, s), "scores");
-        HIP_TRY(launch_keys_to_f32(keys, rm, bh, ni, ni, 0, s), "rowmax");
-        HIP_TRY(launch_pv(tv, g, vp, sc, rm, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr, nullptr,
-                          0, 0, 0, ff, s),
+        HIP_TRY(launch_pv(tv, g, vp, sc, nullptr, keys, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr,
+                          nullptr, 0, 0, 0, ff, s),
                 "deposit");
     }
     return ok();
@@ -523,7 +526,6 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         for (int32_t a = 0; a < n_splits; ++a) {
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
-            HIP_TRY(launch_fill_u32(keys, rows, kKeyNegInf, s), "fill keys");
             HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
             HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, nullptr, keys, ni, i0, s), "scores");
             HIP_TRY(launch_keys_to_f32(keys, rm_part, bh, ni, ni, 0, s), "rowmax");
@@ -541,7 +543,7 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
                 HIP_TRY(launch_vprep(tv, g, l, h, vp, s), "prepare v");
                 HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
                 HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
-                HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
+                HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, nullptr, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
                                   num_part, den_part, rows, ni, i0, ff, s),
                         "deposit");
             }

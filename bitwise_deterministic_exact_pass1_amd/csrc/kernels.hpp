@@ -91,23 +91,26 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
 // Prepared V of one key range: per-column grid exponents and balanced int8
 // digits in MFMA lane order.
 struct VPrep {
-    int *colmax, *colmin, *colgrid, *grpB;
+    void *stats;  // column statistics per key chunk
+    int *colgrid, *grpB;
     void *slices;
     int64_t Dp32, nKB;
 };
 size_t vprep_bytes(const AttnGeom &g, int64_t kv_len);
-// bytes of the V digit slices within vprep_bytes
+// bytes of the V digit slices / of the column statistics within vprep_bytes
 size_t vslice_bytes(const AttnGeom &g, int64_t kv_len);
+size_t vstats_bytes(const AttnGeom &g);
 size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i);
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
                         hipStream_t s);
 // Exact NUM/DEN of query rows [i0,i1) against keys [kv_lo,kv_hi) from stored
-// scores (chunk layout [bh][i-i0][j-kv_lo]) and rowmax[bh*rm_rows + i - rm_row0].
+// scores (chunk layout [bh][i-i0][j-kv_lo]) and rowmax[bh*rm_rows + i - rm_row0]
+// (or, when rowmax is null, the order keys rowmax_keys at the same place).
 // With `o` the tile is finalized into o; otherwise its exact values are added
 // into the digit planes num/den (rows bh*rows_per_bh + i - row0).  Tiles the
 // matrix-core path cannot represent exactly are redone by the generic path.
 hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
-                     int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
+                     const uint32_t *rowmax_keys, int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
                      int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
                      int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s);
 

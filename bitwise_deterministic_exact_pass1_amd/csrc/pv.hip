@@ -35,25 +35,30 @@ constexpr int kNC = kAw + kBmax - 1;    // shift classes s = a + b
 constexpr int kKB = 32;                 // keys per block (the MFMA K)
 constexpr int kCarryEvery = 256;        // blocks (8192 keys) between carry passes
 constexpr int kBvFallback = 99;         // "needs the generic path" marker
-constexpr int kStatKeys = 64;           // keys per workgroup of the column statistics
 
 // ---------------------------------------------------------------- V preparation
 
-// Column statistics over keys [kv_lo, kv_hi): max exponent and min lsb exponent
-// of the nonzero entries, folded into per-column int32 by atomic max/min.
+constexpr int kVChunks = 16;  // key chunks of the V column statistics
+
+// Column statistics of V over one key chunk: per column the largest exponent
+// and the smallest lsb exponent of the nonzero entries.  Grid (chunk, 32-column
+// group, head); 8 key strides x 32 columns per workgroup, reduced in LDS and
+// written to stats[((bhk * nG + G) * kVChunks + chunk) * 32 + column] as
+// int2 {emax, lmin} (no atomics, nothing to clear).
 template <typename TV>
 __global__ __launch_bounds__(256) void k_vstats(const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
-                                                int64_t Hkv, int64_t D, int64_t Dp32, int64_t kv_lo, int64_t kv_hi,
-                                                int *__restrict__ colmax, int *__restrict__ colmin) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t bhk = blockIdx.z, b = bhk / Hkv, hk = bhk % Hkv;
-    const int64_t d = (int64_t)blockIdx.y * 64 + lane;
-    const int64_t j0 = kv_lo + (int64_t)blockIdx.x * kStatKeys;
-    const int64_t j1 = std::min<int64_t>(kv_hi, j0 + kStatKeys);
+                                                int64_t Hkv, int64_t D, int64_t nG, int64_t kv_lo, int64_t kv_hi,
+                                                int2 *__restrict__ stats) {
+    const int t = threadIdx.x, c = t & 31, st = t >> 5;
+    const int64_t chunk = blockIdx.x, G = blockIdx.y, bhk = blockIdx.z, b = bhk / Hkv, hk = bhk % Hkv;
+    const int64_t len = kv_hi - kv_lo, per = (len + kVChunks - 1) / kVChunks;
+    const int64_t j0 = kv_lo + chunk * per, j1 = std::min<int64_t>(kv_hi, j0 + per);
+    const int64_t d = G * 32 + c;
     int emax = INT_MIN, lmin = INT_MAX;
     if (d < D) {
         const TV *col = vp + b * vsB + hk * vsH + d;
-        for (int64_t j = j0 + wave; j < j1; j += 4) {
+#pragma unroll 4
+        for (int64_t j = j0 + st; j < j1; j += 8) {
             const float x = elem<TV>::to_f32(col[j * vsS]);
             if (x != 0.0f) {
                 const int e = f32_exp(x);
@@ -62,40 +67,47 @@ __global__ __launch_bounds__(256) void k_vstats(const TV *__restrict__ vp, int64
             }
         }
     }
-    __shared__ int smax[256], smin[256];
-    smax[threadIdx.x] = emax;
-    smin[threadIdx.x] = lmin;
+    __shared__ int smax[8][32], smin[8][32];
+    smax[st][c] = emax;
+    smin[st][c] = lmin;
     __syncthreads();
-    if (wave == 0 && d < Dp32) {
-        for (int w = 1; w < 4; ++w) {
-            emax = max(emax, smax[w * 64 + lane]);
-            lmin = min(lmin, smin[w * 64 + lane]);
-        }
-        if (emax != INT_MIN) atomicMax(&colmax[bhk * Dp32 + d], emax);
-        if (lmin != INT_MAX) atomicMin(&colmin[bhk * Dp32 + d], lmin);
+    if (t >= 32) return;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+        emax = max(emax, smax[k][c]);
+        lmin = min(lmin, smin[k][c]);
     }
+    stats[((bhk * nG + G) * kVChunks + chunk) * 32 + c] = int2{emax, lmin};
 }
 
 // Digits of Vi = V * 2^-g_d in MFMA lane order: block (bhk, G, kb, b) holds
 // 64 lanes x 16 bytes, lane l byte p = e_b(Vi[key kv_lo + 32kb + 16(l/32) + p][dim 32G + l%32]).
-// Also writes the per-column grid g_d and the per-group digit count.
+// g_d = the smallest lsb exponent of the column's nonzero entries (so Vi is an
+// integer), from the chunk statistics; the group's digit count is what the
+// largest |Vi| of its 32 columns needs (kBvFallback when more than kBmax).
+// The workgroups of block 0 also record g_d and the count for pass 2.
 template <typename TV>
 __global__ __launch_bounds__(64) void k_vslice(const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
                                                int64_t Hkv, int64_t D, int64_t Dp32, int64_t kv_lo, int64_t kv_hi,
-                                               int64_t nKB, const int *__restrict__ colmax,
-                                               const int *__restrict__ colmin, int *__restrict__ colgrid,
+                                               int64_t nKB, const int2 *__restrict__ stats, int *__restrict__ colgrid,
                                                int *__restrict__ grpB, v4i *__restrict__ vsl) {
     const int lane = threadIdx.x;
     const int64_t kb = blockIdx.x, G = blockIdx.y, bhk = blockIdx.z;
     const int64_t b = bhk / Hkv, hk = bhk % Hkv;
     const int64_t nG = Dp32 / 32;
     const int64_t d = G * 32 + (lane & 31);
-    const int cmax = colmax[bhk * Dp32 + d], cmin = colmin[bhk * Dp32 + d];
-    const bool nonzero = cmax != INT_MIN;
-    const int g = nonzero ? cmin : 0;
-    // digits needed: |Vi| < 2^(cmax + 1 - g); balanced digits hold |x| <= 2^(8B-2)
-    int need = nonzero ? (cmax + 1 - g + 2 + 7) / 8 : 0;
-    int bg = need;
+    int emax = INT_MIN, lmin = INT_MAX;
+    const int2 *cs = stats + (bhk * nG + G) * kVChunks * 32 + (lane & 31);
+#pragma unroll
+    for (int k = 0; k < kVChunks; ++k) {
+        const int2 e = cs[k * 32];
+        emax = max(emax, e.x);
+        lmin = min(lmin, e.y);
+    }
+    const bool nonzero = emax != INT_MIN;
+    const int g = nonzero ? lmin : 0;
+    // digits needed: |Vi| < 2^(emax + 1 - g); balanced digits hold |x| <= 2^(8B-2)
+    int bg = nonzero ? (emax + 1 - g + 2 + 7) / 8 : 0;
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) bg = max(bg, __shfl_xor(bg, off, 64));
     bg = max(bg, 1);
@@ -103,13 +115,15 @@ __global__ __launch_bounds__(64) void k_vslice(const TV *__restrict__ vp, int64_
     if (kb == 0 && lane < 32) colgrid[bhk * Dp32 + d] = g;
     if (kb == 0 && lane == 0) grpB[bhk * nG + G] = bg;
     const TV *col = vp + b * vsB + hk * vsH + (d < D ? d : 0);
-    int64_t vi[16];
+    // the kBmax balanced digits of Vi (|Vi| < 2^38 when bg <= kBmax) are the
+    // bytes of Vi + 0x8080808080 with their top bit flipped
+    uint64_t U[16];
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
         const int64_t j = kv_lo + kb * kKB + 16 * (lane >> 5) + p;
         double x = 0.0;
         if (d < D && j < kv_hi && bg != kBvFallback) x = (double)elem<TV>::to_f32(col[j * vsS]);
-        vi[p] = (int64_t)ldexp(x, -g);  // exact: x is a multiple of 2^g and |x/2^g| < 2^48
+        U[p] = (uint64_t)((int64_t)ldexp(x, -g) + 0x8080808080ll);  // exact: x is a multiple of 2^g
     }
     v4i *out = vsl + ((bhk * nG + G) * nKB + kb) * kBmax * 64;
 #pragma unroll
@@ -119,13 +133,8 @@ __global__ __launch_bounds__(64) void k_vslice(const TV *__restrict__ vp, int64_
         for (int q = 0; q < 4; ++q) {
             uint32_t pack = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int64_t x = vi[4 * q + u];
-                const int64_t c = ((x & 255) ^ 128) - 128;  // balanced low digit
-                vi[4 * q + u] = (x - c) >> 8;
-                pack |= ((uint32_t)(c & 255)) << (8 * u);
-            }
-            wv[q] = pack;
+            for (int u = 0; u < 4; ++u) pack |= ((uint32_t)(U[4 * q + u] >> (8 * s)) & 255u) << (8 * u);
+            wv[q] = pack ^ 0x80808080u;
         }
         out[s * 64 + lane] = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
     }
@@ -190,7 +199,8 @@ __device__ __forceinline__ void add_i128_digits(__int128 x, int pos, int64_t *dg
 
 struct PvArgs {
     const float *scores;  // [bh][ni][W] chunk scores
-    const float *rowmax;  // rowmax[bh*rm_rows + i - rm_row0]
+    const float *rowmax;          // rowmax[bh*rm_rows + i - rm_row0], or null and then
+    const uint32_t *rowmax_keys;  // its order keys at the same place
     int64_t rm_rows, rm_row0;
     int64_t ni, W, i0, kv_lo, kv_hi;
     int64_t Hq, Hkv, group, D, Dp32, nKB;
@@ -207,6 +217,13 @@ struct PvArgs {
     int64_t *num, *den;
     int64_t plane_rows, rows_per_bh, row0;
 };
+
+// The row max of row i of head bh (from floats or from order keys).
+__device__ __forceinline__ float pv_rowmax(const PvArgs &A, int64_t bh, int64_t i) {
+    const int64_t at = bh * A.rm_rows + (i - A.rm_row0);
+    return A.rowmax_keys ? key_value(A.rowmax_keys[at]) : A.rowmax[at];
+}
+
 
 // Weights of one 32-key block for the calling thread: KPT consecutive keys of
 // one row with scores sc[]; the first nv of them are visible.  w =
@@ -324,7 +341,7 @@ __device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t 
     const int dofs = ((r + 32 * (k0 >> 4)) * 16) + (k0 & 15);
     const int64_t i = T.it0 + r;
     const bool rowok = i < T.i_end;
-    const float m = rowok ? A.rowmax[bh * A.rm_rows + (i - A.rm_row0)] : 0.0f;
+    const float m = rowok ? pv_rowmax(A, bh, i) : 0.0f;
     const float *srow = A.scores + (bh * A.ni + (rowok ? i - A.i0 : 0)) * A.W - A.kv_lo;
     // keys this row sees: [kv_lo, jend)
     const int64_t jend = rowok ? (A.causal ? std::min<int64_t>(T.jhi, i + 1) : T.jhi) : A.kv_lo;
@@ -505,14 +522,13 @@ __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
 
 // ---------------------------------------------------------------- generic exact fallback
 
-// One workgroup per flagged tile: the windowed exact deposit of the general
-// path over all keys of the tile's rows, then (fused) an in-kernel finalize.
+// One flagged tile, by the whole workgroup: the windowed exact deposit of the
+// general path over all keys of the tile's rows, then (fused) an in-kernel
+// finalize.  nbh = number of heads in the launch.
 template <typename TV, bool FUSED>
-__global__ __launch_bounds__(256) void k_tile_fallback(PvArgs A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH,
-                                                       int64_t vsS, int64_t *__restrict__ num_ws,
-                                                       int64_t *__restrict__ den_ws) {
-    const int64_t bh = blockIdx.y, tile = blockIdx.x;
-    if (!A.flags[bh * A.ntiles + tile]) return;
+__device__ void fallback_tile(const PvArgs &A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
+                              int64_t *__restrict__ num_ws, int64_t *__restrict__ den_ws, int64_t bh, int64_t tile,
+                              int64_t nbh) {
     const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group;
     const int64_t it0 = A.i0 + tile * 32, i_end = A.i0 + A.ni;
     const int64_t D = A.D;
@@ -520,7 +536,7 @@ __global__ __launch_bounds__(256) void k_tile_fallback(PvArgs A, const TV *__res
     // digit target: fused -> 32-row scratch of this tile (zeroed here); digits -> caller planes
     int64_t *num = FUSED ? num_ws : A.num;
     int64_t *den = FUSED ? den_ws : A.den;
-    const int64_t nplane_rows = FUSED ? A.ntiles * 32 * (int64_t)gridDim.y : A.plane_rows;
+    const int64_t nplane_rows = FUSED ? A.ntiles * 32 * nbh : A.plane_rows;
     auto prow_of = [&](int64_t i) -> int64_t {
         return FUSED ? (bh * A.ntiles + tile) * 32 + (i - it0) : bh * A.rows_per_bh + (i - A.row0);
     };
@@ -539,7 +555,7 @@ __global__ __launch_bounds__(256) void k_tile_fallback(PvArgs A, const TV *__res
         const int64_t i = it0 + r;
         if (i >= i_end) continue;
         const int64_t row = bh * A.ni + (i - A.i0);
-        const float m = A.rowmax[bh * A.rm_rows + (i - A.rm_row0)];
+        const float m = pv_rowmax(A, bh, i);
         const int64_t jend = A.causal ? std::min<int64_t>(A.kv_hi, i + 1) : A.kv_hi;
         const TV *vcol = vp + b * vsB + hk * vsH + (d < D ? d : 0);
         const int64_t prow = prow_of(i);
@@ -584,6 +600,17 @@ __global__ __launch_bounds__(256) void k_tile_fallback(PvArgs A, const TV *__res
     }
 }
 
+// The generic path for the tiles k_pv flagged: one workgroup per tile, which
+// returns at once unless its tile is flagged.
+template <typename TV, bool FUSED>
+__global__ __launch_bounds__(256) void k_tile_fallback(PvArgs A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH,
+                                                       int64_t vsS, int64_t *__restrict__ num_ws,
+                                                       int64_t *__restrict__ den_ws) {
+    const int64_t bh = blockIdx.y, tile = blockIdx.x;
+    if (A.flags[bh * A.ntiles + tile])
+        fallback_tile<TV, FUSED>(A, vp, vsB, vsH, vsS, num_ws, den_ws, bh, tile, (int64_t)gridDim.y);
+}
+
 // ---------------------------------------------------------------- launchers
 
 size_t vslice_bytes(const AttnGeom &g, int64_t kv_len) {
@@ -592,9 +619,15 @@ size_t vslice_bytes(const AttnGeom &g, int64_t kv_len) {
     return align256((size_t)bhk * nG * nKB * kBmax * 1024);
 }
 
+size_t vstats_bytes(const AttnGeom &g) {
+    const int64_t bhk = g.B * g.Hkv, nG = (g.D + 31) / 32;
+    return align256((size_t)bhk * nG * kVChunks * 32 * 8);
+}
+
 size_t vprep_bytes(const AttnGeom &g, int64_t kv_len) {
     const int64_t bhk = g.B * g.Hkv, Dp32 = (g.D + 31) / 32 * 32, nG = Dp32 / 32;
-    return 3 * align256((size_t)bhk * Dp32 * 4) + align256((size_t)bhk * nG * 4) + vslice_bytes(g, kv_len);
+    return vstats_bytes(g) + align256((size_t)bhk * Dp32 * 4) + align256((size_t)bhk * nG * 4) +
+           vslice_bytes(g, kv_len);
 }
 
 size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i) {
@@ -611,27 +644,23 @@ hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64
     const int64_t len = kv_hi - kv_lo, nKB = std::max<int64_t>((len + kKB - 1) / kKB, 1);
     vp.Dp32 = Dp32;
     vp.nKB = nKB;
+    int2 *stats = (int2 *)vp.stats;
     hipError_t e;
-    if ((e = launch_fill_u32((uint32_t *)vp.colmax, bhk * Dp32, (uint32_t)INT_MIN, s)) != hipSuccess) return e;
-    if ((e = launch_fill_u32((uint32_t *)vp.colmin, bhk * Dp32, (uint32_t)INT_MAX, s)) != hipSuccess) return e;
-    if (len > 0) {
-        dim3 gs((unsigned)((len + kStatKeys - 1) / kStatKeys), (unsigned)((Dp32 + 63) / 64), (unsigned)bhk);
-        if (v.dtype == 0)
-            hipLaunchKernelGGL(k_vstats<float>, gs, dim3(256), 0, s, (const float *)v.data, v.sB, v.sH, v.sS, g.Hkv,
-                               g.D, Dp32, kv_lo, kv_hi, vp.colmax, vp.colmin);
-        else
-            hipLaunchKernelGGL(k_vstats<bf16_t>, gs, dim3(256), 0, s, (const bf16_t *)v.data, v.sB, v.sH, v.sS,
-                               g.Hkv, g.D, Dp32, kv_lo, kv_hi, vp.colmax, vp.colmin);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    dim3 gs((unsigned)kVChunks, (unsigned)nG, (unsigned)bhk);  // (an empty range leaves every chunk empty)
+    if (v.dtype == 0)
+        hipLaunchKernelGGL(k_vstats<float>, gs, dim3(256), 0, s, (const float *)v.data, v.sB, v.sH, v.sS, g.Hkv, g.D,
+                           nG, kv_lo, kv_hi, stats);
+    else
+        hipLaunchKernelGGL(k_vstats<bf16_t>, gs, dim3(256), 0, s, (const bf16_t *)v.data, v.sB, v.sH, v.sS, g.Hkv,
+                           g.D, nG, kv_lo, kv_hi, stats);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     dim3 gsl((unsigned)nKB, (unsigned)nG, (unsigned)bhk);
     if (v.dtype == 0)
         hipLaunchKernelGGL(k_vslice<float>, gsl, dim3(64), 0, s, (const float *)v.data, v.sB, v.sH, v.sS, g.Hkv, g.D,
-                           Dp32, kv_lo, kv_hi, nKB, vp.colmax, vp.colmin, vp.colgrid, vp.grpB, (v4i *)vp.slices);
+                           Dp32, kv_lo, kv_hi, nKB, stats, vp.colgrid, vp.grpB, (v4i *)vp.slices);
     else
         hipLaunchKernelGGL(k_vslice<bf16_t>, gsl, dim3(64), 0, s, (const bf16_t *)v.data, v.sB, v.sH, v.sS, g.Hkv,
-                           g.D, Dp32, kv_lo, kv_hi, nKB, vp.colmax, vp.colmin, vp.colgrid, vp.grpB,
-                           (v4i *)vp.slices);
+                           g.D, Dp32, kv_lo, kv_hi, nKB, stats, vp.colgrid, vp.grpB, (v4i *)vp.slices);
     return hipGetLastError();
 }
 
@@ -665,7 +694,7 @@ static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &v
 }
 
 hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
-                     int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
+                     const uint32_t *rowmax_keys, int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
                      int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
                      int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s) {
     const int64_t ni = i1 - i0;
@@ -675,6 +704,7 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     PvArgs a{};
     a.scores = scores;
     a.rowmax = rowmax;
+    a.rowmax_keys = rowmax_keys;
     a.rm_rows = rm_rows;
     a.rm_row0 = rm_row0;
     a.ni = ni;

@@ -32,7 +32,8 @@ template <bool IS_K>
 __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, int64_t sB, int64_t sH, int64_t sS,
                                                 int64_t H, int64_t D, int64_t Dp64, int64_t s0, int64_t ns,
                                                 int64_t ns_pad, int64_t nrows, int4 *__restrict__ info,
-                                                int8_t *__restrict__ dig) {
+                                                int8_t *__restrict__ dig, uint32_t *__restrict__ keys,
+                                                int64_t key_rows, int64_t key_row0, int *__restrict__ nfix) {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= nrows) return;
@@ -76,6 +77,10 @@ __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, in
         bound = l1 ? 64 - __clzll((long long)l1) : 0;  // sum|Ki| < 2^bound
     }
     if (lane == 0) info[row] = int4{g, nd, bound, 0};
+    if (!IS_K && lane == 0) {  // the score pass that follows max-reduces into these
+        if (keys && live) keys[bh * key_rows + (s0 + ii - key_row0)] = kKeyNegInf;
+        if (row == 0) *nfix = 0;
+    }
     int8_t *out = dig + row * kQKmax * Dp64;
 #pragma unroll
     for (int a = 0; a < kQKmax; ++a) {
@@ -366,7 +371,8 @@ hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, in
     int4 *info = (int4 *)ws;
     int8_t *dig = (int8_t *)ws + align256((size_t)rows * 16);
     hipLaunchKernelGGL(k_qkprep<true>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const bf16_t *)k.data,
-                       k.sB, k.sH, k.sS, g.Hkv, g.D, Dp64, kv_lo, len, kv_pad, rows, info, dig);
+                       k.sB, k.sH, k.sS, g.Hkv, g.D, Dp64, kv_lo, len, kv_pad, rows, info, dig, nullptr, (int64_t)0,
+                       (int64_t)0, nullptr);
     return hipGetLastError();
 }
 
@@ -388,19 +394,19 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     c += 256;
     int4 *fixlist = (int4 *)c;
     const int64_t krows = g.B * g.Hkv * kv_pad;
-    hipError_t e;
-    {
-        ProfScope prof_("qk_prep", s);
-        hipLaunchKernelGGL(k_qkprep<false>, dim3((unsigned)((bh * ni_pad + 3) / 4)), dim3(256), 0, s,
-                           (const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad, bh * ni_pad,
-                           qinfo, qdig);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = launch_fill_u32((uint32_t *)nfix, 1, 0u, s)) != hipSuccess) return e;
-    }
     // every extent the kernels see must fit 32 bits (offsets are formed in 64)
     const int64_t lim = INT32_MAX;
     if (ni_pad > lim || kv_pad > lim || i0 + ni_pad > lim || kv_hi > lim || key_rows > lim || g.Hq > lim)
         return hipErrorInvalidValue;
+    hipError_t e;
+    {
+        ProfScope prof_("qk_prep", s);
+        // also sets the rowmax keys of the chunk to "empty" and the fix count to 0
+        hipLaunchKernelGGL(k_qkprep<false>, dim3((unsigned)((bh * ni_pad + 3) / 4)), dim3(256), 0, s,
+                           (const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad, bh * ni_pad,
+                           qinfo, qdig, rowmax_keys, key_rows, key_row0, nfix);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     QkArgs a{};
     a.qdig = qdig;
     a.kdig = (const int8_t *)kprep + align256((size_t)krows * 16);
