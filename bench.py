@@ -37,6 +37,23 @@ def visible_pairs(B, Hq, Sq, Skv, causal):
     return B * Hq * Sq * Skv
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/hbm_traffic_<kernel>_<workload>.json: FETCH_SIZE and WRITE_SIZE
+    scaled by a plain copy), or None when there is none or the kernel source
+    changed after the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"hbm_traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(root, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
 def kernel_work(name, pairs, rows, D, kv_elems=0, q_elems=0):
     """(amount, unit, bound) of algorithmic work of one launch of `name`: fp64
     flops of the method's steps for the compute kernels (whatever units run
@@ -66,6 +83,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the sharded / cross-entropy side measurements")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only copy MB megabytes device to device 5 times (the reference kernel for the HBM "
+                         "byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
@@ -74,6 +94,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+        return
 
     from bitwise_deterministic_exact_pass1_amd import _lib, attention, workloads as W
 
@@ -123,7 +152,7 @@ def main():
         else:
             achieved, peak, runit = amount / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
         roofline = {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": runit,
-                    "frac": achieved / peak, "traffic": None}
+                    "frac": achieved / peak, "traffic": measured_traffic(dominant, args.workload)}
     else:
         roofline = {"bound": "alu", "kernel": dominant, "achieved": None, "peak": FP64_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": None, "traffic": None}
