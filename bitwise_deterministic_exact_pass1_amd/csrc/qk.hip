@@ -25,28 +25,32 @@ constexpr int kQKmax = 4;              // digits per Q or K row (32-bit integers
 constexpr int kQKC = 2 * kQKmax - 1;   // shift classes of the product
 constexpr int kQKbad = 99;             // row needs more digits than kQKmax
 
-// Per-row statistics and digits.  One wave per row: grid exponent g (smallest
-// lsb), digit count, log2 bound of max|Xi| (Q) or of sum|Xi| (K); digits in
-// [row][kQKmax][Dp64] bytes, zero padded to a multiple of 64 dims.
-template <bool IS_K>
+// Per-row statistics and digits: grid exponent g (smallest lsb), digit count,
+// log2 bound of max|Xi| (Q) or of sum|Xi| (K); digits in [row][kQKmax][Dp64]
+// bytes, zero padded to a multiple of 64 dims.  16 lanes per row, DPL = Dp64/16
+// consecutive dims per lane, so each digit plane is one DPL-byte store per
+// lane.  The Q pass also starts the rowmax keys of its rows at "empty" and the
+// fix count at 0 (the score pass that follows max-reduces and counts into them).
+template <bool IS_K, int DPL>
 __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, int64_t sB, int64_t sH, int64_t sS,
                                                 int64_t H, int64_t D, int64_t Dp64, int64_t s0, int64_t ns,
                                                 int64_t ns_pad, int64_t nrows, int4 *__restrict__ info,
                                                 int8_t *__restrict__ dig, uint32_t *__restrict__ keys,
                                                 int64_t key_rows, int64_t key_row0, int *__restrict__ nfix) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= nrows) return;
+    const int sub = threadIdx.x & 15;
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (row >= nrows) return;  // whole 16-lane groups leave together
     const int64_t bh = row / ns_pad, ii = row % ns_pad;
     const int64_t b = bh / H, h = bh % H;
     const bool live = ii < ns;
     const bf16_t *xr = x + b * sB + h * sH + (s0 + (live ? ii : 0)) * sS;
-    float v[4];
+    float v[DPL];
     int emax = INT_MIN, lmin = INT_MAX;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int64_t d = lane + 64 * t;
-        v[t] = (live && d < D) ? elem<bf16_t>::to_f32(xr[d]) : 0.0f;
+    for (int t = 0; t < DPL; ++t) {
+        const int64_t d = sub * DPL + t;
+        const float xv = elem<bf16_t>::to_f32(xr[std::min<int64_t>(d, D - 1)]);  // in range; used only if d < D
+        v[t] = (live && d < D) ? xv : 0.0f;
         if (v[t] != 0.0f) {
             const int e = f32_exp(v[t]);
             emax = max(emax, e);
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, in
         }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
+    for (int off = 8; off > 0; off >>= 1) {
         emax = max(emax, __shfl_xor(emax, off, 64));
         lmin = min(lmin, __shfl_xor(lmin, off, 64));
     }
@@ -63,37 +67,67 @@ __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, in
     const int mbits = zero ? 0 : emax + 1 - g;  // |Xi| < 2^mbits
     int nd = zero ? 1 : (mbits + 2 + 7) / 8;
     if (nd > kQKmax) nd = kQKbad;
-    int64_t xi[4];
+    // balanced base-256 digits of |Xi| < 2^30: the bytes of Xi + 0x80808080
+    // with their top bit flipped (digit set [-128, 127])
+    uint32_t U[DPL];
     int64_t l1 = 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        xi[t] = nd == kQKbad ? 0 : (int64_t)ldexp((double)v[t], -g);
-        l1 += xi[t] < 0 ? -xi[t] : xi[t];
+    for (int t = 0; t < DPL; ++t) {
+        const int64_t xi = nd == kQKbad ? 0 : (int64_t)ldexp((double)v[t], -g);
+        l1 += xi < 0 ? -xi : xi;
+        U[t] = (uint32_t)(xi + 0x80808080ll);
     }
     int bound = mbits;
     if (IS_K) {
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) l1 += __shfl_xor(l1, off, 64);
+        for (int off = 8; off > 0; off >>= 1) l1 += __shfl_xor(l1, off, 64);
         bound = l1 ? 64 - __clzll((long long)l1) : 0;  // sum|Ki| < 2^bound
     }
-    if (lane == 0) info[row] = int4{g, nd, bound, 0};
-    if (!IS_K && lane == 0) {  // the score pass that follows max-reduces into these
-        if (keys && live) keys[bh * key_rows + (s0 + ii - key_row0)] = kKeyNegInf;
-        if (row == 0) *nfix = 0;
-    }
-    int8_t *out = dig + row * kQKmax * Dp64;
-#pragma unroll
-    for (int a = 0; a < kQKmax; ++a) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int64_t d = lane + 64 * t;
-            if (d < Dp64) {
-                const int64_t c = ((xi[t] & 255) ^ 128) - 128;
-                xi[t] = (xi[t] - c) >> 8;
-                out[a * Dp64 + d] = (int8_t)c;
-            }
+    if (sub == 0) {
+        info[row] = int4{g, nd, bound, 0};
+        if (!IS_K) {
+            if (keys && live) keys[bh * key_rows + (s0 + ii - key_row0)] = kKeyNegInf;
+            if (row == 0) *nfix = 0;
         }
     }
+    int8_t *out = dig + row * kQKmax * Dp64 + sub * DPL;
+#pragma unroll
+    for (int a = 0; a < kQKmax; ++a) {
+        uint32_t w[DPL / 4];
+#pragma unroll
+        for (int q = 0; q < DPL / 4; ++q) {
+            uint32_t pack = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pack |= ((U[4 * q + u] >> (8 * a)) & 255u) << (8 * u);
+            w[q] = pack ^ 0x80808080u;
+        }
+        uint32_t *o = (uint32_t *)(out + a * Dp64);
+        if constexpr (DPL == 8) {
+            *(uint2 *)o = uint2{w[0], w[1]};
+        } else if constexpr (DPL == 16) {
+            *(uint4 *)o = uint4{w[0], w[1], w[2], w[3]};
+        } else {
+#pragma unroll
+            for (int q = 0; q < DPL / 4; ++q) o[q] = w[q];
+        }
+    }
+}
+
+template <bool IS_K>
+static void launch_qkprep(const bf16_t *x, int64_t sB, int64_t sH, int64_t sS, int64_t H, int64_t D, int64_t Dp64,
+                          int64_t s0, int64_t ns, int64_t ns_pad, int64_t nrows, int4 *info, int8_t *dig,
+                          uint32_t *keys, int64_t key_rows, int64_t key_row0, int *nfix, hipStream_t s) {
+    const dim3 grid((unsigned)((nrows + 15) / 16));
+#define DET_QKPREP(DPL)                                                                                    \
+    hipLaunchKernelGGL((k_qkprep<IS_K, DPL>), grid, dim3(256), 0, s, x, sB, sH, sS, H, D, Dp64, s0, ns, ns_pad, \
+                       nrows, info, dig, keys, key_rows, key_row0, nfix)
+    switch (Dp64 / 16) {
+        case 4: DET_QKPREP(4); break;
+        case 8: DET_QKPREP(8); break;
+        case 12: DET_QKPREP(12); break;
+        default: DET_QKPREP(16); break;
+    }
+#undef DET_QKPREP
 }
 
 constexpr int kQkT = 16;     // rows and keys per matrix-core item
@@ -321,11 +355,17 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
         double acc = 0.0;
         for (int64_t d0 = 0; d0 < D; d0 += kFixDC) {
             __syncthreads();
-            for (int t = tid; t < kQkT * kFixDC; t += 256) {
-                const int rr = t / kFixDC, dd = t % kFixDC;
+            // unconditional loads from clamped (in-range) indices, then a select:
+            // every load of the loop is in flight before the first is used
+#pragma unroll
+            for (int t0 = 0; t0 < kQkT * kFixDC; t0 += 256) {
+                const int t = t0 + tid, rr = t / kFixDC, dd = t % kFixDC;
                 const int64_t d = d0 + dd, i = it0 + rr, j = j0 + rr;
-                sq[rr][dd] = (d < D && i < i_end) ? (double)elem<bf16_t>::to_f32(q[b * qsB + hq * qsH + i * qsS + d]) : 0.0;
-                sk[rr][dd] = (d < D && j < A.kv_hi) ? (double)elem<bf16_t>::to_f32(k[b * ksB + hk * ksH + j * ksS + d]) : 0.0;
+                const int64_t dc = std::min<int64_t>(d, D - 1);
+                const float xq = elem<bf16_t>::to_f32(q[b * qsB + hq * qsH + std::min<int64_t>(i, i_end - 1) * qsS + dc]);
+                const float xk = elem<bf16_t>::to_f32(k[b * ksB + hk * ksH + std::min<int64_t>(j, A.kv_hi - 1) * ksS + dc]);
+                sq[rr][dd] = (d < D && i < i_end) ? (double)xq : 0.0;
+                sk[rr][dd] = (d < D && j < A.kv_hi) ? (double)xk : 0.0;
             }
             __syncthreads();
             const int dn = (int)std::min<int64_t>(kFixDC, D - d0);
@@ -370,9 +410,8 @@ hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, in
     const int64_t kv_pad = qk_pad(len), rows = g.B * g.Hkv * kv_pad;
     int4 *info = (int4 *)ws;
     int8_t *dig = (int8_t *)ws + align256((size_t)rows * 16);
-    hipLaunchKernelGGL(k_qkprep<true>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, (const bf16_t *)k.data,
-                       k.sB, k.sH, k.sS, g.Hkv, g.D, Dp64, kv_lo, len, kv_pad, rows, info, dig, nullptr, (int64_t)0,
-                       (int64_t)0, nullptr);
+    launch_qkprep<true>((const bf16_t *)k.data, k.sB, k.sH, k.sS, g.Hkv, g.D, Dp64, kv_lo, len, kv_pad, rows, info,
+                        dig, nullptr, 0, 0, nullptr, s);
     return hipGetLastError();
 }
 
@@ -402,9 +441,8 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     {
         ProfScope prof_("qk_prep", s);
         // also sets the rowmax keys of the chunk to "empty" and the fix count to 0
-        hipLaunchKernelGGL(k_qkprep<false>, dim3((unsigned)((bh * ni_pad + 3) / 4)), dim3(256), 0, s,
-                           (const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad, bh * ni_pad,
-                           qinfo, qdig, rowmax_keys, key_rows, key_row0, nfix);
+        launch_qkprep<false>((const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad, bh * ni_pad,
+                             qinfo, qdig, rowmax_keys, key_rows, key_row0, nfix, s);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     QkArgs a{};
@@ -450,7 +488,7 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     }
     ProfScope prof_("scores_fix", s);
     const int64_t items = bh * ntiles * nKB;
-    hipLaunchKernelGGL(k_qk_fix, dim3((unsigned)std::min<int64_t>(items, 4096)), dim3(256), 0, s, a,
+    hipLaunchKernelGGL(k_qk_fix, dim3((unsigned)std::min<int64_t>(items, 1024)), dim3(256), 0, s, a,
                        (const bf16_t *)q.data, q.sB, q.sH, q.sS, (const bf16_t *)k.data, k.sB, k.sH, k.sS, g.D);
     return hipGetLastError();
 }
