@@ -131,6 +131,8 @@ static void launch_qkprep(const bf16_t *x, int64_t sB, int64_t sH, int64_t sS, i
 }
 
 constexpr int kQkT = 16;     // rows and keys per matrix-core item
+constexpr int kFixWhole = 1;  // fix-list entry: every pair of the item takes the chain
+constexpr int kFixPairs = 0;  // fix-list entry: the pairs outside their own bound
 constexpr int kQkWaves = 4;  // waves per workgroup, one 16-row tile each: 64-row groups
 
 // Extents are 32-bit (the launcher rejects larger ones); offsets are formed
@@ -141,8 +143,8 @@ struct QkArgs {
     const int4 *qinfo, *kinfo;
     float *scores;  // [bh][ni][W] or null
     uint32_t *keys;  // rowmax keys, [bh*key_rows + i - key_row0], or null
-    int *nfix;       // number of items left to the fp64 chain
-    int4 *fixlist;   // their (kb, tile, bh)
+    int *nfix;       // number of items left (in whole or in part) to the fp64 chain
+    int4 *fixlist;   // their (kb, tile, bh, kFixWhole or kFixPairs)
     double scale;
     int Dp64, ni, ni_pad, i0, kv_lo, kv_hi, kv_pad;
     int Hq, Hkv, group;
@@ -218,9 +220,12 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
     }
     aq = __builtin_amdgcn_readfirstlane(aq);  // wave-uniform after the reduction
     qbt = __builtin_amdgcn_readfirstlane(qbt);
-    int gq[4];
+    int gq[4], qbr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) gq[r] = __shfl(qi.x, 4 * lq + r, 64);
+    for (int r = 0; r < 4; ++r) {
+        gq[r] = __shfl(qi.x, 4 * lq + r, 64);
+        qbr[r] = __shfl(qi.z, 4 * lq + r, 64);
+    }
     uint32_t mkey[4] = {kKeyNegInf, kKeyNegInf, kKeyNegInf, kKeyNegInf};
     float *srow = (A.scores && live) ? A.scores + (bh * A.ni + (it0 + 4 * lq - A.i0)) * (int64_t)A.W : nullptr;
 
@@ -267,12 +272,16 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
             }
             bk = __builtin_amdgcn_readfirstlane(bk);
             kbnd = __builtin_amdgcn_readfirstlane(kbnd);
-            if (aq > kQKmax || bk > kQKmax || qbt + kbnd > 53) {
+            if (aq > kQKmax || bk > kQKmax) {  // rows with more digits: the whole item takes the chain
                 if (lane == 0) {
                     const int at = atomicAdd(A.nfix, 1);
-                    A.fixlist[at] = int4{kb, tile, (int)bh, 0};
+                    A.fixlist[at] = int4{kb, tile, (int)bh, kFixWhole};
                 }
             } else {
+                // pairs within the bound are exact here; when the item's bound does not
+                // hold, each pair is checked against its own row and key bounds and the
+                // others are left to the chain
+                const bool perpair = qbt + kbnd > 53;
                 const uint8_t *krow = S.k[buf] + lr * KROW + 16 * lq;
                 v4i C[kQKC];
 #pragma unroll
@@ -291,6 +300,7 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
                 const int j = j0 + lr;
                 const bool jv = j < A.kv_hi;
                 const int gk = ki.x;
+                bool left = false;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = it0 + 4 * lq + r;
@@ -299,10 +309,16 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
                     for (int c = kQKC - 1; c >= 0; --c) dot = dot * 256 + (int64_t)C[c][r];
                     const double d64 = ldexp((double)dot, gq[r] + gk);  // exact: |dot| < 2^53
                     const float sc = (float)(A.scale * d64);
-                    if (jv && i < i_end) {
+                    const bool ok = !perpair || qbr[r] + ki.z <= 53;
+                    left |= !ok;
+                    if (jv && i < i_end && ok) {
                         if (srow) srow[(int64_t)r * A.W + (j - A.kv_lo)] = sc;
                         if (!A.causal || j <= i) mkey[r] = max(mkey[r], order_key(sc));
                     }
+                }
+                if (__ballot(left) && lane == 0) {
+                    const int at = atomicAdd(A.nfix, 1);
+                    A.fixlist[at] = int4{kb, tile, (int)bh, kFixPairs};
                 }
             }
         }
@@ -334,53 +350,59 @@ __global__ __launch_bounds__(64 * kQkWaves) void k_qk_mfma(QkArgs A) {
     }
 }
 
-// The fp64 chain for the items k_qk_mfma left.  A persistent grid walks the
-// item list; per item the 16 query rows and 16 key rows are staged in LDS as
-// binary64, 64 dims at a time, and each thread runs the chain of one
-// (row, key) pair in ascending d.
-constexpr int kFixDC = 64;
+// The fp64 chain for the pairs k_qk_mfma left: every pair of a kFixWhole
+// item, the pairs of a kFixPairs item whose row bound plus key bound exceeds
+// 53.  Per listed item the workgroup stages its 16 q rows and 16 k rows in LDS
+// as f32 (exact for bf16) with every load issued before the first is used,
+// then one thread per pair that needs it runs the chain in ascending d.
+constexpr int kFixD = 256;
 __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restrict__ q, int64_t qsB, int64_t qsH,
                                                 int64_t qsS, const bf16_t *__restrict__ k, int64_t ksB, int64_t ksH,
                                                 int64_t ksS, int64_t D) {
-    __shared__ double sq[kQkT][kFixDC + 1], sk[kQkT][kFixDC + 1];
+    __shared__ float sq[kQkT][kFixD + 1], sk[kQkT][kFixD + 1];
     const int tid = threadIdx.x;
     const int r = tid >> 4, c = tid & 15;
     const int n = *A.nfix;
+    const int64_t i_end = A.i0 + A.ni;
     for (int it = blockIdx.x; it < n; it += gridDim.x) {
         const int4 item = A.fixlist[it];
         const int64_t kb = item.x, tile = item.y, bh = item.z;
-        const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group;
-        const int64_t it0 = A.i0 + tile * kQkT, i_end = A.i0 + A.ni;
-        const int64_t j0 = A.kv_lo + kb * kQkT;
-        double acc = 0.0;
-        for (int64_t d0 = 0; d0 < D; d0 += kFixDC) {
-            __syncthreads();
-            // unconditional loads from clamped (in-range) indices, then a select:
-            // every load of the loop is in flight before the first is used
+        const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
+        const int64_t it0 = A.i0 + tile * kQkT, j0 = A.kv_lo + kb * kQkT;
+        const bf16_t *qb = q + b * qsB + hq * qsH, *kbp = k + b * ksB + hk * ksH;
+        __syncthreads();  // the previous item's rows are no longer read
+        // thread tid loads dim tid (D <= 256) of the 16 rows of each side; clamped
+        // indices keep every load in range, and clamped values are never used
+        {
+            const int64_t dd = tid < D ? tid : D - 1;
+            float xq[kQkT], xk[kQkT];
 #pragma unroll
-            for (int t0 = 0; t0 < kQkT * kFixDC; t0 += 256) {
-                const int t = t0 + tid, rr = t / kFixDC, dd = t % kFixDC;
-                const int64_t d = d0 + dd, i = it0 + rr, j = j0 + rr;
-                const int64_t dc = std::min<int64_t>(d, D - 1);
-                const float xq = elem<bf16_t>::to_f32(q[b * qsB + hq * qsH + std::min<int64_t>(i, i_end - 1) * qsS + dc]);
-                const float xk = elem<bf16_t>::to_f32(k[b * ksB + hk * ksH + std::min<int64_t>(j, A.kv_hi - 1) * ksS + dc]);
-                sq[rr][dd] = (d < D && i < i_end) ? (double)xq : 0.0;
-                sk[rr][dd] = (d < D && j < A.kv_hi) ? (double)xk : 0.0;
+            for (int rr = 0; rr < kQkT; ++rr) {
+                xq[rr] = elem<bf16_t>::to_f32(qb[std::min<int64_t>(it0 + rr, i_end - 1) * qsS + dd]);
+                xk[rr] = elem<bf16_t>::to_f32(kbp[std::min<int64_t>(j0 + rr, A.kv_hi - 1) * ksS + dd]);
             }
-            __syncthreads();
-            const int dn = (int)std::min<int64_t>(kFixDC, D - d0);
-            for (int dd = 0; dd < dn; ++dd) acc = fma(sq[r][dd], sk[c][dd], acc);
-        }
-        const int64_t i = it0 + r, j = j0 + c;
-        uint32_t m = kKeyNegInf;
-        if (i < i_end && j < A.kv_hi) {
-            const float sc = (float)(A.scale * acc);
-            if (A.scores) A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)] = sc;
-            if (!A.causal || j <= i) m = order_key(sc);
-        }
+            if (tid < D) {
 #pragma unroll
-        for (int off = 8; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-        if (A.keys && c == 0 && i < i_end && m != kKeyNegInf) atomicMax(&A.keys[bh * A.key_rows + (i - A.key_row0)], m);
+                for (int rr = 0; rr < kQkT; ++rr) {
+                    sq[rr][tid] = xq[rr];
+                    sk[rr][tid] = xk[rr];
+                }
+            }
+        }
+        __syncthreads();
+        const int64_t i = it0 + r, j = j0 + c;
+        if (i >= i_end || j >= A.kv_hi) continue;
+        if (item.w == kFixPairs && A.qinfo[bh * A.ni_pad + tile * kQkT + r].z +
+                                           A.kinfo[bhk * A.kv_pad + kb * kQkT + c].z <= 53)
+            continue;
+        // (unrolled: the LDS reads of 16 steps go out together, only the fma chain is serial)
+        double acc = 0.0;
+        const int Di = (int)D;
+#pragma unroll 16
+        for (int d = 0; d < Di; ++d) acc = fma((double)sq[r][d], (double)sk[c][d], acc);
+        const float sc = (float)(A.scale * acc);
+        if (A.scores) A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)] = sc;
+        if (A.keys && (!A.causal || j <= i)) atomicMax(&A.keys[bh * A.key_rows + (i - A.key_row0)], order_key(sc));
     }
 }
 
@@ -488,7 +510,7 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     }
     ProfScope prof_("scores_fix", s);
     const int64_t items = bh * ntiles * nKB;
-    hipLaunchKernelGGL(k_qk_fix, dim3((unsigned)std::min<int64_t>(items, 1024)), dim3(256), 0, s, a,
+    hipLaunchKernelGGL(k_qk_fix, dim3((unsigned)std::min<int64_t>(items, 2048)), dim3(256), 0, s, a,
                        (const bf16_t *)q.data, q.sB, q.sH, q.sS, (const bf16_t *)k.data, k.sB, k.sH, k.sS, g.D);
     return hipGetLastError();
 }
