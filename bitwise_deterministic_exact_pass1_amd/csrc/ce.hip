@@ -179,12 +179,361 @@ __global__ void k_ce_backward(const void *x, int64_t N, int64_t V, int64_t ld, c
     }
 }
 
+// ---------------------------------------------------------------- bf16 pattern tables
+//
+// A bf16 logit is one of 2^16 bit patterns and its weight depends on nothing
+// else in the row, so the exact sum over a row equals the exact sum over
+// patterns of count(pattern) * w(pattern), and a gradient row is a lookup of
+// g(pattern) (plus the target column).  The tables cover a window of 32
+// binades of |x|, both signs (8192 patterns), placed per row from a sample of
+// its values with four times headroom above the largest sampled magnitude;
+// patterns outside the window take the per-element rules instead.  Both forms
+// give the same bits: integer counts times exact f32 weights, summed exactly.
+
+constexpr int kTT = 256;                   // threads of a row workgroup
+constexpr int kHalf = 32 * 128;            // patterns per sign: 32 binades x 128 mantissas
+constexpr int kTab = 2 * kHalf;            // table slots
+constexpr int kSlots = kTab / kTT;         // slots per thread (32)
+constexpr int kQcap = 2048;                // out-of-window patterns kept per row
+constexpr int64_t kTabMinLen = kTab;       // shorter ranges use the per-element kernels
+constexpr int64_t kCountMax = (int64_t)1 << 29;  // count * w stays exact in binary64
+
+__device__ __forceinline__ float bf16_value(uint32_t c) { return __uint_as_float(c << 16); }
+
+// Slot of pattern c in the window starting at magnitude pattern `base`, or a
+// value >= kTab when c lies outside it.  Slot bit 12 is the sign.
+__device__ __forceinline__ uint32_t tab_slot(uint32_t c, uint32_t base) {
+    const uint32_t a = (c & 0x7fffu) - base;
+    return a < (uint32_t)kHalf ? (a | ((c >> 3) & 0x1000u)) : 0xffffffffu;
+}
+__device__ __forceinline__ uint32_t slot_code(uint32_t s, uint32_t base) {
+    return ((s & (kHalf - 1)) + base) | ((s & kHalf) << 3);
+}
+
+// Split [v_lo, v_hi) of one row into a scalar head (up to the first 16-byte
+// boundary), whole 16-byte vectors of 8 patterns, and a scalar tail.
+struct RowSplit {
+    int64_t head, nvec, tail0, len;
+    __device__ RowSplit(const uint16_t *p0, int64_t len_) : len(len_) {
+        head = min((int64_t)((((uintptr_t)0 - (uintptr_t)p0) & 15) >> 1), len);
+        nvec = (len - head) >> 3;
+        tail0 = head + nvec * 8;
+    }
+    // offset (from v_lo) of the j-th scalar element, j < nscalar()
+    __device__ int64_t scalar_at(int64_t j) const { return j < head ? j : tail0 + (j - head); }
+    __device__ int64_t nscalar() const { return head + (len - tail0); }
+};
+
+// Window base for a row: the largest magnitude among the first vector of each
+// thread (or its first scalar), reduced over the workgroup.
+__device__ __forceinline__ uint32_t pick_window(const uint16_t *p0, const RowSplit &rs, uint32_t *red) {
+    const int tid = threadIdx.x;
+    uint32_t mag = 0;
+    if (tid < rs.nvec) {
+        const uint4 u = ((const uint4 *)(p0 + rs.head))[tid];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) mag = max(mag, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
+    } else if (tid < rs.nscalar()) {
+        mag = p0[rs.scalar_at(tid)] & 0x7fffu;
+    }
+    const uint32_t top = block_max_key(mag, red) >> 7;  // exponent field of the largest sample
+    const int lo = max(0, (int)top + 2 - 31);
+    return (uint32_t)lo << 7;
+}
+
+struct HistShared {
+    uint32_t hist[kTab];
+    uint16_t q[kQcap];
+    int64_t sd[kDenDigits];
+    uint32_t red[kTT / 64];
+    uint32_t qn;
+};
+
+__device__ __forceinline__ void hist_put(HistShared &S, uint32_t c, uint32_t base) {
+    const uint32_t s = tab_slot(c, base);
+    if (s < (uint32_t)kTab) {
+        atomicAdd(&S.hist[s], 1u);
+    } else {
+        const uint32_t pos = atomicAdd(&S.qn, 1u);
+        if (pos < (uint32_t)kQcap) S.q[pos] = (uint16_t)c;
+    }
+}
+
+__device__ __forceinline__ void hist_put8(HistShared &S, const uint4 u, uint32_t base) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t s[8];
+    bool out = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        s[2 * k] = tab_slot(w[k] & 0xffffu, base);
+        s[2 * k + 1] = tab_slot(w[k] >> 16, base);
+        out |= (s[2 * k] | s[2 * k + 1]) >= (uint32_t)kTab;
+    }
+    if (!out) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) atomicAdd(&S.hist[s[k]], 1u);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            hist_put(S, w[k] & 0xffffu, base);
+            hist_put(S, w[k] >> 16, base);
+        }
+    }
+}
+
+// Exact weight sum of one row range through the pattern histogram.  FWD: the
+// range is the whole row, the row max comes from the histogram, and the loss,
+// max and RN64(den) are written; otherwise the caller's max is used and the
+// digits go to den[k*N + i] (added to what is there when add_into).
+template <bool FWD>
+__global__ __launch_bounds__(kTT) void k_ce_hist(const uint16_t *x, int64_t N, int64_t ld, int64_t v_lo,
+                                                 int64_t v_hi, const int64_t *targets, const float *rowmax_in,
+                                                 float *loss, float *rowmax_out, double *denom, int64_t *den,
+                                                 int add_into) {
+    __shared__ HistShared S;
+    const int tid = threadIdx.x;
+    const int64_t i = blockIdx.x;
+    const uint16_t *p0 = x + i * ld + v_lo;
+    const RowSplit rs(p0, v_hi - v_lo);
+
+    for (int k = tid; k < kTab / 4; k += kTT) ((uint4 *)S.hist)[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid < kDenDigits) S.sd[tid] = 0;
+    if (tid == 0) S.qn = 0;
+    const uint32_t base = pick_window(p0, rs, S.red);  // synchronizes
+
+    const uint4 *vp = (const uint4 *)(p0 + rs.head);
+    int64_t k = tid;
+    for (; k + 3 * kTT < rs.nvec; k += 4 * kTT) {
+        const uint4 u0 = vp[k], u1 = vp[k + kTT], u2 = vp[k + 2 * kTT], u3 = vp[k + 3 * kTT];
+        hist_put8(S, u0, base);
+        hist_put8(S, u1, base);
+        hist_put8(S, u2, base);
+        hist_put8(S, u3, base);
+    }
+    for (; k < rs.nvec; k += kTT) hist_put8(S, vp[k], base);
+    for (int64_t j = tid; j < rs.nscalar(); j += kTT) hist_put(S, p0[rs.scalar_at(j)], base);
+    __syncthreads();
+
+    const uint32_t qn = S.qn;
+    const bool over = qn > (uint32_t)kQcap;  // some outside patterns were not kept: rescan for them
+    uint32_t cnt[kSlots];
+#pragma unroll
+    for (int j = 0; j < kSlots / 4; ++j) {
+        const uint4 c4 = ((const uint4 *)S.hist)[tid * (kSlots / 4) + j];
+        cnt[4 * j] = c4.x;
+        cnt[4 * j + 1] = c4.y;
+        cnt[4 * j + 2] = c4.z;
+        cnt[4 * j + 3] = c4.w;
+    }
+    const uint32_t s0 = (uint32_t)tid * kSlots;
+
+    float m;
+    if (FWD) {
+        uint32_t key = kKeyNegInf;
+#pragma unroll
+        for (int j = 0; j < kSlots; ++j)
+            if (cnt[j]) key = max(key, order_key(bf16_value(slot_code(s0 + j, base))));
+        if (!over) {
+            for (uint32_t q = tid; q < qn; q += kTT) key = max(key, order_key(bf16_value(S.q[q])));
+        } else {
+            for (int64_t j = tid; j < rs.len; j += kTT) {
+                const uint32_t c = p0[j];
+                if (tab_slot(c, base) >= (uint32_t)kTab) key = max(key, order_key(bf16_value(c)));
+            }
+        }
+        m = key_value(block_max_key(key, S.red));
+    } else {
+        m = rowmax_in[i];
+    }
+
+    Window win;
+    win.init();
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+        if (cnt[j]) {
+            const float w = weight(bf16_value(slot_code(s0 + j, base)), m);
+            if (w != 0.0f) {
+                const double t = (double)w * (double)cnt[j];  // exact: 24 x 29 bits
+                const int ew = f32_exp(w);
+                win.add<kDenDigits>(t, max(ew, -126) - 23, f64_exp(t) + 1, kDenGcap, kDenElo, S.sd, 1);
+            }
+        }
+    }
+    auto add_one = [&](uint32_t c) {
+        const float w = weight(bf16_value(c), m);
+        if (w != 0.0f) {
+            const int ew = f32_exp(w);
+            win.add<kDenDigits>((double)w, max(ew, -126) - 23, ew + 1, kDenGcap, kDenElo, S.sd, 1);
+        }
+    };
+    if (!over) {
+        for (uint32_t q = tid; q < qn; q += kTT) add_one(S.q[q]);
+    } else {
+        for (int64_t j = tid; j < rs.len; j += kTT) {
+            const uint32_t c = p0[j];
+            if (tab_slot(c, base) >= (uint32_t)kTab) add_one(c);
+        }
+    }
+    win.flush<kDenDigits>(kDenElo, S.sd, 1);
+    __syncthreads();
+    if (tid == 0) {
+        int64_t d[kDenDigits];
+#pragma unroll
+        for (int q = 0; q < kDenDigits; ++q) d[q] = S.sd[q] + ((!FWD && add_into) ? den[q * N + i] : 0);
+        canonicalize<kDenDigits>(d);
+        if (FWD) {
+            rowmax_out[i] = m;
+            ce_loss<bf16_t>(d, x, ld, i, targets[i], m, loss, denom);
+        } else {
+#pragma unroll
+            for (int q = 0; q < kDenDigits; ++q) den[q * N + i] = d[q];
+        }
+    }
+}
+
+// Row max of bf16 logits over [v_lo, v_hi): as signed 16-bit integers the
+// non-negative patterns order like their values (+0 above -0) and the negative
+// ones in reverse, so the max is the largest integer when it is >= 0 and the
+// smallest integer otherwise.
+__global__ __launch_bounds__(kTT) void k_ce_rowmax_bf16(const uint16_t *x, int64_t ld, int64_t v_lo, int64_t v_hi,
+                                                        float *rowmax) {
+    __shared__ uint32_t red[kTT / 64];
+    const int tid = threadIdx.x;
+    const int64_t i = blockIdx.x;
+    const uint16_t *p0 = x + i * ld + v_lo;
+    const RowSplit rs(p0, v_hi - v_lo);
+    int hi = -32769, lo = 32768;
+    const uint4 *vp = (const uint4 *)(p0 + rs.head);
+    auto take = [&](uint32_t w) {
+        const int a = (int)(int16_t)(w & 0xffffu), b = (int)(int16_t)(w >> 16);
+        hi = max(hi, max(a, b));
+        lo = min(lo, min(a, b));
+    };
+    int64_t k = tid;
+    for (; k + 3 * kTT < rs.nvec; k += 4 * kTT) {
+        const uint4 u0 = vp[k], u1 = vp[k + kTT], u2 = vp[k + 2 * kTT], u3 = vp[k + 3 * kTT];
+        take(u0.x); take(u0.y); take(u0.z); take(u0.w);
+        take(u1.x); take(u1.y); take(u1.z); take(u1.w);
+        take(u2.x); take(u2.y); take(u2.z); take(u2.w);
+        take(u3.x); take(u3.y); take(u3.z); take(u3.w);
+    }
+    for (; k < rs.nvec; k += kTT) {
+        const uint4 u = vp[k];
+        take(u.x); take(u.y); take(u.z); take(u.w);
+    }
+    for (int64_t j = tid; j < rs.nscalar(); j += kTT) {
+        const int a = (int)(int16_t)p0[rs.scalar_at(j)];
+        hi = max(hi, a);
+        lo = min(lo, a);
+    }
+    // keys: order_key of the candidate values (an empty range keeps -inf)
+    uint32_t key = kKeyNegInf;
+    if (hi >= 0) key = order_key(bf16_value((uint32_t)hi));
+    else if (lo <= 32767) key = order_key(bf16_value((uint32_t)(uint16_t)(int16_t)lo));
+    const float m = key_value(block_max_key(key, red));
+    if (tid == 0) rowmax[i] = m;
+}
+
+// g = RN32(RN64(RN64(w / den64) - [target]) * c)
+__device__ __forceinline__ float grad_value(float x, float m, double d64, double c, bool target) {
+    const double p = (double)weight(x, m) / d64;
+    return (float)((p - (target ? 1.0 : 0.0)) * c);
+}
+
+__device__ __forceinline__ double grad_scale(const float *grad_loss, int reduction, int64_t N, int64_t i) {
+    if (reduction == 0) return (double)grad_loss[i];
+    if (reduction == 1) return (double)grad_loss[0] / (double)N;
+    return (double)grad_loss[0];
+}
+
+// Gradient rows of bf16 logits: one workgroup per row builds g(pattern) for the
+// window's 8192 patterns, then streams the row through the table.
+__global__ __launch_bounds__(kTT) void k_ce_backward_tab(const uint16_t *x, int64_t N, int64_t V, int64_t ld,
+                                                         const int64_t *targets, const float *rowmax,
+                                                         const double *denom, const float *grad_loss,
+                                                         int reduction, float *grad, int64_t grad_ld) {
+    __shared__ float tab[kTab];
+    __shared__ uint32_t red[kTT / 64];
+    const int tid = threadIdx.x;
+    const int64_t i = blockIdx.x;
+    const uint16_t *p0 = x + i * ld;
+    float *o = grad + i * grad_ld;
+    const RowSplit rs(p0, V);
+    const float m = rowmax[i];
+    const double d64 = denom[i];
+    const double c = grad_scale(grad_loss, reduction, N, i);
+    const int64_t t = targets[i];
+    const uint32_t base = pick_window(p0, rs, red);
+    for (int s = tid; s < kTab; s += kTT) tab[s] = grad_value(bf16_value(slot_code(s, base)), m, d64, c, false);
+    __syncthreads();
+
+    const uint4 *vp = (const uint4 *)(p0 + rs.head);
+    const bool vec_out = (((uintptr_t)(o + rs.head)) & 15) == 0;
+    auto one = [&](uint32_t code, int64_t v) {
+        const uint32_t s = tab_slot(code, base);
+        if (s < (uint32_t)kTab && v != t) return tab[s];
+        return grad_value(bf16_value(code), m, d64, c, v == t);
+    };
+    auto row8 = [&](const uint4 u, int64_t k) {
+        const int64_t v0 = rs.head + 8 * k;
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        float g[8];
+        uint32_t s[8];
+        bool slow = (uint64_t)(t - v0) < 8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            s[2 * q] = tab_slot(w[q] & 0xffffu, base);
+            s[2 * q + 1] = tab_slot(w[q] >> 16, base);
+            slow |= (s[2 * q] | s[2 * q + 1]) >= (uint32_t)kTab;
+        }
+        if (!slow) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) g[q] = tab[s[q]];
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                g[2 * q] = one(w[q] & 0xffffu, v0 + 2 * q);
+                g[2 * q + 1] = one(w[q] >> 16, v0 + 2 * q + 1);
+            }
+        }
+        if (vec_out) {
+            ((float4 *)(o + v0))[0] = make_float4(g[0], g[1], g[2], g[3]);
+            ((float4 *)(o + v0))[1] = make_float4(g[4], g[5], g[6], g[7]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[v0 + q] = g[q];
+        }
+    };
+    int64_t k = tid;
+    for (; k + 3 * kTT < rs.nvec; k += 4 * kTT) {
+        const uint4 u0 = vp[k], u1 = vp[k + kTT], u2 = vp[k + 2 * kTT], u3 = vp[k + 3 * kTT];
+        row8(u0, k);
+        row8(u1, k + kTT);
+        row8(u2, k + 2 * kTT);
+        row8(u3, k + 3 * kTT);
+    }
+    for (; k < rs.nvec; k += kTT) row8(vp[k], k);
+    for (int64_t j = tid; j < rs.nscalar(); j += kTT) {
+        const int64_t v = rs.scalar_at(j);
+        o[v] = one(p0[v], v);
+    }
+}
+
+// The pattern-table kernels need 2-byte aligned rows and pay off from a range of
+// about a table's size; counts must stay below 2^29 for exact products.
+static bool bf16_rows_ok(const void *x) { return ((uintptr_t)x & 1) == 0; }
+static bool use_tables(int64_t len) { return len >= kTabMinLen && len < kCountMax; }
+
 hipError_t launch_ce_rowmax(const void *x, int dtype, int64_t N, int64_t ld, int64_t v_lo, int64_t v_hi,
                             float *rowmax, hipStream_t s) {
     ProfScope prof_("ce_rowmax", s);
     if (N <= 0) return hipSuccess;
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_rowmax<float>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, ld, v_lo, v_hi, rowmax);
+    else if (bf16_rows_ok(x))
+        hipLaunchKernelGGL(k_ce_rowmax_bf16, dim3((unsigned)N), dim3(kTT), 0, s, (const uint16_t *)x, ld, v_lo, v_hi,
+                           rowmax);
     else
         hipLaunchKernelGGL(k_ce_rowmax<bf16_t>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, ld, v_lo, v_hi,
                            rowmax);
@@ -198,6 +547,9 @@ hipError_t launch_ce_denom(const void *x, int dtype, int64_t N, int64_t ld, cons
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_denom<float>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, N, ld, rowmax, v_lo,
                            v_hi, den, add_into);
+    else if (bf16_rows_ok(x) && use_tables(v_hi - v_lo))
+        hipLaunchKernelGGL(k_ce_hist<false>, dim3((unsigned)N), dim3(kTT), 0, s, (const uint16_t *)x, N, ld, v_lo,
+                           v_hi, nullptr, rowmax, nullptr, nullptr, nullptr, den, add_into);
     else
         hipLaunchKernelGGL(k_ce_denom<bf16_t>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, N, ld, rowmax, v_lo,
                            v_hi, den, add_into);
@@ -225,6 +577,9 @@ hipError_t launch_ce_forward(const void *x, int dtype, int64_t N, int64_t V, int
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_forward<float>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, V, ld, targets, loss,
                            rowmax, denom);
+    else if (bf16_rows_ok(x) && use_tables(V))
+        hipLaunchKernelGGL(k_ce_hist<true>, dim3((unsigned)N), dim3(kTT), 0, s, (const uint16_t *)x, N, ld, (int64_t)0,
+                           V, targets, nullptr, loss, rowmax, denom, nullptr, 0);
     else
         hipLaunchKernelGGL(k_ce_forward<bf16_t>, dim3((unsigned)N), dim3(kCeThreads), 0, s, x, V, ld, targets,
                            loss, rowmax, denom);
@@ -245,6 +600,9 @@ hipError_t launch_ce_backward(const void *x, int dtype, int64_t N, int64_t V, in
     if (dtype == 0)
         hipLaunchKernelGGL(k_ce_backward<float>, ce_grid(N * V), dim3(256), 0, s, x, N, V, ld, targets, rowmax,
                            denom, grad_loss, reduction, grad, grad_ld);
+    else if (bf16_rows_ok(x) && use_tables(V))
+        hipLaunchKernelGGL(k_ce_backward_tab, dim3((unsigned)N), dim3(kTT), 0, s, (const uint16_t *)x, N, V, ld,
+                           targets, rowmax, denom, grad_loss, reduction, grad, grad_ld);
     else
         hipLaunchKernelGGL(k_ce_backward<bf16_t>, ce_grid(N * V), dim3(256), 0, s, x, N, V, ld, targets, rowmax,
                            denom, grad_loss, reduction, grad, grad_ld);

@@ -127,3 +127,85 @@ def test_f32_logits_small(CE, oracle):
     g = CE.backward(x.cuda(), t.cuda(), m, denom, torch.ones(1).cuda(), "sum")
     ref = oracle.ce_backward(x, t, rm, rd, np.ones(1, np.float32), "sum")
     assert np.array_equal(u32(g), u32(ref))
+
+
+def edge_logits():
+    """bf16 rows that reach every branch of the pattern-table kernels: a row view
+    with an odd row stride and a start offset of 3 (scalar heads and tails), rows
+    whose maximum is negative, +0 or -0, rows with most patterns outside the
+    32-binade window (the out-of-window queue overflows and the row is scanned
+    again), a few outliers (queue without overflow), tiny magnitudes, weights
+    that underflow to zero, constant rows, and targets in the head and tail."""
+    g = torch.Generator().manual_seed(46)
+    N, V = 16, 20011
+    big = torch.randn(N, V + 8, generator=g) * 2.0
+    x = big[:, 3:3 + V]
+    x[1] = -x[1].abs() - 1.0
+    x[2] = -x[2].abs()
+    x[2, 100:140] = -0.0
+    x[2, 7777] = 0.0
+    x[3] = -x[3].abs()
+    x[3, 5000:5010] = -0.0
+    e = torch.randint(-60, 12, (V,), generator=g).float()
+    s = torch.where(torch.rand(V, generator=g) < 0.5, -1.0, 1.0)
+    x[4] = s * torch.exp2(e) * (1 + torch.rand(V, generator=g))
+    x[5] = torch.randn(V, generator=g)
+    idx = 3000 + torch.randperm(V - 3000, generator=g)[:100]   # beyond the sampled first vectors
+    x[5, idx] = torch.where(torch.rand(100, generator=g) < 0.5, -1.0, 1.0) * torch.exp2(
+        torch.randint(8, 14, (100,), generator=g).float())
+    x[6] = torch.randn(V, generator=g) * 2.0 ** -40
+    x[6, :7] = torch.randn(7, generator=g)
+    x[7] = torch.randn(V, generator=g) * 200.0
+    x[8] = 1.5
+    x[9, 0] = 40.0
+    x[10, V - 1] = 40.0
+    xb = big.to(torch.bfloat16)[:, 3:3 + V]
+    t = torch.randint(0, V, (N,), generator=g)
+    t[9], t[10], t[11] = 0, V - 1, 2
+    return xb, t
+
+
+@pytest.fixture(scope="module")
+def edge(CE):
+    say("ce: edge rows N=16 V=20011 bf16, row stride 20019, offset 3")
+    x, t = edge_logits()
+    assert x.stride(0) == 20019 and x.storage_offset() == 3
+    return x, t, x.cuda(), t.cuda()
+
+
+def test_pattern_tables_forward_edge_rows(CE, edge, oracle):
+    x, t, X, T = edge
+    loss, m, denom = CE.forward(X, T)
+    rl, rm, rd = oracle.ce_forward(x, t)
+    assert np.array_equal(u32(m), u32(rm))
+    assert np.array_equal(denom.cpu().numpy(), rd)
+    assert np.array_equal(u32(loss), u32(rl))
+    assert u32(m)[2] == 0 and u32(m)[3] == 0x80000000  # +0 and -0 maxima
+
+
+def test_pattern_tables_split_digits_edge_rows(CE, edge, oracle):
+    x, t, X, T = edge
+    V = X.shape[1]
+    shards = [(0, 8203), (8203, 16411), (16411, V)]   # 8203 and 8208 long: both use the tables
+    ms = [CE.rowmax(X, lo, hi) for lo, hi in shards]
+    for (lo, hi), mm in zip(shards, ms):
+        assert np.array_equal(u32(mm), u32(oracle.ce_rowmax(x, lo, hi)))
+    gm = torch.stack(ms).amax(0)
+    loss, m, denom = CE.forward(X, T)
+    assert torch.equal(gm, m)
+    den = None
+    for lo, hi in shards:
+        part = CE.denom_digits(X, gm, lo, hi)
+        assert np.array_equal(part.cpu().numpy(), oracle.ce_denom_digits(x, gm.cpu().numpy(), lo, hi))
+        den = CE.denom_digits(X, gm, lo, hi) if den is None else CE.denom_digits(X, gm, lo, hi, out=den)
+    l2, d2 = CE.finalize(den, X, T, gm)
+    assert torch.equal(l2, loss) and torch.equal(d2, denom)
+
+
+def test_pattern_tables_gradient_edge_rows(CE, edge, oracle):
+    x, t, X, T = edge
+    loss, m, denom = CE.forward(X, T)
+    g = torch.linspace(-1.5, 1.5, X.shape[0])  # negative upstream values give -0 gradients
+    grad = CE.backward(X, T, m, denom, g.cuda(), "none")
+    ref = oracle.ce_backward(x, t, m.cpu().numpy(), denom.cpu().numpy(), g.numpy(), "none")
+    assert np.array_equal(u32(grad.cpu().numpy()), u32(ref))
