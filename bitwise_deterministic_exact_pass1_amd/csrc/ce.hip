@@ -198,6 +198,8 @@ constexpr int kQcap = 2048;                // out-of-window patterns kept per ro
 constexpr int64_t kTabMinLen = kTab;       // shorter ranges use the per-element kernels
 constexpr int64_t kCountMax = (int64_t)1 << 29;  // count * w stays exact in binary64
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float bf16_value(uint32_t c) { return __uint_as_float(c << 16); }
 
 // Slot of pattern c in the window starting at magnitude pattern `base`, or a
@@ -304,12 +306,12 @@ __global__ __launch_bounds__(kTT) void k_ce_hist(const uint16_t *x, int64_t N, i
 
     const uint4 *vp = (const uint4 *)(p0 + rs.head);
     int64_t k = tid;
-    for (; k + 3 * kTT < rs.nvec; k += 4 * kTT) {
-        const uint4 u0 = vp[k], u1 = vp[k + kTT], u2 = vp[k + 2 * kTT], u3 = vp[k + 3 * kTT];
-        hist_put8(S, u0, base);
-        hist_put8(S, u1, base);
-        hist_put8(S, u2, base);
-        hist_put8(S, u3, base);
+    for (; k + 7 * kTT < rs.nvec; k += 8 * kTT) {
+        uint4 u[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = vp[k + j * kTT];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hist_put8(S, u[j], base);
     }
     for (; k < rs.nvec; k += kTT) hist_put8(S, vp[k], base);
     for (int64_t j = tid; j < rs.nscalar(); j += kTT) hist_put(S, p0[rs.scalar_at(j)], base);
@@ -468,52 +470,54 @@ __global__ __launch_bounds__(kTT) void k_ce_backward_tab(const uint16_t *x, int6
     for (int s = tid; s < kTab; s += kTT) tab[s] = grad_value(bf16_value(slot_code(s, base)), m, d64, c, false);
     __syncthreads();
 
-    const uint4 *vp = (const uint4 *)(p0 + rs.head);
+    // Four patterns per lane and step: 8-byte loads and 16-byte stores, both
+    // contiguous over the wave; the gradient is written with streaming stores.
     const bool vec_out = (((uintptr_t)(o + rs.head)) & 15) == 0;
     auto one = [&](uint32_t code, int64_t v) {
         const uint32_t s = tab_slot(code, base);
         if (s < (uint32_t)kTab && v != t) return tab[s];
         return grad_value(bf16_value(code), m, d64, c, v == t);
     };
-    auto row8 = [&](const uint4 u, int64_t k) {
-        const int64_t v0 = rs.head + 8 * k;
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-        float g[8];
-        uint32_t s[8];
-        bool slow = (uint64_t)(t - v0) < 8;
+    const uint2 *vp = (const uint2 *)(p0 + rs.head);
+    const int64_t n4 = rs.nvec * 2;
+    auto row4 = [&](const uint2 u, int64_t k) {
+        const int64_t v0 = rs.head + 4 * k;
+        const uint32_t w[2] = {u.x, u.y};
+        float g[4];
+        uint32_t s[4];
+        bool slow = (uint64_t)(t - v0) < 4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 2; ++q) {
             s[2 * q] = tab_slot(w[q] & 0xffffu, base);
             s[2 * q + 1] = tab_slot(w[q] >> 16, base);
             slow |= (s[2 * q] | s[2 * q + 1]) >= (uint32_t)kTab;
         }
         if (!slow) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) g[q] = tab[s[q]];
+            for (int q = 0; q < 4; ++q) g[q] = tab[s[q]];
         } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2; ++q) {
                 g[2 * q] = one(w[q] & 0xffffu, v0 + 2 * q);
                 g[2 * q + 1] = one(w[q] >> 16, v0 + 2 * q + 1);
             }
         }
         if (vec_out) {
-            ((float4 *)(o + v0))[0] = make_float4(g[0], g[1], g[2], g[3]);
-            ((float4 *)(o + v0))[1] = make_float4(g[4], g[5], g[6], g[7]);
+            __builtin_nontemporal_store(f32x4{g[0], g[1], g[2], g[3]}, (f32x4 *)(o + v0));
         } else {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) o[v0 + q] = g[q];
+            for (int q = 0; q < 4; ++q) o[v0 + q] = g[q];
         }
     };
     int64_t k = tid;
-    for (; k + 3 * kTT < rs.nvec; k += 4 * kTT) {
-        const uint4 u0 = vp[k], u1 = vp[k + kTT], u2 = vp[k + 2 * kTT], u3 = vp[k + 3 * kTT];
-        row8(u0, k);
-        row8(u1, k + kTT);
-        row8(u2, k + 2 * kTT);
-        row8(u3, k + 3 * kTT);
+    for (; k + 7 * kTT < n4; k += 8 * kTT) {
+        uint2 u[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) u[j] = vp[k + j * kTT];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) row4(u[j], k + j * kTT);
     }
-    for (; k < rs.nvec; k += kTT) row8(vp[k], k);
+    for (; k < n4; k += kTT) row4(vp[k], k);
     for (int64_t j = tid; j < rs.nscalar(); j += kTT) {
         const int64_t v = rs.scalar_at(j);
         o[v] = one(p0[v], v);
