@@ -188,7 +188,7 @@ size_t bytes_sharded(const AttnGeom &g, bool mfma, int64_t ni, int64_t maxlen) {
     return vprep_bytes(g, maxlen) + score_fixed_bytes(g, mfma, maxlen) + score_chunk_bytes(g, mfma, ni, maxlen) +
            align256((size_t)rows * 4) + align256((size_t)rows * maxlen * 4) + 2 * align256((size_t)rows * 4) +
            align256((size_t)bh * ((ni + 31) / 32) * 4) +
-           2 * (align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8));
+           align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8);
 }
 
 VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
@@ -518,8 +518,6 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         int *flags = c.take<int>(bh * ((ni + 31) / 32));
         int64_t *num_acc = c.take<int64_t>(kNumDigits * rows * g.D);
         int64_t *den_acc = c.take<int64_t>(kDenDigits * rows);
-        int64_t *num_part = c.take<int64_t>(kNumDigits * rows * g.D);
-        int64_t *den_part = c.take<int64_t>(kDenDigits * rows);
         if (c.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
         // pass 1: rowmax of each shard, composed by max
         HIP_TRY(launch_fill_u32((uint32_t *)rm_acc, rows, 0xff800000u, s), "fill rowmax");  // -inf
@@ -531,27 +529,24 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
             HIP_TRY(launch_keys_to_f32(keys, rm_part, bh, ni, ni, 0, s), "rowmax");
             HIP_TRY(launch_rowmax_combine(rm_acc, rm_part, rows, s), "rowmax combine");
         }
-        // pass 2: canonical digits of each shard against the global max, composed by int64 add
+        // pass 2: each shard's digits against the global max, composed by int64 add: the
+        // deposit adds its limbs into the shared accumulator (integer atomics), and one
+        // carry pass at the end makes the sum canonical
         HIP_TRY(launch_fill_i64(num_acc, kNumDigits * rows * g.D, 0, s), "fill num");
         HIP_TRY(launch_fill_i64(den_acc, kDenDigits * rows, 0, s), "fill den");
         for (int32_t a = 0; a < n_splits; ++a) {
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
-            HIP_TRY(launch_fill_i64(num_part, kNumDigits * rows * g.D, 0, s), "fill num");
-            HIP_TRY(launch_fill_i64(den_part, kDenDigits * rows, 0, s), "fill den");
-            if (h > l) {
-                HIP_TRY(launch_vprep(tv, g, l, h, vp, s), "prepare v");
-                HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
-                HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
-                HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, nullptr, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
-                                  num_part, den_part, rows, ni, i0, ff, s),
-                        "deposit");
-            }
-            HIP_TRY(launch_normalize(num_part, rows * g.D, kNumDigits, s), "normalize");
-            HIP_TRY(launch_normalize(den_part, rows, kDenDigits, s), "normalize");
-            HIP_TRY(launch_digits_combine(num_acc, num_part, rows * g.D, kNumDigits, s), "combine");
-            HIP_TRY(launch_digits_combine(den_acc, den_part, rows, kDenDigits, s), "combine");
+            if (h <= l) continue;
+            HIP_TRY(launch_vprep(tv, g, l, h, vp, s), "prepare v");
+            HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
+            HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
+            HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, nullptr, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
+                              num_acc, den_acc, rows, ni, i0, ff, s),
+                    "deposit");
         }
+        HIP_TRY(launch_normalize(num_acc, rows * g.D, kNumDigits, s), "normalize");
+        HIP_TRY(launch_normalize(den_acc, rows, kDenDigits, s), "normalize");
         HIP_TRY(launch_finalize(num_acc, den_acc, rows, ni, i0, bh, g.Hq, i0, i1, g.D, ov, s), "finalize");
     }
     return ok();
