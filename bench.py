@@ -211,6 +211,11 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     res["cross_entropy"] = {"workload": "N=4096 V=128256 bf16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                             "forward_token_vocab_per_s": N * Vv / (fwd_ms / 1e3),
                             "backward_hbm_GBps": N * Vv * 6 / (bwd_ms / 1e3) / 1e9}
+    # the float32 combines the exact path replaces, on the same inputs
+    from bitwise_deterministic_exact_pass1_amd import contrast
+    res["contrast"] = {"attention_4_shard_rotations": contrast.attention_contrast(attention, Q, K, V, [K.shape[2] // 4] * 4,
+                                                                                  causal, scale),
+                       "cross_entropy_vocab_splits": contrast.ce_contrast(CE, X, T)}
     return res
 
 
