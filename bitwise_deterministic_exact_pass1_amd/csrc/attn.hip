@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void k_scores(const double *__restrict__ q64, 
     const int64_t ni = i1 - i0;
     const int64_t ir0 = i0 + (int64_t)blockIdx.y * RT;
     if (ir0 >= i1) return;
-    const int nrows = (int)std::min<int64_t>(RT, i1 - ir0);
+    const int nrows = (int)min64(RT, i1 - ir0);
     const int64_t W = kv_hi - kv_lo;
     const double *qtile = q64 + (bh * ni_pad + (ir0 - i0)) * DP;
     const TK *kbase = kp + b * ksB + hk * ksH;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void k_scores(const double *__restrict__ q64, 
                 const int64_t i = ir0 + r;
                 const float sc = (float)(scale * acc[r]);
                 if (scores && jv) scores[(bh * ni + (i - i0)) * W + (j - kv_lo)] = sc;
-                if (jv && (!causal || j <= i)) mkey[r] = std::max(mkey[r], order_key(sc));
+                if (jv && (!causal || j <= i)) mkey[r] = max(mkey[r], order_key(sc));
             }
         }
     }
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void k_scores(const double *__restrict__ q64, 
         if (r < nrows) {
             uint32_t m = mkey[r];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) m = std::max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+            for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
             if (lane == 0) atomicMax(&rowmax_keys[bh * key_rows + (ir0 + r - key_row0)], m);
         }
     }

@@ -28,27 +28,51 @@ constexpr double kSqrt2 = 0x1.6a09e667f3bcdp+0;
 // (coefficients RN64(1/k!)) in Horner form; times 2^n.  Zero below -104,
 // where the f32 weight underflows to zero anyway.  FMA performs the Horner
 // steps: any correctly rounded binary64 fused multiply-add.
+constexpr double kExpC[14] = {
+    1.0,                      // 1/0!
+    1.0,                      // 1/1!
+    0.5,                      // 1/2!
+    0x1.5555555555555p-3,     // 1/3!
+    0x1.5555555555555p-5,     // 1/4!
+    0x1.1111111111111p-7,     // 1/5!
+    0x1.6c16c16c16c17p-10,    // 1/6!
+    0x1.a01a01a01a01ap-13,    // 1/7!
+    0x1.a01a01a01a01ap-16,    // 1/8!
+    0x1.71de3a556c734p-19,    // 1/9!
+    0x1.27e4fb7789f5cp-22,    // 1/10!
+    0x1.ae64567f544e4p-26,    // 1/11!
+    0x1.1eed8eff8d898p-29,    // 1/12!
+    0x1.6124613a86d09p-33,    // 1/13!
+};
+
+// Cody-Waite reduction of t: n and r with t = n ln2 + r.
+__device__ __forceinline__ double exp_det_reduce(double t, double &n) {
+    n = rint(t * kInvLn2);
+    const double r = fma(-n, kLn2Hi, t);
+    return fma(-n, kLn2Lo, r);
+}
+
+// The Horner steps of N independent arguments, step by step across them, so
+// that their dependency chains interleave.
+template <int N, class FMA>
+__device__ __forceinline__ void exp_det_poly(const double (&r)[N], double (&p)[N], FMA fma_step) {
+#pragma unroll
+    for (int u = 0; u < N; ++u) p[u] = kExpC[13];
+#pragma unroll
+    for (int k = 12; k >= 0; --k) {
+#pragma unroll
+        for (int u = 0; u < N; ++u) p[u] = fma_step(p[u], r[u], kExpC[k]);
+    }
+}
+
 template <class FMA>
 __device__ __forceinline__ double exp_det_with(double t, FMA fma_step) {
     if (t < -104.0) return 0.0;
-    const double n = rint(t * kInvLn2);
-    double r = fma(-n, kLn2Hi, t);
-    r = fma(-n, kLn2Lo, r);
-    double p = 0x1.6124613a86d09p-33;             // 1/13!
-    p = fma_step(p, r, 0x1.1eed8eff8d898p-29);  // 1/12!
-    p = fma_step(p, r, 0x1.ae64567f544e4p-26);  // 1/11!
-    p = fma_step(p, r, 0x1.27e4fb7789f5cp-22);  // 1/10!
-    p = fma_step(p, r, 0x1.71de3a556c734p-19);  // 1/9!
-    p = fma_step(p, r, 0x1.a01a01a01a01ap-16);  // 1/8!
-    p = fma_step(p, r, 0x1.a01a01a01a01ap-13);  // 1/7!
-    p = fma_step(p, r, 0x1.6c16c16c16c17p-10);  // 1/6!
-    p = fma_step(p, r, 0x1.1111111111111p-7);   // 1/5!
-    p = fma_step(p, r, 0x1.5555555555555p-5);   // 1/4!
-    p = fma_step(p, r, 0x1.5555555555555p-3);   // 1/3!
-    p = fma_step(p, r, 0.5);                    // 1/2!
-    p = fma_step(p, r, 1.0);                    // 1/1!
-    p = fma_step(p, r, 1.0);                    // 1/0!
-    return ldexp(p, (int)n);
+    double n;
+    const double r[1] = {exp_det_reduce(t, n)};
+    double p[1];
+    exp_det_poly<1>(r, p, fma_step);
+    return ldexp(p[0], (int)n);
 }
 
 struct FmaPlain {
@@ -102,6 +126,12 @@ __device__ __forceinline__ double log_det(double x) {
     const double ed = (double)e;
     return fma(ed, kLn2Hi, fma(ed, kLn2Lo, 2.0 * (u * q)));
 }
+
+// Value min/max of 64-bit integers (std::min returns a reference, which the
+// compiler has been seen to keep in scratch memory when both operands are
+// temporaries).
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 // ---------------------------------------------------------------- total order
 

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void k_vstats(const TV *__restrict__ vp, int64
     const int t = threadIdx.x, c = t & 31, st = t >> 5;
     const int64_t chunk = blockIdx.x, G = blockIdx.y, bhk = blockIdx.z, b = bhk / Hkv, hk = bhk % Hkv;
     const int64_t len = kv_hi - kv_lo, per = (len + kVChunks - 1) / kVChunks;
-    const int64_t j0 = kv_lo + chunk * per, j1 = std::min<int64_t>(kv_hi, j0 + per);
+    const int64_t j0 = kv_lo + chunk * per, j1 = min64(kv_hi, j0 + per);
     const int64_t d = G * 32 + c;
     int emax = INT_MIN, lmin = INT_MAX;
     if (d < D) {
@@ -234,13 +234,26 @@ __device__ __forceinline__ float pv_rowmax(const PvArgs &A, int64_t bh, int64_t 
 // representation).  Digit a of the KPT keys goes to dst + a*1024 (MFMA lane
 // order, set up by the caller).  Returns the mask of digits nonzero for this
 // thread and adds W to wsum.
+//
+// Every key runs the same instructions: exp_det's cutoff (t < -104 gives 0)
+// and the visibility are selects after the arithmetic, on an argument clamped
+// to [-105, 1] (equal to t wherever the result is kept; t > 0 only when the
+// row max is below a score, and then w > 1 sets bad either way), so the KPT
+// exp chains interleave instead of running one after another.
 template <int KPT>
 __device__ __forceinline__ uint32_t block_weights(const float (&sc)[KPT], float m, int nv, uint8_t *dst,
                                                   int64_t &wsum, bool &bad) {
+    double t[KPT], n[KPT], r[KPT], p[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        t[u] = (double)sc[u] - (double)m;
+        r[u] = exp_det_reduce(fmin(fmax(t[u], -105.0), 1.0), n[u]);
+    }
+    exp_det_poly<KPT>(r, p, FmaVreg{});
     uint64_t U[KPT];
 #pragma unroll
     for (int u = 0; u < KPT; ++u) {
-        const float w = u < nv ? weight(sc[u], m, FmaVreg{}) : 0.0f;
+        const float w = (u < nv && t[u] >= -104.0) ? (float)ldexp(p[u], (int)n[u]) : 0.0f;
         const uint32_t bits = __float_as_uint(w);
         // 0x34000000 = 2^-23, 0x3f800000 = 1
         if (bits != 0 && (bits < 0x34000000u || bits > 0x3f800000u)) bad = true;
@@ -319,7 +332,7 @@ __device__ __forceinline__ PvTile pv_tile_of(const PvArgs &A, int64_t bh, int64_
     T.it0 = A.i0 + tile * 32;
     T.i_end = A.i0 + A.ni;
     T.nG = A.Dp32 / 32;
-    T.jhi = A.causal ? std::min<int64_t>(A.kv_hi, T.it0 + 32) : A.kv_hi;
+    T.jhi = A.causal ? min64(A.kv_hi, T.it0 + 32) : A.kv_hi;
     T.nblk = T.jhi > A.kv_lo ? (int)((T.jhi - A.kv_lo + kKB - 1) / kKB) : 0;
     int bad = A.force_fallback;
     for (int64_t g = 0; g < T.nG; ++g) bad |= A.grpB[T.bhk * T.nG + g] > kBmax;
@@ -342,38 +355,55 @@ __device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t 
     const int64_t i = T.it0 + r;
     const bool rowok = i < T.i_end;
     const float m = rowok ? pv_rowmax(A, bh, i) : 0.0f;
-    const float *srow = A.scores + (bh * A.ni + (rowok ? i - A.i0 : 0)) * A.W - A.kv_lo;
-    // keys this row sees: [kv_lo, jend)
-    const int64_t jend = rowok ? (A.causal ? std::min<int64_t>(T.jhi, i + 1) : T.jhi) : A.kv_lo;
+    // keys this row sees: [kv_lo, jend), counted from this thread's first key
+    // kv_lo + k0 (32-bit: the launcher bounds the key range)
+    const int64_t jend = rowok ? (A.causal ? min64(T.jhi, i + 1) : T.jhi) : A.kv_lo;
+    const int vis0 = (int)(jend - A.kv_lo - k0);
     auto nvis = [&](int kb) {  // visible keys among this thread's KPT keys of block kb
-        const int64_t n = jend - (A.kv_lo + (int64_t)kb * kKB + k0);
-        return (int)std::max<int64_t>(0, std::min<int64_t>(KPT, n));
+        return max(0, min(KPT, vis0 - kb * kKB));
     };
-    // the KPT scores of block kb; every load reads an in-range key (kv_hi > kv_lo
-    // whenever there is a block), the invisible ones are not used
-    const int64_t jlast = A.kv_hi - 1;
+    // The tile's scores through a buffer resource based at its first row: key
+    // kv_lo + j of row r at byte (r W + j) 4.  A lane's offset is fixed and the
+    // block step is the scalar offset, so a load needs no address registers.
+    // Keys past a row's end read the next row or, past the scores array, zero
+    // (buffer bounds); those keys are invisible and their weights discarded.
+    const int64_t row_first = bh * A.ni + (T.it0 - A.i0);
+    const int64_t bytes_left = ((int64_t)gridDim.y * A.ni - row_first) * A.W * 4;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(A.scores + row_first * A.W), (short)0, (int)min64(bytes_left, INT32_MAX), 0x00020000);
+    const int voff = (r * (int)A.W + k0) * 4;
     auto load_scores = [&](int kb, float (&x)[KPT]) {
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) x[u] = srow[std::min<int64_t>(A.kv_lo + (int64_t)kb * kKB + k0 + u, jlast)];
+        for (int u = 0; u < KPT; ++u)
+            x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, voff + 4 * u, kb * kKB * 4, 0));
     };
     float *my0 = &S.sc[0][r][k0], *my1 = &S.sc[1][r][k0];
     int64_t wsum = 0;
     bool bad = false;
+    // Scores travel three blocks ahead of their use: loaded into registers,
+    // parked in this thread's LDS slots one block later, read the block after.
+    float pend[KPT];
     if (T.nblk > 0) {
         float sc[KPT], s1[KPT];
         load_scores(0, sc);
         load_scores(1, s1);
+        load_scores(2, pend);
         const uint32_t nz = wave_or_mask(block_weights<KPT>(sc, m, nvis(0), S.dig[0] + dofs, wsum, bad));
         if (lane == 0) S.mask[0][pw] = nz;
 #pragma unroll
         for (int u = 0; u < KPT; ++u) my1[u] = s1[u];
     }
     __syncthreads();
-    for (int kb = 0; kb < T.nblk; ++kb) {
+    // One block step: weights of block kb+1 into the digit buffer the consumers
+    // read next, scores of block kb+3 into `load`, block kb+2's scores (`park`,
+    // loaded one step earlier) into this thread's LDS slots.  The loop is
+    // unrolled by two so that the two register sets swap roles without copies
+    // (a copy of a register still being loaded would wait for the load).
+    auto step = [&](int kb, float (&park)[KPT], float (&load)[KPT]) {
         const int nb = (kb & 1) ^ 1;
         if (kb + 1 < T.nblk) {
-            float s2[KPT], sc[KPT];
-            load_scores(kb + 2, s2);
+            float sc[KPT];
+            load_scores(kb + 3, load);
             const float *cur = nb ? my1 : my0;
 #pragma unroll
             for (int u = 0; u < KPT; ++u) sc[u] = cur[u];
@@ -381,9 +411,14 @@ __device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t 
             if (lane == 0) S.mask[nb][pw] = nz;
             float *nxt = nb ? my0 : my1;  // block kb+2 uses buffer (kb+2)&1
 #pragma unroll
-            for (int u = 0; u < KPT; ++u) nxt[u] = s2[u];
+            for (int u = 0; u < KPT; ++u) nxt[u] = park[u];
         }
         __syncthreads();
+    };
+    float pend2[KPT];
+    for (int kb = 0; kb < T.nblk; kb += 2) {
+        step(kb, pend, pend2);
+        if (kb + 1 < T.nblk) step(kb + 1, pend2, pend);
     }
     // exact row sums of W: the TPR threads of a row are consecutive lanes
 #pragma unroll
@@ -556,7 +591,7 @@ __device__ void fallback_tile(const PvArgs &A, const TV *__restrict__ vp, int64_
         if (i >= i_end) continue;
         const int64_t row = bh * A.ni + (i - A.i0);
         const float m = pv_rowmax(A, bh, i);
-        const int64_t jend = A.causal ? std::min<int64_t>(A.kv_hi, i + 1) : A.kv_hi;
+        const int64_t jend = A.causal ? min64(A.kv_hi, i + 1) : A.kv_hi;
         const TV *vcol = vp + b * vsB + hk * vsH + (d < D ? d : 0);
         const int64_t prow = prow_of(i);
         Window win;
@@ -700,6 +735,8 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     const int64_t ni = i1 - i0;
     if (ni <= 0) return hipSuccess;
     if (vp.Dp32 > 256) return hipErrorInvalidValue;
+    // key offsets, and byte offsets within a 32-row tile of scores, are 32-bit in the kernel
+    if ((kv_hi - kv_lo + 64) * 32 * 4 > INT32_MAX) return hipErrorInvalidValue;
     const int64_t ntiles = (ni + 31) / 32, bh = g.B * g.Hq;
     PvArgs a{};
     a.scores = scores;

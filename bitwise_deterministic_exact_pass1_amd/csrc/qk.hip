@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, in
 #pragma unroll
     for (int t = 0; t < DPL; ++t) {
         const int64_t d = sub * DPL + t;
-        const float xv = elem<bf16_t>::to_f32(xr[std::min<int64_t>(d, D - 1)]);  // in range; used only if d < D
+        const float xv = elem<bf16_t>::to_f32(xr[min64(d, D - 1)]);  // in range; used only if d < D
         v[t] = (live && d < D) ? xv : 0.0f;
         if (v[t] != 0.0f) {
             const int e = f32_exp(v[t]);
@@ -378,8 +378,8 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
             float xq[kQkT], xk[kQkT];
 #pragma unroll
             for (int rr = 0; rr < kQkT; ++rr) {
-                xq[rr] = elem<bf16_t>::to_f32(qb[std::min<int64_t>(it0 + rr, i_end - 1) * qsS + dd]);
-                xk[rr] = elem<bf16_t>::to_f32(kbp[std::min<int64_t>(j0 + rr, A.kv_hi - 1) * ksS + dd]);
+                xq[rr] = elem<bf16_t>::to_f32(qb[min64(it0 + rr, i_end - 1) * qsS + dd]);
+                xk[rr] = elem<bf16_t>::to_f32(kbp[min64(j0 + rr, A.kv_hi - 1) * ksS + dd]);
             }
             if (tid < D) {
 #pragma unroll
