@@ -153,21 +153,16 @@ __device__ __forceinline__ int clz128(unsigned __int128 u) {
 // rounded) uint64 conversion, with every lower bit folded into bit 0 as a
 // sticky bit: bit 0 lies below the rounding position of a 64-bit value.
 __device__ __forceinline__ double i128_to_f64(int64_t hi, uint64_t lo, int e) {
+    // straight-line (selects only), so that a lane's conversions interleave
     const bool neg = hi < 0;
-    uint64_t mh = (uint64_t)hi, ml = lo;
-    if (neg) {  // |N|: two's complement negation over both words
-        ml = ~ml + 1;
-        mh = ~mh + (ml == 0 ? 1 : 0);
-    }
-    double r;
-    if (mh == 0) {
-        r = ldexp((double)ml, e);
-    } else {
-        const int k = __clzll((long long)mh);
-        const uint64_t top = k ? (mh << k) | (ml >> (64 - k)) : mh;
-        const uint64_t rest = ml << k;
-        r = ldexp((double)(top | (rest != 0 ? 1ull : 0ull)), e + 64 - k);
-    }
+    const unsigned __int128 n = ((unsigned __int128)(uint64_t)hi << 64) | lo;
+    const unsigned __int128 u = neg ? (unsigned __int128)0 - n : n;  // |N|
+    const uint64_t uh = (uint64_t)(u >> 64), ul = (uint64_t)u;
+    const int lz = uh ? __builtin_clzll(uh) : 64 + (ul ? __builtin_clzll(ul) : 64);
+    const int s = max(64 - lz, 0);  // bits of |N| above the low 64: shift them out into the sticky bit
+    const unsigned __int128 below = s ? (((unsigned __int128)1 << s) - 1) : 0;
+    const uint64_t top = (uint64_t)(u >> s) | ((u & below) != 0 ? 1ull : 0ull);
+    const double r = ldexp((double)top, e + s);
     return neg ? -r : r;
 }
 
@@ -431,6 +426,63 @@ __device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t 
     __syncthreads();
 }
 
+// The consumer's block loop for a wave whose group has BV V digits (0: no
+// group, barriers only).  Per block: the six W digit fragments of the block
+// are read from LDS up front, the next block's V digits are fetched into the
+// other register set (the loop is unrolled by two so the sets swap roles
+// without copies), and the class sums C_(a+b) += W_a x V_b run on the matrix
+// cores for the W digit planes the producers marked nonzero.
+template <int BV>
+__device__ __forceinline__ void pv_consume_loop(const PvTile &T, const v4i *vb, int lane, v16i (&C)[kNC],
+                                                PvShared &S) {
+    v4i VA[BV > 0 ? BV : 1], VB[BV > 0 ? BV : 1];
+    if (BV > 0 && T.nblk > 0) {
+#pragma unroll
+        for (int s = 0; s < BV; ++s) VA[s] = vb[s * 64];
+    }
+    __syncthreads();
+    auto step = [&](int kb, const v4i (&cur)[BV > 0 ? BV : 1], v4i (&nxt)[BV > 0 ? BV : 1]) {
+        if (BV > 0) {
+            const int buf = kb & 1;
+            if (kb + 1 < T.nblk) {
+#pragma unroll
+                for (int s = 0; s < BV; ++s) nxt[s] = vb[((int64_t)(kb + 1) * kBmax + s) * 64];
+            }
+            const uint8_t *dg = S.dig[buf] + lane * 16;
+            uint32_t mask = 0;
+#pragma unroll
+            for (int w = 0; w < kPW; ++w) mask |= S.mask[buf][w];
+            mask = __builtin_amdgcn_readfirstlane(mask);
+            // W digit a+1 is read while digit a's products run
+            v4i Acur = *(const v4i *)dg;
+#pragma unroll
+            for (int a = 0; a < kAw; ++a) {
+                const v4i Anext = *(const v4i *)(dg + ((a + 1) % kAw) * 1024);
+                if (mask & (1u << a)) {
+#pragma unroll
+                    for (int s = 0; s < BV; ++s)
+                        C[a + s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Acur, cur[s], C[a + s], 0, 0, 0);
+                }
+                Acur = Anext;
+            }
+            if ((kb % kCarryEvery) == kCarryEvery - 1) {
+                // carry each class into the next so every partial sum stays far below 2^31
+#pragma unroll
+                for (int s = 0; s < kNC - 1; ++s) {
+                    const v16i c = C[s] >> 8;
+                    C[s] -= c << 8;
+                    C[s + 1] += c;
+                }
+            }
+        }
+        __syncthreads();
+    };
+    for (int kb = 0; kb < T.nblk; kb += 2) {
+        step(kb, VA, VB);
+        if (kb + 1 < T.nblk) step(kb + 1, VB, VA);
+    }
+}
+
 // Consumer side of one tile: wave `wave` (< NG) owns 32-dim group G0 + wave.
 template <bool FUSED, int NG>
 __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, int64_t tile, int wave, int par,
@@ -449,48 +501,15 @@ __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, 
     v16i C[kNC];
 #pragma unroll
     for (int s = 0; s < kNC; ++s) C[s] = v16i{0};
-    v4i Bn[kBmax];
-#pragma unroll
-    for (int s = 0; s < kBmax; ++s)
-        if (s < Bv && T.nblk > 0) Bn[s] = vb[s * 64];
-    __syncthreads();
-    for (int kb = 0; kb < T.nblk; ++kb) {
-        const int buf = kb & 1;
-        if (mine) {
-            // this block's V digits (fetched one block earlier), then the next block's
-            v4i Bd[kBmax];
-#pragma unroll
-            for (int s = 0; s < kBmax; ++s) Bd[s] = Bn[s];
-            __builtin_amdgcn_sched_barrier(0);
-            if (kb + 1 < T.nblk) {
-#pragma unroll
-                for (int s = 0; s < kBmax; ++s)
-                    if (s < Bv) Bn[s] = vb[((int64_t)(kb + 1) * kBmax + s) * 64];
-            }
-            uint32_t mask = 0;
-#pragma unroll
-            for (int w = 0; w < kPW; ++w) mask |= S.mask[buf][w];
-            mask = __builtin_amdgcn_readfirstlane(mask);
-#pragma unroll
-            for (int a = 0; a < kAw; ++a) {
-                if (mask & (1u << a)) {
-                    const v4i Aa = *(const v4i *)(S.dig[buf] + (a * 64 + lane) * 16);
-#pragma unroll
-                    for (int s = 0; s < kBmax; ++s)
-                        if (s < Bv) C[a + s] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aa, Bd[s], C[a + s], 0, 0, 0);
-                }
-            }
-            if ((kb % kCarryEvery) == kCarryEvery - 1) {
-                // carry each class into the next so every partial sum stays far below 2^31
-#pragma unroll
-                for (int s = 0; s < kNC - 1; ++s) {
-                    const v16i c = C[s] >> 8;
-                    C[s] -= c << 8;
-                    C[s + 1] += c;
-                }
-            }
-        }
-        __syncthreads();
+    // the block loop with the wave's V digit count as a constant (one copy per
+    // count; a wave without a group only meets the barriers)
+    switch (mine ? Bv : 0) {
+        case 1: pv_consume_loop<1>(T, vb, lane, C, S); break;
+        case 2: pv_consume_loop<2>(T, vb, lane, C, S); break;
+        case 3: pv_consume_loop<3>(T, vb, lane, C, S); break;
+        case 4: pv_consume_loop<4>(T, vb, lane, C, S); break;
+        case 5: pv_consume_loop<5>(T, vb, lane, C, S); break;
+        default: pv_consume_loop<0>(T, vb, lane, C, S); break;
     }
     __syncthreads();
     if (S.bad[par]) {
@@ -510,6 +529,57 @@ __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, 
     }
     const int64_t d = G * 32 + (lane & 31);
     const int g = A.colgrid[T.bhk * A.Dp32 + d];
+    if (FUSED) {
+        // all 16 outputs of the lane first (no branches: their conversions and
+        // divisions interleave), then the stores of the rows that exist
+        // NUM = P_hi 2^48 + P_lo with P_lo = bytes C_0..C_5 (48 bits) and
+        // P_hi = C_9 2^24 + bytes C_8 C_7 C_6: both exact in binary64 while
+        // |P_hi| < 2^53, and then fma(P_hi, 2^48, P_lo) is the correctly rounded
+        // NUM (one rounding).  A lane holding a larger P_hi redoes its outputs
+        // by the 128-bit conversion.
+        float out[16];
+        bool big = false;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+            const uint64_t plo = (uint64_t)((uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) |
+                                            ((uint32_t)C[2][rr] << 16) | ((uint32_t)C[3][rr] << 24)) |
+                                 ((uint64_t)((uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8)) << 32);
+            const int64_t phi = (int64_t)C[9][rr] * (1 << 24) +
+                                (int64_t)((uint32_t)C[6][rr] | ((uint32_t)C[7][rr] << 8) | ((uint32_t)C[8][rr] << 16));
+            big |= (uint64_t)(phi + ((int64_t)1 << 53)) >= ((uint64_t)1 << 54);
+            const double n64 = ldexp(fma((double)phi, 0x1p48, (double)plo), g - kSw);
+            out[rr] = (float)(n64 / S.d64[par][row]);
+        }
+        if (big) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+                const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) | ((uint32_t)C[2][rr] << 16) |
+                                    ((uint32_t)C[3][rr] << 24);
+                const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) | ((uint32_t)C[6][rr] << 16) |
+                                    ((uint32_t)C[7][rr] << 24);
+                const uint64_t lo = ((uint64_t)l1 << 32) | l0;
+                const int64_t hi = (int64_t)C[kNC - 1][rr] * 256 + C[kNC - 2][rr];
+                out[rr] = (float)(i128_to_f64(hi, lo, g - kSw) / S.d64[par][row]);
+            }
+        }
+        // keep the arithmetic here, ahead of the guarded stores (else it is
+        // moved into each store's branch and the outputs run one after another)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) asm volatile("" ::"v"(out[rr]));
+        // the tile's output rows from a wave-uniform base, 32-bit lane offsets
+        // (the launcher bounds 32 rows of output stride)
+        float *ob = A.o + T.b * A.osB + T.hq * A.osH + T.it0 * A.osS;
+        const int nrows = (int)min64(32, T.i_end - T.it0), ostride = (int)A.osS;
+        const bool dok = d < A.D;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+            if (row < nrows && dok) ob[row * ostride + (int)d] = out[rr];
+        }
+        return;
+    }
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
         const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
@@ -521,16 +591,11 @@ __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, 
                             ((uint32_t)C[7][rr] << 24);
         const uint64_t lo = ((uint64_t)l1 << 32) | l0;
         const int64_t hi = (int64_t)C[kNC - 1][rr] * 256 + C[kNC - 2][rr];
-        if (FUSED) {
-            const double n64 = i128_to_f64(hi, lo, g - kSw);
-            A.o[T.b * A.osB + T.hq * A.osH + io * A.osS + d] = (float)(n64 / S.d64[par][row]);
-        } else {
-            const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
-            const int64_t prow = bh * A.rows_per_bh + (io - A.row0);
-            add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, A.num + prow * A.D + d, A.plane_rows * A.D);
-            if (G == 0 && (lane & 31) == 0)
-                add_i128_digits<kDenDigits>((__int128)S.den[par][row], -kSw - kDenElo, A.den + prow, A.plane_rows);
-        }
+        const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
+        const int64_t prow = bh * A.rows_per_bh + (io - A.row0);
+        add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, A.num + prow * A.D + d, A.plane_rows * A.D);
+        if (G == 0 && (lane & 31) == 0)
+            add_i128_digits<kDenDigits>((__int128)S.den[par][row], -kSw - kDenElo, A.den + prow, A.plane_rows);
     }
 }
 
@@ -763,6 +828,7 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     a.ntiles = ntiles;
     a.force_fallback = force_fallback;
     if (o) {
+        if (o->sS < 0 || o->sS * 32 + g.D > INT32_MAX) return hipErrorInvalidValue;  // 32-bit offsets in a tile
         a.o = o->data;
         a.osB = o->sB;
         a.osH = o->sH;
