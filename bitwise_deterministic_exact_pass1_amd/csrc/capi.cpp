@@ -139,19 +139,25 @@ size_t score_chunk_bytes(const AttnGeom &g, bool mfma, int64_t ni, int64_t kv_le
     return mfma ? qk_chunk_bytes(g, ni, kv_len) : align256((size_t)g.B * g.Hq * padded_rows(ni) * g.Dp * 8);
 }
 
-hipError_t prep_keys(const Tensor &tk, const AttnGeom &g, bool mfma, void *kprep, int64_t lo, int64_t hi,
-                     hipStream_t s) {
-    if (!mfma || hi <= lo) return hipSuccess;
-    return launch_qk_kprep(tk, g, lo, hi, kprep, s);
-}
-
-hipError_t run_scores(const Tensor &tq, const Tensor &tk, const AttnGeom &g, bool mfma, const void *kprep,
-                      void *chunk_ws, int64_t i0, int64_t i1, int64_t lo, int64_t hi, float *scores, uint32_t *keys,
-                      int64_t key_rows, int64_t key_row0, hipStream_t s) {
-    // both paths start the rowmax keys of rows [i0, i1) at "empty" themselves
-    if (mfma)
-        return launch_scores_qk(tq, tk, g, kprep, chunk_ws, i0, i1, lo, hi, scores, keys, key_rows, key_row0, s);
+// Scores of rows [i0, i1) against keys [lo, hi), with the rowmax keys when
+// `keys` is set.  prep_k: K's digits for the range are prepared first (the
+// matrix-core path prepares them in the same launch as Q's); vp: V is prepared
+// too (on the matrix-core path beside the score preparation and the score fix,
+// otherwise by its own launches).  Both paths start the rowmax keys of rows
+// [i0, i1) at "empty" themselves.
+hipError_t run_scores(const Tensor &tq, const Tensor &tk, const Tensor &tv, const AttnGeom &g, bool mfma, void *kprep,
+                      bool prep_k, VPrep *vp, void *chunk_ws, int64_t i0, int64_t i1, int64_t lo, int64_t hi,
+                      float *scores, uint32_t *keys, int64_t key_rows, int64_t key_row0, hipStream_t s) {
     hipError_t e;
+    const bool host = mfma && hi > lo && i1 > i0;  // the score launches can carry the preparations
+    if (vp && !host && (e = launch_vprep(tv, g, lo, hi, *vp, s)) != hipSuccess) return e;
+    if (mfma) {
+        if (!host) return hipSuccess;
+        VJob vj{};
+        if (vp) vj = make_vjob(tv, g, lo, hi, *vp);
+        return launch_scores_qk(tq, tk, g, kprep, prep_k, vp ? &vj : nullptr, chunk_ws, i0, i1, lo, hi, scores, keys,
+                                key_rows, key_row0, s);
+    }
     if (keys) {  // keys[h * key_rows + i - key_row0]: one run per head, or one in all when contiguous
         const int64_t bh = g.B * g.Hq, n = i1 - i0;
         const bool whole = key_rows == n && key_row0 == i0;
@@ -299,10 +305,11 @@ int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int
     void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, W));
     uint32_t *keys = c0.take<uint32_t>(bh * chunk);
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
-    HIP_TRY(prep_keys(tk, g, mf, kprep, kv_lo, kv_hi, s), "prepare k");
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, kv_lo, kv_hi, nullptr, keys, ni, i0, s), "scores");
+        HIP_TRY(run_scores(tq, tk, tk, g, mf, kprep, i0 == 0, nullptr, cws, i0, i1, kv_lo, kv_hi, nullptr, keys, ni, i0,
+                           s),
+                "scores");
         HIP_TRY(launch_keys_to_f32(keys, rowmax, bh, ni, g.Sq, i0, s), "rowmax");
     }
     return ok();
@@ -346,14 +353,13 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
         HIP_TRY(launch_fill_i64(num, kNumDigits * rows * g.D, 0, s), "fill num");
         HIP_TRY(launch_fill_i64(den, kDenDigits * rows, 0, s), "fill den");
     }
-    if (W > 0) {
-        HIP_TRY(launch_vprep(tv, g, kv_lo, kv_hi, vp, s), "prepare v");
-        HIP_TRY(prep_keys(tk, g, mf, kprep, kv_lo, kv_hi, s), "prepare k");
-    }
     const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq && W > 0; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk);
-        HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, kv_lo, kv_hi, sc, nullptr, 0, 0, s), "scores");
+        // the first chunk's launches also prepare K and V
+        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, i0 == 0 ? &vp : nullptr, cws, i0, i1, kv_lo, kv_hi, sc,
+                           nullptr, 0, 0, s),
+                "scores");
         HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, nullptr, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr,
                           nullptr, num, den, rows, g.Sq, 0, ff, s),
                 "deposit");
@@ -432,12 +438,13 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     int64_t *fnum = c0.take<int64_t>(kNumDigits * bh * ctiles * 32 * g.D);
     int64_t *fden = c0.take<int64_t>(kDenDigits * bh * ctiles * 32);
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
-    HIP_TRY(launch_vprep(tv, g, 0, g.Skv, vp, s), "prepare v");
-    HIP_TRY(prep_keys(tk, g, mf, kprep, 0, g.Skv, s), "prepare k");
     const int ff = force_fallback();
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, 0, g.Skv, sc, keys, ni, i0, s), "scores");
+        // the first chunk's launches also prepare K and V
+        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, i0 == 0 ? &vp : nullptr, cws, i0, i1, 0, g.Skv, sc, keys,
+                           ni, i0, s),
+                "scores");
         HIP_TRY(launch_pv(tv, g, vp, sc, nullptr, keys, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr,
                           nullptr, 0, 0, 0, ff, s),
                 "deposit");
@@ -524,8 +531,9 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         for (int32_t a = 0; a < n_splits; ++a) {
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
-            HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
-            HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, nullptr, keys, ni, i0, s), "scores");
+            if (h <= l) continue;  // an empty shard has no scores: its max is -inf, the identity
+            HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, nullptr, cws, i0, i1, l, h, nullptr, keys, ni, i0, s),
+                    "scores");
             HIP_TRY(launch_keys_to_f32(keys, rm_part, bh, ni, ni, 0, s), "rowmax");
             HIP_TRY(launch_rowmax_combine(rm_acc, rm_part, rows, s), "rowmax combine");
         }
@@ -538,9 +546,7 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
             if (h <= l) continue;
-            HIP_TRY(launch_vprep(tv, g, l, h, vp, s), "prepare v");
-            HIP_TRY(prep_keys(tk, g, mf, kprep, l, h, s), "prepare k");
-            HIP_TRY(run_scores(tq, tk, g, mf, kprep, cws, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
+            HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, &vp, cws, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
             HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, nullptr, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
                               num_acc, den_acc, rows, ni, i0, ff, s),
                     "deposit");

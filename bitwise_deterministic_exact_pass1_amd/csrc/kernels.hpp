@@ -82,9 +82,24 @@ size_t qk_kprep_bytes(const AttnGeom &g, int64_t kv_len);
 size_t qk_chunk_bytes(const AttnGeom &g, int64_t ni, int64_t kv_len);
 hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws,
                            hipStream_t s);
-hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g, const void *kprep, void *chunk_ws,
-                            int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, float *scores,
-                            uint32_t *rowmax_keys, int64_t key_rows, int64_t key_row0, hipStream_t s);
+// All arguments of the V preparation of one key range (device code in
+// vprep.hpp): V's strides, the group geometry and the prepared arrays.
+struct VJob {
+    const void *v;
+    int dtype;
+    int64_t vsB, vsH, vsS, Hkv, D, Dp32, nG, kv_lo, kv_hi, nKB, nbhk;
+    void *stats;
+    int *colgrid, *grpB;
+    void *vsl;
+};
+// Scores of rows [i0, i1) against keys [kv_lo, kv_hi) on the matrix cores.
+// prep_k: K's digit rows are prepared into kprep in the same launch as Q's;
+// vj (bf16 V, nullable): V's column statistics are computed in that launch and
+// its digit slices in the score-fix launch.  Both need a nonempty range.
+hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g, void *kprep, bool prep_k,
+                            const VJob *vj, void *chunk_ws, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
+                            float *scores, uint32_t *rowmax_keys, int64_t key_rows, int64_t key_row0,
+                            hipStream_t s);
 
 // ---- pass 2 on the matrix cores (pv.hip)
 
@@ -96,6 +111,7 @@ struct VPrep {
     void *slices;
     int64_t Dp32, nKB;
 };
+VJob make_vjob(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp);
 size_t vprep_bytes(const AttnGeom &g, int64_t kv_len);
 // bytes of the V digit slices / of the column statistics within vprep_bytes
 size_t vslice_bytes(const AttnGeom &g, int64_t kv_len);

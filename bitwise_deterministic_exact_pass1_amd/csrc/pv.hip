@@ -20,124 +20,30 @@
 // (k_tile_fallback): results never depend on which path ran.
 #include "dev_math.hpp"
 #include "kernels.hpp"
+#include "vprep.hpp"
 
 #include <algorithm>
 
 namespace det {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kAw = 6;                  // digits of W
 constexpr int kSw = 8 * kAw - 2;        // W = w * 2^46, |W| <= 2^46 fits six balanced digits
-constexpr int kBmax = 5;                // at most five digits of a V column (40-bit integers)
 constexpr int kNC = kAw + kBmax - 1;    // shift classes s = a + b
-constexpr int kKB = 32;                 // keys per block (the MFMA K)
 constexpr int kCarryEvery = 256;        // blocks (8192 keys) between carry passes
-constexpr int kBvFallback = 99;         // "needs the generic path" marker
 
 // ---------------------------------------------------------------- V preparation
 
-constexpr int kVChunks = 16;  // key chunks of the V column statistics
-
-// Column statistics of V over one key chunk: per column the largest exponent
-// and the smallest lsb exponent of the nonzero entries.  Grid (chunk, 32-column
-// group, head); 8 key strides x 32 columns per workgroup, reduced in LDS and
-// written to stats[((bhk * nG + G) * kVChunks + chunk) * 32 + column] as
-// int2 {emax, lmin} (no atomics, nothing to clear).
+// Standalone launches of the V preparation (vprep.hpp): grid (chunk, group,
+// head) for the statistics, (block, group, head) for the digit slices.
 template <typename TV>
-__global__ __launch_bounds__(256) void k_vstats(const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
-                                                int64_t Hkv, int64_t D, int64_t nG, int64_t kv_lo, int64_t kv_hi,
-                                                int2 *__restrict__ stats) {
-    const int t = threadIdx.x, c = t & 31, st = t >> 5;
-    const int64_t chunk = blockIdx.x, G = blockIdx.y, bhk = blockIdx.z, b = bhk / Hkv, hk = bhk % Hkv;
-    const int64_t len = kv_hi - kv_lo, per = (len + kVChunks - 1) / kVChunks;
-    const int64_t j0 = kv_lo + chunk * per, j1 = min64(kv_hi, j0 + per);
-    const int64_t d = G * 32 + c;
-    int emax = INT_MIN, lmin = INT_MAX;
-    if (d < D) {
-        const TV *col = vp + b * vsB + hk * vsH + d;
-#pragma unroll 4
-        for (int64_t j = j0 + st; j < j1; j += 8) {
-            const float x = elem<TV>::to_f32(col[j * vsS]);
-            if (x != 0.0f) {
-                const int e = f32_exp(x);
-                emax = max(emax, e);
-                lmin = min(lmin, max(e, -126) - elem<TV>::mant_bits);
-            }
-        }
-    }
-    __shared__ int smax[8][32], smin[8][32];
-    smax[st][c] = emax;
-    smin[st][c] = lmin;
-    __syncthreads();
-    if (t >= 32) return;
-#pragma unroll
-    for (int k = 1; k < 8; ++k) {
-        emax = max(emax, smax[k][c]);
-        lmin = min(lmin, smin[k][c]);
-    }
-    stats[((bhk * nG + G) * kVChunks + chunk) * 32 + c] = int2{emax, lmin};
+__global__ __launch_bounds__(256) void k_vstats(VJob J) {
+    vstats_block<TV>(J, blockIdx.x, blockIdx.y, blockIdx.z);
 }
-
-// Digits of Vi = V * 2^-g_d in MFMA lane order: block (bhk, G, kb, b) holds
-// 64 lanes x 16 bytes, lane l byte p = e_b(Vi[key kv_lo + 32kb + 16(l/32) + p][dim 32G + l%32]).
-// g_d = the smallest lsb exponent of the column's nonzero entries (so Vi is an
-// integer), from the chunk statistics; the group's digit count is what the
-// largest |Vi| of its 32 columns needs (kBvFallback when more than kBmax).
-// The workgroups of block 0 also record g_d and the count for pass 2.
 template <typename TV>
-__global__ __launch_bounds__(64) void k_vslice(const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
-                                               int64_t Hkv, int64_t D, int64_t Dp32, int64_t kv_lo, int64_t kv_hi,
-                                               int64_t nKB, const int2 *__restrict__ stats, int *__restrict__ colgrid,
-                                               int *__restrict__ grpB, v4i *__restrict__ vsl) {
-    const int lane = threadIdx.x;
-    const int64_t kb = blockIdx.x, G = blockIdx.y, bhk = blockIdx.z;
-    const int64_t b = bhk / Hkv, hk = bhk % Hkv;
-    const int64_t nG = Dp32 / 32;
-    const int64_t d = G * 32 + (lane & 31);
-    int emax = INT_MIN, lmin = INT_MAX;
-    const int2 *cs = stats + (bhk * nG + G) * kVChunks * 32 + (lane & 31);
-#pragma unroll
-    for (int k = 0; k < kVChunks; ++k) {
-        const int2 e = cs[k * 32];
-        emax = max(emax, e.x);
-        lmin = min(lmin, e.y);
-    }
-    const bool nonzero = emax != INT_MIN;
-    const int g = nonzero ? lmin : 0;
-    // digits needed: |Vi| < 2^(emax + 1 - g); balanced digits hold |x| <= 2^(8B-2)
-    int bg = nonzero ? (emax + 1 - g + 2 + 7) / 8 : 0;
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) bg = max(bg, __shfl_xor(bg, off, 64));
-    bg = max(bg, 1);
-    if (bg > kBmax) bg = kBvFallback;
-    if (kb == 0 && lane < 32) colgrid[bhk * Dp32 + d] = g;
-    if (kb == 0 && lane == 0) grpB[bhk * nG + G] = bg;
-    const TV *col = vp + b * vsB + hk * vsH + (d < D ? d : 0);
-    // the kBmax balanced digits of Vi (|Vi| < 2^38 when bg <= kBmax) are the
-    // bytes of Vi + 0x8080808080 with their top bit flipped
-    uint64_t U[16];
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-        const int64_t j = kv_lo + kb * kKB + 16 * (lane >> 5) + p;
-        double x = 0.0;
-        if (d < D && j < kv_hi && bg != kBvFallback) x = (double)elem<TV>::to_f32(col[j * vsS]);
-        U[p] = (uint64_t)((int64_t)ldexp(x, -g) + 0x8080808080ll);  // exact: x is a multiple of 2^g
-    }
-    v4i *out = vsl + ((bhk * nG + G) * nKB + kb) * kBmax * 64;
-#pragma unroll
-    for (int s = 0; s < kBmax; ++s) {
-        uint32_t wv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t pack = 0;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) pack |= ((uint32_t)(U[4 * q + u] >> (8 * s)) & 255u) << (8 * u);
-            wv[q] = pack ^ 0x80808080u;
-        }
-        out[s * 64 + lane] = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
-    }
+__global__ __launch_bounds__(64) void k_vslice(VJob J) {
+    vslice_block<TV>(J, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- exact int128 helpers
@@ -737,30 +643,43 @@ size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i) {
            align256((size_t)kDenDigits * bh * tiles * 32 * 8);                  // fused scratch DEN
 }
 
+VJob make_vjob(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp) {
+    const int64_t Dp32 = (g.D + 31) / 32 * 32, len = kv_hi - kv_lo;
+    vp.Dp32 = Dp32;
+    vp.nKB = std::max<int64_t>((len + kKB - 1) / kKB, 1);
+    VJob J{};
+    J.v = v.data;
+    J.dtype = v.dtype;
+    J.vsB = v.sB;
+    J.vsH = v.sH;
+    J.vsS = v.sS;
+    J.Hkv = g.Hkv;
+    J.D = g.D;
+    J.Dp32 = Dp32;
+    J.nG = Dp32 / 32;
+    J.kv_lo = kv_lo;
+    J.kv_hi = kv_hi;
+    J.nKB = vp.nKB;
+    J.nbhk = g.B * g.Hkv;
+    J.stats = vp.stats;
+    J.colgrid = vp.colgrid;
+    J.grpB = vp.grpB;
+    J.vsl = vp.slices;
+    return J;
+}
+
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
                         hipStream_t s) {
     ProfScope prof_("vprep", s);
-    const int64_t bhk = g.B * g.Hkv, Dp32 = (g.D + 31) / 32 * 32, nG = Dp32 / 32;
-    const int64_t len = kv_hi - kv_lo, nKB = std::max<int64_t>((len + kKB - 1) / kKB, 1);
-    vp.Dp32 = Dp32;
-    vp.nKB = nKB;
-    int2 *stats = (int2 *)vp.stats;
+    const VJob J = make_vjob(v, g, kv_lo, kv_hi, vp);
     hipError_t e;
-    dim3 gs((unsigned)kVChunks, (unsigned)nG, (unsigned)bhk);  // (an empty range leaves every chunk empty)
-    if (v.dtype == 0)
-        hipLaunchKernelGGL(k_vstats<float>, gs, dim3(256), 0, s, (const float *)v.data, v.sB, v.sH, v.sS, g.Hkv, g.D,
-                           nG, kv_lo, kv_hi, stats);
-    else
-        hipLaunchKernelGGL(k_vstats<bf16_t>, gs, dim3(256), 0, s, (const bf16_t *)v.data, v.sB, v.sH, v.sS, g.Hkv,
-                           g.D, nG, kv_lo, kv_hi, stats);
+    dim3 gs((unsigned)kVChunks, (unsigned)J.nG, (unsigned)J.nbhk);  // (an empty range leaves every chunk empty)
+    if (v.dtype == 0) hipLaunchKernelGGL(k_vstats<float>, gs, dim3(256), 0, s, J);
+    else hipLaunchKernelGGL(k_vstats<bf16_t>, gs, dim3(256), 0, s, J);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 gsl((unsigned)nKB, (unsigned)nG, (unsigned)bhk);
-    if (v.dtype == 0)
-        hipLaunchKernelGGL(k_vslice<float>, gsl, dim3(64), 0, s, (const float *)v.data, v.sB, v.sH, v.sS, g.Hkv, g.D,
-                           Dp32, kv_lo, kv_hi, nKB, stats, vp.colgrid, vp.grpB, (v4i *)vp.slices);
-    else
-        hipLaunchKernelGGL(k_vslice<bf16_t>, gsl, dim3(64), 0, s, (const bf16_t *)v.data, v.sB, v.sH, v.sS, g.Hkv,
-                           g.D, Dp32, kv_lo, kv_hi, nKB, stats, vp.colgrid, vp.grpB, (v4i *)vp.slices);
+    dim3 gsl((unsigned)J.nKB, (unsigned)J.nG, (unsigned)J.nbhk);
+    if (v.dtype == 0) hipLaunchKernelGGL(k_vslice<float>, gsl, dim3(64), 0, s, J);
+    else hipLaunchKernelGGL(k_vslice<bf16_t>, gsl, dim3(64), 0, s, J);
     return hipGetLastError();
 }
 

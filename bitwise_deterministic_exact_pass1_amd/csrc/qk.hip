@@ -14,12 +14,12 @@
 // plain fp64 chain in k_qk_fix, so the scores are the chain's bits either way.
 #include "dev_math.hpp"
 #include "kernels.hpp"
+#include "vprep.hpp"
 
 #include <algorithm>
 
 namespace det {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kQKmax = 4;              // digits per Q or K row (32-bit integers)
 constexpr int kQKC = 2 * kQKmax - 1;   // shift classes of the product
@@ -31,14 +31,29 @@ constexpr int kQKbad = 99;             // row needs more digits than kQKmax
 // consecutive dims per lane, so each digit plane is one DPL-byte store per
 // lane.  The Q pass also starts the rowmax keys of its rows at "empty" and the
 // fix count at 0 (the score pass that follows max-reduces and counts into them).
+struct QPrep {
+    const bf16_t *x;
+    int64_t sB, sH, sS, H, D, Dp64, s0, ns, ns_pad, nrows;
+    int4 *info;
+    int8_t *dig;
+    uint32_t *keys;  // Q only (may be null)
+    int64_t key_rows, key_row0;
+    int *nfix;  // Q only
+    int vec;    // rows are whole 64-dim groups on 16-byte boundaries
+};
+
 template <bool IS_K, int DPL>
-__global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, int64_t sB, int64_t sH, int64_t sS,
-                                                int64_t H, int64_t D, int64_t Dp64, int64_t s0, int64_t ns,
-                                                int64_t ns_pad, int64_t nrows, int4 *__restrict__ info,
-                                                int8_t *__restrict__ dig, uint32_t *__restrict__ keys,
-                                                int64_t key_rows, int64_t key_row0, int *__restrict__ nfix) {
+__device__ __forceinline__ void qkprep_rows(const QPrep &P, int64_t blk) {
+    const bf16_t *__restrict__ x = P.x;
+    const int64_t sB = P.sB, sH = P.sH, sS = P.sS, H = P.H, D = P.D, Dp64 = P.Dp64, s0 = P.s0, ns = P.ns;
+    const int64_t ns_pad = P.ns_pad, nrows = P.nrows, key_rows = P.key_rows, key_row0 = P.key_row0;
+    int4 *__restrict__ info = P.info;
+    int8_t *__restrict__ dig = P.dig;
+    uint32_t *__restrict__ keys = P.keys;
+    int *__restrict__ nfix = P.nfix;
+    const int vec = P.vec;
     const int sub = threadIdx.x & 15;
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int64_t row = blk * 16 + (threadIdx.x >> 4);
     if (row >= nrows) return;  // whole 16-lane groups leave together
     const int64_t bh = row / ns_pad, ii = row % ns_pad;
     const int64_t b = bh / H, h = bh % H;
@@ -46,11 +61,33 @@ __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, in
     const bf16_t *xr = x + b * sB + h * sH + (s0 + (live ? ii : 0)) * sS;
     float v[DPL];
     int emax = INT_MIN, lmin = INT_MAX;
+    bool loaded = false;
+    if constexpr (DPL % 8 == 0) {
+        if (vec) {  // whole rows of D = Dp64 dims, 16-byte aligned: DPL/8 vector loads per lane
+            const uint4 *xv = (const uint4 *)(xr + sub * DPL);
+#pragma unroll
+            for (int q = 0; q < DPL / 8; ++q) {
+                const uint4 u = xv[q];
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    v[8 * q + 2 * k] = live ? __uint_as_float(w[k] << 16) : 0.0f;
+                    v[8 * q + 2 * k + 1] = live ? __uint_as_float(w[k] & 0xffff0000u) : 0.0f;
+                }
+            }
+            loaded = true;
+        }
+    }
+    if (!loaded) {
+#pragma unroll
+        for (int t = 0; t < DPL; ++t) {
+            const int64_t d = sub * DPL + t;
+            const float xv = elem<bf16_t>::to_f32(xr[min64(d, D - 1)]);  // in range; used only if d < D
+            v[t] = (live && d < D) ? xv : 0.0f;
+        }
+    }
 #pragma unroll
     for (int t = 0; t < DPL; ++t) {
-        const int64_t d = sub * DPL + t;
-        const float xv = elem<bf16_t>::to_f32(xr[min64(d, D - 1)]);  // in range; used only if d < D
-        v[t] = (live && d < D) ? xv : 0.0f;
         if (v[t] != 0.0f) {
             const int e = f32_exp(v[t]);
             emax = max(emax, e);
@@ -113,21 +150,85 @@ __global__ __launch_bounds__(256) void k_qkprep(const bf16_t *__restrict__ x, in
     }
 }
 
+template <bool IS_K, int DPL>
+__global__ __launch_bounds__(256) void k_qkprep(QPrep P) {
+    qkprep_rows<IS_K, DPL>(P, blockIdx.x);
+}
+
+// One launch for the independent preparations before the scores: K's digit
+// rows (nk workgroups, when K is prepared here), Q's digit rows (nq), and the
+// column statistics of V (the rest, when V is prepared here).
+template <int DPL>
+__global__ __launch_bounds__(256) void k_prep(QPrep K, QPrep Q, VJob J, int64_t nk, int64_t nq) {
+    int64_t blk = blockIdx.x;
+    if (blk < nk) {
+        qkprep_rows<true, DPL>(K, blk);
+        return;
+    }
+    blk -= nk;
+    if (blk < nq) {
+        qkprep_rows<false, DPL>(Q, blk);
+        return;
+    }
+    blk -= nq;
+    const int64_t chunk = blk % kVChunks, rest = blk / kVChunks;
+    vstats_block<bf16_t>(J, chunk, rest % J.nG, rest / J.nG);
+}
+
+static QPrep make_qprep(const bf16_t *x, int64_t sB, int64_t sH, int64_t sS, int64_t H, int64_t D, int64_t Dp64,
+                        int64_t s0, int64_t ns, int64_t ns_pad, int64_t nrows, int4 *info, int8_t *dig,
+                        uint32_t *keys, int64_t key_rows, int64_t key_row0, int *nfix) {
+    QPrep P{};
+    P.x = x;
+    P.sB = sB;
+    P.sH = sH;
+    P.sS = sS;
+    P.H = H;
+    P.D = D;
+    P.Dp64 = Dp64;
+    P.s0 = s0;
+    P.ns = ns;
+    P.ns_pad = ns_pad;
+    P.nrows = nrows;
+    P.info = info;
+    P.dig = dig;
+    P.keys = keys;
+    P.key_rows = key_rows;
+    P.key_row0 = key_row0;
+    P.nfix = nfix;
+    // vector loads when every row is whole 64-dim groups starting on 16 bytes
+    P.vec = D == Dp64 && ((uintptr_t)x & 15) == 0 && sS % 8 == 0 && sH % 8 == 0 && sB % 8 == 0;
+    return P;
+}
+
 template <bool IS_K>
-static void launch_qkprep(const bf16_t *x, int64_t sB, int64_t sH, int64_t sS, int64_t H, int64_t D, int64_t Dp64,
-                          int64_t s0, int64_t ns, int64_t ns_pad, int64_t nrows, int4 *info, int8_t *dig,
-                          uint32_t *keys, int64_t key_rows, int64_t key_row0, int *nfix, hipStream_t s) {
-    const dim3 grid((unsigned)((nrows + 15) / 16));
-#define DET_QKPREP(DPL)                                                                                    \
-    hipLaunchKernelGGL((k_qkprep<IS_K, DPL>), grid, dim3(256), 0, s, x, sB, sH, sS, H, D, Dp64, s0, ns, ns_pad, \
-                       nrows, info, dig, keys, key_rows, key_row0, nfix)
-    switch (Dp64 / 16) {
+static void launch_qkprep(const QPrep &P, hipStream_t s) {
+    const dim3 grid((unsigned)((P.nrows + 15) / 16));
+#define DET_QKPREP(DPL) hipLaunchKernelGGL((k_qkprep<IS_K, DPL>), grid, dim3(256), 0, s, P)
+    switch (P.Dp64 / 16) {
         case 4: DET_QKPREP(4); break;
         case 8: DET_QKPREP(8); break;
         case 12: DET_QKPREP(12); break;
         default: DET_QKPREP(16); break;
     }
 #undef DET_QKPREP
+}
+
+// K, Q and (when J is set) V statistics in one launch.
+static void launch_prep(const QPrep *K, const QPrep &Q, const VJob *J, hipStream_t s) {
+    const int64_t nk = K ? (K->nrows + 15) / 16 : 0, nq = (Q.nrows + 15) / 16;
+    const int64_t nv = J ? kVChunks * J->nG * J->nbhk : 0;
+    const QPrep k0 = K ? *K : QPrep{};
+    const VJob j0 = J ? *J : VJob{};
+    const dim3 grid((unsigned)(nk + nq + nv));
+#define DET_PREP(DPL) hipLaunchKernelGGL((k_prep<DPL>), grid, dim3(256), 0, s, k0, Q, j0, nk, nq)
+    switch (Q.Dp64 / 16) {
+        case 4: DET_PREP(4); break;
+        case 8: DET_PREP(8); break;
+        case 12: DET_PREP(12); break;
+        default: DET_PREP(16); break;
+    }
+#undef DET_PREP
 }
 
 constexpr int kQkT = 16;     // rows and keys per matrix-core item
@@ -356,15 +457,25 @@ __global__ __launch_bounds__(64 * kQkWaves) void k_qk_mfma(QkArgs A) {
 // as f32 (exact for bf16) with every load issued before the first is used,
 // then one thread per pair that needs it runs the chain in ascending d.
 constexpr int kFixD = 256;
+//
+// Workgroups from nfw on instead prepare V's digit slices (when V is prepared
+// in this launch), one 32-key block per wave: both kinds of work are short and
+// bound by memory latency, so they share one launch.
 __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restrict__ q, int64_t qsB, int64_t qsH,
                                                 int64_t qsS, const bf16_t *__restrict__ k, int64_t ksB, int64_t ksH,
-                                                int64_t ksS, int64_t D) {
+                                                int64_t ksS, int64_t D, int nfw, VJob J) {
     __shared__ float sq[kQkT][kFixD + 1], sk[kQkT][kFixD + 1];
     const int tid = threadIdx.x;
+    if ((int)blockIdx.x >= nfw) {
+        const int64_t blk = blockIdx.x - nfw, nkb4 = (J.nKB + 3) / 4;
+        const int64_t kb = (blk % nkb4) * 4 + (tid >> 6), rest = blk / nkb4;
+        if (kb < J.nKB) vslice_block<bf16_t>(J, kb, rest % J.nG, rest / J.nG, tid & 63);
+        return;
+    }
     const int r = tid >> 4, c = tid & 15;
     const int n = *A.nfix;
     const int64_t i_end = A.i0 + A.ni;
-    for (int it = blockIdx.x; it < n; it += gridDim.x) {
+    for (int it = blockIdx.x; it < n; it += nfw) {
         const int4 item = A.fixlist[it];
         const int64_t kb = item.x, tile = item.y, bh = item.z;
         const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
@@ -425,23 +536,28 @@ size_t qk_chunk_bytes(const AttnGeom &g, int64_t ni, int64_t kv_len) {
 
 bool qk_uses_mfma(const Tensor &q) { return q.dtype == 1; }
 
-hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws,
-                           hipStream_t s) {
-    ProfScope prof_("qk_prep", s);
+static QPrep k_rows(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws) {
     const int64_t Dp64 = qk_dp64(g), len = kv_hi - kv_lo;
     const int64_t kv_pad = qk_pad(len), rows = g.B * g.Hkv * kv_pad;
     int4 *info = (int4 *)ws;
     int8_t *dig = (int8_t *)ws + align256((size_t)rows * 16);
-    launch_qkprep<true>((const bf16_t *)k.data, k.sB, k.sH, k.sS, g.Hkv, g.D, Dp64, kv_lo, len, kv_pad, rows, info,
-                        dig, nullptr, 0, 0, nullptr, s);
+    return make_qprep((const bf16_t *)k.data, k.sB, k.sH, k.sS, g.Hkv, g.D, Dp64, kv_lo, len, kv_pad, rows, info, dig,
+                      nullptr, 0, 0, nullptr);
+}
+
+hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws,
+                           hipStream_t s) {
+    ProfScope prof_("qk_prep", s);
+    launch_qkprep<true>(k_rows(k, g, kv_lo, kv_hi, ws), s);
     return hipGetLastError();
 }
 
-hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g, const void *kprep, void *chunk_ws,
-                            int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi, float *scores,
-                            uint32_t *rowmax_keys, int64_t key_rows, int64_t key_row0, hipStream_t s) {
+hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g, void *kprep, bool prep_k,
+                            const VJob *vj, void *chunk_ws, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
+                            float *scores, uint32_t *rowmax_keys, int64_t key_rows, int64_t key_row0,
+                            hipStream_t s) {
     const int64_t ni = i1 - i0;
-    if (ni <= 0 || kv_hi <= kv_lo) return hipSuccess;
+    if (ni <= 0 || kv_hi <= kv_lo) return (prep_k || vj) ? hipErrorInvalidValue : hipSuccess;
     if (g.D > 256) return hipErrorInvalidValue;
     const int64_t Dp64 = qk_dp64(g), ni_pad = padded_rows(ni), bh = g.B * g.Hq;
     const int64_t len = kv_hi - kv_lo, kv_pad = qk_pad(len);
@@ -462,9 +578,16 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     hipError_t e;
     {
         ProfScope prof_("qk_prep", s);
-        // also sets the rowmax keys of the chunk to "empty" and the fix count to 0
-        launch_qkprep<false>((const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad, bh * ni_pad,
-                             qinfo, qdig, rowmax_keys, key_rows, key_row0, nfix, s);
+        // also sets the rowmax keys of the chunk to "empty" and the fix count to
+        // 0; with K's digit rows and V's column statistics when they are asked for
+        const QPrep Q = make_qprep((const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad,
+                                   bh * ni_pad, qinfo, qdig, rowmax_keys, key_rows, key_row0, nfix);
+        if (prep_k || vj) {
+            const QPrep K = prep_k ? k_rows(k, g, kv_lo, kv_hi, kprep) : QPrep{};
+            launch_prep(prep_k ? &K : nullptr, Q, vj, s);
+        } else {
+            launch_qkprep<false>(Q, s);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     QkArgs a{};
@@ -509,9 +632,10 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     ProfScope prof_("scores_fix", s);
-    const int64_t items = bh * ntiles * nKB;
-    hipLaunchKernelGGL(k_qk_fix, dim3((unsigned)std::min<int64_t>(items, 2048)), dim3(256), 0, s, a,
-                       (const bf16_t *)q.data, q.sB, q.sH, q.sS, (const bf16_t *)k.data, k.sB, k.sH, k.sS, g.D);
+    const int64_t items = bh * ntiles * nKB, nfw = std::min<int64_t>(items, 2048);
+    const int64_t nvw = vj ? (vj->nKB + 3) / 4 * vj->nG * vj->nbhk : 0;  // V slice workgroups, 4 blocks each
+    hipLaunchKernelGGL(k_qk_fix, dim3((unsigned)(nfw + nvw)), dim3(256), 0, s, a, (const bf16_t *)q.data, q.sB, q.sH,
+                       q.sS, (const bf16_t *)k.data, k.sB, k.sH, k.sS, g.D, (int)nfw, vj ? *vj : VJob{});
     return hipGetLastError();
 }
 
