@@ -16,8 +16,9 @@
 // result is the exact NUM whatever the order of keys, blocks or instructions.
 // DEN is the exact int64 sum of the W_ij.  A tile whose weights do not fit the
 // grid (w < 2^-23, or w > 1 from a rowmax below the scores) or whose V columns
-// need more than six digits is flagged and redone by the generic exact kernel
-// (k_tile_fallback): results never depend on which path ran.
+// need more than five digits is redone by the generic exact path (windowed
+// binary64 sums into digit planes) by the same workgroup: results never depend
+// on which path ran.
 #include "dev_math.hpp"
 #include "kernels.hpp"
 #include "vprep.hpp"
@@ -117,6 +118,11 @@ struct PvArgs {
     // digit output (accumulate): num [14][plane_rows][D], den [9][plane_rows]
     int64_t *num, *den;
     int64_t plane_rows, rows_per_bh, row0;
+    // the generic path of flagged tiles: V itself and (fused) 32-row digit scratch per tile
+    const void *v;
+    int vdtype;
+    int64_t vsB, vsH, vsS;
+    int64_t *fb_num, *fb_den;
 };
 
 // The row max of row i of head bh (from floats or from order keys).
@@ -242,14 +248,16 @@ __device__ __forceinline__ PvTile pv_tile_of(const PvArgs &A, int64_t bh, int64_
 }
 
 // Producer side of one tile: thread ptid of the kPW producer waves.
+// Returns whether the tile needs the generic path (known to both roles after
+// the tile's last barrier).
 template <int NG>
-__device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t tile, int ptid, int par,
+__device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t tile, int ptid, int par,
                                            PvShared &S) {
     constexpr int NPT = 64 * kPW;  // producer threads
     constexpr int TPR = NPT / 32;  // producer threads per row
     constexpr int KPT = 32 / TPR;  // keys per producer thread and block
     const PvTile T = pv_tile_of(A, bh, tile);
-    if (T.badv) return;
+    if (T.badv) return true;
     const int lane = ptid & 63, pw = ptid >> 6;
     const int r = ptid / TPR, k0 = (ptid % TPR) * KPT;
     const int dofs = ((r + 32 * (k0 >> 4)) * 16) + (k0 & 15);
@@ -330,6 +338,7 @@ __device__ __forceinline__ void pv_produce(const PvArgs &A, int64_t bh, int64_t 
     }
     if (bad) S.bad[par] = 1;
     __syncthreads();
+    return S.bad[par] != 0;
 }
 
 // The consumer's block loop for a wave whose group has BV V digits (0: no
@@ -390,14 +399,15 @@ __device__ __forceinline__ void pv_consume_loop(const PvTile &T, const v4i *vb, 
 }
 
 // Consumer side of one tile: wave `wave` (< NG) owns 32-dim group G0 + wave.
+// Returns whether the tile needs the generic path.
 template <bool FUSED, int NG>
-__device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, int64_t tile, int wave, int par,
+__device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, int64_t tile, int wave, int par,
                                            PvShared &S) {
     const int tid = threadIdx.x, lane = tid & 63;
     const PvTile T = pv_tile_of(A, bh, tile);
     if (T.badv) {
         if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
-        return;
+        return true;
     }
     if (tid == 0) S.bad[par] = 0;
     const int64_t G = G0 + wave;
@@ -420,10 +430,10 @@ __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, 
     __syncthreads();
     if (S.bad[par]) {
         if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
-        return;
+        return true;
     }
     if (tid == 0) A.flags[bh * A.ntiles + tile] = 0;
-    if (!mine) return;
+    if (!mine) return false;
 
     // carry the classes into bytes: C_0..C_8 in [0, 256), C_9 signed, so that
     // NUM = C_9 2^72 + sum_{s<9} C_s 2^(8s) = hi 2^64 + lo
@@ -484,7 +494,7 @@ __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, 
             const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
             if (row < nrows && dok) ob[row * ostride + (int)d] = out[rr];
         }
-        return;
+        return false;
     }
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -503,12 +513,30 @@ __device__ __forceinline__ void pv_consume(const PvArgs &A, int G0, int64_t bh, 
         if (G == 0 && (lane & 31) == 0)
             add_i128_digits<kDenDigits>((__int128)S.den[par][row], -kSw - kDenElo, A.den + prow, A.plane_rows);
     }
+    return false;
 }
 
 // One workgroup per tile, or for causal attention per pair of tiles (x,
 // ntiles-1-x), whose key counts add up to the same total for every pair: the
 // whole grid then runs in one balanced round.  Both roles walk the same tiles
 // and meet at the same barriers.
+template <typename TV, bool FUSED>
+__device__ __forceinline__ void fallback_tile(const PvArgs &A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
+                              int64_t *__restrict__ num_ws, int64_t *__restrict__ den_ws, int64_t bh, int64_t tile,
+                              int64_t nbh);
+
+// A flagged tile, by the whole workgroup right after both roles learn of it
+// (the launch over the first four groups only: it covers every dimension).
+template <bool FUSED>
+__device__ __forceinline__ void pv_generic_tile(const PvArgs &A, int64_t bh, int64_t tile) {
+    if (A.vdtype == 0)
+        fallback_tile<float, FUSED>(A, (const float *)A.v, A.vsB, A.vsH, A.vsS, A.fb_num, A.fb_den, bh, tile,
+                                    (int64_t)gridDim.y);
+    else
+        fallback_tile<bf16_t, FUSED>(A, (const bf16_t *)A.v, A.vsB, A.vsH, A.vsS, A.fb_num, A.fb_den, bh, tile,
+                                     (int64_t)gridDim.y);
+}
+
 template <bool FUSED, int NG>
 __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
     __shared__ __align__(16) PvShared S;
@@ -517,13 +545,21 @@ __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // No barrier between the tiles: the producers start the second tile while
     // the consumers finalize the first (row sums and flags are kept per tile).
+    // Both roles learn whether a tile needs the generic path; such tiles are
+    // redone at the end by the whole workgroup (from one call site).
+    bool generic[2] = {false, false};
     if (wave >= NG) {
         for (int pass = 0; pass < npass; ++pass)
-            pv_produce<NG>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, threadIdx.x - 64 * NG, pass, S);
+            generic[pass] = pv_produce<NG>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x,
+                                           threadIdx.x - 64 * NG, pass, S);
     } else {
         for (int pass = 0; pass < npass; ++pass)
-            pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave, pass, S);
+            generic[pass] =
+                pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave, pass, S);
     }
+    if (G0 != 0) return;
+    for (int pass = 0; pass < npass; ++pass)
+        if (generic[pass]) pv_generic_tile<FUSED>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x);
 }
 
 // ---------------------------------------------------------------- generic exact fallback
@@ -532,7 +568,7 @@ __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
 // general path over all keys of the tile's rows, then (fused) an in-kernel
 // finalize.  nbh = number of heads in the launch.
 template <typename TV, bool FUSED>
-__device__ void fallback_tile(const PvArgs &A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
+__device__ __forceinline__ void fallback_tile(const PvArgs &A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
                               int64_t *__restrict__ num_ws, int64_t *__restrict__ den_ws, int64_t bh, int64_t tile,
                               int64_t nbh) {
     const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group;
@@ -604,17 +640,6 @@ __device__ void fallback_tile(const PvArgs &A, const TV *__restrict__ vp, int64_
         const double d64 = digits_to_f64<kDenDigits>(dd, kDenElo);
         A.o[b * A.osB + hq * A.osH + i * A.osS + d] = (float)(n64 / d64);
     }
-}
-
-// The generic path for the tiles k_pv flagged: one workgroup per tile, which
-// returns at once unless its tile is flagged.
-template <typename TV, bool FUSED>
-__global__ __launch_bounds__(256) void k_tile_fallback(PvArgs A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH,
-                                                       int64_t vsS, int64_t *__restrict__ num_ws,
-                                                       int64_t *__restrict__ den_ws) {
-    const int64_t bh = blockIdx.y, tile = blockIdx.x;
-    if (A.flags[bh * A.ntiles + tile])
-        fallback_tile<TV, FUSED>(A, vp, vsB, vsH, vsS, num_ws, den_ws, bh, tile, (int64_t)gridDim.y);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -701,15 +726,7 @@ static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &v
         }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    ProfScope prof_("pv_fallback", s);
-    dim3 grid((unsigned)a.ntiles, (unsigned)bh);
-    if (v.dtype == 0)
-        hipLaunchKernelGGL((k_tile_fallback<float, FUSED>), grid, dim3(256), 0, s, a, (const float *)v.data, v.sB,
-                           v.sH, v.sS, num_ws, den_ws);
-    else
-        hipLaunchKernelGGL((k_tile_fallback<bf16_t, FUSED>), grid, dim3(256), 0, s, a, (const bf16_t *)v.data, v.sB,
-                           v.sH, v.sS, num_ws, den_ws);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
@@ -758,6 +775,13 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     a.plane_rows = plane_rows;
     a.rows_per_bh = rows_per_bh;
     a.row0 = row0;
+    a.v = v.data;
+    a.vdtype = v.dtype;
+    a.vsB = v.sB;
+    a.vsH = v.sH;
+    a.vsS = v.sS;
+    a.fb_num = fb_num;
+    a.fb_den = fb_den;
     return o ? launch_pv_t<true>(v, g, vp, a, bh, fb_num, fb_den, s)
              : launch_pv_t<false>(v, g, vp, a, bh, fb_num, fb_den, s);
 }
