@@ -343,3 +343,23 @@ def test_bf16_scores_outlier_rows_take_the_fp64_chain(A, oracle, causal):
     assert_bits_equal(out, ref, "outliers")
     m = A.rowmax(*gpu(q, k), 0, 96, causal, 0.02)
     assert_bits_equal(m, oracle.attn_rowmax(q, k, 0, 96, causal, 0.02), "rowmax")
+
+
+def test_small_workspace_many_row_chunks_bit_identical(A, gqa):
+    """A workspace a sixth of the default size makes the library run the query
+    rows in several chunks (K and V are prepared by the first chunk's launches
+    only); the output must be the same bits."""
+    import ctypes as C
+    from bitwise_deterministic_exact_pass1_amd import _lib
+    wl, Q, K, V, out = gqa
+    say("gqa: det_attn with a small workspace")
+    q, k, v = A._desc(Q), A._desc(K), A._desc(V)
+    L = _lib.lib()
+    full = L.det_attn_workspace_size(C.byref(q), C.byref(k), C.byref(v), 1)
+    small = (full // 6) // 256 * 256
+    ws = torch.empty(small + 256, dtype=torch.uint8, device=Q.device)
+    addr = (ws.data_ptr() + 255) & ~255
+    o2 = torch.empty_like(out)
+    _lib.check(L.det_attn(C.byref(q), C.byref(k), C.byref(v), 1, wl["scale"], C.byref(A._out(o2)), addr, small,
+                          A._stream(Q)))
+    assert torch.equal(o2, out)
