@@ -25,7 +25,7 @@ __device__ __forceinline__ float ce_load(const void *x, int64_t ld, int64_t i, i
     return elem<T>::to_f32(((const T *)x)[i * ld + v]);
 }
 
-// Block-wide max of order keys; every thread gets the result.
+// Block-wide max of order keys (sh holds one word per wave); every thread gets the result.
 __device__ __forceinline__ uint32_t block_max_key(uint32_t k, uint32_t *sh) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) k = max(k, (uint32_t)__shfl_xor((int)k, off, 64));
@@ -33,7 +33,7 @@ __device__ __forceinline__ uint32_t block_max_key(uint32_t k, uint32_t *sh) {
     if (lane == 0) sh[wave] = k;
     __syncthreads();
     uint32_t r = sh[0];
-    for (int w = 1; w < kCeThreads / 64; ++w) r = max(r, sh[w]);
+    for (int w = 1; w < (int)(blockDim.x / 64); ++w) r = max(r, sh[w]);
     __syncthreads();
     return r;
 }
@@ -190,10 +190,10 @@ __global__ void k_ce_backward(const void *x, int64_t N, int64_t V, int64_t ld, c
 // patterns outside the window take the per-element rules instead.  Both forms
 // give the same bits: integer counts times exact f32 weights, summed exactly.
 
-constexpr int kTT = 256;                   // threads of a row workgroup
+constexpr int kTT = 512;                   // threads of a row workgroup
 constexpr int kHalf = 32 * 128;            // patterns per sign: 32 binades x 128 mantissas
 constexpr int kTab = 2 * kHalf;            // table slots
-constexpr int kSlots = kTab / kTT;         // slots per thread (32)
+constexpr int kSlots = kTab / kTT;         // slots per thread (16)
 constexpr int kQcap = 2048;                // out-of-window patterns kept per row
 constexpr int64_t kTabMinLen = kTab;       // shorter ranges use the per-element kernels
 constexpr int64_t kCountMax = (int64_t)1 << 29;  // count * w stays exact in binary64
