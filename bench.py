@@ -179,7 +179,9 @@ def main():
 
 def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     """Side numbers: the sharded composition (16 x 64 keys) on the same inputs,
-    and cross-entropy forward/backward on N=4096, V=128256 bf16."""
+    cross-entropy forward/backward on N=4096, V=128256 bf16, the float32
+    contrast, and the fused path on the larger causal shares (S=8192 D=128,
+    S=2048 D=256)."""
     from bitwise_deterministic_exact_pass1_amd import cross_entropy as CE
     res = {}
     splits = [64] * (K.shape[2] // 64)
@@ -216,6 +218,24 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     res["contrast"] = {"attention_4_shard_rotations": contrast.attention_contrast(attention, Q, K, V, [K.shape[2] // 4] * 4,
                                                                                   causal, scale),
                        "cross_entropy_vocab_splits": contrast.ce_contrast(CE, X, T)}
+    # larger causal shares of one GPU: B=1 Hq=32 Hkv=8 S=8192 D=128 and S=2048 D=256 (bf16)
+    for name in ("cp_share_bf16", "cp_share_d256_bf16"):
+        wl = W.attn_workload(name)
+        q2, k2, v2 = wl["q"].cuda(), wl["k"].cuda(), wl["v"].cuda()
+        attention.det_attn(q2, k2, v2, True, wl["scale"])
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(3):
+            attention.det_attn(q2, k2, v2, True, wl["scale"])
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms2 = ev[0].elapsed_time(ev[1]) / 3
+        Sx, Dx = q2.shape[2], q2.shape[3]
+        pairs2 = q2.shape[0] * q2.shape[1] * Sx * (Sx + 1) // 2
+        res[name] = {"workload": wl["desc"], "ms": ms2, "pairs_per_s": pairs2 / (ms2 / 1e3),
+                     "frac_of_fp64_path_roofline": pairs2 * (6 * Dx + 32) / (ms2 / 1e3) / 1e12 / FP64_PEAK_TFLOPS}
+        del q2, k2, v2
     return res
 
 
