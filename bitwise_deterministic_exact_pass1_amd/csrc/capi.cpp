@@ -140,14 +140,16 @@ size_t score_chunk_bytes(const AttnGeom &g, bool mfma, int64_t ni, int64_t kv_le
 }
 
 // Scores of rows [i0, i1) against keys [lo, hi), with the rowmax keys when
-// `keys` is set.  prep_k: K's digits for the range are prepared first (the
+// `keys` is set.  prep_q: Q's part of the chunk is prepared and the rowmax
+// keys of rows [i0, i1) start at "empty"; without it both are kept from an
+// earlier call on the same chunk (the keys then accumulate the max over the
+// calls).  prep_k: K's digits for the range are prepared first (the
 // matrix-core path prepares them in the same launch as Q's); vp: V is prepared
 // too (on the matrix-core path beside the score preparation and the score fix,
-// otherwise by its own launches).  Both paths start the rowmax keys of rows
-// [i0, i1) at "empty" themselves.
+// otherwise by its own launches).
 hipError_t run_scores(const Tensor &tq, const Tensor &tk, const Tensor &tv, const AttnGeom &g, bool mfma, void *kprep,
-                      bool prep_k, VPrep *vp, void *chunk_ws, int64_t i0, int64_t i1, int64_t lo, int64_t hi,
-                      float *scores, uint32_t *keys, int64_t key_rows, int64_t key_row0, hipStream_t s) {
+                      bool prep_k, bool prep_q, VPrep *vp, void *chunk_ws, int64_t i0, int64_t i1, int64_t lo,
+                      int64_t hi, float *scores, uint32_t *keys, int64_t key_rows, int64_t key_row0, hipStream_t s) {
     hipError_t e;
     const bool host = mfma && hi > lo && i1 > i0;  // the score launches can carry the preparations
     if (vp && !host && (e = launch_vprep(tv, g, lo, hi, *vp, s)) != hipSuccess) return e;
@@ -155,10 +157,10 @@ hipError_t run_scores(const Tensor &tq, const Tensor &tk, const Tensor &tv, cons
         if (!host) return hipSuccess;
         VJob vj{};
         if (vp) vj = make_vjob(tv, g, lo, hi, *vp);
-        return launch_scores_qk(tq, tk, g, kprep, prep_k, vp ? &vj : nullptr, chunk_ws, i0, i1, lo, hi, scores, keys,
+        return launch_scores_qk(tq, tk, g, kprep, prep_k, prep_q, vp ? &vj : nullptr, chunk_ws, i0, i1, lo, hi, scores, keys,
                                 key_rows, key_row0, s);
     }
-    if (keys) {  // keys[h * key_rows + i - key_row0]: one run per head, or one in all when contiguous
+    if (keys && prep_q) {  // keys[h * key_rows + i - key_row0]: one run per head, or one in all when contiguous
         const int64_t bh = g.B * g.Hq, n = i1 - i0;
         const bool whole = key_rows == n && key_row0 == i0;
         for (int64_t h = 0; h < (whole ? 1 : bh); ++h)
@@ -166,7 +168,7 @@ hipError_t run_scores(const Tensor &tq, const Tensor &tk, const Tensor &tv, cons
                 hipSuccess)
                 return e;
     }
-    if ((e = launch_widen_q(tq, g, i0, i1, (double *)chunk_ws, s)) != hipSuccess) return e;
+    if (prep_q && (e = launch_widen_q(tq, g, i0, i1, (double *)chunk_ws, s)) != hipSuccess) return e;
     return launch_scores(tk, g, (const double *)chunk_ws, i0, i1, lo, hi, scores, keys, key_rows, key_row0, s);
 }
 
@@ -192,7 +194,7 @@ size_t bytes_fused(const AttnGeom &g, bool mfma, int64_t ni) {
 size_t bytes_sharded(const AttnGeom &g, bool mfma, int64_t ni, int64_t maxlen) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, maxlen) + score_fixed_bytes(g, mfma, maxlen) + score_chunk_bytes(g, mfma, ni, maxlen) +
-           align256((size_t)rows * 4) + align256((size_t)rows * maxlen * 4) + 2 * align256((size_t)rows * 4) +
+           align256((size_t)rows * 4) + align256((size_t)rows * maxlen * 4) + align256((size_t)rows * 4) +
            align256((size_t)bh * ((ni + 31) / 32) * 4) +
            align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8);
 }
@@ -307,8 +309,8 @@ int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        HIP_TRY(run_scores(tq, tk, tk, g, mf, kprep, i0 == 0, nullptr, cws, i0, i1, kv_lo, kv_hi, nullptr, keys, ni, i0,
-                           s),
+        HIP_TRY(run_scores(tq, tk, tk, g, mf, kprep, i0 == 0, true, nullptr, cws, i0, i1, kv_lo, kv_hi, nullptr, keys,
+                           ni, i0, s),
                 "scores");
         HIP_TRY(launch_keys_to_f32(keys, rowmax, bh, ni, g.Sq, i0, s), "rowmax");
     }
@@ -357,8 +359,8 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     for (int64_t i0 = 0; i0 < g.Sq && W > 0; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk);
         // the first chunk's launches also prepare K and V
-        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, i0 == 0 ? &vp : nullptr, cws, i0, i1, kv_lo, kv_hi, sc,
-                           nullptr, 0, 0, s),
+        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, true, i0 == 0 ? &vp : nullptr, cws, i0, i1, kv_lo, kv_hi,
+                           sc, nullptr, 0, 0, s),
                 "scores");
         HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, nullptr, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr,
                           nullptr, num, den, rows, g.Sq, 0, ff, s),
@@ -442,8 +444,8 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
         // the first chunk's launches also prepare K and V
-        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, i0 == 0 ? &vp : nullptr, cws, i0, i1, 0, g.Skv, sc, keys,
-                           ni, i0, s),
+        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, true, i0 == 0 ? &vp : nullptr, cws, i0, i1, 0, g.Skv, sc,
+                           keys, ni, i0, s),
                 "scores");
         HIP_TRY(launch_pv(tv, g, vp, sc, nullptr, keys, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr,
                           nullptr, 0, 0, 0, ff, s),
@@ -521,22 +523,26 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         uint32_t *keys = c.take<uint32_t>(rows);
         float *sc = c.take<float>(rows * ml);
         float *rm_acc = c.take<float>(rows);
-        float *rm_part = c.take<float>(rows);
         int *flags = c.take<int>(bh * ((ni + 31) / 32));
         int64_t *num_acc = c.take<int64_t>(kNumDigits * rows * g.D);
         int64_t *den_acc = c.take<int64_t>(kDenDigits * rows);
         if (c.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
-        // pass 1: rowmax of each shard, composed by max
-        HIP_TRY(launch_fill_u32((uint32_t *)rm_acc, rows, 0xff800000u, s), "fill rowmax");  // -inf
+        // pass 1: the rowmax of each shard, composed by max: every shard's score
+        // launch max-reduces its rows into the same order keys (an integer max,
+        // so the result does not depend on the order); Q's digits are prepared by
+        // the first shard's launch and kept for every later launch of this chunk
+        bool any = false;
         for (int32_t a = 0; a < n_splits; ++a) {
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
             if (h <= l) continue;  // an empty shard has no scores: its max is -inf, the identity
-            HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, nullptr, cws, i0, i1, l, h, nullptr, keys, ni, i0, s),
+            HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, !any, nullptr, cws, i0, i1, l, h, nullptr, keys, ni, i0,
+                               s),
                     "scores");
-            HIP_TRY(launch_keys_to_f32(keys, rm_part, bh, ni, ni, 0, s), "rowmax");
-            HIP_TRY(launch_rowmax_combine(rm_acc, rm_part, rows, s), "rowmax combine");
+            any = true;
         }
+        if (any) HIP_TRY(launch_keys_to_f32(keys, rm_acc, bh, ni, ni, 0, s), "rowmax");
+        else HIP_TRY(launch_fill_u32((uint32_t *)rm_acc, rows, 0xff800000u, s), "fill rowmax");  // -inf
         // pass 2: each shard's digits against the global max, composed by int64 add: the
         // deposit adds its limbs into the shared accumulator (integer atomics), and one
         // carry pass at the end makes the sum canonical
@@ -546,7 +552,8 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
             if (h <= l) continue;
-            HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, &vp, cws, i0, i1, l, h, sc, nullptr, 0, 0, s), "scores");
+            HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, false, &vp, cws, i0, i1, l, h, sc, nullptr, 0, 0, s),
+                    "scores");
             HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, nullptr, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
                               num_acc, den_acc, rows, ni, i0, ff, s),
                     "deposit");

@@ -93,11 +93,14 @@ struct VJob {
     void *vsl;
 };
 // Scores of rows [i0, i1) against keys [kv_lo, kv_hi) on the matrix cores.
+// prep_q: Q's digit rows of the chunk are prepared (and the chunk's rowmax
+// keys started at "empty"); otherwise the chunk workspace still holds them from
+// an earlier call, and the keys keep their values (the max accumulates).
 // prep_k: K's digit rows are prepared into kprep in the same launch as Q's;
 // vj (bf16 V, nullable): V's column statistics are computed in that launch and
 // its digit slices in the score-fix launch.  Both need a nonempty range.
 hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g, void *kprep, bool prep_k,
-                            const VJob *vj, void *chunk_ws, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
+                            bool prep_q, const VJob *vj, void *chunk_ws, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
                             float *scores, uint32_t *rowmax_keys, int64_t key_rows, int64_t key_row0,
                             hipStream_t s);
 

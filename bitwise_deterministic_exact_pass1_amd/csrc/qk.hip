@@ -161,6 +161,8 @@ __global__ __launch_bounds__(256) void k_qkprep(QPrep P) {
 template <int DPL>
 __global__ __launch_bounds__(256) void k_prep(QPrep K, QPrep Q, VJob J, int64_t nk, int64_t nq) {
     int64_t blk = blockIdx.x;
+    // Q's rows reset the fix count; without them the first workgroup does
+    if (nq == 0 && blk == 0 && threadIdx.x == 0) *Q.nfix = 0;
     if (blk < nk) {
         qkprep_rows<true, DPL>(K, blk);
         return;
@@ -214,9 +216,10 @@ static void launch_qkprep(const QPrep &P, hipStream_t s) {
 #undef DET_QKPREP
 }
 
-// K, Q and (when J is set) V statistics in one launch.
-static void launch_prep(const QPrep *K, const QPrep &Q, const VJob *J, hipStream_t s) {
-    const int64_t nk = K ? (K->nrows + 15) / 16 : 0, nq = (Q.nrows + 15) / 16;
+// K (when set), Q (when with_q) and V statistics (when J is set) in one launch.
+static void launch_prep(const QPrep *K, const QPrep &Q, bool with_q, const VJob *J, hipStream_t s) {
+    const int64_t nk = K ? (K->nrows + 15) / 16 : 0, nq = with_q ? (Q.nrows + 15) / 16 : 0;
+    if (nk + nq == 0 && !J) return;
     const int64_t nv = J ? kVChunks * J->nG * J->nbhk : 0;
     const QPrep k0 = K ? *K : QPrep{};
     const VJob j0 = J ? *J : VJob{};
@@ -246,6 +249,7 @@ struct QkArgs {
     uint32_t *keys;  // rowmax keys, [bh*key_rows + i - key_row0], or null
     int *nfix;       // number of items left (in whole or in part) to the fp64 chain
     int4 *fixlist;   // their (kb, tile, bh, kFixWhole or kFixPairs)
+    int fixcap;      // capacity of the list: one entry per item of the launch
     double scale;
     int Dp64, ni, ni_pad, i0, kv_lo, kv_hi, kv_pad;
     int Hq, Hkv, group;
@@ -376,7 +380,7 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
             if (aq > kQKmax || bk > kQKmax) {  // rows with more digits: the whole item takes the chain
                 if (lane == 0) {
                     const int at = atomicAdd(A.nfix, 1);
-                    A.fixlist[at] = int4{kb, tile, (int)bh, kFixWhole};
+                    if (at < A.fixcap) A.fixlist[at] = int4{kb, tile, (int)bh, kFixWhole};
                 }
             } else {
                 // pairs within the bound are exact here; when the item's bound does not
@@ -419,7 +423,7 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
                 }
                 if (__ballot(left) && lane == 0) {
                     const int at = atomicAdd(A.nfix, 1);
-                    A.fixlist[at] = int4{kb, tile, (int)bh, kFixPairs};
+                    if (at < A.fixcap) A.fixlist[at] = int4{kb, tile, (int)bh, kFixPairs};
                 }
             }
         }
@@ -473,7 +477,7 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
         return;
     }
     const int r = tid >> 4, c = tid & 15;
-    const int n = *A.nfix;
+    const int n = min(*A.nfix, A.fixcap);
     const int64_t i_end = A.i0 + A.ni;
     for (int it = blockIdx.x; it < n; it += nfw) {
         const int4 item = A.fixlist[it];
@@ -553,7 +557,7 @@ hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, in
 }
 
 hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g, void *kprep, bool prep_k,
-                            const VJob *vj, void *chunk_ws, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
+                            bool prep_q, const VJob *vj, void *chunk_ws, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
                             float *scores, uint32_t *rowmax_keys, int64_t key_rows, int64_t key_row0,
                             hipStream_t s) {
     const int64_t ni = i1 - i0;
@@ -573,7 +577,8 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     const int64_t krows = g.B * g.Hkv * kv_pad;
     // every extent the kernels see must fit 32 bits (offsets are formed in 64)
     const int64_t lim = INT32_MAX;
-    if (ni_pad > lim || kv_pad > lim || i0 + ni_pad > lim || kv_hi > lim || key_rows > lim || g.Hq > lim)
+    if (ni_pad > lim || kv_pad > lim || i0 + ni_pad > lim || kv_hi > lim || key_rows > lim || g.Hq > lim ||
+        bh * ntiles * nKB > lim)
         return hipErrorInvalidValue;
     hipError_t e;
     {
@@ -582,9 +587,11 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
         // 0; with K's digit rows and V's column statistics when they are asked for
         const QPrep Q = make_qprep((const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad,
                                    bh * ni_pad, qinfo, qdig, rowmax_keys, key_rows, key_row0, nfix);
-        if (prep_k || vj) {
+        if (!prep_q && !prep_k && !vj) {
+            if ((e = launch_fill_u32((uint32_t *)nfix, 1, 0u, s)) != hipSuccess) return e;  // the fix count
+        } else if (prep_k || vj || !prep_q) {
             const QPrep K = prep_k ? k_rows(k, g, kv_lo, kv_hi, kprep) : QPrep{};
-            launch_prep(prep_k ? &K : nullptr, Q, vj, s);
+            launch_prep(prep_k ? &K : nullptr, Q, prep_q, vj, s);
         } else {
             launch_qkprep<false>(Q, s);
         }
@@ -599,6 +606,7 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     a.keys = rowmax_keys;
     a.nfix = nfix;
     a.fixlist = fixlist;
+    a.fixcap = (int)(bh * ntiles * nKB);  // the list region holds one entry per item
     a.scale = g.scale;
     a.Dp64 = (int)Dp64;
     a.ni = (int)ni;
