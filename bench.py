@@ -180,8 +180,8 @@ def main():
 def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     """Side numbers: the sharded composition (16 x 64 keys) on the same inputs,
     cross-entropy forward/backward on N=4096, V=128256 bf16, the float32
-    contrast, and the fused path on the larger causal shares (S=8192 D=128,
-    S=2048 D=256)."""
+    contrast, the fused path on the larger causal shares (S=8192 D=128,
+    S=2048 D=256), and on the long non-causal NHD share (S=37810, 56 heads)."""
     from bitwise_deterministic_exact_pass1_amd import cross_entropy as CE
     res = {}
     splits = [64] * (K.shape[2] // 64)
@@ -236,6 +236,26 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
         res[name] = {"workload": wl["desc"], "ms": ms2, "pairs_per_s": pairs2 / (ms2 / 1e3),
                      "frac_of_fp64_path_roofline": pairs2 * (6 * Dx + 32) / (ms2 / 1e3) / 1e12 / FP64_PEAK_TFLOPS}
         del q2, k2, v2
+    # the long non-causal share: one interleaved QKV buffer [37810, 21504] bf16, heads 56, D=128,
+    # Q/K/V as strided NHD views, f32 output
+    dbuf = W.long_nhd_buffer().cuda()
+    q5, k5, v5 = W.long_nhd_views(dbuf)
+    sc5 = W.default_scale(W.LONG_D)
+    attention.det_attn(q5, k5, v5, False, sc5)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(2):
+        attention.det_attn(q5, k5, v5, False, sc5)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms5 = ev[0].elapsed_time(ev[1]) / 2
+    pairs5 = W.LONG_H * W.LONG_S * W.LONG_S
+    res["long_nhd_bf16"] = {"workload": "B=1 H=56 S=37810 D=128 bfloat16 NHD views of one QKV buffer, non-causal",
+                            "ms": ms5, "pairs_per_s": pairs5 / (ms5 / 1e3),
+                            "frac_of_fp64_path_roofline": pairs5 * (6 * W.LONG_D + 32) / (ms5 / 1e3) / 1e12
+                            / FP64_PEAK_TFLOPS}
+    del q5, k5, v5, dbuf
     return res
 
 

@@ -207,6 +207,9 @@ VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
     v.colgrid = c.take<int>(bhk * Dp32);
     v.grpB = c.take<int>(bhk * nG);
     v.slices = c.take<char>(vslice_bytes(g, kv_len));
+    v.rare_n = c.take<int>(1);
+    v.rare_grp = c.take<int>(bhk * nG);
+    v.rare = c.take<int4>(kRareCap);
     v.Dp32 = Dp32;
     v.nKB = nKB;
     return v;

@@ -82,6 +82,9 @@ size_t qk_kprep_bytes(const AttnGeom &g, int64_t kv_len);
 size_t qk_chunk_bytes(const AttnGeom &g, int64_t ni, int64_t kv_len);
 hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws,
                            hipStream_t s);
+// Capacity of the remainder list of one V preparation (entries of all heads);
+// heads whose remainders do not fit take the generic exact path.
+constexpr int kRareCap = 4096;
 // All arguments of the V preparation of one key range (device code in
 // vprep.hpp): V's strides, the group geometry and the prepared arrays.
 struct VJob {
@@ -91,6 +94,10 @@ struct VJob {
     void *stats;
     int *colgrid, *grpB;
     void *vsl;
+    // entries whose low bits fall below their column's digit grid: a count, a
+    // flag per (head, 32-column group) and the list of (head, key, column, remainder)
+    int *rare_n, *rare_grp;
+    int4 *rare;
 };
 // Scores of rows [i0, i1) against keys [kv_lo, kv_hi) on the matrix cores.
 // prep_q: Q's digit rows of the chunk are prepared (and the chunk's rowmax
@@ -112,6 +119,8 @@ struct VPrep {
     void *stats;  // column statistics per key chunk
     int *colgrid, *grpB;
     void *slices;
+    int *rare_n, *rare_grp;  // remainders below the column grids (see VJob)
+    int4 *rare;
     int64_t Dp32, nKB;
 };
 VJob make_vjob(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp);
@@ -119,6 +128,8 @@ size_t vprep_bytes(const AttnGeom &g, int64_t kv_len);
 // bytes of the V digit slices / of the column statistics within vprep_bytes
 size_t vslice_bytes(const AttnGeom &g, int64_t kv_len);
 size_t vstats_bytes(const AttnGeom &g);
+// bytes of the remainder count, group flags and list within vprep_bytes
+size_t vrare_bytes(const AttnGeom &g);
 size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i);
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
                         hipStream_t s);

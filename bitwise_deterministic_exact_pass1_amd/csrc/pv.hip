@@ -123,6 +123,9 @@ struct PvArgs {
     int vdtype;
     int64_t vsB, vsH, vsS;
     int64_t *fb_num, *fb_den;
+    // remainders of V entries below their column grids (vprep.hpp)
+    const int *rare_n, *rare_grp;
+    const int4 *rare;
 };
 
 // The row max of row i of head bh (from floats or from order keys).
@@ -228,7 +231,8 @@ struct PvShared {
 struct PvTile {
     int64_t b, hq, bhk, it0, i_end, nG, jhi;
     int nblk;
-    bool badv;  // a V group the grid cannot hold: the whole tile takes the generic path
+    bool badv;     // a V group the grid cannot hold: the whole tile takes the generic path
+    uint32_t rem;  // groups with remainders below their grid: finalized through digits
 };
 
 __device__ __forceinline__ PvTile pv_tile_of(const PvArgs &A, int64_t bh, int64_t tile) {
@@ -242,8 +246,14 @@ __device__ __forceinline__ PvTile pv_tile_of(const PvArgs &A, int64_t bh, int64_
     T.jhi = A.causal ? min64(A.kv_hi, T.it0 + 32) : A.kv_hi;
     T.nblk = T.jhi > A.kv_lo ? (int)((T.jhi - A.kv_lo + kKB - 1) / kKB) : 0;
     int bad = A.force_fallback;
-    for (int64_t g = 0; g < T.nG; ++g) bad |= A.grpB[T.bhk * T.nG + g] > kBmax;
+    uint32_t rem = 0;
+    for (int64_t g = 0; g < T.nG; ++g) {
+        bad |= A.grpB[T.bhk * T.nG + g] > kBmax;
+        if (A.rare_grp[T.bhk * T.nG + g]) rem |= 1u << g;
+    }
+    if (rem && *A.rare_n > kRareCap) bad = 1;  // the list lost entries
     T.badv = bad;
+    T.rem = rem;
     return T;
 }
 
@@ -445,6 +455,33 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
     }
     const int64_t d = G * 32 + (lane & 31);
     const int g = A.colgrid[T.bhk * A.Dp32 + d];
+    if (FUSED && ((T.rem >> G) & 1)) {
+        // this group's remainders are added later: its exact NUM goes to the
+        // tile's 32-row digit scratch (cleared here), finalized after them
+        const int64_t nplane = A.ntiles * 32 * (int64_t)gridDim.y * A.D;
+        int64_t *nb = A.fb_num + (bh * A.ntiles + tile) * 32 * A.D;
+        for (int t = lane; t < 32 * 32 * kNumDigits; t += 64) {
+            const int k = t >> 10, r = (t >> 5) & 31, c = t & 31;
+            if (G * 32 + c < A.D) nb[k * nplane + r * A.D + G * 32 + c] = 0;
+        }
+        __threadfence();
+        if (d < A.D) {
+#pragma unroll 1
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+                const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) |
+                                    ((uint32_t)C[2][rr] << 16) | ((uint32_t)C[3][rr] << 24);
+                const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) |
+                                    ((uint32_t)C[6][rr] << 16) | ((uint32_t)C[7][rr] << 24);
+                const uint64_t lo = ((uint64_t)l1 << 32) | l0;
+                const int64_t hi = (int64_t)C[kNC - 1][rr] * 256 + C[kNC - 2][rr];
+                const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
+                add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, nb + row * A.D + d, nplane);
+            }
+        }
+        __threadfence();
+        return false;
+    }
     if (FUSED) {
         // all 16 outputs of the lane first (no branches: their conversions and
         // divisions interleave), then the stores of the rows that exist
@@ -537,6 +574,62 @@ __device__ __forceinline__ void pv_generic_tile(const PvArgs &A, int64_t bh, int
                                      (int64_t)gridDim.y);
 }
 
+// The remainders of a tile's groups G0 .. G0+NG-1 (V entries with bits below
+// their column grid, vprep.hpp), by the whole workgroup after both roles are
+// done: each visible (row, remainder) product w V_rem is exact in binary64 and
+// is added into the row's digits (the caller's planes, or the tile's scratch,
+// where the consumers left the matrix-core part of those groups), then (fused)
+// those groups' outputs are finalized from the digits.  Returns at once when
+// none of these groups has remainders (the same for every thread).
+template <bool FUSED, int NG>
+__device__ __forceinline__ void pv_remainder_tile(const PvArgs &A, int G0, int64_t bh, int64_t tile, int par,
+                                                  PvShared &S) {
+    const PvTile T = pv_tile_of(A, bh, tile);
+    const uint32_t grp = (T.rem >> G0) & ((1u << NG) - 1);
+    if (!grp) return;
+    __syncthreads();  // the consumers' scratch deposits of this tile are done (and fenced)
+    int64_t *num = FUSED ? A.fb_num : A.num;
+    const int64_t nplane_rows = FUSED ? A.ntiles * 32 * (int64_t)gridDim.y : A.plane_rows;
+    auto prow_of = [&](int64_t i) -> int64_t {
+        return FUSED ? (bh * A.ntiles + tile) * 32 + (i - T.it0) : bh * A.rows_per_bh + (i - A.row0);
+    };
+    const int n = min(*A.rare_n, kRareCap);
+    for (int t = threadIdx.x; t < n * 32; t += blockDim.x) {
+        const int4 E = A.rare[t >> 5];
+        const int64_t i = T.it0 + (t & 31), j = E.y, d = E.z;
+        const int gd = E.z / 32 - G0;  // the entry's group within this launch
+        if (E.x != T.bhk || gd < 0 || gd >= NG || !((grp >> gd) & 1) || i >= T.i_end) continue;
+        const int64_t jend = A.causal ? min64(A.kv_hi, i + 1) : A.kv_hi;
+        if (j < A.kv_lo || j >= jend) continue;
+        const float w = weight(A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)], pv_rowmax(A, bh, i));
+        if (w == 0.0f) continue;
+        const float rv = __int_as_float(E.w);
+        const int ew = f32_exp(w), ev = f32_exp(rv);
+        int64_t *dst = num + prow_of(i) * A.D + d;
+        Window win;
+        win.init();
+        win.add<kNumDigits>((double)w * (double)rv, max(ew, -126) - 23 + max(ev, -126) - 23, ew + ev + 2, kNumGcap,
+                            kNumElo, dst, nplane_rows * A.D);
+        win.flush<kNumDigits>(kNumElo, dst, nplane_rows * A.D);
+    }
+    __threadfence();
+    __syncthreads();
+    if (!FUSED) return;
+    for (int t = threadIdx.x; t < 32 * NG * 32; t += blockDim.x) {
+        const int r = t / (NG * 32), c = t % (NG * 32);
+        const int64_t d = G0 * 32 + c, i = T.it0 + r;
+        if (!((grp >> (c >> 5)) & 1) || d >= A.D || i >= T.i_end) continue;
+        const int64_t at = prow_of(i) * A.D + d;
+        int64_t nd[kNumDigits];
+        unsigned long long *np = (unsigned long long *)num;
+#pragma unroll
+        for (int k = 0; k < kNumDigits; ++k) nd[k] = (int64_t)atomicAdd(np + k * nplane_rows * A.D + at, 0ull);
+        canonicalize<kNumDigits>(nd);
+        const double n64 = digits_to_f64<kNumDigits>(nd, kNumElo);
+        A.o[T.b * A.osB + T.hq * A.osH + i * A.osS + d] = (float)(n64 / S.d64[par][r]);
+    }
+}
+
 template <bool FUSED, int NG>
 __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
     __shared__ __align__(16) PvShared S;
@@ -557,9 +650,11 @@ __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
             generic[pass] =
                 pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave, pass, S);
     }
-    if (G0 != 0) return;
-    for (int pass = 0; pass < npass; ++pass)
-        if (generic[pass]) pv_generic_tile<FUSED>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x);
+    for (int pass = 0; pass < npass; ++pass) {
+        const int64_t tile = (A.causal && pass == 0) ? A.ntiles - 1 - x : x;
+        if (!generic[pass]) pv_remainder_tile<FUSED, NG>(A, G0, bh, tile, pass, S);
+        else if (G0 == 0) pv_generic_tile<FUSED>(A, bh, tile);
+    }
 }
 
 // ---------------------------------------------------------------- generic exact fallback
@@ -655,10 +750,15 @@ size_t vstats_bytes(const AttnGeom &g) {
     return align256((size_t)bhk * nG * kVChunks * 32 * 8);
 }
 
+size_t vrare_bytes(const AttnGeom &g) {
+    const int64_t bhk = g.B * g.Hkv, nG = (g.D + 31) / 32;
+    return align256(4) + align256((size_t)bhk * nG * 4) + align256((size_t)kRareCap * 16);
+}
+
 size_t vprep_bytes(const AttnGeom &g, int64_t kv_len) {
     const int64_t bhk = g.B * g.Hkv, Dp32 = (g.D + 31) / 32 * 32, nG = Dp32 / 32;
     return vstats_bytes(g) + align256((size_t)bhk * Dp32 * 4) + align256((size_t)bhk * nG * 4) +
-           vslice_bytes(g, kv_len);
+           vslice_bytes(g, kv_len) + vrare_bytes(g);
 }
 
 size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i) {
@@ -690,6 +790,9 @@ VJob make_vjob(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi,
     J.colgrid = vp.colgrid;
     J.grpB = vp.grpB;
     J.vsl = vp.slices;
+    J.rare_n = vp.rare_n;
+    J.rare_grp = vp.rare_grp;
+    J.rare = vp.rare;
     return J;
 }
 
@@ -782,6 +885,9 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     a.vsS = v.sS;
     a.fb_num = fb_num;
     a.fb_den = fb_den;
+    a.rare_n = vp.rare_n;
+    a.rare_grp = vp.rare_grp;
+    a.rare = vp.rare;
     return o ? launch_pv_t<true>(v, g, vp, a, bh, fb_num, fb_den, s)
              : launch_pv_t<false>(v, g, vp, a, bh, fb_num, fb_den, s);
 }

@@ -16,7 +16,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kBmax = 5;          // at most five digits of a V column (40-bit integers)
 constexpr int kKB = 32;           // keys per block (the MFMA K)
-constexpr int kBvFallback = 99;   // "needs the generic path" marker
 constexpr int kVChunks = 16;      // key chunks of the V column statistics
 
 // Column statistics of V over one key chunk, by one 256-thread workgroup: per
@@ -28,6 +27,11 @@ template <typename TV>
 __device__ __forceinline__ void vstats_block(const VJob &J, int64_t chunk, int64_t G, int64_t bhk) {
     __shared__ int smax[8][32], smin[8][32];
     const int t = threadIdx.x, c = t & 31, st = t >> 5;
+    // start the remainder list (the digit slices, a later launch, fill it)
+    if (chunk == 0 && t == 0) {
+        J.rare_grp[bhk * J.nG + G] = 0;
+        if (G == 0 && bhk == 0) *J.rare_n = 0;
+    }
     const int64_t b = bhk / J.Hkv, hk = bhk % J.Hkv;
     const int64_t len = J.kv_hi - J.kv_lo, per = (len + kVChunks - 1) / kVChunks;
     const int64_t j0 = J.kv_lo + chunk * per, j1 = min64(J.kv_hi, j0 + per);
@@ -59,9 +63,13 @@ __device__ __forceinline__ void vstats_block(const VJob &J, int64_t chunk, int64
 
 // Digits of key block kb of 32-column group G, by one wave: block (bhk, G, kb)
 // holds 64 lanes x 16 bytes, lane l byte p = e_b(Vi[key kv_lo + 32kb + 16(l/32) + p][dim 32G + l%32]).
-// The group's digit count is what the largest |Vi| of its 32 columns needs
-// (kBvFallback when more than kBmax).  The waves of block 0 also record g_d and
-// the count for pass 2.
+// The group's digit count is what the largest |Vi| of its 32 columns needs.  A
+// column that would need more than kBmax digits on its own lsb grid gets the
+// coarser grid g_d = emax_d - 37 instead (|Vi| < 2^38, five digits): Vi is then
+// V rounded toward zero to that grid, and every entry with bits below it leaves
+// an exact remainder V - Vi 2^g_d (|remainder| < 2^g_d) that is appended to the
+// remainder list, with its group flagged; pass 2 adds those products exactly.
+// The waves of block 0 also record g_d and the count for pass 2.
 template <typename TV>
 __device__ __forceinline__ void vslice_block(const VJob &J, int64_t kb, int64_t G, int64_t bhk, int lane) {
     const int64_t b = bhk / J.Hkv, hk = bhk % J.Hkv;
@@ -75,25 +83,35 @@ __device__ __forceinline__ void vslice_block(const VJob &J, int64_t kb, int64_t 
         lmin = min(lmin, e.y);
     }
     const bool nonzero = emax != INT_MIN;
-    const int g = nonzero ? lmin : 0;
     // digits needed: |Vi| < 2^(emax + 1 - g); balanced digits hold |x| <= 2^(8B-2)
+    int g = nonzero ? lmin : 0;
     int bg = nonzero ? (emax + 1 - g + 2 + 7) / 8 : 0;
+    if (bg > kBmax) {
+        g = emax - 37;  // > lmin: the column keeps its top 38 bits on the grid
+        bg = kBmax;
+    }
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) bg = max(bg, __shfl_xor(bg, off, 64));
     bg = max(bg, 1);
-    if (bg > kBmax) bg = kBvFallback;
     if (kb == 0 && lane < 32) J.colgrid[bhk * J.Dp32 + d] = g;
     if (kb == 0 && lane == 0) J.grpB[bhk * J.nG + G] = bg;
     const TV *col = (const TV *)J.v + b * J.vsB + hk * J.vsH + (d < J.D ? d : 0);
-    // the kBmax balanced digits of Vi (|Vi| < 2^38 when bg <= kBmax) are the
-    // bytes of Vi + 0x8080808080 with their top bit flipped
+    // the kBmax balanced digits of Vi (|Vi| < 2^38) are the bytes of
+    // Vi + 0x8080808080 with their top bit flipped
     uint64_t U[16];
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
         const int64_t j = J.kv_lo + kb * kKB + 16 * (lane >> 5) + p;
         double x = 0.0;
-        if (d < J.D && j < J.kv_hi && bg != kBvFallback) x = (double)elem<TV>::to_f32(col[j * J.vsS]);
-        U[p] = (uint64_t)((int64_t)ldexp(x, -g) + 0x8080808080ll);  // exact: x is a multiple of 2^g
+        if (d < J.D && j < J.kv_hi) x = (double)elem<TV>::to_f32(col[j * J.vsS]);
+        const int64_t vi = (int64_t)ldexp(x, -g);  // toward zero; exact unless x has bits below 2^g
+        const double rem = x - ldexp((double)vi, g);  // exact (the low bits of x)
+        if (rem != 0.0) {
+            const int at = atomicAdd(J.rare_n, 1);
+            if (at < kRareCap) J.rare[at] = int4{(int)bhk, (int)j, (int)d, __float_as_int((float)rem)};
+            J.rare_grp[bhk * J.nG + G] = 1;
+        }
+        U[p] = (uint64_t)(vi + 0x8080808080ll);
     }
     v4i *out = (v4i *)J.vsl + ((bhk * J.nG + G) * J.nKB + kb) * kBmax * 64;
 #pragma unroll

@@ -363,3 +363,56 @@ def test_small_workspace_many_row_chunks_bit_identical(A, gqa):
     _lib.check(L.det_attn(C.byref(q), C.byref(k), C.byref(v), 1, wl["scale"], C.byref(A._out(o2)), addr, small,
                           A._stream(Q)))
     assert torch.equal(o2, out)
+
+
+# ---------------------------------------------------------------- V columns wider than the digit grid
+
+def v_with_low_bits(v, D):
+    """bf16 V with a few entries whose bits reach far below the rest of their
+    column: wholly (2^-40, -2^-60, 3 2^-45) or partly (1.0078125 2^-30,
+    1.5 2^-33) under a five-digit column grid."""
+    v = v.clone()
+    for b, h, j, d, x in [(0, 0, 17, 5, 2.0 ** -40), (0, 0, 250, 5, -1.0078125 * 2.0 ** -30),
+                          (0, 1, 3, D - 1, 3 * 2.0 ** -45), (0, 1, 299, 40, -2.0 ** -60),
+                          (0, 0, 0, 0, 1.5 * 2.0 ** -33)]:
+        v[b, h, j, d] = x
+    return v
+
+
+@pytest.mark.parametrize("causal,D", [(False, 128), (True, 128), (True, 256)])
+def test_v_columns_wider_than_the_digit_grid(A, oracle, causal, D):
+    """The matrix-core part on the coarser column grid plus the exact remainder
+    products: the fused, sharded and digit paths equal the oracle and the
+    generic path bit for bit."""
+    q, k, v = W.attn_inputs(610 + D + int(causal), 1, 4, 2, 300, 300, D, torch.bfloat16)
+    v = v_with_low_bits(v, D)
+    scale = W.default_scale(D)
+    say(f"wide V columns: oracle causal={causal} D={D}")
+    ref = oracle.det_attn(q, k, v, causal, scale)
+    Q, K, V = gpu(q, k, v)
+    out = A.det_attn(Q, K, V, causal, scale)
+    assert_bits_equal(out, ref, "fused")
+    sh = A.det_attn_sharded(Q, K, V, [100, 64, 136], causal, scale, order=[2, 0, 1])
+    assert torch.equal(sh, out)
+    m = A.rowmax(Q, K, 0, 300, causal, scale)
+    n1, d1 = A.accumulate(Q, K, V, m, 0, 300, causal, scale)
+    assert torch.equal(A.finalize(n1, d1), out)
+    with generic_path():
+        n2, d2 = A.accumulate(Q, K, V, m, 0, 300, causal, scale)
+    assert torch.equal(n1, n2) and torch.equal(d1, d2)
+
+
+def test_v_remainder_list_overflow_takes_the_generic_path(A, oracle):
+    """More remainders than the list holds: their heads take the generic exact
+    path, with the same bits."""
+    q, k, v = W.attn_inputs(620, 1, 2, 2, 640, 640, 32, torch.bfloat16)
+    g = torch.Generator().manual_seed(621)
+    idx = torch.randperm(640 * 32, generator=g)[:5000]
+    flat = v[0, 1].reshape(-1)
+    flat[idx] = (flat[idx] * 2.0 ** -45).to(torch.bfloat16)
+    v[0, 1] = flat.reshape(640, 32)
+    scale = W.default_scale(32)
+    say("remainder overflow: oracle")
+    ref = oracle.det_attn(q, k, v, True, scale)
+    out = A.det_attn(*gpu(q, k, v), True, scale)
+    assert_bits_equal(out, ref, "overflow")
