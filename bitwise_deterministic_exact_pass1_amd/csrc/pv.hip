@@ -262,11 +262,12 @@ __device__ __forceinline__ PvTile pv_tile_of(const PvArgs &A, int64_t bh, int64_
 // the tile's last barrier).
 template <int NG>
 __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t tile, int ptid, int par,
-                                           PvShared &S) {
+                                           PvShared &S, uint32_t &rem) {
     constexpr int NPT = 64 * kPW;  // producer threads
     constexpr int TPR = NPT / 32;  // producer threads per row
     constexpr int KPT = 32 / TPR;  // keys per producer thread and block
     const PvTile T = pv_tile_of(A, bh, tile);
+    rem = T.rem;
     if (T.badv) return true;
     const int lane = ptid & 63, pw = ptid >> 6;
     const int r = ptid / TPR, k0 = (ptid % TPR) * KPT;
@@ -412,9 +413,10 @@ __device__ __forceinline__ void pv_consume_loop(const PvTile &T, const v4i *vb, 
 // Returns whether the tile needs the generic path.
 template <bool FUSED, int NG>
 __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, int64_t tile, int wave, int par,
-                                           PvShared &S) {
+                                           PvShared &S, uint32_t &rem) {
     const int tid = threadIdx.x, lane = tid & 63;
     const PvTile T = pv_tile_of(A, bh, tile);
+    rem = T.rem;
     if (T.badv) {
         if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
         return true;
@@ -579,14 +581,12 @@ __device__ __forceinline__ void pv_generic_tile(const PvArgs &A, int64_t bh, int
 // done: each visible (row, remainder) product w V_rem is exact in binary64 and
 // is added into the row's digits (the caller's planes, or the tile's scratch,
 // where the consumers left the matrix-core part of those groups), then (fused)
-// those groups' outputs are finalized from the digits.  Returns at once when
-// none of these groups has remainders (the same for every thread).
+// those groups' outputs are finalized from the digits.  grp: the groups of
+// this launch that have remainders (nonzero, the same for every thread).
 template <bool FUSED, int NG>
 __device__ __forceinline__ void pv_remainder_tile(const PvArgs &A, int G0, int64_t bh, int64_t tile, int par,
-                                                  PvShared &S) {
+                                                  uint32_t grp, PvShared &S) {
     const PvTile T = pv_tile_of(A, bh, tile);
-    const uint32_t grp = (T.rem >> G0) & ((1u << NG) - 1);
-    if (!grp) return;
     __syncthreads();  // the consumers' scratch deposits of this tile are done (and fenced)
     int64_t *num = FUSED ? A.fb_num : A.num;
     const int64_t nplane_rows = FUSED ? A.ntiles * 32 * (int64_t)gridDim.y : A.plane_rows;
@@ -641,19 +641,24 @@ __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
     // Both roles learn whether a tile needs the generic path; such tiles are
     // redone at the end by the whole workgroup (from one call site).
     bool generic[2] = {false, false};
+    uint32_t rem[2] = {0u, 0u};
     if (wave >= NG) {
         for (int pass = 0; pass < npass; ++pass)
             generic[pass] = pv_produce<NG>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x,
-                                           threadIdx.x - 64 * NG, pass, S);
+                                           threadIdx.x - 64 * NG, pass, S, rem[pass]);
     } else {
         for (int pass = 0; pass < npass; ++pass)
-            generic[pass] =
-                pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave, pass, S);
+            generic[pass] = pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave,
+                                                  pass, S, rem[pass]);
     }
     for (int pass = 0; pass < npass; ++pass) {
         const int64_t tile = (A.causal && pass == 0) ? A.ntiles - 1 - x : x;
-        if (!generic[pass]) pv_remainder_tile<FUSED, NG>(A, G0, bh, tile, pass, S);
-        else if (G0 == 0) pv_generic_tile<FUSED>(A, bh, tile);
+        const uint32_t grp = (rem[pass] >> G0) & ((1u << NG) - 1);
+        if (generic[pass]) {
+            if (G0 == 0) pv_generic_tile<FUSED>(A, bh, tile);
+        } else if (grp) {
+            pv_remainder_tile<FUSED, NG>(A, G0, bh, tile, pass, grp, S);
+        }
     }
 }
 

@@ -86,7 +86,8 @@ __device__ __forceinline__ void vslice_block(const VJob &J, int64_t kb, int64_t 
     // digits needed: |Vi| < 2^(emax + 1 - g); balanced digits hold |x| <= 2^(8B-2)
     int g = nonzero ? lmin : 0;
     int bg = nonzero ? (emax + 1 - g + 2 + 7) / 8 : 0;
-    if (bg > kBmax) {
+    const bool split = bg > kBmax;
+    if (split) {
         g = emax - 37;  // > lmin: the column keeps its top 38 bits on the grid
         bg = kBmax;
     }
@@ -104,14 +105,21 @@ __device__ __forceinline__ void vslice_block(const VJob &J, int64_t kb, int64_t 
         const int64_t j = J.kv_lo + kb * kKB + 16 * (lane >> 5) + p;
         double x = 0.0;
         if (d < J.D && j < J.kv_hi) x = (double)elem<TV>::to_f32(col[j * J.vsS]);
-        const int64_t vi = (int64_t)ldexp(x, -g);  // toward zero; exact unless x has bits below 2^g
-        const double rem = x - ldexp((double)vi, g);  // exact (the low bits of x)
-        if (rem != 0.0) {
-            const int at = atomicAdd(J.rare_n, 1);
-            if (at < kRareCap) J.rare[at] = int4{(int)bhk, (int)j, (int)d, __float_as_int((float)rem)};
-            J.rare_grp[bhk * J.nG + G] = 1;
+        U[p] = (uint64_t)((int64_t)ldexp(x, -g) + 0x8080808080ll);  // toward zero onto the grid
+    }
+    if (__ballot(split)) {
+        // the exact remainders of a split column's entries (reread: a rare path)
+        for (int p = 0; p < 16; ++p) {
+            const int64_t j = J.kv_lo + kb * kKB + 16 * (lane >> 5) + p;
+            if (!split || d >= J.D || j >= J.kv_hi) continue;
+            const double x = (double)elem<TV>::to_f32(col[j * J.vsS]);
+            const double rem = x - ldexp((double)(int64_t)ldexp(x, -g), g);  // exact: the low bits of x
+            if (rem != 0.0) {
+                const int at = atomicAdd(J.rare_n, 1);
+                if (at < kRareCap) J.rare[at] = int4{(int)bhk, (int)j, (int)d, __float_as_int((float)rem)};
+                J.rare_grp[bhk * J.nG + G] = 1;
+            }
         }
-        U[p] = (uint64_t)(vi + 0x8080808080ll);
     }
     v4i *out = (v4i *)J.vsl + ((bhk * J.nG + G) * J.nKB + kb) * kBmax * 64;
 #pragma unroll
