@@ -79,7 +79,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa_causal_bf16")
+    ap.add_argument("--workload", default="gqa_causal_bf16",
+                    help="gqa_causal_bf16 (default), cp_share_bf16, cp_share_d256_bf16, tiny_mha_f32 or "
+                         "long_nhd_bf16 (use --no-extra with the others)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the sharded / cross-entropy side measurements")
@@ -106,11 +108,19 @@ def main():
 
     from bitwise_deterministic_exact_pass1_amd import _lib, attention, workloads as W
 
-    wl = W.attn_workload(args.workload)
-    q, k, v, causal, scale = wl["q"], wl["k"], wl["v"], wl["causal"], wl["scale"]
+    if args.workload == "long_nhd_bf16":
+        # Q, K, V as strided NHD views of one interleaved QKV buffer [37810, 21504] bf16 (on both sides)
+        buf = W.long_nhd_buffer()
+        q, k, v = W.long_nhd_views(buf)
+        Q, K, V = W.long_nhd_views(buf.cuda())
+        causal, scale = False, W.default_scale(W.LONG_D)
+        desc = f"B=1 H={W.LONG_H} S={W.LONG_S} D={W.LONG_D} bfloat16 NHD views of one QKV buffer, non-causal"
+    else:
+        wl = W.attn_workload(args.workload)
+        q, k, v, causal, scale, desc = wl["q"], wl["k"], wl["v"], wl["causal"], wl["scale"], wl["desc"]
+        Q, K, V = q.cuda(), k.cuda(), v.cuda()
     B, Hq, Sq, D = q.shape
     Skv = k.shape[2]
-    Q, K, V = q.cuda(), k.cuda(), v.cuda()
     pairs = visible_pairs(B, Hq, Sq, Skv, causal)
     rows = B * Hq * Sq
 
@@ -164,7 +174,7 @@ def main():
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f64+int64", "data": "synthetic",
-        "config": {"workload": f"fused det_attn, {wl['desc']}", "B": B, "Hq": Hq, "Hkv": k.shape[1],
+        "config": {"workload": f"fused det_attn, {desc}", "B": B, "Hq": Hq, "Hkv": k.shape[1],
                    "S": Sq, "D": D, "causal": causal, "pairs_per_step": pairs},
         "roofline": roofline, "path_roofline": path, "kernels": kernels,
     }

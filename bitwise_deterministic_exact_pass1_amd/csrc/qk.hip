@@ -504,20 +504,33 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
                 }
             }
         }
-        __syncthreads();
         const int64_t i = it0 + r, j = j0 + c;
-        if (i >= i_end || j >= A.kv_hi) continue;
-        if (item.w == kFixPairs && A.qinfo[bh * A.ni_pad + tile * kQkT + r].z +
-                                           A.kinfo[bhk * A.kv_pad + kb * kQkT + c].z <= 53)
-            continue;
-        // (unrolled: the LDS reads of 16 steps go out together, only the fma chain is serial)
-        double acc = 0.0;
-        const int Di = (int)D;
+        bool need = i < i_end && j < A.kv_hi;
+        if (need && item.w == kFixPairs)  // (read before the barrier: its latency overlaps the staging)
+            need = A.qinfo[bh * A.ni_pad + tile * kQkT + r].z + A.kinfo[bhk * A.kv_pad + kb * kQkT + c].z > 53;
+        __syncthreads();
+        uint32_t key = 0;  // below order_key of every number
+        if (need) {
+            // (unrolled: the LDS reads of 16 steps go out together, only the fma chain is serial)
+            double acc = 0.0;
+            const int Di = (int)D;
 #pragma unroll 16
-        for (int d = 0; d < Di; ++d) acc = fma((double)sq[r][d], (double)sk[c][d], acc);
-        const float sc = (float)(A.scale * acc);
-        if (A.scores) A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)] = sc;
-        if (A.keys && (!A.causal || j <= i)) atomicMax(&A.keys[bh * A.key_rows + (i - A.key_row0)], order_key(sc));
+            for (int d = 0; d < Di; ++d) acc = fma((double)sq[r][d], (double)sk[c][d], acc);
+            const float sc = (float)(A.scale * acc);
+            if (A.scores) A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)] = sc;
+            if (!A.causal || j <= i) key = order_key(sc);
+        }
+        // the row's max over the item's 16 keys (16 consecutive lanes), then one
+        // atomic per row, skipped when the row's key is already at least as large
+        // (keys only grow within the launch, so a stale read only costs an atomic):
+        // a row listed for every key block would otherwise send all its pairs to
+        // one address
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) key = max(key, (uint32_t)__shfl_xor((int)key, off, 64));
+        if (A.keys && c == 0 && key != 0) {
+            uint32_t *kp = &A.keys[bh * A.key_rows + (i - A.key_row0)];
+            if (key > __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(kp, key);
+        }
     }
 }
 
