@@ -306,6 +306,112 @@ int32_t ora_attn_accumulate_rows(const ora_tensor *q, const ora_tensor *k, const
     return failed ? -1 : 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Attention backward (the reading stated in det_oracle.h)                   */
+/* ------------------------------------------------------------------------ */
+
+/* Per query row of the forward over all keys: rowmax, RN64(DEN), and delta =
+ * the fp64 fma chain of dO . O with O the f32 output. */
+static void backward_row_stats(const ora_tensor *q, const ora_tensor *k, const ora_tensor *v,
+                               const ora_tensor *dout, int64_t b, int64_t hq, int64_t hk, int64_t i, int32_t causal,
+                               double scale, float *m_out, double *den_out, double *delta_out) {
+    const int64_t D = q->D;
+    float m = -INFINITY;
+    for (int64_t j = 0; j < k->S; j++)
+        if (visible(i, j, causal)) m = max_total(m, score_at(q, k, b, hq, hk, i, j, scale));
+    big_t *num = (big_t *)calloc((size_t)D, sizeof(big_t));
+    big_t den;
+    big_zero(&den);
+    for (int64_t j = 0; j < k->S; j++) {
+        if (!visible(i, j, causal)) continue;
+        float w = (float)ora_exp_det((double)score_at(q, k, b, hq, hk, i, j, scale) - (double)m);
+        big_add_double(&den, (double)w);
+        for (int64_t d = 0; d < D; d++) big_add_double(&num[d], (double)w * ora_load(v, b, hk, j, d));
+    }
+    double den64 = big_to_double(&den), delta = 0.0;
+    for (int64_t d = 0; d < D; d++) {
+        float o = (float)(big_to_double(&num[d]) / den64);
+        delta = fma(ora_load(dout, b, hq, i, d), (double)o, delta);
+    }
+    free(num);
+    *m_out = m;
+    *den_out = den64;
+    *delta_out = delta;
+}
+
+/* p_ij and ds_ij of one visible pair. */
+static void backward_pair(const ora_tensor *q, const ora_tensor *k, const ora_tensor *v, const ora_tensor *dout,
+                          int64_t b, int64_t hq, int64_t hk, int64_t i, int64_t j, double scale, float m,
+                          double den64, double delta, float *p_out, float *ds_out) {
+    float w = (float)ora_exp_det((double)score_at(q, k, b, hq, hk, i, j, scale) - (double)m);
+    float p = (float)((double)w / den64);
+    double dp = 0.0;
+    for (int64_t d = 0; d < q->D; d++) dp = fma(ora_load(dout, b, hq, i, d), ora_load(v, b, hk, j, d), dp);
+    *p_out = p;
+    *ds_out = (float)((double)p * (dp - delta));
+}
+
+int32_t ora_attn_backward(const ora_tensor *q, const ora_tensor *k, const ora_tensor *v, const ora_tensor *dout,
+                          int32_t causal, double scale, float *dq, float *dk, float *dv) {
+    if (!shapes_ok(q, k, v, 0, k->S, causal)) return -1;
+    if (dout->dtype != 0 || dout->B != q->B || dout->H != q->H || dout->S != q->S || dout->D != q->D) return -1;
+    const int64_t B = q->B, Hq = q->H, Hkv = k->H, Sq = q->S, Skv = k->S, D = q->D, group = Hq / Hkv;
+    const int64_t nq = B * Hq * Sq;
+    float *m = (float *)malloc((size_t)(nq ? nq : 1) * sizeof(float));
+    double *den = (double *)malloc((size_t)(nq ? nq : 1) * sizeof(double));
+    double *delta = (double *)malloc((size_t)(nq ? nq : 1) * sizeof(double));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nq; r++) {
+        int64_t b = r / (Hq * Sq), hq = (r / Sq) % Hq, i = r % Sq;
+        backward_row_stats(q, k, v, dout, b, hq, hq / group, i, causal, scale, &m[r], &den[r], &delta[r]);
+    }
+    /* dQ: exact sum over the keys of each query row */
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < nq; r++) {
+        int64_t b = r / (Hq * Sq), hq = (r / Sq) % Hq, i = r % Sq, hk = hq / group;
+        big_t *acc = (big_t *)calloc((size_t)D, sizeof(big_t));
+        for (int64_t j = 0; j < Skv; j++) {
+            if (!visible(i, j, causal)) continue;
+            float p, ds;
+            backward_pair(q, k, v, dout, b, hq, hk, i, j, scale, m[r], den[r], delta[r], &p, &ds);
+            for (int64_t d = 0; d < D; d++) big_add_double(&acc[d], (double)ds * ora_load(k, b, hk, j, d));
+        }
+        for (int64_t d = 0; d < D; d++) dq[r * D + d] = (float)(scale * big_to_double(&acc[d]));
+        free(acc);
+    }
+    /* dK, dV: exact sums over the (query head, row) pairs that see each key */
+    const int64_t nk = B * Hkv * Skv;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t c = 0; c < nk; c++) {
+        int64_t b = c / (Hkv * Skv), hk = (c / Skv) % Hkv, j = c % Skv;
+        big_t *ak = (big_t *)calloc((size_t)D, sizeof(big_t));
+        big_t *av = (big_t *)calloc((size_t)D, sizeof(big_t));
+        for (int64_t g = 0; g < group; g++) {
+            int64_t hq = hk * group + g;
+            for (int64_t i = 0; i < Sq; i++) {
+                if (!visible(i, j, causal)) continue;
+                int64_t r = (b * Hq + hq) * Sq + i;
+                float p, ds;
+                backward_pair(q, k, v, dout, b, hq, hk, i, j, scale, m[r], den[r], delta[r], &p, &ds);
+                for (int64_t d = 0; d < D; d++) {
+                    big_add_double(&ak[d], (double)ds * ora_load(q, b, hq, i, d));
+                    big_add_double(&av[d], (double)p * ora_load(dout, b, hq, i, d));
+                }
+            }
+        }
+        for (int64_t d = 0; d < D; d++) {
+            dk[c * D + d] = (float)(scale * big_to_double(&ak[d]));
+            dv[c * D + d] = (float)big_to_double(&av[d]);
+        }
+        free(ak);
+        free(av);
+    }
+    free(m);
+    free(den);
+    free(delta);
+    return 0;
+}
+
 void ora_attn_finalize(const int64_t *num, const int64_t *den, int64_t n, int64_t D, float *out) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; r++) {

@@ -91,6 +91,23 @@ void ora_digits_to_double(const int64_t *digits, int64_t n, int32_t K, int32_t E
  * 2^E_lo); planes [K][n].  Returns 0 or -1. */
 int32_t ora_double_to_digits(const double *x, int64_t n, int32_t K, int32_t E_lo, int64_t *digits);
 
+/* Attention backward over the whole key range (no page gives a backward rule;
+ * the reading fixed here keeps every sum over the sequence axes exact, so any
+ * sharding of queries or keys gives the same bits):
+ *   forward  m_i, den64_i = RN64(DEN_i), O_i as above (all keys)
+ *   delta_i  = fp64 fma chain over d of dO_id * O_id, from +0.0
+ *   dp_ij    = fp64 fma chain over d of dO_id * V_jd, from +0.0
+ *   p_ij     = RN32( RN64( w_ij / den64_i ) )
+ *   ds_ij    = RN32( RN64( p_ij * RN64( dp_ij - delta_i ) ) )
+ *   dV_jd    = RN32( RN64( sum p_ij dO_id ) )            exact sum over the visible
+ *   dK_jd    = RN32( RN64( scale * RN64( sum ds_ij Q_id ) ) )   (query head, row)
+ *   dQ_id    = RN32( RN64( scale * RN64( sum ds_ij K_jd ) ) )   exact sum over keys
+ * (dK, dV sum over the query heads that share key head hk).  dout: f32
+ * [B,Hq,Sq,D].  Outputs are contiguous f32: dq [B,Hq,Sq,D], dk and dv
+ * [B,Hkv,Skv,D].  Returns 0, or -1 on a precondition failure. */
+int32_t ora_attn_backward(const ora_tensor *q, const ora_tensor *k, const ora_tensor *v, const ora_tensor *dout,
+                          int32_t causal, double scale, float *dq, float *dk, float *dv);
+
 /* Cross-entropy.  logits: dtype 0 f32 / 1 bf16, row i at logits + i*ld. */
 void ora_ce_rowmax(const void *logits, int32_t dtype, int64_t N, int64_t ld, int64_t v_lo, int64_t v_hi,
                    float *rowmax);

@@ -59,6 +59,7 @@ def lib():
             "ora_attn_rowmax_rows": (I32, [T, T, I64, P, I64, I64, I32, D, P]),
             "ora_attn_accumulate_rows": (I32, [T, T, T, I64, P, P, I64, I64, I32, D, P, P]),
             "ora_attn_finalize": (None, [P, P, I64, I64, P]),
+            "ora_attn_backward": (I32, [T, T, T, T, I32, D, P, P, P]),
             "ora_digits_combine": (I32, [P, P, I64, I32, I32]),
             "ora_digits_to_double": (None, [P, I64, I32, I32, P]),
             "ora_double_to_digits": (I32, [P, I64, I32, I32, P]),
@@ -186,6 +187,23 @@ def det_attn(Q, K, V, causal=False, scale=None, rows=None, return_parts=False):
     if return_parts:
         return out, m, num, den
     return out
+
+
+def attn_backward(Q, K, V, dO, causal=False, scale=None):
+    """(dQ, dK, dV) as f32 arrays shaped like Q, K, V: the backward reading
+    stated in det_oracle.h (exact sums over the sequence axes)."""
+    scale = default_scale(Q.shape[3]) if scale is None else scale
+    if dO.dtype != torch.float32 or tuple(dO.shape) != tuple(Q.shape):
+        raise ValueError("dO must be float32 shaped like Q")
+    keep = []
+    dq = np.zeros(tuple(Q.shape), np.float32)
+    dk = np.zeros(tuple(K.shape), np.float32)
+    dv = np.zeros(tuple(V.shape), np.float32)
+    rc = lib().ora_attn_backward(C.byref(_tensor(Q, keep)), C.byref(_tensor(K, keep)), C.byref(_tensor(V, keep)),
+                                 C.byref(_tensor(dO, keep)), int(causal), scale, _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc:
+        raise ValueError("oracle: bad shapes")
+    return dq, dk, dv
 
 
 def digits_combine(acc: np.ndarray, part: np.ndarray, K: int, E_lo: int) -> np.ndarray:

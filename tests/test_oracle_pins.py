@@ -437,3 +437,98 @@ def test_ce_vocab_split_invariance(oracle):
         loss, denom = oracle.ce_finalize(den, x, t, m)
         assert np.array_equal(loss.view(np.uint32), ref_loss.view(np.uint32))
         assert np.array_equal(denom, ref_den)
+
+
+# ---------------------------------------------------------------- attention backward
+
+def _fp64_backward(q, k, v, dO, causal, scale):
+    """Gradients of plain fp64 softmax attention (torch autograd, CPU)."""
+    Q, K, V = [t.double().requires_grad_() for t in (q, k, v)]
+    g = q.shape[1] // k.shape[1]
+    Kr, Vr = K.repeat_interleave(g, 1), V.repeat_interleave(g, 1)
+    s = (Q @ Kr.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        Sq = q.shape[2]
+        s = s.masked_fill(~torch.ones(Sq, Sq, dtype=torch.bool).tril(), float("-inf"))
+    (torch.softmax(s, -1) @ Vr).backward(dO.double())
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_matches_fp64_autograd(oracle, causal, dtype):
+    """Within f32 rounding of the fp64 gradients: the scores, weights, p and ds
+    are each rounded to f32 once (relative 2^-24) and the exact sums once more,
+    so every gradient lies within 2^-20 (max|grad| + 1) of the fp64 value.  A
+    dropped scale, a sign, or a transposed operand is off by O(1)."""
+    q, k, v = W.attn_inputs(71, 1, 4, 2, 24, 24, 16, dtype)
+    dO = torch.randn(1, 4, 24, 16, generator=torch.Generator().manual_seed(72))
+    got = oracle.attn_backward(q, k, v, dO, causal, 0.25)
+    ref = _fp64_backward(q, k, v, dO, causal, 0.25)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        tol = 2.0 ** -20 * (np.abs(b).max() + 1)
+        assert np.abs(a - b).max() <= tol, (name, np.abs(a - b).max(), tol)
+
+
+def test_backward_single_key_closed_form(oracle):
+    """One key: O = V_0 exactly, so delta_i equals dp_i0 bit for bit and every
+    ds is 0 (dQ = dK = +0); p = 1, so dV_0 = RN32(RN64(exact sum of dO)) over
+    all query heads and rows, which math.fsum rounds correctly."""
+    q, k, v = W.attn_inputs(73, 1, 4, 2, 9, 1, 8, torch.float32)
+    dO = torch.randn(1, 4, 9, 8, generator=torch.Generator().manual_seed(74))
+    dq, dk, dv = oracle.attn_backward(q, k, v, dO, False, 0.3)
+    assert not dq.any() and not np.signbit(dq).any()
+    assert not dk.any() and not np.signbit(dk).any()
+    for hk in range(2):
+        for d in range(8):
+            terms = [float(x) for x in dO[0, 2 * hk:2 * hk + 2, :, d].reshape(-1)]
+            assert dv[0, hk, 0, d] == np.float32(math.fsum(terms))
+
+
+def test_backward_zero_upstream(oracle):
+    q, k, v = W.attn_inputs(75, 1, 2, 1, 12, 12, 8, torch.bfloat16)
+    dq, dk, dv = oracle.attn_backward(q, k, v, torch.zeros(1, 2, 12, 8), True, 0.35)
+    for g in (dq, dk, dv):
+        assert not g.any() and not np.signbit(g).any()
+
+
+def test_backward_uniform_scores_closed_form(oracle):
+    """K = 0: every score is 0, every weight 1, and p_ij = RN32(1/n_i) with n_i
+    the keys row i sees; dV_jd = RN32(exact sum of p_ij dO_id) (Fractions) and
+    dQ = 0 (every term has a zero factor)."""
+    q, k, v = W.attn_inputs(76, 1, 2, 1, 10, 10, 4, torch.float32)
+    k = torch.zeros_like(k)
+    dO = torch.randn(1, 2, 10, 4, generator=torch.Generator().manual_seed(77))
+    for causal in (False, True):
+        dq, dk, dv = oracle.attn_backward(q, k, v, dO, causal, 0.5)
+        assert not dq.any()
+        for j in range(10):
+            for d in range(4):
+                tot = Fraction(0)
+                for h in range(2):
+                    for i in range(10):
+                        if causal and j > i:
+                            continue
+                        n = i + 1 if causal else 10
+                        p = float(np.float32(1.0 / n))
+                        tot += Fraction(p) * Fraction(float(dO[0, h, i, d]))
+                assert dv[0, 0, j, d] == rn32_exact(tot), (causal, j, d)
+
+
+def test_backward_sequence_permutations(oracle):
+    """The sums over keys and over queries are exact: permuting K/V rows
+    permutes dK/dV and leaves dQ's bits; permuting Q/dO rows permutes dQ and
+    leaves dK/dV's bits (non-causal, where the order of rows carries no mask)."""
+    q, k, v = W.attn_inputs(78, 1, 4, 2, 20, 28, 16, torch.bfloat16)
+    dO = torch.randn(1, 4, 20, 16, generator=torch.Generator().manual_seed(79))
+    base = oracle.attn_backward(q, k, v, dO, False, 0.25)
+    pk = torch.randperm(28, generator=torch.Generator().manual_seed(80))
+    dq, dk, dv = oracle.attn_backward(q, k[:, :, pk], v[:, :, pk], dO, False, 0.25)
+    assert np.array_equal(dq.view(np.uint32), base[0].view(np.uint32))
+    assert np.array_equal(dk.view(np.uint32), base[1][:, :, pk.numpy()].view(np.uint32))
+    assert np.array_equal(dv.view(np.uint32), base[2][:, :, pk.numpy()].view(np.uint32))
+    pq = torch.randperm(20, generator=torch.Generator().manual_seed(81))
+    dq, dk, dv = oracle.attn_backward(q[:, :, pq], k, v, dO[:, :, pq].contiguous(), False, 0.25)
+    assert np.array_equal(dq.view(np.uint32), base[0][:, :, pq.numpy()].view(np.uint32))
+    assert np.array_equal(dk.view(np.uint32), base[1].view(np.uint32))
+    assert np.array_equal(dv.view(np.uint32), base[2].view(np.uint32))
