@@ -46,6 +46,9 @@ SIGNATURES = {
     "det_profile_end": (_SZ, [C.c_char_p, _SZ]),
     "det_attn_workspace_size": (_SZ, [_T, _T, _T, _I32]),
     "det_attn": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _SZ, _P]),
+    "det_attn_stats": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _P, _P, _SZ, _P]),
+    "det_attn_backward_workspace_size": (_SZ, [_T, _T, _T, _I32]),
+    "det_attn_backward": (C.c_int, [_T, _T, _T, _T, _T, _P, _P, _I32, _D, _O, _O, _O, _P, _SZ, _P]),
     "det_attn_rowmax_workspace_size": (_SZ, [_T, _T, _I64, _I64]),
     "det_attn_rowmax": (C.c_int, [_T, _T, _I64, _I64, _I32, _D, _P, _P, _SZ, _P]),
     "det_attn_accumulate_workspace_size": (_SZ, [_T, _T, _T, _I64, _I64]),

@@ -75,6 +75,72 @@ def det_attn(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = F
     return out
 
 
+def det_attn_with_stats(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = False,
+                        scale: Optional[float] = None):
+    """det_attn plus each row's max (f32 [B, Hq, Sq]) and RN64(DEN) (f64
+    [B, Hq, Sq]), the two values the gradients need."""
+    scale = default_scale(Q.shape[3]) if scale is None else float(scale)
+    q, k, v = _desc(Q), _desc(K), _desc(V)
+    out = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
+    m = torch.empty(Q.shape[:3], dtype=torch.float32, device=Q.device)
+    den = torch.empty(Q.shape[:3], dtype=torch.float64, device=Q.device)
+    L = lib()
+    nbytes = L.det_attn_workspace_size(C.byref(q), C.byref(k), C.byref(v), int(causal))
+    ws, addr = _workspace(nbytes, Q.device)
+    check(L.det_attn_stats(C.byref(q), C.byref(k), C.byref(v), int(causal), scale, C.byref(_out(out)),
+                           m.data_ptr(), den.data_ptr(), addr, nbytes, _stream(Q)))
+    return out, m, den
+
+
+def det_attn_backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor,
+                      rowmax: torch.Tensor, den64: torch.Tensor, causal: bool = False,
+                      scale: Optional[float] = None):
+    """(dQ, dK, dV) as float32 tensors shaped like Q, K, V: exact sums over
+    the sequence axes (the rule stated in include/det_attn.h).  O and dO are
+    the float32 forward output and its gradient; rowmax and den64 come from
+    det_attn_with_stats."""
+    scale = default_scale(Q.shape[3]) if scale is None else float(scale)
+    if O.dtype != torch.float32 or dO.dtype != torch.float32:
+        raise TypeError("O and dO must be float32")
+    for t, dt in ((rowmax, torch.float32), (den64, torch.float64)):
+        if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != tuple(Q.shape[:3]):
+            raise ValueError("rowmax / den64 must be contiguous [B, Hq, Sq] float32 / float64")
+    q, k, v, o, g = _desc(Q), _desc(K), _desc(V), _desc(O), _desc(dO)
+    dq = torch.empty(Q.shape, dtype=torch.float32, device=Q.device)
+    dk = torch.empty(K.shape, dtype=torch.float32, device=Q.device)
+    dv = torch.empty(V.shape, dtype=torch.float32, device=Q.device)
+    L = lib()
+    nbytes = L.det_attn_backward_workspace_size(C.byref(q), C.byref(k), C.byref(v), int(causal))
+    ws, addr = _workspace(nbytes, Q.device)
+    check(L.det_attn_backward(C.byref(q), C.byref(k), C.byref(v), C.byref(o), C.byref(g), rowmax.data_ptr(),
+                              den64.data_ptr(), int(causal), scale, C.byref(_out(dq)), C.byref(_out(dk)),
+                              C.byref(_out(dv)), addr, nbytes, _stream(Q)))
+    return dq, dk, dv
+
+
+class _DetAttnFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, Q, K, V, causal, scale):
+        out, m, den = det_attn_with_stats(Q, K, V, causal, scale)
+        ctx.save_for_backward(Q, K, V, out, m, den)
+        ctx.causal, ctx.scale = causal, scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dO):
+        Q, K, V, out, m, den = ctx.saved_tensors
+        dq, dk, dv = det_attn_backward(Q, K, V, out, dO.float(), m, den, ctx.causal, ctx.scale)
+        return dq.to(Q.dtype), dk.to(K.dtype), dv.to(V.dtype), None, None
+
+
+def det_attn_autograd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal: bool = False,
+                      scale: Optional[float] = None) -> torch.Tensor:
+    """det_attn with gradients through det_attn_backward (cast to the input
+    dtypes, round to nearest)."""
+    scale = default_scale(Q.shape[3]) if scale is None else float(scale)
+    return _DetAttnFunction.apply(Q, K, V, causal, scale)
+
+
 def rowmax(Q: torch.Tensor, K: torch.Tensor, kv_lo: int = 0, kv_hi: Optional[int] = None, causal: bool = False,
            scale: Optional[float] = None) -> torch.Tensor:
     """Per-query max score over keys [kv_lo, kv_hi): f32 [B, Hq, Sq]."""

@@ -417,8 +417,9 @@ size_t det_attn_workspace_size(const det_tensor *q, const det_tensor *k, const d
     return default_size(g.Sq, [&](int64_t ni) { return bytes_fused(g, mf, ni); });
 }
 
-int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
-             const det_out *o, void *workspace, size_t ws_bytes, void *stream) {
+static int fused_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
+                      const det_out *o, float *stat_m, double *stat_den, void *workspace, size_t ws_bytes,
+                      void *stream) {
     int rc;
     if ((rc = check_qkv(q, k, v, causal))) return rc;
     if (q->S > 0 && (rc = check_out(o))) return rc;
@@ -451,9 +452,74 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
                            keys, ni, i0, s),
                 "scores");
         HIP_TRY(launch_pv(tv, g, vp, sc, nullptr, keys, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr,
-                          nullptr, 0, 0, 0, ff, s),
+                          nullptr, 0, 0, 0, ff, s, stat_m, stat_den, g.Sq),
                 "deposit");
     }
+    return ok();
+}
+
+int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
+             const det_out *o, void *workspace, size_t ws_bytes, void *stream) {
+    return fused_attn(q, k, v, causal, scale, o, nullptr, nullptr, workspace, ws_bytes, stream);
+}
+
+int det_attn_stats(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
+                   const det_out *o, float *rowmax, double *den64, void *workspace, size_t ws_bytes, void *stream) {
+    if (q && q->S > 0 && (!rowmax || !den64)) return fail(DET_E_NULL, "rowmax or den64 is NULL");
+    if (k && k->S == 0 && q && q->S > 0) return fail(DET_E_SHAPE, "det_attn_stats needs a nonempty key range");
+    return fused_attn(q, k, v, causal, scale, o, rowmax, den64, workspace, ws_bytes, stream);
+}
+
+static int check_grad_operand(const det_tensor *t, const det_tensor *q, const char *name) {
+    int rc;
+    if ((rc = check_tensor(t, name))) return rc;
+    if (t->dtype != DET_F32) return fail(DET_E_DTYPE, "%s must be DET_F32", name);
+    if (t->B != q->B || t->H != q->H || t->S != q->S || t->D != q->D)
+        return fail(DET_E_SHAPE, "%s shape differs from q", name);
+    return DET_OK;
+}
+
+static size_t bytes_backward(const AttnGeom &g, int64_t ni) { return bwd_fixed_bytes(g) + bwd_chunk_bytes(g, ni); }
+
+size_t det_attn_backward_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
+                                        int32_t causal) {
+    if (check_qkv(q, k, v, causal)) return 0;
+    const AttnGeom g = geom(q, k, causal, 1.0);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_backward(g, ni); });
+}
+
+int det_attn_backward(const det_tensor *q, const det_tensor *k, const det_tensor *v, const det_tensor *o,
+                      const det_tensor *dout, const float *rowmax, const double *den64, int32_t causal,
+                      double scale, const det_out *dq, const det_out *dk, const det_out *dv, void *workspace,
+                      size_t ws_bytes, void *stream) {
+    int rc;
+    if ((rc = check_qkv(q, k, v, causal))) return rc;
+    if ((rc = check_grad_operand(o, q, "o")) || (rc = check_grad_operand(dout, q, "dout"))) return rc;
+    if (q->S > 0 && (rc = check_out(dq))) return rc;
+    if (k->S > 0 && ((rc = check_out(dk)) || (rc = check_out(dv)))) return rc;
+    if (q->S > 0 && k->S > 0 && (!rowmax || !den64)) return fail(DET_E_NULL, "rowmax or den64 is NULL");
+    const AttnGeom g = geom(q, k, causal, scale);
+    auto need = [&](int64_t ni) { return bytes_backward(g, ni); };
+    const bool work = g.Sq > 0 && g.Skv > 0;
+    if ((rc = check_ws(workspace, ws_bytes, work ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (!work) {  // no pair: every gradient is zero
+        if (g.Sq > 0) HIP_TRY(launch_zero_view(OutView{dq->data, dq->sB, dq->sH, dq->sS}, g.B, g.Hq, g.Sq, g.D, s), "zero dq");
+        if (g.Skv > 0) {
+            HIP_TRY(launch_zero_view(OutView{dk->data, dk->sB, dk->sH, dk->sS}, g.B, g.Hkv, g.Skv, g.D, s), "zero dk");
+            HIP_TRY(launch_zero_view(OutView{dv->data, dv->sB, dv->sH, dv->sS}, g.B, g.Hkv, g.Skv, g.D, s), "zero dv");
+        }
+        return ok();
+    }
+    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need);
+    Carver c0{(char *)workspace, ws_bytes};
+    void *fixed = c0.take<char>(bwd_fixed_bytes(g));
+    void *cws = c0.take<char>(bwd_chunk_bytes(g, chunk));
+    if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
+    HIP_TRY(launch_attn_backward(to_t(q), to_t(k), to_t(v), to_t(o), to_t(dout), rowmax, den64, g, fixed, cws, chunk,
+                                 OutView{dq->data, dq->sB, dq->sH, dq->sS}, OutView{dk->data, dk->sB, dk->sH, dk->sS},
+                                 OutView{dv->data, dv->sB, dv->sH, dv->sS}, s),
+            "backward");
     return ok();
 }
 

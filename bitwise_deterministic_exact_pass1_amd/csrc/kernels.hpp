@@ -82,6 +82,19 @@ size_t qk_kprep_bytes(const AttnGeom &g, int64_t kv_len);
 size_t qk_chunk_bytes(const AttnGeom &g, int64_t ni, int64_t kv_len);
 hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws,
                            hipStream_t s);
+// ---- attention backward (bwd.hip)
+constexpr int kBwdDigits = 18;   // radix-2^32 digits of a gradient sum (products of two f32 values)
+constexpr int kBwdElo = -298;    // their lsb exponent
+// delta and the dK / dV digit planes (whole problem) / P, DS and the dQ digit
+// planes of a chunk of ni query rows
+size_t bwd_fixed_bytes(const AttnGeom &g);
+size_t bwd_chunk_bytes(const AttnGeom &g, int64_t ni);
+hipError_t launch_zero_view(const OutView &o, int64_t B, int64_t H, int64_t S, int64_t D, hipStream_t s);
+hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &v, const Tensor &o,
+                                const Tensor &dout, const float *rowmax, const double *den64, const AttnGeom &g,
+                                void *fixed_ws, void *chunk_ws, int64_t chunk, const OutView &dq,
+                                const OutView &dk, const OutView &dv, hipStream_t s);
+
 // Capacity of the remainder list of one V preparation (entries of all heads);
 // heads whose remainders do not fit take the generic exact path.
 constexpr int kRareCap = 4096;
@@ -133,6 +146,8 @@ size_t vrare_bytes(const AttnGeom &g);
 size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i);
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
                         hipStream_t s);
+// With `o`, stat_m / stat_den (both or neither) also receive each row's max
+// and RN64(DEN) at [bh * stat_rows + i].
 // Exact NUM/DEN of query rows [i0,i1) against keys [kv_lo,kv_hi) from stored
 // scores (chunk layout [bh][i-i0][j-kv_lo]) and rowmax[bh*rm_rows + i - rm_row0]
 // (or, when rowmax is null, the order keys rowmax_keys at the same place).
@@ -142,7 +157,8 @@ hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64
 hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
                      const uint32_t *rowmax_keys, int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
                      int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
-                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s);
+                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s,
+                     float *stat_m = nullptr, double *stat_den = nullptr, int64_t stat_rows = 0);
 
 hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hipStream_t s);
 hipError_t launch_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int n_digits,

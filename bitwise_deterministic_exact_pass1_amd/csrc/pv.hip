@@ -126,6 +126,10 @@ struct PvArgs {
     // remainders of V entries below their column grids (vprep.hpp)
     const int *rare_n, *rare_grp;
     const int4 *rare;
+    // fused, optional: each row's max and RN64(DEN) at [bh * stat_rows + i]
+    float *stat_m;
+    double *stat_den;
+    int64_t stat_rows;
 };
 
 // The row max of row i of head bh (from floats or from order keys).
@@ -349,7 +353,12 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
     }
     if (bad) S.bad[par] = 1;
     __syncthreads();
-    return S.bad[par] != 0;
+    const bool generic = S.bad[par] != 0;
+    if (A.stat_den && !generic && rowok && ptid % TPR == 0) {  // (generic tiles write theirs there)
+        A.stat_den[bh * A.stat_rows + i] = S.d64[par][r];
+        A.stat_m[bh * A.stat_rows + i] = m;
+    }
+    return generic;
 }
 
 // The consumer's block loop for a wave whose group has BV V digits (0: no
@@ -739,6 +748,10 @@ __device__ __forceinline__ void fallback_tile(const PvArgs &A, const TV *__restr
         const double n64 = digits_to_f64<kNumDigits>(nd, kNumElo);
         const double d64 = digits_to_f64<kDenDigits>(dd, kDenElo);
         A.o[b * A.osB + hq * A.osH + i * A.osS + d] = (float)(n64 / d64);
+        if (A.stat_den && d == 0) {
+            A.stat_den[bh * A.stat_rows + i] = d64;
+            A.stat_m[bh * A.stat_rows + i] = pv_rowmax(A, bh, i);
+        }
     }
 }
 
@@ -840,7 +853,8 @@ static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &v
 hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
                      const uint32_t *rowmax_keys, int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
                      int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
-                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s) {
+                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s,
+                     float *stat_m, double *stat_den, int64_t stat_rows) {
     const int64_t ni = i1 - i0;
     if (ni <= 0) return hipSuccess;
     if (vp.Dp32 > 256) return hipErrorInvalidValue;
@@ -893,6 +907,11 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
     a.rare_n = vp.rare_n;
     a.rare_grp = vp.rare_grp;
     a.rare = vp.rare;
+    if (o && stat_m && stat_den) {
+        a.stat_m = stat_m;
+        a.stat_den = stat_den;
+        a.stat_rows = stat_rows;
+    }
     return o ? launch_pv_t<true>(v, g, vp, a, bh, fb_num, fb_den, s)
              : launch_pv_t<false>(v, g, vp, a, bh, fb_num, fb_den, s);
 }

@@ -115,6 +115,35 @@ size_t det_attn_workspace_size(const det_tensor *q, const det_tensor *k, const d
 int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
              const det_out *o, void *workspace, size_t ws_bytes, void *stream);
 
+/* det_attn plus the two per-row values its gradients need (det-attn page,
+ * "Method": the global row max and the exact denominator): rowmax (device)
+ * f32 [B][Hq][Sq] and den64 (device) f64 [B][Hq][Sq] = RN64(DEN).  Same
+ * workspace as det_attn; o is bit-identical to det_attn's. */
+int det_attn_stats(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
+                   const det_out *o, float *rowmax, double *den64, void *workspace, size_t ws_bytes, void *stream);
+
+/* Gradients of det_attn over the whole key range.  The pages give no
+ * backward rule; this one keeps every sum over the sequence axes exact (the
+ * det-attn page's "Method" property), so any sharding of queries or keys
+ * gives the same bits.  With w and den64 as in the forward:
+ *   delta_i = fp64 fma chain over d of dO_id O_id;  dp_ij = the chain of dO_id V_jd
+ *   p_ij = RN32(RN64(w_ij / den64_i));  ds_ij = RN32(RN64(p_ij RN64(dp_ij - delta_i)))
+ *   dV_jd = RN32(RN64(sum p_ij dO_id)), dK_jd = RN32(RN64(scale RN64(sum ds_ij Q_id))),
+ *   dQ_id = RN32(RN64(scale RN64(sum ds_ij K_jd))), every sum exact (dK and dV
+ *   over all query heads that share the key head).
+ * q, k, v: as det_attn.  o: the forward output and dout: its gradient, both
+ * DET_F32 [B][Hq][Sq][D] (any strides, D stride 1).  rowmax, den64: (device)
+ * from det_attn_stats.  dq: f32 [B][Hq][Sq][D]; dk, dv: f32 [B][Hkv][Skv][D]
+ * (caller-owned device memory, D stride 1).  Rows without a visible key get
+ * dq = 0.  Workspace: det_attn_backward_workspace_size() bytes or more (more
+ * lets the library take more query rows per launch; bits never change). */
+size_t det_attn_backward_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
+                                        int32_t causal);
+int det_attn_backward(const det_tensor *q, const det_tensor *k, const det_tensor *v, const det_tensor *o,
+                      const det_tensor *dout, const float *rowmax, const double *den64, int32_t causal,
+                      double scale, const det_out *dq, const det_out *dk, const det_out *dv, void *workspace,
+                      size_t ws_bytes, void *stream);
+
 /* det-attn page, "API": rowmax(Q, K, ..., kv_lo, kv_hi) -- per-query max
  * score over keys [kv_lo, kv_hi) (combine shards by max).
  * rowmax: (device) f32 [B][Hq][Sq].  Workspace: det_attn_rowmax_workspace_size(). */

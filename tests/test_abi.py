@@ -102,6 +102,28 @@ def test_workspace_sizes_are_host_only(lib):
     assert lib.det_attn_workspace_size(None, C.byref(k), C.byref(v), 0) == 0
 
 
+def _call_bwd(lib, q, k, v, o, g, rowmax=0x6000, den=0x7000, out=True, ws=0x10000, nbytes=1 << 30):
+    d = L.Out(0x2000, 2 * 8 * 16, 8 * 16, 16) if out else None
+    return lib.det_attn_backward(C.byref(q), C.byref(k), C.byref(v), C.byref(o), C.byref(g), rowmax, den, 0, 0.25,
+                                 C.byref(d) if d else None, C.byref(d) if d else None, C.byref(d) if d else None,
+                                 ws, nbytes, None)
+
+
+def test_backward_argument_errors(lib):
+    q, k, v = _t(), _t(H=1), _t(H=1)
+    o, g = _t(dtype=L.DET_F32), _t(dtype=L.DET_F32)
+    assert _call_bwd(lib, q, k, v, _t(dtype=L.DET_BF16), g) == -3  # o must be f32
+    assert _call_bwd(lib, q, k, v, o, _t(S=7, dtype=L.DET_F32)) == -2  # dout shaped like q
+    assert _call_bwd(lib, q, k, v, o, g, rowmax=0) == -1
+    assert _call_bwd(lib, q, k, v, o, g, out=False) == -1
+    assert _call_bwd(lib, q, k, v, o, g, ws=0) == -5
+    assert _call_bwd(lib, q, k, _t(H=1, S=9), o, g) == -2
+    assert lib.det_attn_backward_workspace_size(C.byref(q), C.byref(k), C.byref(v), 0) > 0
+    so = L.Out(0x2000, 256, 128, 16)
+    assert lib.det_attn_stats(C.byref(q), C.byref(k), C.byref(v), 0, 0.25, C.byref(so), None, 0x7000, 0x10000,
+                              1 << 30, None) == -1
+
+
 def test_cross_entropy_argument_errors(lib):
     assert lib.det_ce_rowmax(0x1000, 3, 4, 10, 0, 10, 0x2000, None) == -3
     assert lib.det_ce_rowmax(0x1000, 1, 4, 10, 0, 11, 0x2000, None) == -2
@@ -158,4 +180,13 @@ def test_workspace_layout_fits_the_reported_size(lib, case, dtype):
     n = lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), lo, hi)
     rc = lib.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), 0x500000, lo, hi, causal, 0.125, 0x600000,
                                  0x700000, 0, ws, n, None)
+    assert rc == -6, (rc, lib.det_last_error())
+    n = lib.det_attn_workspace_size(C.byref(q), C.byref(k), C.byref(v), causal)
+    rc = lib.det_attn_stats(C.byref(q), C.byref(k), C.byref(v), causal, 0.125, C.byref(o), 0x500000, 0x600000, ws,
+                            n, None)
+    assert rc == -6, (rc, lib.det_last_error())
+    of = _t(B=B, H=Hq, S=S, D=D, dtype=L.DET_F32, data=0x400000)
+    n = lib.det_attn_backward_workspace_size(C.byref(q), C.byref(k), C.byref(v), causal)
+    rc = lib.det_attn_backward(C.byref(q), C.byref(k), C.byref(v), C.byref(of), C.byref(of), 0x500000, 0x600000,
+                               causal, 0.125, C.byref(o), C.byref(o), C.byref(o), ws, n, None)
     assert rc == -6, (rc, lib.det_last_error())

@@ -1,0 +1,126 @@
+"""GPU parity of the attention backward (exact sums over the sequence axes)
+against the CPU oracle, bit for bit, plus the forward's per-row statistics it
+consumes, key-order invariance and the autograd wrapper.  Inputs come from the
+seeded generators in workloads.py; the upstream gradient is N(0,1) f32."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from bitwise_deterministic_exact_pass1_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def A():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    from bitwise_deterministic_exact_pass1_amd import attention
+    return attention
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bits(x):
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(x, np.float32).view(np.uint32)
+
+
+def assert_bits_equal(a, b, what):
+    ua, ub = bits(a), bits(b)
+    if not np.array_equal(ua, ub):
+        bad = np.argwhere(ua != ub)
+        raise AssertionError(f"{what}: {len(bad)} of {ua.size} differ; first at {bad[0].tolist()}")
+
+
+def upstream(seed, shape):
+    return torch.randn(*shape, generator=torch.Generator().manual_seed(seed))
+
+
+def gpu_backward(A, q, k, v, dO, causal, scale):
+    Q, K, V = q.cuda(), k.cuda(), v.cuda()
+    out, m, den = A.det_attn_with_stats(Q, K, V, causal, scale)
+    return A.det_attn_backward(Q, K, V, out, dO.cuda(), m, den, causal, scale)
+
+
+CASES = [
+    # (seed, B, Hq, Hkv, S_q, S_kv, D, dtype, causal)
+    (901, 1, 4, 2, 40, 40, 16, torch.float32, True),
+    (902, 1, 4, 2, 40, 40, 16, torch.float32, False),
+    (903, 1, 4, 2, 72, 72, 64, torch.bfloat16, True),
+    (904, 2, 2, 1, 33, 50, 64, torch.bfloat16, False),
+    (905, 1, 2, 2, 45, 45, 3, torch.bfloat16, True),
+    (906, 1, 2, 1, 37, 37, 100, torch.float32, True),
+    (907, 1, 2, 2, 24, 24, 256, torch.bfloat16, False),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"s{c[0]}-D{c[6]}-{str(c[7])[6:]}-{'c' if c[8] else 'n'}")
+def test_backward_bit_exact(A, oracle, case):
+    seed, B, Hq, Hkv, Sq, Skv, D, dtype, causal = case
+    q, k, v = W.attn_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
+    dO = upstream(seed + 1, (B, Hq, Sq, D))
+    scale = W.default_scale(D)
+    say(f"backward {case}: oracle")
+    ref = oracle.attn_backward(q, k, v, dO, causal, scale)
+    say("backward: gpu")
+    got = gpu_backward(A, q, k, v, dO, causal, scale)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert_bits_equal(a, b, name)
+
+
+def test_backward_gqa_causal_several_tiles(A, oracle):
+    """B=2 Hq=8 Hkv=2 S=200 D=128 bf16 causal: many 16-row and 16-key tiles,
+    ragged at both ends, four query heads per key head."""
+    q, k, v = W.attn_inputs(910, 2, 8, 2, 200, 200, 128, torch.bfloat16)
+    dO = upstream(911, (2, 8, 200, 128))
+    scale = W.default_scale(128)
+    say("backward gqa S=200: oracle")
+    ref = oracle.attn_backward(q, k, v, dO, True, scale)
+    got = gpu_backward(A, q, k, v, dO, True, scale)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert_bits_equal(a, b, name)
+
+
+def test_forward_stats(A, oracle):
+    """det_attn_with_stats: the same output as det_attn, the oracle's row
+    maxima, and RN64 of the oracle's exact denominators."""
+    q, k, v = W.attn_inputs(912, 1, 4, 2, 130, 130, 64, torch.bfloat16)
+    scale = W.default_scale(64)
+    Q, K, V = q.cuda(), k.cuda(), v.cuda()
+    out, m, den = A.det_attn_with_stats(Q, K, V, True, scale)
+    assert torch.equal(out, A.det_attn(Q, K, V, True, scale))
+    ref, rm, num, dd = oracle.det_attn(q, k, v, True, scale, return_parts=True)
+    assert_bits_equal(m, rm, "rowmax")
+    den_ref = oracle.digits_to_double(dd.reshape(dd.shape[0], -1), oracle.DEN_DIGITS, oracle.DEN_ELO)
+    assert np.array_equal(den.cpu().numpy().reshape(-1), den_ref)
+
+
+def test_backward_key_permutation_invariance(A):
+    """Non-causal: permuting K/V rows permutes dK/dV and leaves dQ's bits."""
+    q, k, v = W.attn_inputs(913, 1, 4, 2, 64, 96, 32, torch.bfloat16)
+    dO = upstream(914, (1, 4, 64, 32))
+    scale = W.default_scale(32)
+    base = gpu_backward(A, q, k, v, dO, False, scale)
+    p = torch.randperm(96, generator=torch.Generator().manual_seed(915))
+    dq, dk, dv = gpu_backward(A, q, k[:, :, p].contiguous(), v[:, :, p].contiguous(), dO, False, scale)
+    assert torch.equal(dq, base[0])
+    assert torch.equal(dk, base[1][:, :, p.cuda()])
+    assert torch.equal(dv, base[2][:, :, p.cuda()])
+
+
+def test_autograd_wrapper(A):
+    q, k, v = W.attn_inputs(916, 1, 4, 2, 48, 48, 32, torch.bfloat16)
+    G = upstream(917, (1, 4, 48, 32)).cuda()
+    scale = W.default_scale(32)
+    Q, K, V = [t.cuda().requires_grad_() for t in (q, k, v)]
+    out = A.det_attn_autograd(Q, K, V, True, scale)
+    (out * G).sum().backward()
+    dq, dk, dv = gpu_backward(A, q, k, v, G.cpu(), True, scale)
+    assert torch.equal(Q.grad, dq.to(torch.bfloat16))
+    assert torch.equal(K.grad, dk.to(torch.bfloat16))
+    assert torch.equal(V.grad, dv.to(torch.bfloat16))
