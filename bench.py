@@ -188,7 +188,8 @@ def main():
 
 
 def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
-    """Side numbers: the sharded composition (16 x 64 keys) on the same inputs,
+    """Side numbers: the sharded composition (16 x 64 keys) and the exact
+    backward on the same inputs,
     cross-entropy forward/backward on N=4096, V=128256 bf16, the float32
     contrast, the fused path on the larger causal shares (S=8192 D=128,
     S=2048 D=256), and on the long non-causal NHD share (S=37810, 56 heads)."""
@@ -223,6 +224,30 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     res["cross_entropy"] = {"workload": "N=4096 V=128256 bf16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                             "forward_token_vocab_per_s": N * Vv / (fwd_ms / 1e3),
                             "backward_hbm_GBps": N * Vv * 6 / (bwd_ms / 1e3) / 1e9}
+    # gradients of the same step: forward with row statistics, then the exact backward
+    Gd = torch.randn(Q.shape, generator=torch.Generator().manual_seed(4242)).cuda()
+    o_s, m_s, den_s = attention.det_attn_with_stats(Q, K, V, causal, scale)
+    attention.det_attn_backward(Q, K, V, o_s, Gd, m_s, den_s, causal, scale)
+    torch.cuda.synchronize()
+    from bitwise_deterministic_exact_pass1_amd import _lib
+    _lib.profile_begin()
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    eb[0].record()
+    o_s, m_s, den_s = attention.det_attn_with_stats(Q, K, V, causal, scale)
+    eb[1].record()
+    attention.det_attn_backward(Q, K, V, o_s, Gd, m_s, den_s, causal, scale)
+    eb[2].record()
+    torch.cuda.synchronize()
+    bprof = _lib.profile_end()
+    bwd_ms = eb[1].elapsed_time(eb[2])
+    D_ = Q.shape[3]
+    res["backward"] = {"workload": "the same inputs, upstream gradient N(0,1) f32",
+                       "forward_with_stats_ms": eb[0].elapsed_time(eb[1]), "backward_ms": bwd_ms,
+                       "pairs_per_s": pairs / (bwd_ms / 1e3),
+                       "flop_per_pair": 10 * D_ + 32,
+                       "frac_of_fp64_roofline": pairs * (10 * D_ + 32) / (bwd_ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS,
+                       "kernels_ms": {k_: round(t, 4) for k_, (c, t) in bprof.items() if k_.startswith("bwd")}}
+    del Gd, o_s, m_s, den_s
     # the float32 combines the exact path replaces, on the same inputs
     from bitwise_deterministic_exact_pass1_amd import contrast
     res["contrast"] = {"attention_4_shard_rotations": contrast.attention_contrast(attention, Q, K, V, [K.shape[2] // 4] * 4,

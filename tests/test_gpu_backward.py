@@ -124,3 +124,31 @@ def test_autograd_wrapper(A):
     assert torch.equal(Q.grad, dq.to(torch.bfloat16))
     assert torch.equal(K.grad, dk.to(torch.bfloat16))
     assert torch.equal(V.grad, dv.to(torch.bfloat16))
+
+
+def test_backward_small_workspace_row_chunks(A):
+    """Half the default workspace makes the library take the query rows in
+    chunks of 32 (dK and dV keep adding into the same digits, dQ is finished
+    chunk by chunk); the gradients must be the same bits."""
+    import ctypes as C
+    from bitwise_deterministic_exact_pass1_amd import _lib
+    q, k, v = W.attn_inputs(918, 2, 8, 2, 200, 200, 128, torch.bfloat16)
+    dO = upstream(919, (2, 8, 200, 128)).cuda()
+    scale = W.default_scale(128)
+    Q, K, V = q.cuda(), k.cuda(), v.cuda()
+    out, m, den = A.det_attn_with_stats(Q, K, V, True, scale)
+    ref = A.det_attn_backward(Q, K, V, out, dO, m, den, True, scale)
+    L = _lib.lib()
+    dq_, dk_, dv_ = A._desc(Q), A._desc(K), A._desc(V)
+    full = L.det_attn_backward_workspace_size(C.byref(dq_), C.byref(dk_), C.byref(dv_), 1)
+    small = (full // 2) // 256 * 256
+    ws = torch.empty(small + 256, dtype=torch.uint8, device=Q.device)
+    addr = (ws.data_ptr() + 255) & ~255
+    g = [torch.empty_like(t, dtype=torch.float32) for t in (Q, K, V)]
+    say(f"backward with {small} of {full} workspace bytes")
+    _lib.check(L.det_attn_backward(C.byref(dq_), C.byref(dk_), C.byref(dv_), C.byref(A._desc(out)),
+                                   C.byref(A._desc(dO)), m.data_ptr(), den.data_ptr(), 1, scale,
+                                   C.byref(A._out(g[0])), C.byref(A._out(g[1])), C.byref(A._out(g[2])), addr, small,
+                                   A._stream(Q)))
+    for a, b in zip(g, ref):
+        assert torch.equal(a, b)
