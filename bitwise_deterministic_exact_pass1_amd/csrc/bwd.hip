@@ -109,25 +109,33 @@ __global__ __launch_bounds__(256) void k_bwd_pds(BwdArgs A) {
     A.DS[at] = ds;
 }
 
-// Adds the exact product t (a multiple of 2^-298, |t| < 2^256) into the
-// calling thread's digits dig[k][tid].
-__device__ __forceinline__ void bwd_deposit(double t, int64_t (*dig)[256], int tid) {
-    if (t == 0.0) return;
-    const uint64_t bits = (uint64_t)__double_as_longlong(t);
-    int64_t m = (int64_t)((bits & 0xfffffffffffffull) | 0x10000000000000ull);
-    int shift = (int)((bits >> 52) & 0x7ff) - 1075 - kBwdElo;  // lsb of m, counted from 2^-298
-    if (shift < 0) {  // the bits below 2^-298 are zero: dropping them is exact
-        m >>= -shift;
-        shift = 0;
+// Adds the exact product of the f32 values with bit patterns ua and ub into
+// the calling thread's digits.  The product is m 2^s with m = ma mb < 2^48
+// (the significands) and s = ea + eb - 2 counted from 2^-298 (ea, eb the
+// biased exponents, 1 for subnormals); its three 32-bit limbs go to digits
+// s/32 .. s/32 + 2 by LDS atomic adds, which need no result and so do not
+// wait on one another (the digits are the thread's own: no contention).
+__device__ __forceinline__ void bwd_term(uint32_t ua, uint32_t ub, int64_t (*dig)[256], int tid) {
+    const uint32_t ea = (ua >> 23) & 0xffu, eb = (ub >> 23) & 0xffu;
+    const uint64_t ma = (ua & 0x7fffffu) | (ea ? 0x800000u : 0u), mb = (ub & 0x7fffffu) | (eb ? 0x800000u : 0u);
+    const uint64_t m = ma * mb;
+    if (m == 0) return;
+    const int s = (int)max(ea, 1u) + (int)max(eb, 1u) - 2;
+    // s <= 506 for finite values: k0 + 2 <= 17 (the clamp keeps inf / nan in the array)
+    const int k0 = min(s >> 5, kBwdDigits - 3), sh = s & 31;
+    const uint64_t lo = m << sh;            // bits 0..63 of m 2^sh (m 2^sh < 2^79)
+    const uint64_t hi = m >> (32 - sh) >> 32;  // bits 64..78
+    const bool neg = ((ua ^ ub) >> 31) != 0;
+    int64_t c0 = (int64_t)(lo & 0xffffffffull), c1 = (int64_t)(lo >> 32), c2 = (int64_t)hi;
+    if (neg) {
+        c0 = -c0;
+        c1 = -c1;
+        c2 = -c2;
     }
-    if (bits >> 63) m = -m;
-    // k0 <= 15 for every finite product in range; the clamp only keeps
-    // out-of-contract values (inf, nan) inside the array
-    const int k0 = min(shift >> 5, kBwdDigits - 3);
-    const limbs3 l = split_limbs(m, shift & 31);
-    dig[k0][tid] += l.c0;
-    dig[k0 + 1][tid] += l.c1;
-    dig[k0 + 2][tid] += l.c2;
+    unsigned long long *d = (unsigned long long *)&dig[k0][tid];
+    atomicAdd(d, (unsigned long long)c0);
+    atomicAdd(d + 256, (unsigned long long)c1);
+    if (c2) atomicAdd(d + 512, (unsigned long long)c2);
 }
 
 // Exact sums for a 16 x 16 tile of outputs, one thread per output.
@@ -161,7 +169,8 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs A) {
             }
             __syncthreads();
 #pragma unroll 4
-            for (int tt = 0; tt < kBStep; ++tt) bwd_deposit((double)sa[r][tt] * (double)sb[tt][c], dig, tid);
+            for (int tt = 0; tt < kBStep; ++tt)
+                bwd_term(__float_as_uint(sa[r][tt]), __float_as_uint(sb[tt][c]), dig, tid);
         }
         const int64_t i = ia + r, d = da + c;
         if (i < iend && d < A.D) {
@@ -194,7 +203,8 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs A) {
             }
             __syncthreads();
 #pragma unroll 4
-            for (int tt = 0; tt < kBStep; ++tt) bwd_deposit((double)sa[r][tt] * (double)sb[tt][c], dig, tid);
+            for (int tt = 0; tt < kBStep; ++tt)
+                bwd_term(__float_as_uint(sa[r][tt]), __float_as_uint(sb[tt][c]), dig, tid);
         }
     }
     const int64_t j = ja + r, d = da + c;
