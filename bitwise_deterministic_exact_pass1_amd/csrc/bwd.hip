@@ -21,13 +21,25 @@
 // every product is split into three 32-bit limbs added to the digits it
 // spans (no carries until the end: 2^30 limbs of at most 2^32 stay below
 // 2^62), so the result does not depend on the order of the terms.
+//
+// The sums run on the int8 matrix cores where an exactness argument holds
+// (k_bwd_slice, k_bwd_mma below); an output tile outside it keeps the per-term
+// digit sums (k_bwd_sum).  Both give the same bits.
 #include "dev_math.hpp"
 #include "kernels.hpp"
 
 namespace det {
 
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
 constexpr int kBT = 16;         // rows (or keys) and columns of a tile
 constexpr int kBStep = 32;      // reduction steps staged per barrier
+constexpr int kXA = 10;         // matrix-core sums: A digits at most (an 80-bit row span)
+constexpr int kXB = 7;          // B digits at most
+constexpr int kXC = 13;         // digit classes s = a + b; a tile needs na + nb <= kXC + 1
+constexpr int kXCarry = 256;    // 32-step blocks between carries of the classes
+constexpr int64_t kXMaxT = (int64_t)1 << 17;  // reduction length bound of the int32 class sums
 
 struct BwdArgs {
     const void *q, *k, *v;
@@ -45,7 +57,41 @@ struct BwdArgs {
     float *P, *DS;                      // [bh][ni][Skv]
     int64_t *dq_dig;                    // [kBwdDigits][nbh * ni][D]
     int64_t *dk_dig, *dv_dig;           // [kBwdDigits][B * Hkv * Skv][D]
+    // matrix-core sums of the chunk.  Statistics {largest exponent, smallest
+    // lsb exponent} of the nonzero entries: of each ds row over keys, of each
+    // ds / p column over (query head, row), of each column of K over keys and
+    // of Q / dO over (query head, row).
+    int2 *st_rds, *st_cds, *st_cp, *st_k, *st_q, *st_o;
+    v4i *xa[3], *xb[3];   // digit blocks of the A / B operands of dQ, dK, dV
+    int *xf[3];           // per (row tile, column group): 1 = left to k_bwd_sum
+    int64_t nIB, nJB, nG;
+    int force_fallback;
+    OutView dq;
 };
+
+constexpr int64_t kStatEmpty = (int64_t)0x7fffffff80000000ll;  // int2 {INT_MIN, INT_MAX}
+
+// Exponent statistics of one f32 value: its exponent and its lsb exponent
+// (subnormals: -127 and -149); a zero is empty.
+__device__ __forceinline__ void stat_of(float x, int &emax, int &lmin) {
+    const int e = f32_exp(x);
+    emax = x != 0.0f ? e : INT_MIN;
+    lmin = x != 0.0f ? max(e, -126) - 23 : INT_MAX;
+}
+
+// Grid exponent g and balanced base-256 digit count n of a row (or column)
+// with statistics st: every entry is an integer multiple of 2^g, |entry| <
+// 2^(emax + 1), so |entry 2^-g| < 2^(8n - 2) holds n balanced digits.
+__device__ __forceinline__ void grid_of(int2 st, int &g, int &n) {
+    g = st.x == INT_MIN ? 0 : st.y;
+    n = st.x == INT_MIN ? 0 : (st.x + 1 - st.y + 2 + 7) >> 3;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v = max(v, __shfl_xor(v, off, 64));
+    return v;
+}
 
 template <typename T>
 __device__ __forceinline__ float ld(const void *base, int64_t off) {
@@ -90,10 +136,10 @@ __global__ __launch_bounds__(256) void k_bwd_pds(BwdArgs A) {
     }
     __syncthreads();
     const int64_t i = ia + r, j = ja + c;
-    if (i >= iend || j >= A.Skv) return;
+    const bool inr = i < iend && j < A.Skv;
     const int64_t row = bh * A.Sq + i;
     float p = 0.0f, ds = 0.0f;
-    if (!A.causal || j <= i) {
+    if (inr && (!A.causal || j <= i)) {
         const int D = (int)A.D;
         double acc = 0.0;
         for (int d = 0; d < D; ++d) acc = fma((double)sq[r][d], (double)sk[c][d], acc);
@@ -104,9 +150,371 @@ __global__ __launch_bounds__(256) void k_bwd_pds(BwdArgs A) {
         for (int d = 0; d < D; ++d) dp = fma((double)sg[r][d], (double)sv[c][d], dp);
         ds = (float)((double)p * (dp - A.delta[row]));
     }
-    const int64_t at = (bh * A.ni + (i - A.i0)) * A.Skv + j;
-    A.P[at] = p;
-    A.DS[at] = ds;
+    if (inr) {
+        const int64_t at = (bh * A.ni + (i - A.i0)) * A.Skv + j;
+        A.P[at] = p;
+        A.DS[at] = ds;
+    }
+    // exponent statistics for the matrix-core sums: ds per row over this
+    // tile's keys (lanes r*16 + c of a wave share r), ds and p per key over
+    // the wave's four rows; zeros (and pairs out of range) are empty
+    int pe, pl, de, dl;
+    stat_of(p, pe, pl);
+    stat_of(ds, de, dl);
+    int re = de, rl = dl;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        re = max(re, __shfl_xor(re, off, 64));
+        rl = min(rl, __shfl_xor(rl, off, 64));
+    }
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
+        de = max(de, __shfl_xor(de, off, 64));
+        dl = min(dl, __shfl_xor(dl, off, 64));
+        pe = max(pe, __shfl_xor(pe, off, 64));
+        pl = min(pl, __shfl_xor(pl, off, 64));
+    }
+    if (c == 0 && i < iend && re != INT_MIN) {
+        int2 *st = A.st_rds + bh * A.ni + (i - A.i0);
+        atomicMax(&st->x, re);
+        atomicMin(&st->y, rl);
+    }
+    if ((tid & 63) < 16 && j < A.Skv) {
+        const int64_t at = (b * A.Hkv + hk) * A.Skv + j;
+        if (de != INT_MIN) {
+            atomicMax(&A.st_cds[at].x, de);
+            atomicMin(&A.st_cds[at].y, dl);
+        }
+        if (pe != INT_MIN) {
+            atomicMax(&A.st_cp[at].x, pe);
+            atomicMin(&A.st_cp[at].y, pl);
+        }
+    }
+}
+
+// Column statistics of a B operand over rows [s0, s1) of the heads h = hk *
+// ng + g, g < ng, of a [B, H, S, D] view (K: ng = 1 and all keys; Q and dO:
+// ng = the group and the chunk's rows), into st[bhk * D + d].  Grid (column
+// groups of 32, row blocks of 256, bhk * ng).
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_colstats(const void *src, int64_t sB, int64_t sH, int64_t sS,
+                                                      int64_t ng, int64_t Hkv, int64_t s0, int64_t s1, int64_t D,
+                                                      int2 *st) {
+    __shared__ int se[8][32], sl[8][32];
+    const int t = threadIdx.x, c = t & 31, s8 = t >> 5;
+    const int64_t z = blockIdx.z, bhk = z / ng, g = z % ng;
+    const int64_t b = bhk / Hkv, hk = bhk % Hkv, h = hk * ng + g;
+    const int64_t d = (int64_t)blockIdx.x * 32 + c;
+    const int64_t r0 = s0 + (int64_t)blockIdx.y * 256, r1 = min64(s1, r0 + 256);
+    int emax = INT_MIN, lmin = INT_MAX;
+    if (d < D) {
+        const T *col = (const T *)src + b * sB + h * sH + d;
+#pragma unroll 4
+        for (int64_t s = r0 + s8; s < r1; s += 8) {
+            int e, l;
+            stat_of(elem<T>::to_f32(col[s * sS]), e, l);
+            emax = max(emax, e);
+            lmin = min(lmin, l);
+        }
+    }
+    se[s8][c] = emax;
+    sl[s8][c] = lmin;
+    __syncthreads();
+    if (t >= 32) return;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+        emax = max(emax, se[k][c]);
+        lmin = min(lmin, sl[k][c]);
+    }
+    if (d < D && emax != INT_MIN) {
+        atomicMax(&st[bhk * D + d].x, emax);
+        atomicMin(&st[bhk * D + d].y, lmin);
+    }
+}
+
+// Digit blocks of the matrix-core sums, one wave per block of 32 operand rows
+// x (here "row" x is the index that survives the sum: a ds / p row or column,
+// or a column d of K, Q, dO) by 32 reduction steps t.  Lane l holds row x =
+// l % 32 at steps 16 (l / 32) + 0..15, the int8 operand order of
+// v_mfma_i32_32x32x32_i8.  Each row is an integer on its grid, Xi = X 2^-g_x,
+// written as n balanced base-256 digits (n of the block = the largest of its
+// rows): the bytes of Xi + 0x80..80 with their top bit flipped.  Blocks whose
+// rows need more digits than the kernel holds are not written (their tiles
+// take the per-term sums), nor are causal blocks that no sum reads.
+//   MODE 0: A of dQ, unit (bh, row tile, key block): ds[i][j]
+//   MODE 1, 2: A of dK, dV, unit (bhk, key tile, query head g, row block): ds / p [i][j], x = j
+//   MODE 3: B of dQ, unit (bhk, column group, key block): K[j][d], x = d
+//   MODE 4, 5: B of dK, dV, unit (bhk, column group, g, row block): Q / dO [i][d], x = d
+template <int MODE, typename T>
+__global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
+    const int lane = threadIdx.x & 63;
+    const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (u >= nunits) return;  // wave-uniform
+    const int xr = lane & 31, tb = 16 * (lane >> 5);
+    float val[16];
+    int2 st = int2{INT_MIN, INT_MAX};
+    int kmax;
+    v4i *out;
+    if (MODE == 0) {
+        const int64_t jb = u % A.nJB, it = (u / A.nJB) % A.nIB, bh = u / (A.nJB * A.nIB);
+        if (A.causal && jb * 32 > A.i0 + it * 32 + 31) return;
+        const int64_t ir = it * 32 + xr, i = A.i0 + ir;
+        if (ir < A.ni) st = A.st_rds[bh * A.ni + ir];
+        const float *src = A.DS + (bh * A.ni + (ir < A.ni ? ir : 0)) * A.Skv;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int64_t j = jb * 32 + tb + p;
+            val[p] = (ir < A.ni && j < A.Skv && (!A.causal || j <= i)) ? src[j] : 0.0f;
+        }
+        kmax = kXA;
+        out = A.xa[0] + u * kXA * 64;
+    } else if (MODE == 1 || MODE == 2) {
+        const int64_t ib = u % A.nIB, g = (u / A.nIB) % A.group, jt = (u / (A.nIB * A.group)) % A.nJB,
+                      bhk = u / (A.nIB * A.group * A.nJB);
+        if (A.causal && A.i0 + ib * 32 + 31 < jt * 32) return;
+        const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, bh = b * A.Hq + hk * A.group + g;
+        const int64_t j = jt * 32 + xr;
+        if (j < A.Skv) st = (MODE == 1 ? A.st_cds : A.st_cp)[bhk * A.Skv + j];
+        const float *src = (MODE == 1 ? A.DS : A.P) + bh * A.ni * A.Skv + (j < A.Skv ? j : 0);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int64_t ir = ib * 32 + tb + p;
+            val[p] = (j < A.Skv && ir < A.ni && (!A.causal || j <= A.i0 + ir)) ? src[ir * A.Skv] : 0.0f;
+        }
+        kmax = kXA;
+        out = A.xa[MODE] + u * kXA * 64;
+    } else if (MODE == 3) {
+        const int64_t jb = u % A.nJB, G = (u / A.nJB) % A.nG, bhk = u / (A.nJB * A.nG);
+        const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, d = G * 32 + xr;
+        if (d < A.D) st = A.st_k[bhk * A.D + d];
+        const int64_t base = b * A.ksB + hk * A.ksH + (d < A.D ? d : 0);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int64_t j = jb * 32 + tb + p;
+            val[p] = (d < A.D && j < A.Skv) ? ld<T>(A.k, base + j * A.ksS) : 0.0f;
+        }
+        kmax = kXB;
+        out = A.xb[0] + u * kXB * 64;
+    } else {
+        const int64_t ib = u % A.nIB, g = (u / A.nIB) % A.group, G = (u / (A.nIB * A.group)) % A.nG,
+                      bhk = u / (A.nIB * A.group * A.nG);
+        const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, hq = hk * A.group + g, d = G * 32 + xr;
+        if (d < A.D) st = (MODE == 4 ? A.st_q : A.st_o)[bhk * A.D + d];
+        const int64_t dd = d < A.D ? d : 0;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const int64_t ir = ib * 32 + tb + p, i = A.i0 + (ir < A.ni ? ir : 0);
+            float x = 0.0f;
+            if (d < A.D && ir < A.ni) {
+                if (MODE == 4) x = ld<T>(A.q, b * A.qsB + hq * A.qsH + i * A.qsS + dd);
+                else x = A.dout[b * A.dsB + hq * A.dsH + i * A.dsS + dd];
+            }
+            val[p] = x;
+        }
+        kmax = kXB;
+        out = A.xb[MODE - 3] + u * kXB * 64;
+    }
+    int g, n;
+    grid_of(st, g, n);
+    const int nt = __builtin_amdgcn_readfirstlane(wave_max(n));
+    if (nt == 0 || nt > kmax) return;
+    // Xi + 0x80..80 (nt bytes) for the 16 values, as 128-bit integers
+    unsigned __int128 off = 0;
+    for (int a = 0; a < nt; ++a) off = (off << 8) | 0x80u;
+    unsigned __int128 U[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+        const uint32_t bits = __float_as_uint(val[p]);
+        const uint32_t be = (bits >> 23) & 0xffu;
+        const uint64_t m = (bits & 0x7fffffu) | (be ? 0x800000u : 0u);
+        const int sh = (int)(be ? be : 1u) - 150 - g;  // >= 0 for every nonzero entry of the row
+        const unsigned __int128 mag = m ? ((unsigned __int128)m << (sh & 127)) : 0;
+        U[p] = ((bits >> 31) ? off - mag : off + mag);
+    }
+    for (int a = 0; a < nt; ++a) {
+        uint32_t wv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t pack = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pack |= ((uint32_t)(U[4 * q + e] >> (8 * a)) & 255u) << (8 * e);
+            wv[q] = pack ^ 0x80808080u;
+        }
+        out[a * 64 + lane] = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+    }
+}
+
+// The matrix-core sums of one 32 x 32 output tile per wave (four column
+// groups per workgroup): C_s += A_a x B_b (s = a + b) over the reduction
+// blocks on v_mfma_i32_32x32x32_i8, exact in int32 (|a_a b_b| <= 2^14, at most
+// seven pairs per class and step, classes carried every kXCarry blocks; the
+// top class only ever holds the product of the two top digits, each at most
+// 2^6), then the exact sum X = sum_s 256^s C_s (|X| < 2^125) times
+// 2^(ga_x + gb_d):
+//   MODE 0 (dQ): grid (column groups / 4, row tiles, bh); the tile owns every
+//     key, so dQ = RN32(RN64(scale RN64(X 2^e))) is stored directly;
+//   MODE 1, 2 (dK, dV): grid (column groups / 4, key tiles, bhk * group); the
+//     workgroup covers one query head's rows of the chunk and adds X 2^e into
+//     the digit planes (integer atomics: any order gives the same digits).
+// The A digits of a block are common to the four waves and staged through
+// LDS (double buffered, one barrier per block); each wave keeps its column
+// group's B digits in registers, fetched one block ahead.  A tile whose rows
+// or columns need more digits than the kernel holds is flagged for k_bwd_sum
+// and left alone here.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
+    __shared__ v4i sA[2][kXA][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int64_t G = (int64_t)blockIdx.x * 4 + (tid >> 6);
+    const int x = lane & 31;
+    const int64_t y = blockIdx.y, z = blockIdx.z;
+    const int64_t d = G * 32 + x;
+    int2 sa = int2{INT_MIN, INT_MAX}, sb = int2{INT_MIN, INT_MAX};
+    int64_t bh = 0, bhk, g = 0, nblk, k0;
+    const v4i *pa, *pb;
+    int *flag;
+    if (MODE == 0) {
+        bh = z;
+        const int64_t b = bh / A.Hq, hk = (bh % A.Hq) / A.group, ir = y * 32 + x;
+        bhk = b * A.Hkv + hk;
+        if (ir < A.ni) sa = A.st_rds[bh * A.ni + ir];
+        k0 = 0;
+        nblk = A.causal ? min64(A.nJB, (A.i0 + y * 32 + 31) / 32 + 1) : A.nJB;
+        pa = A.xa[0] + (bh * A.nIB + y) * A.nJB * kXA * 64;
+        pb = A.xb[0] + (bhk * A.nG + G) * A.nJB * kXB * 64;
+        flag = A.xf[0] + (bh * A.nIB + y) * A.nG + G;
+    } else {
+        bhk = z / A.group;
+        g = z % A.group;
+        const int64_t j = y * 32 + x;
+        if (j < A.Skv) sa = (MODE == 1 ? A.st_cds : A.st_cp)[bhk * A.Skv + j];
+        k0 = (A.causal && y * 32 > A.i0) ? (y * 32 - A.i0) / 32 : 0;
+        nblk = A.nIB;
+        pa = A.xa[MODE] + ((bhk * A.nJB + y) * A.group + g) * A.nIB * kXA * 64;
+        pb = A.xb[MODE] + ((bhk * A.nG + G) * A.group + g) * A.nIB * kXB * 64;
+        flag = A.xf[MODE] + (bhk * A.nJB + y) * A.nG + G;
+    }
+    const bool mine = G < A.nG;  // wave-uniform: the wave has a column group
+    if (mine && d < A.D) sb = (MODE == 0 ? A.st_k : MODE == 1 ? A.st_q : A.st_o)[bhk * A.D + d];
+    int ga, na, gb, nb;
+    grid_of(sa, ga, na);
+    grid_of(sb, gb, nb);
+    const int nat = __builtin_amdgcn_readfirstlane(wave_max(na));  // the same in every wave
+    const int nbt = __builtin_amdgcn_readfirstlane(wave_max(nb));
+    const bool abad = A.force_fallback || nat > kXA || (MODE == 0 ? A.Skv : A.ni) > kXMaxT;
+    const bool bad = abad || nbt > kXB || nat + nbt > kXC + 1;
+    if (mine && (MODE == 0 || g == 0) && lane == 0) *flag = bad ? 1 : 0;
+    if (abad) return;  // workgroup-uniform
+    const bool run = mine && !bad && nbt > 0;  // wave-uniform
+    if (nat == 0) nblk = k0;                   // a zero operand: X = 0
+
+    v16i C[kXC];
+#pragma unroll
+    for (int s = 0; s < kXC; ++s) C[s] = v16i{0};
+    // the block's A digits: nat * 64 v4i, at most three per thread
+    v4i st[3];
+    auto fetch_a = [&](int64_t kb) {
+        const v4i *q = pa + kb * kXA * 64;
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+            if (tid + 256 * u < nat * 64) st[u] = q[tid + 256 * u];
+    };
+    auto stash_a = [&](int buf) {
+        v4i *s = &sA[buf][0][0];
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+            if (tid + 256 * u < nat * 64) s[tid + 256 * u] = st[u];
+    };
+    v4i B0[kXB], B1[kXB];
+    auto fetch_b = [&](int64_t kb, v4i (&Br)[kXB]) {
+        if (!run) return;
+        const v4i *q = pb + kb * kXB * 64 + lane;
+#pragma unroll
+        for (int b = 0; b < kXB; ++b)
+            if (b < nbt) Br[b] = q[b * 64];
+    };
+    auto step = [&](int64_t kb, const v4i (&Bc)[kXB], v4i (&Bn)[kXB]) {
+        const int buf = (int)((kb - k0) & 1);
+        const bool more = kb + 1 < nblk;
+        if (more) {
+            fetch_a(kb + 1);
+            fetch_b(kb + 1, Bn);
+        }
+        if (run) {
+            const v4i *sa_ = &sA[buf][0][lane];
+            v4i Acur = sa_[0];
+#pragma unroll
+            for (int a = 0; a < kXA; ++a) {
+                if (a < nat) {
+                    const v4i Anext = sa_[((a + 1) % kXA) * 64];  // digit a+1 read while a's products run
+#pragma unroll
+                    for (int b = 0; b < kXB; ++b)
+                        if (a + b < kXC && b < nbt)
+                            C[a + b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Acur, Bc[b], C[a + b], 0, 0, 0);
+                    Acur = Anext;
+                }
+            }
+            if (((kb - k0) % kXCarry) == kXCarry - 1) {
+#pragma unroll
+                for (int s = 0; s < kXC - 1; ++s) {
+                    const v16i c = C[s] >> 8;
+                    C[s] -= c << 8;
+                    C[s + 1] += c;
+                }
+            }
+        }
+        if (more) stash_a(buf ^ 1);  // its readers passed the previous barrier
+        __syncthreads();
+    };
+    if (k0 < nblk) {
+        fetch_a(k0);
+        fetch_b(k0, B0);
+        stash_a(0);
+    }
+    __syncthreads();
+    for (int64_t kb = k0; kb < nblk; kb += 2) {
+        step(kb, B0, B1);
+        if (kb + 1 < nblk) step(kb + 1, B1, B0);
+    }
+    if (!mine || bad) return;
+    // classes to bytes: C_0 .. C_11 in [0, 256), C_12 signed
+#pragma unroll
+    for (int s = 0; s < kXC - 1; ++s) {
+        const v16i c = C[s] >> 8;
+        C[s] &= 255;
+        C[s + 1] += c;
+    }
+    int gam[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) gam[rr] = __shfl(ga, 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3), 64);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+        const int m = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+        const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) | ((uint32_t)C[2][rr] << 16) |
+                            ((uint32_t)C[3][rr] << 24);
+        const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) | ((uint32_t)C[6][rr] << 16) |
+                            ((uint32_t)C[7][rr] << 24);
+        const uint32_t l2 = (uint32_t)C[8][rr] | ((uint32_t)C[9][rr] << 8) | ((uint32_t)C[10][rr] << 16) |
+                            ((uint32_t)C[11][rr] << 24);
+        const uint64_t lo = ((uint64_t)l1 << 32) | l0;
+        const int64_t hi = (int64_t)C[12][rr] * ((int64_t)1 << 32) + (int64_t)l2;
+        const int e = gam[rr] + gb;
+        if (d >= A.D) continue;
+        if (MODE == 0) {
+            const int64_t ir = y * 32 + m;
+            if (ir >= A.ni) continue;
+            const int64_t b = bh / A.Hq, hq = bh % A.Hq;
+            const double v = i128_to_f64(hi, lo, e);
+            A.dq.data[b * A.dq.sB + hq * A.dq.sH + (A.i0 + ir) * A.dq.sS + d] = (float)(A.scale * v);
+        } else {
+            const int64_t j = y * 32 + m;
+            if (j >= A.Skv) continue;
+            const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
+            int64_t *dig = MODE == 1 ? A.dk_dig : A.dv_dig;
+            const int64_t plane = A.nbh / A.group * A.Skv * A.D;
+            add_i128_digits<kBwdDigits>(num, e - kBwdElo, dig + (bhk * A.Skv + j) * A.D + d, plane);
+        }
+    }
 }
 
 // Adds the exact product of the f32 values with bit patterns ua and ub into
@@ -150,6 +558,10 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs A) {
     __shared__ float sa[kBT][kBStep + 1], sb[kBStep][kBT + 1];
     const int tid = threadIdx.x, r = tid >> 4, c = tid & 15;
     const int64_t da = (int64_t)blockIdx.x * kBT, ra = (int64_t)blockIdx.y * kBT, hh = blockIdx.z;
+    // only the tiles the matrix-core sums left (flag 1); ra is a chunk row (dQ) or a key
+    const int tf = MODE == 0 ? A.xf[0][(hh * A.nIB + ra / 32) * A.nG + da / 32]
+                             : A.xf[MODE][(hh * A.nJB + ra / 32) * A.nG + da / 32];
+    if (!tf) return;
 #pragma unroll
     for (int k = 0; k < kBwdDigits; ++k) dig[k][tid] = 0;
     const int64_t iend = A.i0 + A.ni;
@@ -218,11 +630,15 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs A) {
 
 // out = RN32(RN64(f * RN64(X))) of each digit sum X (f = scale or 1); row R
 // of the planes is (head, s) = (R / S, R % S) of the output view.
+// With flags (dQ), only outputs of the tiles left to k_bwd_sum: flag of
+// (head, row tile, column group) at flags[(head * nIB + s / 32) * nG + d / 32].
 __global__ __launch_bounds__(256) void k_bwd_finalize(const int64_t *dig, int64_t rows, int64_t D, int64_t S,
-                                                      int64_t s_off, int64_t H, double f, OutView o) {
+                                                      int64_t s_off, int64_t H, double f, OutView o,
+                                                      const int *flags, int64_t nIB, int64_t nG) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= rows * D) return;
     const int64_t R = t / D, d = t % D;
+    if (flags && !flags[((R / S) * nIB + (R % S) / 32) * nG + d / 32]) return;
     int64_t x[kBwdDigits];
 #pragma unroll
     for (int k = 0; k < kBwdDigits; ++k) x[k] = dig[k * rows * D + t];
@@ -247,10 +663,56 @@ size_t bwd_fixed_bytes(const AttnGeom &g) {
     return align256((size_t)g.B * g.Hq * g.Sq * 8) + 2 * align256((size_t)kBwdDigits * g.B * g.Hkv * g.Skv * g.D * 8);
 }
 
-size_t bwd_chunk_bytes(const AttnGeom &g, int64_t ni) {
-    const int64_t bh = g.B * g.Hq;
-    return 2 * align256((size_t)bh * ni * g.Skv * 4) + align256((size_t)kBwdDigits * bh * ni * g.D * 8);
+// The chunk workspace of ni query rows, carved in one place: returns its size
+// and, with A, points A's chunk arrays into base.
+static size_t bwd_chunk_layout(const AttnGeom &g, int64_t ni, BwdArgs *A, char *base) {
+    const int64_t bh = g.B * g.Hq, bhk = g.B * g.Hkv, grp = g.Hq / g.Hkv;
+    const int64_t nIB = (ni + 31) / 32, nJB = (g.Skv + 31) / 32, nG = (g.D + 31) / 32;
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        char *p = base ? base + at : nullptr;
+        at += align256(bytes);
+        return p;
+    };
+    char *P = take((size_t)bh * ni * g.Skv * 4);
+    char *DS = take((size_t)bh * ni * g.Skv * 4);
+    char *dqd = take((size_t)kBwdDigits * bh * ni * g.D * 8);
+    char *st = take((size_t)(bh * ni + 2 * bhk * g.Skv + 3 * bhk * g.D) * 8);
+    char *xa0 = take((size_t)kXA * 1024 * bh * nIB * nJB);
+    char *xa1 = take((size_t)kXA * 1024 * bhk * nJB * grp * nIB);
+    char *xa2 = take((size_t)kXA * 1024 * bhk * nJB * grp * nIB);
+    char *xb0 = take((size_t)kXB * 1024 * bhk * nG * nJB);
+    char *xb1 = take((size_t)kXB * 1024 * bhk * nG * grp * nIB);
+    char *xb2 = take((size_t)kXB * 1024 * bhk * nG * grp * nIB);
+    char *fl = take((size_t)(bh * nIB * nG + 2 * bhk * nJB * nG) * 4);
+    if (A) {
+        A->P = (float *)P;
+        A->DS = (float *)DS;
+        A->dq_dig = (int64_t *)dqd;
+        int2 *s2 = (int2 *)st;
+        A->st_rds = s2;
+        A->st_cds = s2 + bh * ni;
+        A->st_cp = A->st_cds + bhk * g.Skv;
+        A->st_k = A->st_cp + bhk * g.Skv;
+        A->st_q = A->st_k + bhk * g.D;
+        A->st_o = A->st_q + bhk * g.D;
+        A->xa[0] = (v4i *)xa0;
+        A->xa[1] = (v4i *)xa1;
+        A->xa[2] = (v4i *)xa2;
+        A->xb[0] = (v4i *)xb0;
+        A->xb[1] = (v4i *)xb1;
+        A->xb[2] = (v4i *)xb2;
+        A->xf[0] = (int *)fl;
+        A->xf[1] = A->xf[0] + bh * nIB * nG;
+        A->xf[2] = A->xf[1] + bhk * nJB * nG;
+        A->nIB = nIB;
+        A->nJB = nJB;
+        A->nG = nG;
+    }
+    return at;
 }
+
+size_t bwd_chunk_bytes(const AttnGeom &g, int64_t ni) { return bwd_chunk_layout(g, ni, nullptr, nullptr); }
 
 hipError_t launch_zero_view(const OutView &o, int64_t B, int64_t H, int64_t S, int64_t D, hipStream_t s) {
     const int64_t n = B * H * S * D;
@@ -259,10 +721,56 @@ hipError_t launch_zero_view(const OutView &o, int64_t B, int64_t H, int64_t S, i
     return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_sums(BwdArgs &A, const AttnGeom &g, const Tensor &q, const Tensor &k, const Tensor &dout,
+                              hipStream_t s) {
+    const int64_t bh = g.B * g.Hq, bhk = g.B * g.Hkv, grp = A.group;
+    const int64_t nIB = A.nIB, nJB = A.nJB, nG = A.nG;
+    {
+        ProfScope prof_("bwd_slice", s);
+        const dim3 gk((unsigned)nG, (unsigned)((g.Skv + 255) / 256), (unsigned)bhk);
+        const dim3 gq((unsigned)nG, (unsigned)((A.ni + 255) / 256), (unsigned)(bhk * grp));
+        hipLaunchKernelGGL(k_bwd_colstats<T>, gk, dim3(256), 0, s, k.data, k.sB, k.sH, k.sS, (int64_t)1, g.Hkv,
+                           (int64_t)0, g.Skv, g.D, A.st_k);
+        hipLaunchKernelGGL(k_bwd_colstats<T>, gq, dim3(256), 0, s, q.data, q.sB, q.sH, q.sS, grp, g.Hkv, A.i0,
+                           A.i0 + A.ni, g.D, A.st_q);
+        hipLaunchKernelGGL(k_bwd_colstats<float>, gq, dim3(256), 0, s, dout.data, dout.sB, dout.sH, dout.sS, grp,
+                           g.Hkv, A.i0, A.i0 + A.ni, g.D, A.st_o);
+        const int64_t u0 = bh * nIB * nJB, u1 = bhk * nJB * grp * nIB, u3 = bhk * nG * nJB, u4 = bhk * nG * grp * nIB;
+        hipLaunchKernelGGL((k_bwd_slice<0, T>), dim3(blocks_of(u0 * 64)), dim3(256), 0, s, A, u0);
+        hipLaunchKernelGGL((k_bwd_slice<1, T>), dim3(blocks_of(u1 * 64)), dim3(256), 0, s, A, u1);
+        hipLaunchKernelGGL((k_bwd_slice<2, T>), dim3(blocks_of(u1 * 64)), dim3(256), 0, s, A, u1);
+        hipLaunchKernelGGL((k_bwd_slice<3, T>), dim3(blocks_of(u3 * 64)), dim3(256), 0, s, A, u3);
+        hipLaunchKernelGGL((k_bwd_slice<4, T>), dim3(blocks_of(u4 * 64)), dim3(256), 0, s, A, u4);
+        hipLaunchKernelGGL((k_bwd_slice<5, T>), dim3(blocks_of(u4 * 64)), dim3(256), 0, s, A, u4);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        ProfScope prof_("bwd_mma", s);
+        const unsigned gx = (unsigned)((nG + 3) / 4);
+        hipLaunchKernelGGL(k_bwd_mma<0>, dim3(gx, (unsigned)nIB, (unsigned)bh), dim3(256), 0, s, A);
+        hipLaunchKernelGGL(k_bwd_mma<1>, dim3(gx, (unsigned)nJB, (unsigned)(bhk * grp)), dim3(256), 0, s, A);
+        hipLaunchKernelGGL(k_bwd_mma<2>, dim3(gx, (unsigned)nJB, (unsigned)(bhk * grp)), dim3(256), 0, s, A);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        ProfScope prof_("bwd_sum", s);
+        const unsigned cols = (unsigned)((g.D + kBT - 1) / kBT);
+        const dim3 gq(cols, (unsigned)((A.ni + kBT - 1) / kBT), (unsigned)bh);
+        const dim3 gk(cols, (unsigned)((g.Skv + kBT - 1) / kBT), (unsigned)bhk);
+        hipLaunchKernelGGL((k_bwd_sum<0, T>), gq, dim3(256), 0, s, A);
+        hipLaunchKernelGGL((k_bwd_sum<1, T>), gk, dim3(256), 0, s, A);
+        hipLaunchKernelGGL((k_bwd_sum<2, T>), gk, dim3(256), 0, s, A);
+        return hipGetLastError();
+    }
+}
+
 hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &v, const Tensor &o,
                                 const Tensor &dout, const float *rowmax, const double *den64, const AttnGeom &g,
                                 void *fixed_ws, void *chunk_ws, int64_t chunk, const OutView &dq,
-                                const OutView &dk, const OutView &dv, hipStream_t s) {
+                                const OutView &dk, const OutView &dv, int force_fallback, hipStream_t s) {
     const int64_t bh = g.B * g.Hq, bhk = g.B * g.Hkv, rows = bh * g.Sq;
     if (bh > 65535 || bhk > 65535 || (chunk + kBT - 1) / kBT > 65535 || (g.Skv + kBT - 1) / kBT > 65535)
         return hipErrorInvalidValue;  // grid y / z limits
@@ -288,16 +796,15 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
     A.causal = g.causal;
     A.scale = g.scale;
     A.nbh = bh;
+    A.force_fallback = force_fallback;
+    A.dq = dq;
     char *f = (char *)fixed_ws;
     A.delta = (double *)f;
     f += align256((size_t)rows * 8);
     const size_t kvdig = align256((size_t)kBwdDigits * bhk * g.Skv * g.D * 8);
     A.dk_dig = (int64_t *)f;
     A.dv_dig = (int64_t *)(f + kvdig);
-    char *c = (char *)chunk_ws;
-    A.P = (float *)c;
-    A.DS = (float *)(c + align256((size_t)bh * chunk * g.Skv * 4));
-    A.dq_dig = (int64_t *)(c + 2 * align256((size_t)bh * chunk * g.Skv * 4));
+    bwd_chunk_layout(g, chunk, &A, (char *)chunk_ws);
     hipError_t e;
     const int64_t kvn = kBwdDigits * bhk * g.Skv * g.D;
     if ((e = launch_fill_i64(A.dk_dig, kvn, 0, s)) != hipSuccess) return e;
@@ -308,11 +815,13 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const bool bf = q.dtype == 1;
-    const dim3 cols((unsigned)((g.D + kBT - 1) / kBT));
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         A.i0 = i0;
         A.ni = std::min(chunk, g.Sq - i0);
+        A.nIB = (A.ni + 31) / 32;  // the chunk's row blocks (the layout is carved for the largest chunk)
         const int64_t rt = (A.ni + kBT - 1) / kBT;
+        const int64_t nst = bh * chunk + 2 * bhk * g.Skv + 3 * bhk * g.D;  // the carved statistics
+        if ((e = launch_fill_i64((int64_t *)A.st_rds, nst, kStatEmpty, s)) != hipSuccess) return e;
         {
             ProfScope prof_("bwd_pds", s);
             dim3 grid((unsigned)((g.Skv + kBT - 1) / kBT), (unsigned)rt, (unsigned)bh);
@@ -320,34 +829,22 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
             else hipLaunchKernelGGL(k_bwd_pds<float>, grid, dim3(256), 0, s, A);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        {
-            ProfScope prof_("bwd_sum", s);
-            dim3 gq(cols.x, (unsigned)rt, (unsigned)bh), gk(cols.x, (unsigned)((g.Skv + kBT - 1) / kBT), (unsigned)bhk);
-            if (bf) {
-                hipLaunchKernelGGL((k_bwd_sum<0, bf16_t>), gq, dim3(256), 0, s, A);
-                hipLaunchKernelGGL((k_bwd_sum<1, bf16_t>), gk, dim3(256), 0, s, A);
-                hipLaunchKernelGGL((k_bwd_sum<2, bf16_t>), gk, dim3(256), 0, s, A);
-            } else {
-                hipLaunchKernelGGL((k_bwd_sum<0, float>), gq, dim3(256), 0, s, A);
-                hipLaunchKernelGGL((k_bwd_sum<1, float>), gk, dim3(256), 0, s, A);
-                hipLaunchKernelGGL((k_bwd_sum<2, float>), gk, dim3(256), 0, s, A);
-            }
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
+        e = bf ? launch_sums<bf16_t>(A, g, q, k, dout, s) : launch_sums<float>(A, g, q, k, dout, s);
+        if (e != hipSuccess) return e;
         {
             ProfScope prof_("bwd_finalize", s);
             const int64_t n = bh * A.ni;  // rows (head, i) of the chunk, i from i0
             hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(n * g.D)), dim3(256), 0, s, A.dq_dig, n, g.D, A.ni,
-                               i0, g.Hq, g.scale, dq);
+                               i0, g.Hq, g.scale, dq, (const int *)A.xf[0], A.nIB, A.nG);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
     ProfScope prof_("bwd_finalize", s);
     const int64_t nk = bhk * g.Skv;
     hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(nk * g.D)), dim3(256), 0, s, A.dk_dig, nk, g.D, g.Skv,
-                       (int64_t)0, g.Hkv, g.scale, dk);
+                       (int64_t)0, g.Hkv, g.scale, dk, (const int *)nullptr, (int64_t)0, (int64_t)1);
     hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(nk * g.D)), dim3(256), 0, s, A.dv_dig, nk, g.D, g.Skv,
-                       (int64_t)0, g.Hkv, 1.0, dv);
+                       (int64_t)0, g.Hkv, 1.0, dv, (const int *)nullptr, (int64_t)0, (int64_t)1);
     return hipGetLastError();
 }
 

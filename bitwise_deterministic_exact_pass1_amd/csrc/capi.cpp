@@ -518,7 +518,7 @@ int det_attn_backward(const det_tensor *q, const det_tensor *k, const det_tensor
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
     HIP_TRY(launch_attn_backward(to_t(q), to_t(k), to_t(v), to_t(o), to_t(dout), rowmax, den64, g, fixed, cws, chunk,
                                  OutView{dq->data, dq->sB, dq->sH, dq->sS}, OutView{dk->data, dk->sB, dk->sH, dk->sS},
-                                 OutView{dv->data, dv->sB, dv->sH, dv->sS}, s),
+                                 OutView{dv->data, dv->sB, dv->sH, dv->sS}, force_fallback(), s),
             "backward");
     return ok();
 }

@@ -331,4 +331,54 @@ struct Window {
 constexpr int kNumGcap = 32 * (kNumDigits - 2) + 31 + kNumElo;
 constexpr int kDenGcap = 32 * (kDenDigits - 2) + 31 + kDenElo;
 
+// ---------------------------------------------------------------- exact int128 helpers
+
+__device__ __forceinline__ int clz128(unsigned __int128 u) {
+    const uint64_t hi = (uint64_t)(u >> 64), lo = (uint64_t)u;
+    return hi ? __clzll((long long)hi) : 64 + __clzll((long long)lo);
+}
+
+// Correctly rounded (ties to even) binary64 of N * 2^e for the 128-bit
+// integer N = hi * 2^64 + lo (hi signed, lo unsigned); N * 2^e must lie in
+// the normal range.  The top 64 bits of |N| are rounded by the (correctly
+// rounded) uint64 conversion, with every lower bit folded into bit 0 as a
+// sticky bit: bit 0 lies below the rounding position of a 64-bit value.
+__device__ __forceinline__ double i128_to_f64(int64_t hi, uint64_t lo, int e) {
+    // straight-line (selects only), so that a lane's conversions interleave
+    const bool neg = hi < 0;
+    const unsigned __int128 n = ((unsigned __int128)(uint64_t)hi << 64) | lo;
+    const unsigned __int128 u = neg ? (unsigned __int128)0 - n : n;  // |N|
+    const uint64_t uh = (uint64_t)(u >> 64), ul = (uint64_t)u;
+    const int lz = uh ? __builtin_clzll(uh) : 64 + (ul ? __builtin_clzll(ul) : 64);
+    const int s = max(64 - lz, 0);  // bits of |N| above the low 64: shift them out into the sticky bit
+    const unsigned __int128 below = s ? (((unsigned __int128)1 << s) - 1) : 0;
+    const uint64_t top = (uint64_t)(u >> s) | ((u & below) != 0 ? 1ull : 0ull);
+    const double r = ldexp((double)top, e + s);
+    return neg ? -r : r;
+}
+
+// Add x * 2^pos (pos >= 0, in units of the digit lsb) to K radix-2^32 digits.
+template <int K>
+__device__ __forceinline__ void add_i128_digits(__int128 x, int pos, int64_t *dg, int64_t plane) {
+    if (x == 0) return;
+    const bool neg = x < 0;
+    unsigned __int128 u = neg ? (unsigned __int128)(-x) : (unsigned __int128)x;
+    int k = pos >> 5;
+    const int sh = pos & 31;
+    // u * 2^sh < 2^(128+31): emit limbs of (u << sh) without losing the top bits
+    const uint64_t top = sh ? (uint64_t)(u >> (128 - sh)) : 0;  // bits above 128 after the shift
+    u <<= sh;
+    unsigned long long *d = (unsigned long long *)dg;
+    for (int t = 0; t < 5; ++t, ++k) {
+        int64_t limb = t < 4 ? (int64_t)(uint32_t)(u >> (32 * t)) : (int64_t)top;
+        if (!limb) continue;
+        if (neg) limb = -limb;
+        if (k < K) {
+            atomicAdd(d + (int64_t)k * plane, (unsigned long long)limb);
+        } else {  // fold into the signed top digit (only reached by values near the format's ceiling)
+            atomicAdd(d + (int64_t)(K - 1) * plane, (unsigned long long)(limb << (32 * (k - (K - 1)))));
+        }
+    }
+}
+
 }  // namespace det

@@ -93,7 +93,7 @@ hipError_t launch_zero_view(const OutView &o, int64_t B, int64_t H, int64_t S, i
 hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &v, const Tensor &o,
                                 const Tensor &dout, const float *rowmax, const double *den64, const AttnGeom &g,
                                 void *fixed_ws, void *chunk_ws, int64_t chunk, const OutView &dq,
-                                const OutView &dk, const OutView &dv, hipStream_t s);
+                                const OutView &dk, const OutView &dv, int force_fallback, hipStream_t s);
 
 // Capacity of the remainder list of one V preparation (entries of all heads);
 // heads whose remainders do not fit take the generic exact path.

@@ -152,3 +152,52 @@ def test_backward_small_workspace_row_chunks(A):
                                    A._stream(Q)))
     for a, b in zip(g, ref):
         assert torch.equal(a, b)
+
+
+def _backward_both_paths(A, q, k, v, dO, causal, scale):
+    """The gradients with the matrix-core sums, then with every tile forced
+    onto the per-term digit sums (DET_FORCE_FALLBACK is read on each call)."""
+    import os
+    fast = gpu_backward(A, q, k, v, dO, causal, scale)
+    os.environ["DET_FORCE_FALLBACK"] = "1"
+    try:
+        slow = gpu_backward(A, q, k, v, dO, causal, scale)
+    finally:
+        os.environ.pop("DET_FORCE_FALLBACK", None)
+    return fast, slow
+
+
+@pytest.mark.parametrize("shape", [
+    (920, 2, 8, 2, 200, 200, 128, torch.bfloat16, True),
+    (921, 1, 4, 1, 70, 130, 48, torch.bfloat16, False),
+    (922, 1, 2, 2, 65, 65, 256, torch.bfloat16, True),
+    (923, 1, 4, 2, 96, 96, 40, torch.float32, True),
+], ids=["gqa-c-d128", "rect-n-d48", "d256-c", "f32-c-d40"])
+def test_backward_matrix_core_and_per_term_sums_bit_identical(A, shape):
+    seed, B, Hq, Hkv, Sq, Skv, D, dtype, causal = shape
+    q, k, v = W.attn_inputs(seed, B, Hq, Hkv, Sq, Skv, D, dtype)
+    dO = upstream(seed + 50, (B, Hq, Sq, D))
+    say(f"backward both paths {shape}")
+    fast, slow = _backward_both_paths(A, q, k, v, dO, causal, W.default_scale(D))
+    for name, a, b in zip(("dq", "dk", "dv"), fast, slow):
+        assert_bits_equal(a, b, name)
+
+
+def test_backward_wide_ranges_mix_the_paths(A, oracle):
+    """Single entries far below their column's range (a Q entry scaled by
+    2^-60, a K entry by 2^-30, an upstream entry by 2^-40) make one column
+    group of dK, dQ and dV need more digits than the matrix-core sums hold, so
+    those tiles take the per-term sums while the other column groups stay on
+    the matrix cores; all must match the oracle."""
+    q, k, v = W.attn_inputs(930, 1, 4, 2, 100, 100, 64, torch.bfloat16)
+    q[0, 1, 7, 5] = q[0, 1, 7, 5] * 2.0 ** -60
+    k[0, 0, 40, 9] = k[0, 0, 40, 9] * 2.0 ** -30
+    dO = upstream(931, (1, 4, 100, 64))
+    dO[0, 0, 90, 3] *= 2.0 ** -40
+    dO[0, 2, 11, :] *= 8.0
+    scale = W.default_scale(64)
+    say("backward wide ranges: oracle")
+    ref = oracle.attn_backward(q, k, v, dO, True, scale)
+    got = gpu_backward(A, q, k, v, dO, True, scale)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert_bits_equal(a, b, name)
