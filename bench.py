@@ -48,8 +48,14 @@ def measured_traffic(kernel, workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(root, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    srcs = rec["sources"] if "sources" in rec else [rec["source"]]
+    h = hashlib.sha256()
+    for rel in srcs:  # the kernel's file and the headers it includes, in the listed order
+        src = os.path.join(root, rel)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
         return None
     return rec["bytes_per_launch"]
 
@@ -85,6 +91,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the sharded / cross-entropy side measurements")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only the exact backward of the workload (warm-up, then --steps calls) and its JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only copy MB megabytes device to device 5 times (the reference kernel for the HBM "
                          "byte counters) and exit")
@@ -123,6 +131,11 @@ def main():
     Skv = k.shape[2]
     pairs = visible_pairs(B, Hq, Sq, Skv, causal)
     rows = B * Hq * Sq
+
+    if args.backward_only:
+        print(json.dumps({"workload": desc, "backward": backward_measurement(attention, Q, K, V, causal, scale,
+                                                                             pairs, reps=args.steps)}), flush=True)
+        return
 
     for _ in range(args.warmup):
         out = attention.det_attn(Q, K, V, causal, scale)
@@ -187,6 +200,37 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def backward_measurement(attention, Q, K, V, causal, scale, pairs, reps=5):
+    """The exact backward of the same inputs (upstream gradient N(0,1) f32):
+    one forward with row statistics, then `reps` timed backward calls (mean),
+    and the library's per-kernel times of the last call."""
+    from bitwise_deterministic_exact_pass1_amd import _lib
+    Gd = torch.randn(Q.shape, generator=torch.Generator().manual_seed(4242)).cuda()
+    o_s, m_s, den_s = attention.det_attn_with_stats(Q, K, V, causal, scale)
+    attention.det_attn_backward(Q, K, V, o_s, Gd, m_s, den_s, causal, scale)
+    torch.cuda.synchronize()
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    eb[0].record()
+    o_s, m_s, den_s = attention.det_attn_with_stats(Q, K, V, causal, scale)
+    eb[1].record()
+    for _ in range(reps):
+        attention.det_attn_backward(Q, K, V, o_s, Gd, m_s, den_s, causal, scale)
+    eb[2].record()
+    torch.cuda.synchronize()
+    _lib.profile_begin()
+    attention.det_attn_backward(Q, K, V, o_s, Gd, m_s, den_s, causal, scale)
+    torch.cuda.synchronize()
+    bprof = _lib.profile_end()
+    bwd_ms = eb[1].elapsed_time(eb[2]) / reps
+    D_ = Q.shape[3]
+    return {"workload": "the same inputs, upstream gradient N(0,1) f32",
+            "forward_with_stats_ms": eb[0].elapsed_time(eb[1]), "backward_ms": bwd_ms,
+            "pairs_per_s": pairs / (bwd_ms / 1e3),
+            "flop_per_pair": 10 * D_ + 32,
+            "frac_of_fp64_roofline": pairs * (10 * D_ + 32) / (bwd_ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS,
+            "kernels_ms": {k_: round(t, 4) for k_, (c, t) in bprof.items() if k_.startswith("bwd")}}
+
+
 def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     """Side numbers: the sharded composition (16 x 64 keys) and the exact
     backward on the same inputs,
@@ -224,30 +268,8 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     res["cross_entropy"] = {"workload": "N=4096 V=128256 bf16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                             "forward_token_vocab_per_s": N * Vv / (fwd_ms / 1e3),
                             "backward_hbm_GBps": N * Vv * 6 / (bwd_ms / 1e3) / 1e9}
-    # gradients of the same step: forward with row statistics, then the exact backward
-    Gd = torch.randn(Q.shape, generator=torch.Generator().manual_seed(4242)).cuda()
-    o_s, m_s, den_s = attention.det_attn_with_stats(Q, K, V, causal, scale)
-    attention.det_attn_backward(Q, K, V, o_s, Gd, m_s, den_s, causal, scale)
-    torch.cuda.synchronize()
-    from bitwise_deterministic_exact_pass1_amd import _lib
-    _lib.profile_begin()
-    eb = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    eb[0].record()
-    o_s, m_s, den_s = attention.det_attn_with_stats(Q, K, V, causal, scale)
-    eb[1].record()
-    attention.det_attn_backward(Q, K, V, o_s, Gd, m_s, den_s, causal, scale)
-    eb[2].record()
-    torch.cuda.synchronize()
-    bprof = _lib.profile_end()
-    bwd_ms = eb[1].elapsed_time(eb[2])
-    D_ = Q.shape[3]
-    res["backward"] = {"workload": "the same inputs, upstream gradient N(0,1) f32",
-                       "forward_with_stats_ms": eb[0].elapsed_time(eb[1]), "backward_ms": bwd_ms,
-                       "pairs_per_s": pairs / (bwd_ms / 1e3),
-                       "flop_per_pair": 10 * D_ + 32,
-                       "frac_of_fp64_roofline": pairs * (10 * D_ + 32) / (bwd_ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS,
-                       "kernels_ms": {k_: round(t, 4) for k_, (c, t) in bprof.items() if k_.startswith("bwd")}}
-    del Gd, o_s, m_s, den_s
+    res["backward"] = backward_measurement(attention, Q, K, V, causal, scale, pairs)
+
     # the float32 combines the exact path replaces, on the same inputs
     from bitwise_deterministic_exact_pass1_amd import contrast
     res["contrast"] = {"attention_4_shard_rotations": contrast.attention_contrast(attention, Q, K, V, [K.shape[2] // 4] * 4,

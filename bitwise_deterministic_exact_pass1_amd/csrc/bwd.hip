@@ -110,84 +110,176 @@ __global__ __launch_bounds__(256) void k_bwd_delta(BwdArgs A, int64_t rows) {
     A.delta[r] = acc;
 }
 
-// p and ds of a 16 x 16 tile of pairs (rows of the chunk x keys): the 16 rows
-// of Q and dO and the 16 rows of K and V staged in LDS as f32 (exact), then
-// one thread per pair runs the two chains.  Tiles wholly above the causal
-// diagonal are skipped (the sums never read them); invisible pairs of the
-// other tiles get p = ds = 0.  Grid (key tiles, row tiles, heads).
+// p and ds of a 64 x 64 tile of pairs (rows of the chunk x keys):
+//   s = RN32(RN64(scale * chain(q, k))), w = RN32(exp_det(RN64(s - m))),
+//   p = RN32(RN64(w / den64)), ds = RN32(RN64(p * RN64(chain(dO, v) - delta))),
+// invisible pairs 0, with register blocking: thread (tr, tc) = (tid / 16,
+// tid % 16) owns rows 4 tr .. 4 tr + 3 and keys 4 tc .. 4 tc + 3 and runs both
+// chains of its 16 pairs, d ascending.  Q, K, dO and V are staged in LDS as
+// binary64 (exact widening) in chunks of kPdsDc dimensions, transposed to
+// [d][row] so a thread reads its four rows' operands with two 16-byte loads;
+// wave w fills array w, lane = row.  Grid (key tiles, row tiles, heads);
+// tiles wholly above the causal diagonal are skipped.
+constexpr int kPdsT = 64;   // rows and keys of a tile
+constexpr int kPdsDc = 32;  // dimensions per LDS stage
+constexpr int kPdsLd = kPdsT + 2;  // row stride of the staged arrays (16-byte aligned rows of doubles)
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_bwd_pds(BwdArgs A) {
-    __shared__ float sq[kBT][257], sk[kBT][257], sg[kBT][257], sv[kBT][257];
-    const int tid = threadIdx.x, r = tid >> 4, c = tid & 15;
-    const int64_t kb = blockIdx.x, tile = blockIdx.y, bh = blockIdx.z;
+__global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
+    __shared__ __align__(16) double sm[4][kPdsDc][kPdsLd];  // Q, K, dO, V
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tr = tid >> 4, tc = tid & 15;
+    const int64_t kt = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
     const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group;
-    const int64_t ia = A.i0 + tile * kBT, ja = kb * kBT, iend = A.i0 + A.ni;
-    const int64_t ilast = min64(iend, ia + kBT) - 1;
+    const int64_t iend = A.i0 + A.ni, ia = A.i0 + rt * kPdsT, ja = kt * kPdsT;
+    const int64_t ilast = min64(iend, ia + kPdsT) - 1;
     if (A.causal && ja > ilast) return;
-    for (int64_t d = tid; d < A.D; d += 256) {
-#pragma unroll 4
-        for (int rr = 0; rr < kBT; ++rr) {
-            const int64_t iq = min64(ia + rr, iend - 1), jk = min64(ja + rr, A.Skv - 1);  // clamped: in range
-            sq[rr][d] = ld<T>(A.q, b * A.qsB + hq * A.qsH + iq * A.qsS + d);
-            sg[rr][d] = A.dout[b * A.dsB + hq * A.dsH + iq * A.dsS + d];
-            sk[rr][d] = ld<T>(A.k, b * A.ksB + hk * A.ksH + jk * A.ksS + d);
-            sv[rr][d] = ld<T>(A.v, b * A.vsB + hk * A.vsH + jk * A.vsS + d);
+    // wave wv stages array wv: lane handles dimension d0 + lane % 32 of rows
+    // 2 r2 + lane / 32 (clamped into range; such rows are never stored), so
+    // each load instruction reads two rows' contiguous dimensions; the next
+    // stage's values are fetched into registers while this stage computes
+    const void *src;
+    int64_t base, rs;
+    int64_t r0, rmax;
+    bool isf32 = false;
+    switch (wv) {
+        case 0: src = A.q; base = b * A.qsB + hq * A.qsH; rs = A.qsS; r0 = ia; rmax = iend - 1; break;
+        case 1: src = A.k; base = b * A.ksB + hk * A.ksH; rs = A.ksS; r0 = ja; rmax = A.Skv - 1; break;
+        case 2: src = A.dout; base = b * A.dsB + hq * A.dsH; rs = A.dsS; r0 = ia; rmax = iend - 1; isf32 = true; break;
+        default: src = A.v; base = b * A.vsB + hk * A.vsH; rs = A.vsS; r0 = ja; rmax = A.Skv - 1; break;
+    }
+    const int D = (int)A.D, dl = lane & 31, rh = lane >> 5;
+    // all 32 loads of a stage are issued before any is used: in-range
+    // (clamped) addresses, one element width per wave, no branches
+    const bool w32 = __builtin_amdgcn_readfirstlane((int)(isf32 || sizeof(T) == 4)) != 0;
+    uint32_t nx[32];
+    auto gload = [&](int d0) {
+        const int64_t d = min(d0 + dl, D - 1);
+        if (w32) {
+            const uint32_t *p = (const uint32_t *)src + base + d;
+#pragma unroll
+            for (int r2 = 0; r2 < 32; ++r2) nx[r2] = p[min64(r0 + 2 * r2 + rh, rmax) * rs];
+        } else {
+            const uint16_t *p = (const uint16_t *)src + base + d;
+#pragma unroll
+            for (int r2 = 0; r2 < 32; ++r2) nx[r2] = (uint32_t)p[min64(r0 + 2 * r2 + rh, rmax) * rs] << 16;
+        }
+    };
+    double as[4][4], ap[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) as[u][t] = ap[u][t] = 0.0;
+    gload(0);
+    for (int d0 = 0; d0 < D; d0 += kPdsDc) {
+        const int dn = min(kPdsDc, D - d0);
+        __syncthreads();  // the previous stage's readers are done
+        const bool dok = d0 + dl < D;
+#pragma unroll
+        for (int r2 = 0; r2 < 32; ++r2) sm[wv][dl][2 * r2 + rh] = dok ? (double)__uint_as_float(nx[r2]) : 0.0;
+        __syncthreads();
+        if (d0 + kPdsDc < D) gload(d0 + kPdsDc);
+        for (int dd = 0; dd < dn; ++dd) {
+            const double2 *rq = (const double2 *)&sm[0][dd][4 * tr], *rk = (const double2 *)&sm[1][dd][4 * tc];
+            const double2 *ro = (const double2 *)&sm[2][dd][4 * tr], *rv = (const double2 *)&sm[3][dd][4 * tc];
+            const double2 q01 = rq[0], q23 = rq[1], k01 = rk[0], k23 = rk[1];
+            const double2 o01 = ro[0], o23 = ro[1], v01 = rv[0], v23 = rv[1];
+            const double qv[4] = {q01.x, q01.y, q23.x, q23.y}, kv[4] = {k01.x, k01.y, k23.x, k23.y};
+            const double ov[4] = {o01.x, o01.y, o23.x, o23.y}, vv[4] = {v01.x, v01.y, v23.x, v23.y};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    as[u][t] = fma(qv[u], kv[t], as[u][t]);
+                    ap[u][t] = fma(ov[u], vv[t], ap[u][t]);
+                }
         }
     }
-    __syncthreads();
-    const int64_t i = ia + r, j = ja + c;
-    const bool inr = i < iend && j < A.Skv;
-    const int64_t row = bh * A.Sq + i;
-    float p = 0.0f, ds = 0.0f;
-    if (inr && (!A.causal || j <= i)) {
-        const int D = (int)A.D;
-        double acc = 0.0;
-        for (int d = 0; d < D; ++d) acc = fma((double)sq[r][d], (double)sk[c][d], acc);
-        const float s = (float)(A.scale * acc);
-        const float w = weight(s, A.rowmax[row]);
-        p = (float)((double)w / A.den64[row]);
-        double dp = 0.0;
-        for (int d = 0; d < D; ++d) dp = fma((double)sg[r][d], (double)sv[c][d], dp);
-        ds = (float)((double)p * (dp - A.delta[row]));
-    }
-    if (inr) {
-        const int64_t at = (bh * A.ni + (i - A.i0)) * A.Skv + j;
-        A.P[at] = p;
-        A.DS[at] = ds;
-    }
-    // exponent statistics for the matrix-core sums: ds per row over this
-    // tile's keys (lanes r*16 + c of a wave share r), ds and p per key over
-    // the wave's four rows; zeros (and pairs out of range) are empty
-    int pe, pl, de, dl;
-    stat_of(p, pe, pl);
-    stat_of(ds, de, dl);
-    int re = de, rl = dl;
+    // p, ds and the exponent statistics for the matrix-core sums
+    int re[4], rl[4], ce[4], cl[4], pe[4], pl[4];
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-        re = max(re, __shfl_xor(re, off, 64));
-        rl = min(rl, __shfl_xor(rl, off, 64));
+    for (int t = 0; t < 4; ++t) {
+        ce[t] = pe[t] = INT_MIN;
+        cl[t] = pl[t] = INT_MAX;
     }
 #pragma unroll
-    for (int off = 16; off < 64; off <<= 1) {
-        de = max(de, __shfl_xor(de, off, 64));
-        dl = min(dl, __shfl_xor(dl, off, 64));
-        pe = max(pe, __shfl_xor(pe, off, 64));
-        pl = min(pl, __shfl_xor(pl, off, 64));
-    }
-    if (c == 0 && i < iend && re != INT_MIN) {
-        int2 *st = A.st_rds + bh * A.ni + (i - A.i0);
-        atomicMax(&st->x, re);
-        atomicMin(&st->y, rl);
-    }
-    if ((tid & 63) < 16 && j < A.Skv) {
-        const int64_t at = (b * A.Hkv + hk) * A.Skv + j;
-        if (de != INT_MIN) {
-            atomicMax(&A.st_cds[at].x, de);
-            atomicMin(&A.st_cds[at].y, dl);
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = ia + 4 * tr + u;
+        const bool rowok = i < iend;
+        const int64_t row = bh * A.Sq + (rowok ? i : A.i0);
+        const float m = A.rowmax[row];
+        const double den = A.den64[row], delta = A.delta[row];
+        re[u] = INT_MIN;
+        rl[u] = INT_MAX;
+        float pv[4], dv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t j = ja + 4 * tc + t;
+            float p = 0.0f, ds = 0.0f;
+            if (rowok && j < A.Skv && (!A.causal || j <= i)) {
+                const float s = (float)(A.scale * as[u][t]);
+                const float w = weight(s, m);
+                p = (float)((double)w / den);
+                ds = (float)((double)p * (ap[u][t] - delta));
+            }
+            pv[t] = p;
+            dv[t] = ds;
+            int e, l;
+            stat_of(ds, e, l);
+            re[u] = max(re[u], e);
+            rl[u] = min(rl[u], l);
+            ce[t] = max(ce[t], e);
+            cl[t] = min(cl[t], l);
+            stat_of(p, e, l);
+            pe[t] = max(pe[t], e);
+            pl[t] = min(pl[t], l);
         }
-        if (pe != INT_MIN) {
-            atomicMax(&A.st_cp[at].x, pe);
-            atomicMin(&A.st_cp[at].y, pl);
+        if (rowok) {
+            const int64_t at = (bh * A.ni + (i - A.i0)) * A.Skv + ja + 4 * tc;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (ja + 4 * tc + t < A.Skv) {
+                    A.P[at + t] = pv[t];
+                    A.DS[at + t] = dv[t];
+                }
+        }
+    }
+    // ds row statistics over the tile's keys: lanes of one tr differ in tc (xor 1..8)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            re[u] = max(re[u], __shfl_xor(re[u], o, 64));
+            rl[u] = min(rl[u], __shfl_xor(rl[u], o, 64));
+        }
+        const int64_t i = ia + 4 * tr + u;
+        if (tc == 0 && i < iend && re[u] != INT_MIN) {
+            int2 *st = A.st_rds + bh * A.ni + (i - A.i0);
+            atomicMax(&st->x, re[u]);
+            atomicMin(&st->y, rl[u]);
+        }
+    }
+    // ds and p key statistics over the wave's 16 rows (xor 16, 32)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) {
+            ce[t] = max(ce[t], __shfl_xor(ce[t], o, 64));
+            cl[t] = min(cl[t], __shfl_xor(cl[t], o, 64));
+            pe[t] = max(pe[t], __shfl_xor(pe[t], o, 64));
+            pl[t] = min(pl[t], __shfl_xor(pl[t], o, 64));
+        }
+        const int64_t j = ja + 4 * tc + t;
+        if (lane < 16 && j < A.Skv) {
+            const int64_t at = (b * A.Hkv + hk) * A.Skv + j;
+            if (ce[t] != INT_MIN) {
+                atomicMax(&A.st_cds[at].x, ce[t]);
+                atomicMin(&A.st_cds[at].y, cl[t]);
+            }
+            if (pe[t] != INT_MIN) {
+                atomicMax(&A.st_cp[at].x, pe[t]);
+                atomicMin(&A.st_cp[at].y, pl[t]);
+            }
         }
     }
 }
@@ -262,9 +354,10 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
         if (ir < A.ni) st = A.st_rds[bh * A.ni + ir];
         const float *src = A.DS + (bh * A.ni + (ir < A.ni ? ir : 0)) * A.Skv;
 #pragma unroll
-        for (int p = 0; p < 16; ++p) {
+        for (int p = 0; p < 16; ++p) {  // loads from in-range addresses, then selects
             const int64_t j = jb * 32 + tb + p;
-            val[p] = (ir < A.ni && j < A.Skv && (!A.causal || j <= i)) ? src[j] : 0.0f;
+            const float x = src[min64(j, A.Skv - 1)];
+            val[p] = (ir < A.ni && j < A.Skv && (!A.causal || j <= i)) ? x : 0.0f;
         }
         kmax = kXA;
         out = A.xa[0] + u * kXA * 64;
@@ -279,7 +372,8 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
             const int64_t ir = ib * 32 + tb + p;
-            val[p] = (j < A.Skv && ir < A.ni && (!A.causal || j <= A.i0 + ir)) ? src[ir * A.Skv] : 0.0f;
+            const float x = src[min64(ir, A.ni - 1) * A.Skv];
+            val[p] = (j < A.Skv && ir < A.ni && (!A.causal || j <= A.i0 + ir)) ? x : 0.0f;
         }
         kmax = kXA;
         out = A.xa[MODE] + u * kXA * 64;
@@ -291,7 +385,8 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
             const int64_t j = jb * 32 + tb + p;
-            val[p] = (d < A.D && j < A.Skv) ? ld<T>(A.k, base + j * A.ksS) : 0.0f;
+            const float x = ld<T>(A.k, base + min64(j, A.Skv - 1) * A.ksS);
+            val[p] = (d < A.D && j < A.Skv) ? x : 0.0f;
         }
         kmax = kXB;
         out = A.xb[0] + u * kXB * 64;
@@ -303,13 +398,10 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
         const int64_t dd = d < A.D ? d : 0;
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
-            const int64_t ir = ib * 32 + tb + p, i = A.i0 + (ir < A.ni ? ir : 0);
-            float x = 0.0f;
-            if (d < A.D && ir < A.ni) {
-                if (MODE == 4) x = ld<T>(A.q, b * A.qsB + hq * A.qsH + i * A.qsS + dd);
-                else x = A.dout[b * A.dsB + hq * A.dsH + i * A.dsS + dd];
-            }
-            val[p] = x;
+            const int64_t ir = ib * 32 + tb + p, i = A.i0 + min64(ir, A.ni - 1);
+            const float x = MODE == 4 ? ld<T>(A.q, b * A.qsB + hq * A.qsH + i * A.qsS + dd)
+                                      : A.dout[b * A.dsB + hq * A.dsH + i * A.dsS + dd];
+            val[p] = (d < A.D && ir < A.ni) ? x : 0.0f;
         }
         kmax = kXB;
         out = A.xb[MODE - 3] + u * kXB * 64;
@@ -824,9 +916,9 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
         if ((e = launch_fill_i64((int64_t *)A.st_rds, nst, kStatEmpty, s)) != hipSuccess) return e;
         {
             ProfScope prof_("bwd_pds", s);
-            dim3 grid((unsigned)((g.Skv + kBT - 1) / kBT), (unsigned)rt, (unsigned)bh);
-            if (bf) hipLaunchKernelGGL(k_bwd_pds<bf16_t>, grid, dim3(256), 0, s, A);
-            else hipLaunchKernelGGL(k_bwd_pds<float>, grid, dim3(256), 0, s, A);
+            dim3 grid((unsigned)((g.Skv + kPdsT - 1) / kPdsT), (unsigned)((A.ni + kPdsT - 1) / kPdsT), (unsigned)bh);
+            if (bf) hipLaunchKernelGGL(k_bwd_pds64<bf16_t>, grid, dim3(256), 0, s, A);
+            else hipLaunchKernelGGL(k_bwd_pds64<float>, grid, dim3(256), 0, s, A);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         e = bf ? launch_sums<bf16_t>(A, g, q, k, dout, s) : launch_sums<float>(A, g, q, k, dout, s);
