@@ -532,3 +532,51 @@ def test_backward_sequence_permutations(oracle):
     assert np.array_equal(dq.view(np.uint32), base[0][:, :, pq.numpy()].view(np.uint32))
     assert np.array_equal(dk.view(np.uint32), base[1].view(np.uint32))
     assert np.array_equal(dv.view(np.uint32), base[2].view(np.uint32))
+
+
+def test_backward_rounding_points_exact(oracle):
+    """Every rounding point of the backward reading, recomputed independently
+    in Python on a tiny causal GQA case: the chains as sequential Python float
+    sums (each f32 x f32 product is exact in binary64, so a product-then-add
+    chain equals the fma chain), w from the pinned exp_det, den64 from a
+    Fraction sum, p and ds rounded to f32, and the three gradient sums as exact
+    Fractions rounded once (dK and dQ rounded, scaled, rounded again).  The
+    oracle must agree bit for bit; scaling before rounding the sum, or a
+    dropped RN64, changes some of these bits."""
+    B, Hq, Hkv, S, D, sc = 1, 2, 1, 6, 4, 0.35
+    q, k, v = W.attn_inputs(82, B, Hq, Hkv, S, S, D, torch.float32)
+    dO = torch.randn(B, Hq, S, D, generator=torch.Generator().manual_seed(83))
+    dq, dk, dv = oracle.attn_backward(q, k, v, dO, True, sc)
+    O = oracle.det_attn(q, k, v, True, sc)
+    f = lambda t: [[[float(x) for x in row] for row in h] for h in t[0]]
+    Q, K, V, G = f(q), f(k), f(v), f(dO)
+
+    def chain(a, b):
+        acc = 0.0
+        for x, y in zip(a, b):
+            acc = acc + x * y
+        return acc
+
+    P = {}
+    DS = {}
+    for h in range(Hq):
+        for i in range(S):
+            s = [float(np.float32(sc * chain(Q[h][i], K[0][j]))) for j in range(i + 1)]
+            m = max(s)
+            w = [float(np.float32(oracle.exp_det(x - m))) for x in s]
+            den = float(sum(Fraction(x) for x in w))
+            delta = chain(G[h][i], [float(x) for x in O[0, h, i]])
+            for j in range(i + 1):
+                p = float(np.float32(w[j] / den))
+                P[h, i, j] = p
+                DS[h, i, j] = float(np.float32(p * (chain(G[h][i], V[0][j]) - delta)))
+    for d in range(D):
+        for j in range(S):
+            tv = sum((Fraction(P[h, i, j]) * Fraction(G[h][i][d]) for h in range(Hq) for i in range(j, S)), Fraction(0))
+            tk = sum((Fraction(DS[h, i, j]) * Fraction(Q[h][i][d]) for h in range(Hq) for i in range(j, S)), Fraction(0))
+            assert dv[0, 0, j, d] == np.float32(float(tv))  # RN32(RN64(exact sum))
+            assert dk[0, 0, j, d] == np.float32(sc * float(tk))
+        for h in range(Hq):
+            for i in range(S):
+                tq = sum((Fraction(DS[h, i, j]) * Fraction(K[0][j][d]) for j in range(i + 1)), Fraction(0))
+                assert dq[0, h, i, d] == np.float32(sc * float(tq))
