@@ -55,14 +55,13 @@ struct BwdArgs {
     // query-row chunk [i0, i0 + ni)
     int64_t i0, ni, nbh;
     float *P, *DS;                      // [bh][ni][Skv]
-    int64_t *dq_dig;                    // [kBwdDigits][nbh * ni][D]
     int64_t *dk_dig, *dv_dig;           // [kBwdDigits][B * Hkv * Skv][D]
     // matrix-core sums of the chunk.  Statistics {largest exponent, smallest
     // lsb exponent} of the nonzero entries: of each ds row over keys, of each
     // ds / p column over (query head, row), of each column of K over keys and
     // of Q / dO over (query head, row).
     int2 *st_rds, *st_cds, *st_cp, *st_k, *st_q, *st_o;
-    v4i *xa[3], *xb[3];   // digit blocks of the A / B operands of dQ, dK, dV
+    v4i *xb[3];           // digit blocks of the right operands of dQ, dK, dV (K, Q, dO)
     int *xf[3];           // per (row tile, column group): 1 = left to k_bwd_sum
     int64_t nIB, nJB, nG;
     int force_fallback;
@@ -98,15 +97,28 @@ __device__ __forceinline__ float ld(const void *base, int64_t off) {
     return elem<T>::to_f32(((const T *)base)[off]);
 }
 
-// delta_i, one thread per row.
-__global__ __launch_bounds__(256) void k_bwd_delta(BwdArgs A, int64_t rows) {
+// delta_i, one thread per row; the row is read 32 dimensions at a time with
+// all 64 loads issued before the chain uses them (clamped, in range).
+__global__ __launch_bounds__(64) void k_bwd_delta(BwdArgs A, int64_t rows) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r >= rows) return;
     const int64_t b = r / (A.Hq * A.Sq), hq = (r / A.Sq) % A.Hq, i = r % A.Sq;
     const float *o = A.o + b * A.osB + hq * A.osH + i * A.osS;
     const float *g = A.dout + b * A.dsB + hq * A.dsH + i * A.dsS;
+    const int D = (int)A.D;
     double acc = 0.0;
-    for (int64_t d = 0; d < A.D; ++d) acc = fma((double)g[d], (double)o[d], acc);
+    for (int d0 = 0; d0 < D; d0 += 32) {
+        float go[32], oo[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+            const int d = min(d0 + u, D - 1);
+            go[u] = g[d];
+            oo[u] = o[d];
+        }
+#pragma unroll
+        for (int u = 0; u < 32; ++u)
+            if (d0 + u < D) acc = fma((double)go[u], (double)oo[u], acc);
+    }
     A.delta[r] = acc;
 }
 
@@ -324,17 +336,14 @@ __global__ __launch_bounds__(256) void k_bwd_colstats(const void *src, int64_t s
     }
 }
 
-// Digit blocks of the matrix-core sums, one wave per block of 32 operand rows
-// x (here "row" x is the index that survives the sum: a ds / p row or column,
-// or a column d of K, Q, dO) by 32 reduction steps t.  Lane l holds row x =
+// Digit blocks of the right operands of the matrix-core sums (K, Q, dO), one
+// wave per block of 32 operand columns d by 32 reduction steps t.  Lane l holds row x =
 // l % 32 at steps 16 (l / 32) + 0..15, the int8 operand order of
 // v_mfma_i32_32x32x32_i8.  Each row is an integer on its grid, Xi = X 2^-g_x,
 // written as n balanced base-256 digits (n of the block = the largest of its
 // rows): the bytes of Xi + 0x80..80 with their top bit flipped.  Blocks whose
 // rows need more digits than the kernel holds are not written (their tiles
-// take the per-term sums), nor are causal blocks that no sum reads.
-//   MODE 0: A of dQ, unit (bh, row tile, key block): ds[i][j]
-//   MODE 1, 2: A of dK, dV, unit (bhk, key tile, query head g, row block): ds / p [i][j], x = j
+// take the per-term sums).
 //   MODE 3: B of dQ, unit (bhk, column group, key block): K[j][d], x = d
 //   MODE 4, 5: B of dK, dV, unit (bhk, column group, g, row block): Q / dO [i][d], x = d
 template <int MODE, typename T>
@@ -347,37 +356,7 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
     int2 st = int2{INT_MIN, INT_MAX};
     int kmax;
     v4i *out;
-    if (MODE == 0) {
-        const int64_t jb = u % A.nJB, it = (u / A.nJB) % A.nIB, bh = u / (A.nJB * A.nIB);
-        if (A.causal && jb * 32 > A.i0 + it * 32 + 31) return;
-        const int64_t ir = it * 32 + xr, i = A.i0 + ir;
-        if (ir < A.ni) st = A.st_rds[bh * A.ni + ir];
-        const float *src = A.DS + (bh * A.ni + (ir < A.ni ? ir : 0)) * A.Skv;
-#pragma unroll
-        for (int p = 0; p < 16; ++p) {  // loads from in-range addresses, then selects
-            const int64_t j = jb * 32 + tb + p;
-            const float x = src[min64(j, A.Skv - 1)];
-            val[p] = (ir < A.ni && j < A.Skv && (!A.causal || j <= i)) ? x : 0.0f;
-        }
-        kmax = kXA;
-        out = A.xa[0] + u * kXA * 64;
-    } else if (MODE == 1 || MODE == 2) {
-        const int64_t ib = u % A.nIB, g = (u / A.nIB) % A.group, jt = (u / (A.nIB * A.group)) % A.nJB,
-                      bhk = u / (A.nIB * A.group * A.nJB);
-        if (A.causal && A.i0 + ib * 32 + 31 < jt * 32) return;
-        const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, bh = b * A.Hq + hk * A.group + g;
-        const int64_t j = jt * 32 + xr;
-        if (j < A.Skv) st = (MODE == 1 ? A.st_cds : A.st_cp)[bhk * A.Skv + j];
-        const float *src = (MODE == 1 ? A.DS : A.P) + bh * A.ni * A.Skv + (j < A.Skv ? j : 0);
-#pragma unroll
-        for (int p = 0; p < 16; ++p) {
-            const int64_t ir = ib * 32 + tb + p;
-            const float x = src[min64(ir, A.ni - 1) * A.Skv];
-            val[p] = (j < A.Skv && ir < A.ni && (!A.causal || j <= A.i0 + ir)) ? x : 0.0f;
-        }
-        kmax = kXA;
-        out = A.xa[MODE] + u * kXA * 64;
-    } else if (MODE == 3) {
+    if (MODE == 3) {
         const int64_t jb = u % A.nJB, G = (u / A.nJB) % A.nG, bhk = u / (A.nJB * A.nG);
         const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, d = G * 32 + xr;
         if (d < A.D) st = A.st_k[bhk * A.D + d];
@@ -463,7 +442,7 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
     const int64_t d = G * 32 + x;
     int2 sa = int2{INT_MIN, INT_MAX}, sb = int2{INT_MIN, INT_MAX};
     int64_t bh = 0, bhk, g = 0, nblk, k0;
-    const v4i *pa, *pb;
+    const v4i *pb;
     int *flag;
     if (MODE == 0) {
         bh = z;
@@ -472,7 +451,7 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
         if (ir < A.ni) sa = A.st_rds[bh * A.ni + ir];
         k0 = 0;
         nblk = A.causal ? min64(A.nJB, (A.i0 + y * 32 + 31) / 32 + 1) : A.nJB;
-        pa = A.xa[0] + (bh * A.nIB + y) * A.nJB * kXA * 64;
+
         pb = A.xb[0] + (bhk * A.nG + G) * A.nJB * kXB * 64;
         flag = A.xf[0] + (bh * A.nIB + y) * A.nG + G;
     } else {
@@ -482,7 +461,7 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
         if (j < A.Skv) sa = (MODE == 1 ? A.st_cds : A.st_cp)[bhk * A.Skv + j];
         k0 = (A.causal && y * 32 > A.i0) ? (y * 32 - A.i0) / 32 : 0;
         nblk = A.nIB;
-        pa = A.xa[MODE] + ((bhk * A.nJB + y) * A.group + g) * A.nIB * kXA * 64;
+
         pb = A.xb[MODE] + ((bhk * A.nG + G) * A.group + g) * A.nIB * kXB * 64;
         flag = A.xf[MODE] + (bhk * A.nJB + y) * A.nG + G;
     }
@@ -504,18 +483,69 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
 #pragma unroll
     for (int s = 0; s < kXC; ++s) C[s] = v16i{0};
     // the block's A digits: nat * 64 v4i, at most three per thread
-    v4i st[3];
+    // The left operand's digits are made here from the f32 ds / p of the
+    // block: thread tid holds 4 consecutive steps t0..t0+3 of one operand row
+    // xa (dQ: xa = tid / 8, the 4 keys are adjacent in memory; dK, dV: xa =
+    // tid % 32, the 4 query rows are adjacent in the A layout and each load
+    // is coalesced over the lanes), converts them on the row's grid and writes
+    // one 32-bit word per digit plane into the LDS operand image (lane xa +
+    // 32 (t0 / 16), bytes t0 % 16 ..).
+    const int xa = MODE == 0 ? (tid >> 3) : (tid & 31), t0 = MODE == 0 ? 4 * (tid & 7) : 4 * (tid >> 5);
+    int gx;
+    const float *srow;  // this thread's operand row (or column) of ds / p
+    int64_t sstep;      // elements between consecutive steps t
+    bool xok;
+    {
+        int2 st = int2{INT_MIN, INT_MAX};
+        if (MODE == 0) {
+            const int64_t ir = y * 32 + xa;
+            xok = ir < A.ni;
+            if (xok) st = A.st_rds[bh * A.ni + ir];
+            srow = A.DS + (bh * A.ni + (xok ? ir : 0)) * A.Skv;
+            sstep = 1;
+        } else {
+            const int64_t j = y * 32 + xa, b = bhk / A.Hkv, hk = bhk % A.Hkv;
+            xok = j < A.Skv;
+            if (xok) st = (MODE == 1 ? A.st_cds : A.st_cp)[bhk * A.Skv + j];
+            srow = (MODE == 1 ? A.DS : A.P) + (b * A.Hq + hk * A.group + g) * A.ni * A.Skv + (xok ? j : 0);
+            sstep = A.Skv;
+        }
+        int nx_;
+        grid_of(st, gx, nx_);
+    }
+    unsigned __int128 aoff = 0;  // 0x80..80, nat bytes
+    for (int a = 0; a < nat; ++a) aoff = (aoff << 8) | 0x80u;
+    float av[4];
     auto fetch_a = [&](int64_t kb) {
-        const v4i *q = pa + kb * kXA * 64;
 #pragma unroll
-        for (int u = 0; u < 3; ++u)
-            if (tid + 256 * u < nat * 64) st[u] = q[tid + 256 * u];
+        for (int e = 0; e < 4; ++e) {
+            // step t of block kb: key (dQ) or chunk row (dK, dV) kb*32 + t0 + e
+            const int64_t t = kb * 32 + t0 + e;
+            const int64_t tmax = MODE == 0 ? A.Skv - 1 : A.ni - 1;
+            const float x = srow[(t < tmax ? t : tmax) * sstep];
+            bool vis = xok && t <= tmax;
+            if (A.causal) vis = vis && (MODE == 0 ? t <= A.i0 + y * 32 + xa : y * 32 + xa <= A.i0 + t);
+            av[e] = vis ? x : 0.0f;
+        }
     };
     auto stash_a = [&](int buf) {
-        v4i *s = &sA[buf][0][0];
+        unsigned __int128 U[4];
 #pragma unroll
-        for (int u = 0; u < 3; ++u)
-            if (tid + 256 * u < nat * 64) s[tid + 256 * u] = st[u];
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t bits = __float_as_uint(av[e]);
+            const uint32_t be = (bits >> 23) & 0xffu;
+            const uint64_t m = (bits & 0x7fffffu) | (be ? 0x800000u : 0u);
+            const int sh = (int)(be ? be : 1u) - 150 - gx;  // >= 0 for every nonzero entry of the row
+            const unsigned __int128 mag = m ? ((unsigned __int128)m << (sh & 127)) : 0;
+            U[e] = (bits >> 31) ? aoff - mag : aoff + mag;
+        }
+        uint32_t *s = (uint32_t *)&sA[buf][0][0] + (xa + 32 * (t0 >> 4)) * 4 + ((t0 & 15) >> 2);
+        for (int a = 0; a < nat; ++a) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w |= ((uint32_t)(U[e] >> (8 * a)) & 255u) << (8 * e);
+            s[a * 256] = w ^ 0x80808080u;
+        }
     };
     v4i B0[kXB], B1[kXB];
     auto fetch_b = [&](int64_t kb, v4i (&Br)[kXB]) {
@@ -676,11 +706,15 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs A) {
             for (int tt = 0; tt < kBStep; ++tt)
                 bwd_term(__float_as_uint(sa[r][tt]), __float_as_uint(sb[tt][c]), dig, tid);
         }
+        // the tile owns every key of its rows: dQ = RN32(RN64(scale RN64(sum)))
         const int64_t i = ia + r, d = da + c;
         if (i < iend && d < A.D) {
-            const int64_t plane = A.nbh * A.ni * A.D, at = (bh * A.ni + (i - A.i0)) * A.D + d;
+            int64_t x[kBwdDigits];
 #pragma unroll
-            for (int k = 0; k < kBwdDigits; ++k) A.dq_dig[k * plane + at] = dig[k][tid];
+            for (int k = 0; k < kBwdDigits; ++k) x[k] = dig[k][tid];
+            canonicalize<kBwdDigits>(x);
+            A.dq.data[b * A.dq.sB + (bh % A.Hq) * A.dq.sH + i * A.dq.sS + d] =
+                (float)(A.scale * digits_to_f64<kBwdDigits>(x, kBwdElo));
         }
         return;
     }
@@ -722,15 +756,11 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs A) {
 
 // out = RN32(RN64(f * RN64(X))) of each digit sum X (f = scale or 1); row R
 // of the planes is (head, s) = (R / S, R % S) of the output view.
-// With flags (dQ), only outputs of the tiles left to k_bwd_sum: flag of
-// (head, row tile, column group) at flags[(head * nIB + s / 32) * nG + d / 32].
 __global__ __launch_bounds__(256) void k_bwd_finalize(const int64_t *dig, int64_t rows, int64_t D, int64_t S,
-                                                      int64_t s_off, int64_t H, double f, OutView o,
-                                                      const int *flags, int64_t nIB, int64_t nG) {
+                                                      int64_t s_off, int64_t H, double f, OutView o) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= rows * D) return;
     const int64_t R = t / D, d = t % D;
-    if (flags && !flags[((R / S) * nIB + (R % S) / 32) * nG + d / 32]) return;
     int64_t x[kBwdDigits];
 #pragma unroll
     for (int k = 0; k < kBwdDigits; ++k) x[k] = dig[k * rows * D + t];
@@ -768,11 +798,7 @@ static size_t bwd_chunk_layout(const AttnGeom &g, int64_t ni, BwdArgs *A, char *
     };
     char *P = take((size_t)bh * ni * g.Skv * 4);
     char *DS = take((size_t)bh * ni * g.Skv * 4);
-    char *dqd = take((size_t)kBwdDigits * bh * ni * g.D * 8);
     char *st = take((size_t)(bh * ni + 2 * bhk * g.Skv + 3 * bhk * g.D) * 8);
-    char *xa0 = take((size_t)kXA * 1024 * bh * nIB * nJB);
-    char *xa1 = take((size_t)kXA * 1024 * bhk * nJB * grp * nIB);
-    char *xa2 = take((size_t)kXA * 1024 * bhk * nJB * grp * nIB);
     char *xb0 = take((size_t)kXB * 1024 * bhk * nG * nJB);
     char *xb1 = take((size_t)kXB * 1024 * bhk * nG * grp * nIB);
     char *xb2 = take((size_t)kXB * 1024 * bhk * nG * grp * nIB);
@@ -780,7 +806,6 @@ static size_t bwd_chunk_layout(const AttnGeom &g, int64_t ni, BwdArgs *A, char *
     if (A) {
         A->P = (float *)P;
         A->DS = (float *)DS;
-        A->dq_dig = (int64_t *)dqd;
         int2 *s2 = (int2 *)st;
         A->st_rds = s2;
         A->st_cds = s2 + bh * ni;
@@ -788,9 +813,6 @@ static size_t bwd_chunk_layout(const AttnGeom &g, int64_t ni, BwdArgs *A, char *
         A->st_k = A->st_cp + bhk * g.Skv;
         A->st_q = A->st_k + bhk * g.D;
         A->st_o = A->st_q + bhk * g.D;
-        A->xa[0] = (v4i *)xa0;
-        A->xa[1] = (v4i *)xa1;
-        A->xa[2] = (v4i *)xa2;
         A->xb[0] = (v4i *)xb0;
         A->xb[1] = (v4i *)xb1;
         A->xb[2] = (v4i *)xb2;
@@ -828,10 +850,7 @@ static hipError_t launch_sums(BwdArgs &A, const AttnGeom &g, const Tensor &q, co
                            A.i0 + A.ni, g.D, A.st_q);
         hipLaunchKernelGGL(k_bwd_colstats<float>, gq, dim3(256), 0, s, dout.data, dout.sB, dout.sH, dout.sS, grp,
                            g.Hkv, A.i0, A.i0 + A.ni, g.D, A.st_o);
-        const int64_t u0 = bh * nIB * nJB, u1 = bhk * nJB * grp * nIB, u3 = bhk * nG * nJB, u4 = bhk * nG * grp * nIB;
-        hipLaunchKernelGGL((k_bwd_slice<0, T>), dim3(blocks_of(u0 * 64)), dim3(256), 0, s, A, u0);
-        hipLaunchKernelGGL((k_bwd_slice<1, T>), dim3(blocks_of(u1 * 64)), dim3(256), 0, s, A, u1);
-        hipLaunchKernelGGL((k_bwd_slice<2, T>), dim3(blocks_of(u1 * 64)), dim3(256), 0, s, A, u1);
+        const int64_t u3 = bhk * nG * nJB, u4 = bhk * nG * grp * nIB;
         hipLaunchKernelGGL((k_bwd_slice<3, T>), dim3(blocks_of(u3 * 64)), dim3(256), 0, s, A, u3);
         hipLaunchKernelGGL((k_bwd_slice<4, T>), dim3(blocks_of(u4 * 64)), dim3(256), 0, s, A, u4);
         hipLaunchKernelGGL((k_bwd_slice<5, T>), dim3(blocks_of(u4 * 64)), dim3(256), 0, s, A, u4);
@@ -903,7 +922,7 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
     if ((e = launch_fill_i64(A.dv_dig, kvn, 0, s)) != hipSuccess) return e;
     {
         ProfScope prof_("bwd_delta", s);
-        hipLaunchKernelGGL(k_bwd_delta, dim3(blocks_of(rows)), dim3(256), 0, s, A, rows);
+        hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((rows + 63) / 64)), dim3(64), 0, s, A, rows);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const bool bf = q.dtype == 1;
@@ -923,20 +942,13 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
         }
         e = bf ? launch_sums<bf16_t>(A, g, q, k, dout, s) : launch_sums<float>(A, g, q, k, dout, s);
         if (e != hipSuccess) return e;
-        {
-            ProfScope prof_("bwd_finalize", s);
-            const int64_t n = bh * A.ni;  // rows (head, i) of the chunk, i from i0
-            hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(n * g.D)), dim3(256), 0, s, A.dq_dig, n, g.D, A.ni,
-                               i0, g.Hq, g.scale, dq, (const int *)A.xf[0], A.nIB, A.nG);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-        }
     }
     ProfScope prof_("bwd_finalize", s);
     const int64_t nk = bhk * g.Skv;
     hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(nk * g.D)), dim3(256), 0, s, A.dk_dig, nk, g.D, g.Skv,
-                       (int64_t)0, g.Hkv, g.scale, dk, (const int *)nullptr, (int64_t)0, (int64_t)1);
+                       (int64_t)0, g.Hkv, g.scale, dk);
     hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(nk * g.D)), dim3(256), 0, s, A.dv_dig, nk, g.D, g.Skv,
-                       (int64_t)0, g.Hkv, 1.0, dv, (const int *)nullptr, (int64_t)0, (int64_t)1);
+                       (int64_t)0, g.Hkv, 1.0, dv);
     return hipGetLastError();
 }
 

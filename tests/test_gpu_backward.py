@@ -127,9 +127,11 @@ def test_autograd_wrapper(A):
 
 
 def test_backward_small_workspace_row_chunks(A):
-    """Half the default workspace makes the library take the query rows in
-    chunks of 32 (dK and dV keep adding into the same digits, dQ is finished
-    chunk by chunk); the gradients must be the same bits."""
+    """The smallest workspace the library accepts (the size of one 32-row
+    chunk, read from its DET_E_WORKSPACE message) makes it take the query rows
+    in chunks of 32 (dK and dV keep adding into the same digits, dQ is
+    finished chunk by chunk); the gradients must be the same bits."""
+    import re
     import ctypes as C
     from bitwise_deterministic_exact_pass1_amd import _lib
     q, k, v = W.attn_inputs(918, 2, 8, 2, 200, 200, 128, torch.bfloat16)
@@ -141,10 +143,15 @@ def test_backward_small_workspace_row_chunks(A):
     L = _lib.lib()
     dq_, dk_, dv_ = A._desc(Q), A._desc(K), A._desc(V)
     full = L.det_attn_backward_workspace_size(C.byref(dq_), C.byref(dk_), C.byref(dv_), 1)
-    small = (full // 2) // 256 * 256
+    g = [torch.empty_like(t, dtype=torch.float32) for t in (Q, K, V)]
+    rc = L.det_attn_backward(C.byref(dq_), C.byref(dk_), C.byref(dv_), C.byref(A._desc(out)), C.byref(A._desc(dO)),
+                             m.data_ptr(), den.data_ptr(), 1, scale, C.byref(A._out(g[0])), C.byref(A._out(g[1])),
+                             C.byref(A._out(g[2])), 256, 256, A._stream(Q))
+    assert _lib.ERRORS[rc] == "DET_E_WORKSPACE"  # a host-side check: nothing was launched
+    small = int(re.search(r"need at least (\d+)", L.det_last_error().decode()).group(1))
+    assert small < full
     ws = torch.empty(small + 256, dtype=torch.uint8, device=Q.device)
     addr = (ws.data_ptr() + 255) & ~255
-    g = [torch.empty_like(t, dtype=torch.float32) for t in (Q, K, V)]
     say(f"backward with {small} of {full} workspace bytes")
     _lib.check(L.det_attn_backward(C.byref(dq_), C.byref(dk_), C.byref(dv_), C.byref(A._desc(out)),
                                    C.byref(A._desc(dO)), m.data_ptr(), den.data_ptr(), 1, scale,
