@@ -208,3 +208,28 @@ def test_backward_wide_ranges_mix_the_paths(A, oracle):
     got = gpu_backward(A, q, k, v, dO, True, scale)
     for name, a, b in zip(("dq", "dk", "dv"), got, ref):
         assert_bits_equal(a, b, name)
+
+
+def test_backward_full_bench_size_both_paths_and_fp64(A):
+    """The bench workload (B=2 Hq=8 Hkv=2 S=1024 D=128 bf16 causal, N(0,1) f32
+    upstream gradient), too large for the oracle: the matrix-core sums and the
+    per-term digit sums (two independent exact arithmetics) must give the same
+    bits, and every gradient must lie within f32 rounding of fp64 autograd
+    (2^-20 of the gradient scale, as the oracle's own pin)."""
+    q, k, v = W.attn_inputs(2, 2, 8, 2, 1024, 1024, 128, torch.bfloat16)
+    dO = upstream(4242, (2, 8, 1024, 128))
+    scale = W.default_scale(128)
+    say("backward at the bench size: both paths")
+    fast, slow = _backward_both_paths(A, q, k, v, dO, True, scale)
+    for name, a, b in zip(("dq", "dk", "dv"), fast, slow):
+        assert_bits_equal(a, b, name)
+    say("backward at the bench size: fp64 autograd on the GPU")
+    Q, K, V = [t.cuda().double().requires_grad_() for t in (q, k, v)]
+    Kr, Vr = K.repeat_interleave(4, 1), V.repeat_interleave(4, 1)
+    s = torch.matmul(Q, Kr.transpose(-1, -2).contiguous()) * scale
+    s = s.masked_fill(~torch.ones(1024, 1024, dtype=torch.bool, device=s.device).tril(), float("-inf"))
+    torch.matmul(torch.softmax(s, -1), Vr).backward(dO.cuda().double())
+    for name, a, b in zip(("dq", "dk", "dv"), fast, (Q.grad, K.grad, V.grad)):
+        err = (a.double() - b).abs().max().item()
+        tol = 2.0 ** -20 * (b.abs().max().item() + 1)
+        assert err <= tol, (name, err, tol)
