@@ -513,10 +513,7 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
         int nx_;
         grid_of(st, gx, nx_);
     }
-    unsigned __int128 aoff = 0;  // 0x80..80, nat bytes
-    for (int a = 0; a < nat; ++a) aoff = (aoff << 8) | 0x80u;
-    float av[4];
-    auto fetch_a = [&](int64_t kb) {
+    auto fetch_a = [&](int64_t kb, float (&av)[4]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             // step t of block kb: key (dQ) or chunk row (dK, dV) kb*32 + t0 + e
@@ -528,23 +525,35 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
             av[e] = vis ? x : 0.0f;
         }
     };
-    auto stash_a = [&](int buf) {
-        unsigned __int128 U[4];
+    // Digits of one entry: Xi = +-x 256^q with x = m 2^r < 2^31 (m the 24-bit
+    // significand, sh = 8q + r its shift onto the row's grid).  The bytes of
+    // 0x80..80 +- x 256^q are 0x80 below q, the four bytes of w = 0x80808080
+    // +- x at q..q+3 (no borrow: x < 0x80808080), 0x80 plus the carry of
+    // that add at q+4 and 0x80 above, so the balanced digits (bytes ^ 0x80)
+    // are the bytes of w ^ 0x80808080, then the carry, and 0 elsewhere.  Each
+    // thread zeroes its own word of every digit plane and stores its entries'
+    // nonzero digits as bytes (same thread: the stores land in order).
+    auto stash_a = [&](int buf, const float (&av)[4]) {
+        uint32_t *wb = (uint32_t *)&sA[buf][0][0] + (xa + 32 * (t0 >> 4)) * 4 + ((t0 & 15) >> 2);
+        for (int a = 0; a < nat; ++a) wb[a * 256] = 0u;
+        uint8_t *bb = (uint8_t *)wb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t bits = __float_as_uint(av[e]);
+            if ((bits & 0x7fffffffu) == 0u) continue;
             const uint32_t be = (bits >> 23) & 0xffu;
-            const uint64_t m = (bits & 0x7fffffu) | (be ? 0x800000u : 0u);
+            const uint32_t m = (bits & 0x7fffffu) | (be ? 0x800000u : 0u);
             const int sh = (int)(be ? be : 1u) - 150 - gx;  // >= 0 for every nonzero entry of the row
-            const unsigned __int128 mag = m ? ((unsigned __int128)m << (sh & 127)) : 0;
-            U[e] = (bits >> 31) ? aoff - mag : aoff + mag;
-        }
-        uint32_t *s = (uint32_t *)&sA[buf][0][0] + (xa + 32 * (t0 >> 4)) * 4 + ((t0 & 15) >> 2);
-        for (int a = 0; a < nat; ++a) {
-            uint32_t w = 0;
+            const int q = sh >> 3;
+            const uint32_t x = m << (sh & 7);
+            const bool neg = (bits >> 31) != 0;
+            const uint32_t w = neg ? 0x80808080u - x : 0x80808080u + x;
+            const uint32_t dg = w ^ 0x80808080u;
+            const bool carry = !neg && w < x;  // the add wrapped past 2^32
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w |= ((uint32_t)(U[e] >> (8 * a)) & 255u) << (8 * e);
-            s[a * 256] = w ^ 0x80808080u;
+            for (int k = 0; k < 4; ++k)  // (q >= 0 by the grid; the bounds keep every store in the slot)
+                if (q + k >= 0 && q + k < nat) bb[(q + k) * 1024 + e] = (uint8_t)(dg >> (8 * k));
+            if (carry && q + 4 >= 0 && q + 4 < nat) bb[(q + 4) * 1024 + e] = 1;
         }
     };
     v4i B0[kXB], B1[kXB];
@@ -555,11 +564,15 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
         for (int b = 0; b < kXB; ++b)
             if (b < nbt) Br[b] = q[b * 64];
     };
+    // step kb: block kb's digits in slot (kb - k0) & 1; block kb + 1's f32
+    // values and the wave's B digits are fetched first and its digits made
+    // after the products of block kb
+    float F[4];
     auto step = [&](int64_t kb, const v4i (&Bc)[kXB], v4i (&Bn)[kXB]) {
         const int buf = (int)((kb - k0) & 1);
         const bool more = kb + 1 < nblk;
         if (more) {
-            fetch_a(kb + 1);
+            fetch_a(kb + 1, F);
             fetch_b(kb + 1, Bn);
         }
         if (run) {
@@ -585,13 +598,13 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
                 }
             }
         }
-        if (more) stash_a(buf ^ 1);  // its readers passed the previous barrier
+        if (more) stash_a(buf ^ 1, F);  // its readers passed the previous barrier
         __syncthreads();
     };
     if (k0 < nblk) {
-        fetch_a(k0);
+        fetch_a(k0, F);
         fetch_b(k0, B0);
-        stash_a(0);
+        stash_a(0, F);
     }
     __syncthreads();
     for (int64_t kb = k0; kb < nblk; kb += 2) {
