@@ -233,3 +233,27 @@ def test_backward_full_bench_size_both_paths_and_fp64(A):
         err = (a.double() - b).abs().max().item()
         tol = 2.0 ** -20 * (b.abs().max().item() + 1)
         assert err <= tol, (name, err, tol)
+
+
+def test_backward_strided_nhd_views_and_strided_upstream(A, oracle):
+    """Q, K, V as [B, H, S, D] views of one interleaved QKV buffer (row stride
+    3 H D, head stride D, as the long workload's layout; GQA with the same
+    head count for K and V here), a causal case, and an upstream gradient that
+    is itself a strided view: the gradients must equal the oracle's on the
+    same views, bit for bit."""
+    S, H, D = 77, 4, 32
+    buf = torch.randn(S, 3 * H * D, generator=torch.Generator().manual_seed(940)).to(torch.bfloat16)
+    views = [torch.as_strided(buf, (1, H, S, D), (S * 3 * H * D, D, 3 * H * D, 1), off * H * D) for off in range(3)]
+    q, k, v = views
+    gbuf = torch.randn(S, 2 * H * D, generator=torch.Generator().manual_seed(941))
+    dO = torch.as_strided(gbuf, (1, H, S, D), (S * 2 * H * D, D, 2 * H * D, 1), H * D)
+    scale = W.default_scale(D)
+    say("backward strided views: oracle")
+    ref = oracle.attn_backward(q, k, v, dO, True, scale)
+    bd, gd = buf.cuda(), gbuf.cuda()
+    Qd, Kd, Vd = [torch.as_strided(bd, (1, H, S, D), (S * 3 * H * D, D, 3 * H * D, 1), off * H * D) for off in range(3)]
+    dOd = torch.as_strided(gd, (1, H, S, D), (S * 2 * H * D, D, 2 * H * D, 1), H * D)
+    out, m, den = A.det_attn_with_stats(Qd, Kd, Vd, True, scale)
+    got = A.det_attn_backward(Qd, Kd, Vd, out, dOd, m, den, True, scale)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert_bits_equal(a, b, name)
