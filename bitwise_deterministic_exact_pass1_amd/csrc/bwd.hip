@@ -122,7 +122,9 @@ __global__ __launch_bounds__(64) void k_bwd_delta(BwdArgs A, int64_t rows) {
     A.delta[r] = acc;
 }
 
-// p and ds of a 64 x 64 tile of pairs (rows of the chunk x keys):
+// p and ds of a 64 x 64 tile of pairs (rows of the chunk x keys); with SC the
+// scores were stored in P by the matrix-core score path (bf16 inputs; the
+// same s, see qk.hip) and only the dp chain runs here:
 //   s = RN32(RN64(scale * chain(q, k))), w = RN32(exp_det(RN64(s - m))),
 //   p = RN32(RN64(w / den64)), ds = RN32(RN64(p * RN64(chain(dO, v) - delta))),
 // invisible pairs 0, with register blocking: thread (tr, tc) = (tid / 16,
@@ -136,7 +138,7 @@ constexpr int kPdsT = 64;   // rows and keys of a tile
 constexpr int kPdsDc = 32;  // dimensions per LDS stage
 constexpr int kPdsLd = kPdsT + 2;  // row stride of the staged arrays (16-byte aligned rows of doubles)
 
-template <typename T>
+template <typename T, bool SC>
 __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
     __shared__ __align__(16) double sm[4][kPdsDc][kPdsLd];  // Q, K, dO, V
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -182,29 +184,35 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
     for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int t = 0; t < 4; ++t) as[u][t] = ap[u][t] = 0.0;
-    gload(0);
+    const bool stage = !SC || wv >= 2;  // with stored scores only dO and V are staged
+    if (stage) gload(0);
     for (int d0 = 0; d0 < D; d0 += kPdsDc) {
         const int dn = min(kPdsDc, D - d0);
         __syncthreads();  // the previous stage's readers are done
         const bool dok = d0 + dl < D;
+        if (stage) {
 #pragma unroll
-        for (int r2 = 0; r2 < 32; ++r2) sm[wv][dl][2 * r2 + rh] = dok ? (double)__uint_as_float(nx[r2]) : 0.0;
+            for (int r2 = 0; r2 < 32; ++r2) sm[wv][dl][2 * r2 + rh] = dok ? (double)__uint_as_float(nx[r2]) : 0.0;
+        }
         __syncthreads();
-        if (d0 + kPdsDc < D) gload(d0 + kPdsDc);
+        if (stage && d0 + kPdsDc < D) gload(d0 + kPdsDc);
         for (int dd = 0; dd < dn; ++dd) {
-            const double2 *rq = (const double2 *)&sm[0][dd][4 * tr], *rk = (const double2 *)&sm[1][dd][4 * tc];
             const double2 *ro = (const double2 *)&sm[2][dd][4 * tr], *rv = (const double2 *)&sm[3][dd][4 * tc];
-            const double2 q01 = rq[0], q23 = rq[1], k01 = rk[0], k23 = rk[1];
             const double2 o01 = ro[0], o23 = ro[1], v01 = rv[0], v23 = rv[1];
-            const double qv[4] = {q01.x, q01.y, q23.x, q23.y}, kv[4] = {k01.x, k01.y, k23.x, k23.y};
             const double ov[4] = {o01.x, o01.y, o23.x, o23.y}, vv[4] = {v01.x, v01.y, v23.x, v23.y};
+            if (!SC) {
+                const double2 *rq = (const double2 *)&sm[0][dd][4 * tr], *rk = (const double2 *)&sm[1][dd][4 * tc];
+                const double2 q01 = rq[0], q23 = rq[1], k01 = rk[0], k23 = rk[1];
+                const double qv[4] = {q01.x, q01.y, q23.x, q23.y}, kv[4] = {k01.x, k01.y, k23.x, k23.y};
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) as[u][t] = fma(qv[u], kv[t], as[u][t]);
+            }
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    as[u][t] = fma(qv[u], kv[t], as[u][t]);
-                    ap[u][t] = fma(ov[u], vv[t], ap[u][t]);
-                }
+                for (int t = 0; t < 4; ++t) ap[u][t] = fma(ov[u], vv[t], ap[u][t]);
         }
     }
     // p, ds and the exponent statistics for the matrix-core sums
@@ -229,7 +237,8 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
             const int64_t j = ja + 4 * tc + t;
             float p = 0.0f, ds = 0.0f;
             if (rowok && j < A.Skv && (!A.causal || j <= i)) {
-                const float s = (float)(A.scale * as[u][t]);
+                // the stored score (the matrix-core score path wrote it into P) or the chain's
+                const float s = SC ? A.P[(bh * A.ni + (i - A.i0)) * A.Skv + j] : (float)(A.scale * as[u][t]);
                 const float w = weight(s, m);
                 p = (float)((double)w / den);
                 ds = (float)((double)p * (ap[u][t] - delta));
@@ -271,7 +280,9 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
             atomicMin(&st->y, rl[u]);
         }
     }
-    // ds and p key statistics over the wave's 16 rows (xor 16, 32)
+    // ds and p key statistics over the wave's 16 rows (xor 16, 32), then over
+    // the four waves in LDS (the staging arrays are free after the barrier):
+    // one atomic per key and value from the workgroup
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -281,17 +292,32 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
             pe[t] = max(pe[t], __shfl_xor(pe[t], o, 64));
             pl[t] = min(pl[t], __shfl_xor(pl[t], o, 64));
         }
-        const int64_t j = ja + 4 * tc + t;
-        if (lane < 16 && j < A.Skv) {
-            const int64_t at = (b * A.Hkv + hk) * A.Skv + j;
-            if (ce[t] != INT_MIN) {
-                atomicMax(&A.st_cds[at].x, ce[t]);
-                atomicMin(&A.st_cds[at].y, cl[t]);
-            }
-            if (pe[t] != INT_MIN) {
-                atomicMax(&A.st_cp[at].x, pe[t]);
-                atomicMin(&A.st_cp[at].y, pl[t]);
-            }
+    }
+    __syncthreads();  // every wave is done with the staged operands
+    int4 *ks = (int4 *)&sm[0][0][0];  // [wave][key] {ds emax, ds lmin, p emax, p lmin}
+    if (lane < 16) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ks[wv * kPdsT + 4 * tc + t] = int4{ce[t], cl[t], pe[t], pl[t]};
+    }
+    __syncthreads();
+    if (tid < kPdsT && ja + tid < A.Skv) {
+        int4 v = ks[tid];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            const int4 u = ks[w * kPdsT + tid];
+            v.x = max(v.x, u.x);
+            v.y = min(v.y, u.y);
+            v.z = max(v.z, u.z);
+            v.w = min(v.w, u.w);
+        }
+        const int64_t at = (b * A.Hkv + hk) * A.Skv + ja + tid;
+        if (v.x != INT_MIN) {
+            atomicMax(&A.st_cds[at].x, v.x);
+            atomicMin(&A.st_cds[at].y, v.y);
+        }
+        if (v.z != INT_MIN) {
+            atomicMax(&A.st_cp[at].x, v.z);
+            atomicMin(&A.st_cp[at].y, v.w);
         }
     }
 }
@@ -894,7 +920,8 @@ static hipError_t launch_sums(BwdArgs &A, const AttnGeom &g, const Tensor &q, co
 hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &v, const Tensor &o,
                                 const Tensor &dout, const float *rowmax, const double *den64, const AttnGeom &g,
                                 void *fixed_ws, void *chunk_ws, int64_t chunk, const OutView &dq,
-                                const OutView &dk, const OutView &dv, int force_fallback, hipStream_t s) {
+                                const OutView &dk, const OutView &dv, int force_fallback, const ScoreFn *scores,
+                                hipStream_t s) {
     const int64_t bh = g.B * g.Hq, bhk = g.B * g.Hkv, rows = bh * g.Sq;
     if (bh > 65535 || bhk > 65535 || (chunk + kBT - 1) / kBT > 65535 || (g.Skv + kBT - 1) / kBT > 65535)
         return hipErrorInvalidValue;  // grid y / z limits
@@ -946,11 +973,17 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
         const int64_t rt = (A.ni + kBT - 1) / kBT;
         const int64_t nst = bh * chunk + 2 * bhk * g.Skv + 3 * bhk * g.D;  // the carved statistics
         if ((e = launch_fill_i64((int64_t *)A.st_rds, nst, kStatEmpty, s)) != hipSuccess) return e;
+        if (scores && (e = (*scores)(i0, i0 + A.ni, A.P)) != hipSuccess) return e;
         {
             ProfScope prof_("bwd_pds", s);
             dim3 grid((unsigned)((g.Skv + kPdsT - 1) / kPdsT), (unsigned)((A.ni + kPdsT - 1) / kPdsT), (unsigned)bh);
-            if (bf) hipLaunchKernelGGL(k_bwd_pds64<bf16_t>, grid, dim3(256), 0, s, A);
-            else hipLaunchKernelGGL(k_bwd_pds64<float>, grid, dim3(256), 0, s, A);
+            if (scores) {
+                if (bf) hipLaunchKernelGGL((k_bwd_pds64<bf16_t, true>), grid, dim3(256), 0, s, A);
+                else hipLaunchKernelGGL((k_bwd_pds64<float, true>), grid, dim3(256), 0, s, A);
+            } else {
+                if (bf) hipLaunchKernelGGL((k_bwd_pds64<bf16_t, false>), grid, dim3(256), 0, s, A);
+                else hipLaunchKernelGGL((k_bwd_pds64<float, false>), grid, dim3(256), 0, s, A);
+            }
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         e = bf ? launch_sums<bf16_t>(A, g, q, k, dout, s) : launch_sums<float>(A, g, q, k, dout, s);

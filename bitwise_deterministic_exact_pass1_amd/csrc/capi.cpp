@@ -479,13 +479,21 @@ static int check_grad_operand(const det_tensor *t, const det_tensor *q, const ch
     return DET_OK;
 }
 
-static size_t bytes_backward(const AttnGeom &g, int64_t ni) { return bwd_fixed_bytes(g) + bwd_chunk_bytes(g, ni); }
+// With bf16 inputs the backward's scores come from the matrix-core score path,
+// which needs its K preparation, its chunk part and rowmax keys (unused here).
+static size_t bytes_backward(const AttnGeom &g, bool mf, int64_t ni) {
+    const size_t sc = mf ? score_fixed_bytes(g, true, g.Skv) + score_chunk_bytes(g, true, ni, g.Skv) +
+                               align256((size_t)g.B * g.Hq * ni * 4)
+                         : 0;
+    return bwd_fixed_bytes(g) + bwd_chunk_bytes(g, ni) + sc;
+}
 
 size_t det_attn_backward_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
                                         int32_t causal) {
     if (check_qkv(q, k, v, causal)) return 0;
     const AttnGeom g = geom(q, k, causal, 1.0);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_backward(g, ni); });
+    const bool mf = use_mfma_scores(q);
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_backward(g, mf, ni); });
 }
 
 int det_attn_backward(const det_tensor *q, const det_tensor *k, const det_tensor *v, const det_tensor *o,
@@ -499,7 +507,8 @@ int det_attn_backward(const det_tensor *q, const det_tensor *k, const det_tensor
     if (k->S > 0 && ((rc = check_out(dk)) || (rc = check_out(dv)))) return rc;
     if (q->S > 0 && k->S > 0 && (!rowmax || !den64)) return fail(DET_E_NULL, "rowmax or den64 is NULL");
     const AttnGeom g = geom(q, k, causal, scale);
-    auto need = [&](int64_t ni) { return bytes_backward(g, ni); };
+    const bool mf = use_mfma_scores(q);
+    auto need = [&](int64_t ni) { return bytes_backward(g, mf, ni); };
     const bool work = g.Sq > 0 && g.Skv > 0;
     if ((rc = check_ws(workspace, ws_bytes, work ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
     hipStream_t s = (hipStream_t)stream;
@@ -515,10 +524,18 @@ int det_attn_backward(const det_tensor *q, const det_tensor *k, const det_tensor
     Carver c0{(char *)workspace, ws_bytes};
     void *fixed = c0.take<char>(bwd_fixed_bytes(g));
     void *cws = c0.take<char>(bwd_chunk_bytes(g, chunk));
+    void *kprep = mf ? c0.take<char>(score_fixed_bytes(g, true, g.Skv)) : nullptr;
+    void *sws = mf ? c0.take<char>(score_chunk_bytes(g, true, chunk, g.Skv)) : nullptr;
+    uint32_t *keys = mf ? c0.take<uint32_t>(g.B * g.Hq * chunk) : nullptr;
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
-    HIP_TRY(launch_attn_backward(to_t(q), to_t(k), to_t(v), to_t(o), to_t(dout), rowmax, den64, g, fixed, cws, chunk,
+    const Tensor tq = to_t(q), tk = to_t(k);
+    const ScoreFn scores = [&](int64_t i0, int64_t i1, float *out) {
+        return run_scores(tq, tk, tk, g, true, kprep, i0 == 0, true, nullptr, sws, i0, i1, 0, g.Skv, out, keys, i1 - i0,
+                          i0, s);
+    };
+    HIP_TRY(launch_attn_backward(tq, tk, to_t(v), to_t(o), to_t(dout), rowmax, den64, g, fixed, cws, chunk,
                                  OutView{dq->data, dq->sB, dq->sH, dq->sS}, OutView{dk->data, dk->sB, dk->sH, dk->sS},
-                                 OutView{dv->data, dv->sB, dv->sH, dv->sS}, force_fallback(), s),
+                                 OutView{dv->data, dv->sB, dv->sH, dv->sS}, force_fallback(), mf ? &scores : nullptr, s),
             "backward");
     return ok();
 }

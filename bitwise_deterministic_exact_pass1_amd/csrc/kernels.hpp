@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <functional>
+
 #include "dev_math.hpp"
 
 namespace det {
@@ -90,10 +92,15 @@ constexpr int kBwdElo = -298;    // their lsb exponent
 size_t bwd_fixed_bytes(const AttnGeom &g);
 size_t bwd_chunk_bytes(const AttnGeom &g, int64_t ni);
 hipError_t launch_zero_view(const OutView &o, int64_t B, int64_t H, int64_t S, int64_t D, hipStream_t s);
+// scores (nullable): writes the scores of query rows [i0, i1) against every
+// key into the given [B*Hq][i1-i0][Skv] array (the matrix-core score path);
+// without it the chains kernel runs the score chain itself.
+typedef std::function<hipError_t(int64_t i0, int64_t i1, float *scores)> ScoreFn;
 hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &v, const Tensor &o,
                                 const Tensor &dout, const float *rowmax, const double *den64, const AttnGeom &g,
                                 void *fixed_ws, void *chunk_ws, int64_t chunk, const OutView &dq,
-                                const OutView &dk, const OutView &dv, int force_fallback, hipStream_t s);
+                                const OutView &dk, const OutView &dv, int force_fallback, const ScoreFn *scores,
+                                hipStream_t s);
 
 // Capacity of the remainder list of one V preparation (entries of all heads);
 // heads whose remainders do not fit take the generic exact path.
