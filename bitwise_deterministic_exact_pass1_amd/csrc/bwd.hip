@@ -63,7 +63,8 @@ struct BwdArgs {
     int2 *st_rds, *st_cds, *st_cp, *st_k, *st_q, *st_o;
     v4i *xb[3];           // digit blocks of the right operands of dQ, dK, dV (K, Q, dO)
     int *xf[3];           // per (row tile, column group): 1 = left to k_bwd_sum
-    int64_t nIB, nJB, nG;
+    int64_t nIB, nJB, nG;          // 32-row tiles, 32-key tiles, 32-column groups (flags, per-term sums)
+    int64_t nIB64, nJB64, nG16;    // 64-step blocks and 16-column groups of the matrix-core sums
     int force_fallback;
     OutView dq;
 };
@@ -363,47 +364,47 @@ __global__ __launch_bounds__(256) void k_bwd_colstats(const void *src, int64_t s
 }
 
 // Digit blocks of the right operands of the matrix-core sums (K, Q, dO), one
-// wave per block of 32 operand columns d by 32 reduction steps t.  Lane l holds row x =
-// l % 32 at steps 16 (l / 32) + 0..15, the int8 operand order of
-// v_mfma_i32_32x32x32_i8.  Each row is an integer on its grid, Xi = X 2^-g_x,
-// written as n balanced base-256 digits (n of the block = the largest of its
-// rows): the bytes of Xi + 0x80..80 with their top bit flipped.  Blocks whose
-// rows need more digits than the kernel holds are not written (their tiles
-// take the per-term sums).
-//   MODE 3: B of dQ, unit (bhk, column group, key block): K[j][d], x = d
-//   MODE 4, 5: B of dK, dV, unit (bhk, column group, g, row block): Q / dO [i][d], x = d
+// wave per block of 16 operand columns d by 64 reduction steps t.  Lane l
+// holds column x = l % 16 at steps 16 (l / 16) + 0..15, the int8 operand
+// order of v_mfma_i32_16x16x64_i8.  Each column is an integer on its grid,
+// Xi = X 2^-g_x, written as n balanced base-256 digits (n of the block = the
+// largest of its columns): the bytes of Xi + 0x80..80 with their top bit
+// flipped.  Blocks whose columns need more digits than the kernel holds are
+// not written (their tiles take the per-term sums).
+//   MODE 3: B of dQ, unit (bhk, 16-column group, 64-key block): K[j][d]
+//   MODE 4, 5: B of dK, dV, unit (bhk, 16-column group, g, 64-row block): Q / dO [i][d]
 template <int MODE, typename T>
 __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
     const int lane = threadIdx.x & 63;
     const int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (u >= nunits) return;  // wave-uniform
-    const int xr = lane & 31, tb = 16 * (lane >> 5);
+    const int xr = lane & 15, tb = 16 * (lane >> 4);
     float val[16];
     int2 st = int2{INT_MIN, INT_MAX};
     int kmax;
     v4i *out;
     if (MODE == 3) {
-        const int64_t jb = u % A.nJB, G = (u / A.nJB) % A.nG, bhk = u / (A.nJB * A.nG);
-        const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, d = G * 32 + xr;
+        const int64_t jb = u % A.nJB64, G = (u / A.nJB64) % A.nG16, bhk = u / (A.nJB64 * A.nG16);
+        const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, d = G * 16 + xr;
         if (d < A.D) st = A.st_k[bhk * A.D + d];
         const int64_t base = b * A.ksB + hk * A.ksH + (d < A.D ? d : 0);
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
-            const int64_t j = jb * 32 + tb + p;
+            const int64_t j = jb * 64 + tb + p;
             const float x = ld<T>(A.k, base + min64(j, A.Skv - 1) * A.ksS);
             val[p] = (d < A.D && j < A.Skv) ? x : 0.0f;
         }
         kmax = kXB;
         out = A.xb[0] + u * kXB * 64;
     } else {
-        const int64_t ib = u % A.nIB, g = (u / A.nIB) % A.group, G = (u / (A.nIB * A.group)) % A.nG,
-                      bhk = u / (A.nIB * A.group * A.nG);
-        const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, hq = hk * A.group + g, d = G * 32 + xr;
+        const int64_t ib = u % A.nIB64, g = (u / A.nIB64) % A.group, G = (u / (A.nIB64 * A.group)) % A.nG16,
+                      bhk = u / (A.nIB64 * A.group * A.nG16);
+        const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, hq = hk * A.group + g, d = G * 16 + xr;
         if (d < A.D) st = (MODE == 4 ? A.st_q : A.st_o)[bhk * A.D + d];
         const int64_t dd = d < A.D ? d : 0;
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
-            const int64_t ir = ib * 32 + tb + p, i = A.i0 + min64(ir, A.ni - 1);
+            const int64_t ir = ib * 64 + tb + p, i = A.i0 + min64(ir, A.ni - 1);
             const float x = MODE == 4 ? ld<T>(A.q, b * A.qsB + hq * A.qsH + i * A.qsS + dd)
                                       : A.dout[b * A.dsB + hq * A.dsH + i * A.dsS + dd];
             val[p] = (d < A.D && ir < A.ni) ? x : 0.0f;
@@ -441,85 +442,95 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
     }
 }
 
-// The matrix-core sums of one 32 x 32 output tile per wave (four column
-// groups per workgroup): C_s += A_a x B_b (s = a + b) over the reduction
-// blocks on v_mfma_i32_32x32x32_i8, exact in int32 (|a_a b_b| <= 2^14, at most
-// seven pairs per class and step, classes carried every kXCarry blocks; the
-// top class only ever holds the product of the two top digits, each at most
-// 2^6), then the exact sum X = sum_s 256^s C_s (|X| < 2^125) times
-// 2^(ga_x + gb_d):
-//   MODE 0 (dQ): grid (column groups / 4, row tiles, bh); the tile owns every
+// The matrix-core sums.  A workgroup of eight waves owns 32 rows x 64
+// columns of one head's outputs; wave w takes the 16 x 16 tile of row half
+// w & 1 and 16-column group w >> 1.  C_s += A_a x B_b (s = a + b) over the
+// 64-step reduction blocks on v_mfma_i32_16x16x64_i8, exact in int32
+// (|a_a b_b| <= 2^14, at most seven pairs per class and step, classes carried
+// every 8192 steps; the top class only ever holds the product of the two top
+// digits, each at most 2^6), then the exact sum X = sum_s 256^s C_s
+// (|X| < 2^125) times 2^(ga_x + gb_d):
+//   MODE 0 (dQ): grid (64-column groups, 32-row tiles, bh); the tile owns every
 //     key, so dQ = RN32(RN64(scale RN64(X 2^e))) is stored directly;
-//   MODE 1, 2 (dK, dV): grid (column groups / 4, key tiles, bhk * group); the
-//     workgroup covers one query head's rows of the chunk and adds X 2^e into
-//     the digit planes (integer atomics: any order gives the same digits).
-// The A digits of a block are common to the four waves and staged through
-// LDS (double buffered, one barrier per block); each wave keeps its column
-// group's B digits in registers, fetched one block ahead.  A tile whose rows
-// or columns need more digits than the kernel holds is flagged for k_bwd_sum
-// and left alone here.
+//   MODE 1, 2 (dK, dV): grid (64-column groups, 32-key tiles, bhk * group);
+//     the workgroup covers one query head's rows of the chunk and adds X 2^e
+//     into the digit planes (integer atomics: any order gives the same digits).
+// The left operand's digits are made here from the f32 ds / p of each block
+// and shared by the eight waves through LDS (double buffered, one barrier per
+// block); each wave keeps its B digits in registers, fetched one block ahead.
+// Thirteen classes of a 16 x 16 tile take 52 registers, so two waves share a
+// SIMD.  A tile whose rows or 32-column group need more digits than the kernel
+// holds is flagged for k_bwd_sum (flags per 32 x 32 tile) and left alone.
+constexpr int kT16 = 64;                 // reduction steps per block
+constexpr int kXCarry16 = 8192 / kT16;   // blocks between class carries
+
 template <int MODE>
-__global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
-    __shared__ v4i sA[2][kXA][64];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int64_t G = (int64_t)blockIdx.x * 4 + (tid >> 6);
-    const int x = lane & 31;
+__global__ __launch_bounds__(512) void k_bwd_mma(BwdArgs A) {
+    __shared__ v4i sA[2][kXA][2][64];  // [slot][digit][row half][lane]
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int rh = wv & 1;
+    const int64_t G16 = (int64_t)blockIdx.x * 4 + (wv >> 1), G32 = G16 >> 1;
     const int64_t y = blockIdx.y, z = blockIdx.z;
-    const int64_t d = G * 32 + x;
-    int2 sa = int2{INT_MIN, INT_MAX}, sb = int2{INT_MIN, INT_MAX};
+    const int64_t d = G16 * 16 + (lane & 15);
+    int2 sa = int2{INT_MIN, INT_MAX}, sb = int2{INT_MIN, INT_MAX}, sb32 = int2{INT_MIN, INT_MAX};
     int64_t bh = 0, bhk, g = 0, nblk, k0;
     const v4i *pb;
     int *flag;
-    if (MODE == 0) {
-        bh = z;
-        const int64_t b = bh / A.Hq, hk = (bh % A.Hq) / A.group, ir = y * 32 + x;
-        bhk = b * A.Hkv + hk;
-        if (ir < A.ni) sa = A.st_rds[bh * A.ni + ir];
-        k0 = 0;
-        nblk = A.causal ? min64(A.nJB, (A.i0 + y * 32 + 31) / 32 + 1) : A.nJB;
-
-        pb = A.xb[0] + (bhk * A.nG + G) * A.nJB * kXB * 64;
-        flag = A.xf[0] + (bh * A.nIB + y) * A.nG + G;
-    } else {
-        bhk = z / A.group;
-        g = z % A.group;
-        const int64_t j = y * 32 + x;
-        if (j < A.Skv) sa = (MODE == 1 ? A.st_cds : A.st_cp)[bhk * A.Skv + j];
-        k0 = (A.causal && y * 32 > A.i0) ? (y * 32 - A.i0) / 32 : 0;
-        nblk = A.nIB;
-
-        pb = A.xb[MODE] + ((bhk * A.nG + G) * A.group + g) * A.nIB * kXB * 64;
-        flag = A.xf[MODE] + (bhk * A.nJB + y) * A.nG + G;
+    {
+        const int x32 = lane & 31;  // rows 0..31 of the tile, for the tile's digit count
+        if (MODE == 0) {
+            bh = z;
+            const int64_t b = bh / A.Hq, hk = (bh % A.Hq) / A.group, ir = y * 32 + x32;
+            bhk = b * A.Hkv + hk;
+            if (ir < A.ni) sa = A.st_rds[bh * A.ni + ir];
+            k0 = 0;
+            nblk = A.causal ? min64(A.nJB64, (A.i0 + y * 32 + 31) / kT16 + 1) : A.nJB64;
+            pb = A.xb[0] + (bhk * A.nG16 + G16) * A.nJB64 * kXB * 64;
+            flag = A.xf[0] + (bh * A.nIB + y) * A.nG + G32;
+        } else {
+            bhk = z / A.group;
+            g = z % A.group;
+            const int64_t j = y * 32 + x32;
+            if (j < A.Skv) sa = (MODE == 1 ? A.st_cds : A.st_cp)[bhk * A.Skv + j];
+            k0 = (A.causal && y * 32 > A.i0) ? (y * 32 - A.i0) / kT16 : 0;
+            nblk = A.nIB64;
+            pb = A.xb[MODE] + ((bhk * A.nG16 + G16) * A.group + g) * A.nIB64 * kXB * 64;
+            flag = A.xf[MODE] + (bhk * A.nJB + y) * A.nG + G32;
+        }
     }
-    const bool mine = G < A.nG;  // wave-uniform: the wave has a column group
-    if (mine && d < A.D) sb = (MODE == 0 ? A.st_k : MODE == 1 ? A.st_q : A.st_o)[bhk * A.D + d];
-    int ga, na, gb, nb;
+    const int2 *stb = MODE == 0 ? A.st_k : MODE == 1 ? A.st_q : A.st_o;
+    const bool mine = G16 < A.nG16;  // wave-uniform: the wave has columns
+    if (mine && d < A.D) sb = stb[bhk * A.D + d];
+    const int64_t d32 = G32 * 32 + (lane & 31);
+    if (G32 < A.nG && d32 < A.D) sb32 = stb[bhk * A.D + d32];
+    int ga, na, gb, nb, gb32, nb32;
     grid_of(sa, ga, na);
     grid_of(sb, gb, nb);
+    grid_of(sb32, gb32, nb32);
     const int nat = __builtin_amdgcn_readfirstlane(wave_max(na));  // the same in every wave
     const int nbt = __builtin_amdgcn_readfirstlane(wave_max(nb));
+    const int nbg = __builtin_amdgcn_readfirstlane(wave_max(nb32));  // the 32-column group's count
     const bool abad = A.force_fallback || nat > kXA || (MODE == 0 ? A.Skv : A.ni) > kXMaxT;
-    const bool bad = abad || nbt > kXB || nat + nbt > kXC + 1;
-    if (mine && (MODE == 0 || g == 0) && lane == 0) *flag = bad ? 1 : 0;
+    const bool bad = abad || nbg > kXB || nat + nbg > kXC + 1;
+    if (G32 < A.nG && (G16 & 1) == 0 && rh == 0 && (MODE == 0 || g == 0) && lane == 0) *flag = bad ? 1 : 0;
     if (abad) return;  // workgroup-uniform
     const bool run = mine && !bad && nbt > 0;  // wave-uniform
-    if (nat == 0) nblk = k0;                   // a zero operand: X = 0
+    if (nat == 0) nblk = k0;  // a zero operand: X = 0
 
-    v16i C[kXC];
+    v4i C[kXC];
 #pragma unroll
-    for (int s = 0; s < kXC; ++s) C[s] = v16i{0};
-    // the block's A digits: nat * 64 v4i, at most three per thread
-    // The left operand's digits are made here from the f32 ds / p of the
-    // block: thread tid holds 4 consecutive steps t0..t0+3 of one operand row
-    // xa (dQ: xa = tid / 8, the 4 keys are adjacent in memory; dK, dV: xa =
-    // tid % 32, the 4 query rows are adjacent in the A layout and each load
-    // is coalesced over the lanes), converts them on the row's grid and writes
-    // one 32-bit word per digit plane into the LDS operand image (lane xa +
-    // 32 (t0 / 16), bytes t0 % 16 ..).
-    const int xa = MODE == 0 ? (tid >> 3) : (tid & 31), t0 = MODE == 0 ? 4 * (tid & 7) : 4 * (tid >> 5);
+    for (int s = 0; s < kXC; ++s) C[s] = v4i{0, 0, 0, 0};
+    // The left operand's digits, made from the f32 ds / p of each block:
+    // thread tid holds 4 consecutive steps t0..t0+3 of operand row xa (dQ:
+    // xa = tid / 16, the 4 keys adjacent in memory; dK, dV: xa = tid % 32, the
+    // 4 query rows adjacent in the operand and each load coalesced over the
+    // lanes), converts them on the row's grid and writes its 32-bit word of
+    // every digit plane of the LDS operand image (half xa / 16, lane xa % 16 +
+    // 16 (t0 / 16), bytes t0 % 16 ..).
+    const int xa = MODE == 0 ? (tid >> 4) : (tid & 31), t0 = MODE == 0 ? 4 * (tid & 15) : 4 * (tid >> 5);
     int gx;
-    const float *srow;  // this thread's operand row (or column) of ds / p
-    int64_t sstep;      // elements between consecutive steps t
+    const float *srow;
+    int64_t sstep;
     bool xok;
     {
         int2 st = int2{INT_MIN, INT_MAX};
@@ -542,8 +553,8 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
     auto fetch_a = [&](int64_t kb, float (&av)[4]) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // step t of block kb: key (dQ) or chunk row (dK, dV) kb*32 + t0 + e
-            const int64_t t = kb * 32 + t0 + e;
+            // step t of block kb: key (dQ) or chunk row (dK, dV) kb*64 + t0 + e
+            const int64_t t = kb * kT16 + t0 + e;
             const int64_t tmax = MODE == 0 ? A.Skv - 1 : A.ni - 1;
             const float x = srow[(t < tmax ? t : tmax) * sstep];
             bool vis = xok && t <= tmax;
@@ -559,9 +570,10 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
     // are the bytes of w ^ 0x80808080, then the carry, and 0 elsewhere.  Each
     // thread zeroes its own word of every digit plane and stores its entries'
     // nonzero digits as bytes (same thread: the stores land in order).
+    const int wofs = (((xa >> 4) * 64) + (xa & 15) + 16 * (t0 >> 4)) * 4 + ((t0 & 15) >> 2);  // in uint32
     auto stash_a = [&](int buf, const float (&av)[4]) {
-        uint32_t *wb = (uint32_t *)&sA[buf][0][0] + (xa + 32 * (t0 >> 4)) * 4 + ((t0 & 15) >> 2);
-        for (int a = 0; a < nat; ++a) wb[a * 256] = 0u;
+        uint32_t *wb = (uint32_t *)&sA[buf][0][0][0] + wofs;
+        for (int a = 0; a < nat; ++a) wb[a * 512] = 0u;
         uint8_t *bb = (uint8_t *)wb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -578,47 +590,47 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
             const bool carry = !neg && w < x;  // the add wrapped past 2^32
 #pragma unroll
             for (int k = 0; k < 4; ++k)  // (q >= 0 by the grid; the bounds keep every store in the slot)
-                if (q + k >= 0 && q + k < nat) bb[(q + k) * 1024 + e] = (uint8_t)(dg >> (8 * k));
-            if (carry && q + 4 >= 0 && q + 4 < nat) bb[(q + 4) * 1024 + e] = 1;
+                if (q + k >= 0 && q + k < nat) bb[(q + k) * 2048 + e] = (uint8_t)(dg >> (8 * k));
+            if (carry && q + 4 >= 0 && q + 4 < nat) bb[(q + 4) * 2048 + e] = 1;
         }
     };
-    v4i B0[kXB], B1[kXB];
-    auto fetch_b = [&](int64_t kb, v4i (&Br)[kXB]) {
+    // the wave's B digits of a block are loaded at the start of its step
+    // (other waves on the SIMD cover the latency: two workgroups per CU)
+    v4i Bc[kXB];
+    auto fetch_b = [&](int64_t kb) {
         if (!run) return;
         const v4i *q = pb + kb * kXB * 64 + lane;
 #pragma unroll
         for (int b = 0; b < kXB; ++b)
-            if (b < nbt) Br[b] = q[b * 64];
+            if (b < nbt) Bc[b] = q[b * 64];
     };
     // step kb: block kb's digits in slot (kb - k0) & 1; block kb + 1's f32
-    // values and the wave's B digits are fetched first and its digits made
-    // after the products of block kb
+    // values are fetched first and its digits made after the products of
+    // block kb
     float F[4];
-    auto step = [&](int64_t kb, const v4i (&Bc)[kXB], v4i (&Bn)[kXB]) {
+    auto step = [&](int64_t kb) {
         const int buf = (int)((kb - k0) & 1);
         const bool more = kb + 1 < nblk;
-        if (more) {
-            fetch_a(kb + 1, F);
-            fetch_b(kb + 1, Bn);
-        }
+        fetch_b(kb);
+        if (more) fetch_a(kb + 1, F);
         if (run) {
-            const v4i *sa_ = &sA[buf][0][lane];
+            const v4i *sa_ = &sA[buf][0][rh][lane];
             v4i Acur = sa_[0];
 #pragma unroll
             for (int a = 0; a < kXA; ++a) {
                 if (a < nat) {
-                    const v4i Anext = sa_[((a + 1) % kXA) * 64];  // digit a+1 read while a's products run
+                    const v4i Anext = sa_[((a + 1) % kXA) * 128];  // digit a+1 read while a's products run
 #pragma unroll
                     for (int b = 0; b < kXB; ++b)
                         if (a + b < kXC && b < nbt)
-                            C[a + b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Acur, Bc[b], C[a + b], 0, 0, 0);
+                            C[a + b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Acur, Bc[b], C[a + b], 0, 0, 0);
                     Acur = Anext;
                 }
             }
-            if (((kb - k0) % kXCarry) == kXCarry - 1) {
+            if (((kb - k0) % kXCarry16) == kXCarry16 - 1) {
 #pragma unroll
                 for (int s = 0; s < kXC - 1; ++s) {
-                    const v16i c = C[s] >> 8;
+                    const v4i c = C[s] >> 8;
                     C[s] -= c << 8;
                     C[s + 1] += c;
                 }
@@ -629,37 +641,33 @@ __global__ __launch_bounds__(256) void k_bwd_mma(BwdArgs A) {
     };
     if (k0 < nblk) {
         fetch_a(k0, F);
-        fetch_b(k0, B0);
         stash_a(0, F);
     }
     __syncthreads();
-    for (int64_t kb = k0; kb < nblk; kb += 2) {
-        step(kb, B0, B1);
-        if (kb + 1 < nblk) step(kb + 1, B1, B0);
-    }
+    for (int64_t kb = k0; kb < nblk; ++kb) step(kb);
     if (!mine || bad) return;
     // classes to bytes: C_0 .. C_11 in [0, 256), C_12 signed
 #pragma unroll
     for (int s = 0; s < kXC - 1; ++s) {
-        const v16i c = C[s] >> 8;
+        const v4i c = C[s] >> 8;
         C[s] &= 255;
         C[s + 1] += c;
     }
-    int gam[16];
+    int gam[4];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) gam[rr] = __shfl(ga, 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3), 64);
+    for (int r = 0; r < 4; ++r) gam[r] = __shfl(ga, rh * 16 + 4 * (lane >> 4) + r, 64);
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-        const int m = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-        const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) | ((uint32_t)C[2][rr] << 16) |
-                            ((uint32_t)C[3][rr] << 24);
-        const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) | ((uint32_t)C[6][rr] << 16) |
-                            ((uint32_t)C[7][rr] << 24);
-        const uint32_t l2 = (uint32_t)C[8][rr] | ((uint32_t)C[9][rr] << 8) | ((uint32_t)C[10][rr] << 16) |
-                            ((uint32_t)C[11][rr] << 24);
+    for (int r = 0; r < 4; ++r) {
+        const int m = rh * 16 + 4 * (lane >> 4) + r;  // row of the 32-row tile
+        const uint32_t l0 = (uint32_t)C[0][r] | ((uint32_t)C[1][r] << 8) | ((uint32_t)C[2][r] << 16) |
+                            ((uint32_t)C[3][r] << 24);
+        const uint32_t l1 = (uint32_t)C[4][r] | ((uint32_t)C[5][r] << 8) | ((uint32_t)C[6][r] << 16) |
+                            ((uint32_t)C[7][r] << 24);
+        const uint32_t l2 = (uint32_t)C[8][r] | ((uint32_t)C[9][r] << 8) | ((uint32_t)C[10][r] << 16) |
+                            ((uint32_t)C[11][r] << 24);
         const uint64_t lo = ((uint64_t)l1 << 32) | l0;
-        const int64_t hi = (int64_t)C[12][rr] * ((int64_t)1 << 32) + (int64_t)l2;
-        const int e = gam[rr] + gb;
+        const int64_t hi = (int64_t)C[12][r] * ((int64_t)1 << 32) + (int64_t)l2;
+        const int e = gam[r] + gb;
         if (d >= A.D) continue;
         if (MODE == 0) {
             const int64_t ir = y * 32 + m;
@@ -829,6 +837,7 @@ size_t bwd_fixed_bytes(const AttnGeom &g) {
 static size_t bwd_chunk_layout(const AttnGeom &g, int64_t ni, BwdArgs *A, char *base) {
     const int64_t bh = g.B * g.Hq, bhk = g.B * g.Hkv, grp = g.Hq / g.Hkv;
     const int64_t nIB = (ni + 31) / 32, nJB = (g.Skv + 31) / 32, nG = (g.D + 31) / 32;
+    const int64_t nIB64 = (ni + kT16 - 1) / kT16, nJB64 = (g.Skv + kT16 - 1) / kT16, nG16 = (g.D + 15) / 16;
     size_t at = 0;
     auto take = [&](size_t bytes) {
         char *p = base ? base + at : nullptr;
@@ -838,9 +847,9 @@ static size_t bwd_chunk_layout(const AttnGeom &g, int64_t ni, BwdArgs *A, char *
     char *P = take((size_t)bh * ni * g.Skv * 4);
     char *DS = take((size_t)bh * ni * g.Skv * 4);
     char *st = take((size_t)(bh * ni + 2 * bhk * g.Skv + 3 * bhk * g.D) * 8);
-    char *xb0 = take((size_t)kXB * 1024 * bhk * nG * nJB);
-    char *xb1 = take((size_t)kXB * 1024 * bhk * nG * grp * nIB);
-    char *xb2 = take((size_t)kXB * 1024 * bhk * nG * grp * nIB);
+    char *xb0 = take((size_t)kXB * 1024 * bhk * nG16 * nJB64);
+    char *xb1 = take((size_t)kXB * 1024 * bhk * nG16 * grp * nIB64);
+    char *xb2 = take((size_t)kXB * 1024 * bhk * nG16 * grp * nIB64);
     char *fl = take((size_t)(bh * nIB * nG + 2 * bhk * nJB * nG) * 4);
     if (A) {
         A->P = (float *)P;
@@ -861,6 +870,9 @@ static size_t bwd_chunk_layout(const AttnGeom &g, int64_t ni, BwdArgs *A, char *
         A->nIB = nIB;
         A->nJB = nJB;
         A->nG = nG;
+        A->nIB64 = nIB64;
+        A->nJB64 = nJB64;
+        A->nG16 = nG16;
     }
     return at;
 }
@@ -889,7 +901,7 @@ static hipError_t launch_sums(BwdArgs &A, const AttnGeom &g, const Tensor &q, co
                            A.i0 + A.ni, g.D, A.st_q);
         hipLaunchKernelGGL(k_bwd_colstats<float>, gq, dim3(256), 0, s, dout.data, dout.sB, dout.sH, dout.sS, grp,
                            g.Hkv, A.i0, A.i0 + A.ni, g.D, A.st_o);
-        const int64_t u3 = bhk * nG * nJB, u4 = bhk * nG * grp * nIB;
+        const int64_t u3 = bhk * A.nG16 * A.nJB64, u4 = bhk * A.nG16 * grp * A.nIB64;
         hipLaunchKernelGGL((k_bwd_slice<3, T>), dim3(blocks_of(u3 * 64)), dim3(256), 0, s, A, u3);
         hipLaunchKernelGGL((k_bwd_slice<4, T>), dim3(blocks_of(u4 * 64)), dim3(256), 0, s, A, u4);
         hipLaunchKernelGGL((k_bwd_slice<5, T>), dim3(blocks_of(u4 * 64)), dim3(256), 0, s, A, u4);
@@ -898,10 +910,10 @@ static hipError_t launch_sums(BwdArgs &A, const AttnGeom &g, const Tensor &q, co
     }
     {
         ProfScope prof_("bwd_mma", s);
-        const unsigned gx = (unsigned)((nG + 3) / 4);
-        hipLaunchKernelGGL(k_bwd_mma<0>, dim3(gx, (unsigned)nIB, (unsigned)bh), dim3(256), 0, s, A);
-        hipLaunchKernelGGL(k_bwd_mma<1>, dim3(gx, (unsigned)nJB, (unsigned)(bhk * grp)), dim3(256), 0, s, A);
-        hipLaunchKernelGGL(k_bwd_mma<2>, dim3(gx, (unsigned)nJB, (unsigned)(bhk * grp)), dim3(256), 0, s, A);
+        const unsigned gx = (unsigned)((A.nG16 + 3) / 4);
+        hipLaunchKernelGGL(k_bwd_mma<0>, dim3(gx, (unsigned)nIB, (unsigned)bh), dim3(512), 0, s, A);
+        hipLaunchKernelGGL(k_bwd_mma<1>, dim3(gx, (unsigned)nJB, (unsigned)(bhk * grp)), dim3(512), 0, s, A);
+        hipLaunchKernelGGL(k_bwd_mma<2>, dim3(gx, (unsigned)nJB, (unsigned)(bhk * grp)), dim3(512), 0, s, A);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -970,6 +982,7 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
         A.i0 = i0;
         A.ni = std::min(chunk, g.Sq - i0);
         A.nIB = (A.ni + 31) / 32;  // the chunk's row blocks (the layout is carved for the largest chunk)
+        A.nIB64 = (A.ni + kT16 - 1) / kT16;
         const int64_t rt = (A.ni + kBT - 1) / kBT;
         const int64_t nst = bh * chunk + 2 * bhk * g.Skv + 3 * bhk * g.D;  // the carved statistics
         if ((e = launch_fill_i64((int64_t *)A.st_rds, nst, kStatEmpty, s)) != hipSuccess) return e;
