@@ -141,7 +141,9 @@ constexpr int kPdsLd = kPdsT + 2;  // row stride of the staged arrays (16-byte a
 
 template <typename T, bool SC>
 __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
-    __shared__ __align__(16) double sm[4][kPdsDc][kPdsLd];  // Q, K, dO, V
+    constexpr int AO = SC ? 2 : 0;  // first staged array: Q, K, dO, V (with stored scores dO, V)
+    constexpr int NR = SC ? 16 : 32;  // staged rows per lane and stage
+    __shared__ __align__(16) double sm[4 - AO][kPdsDc][kPdsLd];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int tr = tid >> 4, tc = tid & 15;
     const int64_t kt = blockIdx.x, rt = blockIdx.y, bh = blockIdx.z;
@@ -149,7 +151,8 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
     const int64_t iend = A.i0 + A.ni, ia = A.i0 + rt * kPdsT, ja = kt * kPdsT;
     const int64_t ilast = min64(iend, ia + kPdsT) - 1;
     if (A.causal && ja > ilast) return;
-    // wave wv stages array wv: lane handles dimension d0 + lane % 32 of rows
+    // wave wv stages array wv (with stored scores: array 2 + wv / 2, rows
+    // 32 (wv % 2) ..): lane handles dimension d0 + lane % 32 of rows
     // 2 r2 + lane / 32 (clamped into range; such rows are never stored), so
     // each load instruction reads two rows' contiguous dimensions; the next
     // stage's values are fetched into registers while this stage computes
@@ -157,27 +160,29 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
     int64_t base, rs;
     int64_t r0, rmax;
     bool isf32 = false;
-    switch (wv) {
+    const int arr = SC ? 2 + (wv >> 1) : wv, rofs = SC ? 32 * (wv & 1) : 0;
+    switch (arr) {
         case 0: src = A.q; base = b * A.qsB + hq * A.qsH; rs = A.qsS; r0 = ia; rmax = iend - 1; break;
         case 1: src = A.k; base = b * A.ksB + hk * A.ksH; rs = A.ksS; r0 = ja; rmax = A.Skv - 1; break;
         case 2: src = A.dout; base = b * A.dsB + hq * A.dsH; rs = A.dsS; r0 = ia; rmax = iend - 1; isf32 = true; break;
         default: src = A.v; base = b * A.vsB + hk * A.vsH; rs = A.vsS; r0 = ja; rmax = A.Skv - 1; break;
     }
+    r0 += rofs;
     const int D = (int)A.D, dl = lane & 31, rh = lane >> 5;
     // all 32 loads of a stage are issued before any is used: in-range
     // (clamped) addresses, one element width per wave, no branches
     const bool w32 = __builtin_amdgcn_readfirstlane((int)(isf32 || sizeof(T) == 4)) != 0;
-    uint32_t nx[32];
+    uint32_t nx[NR];
     auto gload = [&](int d0) {
         const int64_t d = min(d0 + dl, D - 1);
         if (w32) {
             const uint32_t *p = (const uint32_t *)src + base + d;
 #pragma unroll
-            for (int r2 = 0; r2 < 32; ++r2) nx[r2] = p[min64(r0 + 2 * r2 + rh, rmax) * rs];
+            for (int r2 = 0; r2 < NR; ++r2) nx[r2] = p[min64(r0 + 2 * r2 + rh, rmax) * rs];
         } else {
             const uint16_t *p = (const uint16_t *)src + base + d;
 #pragma unroll
-            for (int r2 = 0; r2 < 32; ++r2) nx[r2] = (uint32_t)p[min64(r0 + 2 * r2 + rh, rmax) * rs] << 16;
+            for (int r2 = 0; r2 < NR; ++r2) nx[r2] = (uint32_t)p[min64(r0 + 2 * r2 + rh, rmax) * rs] << 16;
         }
     };
     double as[4][4], ap[4][4];
@@ -185,20 +190,18 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
     for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int t = 0; t < 4; ++t) as[u][t] = ap[u][t] = 0.0;
-    const bool stage = !SC || wv >= 2;  // with stored scores only dO and V are staged
-    if (stage) gload(0);
+    gload(0);
     for (int d0 = 0; d0 < D; d0 += kPdsDc) {
         const int dn = min(kPdsDc, D - d0);
         __syncthreads();  // the previous stage's readers are done
         const bool dok = d0 + dl < D;
-        if (stage) {
 #pragma unroll
-            for (int r2 = 0; r2 < 32; ++r2) sm[wv][dl][2 * r2 + rh] = dok ? (double)__uint_as_float(nx[r2]) : 0.0;
-        }
+        for (int r2 = 0; r2 < NR; ++r2)
+            sm[arr - AO][dl][rofs + 2 * r2 + rh] = dok ? (double)__uint_as_float(nx[r2]) : 0.0;
         __syncthreads();
-        if (stage && d0 + kPdsDc < D) gload(d0 + kPdsDc);
+        if (d0 + kPdsDc < D) gload(d0 + kPdsDc);
         for (int dd = 0; dd < dn; ++dd) {
-            const double2 *ro = (const double2 *)&sm[2][dd][4 * tr], *rv = (const double2 *)&sm[3][dd][4 * tc];
+            const double2 *ro = (const double2 *)&sm[2 - AO][dd][4 * tr], *rv = (const double2 *)&sm[3 - AO][dd][4 * tc];
             const double2 o01 = ro[0], o23 = ro[1], v01 = rv[0], v23 = rv[1];
             const double ov[4] = {o01.x, o01.y, o23.x, o23.y}, vv[4] = {v01.x, v01.y, v23.x, v23.y};
             if (!SC) {
