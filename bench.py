@@ -265,9 +265,15 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     torch.cuda.synchronize()
     N, Vv = X.shape
     fwd_ms, bwd_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
+    # the per-element work model: forward 33 fp64 flops + 2 bytes, backward 36 flops + 6 bytes per
+    # (token, vocab); the ideal time is the larger of the fp64 and HBM times
+    fwd_ideal = max(N * Vv * 33 / (FP64_PEAK_TFLOPS * 1e12), N * Vv * 2 / (HBM_PEAK_GBS * 1e9))
+    bwd_ideal = max(N * Vv * 36 / (FP64_PEAK_TFLOPS * 1e12), N * Vv * 6 / (HBM_PEAK_GBS * 1e9))
     res["cross_entropy"] = {"workload": "N=4096 V=128256 bf16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                             "forward_token_vocab_per_s": N * Vv / (fwd_ms / 1e3),
-                            "backward_hbm_GBps": N * Vv * 6 / (bwd_ms / 1e3) / 1e9}
+                            "backward_hbm_GBps": N * Vv * 6 / (bwd_ms / 1e3) / 1e9,
+                            "forward_frac_of_roofline": fwd_ideal / (fwd_ms / 1e3),
+                            "backward_frac_of_roofline": bwd_ideal / (bwd_ms / 1e3)}
     res["backward"] = backward_measurement(attention, Q, K, V, causal, scale, pairs)
 
     # the float32 combines the exact path replaces, on the same inputs
