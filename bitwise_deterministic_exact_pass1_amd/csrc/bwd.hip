@@ -219,7 +219,24 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
                 for (int t = 0; t < 4; ++t) ap[u][t] = fma(ov[u], vv[t], ap[u][t]);
         }
     }
-    // p, ds and the exponent statistics for the matrix-core sums
+    // p, ds and the exponent statistics for the matrix-core sums.  The row
+    // statistics and (SC) the 16 stored scores are loaded together first, from
+    // in-range (clamped) addresses, so their latencies overlap.
+    float rm[4], sv[4][4];
+    double rden[4], rdelta[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t ic = min64(ia + 4 * tr + u, iend - 1);
+        const int64_t row = bh * A.Sq + ic;
+        rm[u] = A.rowmax[row];
+        rden[u] = A.den64[row];
+        rdelta[u] = A.delta[row];
+        if (SC) {
+            const float *sp = A.P + (bh * A.ni + (ic - A.i0)) * A.Skv;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sv[u][t] = sp[min64(ja + 4 * tc + t, A.Skv - 1)];
+        }
+    }
     int re[4], rl[4], ce[4], cl[4], pe[4], pl[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -230,9 +247,8 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
     for (int u = 0; u < 4; ++u) {
         const int64_t i = ia + 4 * tr + u;
         const bool rowok = i < iend;
-        const int64_t row = bh * A.Sq + (rowok ? i : A.i0);
-        const float m = A.rowmax[row];
-        const double den = A.den64[row], delta = A.delta[row];
+        const float m = rm[u];
+        const double den = rden[u], delta = rdelta[u];
         re[u] = INT_MIN;
         rl[u] = INT_MAX;
         float pv[4], dv[4];
@@ -242,7 +258,7 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
             float p = 0.0f, ds = 0.0f;
             if (rowok && j < A.Skv && (!A.causal || j <= i)) {
                 // the stored score (the matrix-core score path wrote it into P) or the chain's
-                const float s = SC ? A.P[(bh * A.ni + (i - A.i0)) * A.Skv + j] : (float)(A.scale * as[u][t]);
+                const float s = SC ? sv[u][t] : (float)(A.scale * as[u][t]);
                 const float w = weight(s, m);
                 p = (float)((double)w / den);
                 ds = (float)((double)p * (ap[u][t] - delta));
