@@ -257,3 +257,31 @@ def test_backward_strided_nhd_views_and_strided_upstream(A, oracle):
     got = A.det_attn_backward(Qd, Kd, Vd, out, dOd, m, den, True, scale)
     for name, a, b in zip(("dq", "dk", "dv"), got, ref):
         assert_bits_equal(a, b, name)
+
+
+def test_backward_empty_ranges(A):
+    """No keys: every dQ is +0 (no term); no queries: dK and dV are +0 and the
+    call launches nothing else.  Non-causal, so the shapes may differ."""
+    import ctypes as C
+    from bitwise_deterministic_exact_pass1_amd import _lib
+    L = _lib.lib()
+    for Sq, Skv in ((5, 0), (0, 7)):
+        q = torch.randn(1, 2, Sq, 8).to(torch.bfloat16).cuda()
+        k = torch.randn(1, 1, Skv, 8).to(torch.bfloat16).cuda()
+        v = torch.randn(1, 1, Skv, 8).to(torch.bfloat16).cuda()
+        o = torch.zeros(1, 2, Sq, 8, device="cuda")
+        dO = torch.randn(1, 2, Sq, 8).cuda()
+        m = torch.full((1, 2, Sq), float("-inf"), device="cuda")
+        den = torch.zeros(1, 2, Sq, dtype=torch.float64, device="cuda")
+        g = [torch.full(t.shape, 7.0, device="cuda") for t in (q, k, v)]  # sentinels
+        dq_, dk_, dv_ = A._desc(q), A._desc(k), A._desc(v)
+        n = L.det_attn_backward_workspace_size(C.byref(dq_), C.byref(dk_), C.byref(dv_), 0)
+        ws = torch.empty(max(n, 256) + 256, dtype=torch.uint8, device="cuda")
+        addr = (ws.data_ptr() + 255) & ~255
+        _lib.check(L.det_attn_backward(C.byref(dq_), C.byref(dk_), C.byref(dv_), C.byref(A._desc(o)),
+                                       C.byref(A._desc(dO)), m.data_ptr(), den.data_ptr(), 0, 0.25,
+                                       C.byref(A._out(g[0])), C.byref(A._out(g[1])), C.byref(A._out(g[2])),
+                                       addr, max(n, 256), A._stream(q)))
+        torch.cuda.synchronize()
+        for t in g:
+            assert not t.any() and not torch.signbit(t).any()
