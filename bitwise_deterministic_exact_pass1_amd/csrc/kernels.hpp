@@ -87,8 +87,9 @@ hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, in
 // ---- attention backward (bwd.hip)
 constexpr int kBwdDigits = 18;   // radix-2^32 digits of a gradient sum (products of two f32 values)
 constexpr int kBwdElo = -298;    // their lsb exponent
-// delta and the dK / dV digit planes (whole problem) / P, DS and the dQ digit
-// planes of a chunk of ni query rows
+// delta and the dK / dV digit planes (whole problem) / per chunk of ni query
+// rows: p and ds, the exponent statistics, the right operands' digit slices and
+// the per-tile flags
 size_t bwd_fixed_bytes(const AttnGeom &g);
 size_t bwd_chunk_bytes(const AttnGeom &g, int64_t ni);
 hipError_t launch_zero_view(const OutView &o, int64_t B, int64_t H, int64_t S, int64_t D, hipStream_t s);
