@@ -1,0 +1,89 @@
+"""Seeded random sweeps on the GPU: shapes (head dims 1..256, GQA ratios 1/2/4,
+ragged sequence lengths, causal or not, f32 or bf16), input scales, single
+entries far outside their row's or column's range (so that some tiles take
+the generic or per-term exact paths), random KV splits and composition
+orders, and the forced generic paths.  Every forward output and gradient
+must equal the CPU oracle bit for bit, and every sharded composition must
+equal the fused output."""
+import os
+import random
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from bitwise_deterministic_exact_pass1_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DIMS = [1, 3, 8, 16, 17, 32, 40, 64, 96, 100, 128, 129, 200, 256]
+
+
+@pytest.fixture(scope="module")
+def A():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    from bitwise_deterministic_exact_pass1_amd import attention
+    return attention
+
+
+def _case(rng, max_s):
+    B, Hkv, grp = rng.choice([1, 2]), rng.choice([1, 2]), rng.choice([1, 2, 4])
+    causal = rng.random() < 0.5
+    Sq = rng.randint(1, max_s)
+    Skv = Sq if causal else rng.randint(1, max_s)
+    D = rng.choice(DIMS)
+    dt = rng.choice([torch.bfloat16, torch.float32])
+    gen = torch.Generator().manual_seed(rng.randint(0, 10**6))
+    q = torch.randn(B, Hkv * grp, Sq, D, generator=gen) * rng.choice([0.25, 1.0, 3.0])
+    k = torch.randn(B, Hkv, Skv, D, generator=gen) * rng.choice([0.25, 1.0, 3.0])
+    v = torch.randn(B, Hkv, Skv, D, generator=gen)
+    dO = torch.randn(B, Hkv * grp, Sq, D, generator=gen) * rng.choice([1e-3, 1.0, 50.0])
+    if rng.random() < 0.3:
+        q[0, 0, rng.randrange(Sq), rng.randrange(D)] *= 2.0 ** rng.choice([-40, -20, 6])
+        v[0, 0, rng.randrange(Skv), rng.randrange(D)] *= 2.0 ** rng.choice([-40, -20, 8])
+        dO[0, 0, rng.randrange(Sq), rng.randrange(D)] *= 2.0 ** rng.choice([-40, -20, 20])
+    return q.to(dt), k.to(dt), v.to(dt), dO, causal, W.default_scale(D)
+
+
+def _bits(x):
+    return np.ascontiguousarray(x.cpu().numpy() if isinstance(x, torch.Tensor) else x, np.float32).view(np.uint32)
+
+
+@pytest.mark.parametrize("seed", [101, 102])
+def test_sweep_forward_and_shards(A, oracle, seed):
+    rng = random.Random(seed)
+    for c in range(20):
+        q, k, v, _, causal, scale = _case(rng, 300)
+        Skv = k.shape[2]
+        tag = f"seed {seed} case {c}: q {tuple(q.shape)} k {tuple(k.shape)} {q.dtype} causal={causal}"
+        print(tag, file=sys.stderr, flush=True)
+        Q, K, V = q.cuda(), k.cuda(), v.cuda()
+        out = A.det_attn(Q, K, V, causal, scale)
+        assert np.array_equal(_bits(out), _bits(oracle.det_attn(q, k, v, causal, scale))), tag
+        cuts = sorted(rng.sample(range(1, Skv), min(rng.randint(0, 5), Skv - 1))) if Skv > 1 else []
+        splits = [b - a for a, b in zip([0] + cuts, cuts + [Skv])]
+        order = list(range(len(splits)))
+        rng.shuffle(order)
+        assert torch.equal(A.det_attn_sharded(Q, K, V, splits, causal=causal, scale=scale, order=order), out), tag
+
+
+@pytest.mark.parametrize("seed", [201, 202])
+def test_sweep_backward(A, oracle, seed):
+    rng = random.Random(seed)
+    for c in range(20):
+        q, k, v, dO, causal, scale = _case(rng, 200)
+        force = rng.random() < 0.15
+        tag = f"seed {seed} case {c}: q {tuple(q.shape)} k {tuple(k.shape)} {q.dtype} causal={causal} force={force}"
+        print(tag, file=sys.stderr, flush=True)
+        if force:
+            os.environ["DET_FORCE_FALLBACK"] = "1"
+        try:
+            Q, K, V = q.cuda(), k.cuda(), v.cuda()
+            out, m, den = A.det_attn_with_stats(Q, K, V, causal, scale)
+            got = A.det_attn_backward(Q, K, V, out, dO.cuda(), m, den, causal, scale)
+        finally:
+            os.environ.pop("DET_FORCE_FALLBACK", None)
+        ref = oracle.attn_backward(q, k, v, dO, causal, scale)
+        for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+            assert np.array_equal(_bits(a), _bits(b)), f"{tag}: {name}"
