@@ -298,6 +298,8 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
         pairs2 = q2.shape[0] * q2.shape[1] * Sx * (Sx + 1) // 2
         res[name] = {"workload": wl["desc"], "ms": ms2, "pairs_per_s": pairs2 / (ms2 / 1e3),
                      "frac_of_fp64_path_roofline": pairs2 * (6 * Dx + 32) / (ms2 / 1e3) / 1e12 / FP64_PEAK_TFLOPS}
+        if name == "cp_share_bf16":  # the exact backward at this share (query rows in several chunks)
+            res[name]["backward"] = backward_measurement(attention, q2, k2, v2, True, wl["scale"], pairs2, reps=2)
         del q2, k2, v2
     # the long non-causal share: one interleaved QKV buffer [37810, 21504] bf16, heads 56, D=128,
     # Q/K/V as strided NHD views, f32 output

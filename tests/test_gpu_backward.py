@@ -285,3 +285,37 @@ def test_backward_empty_ranges(A):
         torch.cuda.synchronize()
         for t in g:
             assert not t.any() and not torch.signbit(t).any()
+
+
+def test_backward_large_causal_share_chunks_both_paths_and_fp64(A):
+    """The causal share B=1 Hq=32 Hkv=8 S=8192 D=128 bf16: the default
+    workspace takes the query rows in several chunks; the matrix-core and
+    per-term sums must give the same bits, and the gradients must lie within
+    f32 rounding of fp64 autograd (computed on the GPU head by head)."""
+    wl = W.attn_workload("cp_share_bf16")
+    q, k, v, scale = wl["q"], wl["k"], wl["v"], wl["scale"]
+    dO = upstream(4343, tuple(q.shape))
+    say("backward S=8192 Hq=32: both paths")
+    fast, slow = _backward_both_paths(A, q, k, v, dO, True, scale)
+    for name, a, b in zip(("dq", "dk", "dv"), fast, slow):
+        assert_bits_equal(a, b, name)
+    say("backward S=8192 Hq=32: fp64 autograd per head group")
+    S, grp = q.shape[2], q.shape[1] // k.shape[1]
+    mask = ~torch.ones(S, S, dtype=torch.bool, device="cuda").tril()
+    ref = [torch.zeros(t.shape, dtype=torch.float64) for t in (q, k, v)]
+    for hk in range(k.shape[1]):
+        hs = slice(hk * grp, (hk + 1) * grp)
+        Q = q[:, hs].cuda().double().requires_grad_()
+        K = k[:, hk:hk + 1].cuda().double().requires_grad_()
+        V = v[:, hk:hk + 1].cuda().double().requires_grad_()
+        s = torch.matmul(Q, K.expand(-1, grp, -1, -1).transpose(-1, -2).contiguous()) * scale
+        torch.matmul(torch.softmax(s.masked_fill(mask, float("-inf")), -1), V.expand(-1, grp, -1, -1)).backward(
+            dO[:, hs].cuda().double())
+        ref[0][:, hs] = Q.grad.cpu()
+        ref[1][:, hk:hk + 1] = K.grad.cpu()
+        ref[2][:, hk:hk + 1] = V.grad.cpu()
+        del Q, K, V, s
+    for name, a, b in zip(("dq", "dk", "dv"), fast, ref):
+        err = (a.cpu().double() - b).abs().max().item()
+        tol = 2.0 ** -20 * (b.abs().max().item() + 1)
+        assert err <= tol, (name, err, tol)
