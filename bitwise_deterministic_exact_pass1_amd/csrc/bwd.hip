@@ -16,29 +16,27 @@
 //   dV_jd = RN32(RN64(sum p_ij dO_id)),  dK_jd = RN32(RN64(scale RN64(sum ds_ij Q_id))),
 //   dQ_id = RN32(RN64(scale RN64(sum ds_ij K_jd)))
 //
-// The sums are kept as 18 radix-2^32 digits from 2^-298: a workgroup owns a
-// 16 x 16 tile of outputs, each thread one output, whose digits live in LDS;
-// every product is split into three 32-bit limbs added to the digits it
-// spans (no carries until the end: 2^30 limbs of at most 2^32 stay below
-// 2^62), so the result does not depend on the order of the terms.
-//
 // The sums run on the int8 matrix cores where an exactness argument holds
-// (k_bwd_slice, k_bwd_mma below); an output tile outside it keeps the per-term
-// digit sums (k_bwd_sum).  Both give the same bits.
+// (k_bwd_colstats, k_bwd_slice, k_bwd_mma below: integer grids, balanced
+// base-256 digits, exact int32 class sums).  An output tile outside it takes
+// the per-term digit sums (k_bwd_sum): 18 radix-2^32 digits from 2^-298 per
+// output, each f32 x f32 product split into three 32-bit limbs added to the
+// digits it spans (no carries until the end: 2^30 limbs of at most 2^32 stay
+// below 2^62).  Both give the same bits, whatever the order of the terms.
+// dK and dV sums of all tiles end in digit planes (k_bwd_finalize rounds
+// them); dQ tiles own every key and are rounded where they are summed.
 #include "dev_math.hpp"
 #include "kernels.hpp"
 
 namespace det {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int kBT = 16;         // rows (or keys) and columns of a tile
 constexpr int kBStep = 32;      // reduction steps staged per barrier
 constexpr int kXA = 10;         // matrix-core sums: A digits at most (an 80-bit row span)
 constexpr int kXB = 7;          // B digits at most
 constexpr int kXC = 13;         // digit classes s = a + b; a tile needs na + nb <= kXC + 1
-constexpr int kXCarry = 256;    // 32-step blocks between carries of the classes
 constexpr int64_t kXMaxT = (int64_t)1 << 17;  // reduction length bound of the int32 class sums
 
 struct BwdArgs {
@@ -734,10 +732,12 @@ __device__ __forceinline__ void bwd_term(uint32_t ua, uint32_t ub, int64_t (*dig
     if (c2) atomicAdd(d + 512, (unsigned long long)c2);
 }
 
-// Exact sums for a 16 x 16 tile of outputs, one thread per output.
-//   MODE 0 (dQ): rows = chunk rows i of head bh, terms ds_ij K_jd over keys j
+// Per-term exact sums for a 16 x 16 tile of outputs, one thread per output,
+// for the tiles k_bwd_mma flagged (the others return at once).
+//   MODE 0 (dQ): rows = chunk rows i of head bh, terms ds_ij K_jd over keys j;
+//     the tile owns every key, so dQ is rounded and stored here
 //   MODE 1 (dK): rows = keys j of key head bhk, terms ds_ij Q_id over (query head, row)
-//   MODE 2 (dV): the same with p_ij dO_id
+//   MODE 2 (dV): the same with p_ij dO_id; both added into the digit planes
 // Grid (column tiles, row tiles, heads).  Per step 32 terms of the tile's
 // rows and columns are staged in LDS.
 template <int MODE, typename T>
