@@ -820,19 +820,26 @@ __global__ __launch_bounds__(256) void k_bwd_sum(BwdArgs A) {
     }
 }
 
-// out = RN32(RN64(f * RN64(X))) of each digit sum X (f = scale or 1); row R
-// of the planes is (head, s) = (R / S, R % S) of the output view.
-__global__ __launch_bounds__(256) void k_bwd_finalize(const int64_t *dig, int64_t rows, int64_t D, int64_t S,
-                                                      int64_t s_off, int64_t H, double f, OutView o) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= rows * D) return;
+// out = RN32(RN64(f * RN64(X))) of each digit sum X: dK (f = scale) from the
+// planes at dig0, then dV (f = 1) from those at dig1, one launch; row R of the
+// planes is (head, s) = (R / S, R % S) of the output view.
+__global__ __launch_bounds__(256) void k_bwd_finalize(const int64_t *dig0, const int64_t *dig1, int64_t rows,
+                                                      int64_t D, int64_t S, int64_t H, double f0, OutView o0,
+                                                      OutView o1) {
+    int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= 2 * rows * D) return;
+    const bool second = t >= rows * D;
+    if (second) t -= rows * D;
+    const int64_t *dig = second ? dig1 : dig0;
+    const double f = second ? 1.0 : f0;
+    const OutView o = second ? o1 : o0;
     const int64_t R = t / D, d = t % D;
     int64_t x[kBwdDigits];
 #pragma unroll
     for (int k = 0; k < kBwdDigits; ++k) x[k] = dig[k * rows * D + t];
     canonicalize<kBwdDigits>(x);
     const double v = digits_to_f64<kBwdDigits>(x, kBwdElo);
-    const int64_t head = R / S, s = s_off + R % S;
+    const int64_t head = R / S, s = R % S;
     o.data[(head / H) * o.sB + (head % H) * o.sH + s * o.sS + d] = (float)(f * v);
 }
 
@@ -989,8 +996,8 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
     bwd_chunk_layout(g, chunk, &A, (char *)chunk_ws);
     hipError_t e;
     const int64_t kvn = kBwdDigits * bhk * g.Skv * g.D;
-    if ((e = launch_fill_i64(A.dk_dig, kvn, 0, s)) != hipSuccess) return e;
-    if ((e = launch_fill_i64(A.dv_dig, kvn, 0, s)) != hipSuccess) return e;
+    // the dK and dV planes are adjacent (the second starts kvdig bytes after the first)
+    if ((e = launch_fill_i64(A.dk_dig, (int64_t)(kvdig / 8) + kvn, 0, s)) != hipSuccess) return e;
     {
         ProfScope prof_("bwd_delta", s);
         hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((rows + 63) / 64)), dim3(64), 0, s, A, rows);
@@ -1023,10 +1030,8 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
     }
     ProfScope prof_("bwd_finalize", s);
     const int64_t nk = bhk * g.Skv;
-    hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(nk * g.D)), dim3(256), 0, s, A.dk_dig, nk, g.D, g.Skv,
-                       (int64_t)0, g.Hkv, g.scale, dk);
-    hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(nk * g.D)), dim3(256), 0, s, A.dv_dig, nk, g.D, g.Skv,
-                       (int64_t)0, g.Hkv, 1.0, dv);
+    hipLaunchKernelGGL(k_bwd_finalize, dim3(blocks_of(2 * nk * g.D)), dim3(256), 0, s, (const int64_t *)A.dk_dig,
+                       (const int64_t *)A.dv_dig, nk, g.D, g.Skv, g.Hkv, g.scale, dk, dv);
     return hipGetLastError();
 }
 
