@@ -57,7 +57,8 @@ struct BwdArgs {
     // matrix-core sums of the chunk.  Statistics {largest exponent, smallest
     // lsb exponent} of the nonzero entries: of each ds row over keys, of each
     // ds / p column over (query head, row), of each column of K over keys and
-    // of Q / dO over (query head, row).
+    // of Q / dO over (query head, row) (these three with the exponent of each
+    // entry's lowest set bit as its lsb).
     int2 *st_rds, *st_cds, *st_cp, *st_k, *st_q, *st_o;
     v4i *xb[3];           // digit blocks of the right operands of dQ, dK, dV (K, Q, dO)
     int *xf[3];           // per (row tile, column group): 1 = left to k_bwd_sum
@@ -75,6 +76,17 @@ __device__ __forceinline__ void stat_of(float x, int &emax, int &lmin) {
     const int e = f32_exp(x);
     emax = x != 0.0f ? e : INT_MIN;
     lmin = x != 0.0f ? max(e, -126) - 23 : INT_MAX;
+}
+
+// The same with the exponent of the lowest set bit as lsb exponent: a value
+// whose significand ends in c zero bits sits on a grid 2^c times coarser (a
+// bf16 value widened to f32 ends in at least 16).  Used for the right
+// operands, whose digits are made with shifts both ways (k_bwd_slice).
+__device__ __forceinline__ void stat_of_exact(float x, int &emax, int &lmin) {
+    const uint32_t bits = __float_as_uint(x), be = (bits >> 23) & 0xffu;
+    const uint32_t m = (bits & 0x7fffffu) | (be ? 0x800000u : 0u);
+    emax = m ? (int)be - 127 : INT_MIN;
+    lmin = m ? (int)(be ? be : 1u) - 150 + __builtin_ctz(m) : INT_MAX;
 }
 
 // Grid exponent g and balanced base-256 digit count n of a row (or column)
@@ -360,7 +372,7 @@ __global__ __launch_bounds__(256) void k_bwd_colstats(const void *src, int64_t s
 #pragma unroll 4
         for (int64_t s = r0 + s8; s < r1; s += 8) {
             int e, l;
-            stat_of(elem<T>::to_f32(col[s * sS]), e, l);
+            stat_of_exact(elem<T>::to_f32(col[s * sS]), e, l);
             emax = max(emax, e);
             lmin = min(lmin, l);
         }
@@ -442,8 +454,10 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
         const uint32_t bits = __float_as_uint(val[p]);
         const uint32_t be = (bits >> 23) & 0xffu;
         const uint64_t m = (bits & 0x7fffffu) | (be ? 0x800000u : 0u);
-        const int sh = (int)(be ? be : 1u) - 150 - g;  // >= 0 for every nonzero entry of the row
-        const unsigned __int128 mag = m ? ((unsigned __int128)m << (sh & 127)) : 0;
+        // m 2^sh on the column's grid; sh < 0 only where m ends in at least -sh zero bits
+        const int sh = (int)(be ? be : 1u) - 150 - g;
+        const unsigned __int128 mag = !m ? 0 : sh >= 0 ? ((unsigned __int128)m << (sh & 127))
+                                                       : (unsigned __int128)(m >> min(-sh, 63));
         U[p] = ((bits >> 31) ? off - mag : off + mag);
     }
     for (int a = 0; a < nt; ++a) {
