@@ -319,3 +319,36 @@ def test_backward_large_causal_share_chunks_both_paths_and_fp64(A):
         err = (a.cpu().double() - b).abs().max().item()
         tol = 2.0 ** -20 * (b.abs().max().item() + 1)
         assert err <= tol, (name, err, tol)
+
+
+def _dyadic(seed, shape, lo, hi):
+    """Integers in [-64, 64) times 2^e, e uniform in [lo, hi]: few significant
+    bits at many binades, so most entries end in long runs of zero bits."""
+    g = torch.Generator().manual_seed(seed)
+    m = torch.randint(-64, 64, shape, generator=g).double()
+    e = torch.randint(lo, hi + 1, shape, generator=g).double()
+    return (m * torch.pow(2.0, e)).float()
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_backward_right_operands_on_coarse_grids(A, oracle, dtype):
+    """The right operands' grids (K, Q, dO columns) sit at each column's lowest
+    set bit, so an entry can lie above its own f32 lsb grid and its digits are
+    made by a right shift.  Dyadic Q, K, V, dO with a few full-precision
+    entries mixed in exercise both shift directions; the matrix-core sums must
+    match the per-term sums and the oracle bit for bit."""
+    B, Hq, Hkv, S, D = 1, 4, 2, 80, 64
+    q = _dyadic(940, (B, Hq, S, D), -12, 0).to(dtype)
+    k = _dyadic(941, (B, Hkv, S, D), -12, 0).to(dtype)
+    v = _dyadic(942, (B, Hkv, S, D), -20, 0).to(dtype)
+    dO = _dyadic(943, (B, Hq, S, D), -24, 2)
+    dO[0, 1, 5, :8] = torch.randn(8, generator=torch.Generator().manual_seed(944))
+    q[0, 0, 3, 10] = 1.0 + 2.0 ** -7
+    k[0, 1, 60, 20] = 2.0 ** -14
+    scale = W.default_scale(D)
+    say(f"backward coarse grids {dtype}")
+    ref = oracle.attn_backward(q, k, v, dO, True, scale)
+    fast, slow = _backward_both_paths(A, q, k, v, dO, True, scale)
+    for name, a, b, c in zip(("dq", "dk", "dv"), fast, slow, ref):
+        assert_bits_equal(a, c, name)
+        assert_bits_equal(b, c, name + " (per-term)")
