@@ -142,8 +142,9 @@ __global__ __launch_bounds__(64) void k_bwd_delta(BwdArgs A, int64_t rows) {
 // tid % 16) owns rows 4 tr .. 4 tr + 3 and keys 4 tc .. 4 tc + 3 and runs both
 // chains of its 16 pairs, d ascending.  Q, K, dO and V are staged in LDS as
 // binary64 (exact widening) in chunks of kPdsDc dimensions, transposed to
-// [d][row] so a thread reads its four rows' operands with two 16-byte loads;
-// wave w fills array w, lane = row.  Grid (key tiles, row tiles, heads);
+// [d][row] so a thread reads its four rows' operands with two 16-byte loads
+// (K and V with their keys interleaved so those loads are contiguous over
+// the lanes); wave w fills array w, lane = row.  Grid (key tiles, row tiles, heads);
 // tiles wholly above the causal diagonal are skipped.
 constexpr int kPdsT = 64;   // rows and keys of a tile
 constexpr int kPdsDc = 32;  // dimensions per LDS stage
@@ -206,17 +207,22 @@ __global__ __launch_bounds__(256) void k_bwd_pds64(BwdArgs A) {
         __syncthreads();  // the previous stage's readers are done
         const bool dok = d0 + dl < D;
 #pragma unroll
-        for (int r2 = 0; r2 < NR; ++r2)
-            sm[arr - AO][dl][rofs + 2 * r2 + rh] = dok ? (double)__uint_as_float(nx[r2]) : 0.0;
+        for (int r2 = 0; r2 < NR; ++r2) {
+            // K and V keys j = 4 tc + t sit at 32 (t / 2) + 2 tc + t % 2, so the
+            // sixteen tc of a read touch one contiguous 256-byte run
+            const int j = rofs + 2 * r2 + rh;
+            const int col = (arr & 1) ? ((j & 2) << 4) + ((j >> 2) << 1) + (j & 1) : j;
+            sm[arr - AO][dl][col] = dok ? (double)__uint_as_float(nx[r2]) : 0.0;
+        }
         __syncthreads();
         if (d0 + kPdsDc < D) gload(d0 + kPdsDc);
         for (int dd = 0; dd < dn; ++dd) {
-            const double2 *ro = (const double2 *)&sm[2 - AO][dd][4 * tr], *rv = (const double2 *)&sm[3 - AO][dd][4 * tc];
-            const double2 o01 = ro[0], o23 = ro[1], v01 = rv[0], v23 = rv[1];
+            const double2 *ro = (const double2 *)&sm[2 - AO][dd][4 * tr], *rv = (const double2 *)&sm[3 - AO][dd][2 * tc];
+            const double2 o01 = ro[0], o23 = ro[1], v01 = rv[0], v23 = rv[16];
             const double ov[4] = {o01.x, o01.y, o23.x, o23.y}, vv[4] = {v01.x, v01.y, v23.x, v23.y};
             if (!SC) {
-                const double2 *rq = (const double2 *)&sm[0][dd][4 * tr], *rk = (const double2 *)&sm[1][dd][4 * tc];
-                const double2 q01 = rq[0], q23 = rq[1], k01 = rk[0], k23 = rk[1];
+                const double2 *rq = (const double2 *)&sm[0][dd][4 * tr], *rk = (const double2 *)&sm[1][dd][2 * tc];
+                const double2 q01 = rq[0], q23 = rq[1], k01 = rk[0], k23 = rk[16];
                 const double qv[4] = {q01.x, q01.y, q23.x, q23.y}, kv[4] = {k01.x, k01.y, k23.x, k23.y};
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
