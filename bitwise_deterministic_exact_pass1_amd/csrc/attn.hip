@@ -136,23 +136,10 @@ hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) {
     hipLaunchKernelGGL(k_fill_u32, grid_for(n), dim3(256), 0, s, p, n, v);
     return hipGetLastError();
 }
-// The same for a 16-byte aligned p: two values per 16-byte store, the odd
-// last one by the first thread.
-__global__ void k_fill_i64x2(int64_t *p, int64_t n, int64_t v) {
-    const int64_t n2 = n >> 1;
-    longlong2 *q = (longlong2 *)p;
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n2; t += (int64_t)gridDim.x * blockDim.x)
-        q[t] = make_longlong2(v, v);
-    if ((n & 1) && blockIdx.x == 0 && threadIdx.x == 0) p[n - 1] = v;
-}
-
 hipError_t launch_fill_i64(int64_t *p, int64_t n, int64_t v, hipStream_t s) {
     ProfScope prof_("fill", s);
     if (n <= 0) return hipSuccess;
-    if ((((uintptr_t)p) & 15) == 0 && n >= 2)
-        hipLaunchKernelGGL(k_fill_i64x2, grid_for(n >> 1), dim3(256), 0, s, p, n, v);
-    else
-        hipLaunchKernelGGL(k_fill_i64, grid_for(n), dim3(256), 0, s, p, n, v);
+    hipLaunchKernelGGL(k_fill_i64, grid_for(n), dim3(256), 0, s, p, n, v);
     return hipGetLastError();
 }
 
