@@ -580,3 +580,130 @@ def test_backward_rounding_points_exact(oracle):
             for i in range(S):
                 tq = sum((Fraction(DS[h, i, j]) * Fraction(K[0][j][d]) for j in range(i + 1)), Fraction(0))
                 assert dq[0, h, i, d] == np.float32(sc * float(tq))
+
+
+# ---------------------------------------------------------------- cross-entropy rounding points, bit for bit
+
+def _bits32(x) -> int:
+    return int(np.float32(x).view(np.uint32))
+
+
+def _ce_pin_rows(seed: int, N: int, V: int):
+    """bf16 logit rows that reach the rounding points where a regrouped rule
+    shows: half the rows are the cross-entropy workload's distribution (2 N(0,1)
+    with the target raised by 4); in the other half the target is the row max
+    at magnitude 4..48 and every other logit lies at least 17..40 (drawn per
+    row) below it, so the loss is a logsumexp excess of 1e-6..1e-16 computed
+    next to a large m, and the target's probability is that close to 1."""
+    x, t = W.ce_inputs(seed=seed, N=N, V=V, dtype=torch.float32)
+    g = torch.Generator().manual_seed(seed + 1)
+    for i in range(N // 2, N):
+        big = float(torch.randint(8, 96, (1,), generator=g)) * 0.5 * (1 if i % 2 else -1)
+        gmin = 17.0 + 23.0 * float(torch.rand(1, generator=g))
+        gap = gmin + 13.0 * torch.rand(V, generator=g)
+        row = big - gap
+        row[t[i]] = big
+        x[i] = row
+    return x.to(torch.bfloat16), t
+
+
+def test_ce_denom_digits_exact_on_random_rows(oracle):
+    """den_i = the exact sum of RN32(exp_det(RN64(x - m))) over [v_lo, v_hi):
+    recomputed term by term (Python float subtraction is RN64, exp_det is
+    pinned above, numpy float32 is RN32) and summed as Fractions."""
+    N, V = 12, 700
+    x, t = _ce_pin_rows(71, N, V)
+    xf = x.float().numpy().astype(np.float64)
+    for lo, hi in [(0, V), (123, 517)]:
+        m = oracle.ce_rowmax(x, lo, hi)
+        den = oracle.ce_denom_digits(x, m, lo, hi)
+        for i in range(N):
+            assert _bits32(m[i]) == _bits32(max(xf[i, lo:hi].tolist()))
+            ws = [Fraction(float(np.float32(oracle.exp_det(xv - float(m[i]))))) for xv in xf[i, lo:hi].tolist()]
+            assert _int_of_digits(den[:, i]) == int(sum(ws, Fraction(0)) * 2 ** 149), (lo, hi, i)
+            assert den[:8, i].min() >= 0 and den[:8, i].max() < 2 ** 32
+
+
+def test_ce_finalize_rounding_points_bit_exact(oracle):
+    """loss = RN32(RN64(RN64(m + log_det(den64)) - x_t)), den64 = RN64(den):
+    den64 from Python's correctly rounded Fraction -> float, log_det pinned
+    above, the two additions as Python float operations, RN32 by numpy.  The
+    pin has power: on these rows the groupings m + (L - x_t), L + (m - x_t) and
+    RN32(lse) - x_t each give other bits on some rows."""
+    N, V = 40, 500
+    x, t = _ce_pin_rows(72, N, V)
+    xf = x.float().numpy().astype(np.float64)
+    loss, m, denom = oracle.ce_forward(x, t)
+    den = oracle.ce_denom_digits(x, m)
+    alt = [0, 0, 0]
+    for i in range(N):
+        d64 = float(Fraction(_int_of_digits(den[:, i]), 2 ** 149))
+        assert denom[i] == d64
+        L = oracle.log_det(d64)
+        mm, xt = float(m[i]), float(xf[i, int(t[i])])
+        want = np.float32((mm + L) - xt)
+        assert _bits32(loss[i]) == _bits32(want), i
+        alt[0] += _bits32(np.float32(mm + (L - xt))) != _bits32(want)
+        alt[1] += _bits32(np.float32(L + (mm - xt))) != _bits32(want)
+        alt[2] += _bits32(np.float32(float(np.float32(mm + L)) - xt)) != _bits32(want)
+    assert all(a > 0 for a in alt), alt
+
+
+@pytest.mark.parametrize("reduction", ["none", "mean", "sum"])
+def test_ce_backward_rounding_points_bit_exact(oracle, reduction):
+    """grad = RN32(RN64(RN64(RN64(w / den64) - [v = t]) * c)) with c = g_i,
+    RN64(g / N) or g: every operation recomputed in Python floats (each a
+    binary64 IEEE operation) from the pinned exp_det and den64.  Power check:
+    p*c - [v=t]*c (for the mean: c rounded to binary32), and p rounded to
+    binary32 before the subtraction, give other bits on some entries."""
+    N, V = 24, 300
+    x, t = _ce_pin_rows(73, N, V)
+    xf = x.float().numpy().astype(np.float64)
+    loss, m, denom = oracle.ce_forward(x, t)
+    rng = np.random.default_rng(74)
+    gl = (rng.standard_normal(N if reduction == "none" else 1) * 3).astype(np.float32)
+    if reduction == "mean":
+        gl[0] = 1.0  # the usual upstream of a mean loss; 1/24 is not a binary32 value
+    grad = oracle.ce_backward(x, t, m, denom, gl, reduction)
+    alt = [0, 0]
+    for i in range(N):
+        g = float(gl[i if reduction == "none" else 0])
+        c = g / N if reduction == "mean" else g
+        for v in range(V):
+            w = float(np.float32(oracle.exp_det(float(xf[i, v]) - float(m[i]))))
+            p = w / float(denom[i])
+            oh = 1.0 if v == int(t[i]) else 0.0
+            want = np.float32((p - oh) * c)
+            assert _bits32(grad[i, v]) == _bits32(want), (i, v)
+            other = (p - oh) * float(np.float32(g / N)) if reduction == "mean" else p * c - oh * c
+            alt[0] += _bits32(np.float32(other)) != _bits32(want)
+            alt[1] += _bits32(np.float32((float(np.float32(p)) - oh) * c)) != _bits32(want)
+    assert all(a > 0 for a in alt), alt
+
+
+# ---------------------------------------------------------------- totalOrder max with signed zeros
+
+def test_rowmax_total_order_signed_zero_bits(oracle):
+    """The row max is IEEE totalOrder's (-0 < +0), compared as bit patterns.
+    Attention: with f32 q = 2^-100 and k = -/+2^-100 the fp64 dot is -/+2^-200,
+    whose RN32 score is -0 / +0; a key of -1 gives the normal score -2^-100.
+    Cross-entropy: the same orders on bf16 logits."""
+    f = np.float32
+    q = torch.tensor([[[[2.0 ** -100]] * 4]], dtype=torch.float32)  # [1,1,4,1]
+    cases = [  # keys of the row, expected rowmax bits
+        ([-2.0 ** -100, 2.0 ** -100], 0x00000000),
+        ([2.0 ** -100, -2.0 ** -100], 0x00000000),
+        ([-2.0 ** -100, -1.0], 0x80000000),
+        ([-1.0, -2.0 ** -100], 0x80000000),
+    ]
+    for keys, want in cases:
+        k = torch.tensor(keys, dtype=torch.float32).reshape(1, 1, len(keys), 1)
+        m = oracle.attn_rowmax(q, k, 0, len(keys), False, 1.0)
+        assert all(_bits32(v) == want for v in m.reshape(-1)), (keys, [hex(_bits32(v)) for v in m.reshape(-1)])
+    rows = [([-0.0, 0.0, -1.0], 0x00000000), ([0.0, -0.0], 0x00000000), ([-0.0, -1.0], 0x80000000),
+            ([-1.0, -0.0, -3.0], 0x80000000), ([-0.0, -0.0], 0x80000000)]
+    for vals, want in rows:
+        x = torch.tensor([vals], dtype=torch.float32).to(torch.bfloat16)
+        m = oracle.ce_rowmax(x)
+        assert _bits32(m[0]) == want, (vals, hex(_bits32(m[0])))
+        assert _bits32(f(max(vals, key=lambda z: (z, math.copysign(1, z))))) == want  # the pin's own reading
