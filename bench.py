@@ -7,10 +7,13 @@ A step is one fused det_attn call (global rowmax, exact NUM/DEN digits over
 every key, finalize) on the causal GQA workload B=2, Hq=8, Hkv=2, S=1024,
 D=128, bf16 N(0,1) inputs resident in HBM.  The metric is unmasked (i,j)
 pairs per second.  Alongside it the script reports, for the kernel that takes
-the most time, its algorithmic fp64 work per launch divided by its average
-launch time (HIP events recorded by the library on the launch stream), and
-the CPU oracle's throughput on a bounded row sample of the same workload.
-Prints one JSON line.
+the most time, its algorithmic work per launch on each unit it uses (the
+int8 matrix cores for the exact contractions, the fp64 vector ALUs for
+exp_det, HBM for the bytes the method must move) divided by its average
+launch time (HIP events recorded by the library on the launch stream), each
+against that unit's peak; the unit closest to its peak is the binding one.
+It also reports the CPU oracle's throughput on a bounded row sample of the
+same workload.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -29,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "exact-attention (i,j) pairs/sec + % of FP64-vector roofline, bit-exact"
 FP64_PEAK_TFLOPS = 78.6   # MI355X vector fp64 (256 CUs x 2.4 GHz x 128 flops/clk)
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 matrix cores (5.0 POP/s)
 
 
 def visible_pairs(B, Hq, Sq, Skv, causal):
@@ -60,24 +64,43 @@ def measured_traffic(kernel, workload):
     return rec["bytes_per_launch"]
 
 
-def kernel_work(name, pairs, rows, D, kv_elems=0, q_elems=0):
-    """(amount, unit, bound) of algorithmic work of one launch of `name`: fp64
-    flops of the method's steps for the compute kernels (whatever units run
-    them), HBM bytes for the data-movement ones.  kv_elems / q_elems: elements
-    of one of K, V / of Q (bf16 or f32 inputs, counted at 2 bytes)."""
-    if name == "scores":      # pass 1: one fp64 fma chain of length D per pair
-        return 2.0 * D * pairs, "flop", "alu"
-    if name == "pv_mfma":     # pass 2: exp_det (2 mul + 15 fma) and D exact product-accumulates
-        return (2.0 * D + 32.0) * pairs, "flop", "alu"
-    if name == "weights":     # exp_det: 2 mul + 15 fma
-        return 32.0 * pairs, "flop", "alu"
-    if name == "deposit":     # D exact product-accumulates per pair, one fma each
-        return 2.0 * D * pairs, "flop", "alu"
+PEAKS = {"mfma_int8": (INT8_PEAK_TOPS, "TOP/s", 1e12), "fp64_valu": (FP64_PEAK_TFLOPS, "TFLOP/s", 1e12),
+         "hbm": (HBM_PEAK_GBS, "GB/s", 1e9)}
+
+
+def kernel_resources(name, pairs, rows, D, kv_bytes=0, q_bytes=0):
+    """{unit: algorithmic amount} of one launch of `name`, on each unit the
+    kernel uses.  The amounts count what the method computes, not how: the
+    contraction of the scores and of NUM is one multiply-add (2 ops) per
+    (pair, dimension) although each runs as several int8 digit products;
+    exp_det is 2 mul + 15 fma = 32 flops per pair; the bytes are the inputs
+    read once and the outputs written once (the stored scores between the
+    passes are an implementation trade and are not counted).  kv_bytes /
+    q_bytes: bytes of one of K, V / of Q for this launch."""
+    if name == "scores":      # pass 1: the score contraction on the matrix cores; reads Q and K
+        return {"mfma_int8": 2.0 * D * pairs, "hbm": q_bytes + kv_bytes + 4.0 * rows}
+    if name == "pv_mfma":     # pass 2: exp_det per pair, D products per pair, reads V, writes O
+        return {"mfma_int8": 2.0 * D * pairs, "fp64_valu": 32.0 * pairs, "hbm": kv_bytes + 4.0 * rows * D}
     if name == "vprep":       # read V twice (statistics, digits), write five digit bytes per element
-        return kv_elems * (2 + 2 + 5), "byte", "hbm"
+        return {"hbm": kv_bytes * (1 + 1 + 2.5)}
     if name == "finalize":    # read 14+9/D digits, write one f32 per output
-        return rows * D * (112 + 72.0 / D + 4), "byte", "hbm"
+        return {"hbm": rows * D * (112 + 72.0 / D + 4)}
     return None
+
+
+def roofline_of(name, res, avg_s, traffic):
+    """Each unit's achieved rate against its peak; the binding unit is the
+    one closest to its peak."""
+    units = {}
+    for u, amount in res.items():
+        peak, unit, scale = PEAKS[u]
+        ach = amount / avg_s / scale
+        units[u] = {"achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak, "per_launch": amount}
+    bind = max(units, key=lambda u: units[u]["frac"])
+    b = units[bind]
+    return {"bound": {"mfma_int8": "mfma", "fp64_valu": "alu", "hbm": "hbm"}[bind], "kernel": name,
+            "achieved": b["achieved"], "peak": b["peak"], "unit": b["unit"], "frac": b["frac"],
+            "traffic": traffic, "units": units}
 
 
 def main():
@@ -165,31 +188,30 @@ def main():
         kernels[n]["share"] = prof[n][1] / total_k
     dominant = max(prof, key=lambda n: prof[n][1])
     per_step_launches = prof[dominant][0] / args.steps
-    work = kernel_work(dominant, pairs / per_step_launches, rows / per_step_launches, D,
-                       kv_elems=B * k.shape[1] * Skv * D / per_step_launches)
+    esize = q.element_size()
+    res = kernel_resources(dominant, pairs / per_step_launches, rows / per_step_launches, D,
+                           kv_bytes=B * k.shape[1] * Skv * D * esize / per_step_launches,
+                           q_bytes=rows * D * esize / per_step_launches)
     avg_s = prof[dominant][1] / prof[dominant][0] / 1e3
-    if work is not None:
-        amount, unit, bound = work
-        if unit == "flop":
-            achieved, peak, runit = amount / avg_s / 1e12, FP64_PEAK_TFLOPS, "TFLOP/s"
-        else:
-            achieved, peak, runit = amount / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
-        roofline = {"bound": bound, "kernel": dominant, "achieved": achieved, "peak": peak, "unit": runit,
-                    "frac": achieved / peak, "traffic": measured_traffic(dominant, args.workload)}
+    traffic = measured_traffic(dominant, args.workload)
+    if res is not None:
+        roofline = roofline_of(dominant, res, avg_s, traffic)
     else:
-        roofline = {"bound": "alu", "kernel": dominant, "achieved": None, "peak": FP64_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": None, "traffic": None}
+        roofline = {"bound": None, "kernel": dominant, "achieved": None, "peak": None, "unit": None, "frac": None,
+                    "traffic": traffic}
+    # the whole step priced the way the pages' fp64 kernels would run it (6D + 32 fp64 flops per pair at the
+    # fp64 vector peak): a comparison with that design, not a roofline of this one
     path_flops = pairs * (6 * D + 32)
-    path = {"flop_per_pair": 6 * D + 32, "achieved_tflops": path_flops / (ms_step / 1e3) / 1e12,
-            "frac_of_fp64_peak": path_flops / (ms_step / 1e3) / 1e12 / FP64_PEAK_TFLOPS}
+    path = {"flop_per_pair": 6 * D + 32, "fp64_equivalent_tflops": path_flops / (ms_step / 1e3) / 1e12,
+            "fp64_equivalent_frac": path_flops / (ms_step / 1e3) / 1e12 / FP64_PEAK_TFLOPS}
 
     result = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f64+int64", "data": "synthetic",
+        "vs_baseline": None, "dtype": "int8/int32 (matrix cores) + f64 + int64", "data": "synthetic",
         "config": {"workload": f"fused det_attn, {desc}", "B": B, "Hq": Hq, "Hkv": k.shape[1],
                    "S": Sq, "D": D, "causal": causal, "pairs_per_step": pairs},
-        "roofline": roofline, "path_roofline": path, "kernels": kernels,
+        "roofline": roofline, "fp64_equivalent": path, "kernels": kernels,
     }
 
     if not args.no_extra:
@@ -227,7 +249,7 @@ def backward_measurement(attention, Q, K, V, causal, scale, pairs, reps=5):
             "forward_with_stats_ms": eb[0].elapsed_time(eb[1]), "backward_ms": bwd_ms,
             "pairs_per_s": pairs / (bwd_ms / 1e3),
             "flop_per_pair": 10 * D_ + 32,
-            "frac_of_fp64_roofline": pairs * (10 * D_ + 32) / (bwd_ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS,
+            "fp64_equivalent_frac": pairs * (10 * D_ + 32) / (bwd_ms / 1e3) / 1e12 / FP64_PEAK_TFLOPS,
             "kernels_ms": {k_: round(t, 4) for k_, (c, t) in bprof.items() if k_.startswith("bwd")}}
 
 
@@ -265,15 +287,14 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     torch.cuda.synchronize()
     N, Vv = X.shape
     fwd_ms, bwd_ms = e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])
-    # the per-element work model: forward 33 fp64 flops + 2 bytes, backward 36 flops + 6 bytes per
-    # (token, vocab); the ideal time is the larger of the fp64 and HBM times
-    fwd_ideal = max(N * Vv * 33 / (FP64_PEAK_TFLOPS * 1e12), N * Vv * 2 / (HBM_PEAK_GBS * 1e9))
-    bwd_ideal = max(N * Vv * 36 / (FP64_PEAK_TFLOPS * 1e12), N * Vv * 6 / (HBM_PEAK_GBS * 1e9))
+    # both passes are priced against HBM: the forward reads each bf16 logit once (2 bytes; its exp runs
+    # once per distinct bit pattern of a row, not per element), the backward reads it and writes an f32
     res["cross_entropy"] = {"workload": "N=4096 V=128256 bf16", "forward_ms": fwd_ms, "backward_ms": bwd_ms,
                             "forward_token_vocab_per_s": N * Vv / (fwd_ms / 1e3),
+                            "forward_hbm_GBps": N * Vv * 2 / (fwd_ms / 1e3) / 1e9,
                             "backward_hbm_GBps": N * Vv * 6 / (bwd_ms / 1e3) / 1e9,
-                            "forward_frac_of_roofline": fwd_ideal / (fwd_ms / 1e3),
-                            "backward_frac_of_roofline": bwd_ideal / (bwd_ms / 1e3)}
+                            "forward_frac_of_hbm": N * Vv * 2 / (fwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                            "backward_frac_of_hbm": N * Vv * 6 / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS}
     res["backward"] = backward_measurement(attention, Q, K, V, causal, scale, pairs)
 
     # the float32 combines the exact path replaces, on the same inputs
@@ -297,7 +318,7 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
         Sx, Dx = q2.shape[2], q2.shape[3]
         pairs2 = q2.shape[0] * q2.shape[1] * Sx * (Sx + 1) // 2
         res[name] = {"workload": wl["desc"], "ms": ms2, "pairs_per_s": pairs2 / (ms2 / 1e3),
-                     "frac_of_fp64_path_roofline": pairs2 * (6 * Dx + 32) / (ms2 / 1e3) / 1e12 / FP64_PEAK_TFLOPS}
+                     "fp64_equivalent_frac": pairs2 * (6 * Dx + 32) / (ms2 / 1e3) / 1e12 / FP64_PEAK_TFLOPS}
         if name == "cp_share_bf16":  # the exact backward at this share (query rows in several chunks)
             res[name]["backward"] = backward_measurement(attention, q2, k2, v2, True, wl["scale"], pairs2, reps=2)
         del q2, k2, v2
@@ -318,7 +339,7 @@ def extra_measurements(attention, W, Q, K, V, causal, scale, ref, pairs):
     pairs5 = W.LONG_H * W.LONG_S * W.LONG_S
     res["long_nhd_bf16"] = {"workload": "B=1 H=56 S=37810 D=128 bfloat16 NHD views of one QKV buffer, non-causal",
                             "ms": ms5, "pairs_per_s": pairs5 / (ms5 / 1e3),
-                            "frac_of_fp64_path_roofline": pairs5 * (6 * W.LONG_D + 32) / (ms5 / 1e3) / 1e12
+                            "fp64_equivalent_frac": pairs5 * (6 * W.LONG_D + 32) / (ms5 / 1e3) / 1e12
                             / FP64_PEAK_TFLOPS}
     del q5, k5, v5, dbuf
     return res

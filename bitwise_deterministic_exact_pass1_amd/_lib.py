@@ -44,17 +44,20 @@ SIGNATURES = {
     "det_last_error": (C.c_char_p, []),
     "det_profile_begin": (C.c_int, []),
     "det_profile_end": (_SZ, [C.c_char_p, _SZ]),
+    "det_debug_force_generic": (C.c_int, [_I32]),
     "det_attn_workspace_size": (_SZ, [_T, _T, _T, _I32]),
     "det_attn": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _SZ, _P]),
     "det_attn_stats": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _P, _P, _SZ, _P]),
     "det_attn_backward_workspace_size": (_SZ, [_T, _T, _T, _I32]),
     "det_attn_backward": (C.c_int, [_T, _T, _T, _T, _T, _P, _P, _I32, _D, _O, _O, _O, _P, _SZ, _P]),
-    "det_attn_rowmax_workspace_size": (_SZ, [_T, _T, _I64, _I64]),
-    "det_attn_rowmax": (C.c_int, [_T, _T, _I64, _I64, _I32, _D, _P, _P, _SZ, _P]),
-    "det_attn_accumulate_workspace_size": (_SZ, [_T, _T, _T, _I64, _I64]),
-    "det_attn_accumulate": (C.c_int, [_T, _T, _T, _P, _I64, _I64, _I32, _D, _P, _P, _I32, _P, _SZ, _P]),
+    "det_attn_rowmax_workspace_size": (_SZ, [_T, _T, _I64, _I64, _I64, _I64]),
+    "det_attn_rowmax": (C.c_int, [_T, _T, _I64, _I64, _I64, _I64, _I32, _D, _P, _P, _SZ, _P]),
+    "det_attn_accumulate_workspace_size": (_SZ, [_T, _T, _T, _I64, _I64, _I64, _I64]),
+    "det_attn_accumulate": (C.c_int, [_T, _T, _T, _P, _I64, _I64, _I64, _I64, _I32, _D, _P, _P, _I32, _P, _SZ,
+                                      _P]),
     "det_rowmax_combine": (C.c_int, [_P, _P, _I64, _P]),
     "det_digits_combine": (C.c_int, [_P, _P, _I64, _I32, _P]),
+    "det_digits_normalize": (C.c_int, [_P, _I64, _I32, _P]),
     "det_attn_finalize": (C.c_int, [_P, _P, _I64, _I64, _I64, _I64, _O, _P]),
     "det_attn_sharded_workspace_size": (_SZ, [_T, _T, _T, _P, _I32, _I32]),
     "det_attn_sharded": (C.c_int, [_T, _T, _T, _P, _I32, _P, _I32, _D, _O, _P, _SZ, _P]),
@@ -65,7 +68,7 @@ SIGNATURES = {
     "det_ce_forward": (C.c_int, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "det_ce_reduce_workspace_size": (_SZ, [_I64]),
     "det_ce_reduce": (C.c_int, [_P, _I64, _I32, _P, _P, _SZ, _P]),
-    "det_ce_backward": (C.c_int, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I64, _P]),
+    "det_ce_backward": (C.c_int, [_P, _I32, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I64, _P]),
 }
 
 _lib = None
@@ -85,6 +88,12 @@ def lib() -> C.CDLL:
             fn.argtypes = args
         _lib = h
     return _lib
+
+
+def force_generic(on: bool) -> None:
+    """Testing aid: send every tile through the library's generic exact path
+    (bit-identical results) until switched off again."""
+    check(lib().det_debug_force_generic(int(bool(on))))
 
 
 def profile_begin() -> None:

@@ -142,47 +142,57 @@ def det_attn_autograd(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, causal:
 
 
 def rowmax(Q: torch.Tensor, K: torch.Tensor, kv_lo: int = 0, kv_hi: Optional[int] = None, causal: bool = False,
-           scale: Optional[float] = None) -> torch.Tensor:
-    """Per-query max score over keys [kv_lo, kv_hi): f32 [B, Hq, Sq]."""
+           scale: Optional[float] = None, q_lo: int = 0, q_hi: Optional[int] = None,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-query max score over keys [kv_lo, kv_hi): f32 [B, Hq, Sq].  Only
+    query rows [q_lo, q_hi) are computed; the other rows of `out` (a new
+    tensor filled with -inf when not given) are left as they are."""
     kv_hi = K.shape[2] if kv_hi is None else kv_hi
+    q_hi = Q.shape[2] if q_hi is None else q_hi
     scale = default_scale(Q.shape[3]) if scale is None else float(scale)
     q, k = _desc(Q), _desc(K)
-    out = torch.empty(Q.shape[:3], dtype=torch.float32, device=Q.device)
+    if out is None:
+        out = torch.full(Q.shape[:3], float("-inf"), dtype=torch.float32, device=Q.device)
+    elif out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != tuple(Q.shape[:3]):
+        raise ValueError("out must be contiguous float32 [B, Hq, Sq]")
     L = lib()
-    nbytes = L.det_attn_rowmax_workspace_size(C.byref(q), C.byref(k), kv_lo, kv_hi)
+    nbytes = L.det_attn_rowmax_workspace_size(C.byref(q), C.byref(k), q_lo, q_hi, kv_lo, kv_hi)
     ws, addr = _workspace(nbytes, Q.device)
-    check(L.det_attn_rowmax(C.byref(q), C.byref(k), kv_lo, kv_hi, int(causal), scale, out.data_ptr(), addr, nbytes,
-                            _stream(Q)))
+    check(L.det_attn_rowmax(C.byref(q), C.byref(k), q_lo, q_hi, kv_lo, kv_hi, int(causal), scale, out.data_ptr(),
+                            addr, nbytes, _stream(Q)))
     return out
 
 
 def accumulate(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, rowmax: torch.Tensor, kv_lo: int = 0,
                kv_hi: Optional[int] = None, causal: bool = False, scale: Optional[float] = None,
-               num: Optional[torch.Tensor] = None, den: Optional[torch.Tensor] = None
-               ) -> Tuple[torch.Tensor, torch.Tensor]:
+               num: Optional[torch.Tensor] = None, den: Optional[torch.Tensor] = None, q_lo: int = 0,
+               q_hi: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Exact digits of keys [kv_lo, kv_hi) against `rowmax` (normally the
-    composed global max).  Returns canonical (NUM int64 [14,B,Hq,Sq,D],
-    DEN int64 [9,B,Hq,Sq]).  When `num`/`den` are given the shard is added
-    into them in place."""
+    composed global max), for query rows [q_lo, q_hi).  Returns canonical
+    (NUM int64 [14,B,Hq,Sq,D], DEN int64 [9,B,Hq,Sq]).  When `num`/`den` are
+    given the shard is added into their rows [q_lo, q_hi) in place; new arrays
+    start at zero."""
     kv_hi = K.shape[2] if kv_hi is None else kv_hi
+    q_hi = Q.shape[2] if q_hi is None else q_hi
     scale = default_scale(Q.shape[3]) if scale is None else float(scale)
     B, Hq, Sq, D = Q.shape
     add_into = num is not None
     if add_into != (den is not None):
         raise ValueError("pass both num and den, or neither")
     if not add_into:
-        num = torch.empty((NUM_DIGITS, B, Hq, Sq, D), dtype=torch.int64, device=Q.device)
-        den = torch.empty((DEN_DIGITS, B, Hq, Sq), dtype=torch.int64, device=Q.device)
+        num = torch.zeros((NUM_DIGITS, B, Hq, Sq, D), dtype=torch.int64, device=Q.device)
+        den = torch.zeros((DEN_DIGITS, B, Hq, Sq), dtype=torch.int64, device=Q.device)
     _check_digits(num, den, (B, Hq, Sq, D))
     rm = rowmax.contiguous()
     if rm.dtype != torch.float32 or rm.numel() != B * Hq * Sq:
         raise ValueError("rowmax must be float32 [B, Hq, Sq]")
     q, k, v = _desc(Q), _desc(K), _desc(V)
     L = lib()
-    nbytes = L.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), kv_lo, kv_hi)
+    nbytes = L.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), q_lo, q_hi, kv_lo, kv_hi)
     ws, addr = _workspace(nbytes, Q.device)
-    check(L.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), rm.data_ptr(), kv_lo, kv_hi, int(causal),
-                                scale, num.data_ptr(), den.data_ptr(), int(add_into), addr, nbytes, _stream(Q)))
+    check(L.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), rm.data_ptr(), q_lo, q_hi, kv_lo, kv_hi,
+                                int(causal), scale, num.data_ptr(), den.data_ptr(), int(add_into), addr, nbytes,
+                                _stream(Q)))
     return num, den
 
 
@@ -212,6 +222,16 @@ def combine_digits(acc: torch.Tensor, part: torch.Tensor) -> torch.Tensor:
         raise ValueError("digit arrays must be contiguous")
     K = acc.shape[0]
     check(lib().det_digits_combine(acc.data_ptr(), part.data_ptr(), acc.numel() // K, K, _stream(acc)))
+    return acc
+
+
+def normalize_digits(acc: torch.Tensor) -> torch.Tensor:
+    """acc <- canonical(acc), in place (digit-major planes, 14 or 9 digits):
+    the same exact values, e.g. after a caller-side int64 add of digit arrays."""
+    if acc.dtype != torch.int64 or not acc.is_contiguous():
+        raise ValueError("digit arrays must be contiguous int64")
+    K = acc.shape[0]
+    check(lib().det_digits_normalize(acc.data_ptr(), acc.numel() // K, K, _stream(acc)))
     return acc
 
 

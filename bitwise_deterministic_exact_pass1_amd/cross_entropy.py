@@ -114,15 +114,19 @@ def reduce(loss: torch.Tensor, reduction: str) -> torch.Tensor:
 
 
 def backward(logits: torch.Tensor, targets: torch.Tensor, rowmax_: torch.Tensor, denom: torch.Tensor,
-             grad_loss: torch.Tensor, reduction: str) -> torch.Tensor:
-    """dLogits f32 [N, V]: (softmax - onehot) times the upstream gradient."""
+             grad_loss: torch.Tensor, reduction: str, v0: int = 0) -> torch.Tensor:
+    """dLogits f32 [N, V]: (softmax - onehot) times the upstream gradient.
+    For a vocabulary shard, `logits` holds columns [v0, v0 + V) of the
+    vocabulary (e.g. a column slice), `targets` are whole-vocabulary indices
+    and rowmax_ / denom are the composed global values; the result is that
+    shard's columns of the whole gradient, bit for bit."""
     code, N, V, ld = _logits(logits)
     t = _targets(targets, N)
     g = grad_loss.reshape(-1).to(torch.float32).contiguous()
     grad = torch.empty((N, V), dtype=torch.float32, device=logits.device)
-    check(lib().det_ce_backward(logits.data_ptr(), code, N, V, ld, t.data_ptr(), rowmax_.contiguous().data_ptr(),
-                                denom.contiguous().data_ptr(), g.data_ptr(), REDUCTIONS[reduction],
-                                grad.data_ptr(), V, _stream(logits)))
+    check(lib().det_ce_backward(logits.data_ptr(), code, N, V, ld, int(v0), t.data_ptr(),
+                                rowmax_.contiguous().data_ptr(), denom.contiguous().data_ptr(), g.data_ptr(),
+                                REDUCTIONS[reduction], grad.data_ptr(), V, _stream(logits)))
     return grad
 
 

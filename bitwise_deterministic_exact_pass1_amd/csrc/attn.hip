@@ -332,6 +332,69 @@ __global__ void k_digits_combine(int64_t *__restrict__ acc, const int64_t *__res
     }
 }
 
+// Rows [i0, i1) of head blockIdx.y: values bh*rows*width + i0*width + t,
+// t < (i1 - i0) * width, digit k at k * plane.
+template <int K>
+__global__ void k_normalize_rows(int64_t *__restrict__ dg, int64_t plane, int64_t rows, int64_t i0, int64_t run,
+                                 int64_t width) {
+    const int64_t base = (int64_t)blockIdx.y * rows * width + i0 * width;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < run; t += (int64_t)gridDim.x * blockDim.x) {
+        int64_t d[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) d[k] = dg[k * plane + base + t];
+        canonicalize<K>(d);
+#pragma unroll
+        for (int k = 0; k < K; ++k) dg[k * plane + base + t] = d[k];
+    }
+}
+
+__global__ void k_fill_rows_i64(int64_t *__restrict__ p, int64_t plane, int64_t rows, int64_t i0, int64_t run,
+                                int64_t width, int64_t v) {
+    int64_t *q = p + (int64_t)blockIdx.z * plane + (int64_t)blockIdx.y * rows * width + i0 * width;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < run; t += (int64_t)gridDim.x * blockDim.x)
+        q[t] = v;
+}
+
+static dim3 grid_rows(int64_t run, int64_t n_bh, int64_t nz = 1) {
+    const int64_t g = std::min<int64_t>((run + 255) / 256, 4096);
+    return dim3((unsigned)std::max<int64_t>(g, 1), (unsigned)n_bh, (unsigned)nz);
+}
+
+hipError_t launch_normalize_rows(int64_t *digits, int n_digits, int64_t plane, int64_t n_bh, int64_t rows,
+                                 int64_t i0, int64_t i1, int64_t width, hipStream_t s) {
+    ProfScope prof_("normalize", s);
+    const int64_t run = (i1 - i0) * width;
+    if (run <= 0 || n_bh <= 0) return hipSuccess;
+    for (int64_t b0 = 0; b0 < n_bh; b0 += 65535) {  // grid y holds at most 65535 heads per launch
+        const int64_t nb = std::min<int64_t>(65535, n_bh - b0);
+        int64_t *dg = digits + b0 * rows * width;
+        if (n_digits == kNumDigits)
+            hipLaunchKernelGGL(k_normalize_rows<kNumDigits>, grid_rows(run, nb), dim3(256), 0, s, dg, plane, rows, i0,
+                               run, width);
+        else
+            hipLaunchKernelGGL(k_normalize_rows<kDenDigits>, grid_rows(run, nb), dim3(256), 0, s, dg, plane, rows, i0,
+                               run, width);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_fill_rows_i64(int64_t *p, int n_planes, int64_t plane, int64_t n_bh, int64_t rows, int64_t i0,
+                                int64_t i1, int64_t width, int64_t v, hipStream_t s) {
+    ProfScope prof_("fill", s);
+    const int64_t run = (i1 - i0) * width;
+    if (run <= 0 || n_bh <= 0 || n_planes <= 0) return hipSuccess;
+    for (int64_t b0 = 0; b0 < n_bh; b0 += 65535) {  // grid y holds at most 65535 heads per launch
+        const int64_t nb = std::min<int64_t>(65535, n_bh - b0);
+        hipLaunchKernelGGL(k_fill_rows_i64, grid_rows(run, nb, n_planes), dim3(256), 0, s, p + b0 * rows * width,
+                           plane, rows, i0, run, width, v);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hipStream_t s) {
     ProfScope prof_("normalize", s);
     if (n_values <= 0) return hipSuccess;

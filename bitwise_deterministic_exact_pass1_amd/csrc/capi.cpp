@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -86,6 +87,13 @@ int check_qkv(const det_tensor *q, const det_tensor *k, const det_tensor *v, int
 int check_range(const det_tensor *k, int64_t lo, int64_t hi) {
     if (lo < 0 || hi < lo || hi > k->S)
         return fail(DET_E_SHAPE, "key range [%lld,%lld) outside [0,%lld]", (long long)lo, (long long)hi, (long long)k->S);
+    return DET_OK;
+}
+
+int check_qrange(const det_tensor *q, int64_t lo, int64_t hi) {
+    if (lo < 0 || hi < lo || hi > q->S)
+        return fail(DET_E_SHAPE, "query range [%lld,%lld) outside [0,%lld]", (long long)lo, (long long)hi,
+                    (long long)q->S);
     return DET_OK;
 }
 
@@ -215,12 +223,10 @@ VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
     return v;
 }
 
-// DET_FORCE_FALLBACK=1 sends every tile through the generic exact path (tests
-// use it to check that both paths give the same bits).
-int force_fallback() {
-    const char *e = getenv("DET_FORCE_FALLBACK");
-    return e && e[0] == '1';
-}
+// Set by det_debug_force_generic (a testing aid): every tile then takes the
+// generic exact path, so tests can check that both paths give the same bits.
+std::atomic<int> g_force_generic{0};
+int force_fallback() { return g_force_generic.load(std::memory_order_relaxed); }
 
 // Largest chunk (a multiple of kRowTile, or all Sq rows) whose need fits `budget`;
 // 0 if even one tile does not fit.
@@ -228,6 +234,7 @@ template <typename F> int64_t choose_chunk(int64_t Sq, size_t budget, F need) {
     if (Sq <= 0) return 0;
     if (need(Sq) <= budget) return Sq;
     int64_t lo = 0, hi = (Sq - 1) / kRowTile;  // in tiles
+    // (Sq: the number of query rows to process)
     while (lo < hi) {
         const int64_t mid = (lo + hi + 1) / 2;
         if (need(mid * kRowTile) <= budget) lo = mid;
@@ -256,6 +263,11 @@ extern "C" {
 
 const char *det_last_error(void) { return g_err.c_str(); }
 
+int det_debug_force_generic(int32_t on) {
+    g_force_generic.store(on ? 1 : 0, std::memory_order_relaxed);
+    return ok();
+}
+
 int det_profile_begin(void) {
     prof_enable(true);
     return ok();
@@ -283,37 +295,41 @@ int det_digit_format(int32_t which, int32_t *n_digits, int32_t *lsb_exp2) {
 
 // ------------------------------------------------------------------ rowmax
 
-size_t det_attn_rowmax_workspace_size(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi) {
-    if (check_qk(q, k, 0) || check_range(k, kv_lo, kv_hi)) return 0;
+size_t det_attn_rowmax_workspace_size(const det_tensor *q, const det_tensor *k, int64_t q_lo, int64_t q_hi,
+                                      int64_t kv_lo, int64_t kv_hi) {
+    if (check_qk(q, k, 0) || check_qrange(q, q_lo, q_hi) || check_range(k, kv_lo, kv_hi)) return 0;
     const AttnGeom g = geom(q, k, 0, 1.0);
     const bool mf = use_mfma_scores(q);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_rowmax(g, mf, ni, kv_hi - kv_lo); });
+    return default_size(q_hi - q_lo, [&](int64_t ni) { return bytes_rowmax(g, mf, ni, kv_hi - kv_lo); });
 }
 
-int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi, int32_t causal,
-                    double scale, float *rowmax, void *workspace, size_t ws_bytes, void *stream) {
+int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t q_lo, int64_t q_hi, int64_t kv_lo,
+                    int64_t kv_hi, int32_t causal, double scale, float *rowmax, void *workspace, size_t ws_bytes,
+                    void *stream) {
     int rc;
-    if ((rc = check_qk(q, k, causal)) || (rc = check_range(k, kv_lo, kv_hi))) return rc;
-    if (!rowmax && q->S > 0) return fail(DET_E_NULL, "rowmax is NULL");
+    if ((rc = check_qk(q, k, causal)) || (rc = check_qrange(q, q_lo, q_hi)) || (rc = check_range(k, kv_lo, kv_hi)))
+        return rc;
+    const int64_t nq = q_hi - q_lo;
+    if (!rowmax && nq > 0) return fail(DET_E_NULL, "rowmax is NULL");
     const AttnGeom g = geom(q, k, causal, scale);
     const bool mf = use_mfma_scores(q);
     const int64_t W = kv_hi - kv_lo;
     auto need = [&](int64_t ni) { return bytes_rowmax(g, mf, ni, W); };
-    if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
-    if (g.Sq == 0) return ok();
+    if ((rc = check_ws(workspace, ws_bytes, nq > 0 ? need(std::min<int64_t>(nq, kRowTile)) : 0))) return rc;
+    if (nq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
     const Tensor tq = to_t(q), tk = to_t(k);
-    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need), bh = g.B * g.Hq;
+    const int64_t chunk = choose_chunk(nq, ws_bytes, need), bh = g.B * g.Hq;
     Carver c0{(char *)workspace, ws_bytes};
     void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
     // per-chunk regions, sized for the largest chunk and reused by every chunk
     void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, W));
     uint32_t *keys = c0.take<uint32_t>(bh * chunk);
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
-    for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
-        const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
-        HIP_TRY(run_scores(tq, tk, tk, g, mf, kprep, i0 == 0, true, nullptr, cws, i0, i1, kv_lo, kv_hi, nullptr, keys,
-                           ni, i0, s),
+    for (int64_t i0 = q_lo; i0 < q_hi; i0 += chunk) {
+        const int64_t i1 = std::min(q_hi, i0 + chunk), ni = i1 - i0;
+        HIP_TRY(run_scores(tq, tk, tk, g, mf, kprep, i0 == q_lo, true, nullptr, cws, i0, i1, kv_lo, kv_hi, nullptr,
+                           keys, ni, i0, s),
                 "scores");
         HIP_TRY(launch_keys_to_f32(keys, rowmax, bh, ni, g.Sq, i0, s), "rowmax");
     }
@@ -323,29 +339,32 @@ int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int
 // ------------------------------------------------------------------ accumulate
 
 size_t det_attn_accumulate_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
-                                          int64_t kv_lo, int64_t kv_hi) {
-    if (check_qkv(q, k, v, 0) || check_range(k, kv_lo, kv_hi)) return 0;
+                                          int64_t q_lo, int64_t q_hi, int64_t kv_lo, int64_t kv_hi) {
+    if (check_qkv(q, k, v, 0) || check_qrange(q, q_lo, q_hi) || check_range(k, kv_lo, kv_hi)) return 0;
     const AttnGeom g = geom(q, k, 0, 1.0);
     const bool mf = use_mfma_scores(q);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_accumulate(g, mf, ni, kv_hi - kv_lo); });
+    return default_size(q_hi - q_lo, [&](int64_t ni) { return bytes_accumulate(g, mf, ni, kv_hi - kv_lo); });
 }
 
 int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tensor *v, const float *rowmax,
-                        int64_t kv_lo, int64_t kv_hi, int32_t causal, double scale, int64_t *num, int64_t *den,
-                        int32_t add_into, void *workspace, size_t ws_bytes, void *stream) {
+                        int64_t q_lo, int64_t q_hi, int64_t kv_lo, int64_t kv_hi, int32_t causal, double scale,
+                        int64_t *num, int64_t *den, int32_t add_into, void *workspace, size_t ws_bytes,
+                        void *stream) {
     int rc;
-    if ((rc = check_qkv(q, k, v, causal)) || (rc = check_range(k, kv_lo, kv_hi))) return rc;
-    if (q->S > 0 && (!rowmax || !num || !den)) return fail(DET_E_NULL, "rowmax, num or den is NULL");
+    if ((rc = check_qkv(q, k, v, causal)) || (rc = check_qrange(q, q_lo, q_hi)) || (rc = check_range(k, kv_lo, kv_hi)))
+        return rc;
+    const int64_t nq = q_hi - q_lo;
+    if (nq > 0 && (!rowmax || !num || !den)) return fail(DET_E_NULL, "rowmax, num or den is NULL");
     const AttnGeom g = geom(q, k, causal, scale);
     const bool mf = use_mfma_scores(q);
     const int64_t W = kv_hi - kv_lo;
     auto need = [&](int64_t ni) { return bytes_accumulate(g, mf, ni, W); };
-    if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
-    if (g.Sq == 0) return ok();
+    if ((rc = check_ws(workspace, ws_bytes, nq > 0 ? need(std::min<int64_t>(nq, kRowTile)) : 0))) return rc;
+    if (nq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
     const Tensor tq = to_t(q), tk = to_t(k), tv = to_t(v);
     const int64_t bh = g.B * g.Hq, rows = bh * g.Sq;
-    const int64_t chunk = choose_chunk(g.Sq, ws_bytes, need);
+    const int64_t chunk = choose_chunk(nq, ws_bytes, need);
     Carver c0{(char *)workspace, ws_bytes};
     VPrep vp = carve_vprep(c0, g, W);
     void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
@@ -354,23 +373,25 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     float *sc = c0.take<float>(bh * chunk * W);
     int *flags = c0.take<int>(bh * ((chunk + 31) / 32));
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
+    // only rows [q_lo, q_hi) of each head are touched
     if (!add_into) {
-        HIP_TRY(launch_fill_i64(num, kNumDigits * rows * g.D, 0, s), "fill num");
-        HIP_TRY(launch_fill_i64(den, kDenDigits * rows, 0, s), "fill den");
+        HIP_TRY(launch_fill_rows_i64(num, kNumDigits, rows * g.D, bh, g.Sq, q_lo, q_hi, g.D, 0, s), "fill num");
+        HIP_TRY(launch_fill_rows_i64(den, kDenDigits, rows, bh, g.Sq, q_lo, q_hi, 1, 0, s), "fill den");
     }
     const int ff = force_fallback();
-    for (int64_t i0 = 0; i0 < g.Sq && W > 0; i0 += chunk) {
-        const int64_t i1 = std::min(g.Sq, i0 + chunk);
+    for (int64_t i0 = q_lo; i0 < q_hi && W > 0; i0 += chunk) {
+        const int64_t i1 = std::min(q_hi, i0 + chunk);
         // the first chunk's launches also prepare K and V
-        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, true, i0 == 0 ? &vp : nullptr, cws, i0, i1, kv_lo, kv_hi,
+        const bool first = i0 == q_lo;
+        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, first, true, first ? &vp : nullptr, cws, i0, i1, kv_lo, kv_hi,
                            sc, nullptr, 0, 0, s),
                 "scores");
         HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, nullptr, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr,
                           nullptr, num, den, rows, g.Sq, 0, ff, s),
                 "deposit");
     }
-    HIP_TRY(launch_normalize(num, rows * g.D, kNumDigits, s), "normalize num");
-    HIP_TRY(launch_normalize(den, rows, kDenDigits, s), "normalize den");
+    HIP_TRY(launch_normalize_rows(num, kNumDigits, rows * g.D, bh, g.Sq, q_lo, q_hi, g.D, s), "normalize num");
+    HIP_TRY(launch_normalize_rows(den, kDenDigits, rows, bh, g.Sq, q_lo, q_hi, 1, s), "normalize den");
     return ok();
 }
 
@@ -380,6 +401,15 @@ int det_rowmax_combine(float *acc, const float *part, int64_t n, void *stream) {
     if (n < 0) return fail(DET_E_SHAPE, "negative count");
     if (n > 0 && (!acc || !part)) return fail(DET_E_NULL, "acc or part is NULL");
     HIP_TRY(launch_rowmax_combine(acc, part, n, (hipStream_t)stream), "rowmax combine");
+    return ok();
+}
+
+int det_digits_normalize(int64_t *acc, int64_t n_values, int32_t n_digits, void *stream) {
+    if (n_values < 0) return fail(DET_E_SHAPE, "negative count");
+    if (n_digits != kNumDigits && n_digits != kDenDigits)
+        return fail(DET_E_VALUE, "n_digits must be %d or %d", kNumDigits, kDenDigits);
+    if (n_values > 0 && !acc) return fail(DET_E_NULL, "acc is NULL");
+    HIP_TRY(launch_normalize(acc, n_values, n_digits, (hipStream_t)stream), "digits normalize");
     return ok();
 }
 
@@ -734,17 +764,18 @@ int det_ce_reduce(const float *loss, int64_t N, int32_t reduction, float *out, v
     return ok();
 }
 
-int det_ce_backward(const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
-                    const float *rowmax, const double *denom, const float *grad_loss, int32_t reduction,
-                    float *grad, int64_t grad_ld, void *stream) {
+int det_ce_backward(const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, int64_t v0,
+                    const int64_t *targets, const float *rowmax, const double *denom, const float *grad_loss,
+                    int32_t reduction, float *grad, int64_t grad_ld, void *stream) {
     int rc;
     if ((rc = check_logits(logits, dtype, N, V, ld))) return rc;
+    if (v0 < 0) return fail(DET_E_VALUE, "vocabulary offset %lld is negative", (long long)v0);
     if (reduction < 0 || reduction > 2) return fail(DET_E_VALUE, "reduction %d is not 0/1/2", reduction);
     if (grad_ld < V) return fail(DET_E_STRIDE, "grad row stride %lld < V", (long long)grad_ld);
     if (N > 0 && (!targets || !rowmax || !denom || !grad_loss || !grad))
         return fail(DET_E_NULL, "a required pointer is NULL");
-    HIP_TRY(launch_ce_backward(logits, dtype, N, V, ld, targets, rowmax, denom, grad_loss, reduction, grad, grad_ld,
-                               (hipStream_t)stream),
+    HIP_TRY(launch_ce_backward(logits, dtype, N, V, ld, v0, targets, rowmax, denom, grad_loss, reduction, grad,
+                               grad_ld, (hipStream_t)stream),
             "ce backward");
     return ok();
 }

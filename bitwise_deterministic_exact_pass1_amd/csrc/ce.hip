@@ -162,7 +162,7 @@ __global__ __launch_bounds__(1024) void k_ce_reduce(const float *loss, int64_t N
 }
 
 template <typename T>
-__global__ void k_ce_backward(const void *x, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
+__global__ void k_ce_backward(const void *x, int64_t N, int64_t V, int64_t ld, int64_t v0, const int64_t *targets,
                               const float *rowmax, const double *denom, const float *grad_loss, int reduction,
                               float *grad, int64_t grad_ld) {
     const int64_t total = N * V;
@@ -174,7 +174,7 @@ __global__ void k_ce_backward(const void *x, int64_t N, int64_t V, int64_t ld, c
         else c = (double)grad_loss[0];
         const float w = weight(ce_load<T>(x, ld, i, v), rowmax[i]);
         const double p = (double)w / denom[i];
-        const double g = p - (v == targets[i] ? 1.0 : 0.0);
+        const double g = p - (v == targets[i] - v0 ? 1.0 : 0.0);
         grad[i * grad_ld + v] = (float)(g * c);
     }
 }
@@ -452,7 +452,7 @@ __device__ __forceinline__ double grad_scale(const float *grad_loss, int reducti
 // Gradient rows of bf16 logits: one workgroup per row builds g(pattern) for the
 // window's 8192 patterns, then streams the row through the table.
 __global__ __launch_bounds__(kTT) void k_ce_backward_tab(const uint16_t *x, int64_t N, int64_t V, int64_t ld,
-                                                         const int64_t *targets, const float *rowmax,
+                                                         int64_t v0, const int64_t *targets, const float *rowmax,
                                                          const double *denom, const float *grad_loss,
                                                          int reduction, float *grad, int64_t grad_ld) {
     __shared__ float tab[kTab];
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(kTT) void k_ce_backward_tab(const uint16_t *x, int6
     const float m = rowmax[i];
     const double d64 = denom[i];
     const double c = grad_scale(grad_loss, reduction, N, i);
-    const int64_t t = targets[i];
+    const int64_t t = targets[i] - v0;  // the target's column in this shard (outside [0, V): none)
     const uint32_t base = pick_window(p0, rs, red);
     for (int s = tid; s < kTab; s += kTT) tab[s] = grad_value(bf16_value(slot_code(s, base)), m, d64, c, false);
     __syncthreads();
@@ -596,19 +596,19 @@ hipError_t launch_ce_reduce(const float *loss, int64_t N, int reduction, float *
     return hipGetLastError();
 }
 
-hipError_t launch_ce_backward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
-                              const float *rowmax, const double *denom, const float *grad_loss, int reduction,
-                              float *grad, int64_t grad_ld, hipStream_t s) {
+hipError_t launch_ce_backward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, int64_t v0,
+                              const int64_t *targets, const float *rowmax, const double *denom,
+                              const float *grad_loss, int reduction, float *grad, int64_t grad_ld, hipStream_t s) {
     ProfScope prof_("ce_backward", s);
     if (N * V <= 0) return hipSuccess;
     if (dtype == 0)
-        hipLaunchKernelGGL(k_ce_backward<float>, ce_grid(N * V), dim3(256), 0, s, x, N, V, ld, targets, rowmax,
+        hipLaunchKernelGGL(k_ce_backward<float>, ce_grid(N * V), dim3(256), 0, s, x, N, V, ld, v0, targets, rowmax,
                            denom, grad_loss, reduction, grad, grad_ld);
     else if (bf16_rows_ok(x) && use_tables(V))
         hipLaunchKernelGGL(k_ce_backward_tab, dim3((unsigned)N), dim3(kTT), 0, s, (const uint16_t *)x, N, V, ld,
-                           targets, rowmax, denom, grad_loss, reduction, grad, grad_ld);
+                           v0, targets, rowmax, denom, grad_loss, reduction, grad, grad_ld);
     else
-        hipLaunchKernelGGL(k_ce_backward<bf16_t>, ce_grid(N * V), dim3(256), 0, s, x, N, V, ld, targets, rowmax,
+        hipLaunchKernelGGL(k_ce_backward<bf16_t>, ce_grid(N * V), dim3(256), 0, s, x, N, V, ld, v0, targets, rowmax,
                            denom, grad_loss, reduction, grad, grad_ld);
     return hipGetLastError();
 }

@@ -169,6 +169,13 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
                      float *stat_m = nullptr, double *stat_den = nullptr, int64_t stat_rows = 0);
 
 hipError_t launch_normalize(int64_t *digits, int64_t n_values, int n_digits, hipStream_t s);
+// Rows [i0, i1) of each of n_bh runs of `rows` rows (values of `width`
+// consecutive int64 each) in planes of `plane` values: normalize to canonical
+// form, or fill with v.
+hipError_t launch_normalize_rows(int64_t *digits, int n_digits, int64_t plane, int64_t n_bh, int64_t rows,
+                                 int64_t i0, int64_t i1, int64_t width, hipStream_t s);
+hipError_t launch_fill_rows_i64(int64_t *p, int n_planes, int64_t plane, int64_t n_bh, int64_t rows, int64_t i0,
+                                int64_t i1, int64_t width, int64_t v, hipStream_t s);
 hipError_t launch_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int n_digits,
                                  hipStream_t s);
 hipError_t launch_rowmax_combine(float *acc, const float *part, int64_t n, hipStream_t s);
@@ -190,8 +197,10 @@ hipError_t launch_ce_forward(const void *x, int dtype, int64_t N, int64_t V, int
                              float *loss, float *rowmax, double *denom, hipStream_t s);
 hipError_t launch_ce_reduce(const float *loss, int64_t N, int reduction, float *out, int64_t *scratch,
                             hipStream_t s);
-hipError_t launch_ce_backward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
-                              const float *rowmax, const double *denom, const float *grad_loss, int reduction,
-                              float *grad, int64_t grad_ld, hipStream_t s);
+// v0: the vocabulary index of column 0 of x and grad (a vocabulary shard);
+// targets are indices into the whole vocabulary.
+hipError_t launch_ce_backward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, int64_t v0,
+                              const int64_t *targets, const float *rowmax, const double *denom,
+                              const float *grad_loss, int reduction, float *grad, int64_t grad_ld, hipStream_t s);
 
 }  // namespace det

@@ -12,9 +12,12 @@
 //
 // v_mfma_i32_32x32x32_i8 computes one C_s update for a 32-row x 32-dim tile
 // over 32 keys.  Every int32 partial sum is exact (|c e| <= 2^14 per key and
-// pair; the classes are carried into each other every 8192 keys), so the
-// result is the exact NUM whatever the order of keys, blocks or instructions.
-// DEN is the exact int64 sum of the W_ij.  A tile whose weights do not fit the
+// pair; every 8192 keys the classes are carried into each other and the top
+// class, which nothing above it absorbs, is moved into an int64 in LDS), so
+// the result is the exact NUM whatever the order of keys, blocks or
+// instructions, for any key range the launcher admits.  DEN is the exact sum
+// of the W_ij, kept per thread in int64 halves that are folded every 8192
+// keys and added up per row in 128 bits.  A tile whose weights do not fit the
 // grid (w < 2^-23, or w > 1 from a rowmax below the scores) or whose V columns
 // need more than five digits is redone by the generic exact path (windowed
 // binary64 sums into digit planes) by the same workgroup: results never depend
@@ -156,15 +159,17 @@ __device__ __forceinline__ uint32_t wave_or_mask(uint32_t nz) {
 }
 
 // LDS of the pass-2 kernel: W digits of two key blocks, the producers'
-// staged scores of two blocks, digit masks, row sums, the bad-tile flag.
+// staged scores of two blocks, digit masks, row sums, the bad-tile flag, and
+// the consumers' int64 parts of the top class (tiles of 8192 keys or more).
 struct PvShared {
     uint8_t dig[2][kAw * 1024];
     float sc[2][32][32];
     uint32_t mask[2][kPW];
     // per tile parity, so that a tile's finalize overlaps the next tile's start
-    int64_t den[2][32];  // exact sum of W per row
+    int64_t den_hi[2][32], den_lo[2][32];  // exact sum of W per row: hi 2^32 + lo, lo in [0, 2^32)
     double d64[2][32];   // RN64(DEN) of the row
     int bad[2];
+    int64_t top[4][16][64];  // [consumer wave][accumulator register][lane]
 };
 
 // Pass 2 of a 32-row tile for the 32-dim groups G0 .. G0+NG-1.
@@ -252,7 +257,9 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
             x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, voff + 4 * u, kb * kKB * 4, 0));
     };
     float *my0 = &S.sc[0][r][k0], *my1 = &S.sc[1][r][k0];
-    int64_t wsum = 0;
+    // this thread's sum of W: whi 2^32 + wsum; wsum grows by at most KPT 2^46
+    // per block and is folded into whi every kCarryEvery blocks (< 2^57 between)
+    int64_t wsum = 0, whi = 0;
     bool bad = false;
     // Scores travel three blocks ahead of their use: loaded into registers,
     // parked in this thread's LDS slots one block later, read the block after.
@@ -283,6 +290,10 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
             for (int u = 0; u < KPT; ++u) sc[u] = cur[u];
             const uint32_t nz = wave_or_mask(block_weights<KPT>(sc, m, nvis(kb + 1), S.dig[nb] + dofs, wsum, bad));
             if (lane == 0) S.mask[nb][pw] = nz;
+            if (((kb + 1) % kCarryEvery) == 0) {
+                whi += wsum >> 32;
+                wsum &= 0xffffffffll;
+            }
             float *nxt = nb ? my0 : my1;  // block kb+2 uses buffer (kb+2)&1
 #pragma unroll
             for (int u = 0; u < KPT; ++u) nxt[u] = park[u];
@@ -295,11 +306,18 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
         if (kb + 1 < T.nblk) step(kb + 1, pend2, pend);
     }
     // exact row sums of W: the TPR threads of a row are consecutive lanes
+    // (each wsum < 2^57, so their sum fits; whi counts units of 2^32)
 #pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) wsum += __shfl_xor(wsum, off, 64);
+    for (int off = 1; off < TPR; off <<= 1) {
+        wsum += __shfl_xor(wsum, off, 64);
+        whi += __shfl_xor(whi, off, 64);
+    }
     if (ptid % TPR == 0) {
-        S.den[par][r] = wsum;
-        S.d64[par][r] = ldexp((double)wsum, -kSw);  // exact scaling of the correctly rounded conversion
+        const int64_t hi = whi + (wsum >> 32), lo = wsum & 0xffffffffll;  // DEN 2^46 = hi 2^32 + lo
+        S.den_hi[par][r] = hi;
+        S.den_lo[par][r] = lo;
+        // correctly rounded RN64(DEN): the 128-bit value (hi >> 32) 2^64 + ((hi << 32) | lo)
+        S.d64[par][r] = i128_to_f64(hi >> 32, ((uint64_t)hi << 32) | (uint64_t)lo, -kSw);
     }
     if (bad) S.bad[par] = 1;
     __syncthreads();
@@ -318,7 +336,7 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
 // without copies), and the class sums C_(a+b) += W_a x V_b run on the matrix
 // cores for the W digit planes the producers marked nonzero.
 template <int BV>
-__device__ __forceinline__ void pv_consume_loop(const PvTile &T, const v4i *vb, int lane, v16i (&C)[kNC],
+__device__ __forceinline__ void pv_consume_loop(const PvTile &T, const v4i *vb, int lane, int wave, v16i (&C)[kNC],
                                                 PvShared &S) {
     v4i VA[BV > 0 ? BV : 1], VB[BV > 0 ? BV : 1];
     if (BV > 0 && T.nblk > 0) {
@@ -351,13 +369,17 @@ __device__ __forceinline__ void pv_consume_loop(const PvTile &T, const v4i *vb, 
                 Acur = Anext;
             }
             if ((kb % kCarryEvery) == kCarryEvery - 1) {
-                // carry each class into the next so every partial sum stays far below 2^31
+                // carry each class into the next so every partial sum stays far below 2^31,
+                // and move the top class into its int64 part in LDS (wave-private slots)
 #pragma unroll
                 for (int s = 0; s < kNC - 1; ++s) {
                     const v16i c = C[s] >> 8;
                     C[s] -= c << 8;
                     C[s + 1] += c;
                 }
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) S.top[wave][rr][lane] += C[kNC - 1][rr];
+                C[kNC - 1] = v16i{0};
             }
         }
         __syncthreads();
@@ -388,15 +410,21 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
     v16i C[kNC];
 #pragma unroll
     for (int s = 0; s < kNC; ++s) C[s] = v16i{0};
+    // the top class's int64 part, used by tiles of kCarryEvery blocks or more
+    const bool longt = T.nblk >= kCarryEvery;
+    if (longt) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) S.top[wave][rr][lane] = 0;
+    }
     // the block loop with the wave's V digit count as a constant (one copy per
     // count; a wave without a group only meets the barriers)
     switch (mine ? Bv : 0) {
-        case 1: pv_consume_loop<1>(T, vb, lane, C, S); break;
-        case 2: pv_consume_loop<2>(T, vb, lane, C, S); break;
-        case 3: pv_consume_loop<3>(T, vb, lane, C, S); break;
-        case 4: pv_consume_loop<4>(T, vb, lane, C, S); break;
-        case 5: pv_consume_loop<5>(T, vb, lane, C, S); break;
-        default: pv_consume_loop<0>(T, vb, lane, C, S); break;
+        case 1: pv_consume_loop<1>(T, vb, lane, wave, C, S); break;
+        case 2: pv_consume_loop<2>(T, vb, lane, wave, C, S); break;
+        case 3: pv_consume_loop<3>(T, vb, lane, wave, C, S); break;
+        case 4: pv_consume_loop<4>(T, vb, lane, wave, C, S); break;
+        case 5: pv_consume_loop<5>(T, vb, lane, wave, C, S); break;
+        default: pv_consume_loop<0>(T, vb, lane, wave, C, S); break;
     }
     __syncthreads();
     if (S.bad[par]) {
@@ -407,13 +435,18 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
     if (!mine) return false;
 
     // carry the classes into bytes: C_0..C_8 in [0, 256), C_9 signed, so that
-    // NUM = C_9 2^72 + sum_{s<9} C_s 2^(8s) = hi 2^64 + lo
+    // NUM = top 2^72 + sum_{s<9} C_s 2^(8s) = hi 2^64 + lo, with top = C_9
+    // plus its int64 part from LDS
 #pragma unroll
     for (int s = 0; s < kNC - 1; ++s) {
         const v16i c = C[s] >> 8;
         C[s] &= 255;
         C[s + 1] += c;
     }
+    // the top class of accumulator register rr, with its int64 part
+    auto top = [&](int rr) -> int64_t {
+        return (int64_t)C[kNC - 1][rr] + (longt ? S.top[wave][rr][lane] : 0);
+    };
     const int64_t d = G * 32 + (lane & 31);
     const int g = A.colgrid[T.bhk * A.Dp32 + d];
     if (FUSED && ((T.rem >> G) & 1)) {
@@ -435,7 +468,7 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
                 const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) |
                                     ((uint32_t)C[6][rr] << 16) | ((uint32_t)C[7][rr] << 24);
                 const uint64_t lo = ((uint64_t)l1 << 32) | l0;
-                const int64_t hi = (int64_t)C[kNC - 1][rr] * 256 + C[kNC - 2][rr];
+                const int64_t hi = top(rr) * 256 + C[kNC - 2][rr];
                 const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
                 add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, nb + row * A.D + d, nplane);
             }
@@ -459,7 +492,7 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
             const uint64_t plo = (uint64_t)((uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) |
                                             ((uint32_t)C[2][rr] << 16) | ((uint32_t)C[3][rr] << 24)) |
                                  ((uint64_t)((uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8)) << 32);
-            const int64_t phi = (int64_t)C[9][rr] * (1 << 24) +
+            const int64_t phi = top(rr) * (1 << 24) +
                                 (int64_t)((uint32_t)C[6][rr] | ((uint32_t)C[7][rr] << 8) | ((uint32_t)C[8][rr] << 16));
             big |= (uint64_t)(phi + ((int64_t)1 << 53)) >= ((uint64_t)1 << 54);
             const double n64 = ldexp(fma((double)phi, 0x1p48, (double)plo), g - kSw);
@@ -474,7 +507,7 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
                 const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) | ((uint32_t)C[6][rr] << 16) |
                                     ((uint32_t)C[7][rr] << 24);
                 const uint64_t lo = ((uint64_t)l1 << 32) | l0;
-                const int64_t hi = (int64_t)C[kNC - 1][rr] * 256 + C[kNC - 2][rr];
+                const int64_t hi = top(rr) * 256 + C[kNC - 2][rr];
                 out[rr] = (float)(i128_to_f64(hi, lo, g - kSw) / S.d64[par][row]);
             }
         }
@@ -504,12 +537,13 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
         const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) | ((uint32_t)C[6][rr] << 16) |
                             ((uint32_t)C[7][rr] << 24);
         const uint64_t lo = ((uint64_t)l1 << 32) | l0;
-        const int64_t hi = (int64_t)C[kNC - 1][rr] * 256 + C[kNC - 2][rr];
+        const int64_t hi = top(rr) * 256 + C[kNC - 2][rr];
         const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
         const int64_t prow = bh * A.rows_per_bh + (io - A.row0);
         add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, A.num + prow * A.D + d, A.plane_rows * A.D);
         if (G == 0 && (lane & 31) == 0)
-            add_i128_digits<kDenDigits>((__int128)S.den[par][row], -kSw - kDenElo, A.den + prow, A.plane_rows);
+            add_i128_digits<kDenDigits>(((__int128)S.den_hi[par][row] << 32) + S.den_lo[par][row], -kSw - kDenElo,
+                                        A.den + prow, A.plane_rows);
     }
     return false;
 }

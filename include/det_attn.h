@@ -105,6 +105,13 @@ const char *det_last_error(void);
 int det_profile_begin(void);
 size_t det_profile_end(char *buf, size_t len);
 
+/* Testing aid (results never depend on it): with on != 0, every later call
+ * sends every tile of the exact sums through the library's generic exact path
+ * instead of the matrix-core path, until it is called again with 0.  Both
+ * paths compute the same exact sums, so the outputs are bit-identical; the
+ * switch lets tests check that.  Process-wide; returns DET_OK. */
+int det_debug_force_generic(int32_t on);
+
 /* ---------------------------------------------------------------- attention */
 
 /* det-attn page, "API": det_attn(Q, K, V, causal, scale) -- the whole path
@@ -145,23 +152,32 @@ int det_attn_backward(const det_tensor *q, const det_tensor *k, const det_tensor
                       size_t ws_bytes, void *stream);
 
 /* det-attn page, "API": rowmax(Q, K, ..., kv_lo, kv_hi) -- per-query max
- * score over keys [kv_lo, kv_hi) (combine shards by max).
- * rowmax: (device) f32 [B][Hq][Sq].  Workspace: det_attn_rowmax_workspace_size(). */
-size_t det_attn_rowmax_workspace_size(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi);
-int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t kv_lo, int64_t kv_hi, int32_t causal,
-                    double scale, float *rowmax, void *workspace, size_t ws_bytes, void *stream);
+ * score over keys [kv_lo, kv_hi) (combine shards by max), for the query rows
+ * [q_lo, q_hi) (absolute row indices; 0 <= q_lo <= q_hi <= Sq, else
+ * DET_E_SHAPE).  rowmax: (device) f32 [B][Hq][Sq]; only rows in [q_lo, q_hi)
+ * of each head are written, the others are left as they are.  Workspace:
+ * det_attn_rowmax_workspace_size() with the same ranges. */
+size_t det_attn_rowmax_workspace_size(const det_tensor *q, const det_tensor *k, int64_t q_lo, int64_t q_hi,
+                                      int64_t kv_lo, int64_t kv_hi);
+int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t q_lo, int64_t q_hi, int64_t kv_lo,
+                    int64_t kv_hi, int32_t causal, double scale, float *rowmax, void *workspace, size_t ws_bytes,
+                    void *stream);
 
 /* det-attn page, "API": accumulate(Q, K, V, rowmax, ...) -- exact NUM/DEN
  * digits of keys [kv_lo, kv_hi) weighted against `rowmax` (which must be
- * >= every visible score, normally the composed global max).
+ * >= every visible score, normally the composed global max), for the query
+ * rows [q_lo, q_hi) (absolute; range rules as for det_attn_rowmax).
+ * rowmax: (device) f32 [B][Hq][Sq] (rows in range are read);
  * num: (device) int64 [14][B][Hq][Sq][D]; den: (device) int64 [9][B][Hq][Sq].
- * add_into = 0 overwrites them; 1 adds this shard to what they hold.  The
- * result is canonical either way. */
+ * Only rows in [q_lo, q_hi) of each head are touched: add_into = 0
+ * overwrites them; 1 adds this shard to what they hold.  Those rows are
+ * canonical afterwards either way. */
 size_t det_attn_accumulate_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
-                                          int64_t kv_lo, int64_t kv_hi);
+                                          int64_t q_lo, int64_t q_hi, int64_t kv_lo, int64_t kv_hi);
 int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tensor *v, const float *rowmax,
-                        int64_t kv_lo, int64_t kv_hi, int32_t causal, double scale, int64_t *num, int64_t *den,
-                        int32_t add_into, void *workspace, size_t ws_bytes, void *stream);
+                        int64_t q_lo, int64_t q_hi, int64_t kv_lo, int64_t kv_hi, int32_t causal, double scale,
+                        int64_t *num, int64_t *den, int32_t add_into, void *workspace, size_t ws_bytes,
+                        void *stream);
 
 /* Shard composition (det-attn page, "Method": max and int64 add).
  * det_rowmax_combine: acc[i] = totalOrder max(acc[i], part[i]), n values (device).
@@ -169,6 +185,14 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
  * n_digits digits each, planes [n_digits][n_values] (device). */
 int det_rowmax_combine(float *acc, const float *part, int64_t n, void *stream);
 int det_digits_combine(int64_t *acc, const int64_t *part, int64_t n_values, int32_t n_digits, void *stream);
+
+/* Carry normalization of a digit array (det-attn page, "Method": shards
+ * compose by int64 add; the page's caller-side sum of digit arrays is not
+ * canonical): acc <- canonical(acc) in place, the same exact value, for
+ * n_values values of n_digits (14 or 9, else DET_E_VALUE) digits, planes
+ * [n_digits][n_values] (device).  Exact while every |digit| < 2^62 (any sum
+ * of up to 2^30 canonical arrays). */
+int det_digits_normalize(int64_t *acc, int64_t n_values, int32_t n_digits, void *stream);
 
 /* det-attn page, "API": finalize(NUM, DEN, shape) -- out = RN32(RN64(NUM)/RN64(DEN)).
  * num [14][B][Hq][Sq][D], den [9][B][Hq][Sq] (device). */
@@ -225,10 +249,15 @@ int det_ce_reduce(const float *loss, int64_t N, int32_t reduction, float *out, v
 /* Gradient "softmax(x_i) - onehot(t_i)" scaled by the upstream gradient:
  * grad_iv = RN32(RN64(RN64(RN64(w_iv / denom_i) - [v == t_i]) * c_i)),
  * c_i = grad_loss[i] (none), grad_loss[0] (sum), RN64(grad_loss[0]/N) (mean).
+ * A vocabulary shard (det-cross-entropy page, "Correctness": the same bytes on
+ * one device or many): logits and grad hold the V columns [v0, v0 + V) of the
+ * vocabulary, targets are whole-vocabulary indices, and rowmax / denom are the
+ * composed global values; v0 = 0 with the whole vocabulary is the unsharded
+ * call.  v0 < 0 gives DET_E_VALUE.
  * grad_loss: (device) f32 [N] or [1]; grad: (device) f32, row i at grad + i*grad_ld. */
-int det_ce_backward(const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
-                    const float *rowmax, const double *denom, const float *grad_loss, int32_t reduction,
-                    float *grad, int64_t grad_ld, void *stream);
+int det_ce_backward(const void *logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, int64_t v0,
+                    const int64_t *targets, const float *rowmax, const double *denom, const float *grad_loss,
+                    int32_t reduction, float *grad, int64_t grad_ld, void *stream);
 
 #ifdef __cplusplus
 }

@@ -72,11 +72,25 @@ def test_attention_argument_errors(lib):
 
 def test_range_and_split_errors(lib):
     q, k, v = _t(), _t(H=1), _t(H=1)
-    rm = lib.det_attn_rowmax(C.byref(q), C.byref(k), 3, 2, 0, 1.0, 0x3000, 0x10000, 1 << 30, None)
+    rm = lib.det_attn_rowmax(C.byref(q), C.byref(k), 0, 8, 3, 2, 0, 1.0, 0x3000, 0x10000, 1 << 30, None)
     assert rm == -2
-    assert lib.det_attn_rowmax(C.byref(q), C.byref(k), 0, 9, 0, 1.0, 0x3000, 0x10000, 1 << 30, None) == -2
-    assert lib.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), 0x4000, 0, 8, 0, 1.0, None, 0x5000, 0,
+    assert lib.det_attn_rowmax(C.byref(q), C.byref(k), 0, 8, 0, 9, 0, 1.0, 0x3000, 0x10000, 1 << 30, None) == -2
+    # query ranges: lo > hi, below 0, past Sq
+    for qlo, qhi in [(5, 4), (-1, 4), (0, 9)]:
+        assert lib.det_attn_rowmax(C.byref(q), C.byref(k), qlo, qhi, 0, 8, 0, 1.0, 0x3000, 0x10000, 1 << 30,
+                                   None) == -2
+        assert lib.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), 0x4000, qlo, qhi, 0, 8, 0, 1.0, 0x5000,
+                                       0x6000, 0, 0x10000, 1 << 30, None) == -2
+        assert lib.det_attn_rowmax_workspace_size(C.byref(q), C.byref(k), qlo, qhi, 0, 8) == 0
+        assert lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), qlo, qhi, 0, 8) == 0
+    assert lib.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), 0x4000, 0, 8, 0, 8, 0, 1.0, None, 0x5000, 0,
                                    0x10000, 1 << 30, None) == -1
+    # an empty query range needs no pointer, no workspace and launches nothing
+    assert lib.det_attn_rowmax(C.byref(q), C.byref(k), 4, 4, 0, 8, 0, 1.0, None, None, 0, None) == 0
+    assert lib.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), None, 4, 4, 0, 8, 0, 1.0, None, None, 0,
+                                   None, 0, None) == 0
+    # a null rowmax with rows to compute
+    assert lib.det_attn_rowmax(C.byref(q), C.byref(k), 2, 4, 0, 8, 0, 1.0, None, 0x10000, 1 << 30, None) == -1
     o = L.Out(0x2000, 256, 128, 16)
     bad = (C.c_int64 * 2)(4, 3)
     assert lib.det_attn_sharded(C.byref(q), C.byref(k), C.byref(v), bad, 2, None, 0, 1.0, C.byref(o), 0x10000,
@@ -86,6 +100,10 @@ def test_range_and_split_errors(lib):
     assert lib.det_attn_sharded(C.byref(q), C.byref(k), C.byref(v), good, 2, perm, 0, 1.0, C.byref(o), 0x10000,
                                 1 << 30, None) == -7
     assert lib.det_digits_combine(0x1000, 0x2000, 10, 7, None) == -7
+    assert lib.det_digits_normalize(0x1000, 10, 7, None) == -7
+    assert lib.det_digits_normalize(0x1000, -1, 9, None) == -2
+    assert lib.det_digits_normalize(None, 10, 14, None) == -1
+    assert lib.det_digits_normalize(None, 0, 9, None) == 0
     assert lib.det_attn_finalize(0x1000, 0x2000, 1, 1, 4, 300, C.byref(o), None) == -2
 
 
@@ -96,8 +114,11 @@ def test_workspace_sizes_are_host_only(lib):
     splits = (C.c_int64 * 4)(256, 256, 256, 256)
     ns = lib.det_attn_sharded_workspace_size(C.byref(q), C.byref(k), C.byref(v), splits, 4, 1)
     assert ns > 0
-    assert lib.det_attn_rowmax_workspace_size(C.byref(q), C.byref(k), 0, 1024) > 0
-    assert lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), 0, 512) > 0
+    assert lib.det_attn_rowmax_workspace_size(C.byref(q), C.byref(k), 0, 1024, 0, 1024) > 0
+    assert lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), 0, 1024, 0, 512) > 0
+    # fewer query rows never need more workspace
+    assert (lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), 100, 200, 0, 512)
+            <= lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), 0, 1024, 0, 512))
     # an invalid descriptor yields 0 rather than a crash
     assert lib.det_attn_workspace_size(None, C.byref(k), C.byref(v), 0) == 0
 
@@ -132,8 +153,10 @@ def test_cross_entropy_argument_errors(lib):
     assert lib.det_ce_finalize(0x1, 0x1000, 1, 4, 10, 8, 0x2, 0x3, 0x4, 0x5, None) == -4
     assert lib.det_ce_forward(0x1000, 1, 4, 10, 10, None, 0x1, 0x2, 0x3, None, 0, None) == -1
     assert lib.det_ce_reduce(0x1000, 4, 3, 0x2000, None, 0, None) == -7
-    assert lib.det_ce_backward(0x1000, 1, 4, 10, 10, 0x1, 0x2, 0x3, 0x4, 1, 0x5, 9, None) == -4
-    assert lib.det_ce_backward(0x1000, 1, 4, 10, 10, 0x1, 0x2, 0x3, 0x4, 5, 0x5, 10, None) == -7
+    assert lib.det_ce_backward(0x1000, 1, 4, 10, 10, 0, 0x1, 0x2, 0x3, 0x4, 1, 0x5, 9, None) == -4
+    assert lib.det_ce_backward(0x1000, 1, 4, 10, 10, 0, 0x1, 0x2, 0x3, 0x4, 5, 0x5, 10, None) == -7
+    assert lib.det_ce_backward(0x1000, 1, 4, 10, 10, -3, 0x1, 0x2, 0x3, 0x4, 1, 0x5, 10, None) == -7
+    assert lib.det_ce_backward(0x1000, 1, 4, 10, 10, 0, None, 0x2, 0x3, 0x4, 1, 0x5, 10, None) == -1
 
 
 def _no_device():
@@ -174,13 +197,14 @@ def test_workspace_layout_fits_the_reported_size(lib, case, dtype):
                               C.byref(o), ws, n, None)
     assert rc == -6, (rc, lib.det_last_error())
     lo, hi = S // 4, S // 4 + splits[0]
-    n = lib.det_attn_rowmax_workspace_size(C.byref(q), C.byref(k), lo, hi)
-    rc = lib.det_attn_rowmax(C.byref(q), C.byref(k), lo, hi, causal, 0.125, 0x500000, ws, n, None)
-    assert rc == -6, (rc, lib.det_last_error())
-    n = lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), lo, hi)
-    rc = lib.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), 0x500000, lo, hi, causal, 0.125, 0x600000,
-                                 0x700000, 0, ws, n, None)
-    assert rc == -6, (rc, lib.det_last_error())
+    for qlo, qhi in [(0, S), (S // 3, S // 3 + 40)]:
+        n = lib.det_attn_rowmax_workspace_size(C.byref(q), C.byref(k), qlo, qhi, lo, hi)
+        rc = lib.det_attn_rowmax(C.byref(q), C.byref(k), qlo, qhi, lo, hi, causal, 0.125, 0x500000, ws, n, None)
+        assert rc == -6, (rc, lib.det_last_error())
+        n = lib.det_attn_accumulate_workspace_size(C.byref(q), C.byref(k), C.byref(v), qlo, qhi, lo, hi)
+        rc = lib.det_attn_accumulate(C.byref(q), C.byref(k), C.byref(v), 0x500000, qlo, qhi, lo, hi, causal, 0.125,
+                                     0x600000, 0x700000, 0, ws, n, None)
+        assert rc == -6, (rc, lib.det_last_error())
     n = lib.det_attn_workspace_size(C.byref(q), C.byref(k), C.byref(v), causal)
     rc = lib.det_attn_stats(C.byref(q), C.byref(k), C.byref(v), causal, 0.125, C.byref(o), 0x500000, 0x600000, ws,
                             n, None)

@@ -289,12 +289,13 @@ def test_empty_query_rows(A):
 @contextlib.contextmanager
 def generic_path():
     """Send every tile through the generic exact deposit instead of the
-    matrix-core one (DET_FORCE_FALLBACK is read on each call)."""
-    os.environ["DET_FORCE_FALLBACK"] = "1"
+    matrix-core one (the library's testing switch)."""
+    from bitwise_deterministic_exact_pass1_amd import _lib
+    _lib.force_generic(True)
     try:
         yield
     finally:
-        os.environ.pop("DET_FORCE_FALLBACK", None)
+        _lib.force_generic(False)
 
 
 @pytest.mark.parametrize("case", ["tiny", "gqa_small", "d3", "d256", "rect"])

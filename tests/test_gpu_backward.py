@@ -163,14 +163,14 @@ def test_backward_small_workspace_row_chunks(A):
 
 def _backward_both_paths(A, q, k, v, dO, causal, scale):
     """The gradients with the matrix-core sums, then with every tile forced
-    onto the per-term digit sums (DET_FORCE_FALLBACK is read on each call)."""
-    import os
+    onto the per-term digit sums (the library's testing switch)."""
+    from bitwise_deterministic_exact_pass1_amd import _lib
     fast = gpu_backward(A, q, k, v, dO, causal, scale)
-    os.environ["DET_FORCE_FALLBACK"] = "1"
+    _lib.force_generic(True)
     try:
         slow = gpu_backward(A, q, k, v, dO, causal, scale)
     finally:
-        os.environ.pop("DET_FORCE_FALLBACK", None)
+        _lib.force_generic(False)
     return fast, slow
 
 

@@ -82,6 +82,33 @@ def oracle_mean_rows(oracle, xs, ts, m, d, g, N):
     return oracle.ce_backward(xs, ts, m, d, np.full(len(xs), c, np.float32), "none")
 
 
+def test_gradient_bit_exact_all_rows_mean(CE, vocab, oracle):
+    """The whole [4096, 128256] gradient of the mean loss (upstream 1) against
+    the oracle, every element."""
+    x, t, X, T, loss, m, denom = vocab
+    say("ce: full gradient (mean) on the GPU")
+    grad = CE.backward(X, T, m, denom, torch.ones(1).cuda(), "mean").cpu().numpy()
+    say("ce: full gradient (mean) in the oracle")
+    ref = oracle.ce_backward(x, t, m.cpu().numpy(), denom.cpu().numpy(), np.ones(1, np.float32), "mean")
+    assert np.array_equal(u32(grad), u32(ref))
+
+
+@pytest.mark.parametrize("nsplit", [2, 4, 8])
+def test_vocab_shard_gradients_compose_bit_exact(CE, vocab, nsplit):
+    """Each vocabulary shard's gradient (its columns as a view, targets as
+    whole-vocabulary indices, the composed rowmax and denominator) is that
+    shard's columns of the whole gradient, torch.equal, for every reduction."""
+    x, t, X, T, loss, m, denom = vocab
+    V = X.shape[1]
+    bounds = np.linspace(0, V, nsplit + 1).astype(int).tolist()
+    for reduction, g in (("mean", torch.ones(1)), ("sum", torch.tensor([0.5])), ("none", torch.full((4096,), 0.75))):
+        whole = CE.backward(X, T, m, denom, g.cuda(), reduction)
+        parts = [CE.backward(X[:, lo:hi], T, m, denom, g.cuda(), reduction, v0=lo)
+                 for lo, hi in zip(bounds[:-1], bounds[1:])]
+        assert torch.equal(torch.cat(parts, 1), whole), (nsplit, reduction)
+        del whole, parts
+
+
 @pytest.mark.parametrize("nsplit", [1, 2, 4, 8])
 def test_vocab_split_invariance(CE, vocab, nsplit):
     x, t, X, T, loss, m, denom = vocab

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from bitwise_deterministic_exact_pass1_amd import workloads as W
+from bitwise_deterministic_exact_pass1_amd import _lib, workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -77,13 +77,13 @@ def test_sweep_backward(A, oracle, seed):
         tag = f"seed {seed} case {c}: q {tuple(q.shape)} k {tuple(k.shape)} {q.dtype} causal={causal} force={force}"
         print(tag, file=sys.stderr, flush=True)
         if force:
-            os.environ["DET_FORCE_FALLBACK"] = "1"
+            _lib.force_generic(True)
         try:
             Q, K, V = q.cuda(), k.cuda(), v.cuda()
             out, m, den = A.det_attn_with_stats(Q, K, V, causal, scale)
             got = A.det_attn_backward(Q, K, V, out, dO.cuda(), m, den, causal, scale)
         finally:
-            os.environ.pop("DET_FORCE_FALLBACK", None)
+            _lib.force_generic(False)
         ref = oracle.attn_backward(q, k, v, dO, causal, scale)
         for name, a, b in zip(("dq", "dk", "dv"), got, ref):
             assert np.array_equal(_bits(a), _bits(b)), f"{tag}: {name}"
