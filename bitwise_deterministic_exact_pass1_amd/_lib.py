@@ -47,6 +47,7 @@ SIGNATURES = {
     "det_debug_force_generic": (C.c_int, [_I32]),
     "det_attn_workspace_size": (_SZ, [_T, _T, _T, _I32]),
     "det_attn": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _SZ, _P]),
+    "det_attn_noalloc": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P]),
     "det_attn_stats": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _P, _P, _SZ, _P]),
     "det_attn_backward_workspace_size": (_SZ, [_T, _T, _T, _I32]),
     "det_attn_backward": (C.c_int, [_T, _T, _T, _T, _T, _P, _P, _I32, _D, _O, _O, _O, _P, _SZ, _P]),

@@ -493,6 +493,26 @@ int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int3
     return fused_attn(q, k, v, causal, scale, o, nullptr, nullptr, workspace, ws_bytes, stream);
 }
 
+int det_attn_noalloc(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
+                     const det_out *o, void *stream) {
+    int rc;
+    if ((rc = check_qkv(q, k, v, causal))) return rc;
+    if (q->S > 0 && (rc = check_out(o))) return rc;
+    const AttnGeom g = geom(q, k, causal, scale);
+    const bool mf = use_mfma_scores(q);
+    const size_t need_min = g.Sq > 0 ? bytes_fused(g, mf, std::min<int64_t>(g.Sq, kRowTile)) : 0;
+    if (need_min > kNoAllocBytes)
+        return fail(DET_E_WORKSPACE,
+                    "det_attn_noalloc: one %d-row chunk of this problem needs %zu bytes of scratch; the fixed "
+                    "scratch holds %zu (use det_attn with a workspace)",
+                    kRowTile, need_min, kNoAllocBytes);
+    if (g.Sq == 0) return ok();
+    void *scratch = nullptr;
+    size_t cap = 0;
+    HIP_TRY(noalloc_scratch(&scratch, &cap), "noalloc scratch address");
+    return fused_attn(q, k, v, causal, scale, o, nullptr, nullptr, scratch, cap, stream);
+}
+
 int det_attn_stats(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
                    const det_out *o, float *rowmax, double *den64, void *workspace, size_t ws_bytes, void *stream) {
     if (q && q->S > 0 && (!rowmax || !den64)) return fail(DET_E_NULL, "rowmax or den64 is NULL");

@@ -56,6 +56,11 @@ void prof_enable(bool on);
 // "name count total_ms" lines for the launches since prof_enable(true).
 size_t prof_report(char *buf, size_t len);
 
+// ---- the fixed device scratch of det_attn_noalloc (noalloc.hip): its size,
+// and its device address on the current device (looked up once per device).
+constexpr size_t kNoAllocBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void **ptr, size_t *bytes);
+
 // ---- workspace carving (all offsets 256-byte aligned)
 size_t align256(size_t n);
 

@@ -122,6 +122,21 @@ size_t det_attn_workspace_size(const det_tensor *q, const det_tensor *k, const d
 int det_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
              const det_out *o, void *workspace, size_t ws_bytes, void *stream);
 
+/* det_attn for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and the same bits as det_attn, with no workspace argument.  Its
+ * scratch is the library's own fixed device array of DET_NOALLOC_BYTES
+ * (64 MiB), one per GPU the library runs on, held until the process ends; the
+ * call allocates nothing.  Query rows are taken in chunks that fit it; a
+ * problem whose smallest chunk (32 query rows) does not fit gets
+ * DET_E_WORKSPACE before anything is launched.  Every call on one GPU uses
+ * that GPU's one array, so calls that overlap on a GPU (other threads or
+ * streams) race and must be serialized by the caller; nothing in the array
+ * needs to start at zero.  Other errors as det_attn. */
+enum { DET_NOALLOC_BYTES = 64 << 20 };
+int det_attn_noalloc(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
+                     const det_out *o, void *stream);
+
 /* det_attn plus the two per-row values its gradients need (det-attn page,
  * "Method": the global row max and the exact denominator): rowmax (device)
  * f32 [B][Hq][Sq] and den64 (device) f64 [B][Hq][Sq] = RN64(DEN).  Same
