@@ -187,24 +187,40 @@ size_t bytes_rowmax(const AttnGeom &g, bool mfma, int64_t ni, int64_t kv_len) {
     return score_fixed_bytes(g, mfma, kv_len) + score_chunk_bytes(g, mfma, ni, kv_len) + align256((size_t)bh * ni * 4);
 }
 
+// Stored scores between the passes: only the f32 path keeps them (bf16 scores
+// are recomputed in pass 2 from the digit rows pass 1 prepared).
+size_t stored_score_bytes(bool mfma, int64_t rows, int64_t W) { return mfma ? 0 : align256((size_t)rows * W * 4); }
+
 size_t bytes_accumulate(const AttnGeom &g, bool mfma, int64_t ni, int64_t W) {
     const int64_t bh = g.B * g.Hq;
     return vprep_bytes(g, W) + score_fixed_bytes(g, mfma, W) + score_chunk_bytes(g, mfma, ni, W) +
-           align256((size_t)bh * ni * W * 4) + align256((size_t)bh * ((ni + 31) / 32) * 4);
+           stored_score_bytes(mfma, bh * ni, W) + align256((size_t)bh * ((ni + 31) / 32) * 4);
 }
 
 size_t bytes_fused(const AttnGeom &g, bool mfma, int64_t ni) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, g.Skv) + score_fixed_bytes(g, mfma, g.Skv) + score_chunk_bytes(g, mfma, ni, g.Skv) +
-           align256((size_t)rows * 4) + align256((size_t)rows * g.Skv * 4) + pv_fallback_bytes(g, ni);
+           align256((size_t)rows * 4) + stored_score_bytes(mfma, rows, g.Skv) + pv_fallback_bytes(g, ni);
 }
 
 size_t bytes_sharded(const AttnGeom &g, bool mfma, int64_t ni, int64_t maxlen) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, maxlen) + score_fixed_bytes(g, mfma, maxlen) + score_chunk_bytes(g, mfma, ni, maxlen) +
-           align256((size_t)rows * 4) + align256((size_t)rows * maxlen * 4) + align256((size_t)rows * 4) +
+           align256((size_t)rows * 4) + stored_score_bytes(mfma, rows, maxlen) + align256((size_t)rows * 4) +
            align256((size_t)bh * ((ni + 31) / 32) * 4) +
            align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8);
+}
+
+// Pass 2's score source for rows [i0, i1) against [lo, hi): stored scores, or
+// the digit rows in kprep / the chunk workspace (with pass 1's score slots when
+// pass 1 ran on the same rows and range just before: `slots`).
+PvSrc pv_src(const Tensor &tq, const Tensor &tk, const AttnGeom &g, bool mfma, void *kprep, void *cws, float *sc,
+             int64_t i0, int64_t i1, int64_t lo, int64_t hi, bool slots = false) {
+    if (mfma) return qk_pv_src(tq, tk, g, kprep, cws, i1 - i0, hi - lo, slots);
+    PvSrc p{};
+    p.scores = sc;
+    p.W = hi - lo;
+    return p;
 }
 
 VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
@@ -370,7 +386,7 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
     // per-chunk regions, sized for the largest chunk and reused by every chunk
     void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, W));
-    float *sc = c0.take<float>(bh * chunk * W);
+    float *sc = mf ? nullptr : c0.take<float>(bh * chunk * W);
     int *flags = c0.take<int>(bh * ((chunk + 31) / 32));
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
     // only rows [q_lo, q_hi) of each head are touched
@@ -383,11 +399,16 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
         const int64_t i1 = std::min(q_hi, i0 + chunk);
         // the first chunk's launches also prepare K and V
         const bool first = i0 == q_lo;
-        HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, first, true, first ? &vp : nullptr, cws, i0, i1, kv_lo, kv_hi,
-                           sc, nullptr, 0, 0, s),
-                "scores");
-        HIP_TRY(launch_pv(tv, g, vp, sc, rowmax, nullptr, g.Sq, 0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr,
-                          nullptr, num, den, rows, g.Sq, 0, ff, s),
+        if (mf)  // the digit rows pass 2 recomputes the scores from (and V's, on the first chunk)
+            HIP_TRY(launch_qkv_prep(tq, tk, tv, g, kprep, first, true, first ? &vp : nullptr, cws, i0, i1, kv_lo, kv_hi,
+                                    s),
+                    "prepare");
+        else
+            HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, first, true, first ? &vp : nullptr, cws, i0, i1, kv_lo,
+                               kv_hi, sc, nullptr, 0, 0, s),
+                    "scores");
+        HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, mf, kprep, cws, sc, i0, i1, kv_lo, kv_hi), rowmax, nullptr, g.Sq,
+                          0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr, nullptr, num, den, rows, g.Sq, 0, ff, s),
                 "deposit");
     }
     HIP_TRY(launch_normalize_rows(num, kNumDigits, rows * g.D, bh, g.Sq, q_lo, q_hi, g.D, s), "normalize num");
@@ -469,7 +490,7 @@ static int fused_attn(const det_tensor *q, const det_tensor *k, const det_tensor
     const int64_t crows = bh * chunk, ctiles = (chunk + 31) / 32;
     void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, g.Skv));
     uint32_t *keys = c0.take<uint32_t>(crows);
-    float *sc = c0.take<float>(crows * g.Skv);
+    float *sc = mf ? nullptr : c0.take<float>(crows * g.Skv);
     int *flags = c0.take<int>(bh * ctiles);
     int64_t *fnum = c0.take<int64_t>(kNumDigits * bh * ctiles * 32 * g.D);
     int64_t *fden = c0.take<int64_t>(kDenDigits * bh * ctiles * 32);
@@ -478,11 +499,13 @@ static int fused_attn(const det_tensor *q, const det_tensor *k, const det_tensor
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
         // the first chunk's launches also prepare K and V
+        // pass 1 (bf16: the row maxima only; f32: the scores are kept for pass 2)
         HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, true, i0 == 0 ? &vp : nullptr, cws, i0, i1, 0, g.Skv, sc,
                            keys, ni, i0, s),
                 "scores");
-        HIP_TRY(launch_pv(tv, g, vp, sc, nullptr, keys, ni, i0, i0, i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr,
-                          nullptr, 0, 0, 0, ff, s, stat_m, stat_den, g.Sq),
+        HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, mf, kprep, cws, sc, i0, i1, 0, g.Skv, true), nullptr, keys, ni, i0, i0,
+                          i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr, nullptr, 0, 0, 0, ff, s, stat_m, stat_den,
+                          g.Sq),
                 "deposit");
     }
     return ok();
@@ -657,7 +680,7 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         void *kprep = c.take<char>(score_fixed_bytes(g, mf, ml));
         void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, ml));
         uint32_t *keys = c.take<uint32_t>(rows);
-        float *sc = c.take<float>(rows * ml);
+        float *sc = mf ? nullptr : c.take<float>(rows * ml);
         float *rm_acc = c.take<float>(rows);
         int *flags = c.take<int>(bh * ((ni + 31) / 32));
         int64_t *num_acc = c.take<int64_t>(kNumDigits * rows * g.D);
@@ -688,10 +711,13 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
             if (h <= l) continue;
-            HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, false, &vp, cws, i0, i1, l, h, sc, nullptr, 0, 0, s),
-                    "scores");
-            HIP_TRY(launch_pv(tv, g, vp, sc, rm_acc, nullptr, ni, i0, i0, i1, l, h, flags, nullptr, nullptr, nullptr,
-                              num_acc, den_acc, rows, ni, i0, ff, s),
+            if (mf)  // this shard's K and V digit rows; Q's are kept from pass 1
+                HIP_TRY(launch_qkv_prep(tq, tk, tv, g, kprep, true, false, &vp, cws, i0, i1, l, h, s), "prepare");
+            else
+                HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, false, &vp, cws, i0, i1, l, h, sc, nullptr, 0, 0, s),
+                        "scores");
+            HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, mf, kprep, cws, sc, i0, i1, l, h), rm_acc, nullptr, ni, i0,
+                              i0, i1, l, h, flags, nullptr, nullptr, nullptr, num_acc, den_acc, rows, ni, i0, ff, s),
                     "deposit");
         }
         HIP_TRY(launch_normalize(num_acc, rows * g.D, kNumDigits, s), "normalize");

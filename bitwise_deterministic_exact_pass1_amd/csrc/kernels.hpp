@@ -84,6 +84,7 @@ hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t B_Hq, in
                               int64_t out_row0, hipStream_t s);
 
 // ---- pass-1 scores of bf16 inputs on the matrix cores (qk.hip)
+constexpr int kQKmax = 4;  // balanced base-256 digits per Q or K digit row (32-bit integers)
 bool qk_uses_mfma(const Tensor &q);
 size_t qk_kprep_bytes(const AttnGeom &g, int64_t kv_len);
 size_t qk_chunk_bytes(const AttnGeom &g, int64_t ni, int64_t kv_len);
@@ -139,6 +140,38 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
 
 // ---- pass 2 on the matrix cores (pv.hip)
 
+// Where pass 2 takes the scores of a block from.
+struct PvSrc {
+    // stored pass-1 scores [bh][ni][W] of the chunk's rows and the key range
+    // (f32 inputs), or null: the scores are recomputed
+    const float *scores;
+    int64_t W;
+    // recomputed (bf16 inputs): the chunk's Q digit rows and the key range's K
+    // digit rows as the score path laid them out ([row][kQKmax][Dp64] bytes and
+    // one int4 {grid, digit count, log2 bound} per row; Q rows bh * ni_pad + i - i0,
+    // K rows bhk * kv_pad + j - kv_lo)
+    const int8_t *qdig, *kdig;
+    const int4 *qinfo, *kinfo;
+    int64_t ni_pad, kv_pad, Dp64;
+    double scale;
+    // the bf16 rows themselves, for the fp64 chain of the pairs outside the
+    // matrix cores' exactness bound
+    const void *q, *k;
+    int64_t qsB, qsH, qsS, ksB, ksH, ksS;
+    // or null: query rows that need more digits than the digit rows hold have
+    // their scores by the fp64 chain from pass 1 of the same chunk and key
+    // range: qslot[Q row] >= 0 is the row's slot, slots[slot * kv_pad + j - kv_lo]
+    const int *qslot;
+    const float *slots;
+    int64_t slot_bytes;
+};
+// The recomputed-score source of a chunk of ni query rows against a key range
+// of kv_len keys, from the workspace parts the score path prepared; slots:
+// pass 1 ran on this chunk and key range just before, and its score slots of
+// rows with many digits are used.
+PvSrc qk_pv_src(const Tensor &q, const Tensor &k, const AttnGeom &g, void *kprep, void *chunk_ws, int64_t ni,
+                int64_t kv_len, bool slots);
+
 // Prepared V of one key range: per-column grid exponents and balanced int8
 // digits in MFMA lane order.
 struct VPrep {
@@ -159,15 +192,23 @@ size_t vrare_bytes(const AttnGeom &g);
 size_t pv_fallback_bytes(const AttnGeom &g, int64_t rows_i);
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
                         hipStream_t s);
+// V's digit slices alone (after its column statistics).
+hipError_t launch_vslice(const VJob &J, hipStream_t s);
+// The digit rows pass 2 recomputes scores from, without computing any: K's
+// for [kv_lo, kv_hi) (prep_k), the chunk's Q rows [i0, i1) (prep_q) and, with
+// vp, V's column statistics in the same launch, then V's digit slices.
+hipError_t launch_qkv_prep(const Tensor &q, const Tensor &k, const Tensor &v, const AttnGeom &g, void *kprep,
+                           bool prep_k, bool prep_q, VPrep *vp, void *chunk_ws, int64_t i0, int64_t i1, int64_t kv_lo,
+                           int64_t kv_hi, hipStream_t s);
 // With `o`, stat_m / stat_den (both or neither) also receive each row's max
 // and RN64(DEN) at [bh * stat_rows + i].
-// Exact NUM/DEN of query rows [i0,i1) against keys [kv_lo,kv_hi) from stored
-// scores (chunk layout [bh][i-i0][j-kv_lo]) and rowmax[bh*rm_rows + i - rm_row0]
-// (or, when rowmax is null, the order keys rowmax_keys at the same place).
-// With `o` the tile is finalized into o; otherwise its exact values are added
-// into the digit planes num/den (rows bh*rows_per_bh + i - row0).  Tiles the
-// matrix-core path cannot represent exactly are redone by the generic path.
-hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
+// Exact NUM/DEN of query rows [i0,i1) against keys [kv_lo,kv_hi), with scores
+// from `src` and rowmax[bh*rm_rows + i - rm_row0] (or, when rowmax is null, the
+// order keys rowmax_keys at the same place).  With `o` the tile is finalized
+// into o; otherwise its exact values are added into the digit planes num/den
+// (rows bh*rows_per_bh + i - row0).  Tiles the matrix-core path cannot
+// represent exactly are redone by the generic path (a second launch).
+hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const PvSrc &src, const float *rowmax,
                      const uint32_t *rowmax_keys, int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
                      int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
                      int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s,

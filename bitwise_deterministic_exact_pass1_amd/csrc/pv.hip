@@ -1,9 +1,10 @@
 // pv.hip -- pass 2 of the exact softmax on the matrix cores.
 //
 // The det-attn page ("Method") needs NUM_id = sum_j w_ij V_jd and
-// DEN_i = sum_j w_ij exactly.  Both factors are turned into integers on fixed
-// grids, split into balanced base-256 digits, and multiplied on the int8
-// matrix cores, which add exactly in int32:
+// DEN_i = sum_j w_ij exactly, with w_ij = RN32(exp_det(RN64(s_ij - m_i))).
+// Both factors are turned into integers on fixed grids, split into balanced
+// base-256 digits, and multiplied on the int8 matrix cores, which add exactly
+// in int32:
 //
 //   W_ij = w_ij * 2^46                 (an integer when w >= 2^-23: 24-bit mantissa)
 //   Vi_jd = V_jd * 2^-g_d              (g_d = the smallest lsb exponent in column d)
@@ -16,14 +17,24 @@
 // class, which nothing above it absorbs, is moved into an int64 in LDS), so
 // the result is the exact NUM whatever the order of keys, blocks or
 // instructions, for any key range the launcher admits.  DEN is the exact sum
-// of the W_ij, kept per thread in int64 halves that are folded every 8192
-// keys and added up per row in 128 bits.  A tile whose weights do not fit the
-// grid (w < 2^-23, or w > 1 from a rowmax below the scores) or whose V columns
-// need more than five digits is redone by the generic exact path (windowed
-// binary64 sums into digit planes) by the same workgroup: results never depend
-// on which path ran.
+// of the W_ij, kept per lane in int64 halves that are folded every 8192 keys
+// and added up per row in 128 bits.
+//
+// The scores s_ij of bf16 inputs are not stored between the passes: the
+// weight-making waves recompute them on the matrix cores from the digit rows
+// of Q and K that pass 1 prepared (the exactness argument of qk.hip: within
+// the per-pair bound the integer dot product IS the fp64 chain's result), and
+// run the fp64 chain itself for the rare pairs outside that bound.  f32 inputs
+// keep their pass-1 scores in the workspace.
+//
+// A tile whose weights do not fit the grid (w < 2^-23, or w > 1 from a rowmax
+// below the scores) or whose V columns need more than five digits is flagged
+// and redone by the generic exact path (windowed binary64 sums into digit
+// planes) in k_pv_fix, which also adds the exact remainders of V entries below
+// their column grid: results never depend on which path ran.
 #include "dev_math.hpp"
 #include "kernels.hpp"
+#include "qkrow.hpp"
 #include "vprep.hpp"
 
 #include <algorithm>
@@ -36,6 +47,11 @@ constexpr int kAw = 6;                  // digits of W
 constexpr int kSw = 8 * kAw - 2;        // W = w * 2^46, |W| <= 2^46 fits six balanced digits
 constexpr int kNC = kAw + kBmax - 1;    // shift classes s = a + b
 constexpr int kCarryEvery = 256;        // blocks (8192 keys) between carry passes
+constexpr int kPW = 4;                  // weight-making ("producer") waves of the pass-2 kernel
+constexpr int kDeferCap = 1024;         // deferred pairs a tile can hold (more: the tile takes the generic path)
+
+// Tile flags written by the pass-2 kernel and read by k_pv_fix.
+constexpr int kTileDone = 0, kTileGeneric = 1;
 
 // ---------------------------------------------------------------- V preparation
 
@@ -50,19 +66,19 @@ __global__ __launch_bounds__(64) void k_vslice(VJob J) {
     vslice_block<TV>(J, blockIdx.x, blockIdx.y, blockIdx.z, threadIdx.x);
 }
 
-// ---------------------------------------------------------------- the MFMA kernels
+// ---------------------------------------------------------------- arguments
 
 struct PvArgs {
-    const float *scores;  // [bh][ni][W] chunk scores
+    PvSrc src;
     const float *rowmax;          // rowmax[bh*rm_rows + i - rm_row0], or null and then
     const uint32_t *rowmax_keys;  // its order keys at the same place
     int64_t rm_rows, rm_row0;
-    int64_t ni, W, i0, kv_lo, kv_hi;
+    int64_t ni, i0, kv_lo, kv_hi;
     int64_t Hq, Hkv, group, D, Dp32, nKB;
     int causal;
     const v4i *vsl;
     const int *colgrid, *grpB;
-    int *flags;  // [bh][ntiles]: 1 = the tile is left to the generic path
+    int *flags;  // [bh][ntiles]: kTileGeneric = the tile is left to the generic path
     int64_t ntiles;
     int force_fallback;
     // fused output
@@ -71,7 +87,7 @@ struct PvArgs {
     // digit output (accumulate): num [14][plane_rows][D], den [9][plane_rows]
     int64_t *num, *den;
     int64_t plane_rows, rows_per_bh, row0;
-    // the generic path of flagged tiles: V itself and (fused) 32-row digit scratch per tile
+    // the generic path: V itself and (fused) 32-row digit scratch per tile
     const void *v;
     int vdtype;
     int64_t vsB, vsH, vsS;
@@ -91,16 +107,54 @@ __device__ __forceinline__ float pv_rowmax(const PvArgs &A, int64_t bh, int64_t 
     return A.rowmax_keys ? key_value(A.rowmax_keys[at]) : A.rowmax[at];
 }
 
+// The score of query row i and key j of head bh by the rule itself: the
+// stored pass-1 score (f32 inputs), or the fp64 fma chain over d ascending
+// from +0 of the bf16 rows, then RN32(RN64(scale * dot)).  The rows are read
+// 32 dimensions at a time with all of a chunk's loads issued before its
+// chain steps (16-byte loads where both rows allow them).
+__device__ __forceinline__ float pv_score(const PvArgs &A, int64_t bh, int64_t i, int64_t j) {
+    const PvSrc &S = A.src;
+    if (S.scores) return S.scores[(bh * A.ni + (i - A.i0)) * S.W + (j - A.kv_lo)];
+    const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group;
+    const bf16_t *qr = (const bf16_t *)S.q + b * S.qsB + hq * S.qsH + i * S.qsS;
+    const bf16_t *kr = (const bf16_t *)S.k + b * S.ksB + hk * S.ksH + j * S.ksS;
+    const int D = (int)A.D;
+    double acc = 0.0;
+    if (D % 32 == 0 && (((uintptr_t)qr | (uintptr_t)kr) & 15) == 0) {
+        for (int d0 = 0; d0 < D; d0 += 32) {
+            uint4 qv[4], kv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                qv[t] = ((const uint4 *)(qr + d0))[t];
+                kv[t] = ((const uint4 *)(kr + d0))[t];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const uint32_t qw[4] = {qv[t].x, qv[t].y, qv[t].z, qv[t].w};
+                const uint32_t kw[4] = {kv[t].x, kv[t].y, kv[t].z, kv[t].w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    acc = fma((double)__uint_as_float(qw[u] << 16), (double)__uint_as_float(kw[u] << 16), acc);
+                    acc = fma((double)__uint_as_float(qw[u] & 0xffff0000u), (double)__uint_as_float(kw[u] & 0xffff0000u),
+                              acc);
+                }
+            }
+        }
+    } else {
+        for (int d = 0; d < D; ++d)
+            acc = fma((double)elem<bf16_t>::to_f32(qr[d]), (double)elem<bf16_t>::to_f32(kr[d]), acc);
+    }
+    return (float)(S.scale * acc);
+}
 
-// Weights of one 32-key block for the calling thread: KPT consecutive keys of
-// one row with scores sc[]; the first nv of them are visible.  w =
-// RN32(exp_det(s - m)) and W = w 2^46 = M << (E + 23) for the f32 w =
-// M 2^(E-23), an integer for 2^-23 <= w <= 1 (other nonzero weights set bad).
-// The six balanced base-256 digits of W are the bytes of W + 0x808080808080
-// with their top bit flipped (digit set [-128, 127], the unique such
-// representation).  Digit a of the KPT keys goes to dst + a*1024 (MFMA lane
-// order, set up by the caller).  Returns the mask of digits nonzero for this
-// thread and adds W to wsum.
+// Weights of KPT consecutive keys of one row for the calling lane, with
+// scores sc[]; the first nv of them are visible.  w = RN32(exp_det(s - m)) and
+// W = w 2^46 = M << (E + 23) for the f32 w = M 2^(E-23), an integer for
+// 2^-23 <= w <= 1 (other nonzero weights set bad).  The six balanced
+// base-256 digits of W are the bytes of W + 0x808080808080 with their top bit
+// flipped (digit set [-128, 127], the unique such representation).  Digit a of
+// the KPT keys goes to dst + a*1024 (MFMA lane order, set up by the caller).
+// Returns the mask of digits nonzero for this lane and adds W to wsum.
 //
 // Every key runs the same instructions: exp_det's cutoff (t < -104 gives 0)
 // and the visibility are selects after the arithmetic, on an argument clamped
@@ -147,8 +201,6 @@ __device__ __forceinline__ uint32_t block_weights(const float (&sc)[KPT], float 
     return nzm;
 }
 
-constexpr int kPW = 4;  // producer waves of the pass-2 kernel
-
 // OR of a kAw-bit mask over the wave, by one ballot per bit (no LDS traffic).
 __device__ __forceinline__ uint32_t wave_or_mask(uint32_t nz) {
     uint32_t r = 0;
@@ -158,34 +210,38 @@ __device__ __forceinline__ uint32_t wave_or_mask(uint32_t nz) {
     return r;
 }
 
-// LDS of the pass-2 kernel: W digits of two key blocks, the producers'
-// staged scores of two blocks, digit masks, row sums, the bad-tile flag, and
-// the consumers' int64 parts of the top class (tiles of 8192 keys or more).
-struct PvShared {
+// K digit rows of one 32-key block in LDS (recomputed scores, ND 64-dim
+// chunks per row): each row padded by 16 bytes, so the 16 lanes of a read
+// pass fetch 16 different keys from disjoint sets of banks.
+template <int ND> struct PvKRow {
+    static constexpr int RB = kQKmax * 64 * ND;  // digit bytes of one K (or Q) row
+    static constexpr int KROW = RB + 16;
+};
+
+// LDS of the pass-2 kernel: W digits of two key blocks, K digit rows and key
+// statistics of two blocks (recomputed scores: per key its statistics and
+// grid, per 16-key half the largest digit count and bound), digit masks, row
+// sums, the bad-tile flag, and the consumers' int64 parts of the top class
+// (tiles of 8192 keys or more).
+template <int ND> struct PvShared {
     uint8_t dig[2][kAw * 1024];
-    float sc[2][32][32];
+    uint8_t kd[2][ND > 0 ? 32 * PvKRow<ND>::KROW : 16];
+    int4 ki[2][32];
+    int kg[2][32];
+    int2 kh[2][2];
+    // pairs left out of the matrix-core scores (rule outside its bound), per
+    // tile parity: count and {row in tile, key - kv_lo}; their chain scores
+    // for the extra block being made
+    int dn[2];
+    int2 dl[2][kDeferCap];
+    float dsc[32];
     uint32_t mask[2][kPW];
     // per tile parity, so that a tile's finalize overlaps the next tile's start
-    int64_t den_hi[2][32], den_lo[2][32];  // exact sum of W per row: hi 2^32 + lo, lo in [0, 2^32)
-    double d64[2][32];   // RN64(DEN) of the row
+    unsigned long long den_hi[2][32], den_lo[2][32];  // exact sum of W per row: hi 2^32 + lo
+    double d64[2][32];                                // RN64(DEN) of the row
     int bad[2];
     int64_t top[4][16][64];  // [consumer wave][accumulator register][lane]
 };
-
-// Pass 2 of a 32-row tile for the 32-dim groups G0 .. G0+NG-1.
-//
-// NG consumer waves, one per group, run C_s += W_a x V_b (s = a + b) on the
-// matrix cores, with their V digits fetched from global memory one block
-// ahead; kPW producer waves turn the next 32-key block's scores into W
-// digits in LDS meanwhile (double buffered, one barrier per block).  The two
-// roles run separate code with the same barriers, so the weight arithmetic on
-// the vector ALUs overlaps the matrix-core work and neither role's registers
-// are held in the other.  Producers stage the scores of the block after next
-// in LDS, so every global load has a whole block of arithmetic to arrive in.
-// DEN (the exact sum of W per row) stays in the producers' registers.  At the
-// end the consumers finalize the exact NUM and DEN to o or add them into
-// digit planes.  A tile whose weights or V columns do not fit the grids is
-// flagged for the generic path and produces no output here.
 
 struct PvTile {
     int64_t b, hq, bhk, it0, i_end, nG, jhi;
@@ -216,134 +272,402 @@ __device__ __forceinline__ PvTile pv_tile_of(const PvArgs &A, int64_t bh, int64_
     return T;
 }
 
-// Producer side of one tile: thread ptid of the kPW producer waves.
-// Returns whether the tile needs the generic path (known to both roles after
-// the tile's last barrier).
-template <int NG>
+// ---------------------------------------------------------------- producers
+//
+// Producer wave pw owns, in every 32-key block, the 16 x 16 sub-block of
+// query rows qr0 = 16 (pw & 1) .. +15 and keys kc0 = 16 (pw >> 1) .. +15; lane
+// l has row qr0 + l % 16 and the four keys kc0 + 4 (l / 16) + 0..3.  With
+// recomputed scores the wave forms S^T = K Q^T on v_mfma_i32_16x16x64_i8
+// (A = the block's K digit rows from LDS, B = the tile's Q digit rows held in
+// registers; lane l supplies row / column l % 16 with the 16 dims
+// 16 (l / 16) .. of each 64), whose result register r of lane l is exactly
+// key kc0 + 4 (l / 16) + r of row qr0 + l % 16.
+
+// The lane's Q digit row (B operand of every block), its grid exponent, digit
+// count and log2 bound of max|Qi| (qk.hip).
+template <int ND> struct PvQRow {
+    v4i Bq[kQKmax][ND > 0 ? ND : 1];
+    int4 qi;        // {grid, digit count, log2 bound, packed second grid and position} (qkrow.hpp)
+    int qcnt, qbnd;  // the largest digit count and bound of the wave's rows without a slot (wave-uniform)
+    int slot;        // the row's score slot (pass 1's chain scores), or -1
+    bool slots;      // a row of the wave has one (wave-uniform)
+};
+
+// The digit products of the lane's 16 x 16 item over NQ digits per side
+// (NQ = 3 when every row and key of the item has at most three digits: the
+// fourth digit planes are zero and are skipped) into 2 NQ - 1 shift classes.
+template <int ND, int NQ>
+__device__ __forceinline__ void pv_score_products(const PvQRow<ND> &P, const uint8_t *krow, v4i (&C)[2 * NQ - 1]) {
+#pragma unroll
+    for (int c = 0; c < 2 * NQ - 1; ++c) C[c] = v4i{0, 0, 0, 0};
+#pragma unroll
+    for (int n = 0; n < ND; ++n) {
+        v4i Ak[NQ];
+#pragma unroll
+        for (int c = 0; c < NQ; ++c) Ak[c] = *(const v4i *)(krow + c * 64 * ND + 64 * n);
+#pragma unroll
+        for (int c = 0; c < NQ; ++c)
+#pragma unroll
+            for (int a = 0; a < NQ; ++a)
+                C[a + c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ak[c], P.Bq[a][n], C[a + c], 0, 0, 0);
+    }
+}
+
+// Scores of the lane's four keys of a block whose K digit rows and key
+// statistics are in LDS buffer kbuf, recomputed on the matrix cores.  When the
+// item's bound holds for all its pairs (largest row bound plus largest key
+// bound: the common case) that is all.  Otherwise each pair takes the finer
+// test, and the visible pairs outside it are deferred: their score here is
+// -inf (weight 0), and {row in tile, key - kv_lo} goes to the tile's list, from
+// which they are added after the tile's last block with their scores by the
+// rule itself.  r: the lane's row in the tile; jrel: its first key - kv_lo;
+// nv: visible keys among the four.  Returns false when the list is full.
+template <int ND, int NQ>
+__device__ __forceinline__ bool pv_scores_nq(const PvArgs &A, const PvQRow<ND> &P, PvShared<ND> &S, int kbuf, int par,
+                                             int r, int jrel, int nv, int lane, int kc0, bool crude, float (&sc)[4]) {
+    constexpr int KROW = PvKRow<ND>::KROW;
+    const int kk = kc0 + 4 * (lane >> 4);
+    const int4 kg4 = *(const int4 *)&S.kg[kbuf][kk];  // the four keys' grids
+    const int kg[4] = {kg4.x, kg4.y, kg4.z, kg4.w};
+    v4i C[2 * NQ - 1];
+    pv_score_products<ND, NQ>(P, S.kd[kbuf] + (kc0 + (lane & 15)) * KROW + 16 * (lane >> 4), C);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sc[u] = (float)(A.src.scale * qk_dot_value<2 * NQ - 1>(C, u, P.qi.x + kg[u]));
+    if (crude) return true;
+    // the four keys' statistics in registers before any test (read together:
+    // one LDS round trip), then the tests as plain arithmetic
+    const int4 t0 = S.ki[kbuf][kk], t1 = S.ki[kbuf][kk + 1], t2 = S.ki[kbuf][kk + 2], t3 = S.ki[kbuf][kk + 3];
+    int x0 = t0.x, y0 = t0.y, z0 = t0.z, w0 = t0.w, x1 = t1.x, y1 = t1.y, z1 = t1.z, w1 = t1.w;
+    int x2 = t2.x, y2 = t2.y, z2 = t2.z, w2 = t2.w, x3 = t3.x, y3 = t3.y, z3 = t3.z, w3 = t3.w;
+    asm volatile("" : "+v"(x0), "+v"(y0), "+v"(z0), "+v"(w0), "+v"(x1), "+v"(y1), "+v"(z1), "+v"(w1), "+v"(x2),
+                 "+v"(y2), "+v"(z2), "+v"(w2), "+v"(x3), "+v"(y3), "+v"(z3), "+v"(w3));
+    const int4 kis[4] = {int4{x0, y0, z0, w0}, int4{x1, y1, z1, w1}, int4{x2, y2, z2, w2}, int4{x3, y3, z3, w3}};
+    int chain = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        chain |= (u < nv && P.slot < 0 && qk_pair_class(P.qi, kis[u], kQKmax) == kPairChain) ? 1 << u : 0;
+    bool fits = true;
+    if (chain) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if ((chain >> u) & 1) {
+                sc[u] = -__builtin_inff();
+                const int at = atomicAdd(&S.dn[par], 1);
+                if (at < kDeferCap) S.dl[par][at] = int2{r, jrel + u};
+                else fits = false;
+            }
+        }
+    }
+    return fits;
+}
+
+template <int ND>
+__device__ __forceinline__ bool pv_block_scores(const PvArgs &A, const PvQRow<ND> &P, PvShared<ND> &S, int kbuf,
+                                                int par, int r, int jrel, int nv, int lane, int kc0, float (&sc)[4]) {
+    const int2 kh = S.kh[kbuf][kc0 >> 4];
+    const int kcnt = __builtin_amdgcn_readfirstlane(kh.x), kbnd = __builtin_amdgcn_readfirstlane(kh.y);
+    const bool crude = P.qcnt <= kQKmax && kcnt <= kQKmax && P.qbnd + kbnd <= 53;
+    if (P.qcnt <= 3 && kcnt <= 3) return pv_scores_nq<ND, 3>(A, P, S, kbuf, par, r, jrel, nv, lane, kc0, crude, sc);
+    return pv_scores_nq<ND, kQKmax>(A, P, S, kbuf, par, r, jrel, nv, lane, kc0, crude, sc);
+}
+
+// Producer side of one tile: thread ptid of the kPW producer waves.  Returns
+// whether the tile needs the generic path (known to both roles after the
+// tile's last barrier).  Barriers per tile: [A] (the first K blocks staged),
+// [B] (block 0's weights ready), one per key block, [C] (row sums and the bad
+// flag complete), [D] (RN64(DEN) of every row in LDS); the consumers meet the
+// same ones.
+template <int NG, int ND>
 __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t tile, int ptid, int par,
-                                           PvShared &S, uint32_t &rem) {
-    constexpr int NPT = 64 * kPW;  // producer threads
-    constexpr int TPR = NPT / 32;  // producer threads per row
-    constexpr int KPT = 32 / TPR;  // keys per producer thread and block
+                                           PvShared<ND> &S) {
+    constexpr int RB = PvKRow<ND>::RB, KROW = PvKRow<ND>::KROW;
+    constexpr int CPT = ND > 0 ? RB / 128 : 1;  // 16-byte K chunks per producer lane and block
     const PvTile T = pv_tile_of(A, bh, tile);
-    rem = T.rem;
-    if (T.badv) return true;
     const int lane = ptid & 63, pw = ptid >> 6;
-    const int r = ptid / TPR, k0 = (ptid % TPR) * KPT;
-    const int dofs = ((r + 32 * (k0 >> 4)) * 16) + (k0 & 15);
+    const int qr0 = 16 * (pw & 1), kc0 = 16 * (pw >> 1);
+    const int r = qr0 + (lane & 15), k0 = kc0 + 4 * (lane >> 4);
     const int64_t i = T.it0 + r;
     const bool rowok = i < T.i_end;
+    if (ptid < 32) {
+        S.den_hi[par][ptid] = 0;
+        S.den_lo[par][ptid] = 0;
+    }
+    if (T.badv) {
+        __syncthreads();  // [A]
+        __syncthreads();  // [B]
+        __syncthreads();  // [C]
+        __syncthreads();  // [D]
+        return true;
+    }
     const float m = rowok ? pv_rowmax(A, bh, i) : 0.0f;
-    // keys this row sees: [kv_lo, jend), counted from this thread's first key
+    // keys this row sees: [kv_lo, jend), counted from this lane's first key
     // kv_lo + k0 (32-bit: the launcher bounds the key range)
     const int64_t jend = rowok ? (A.causal ? min64(T.jhi, i + 1) : T.jhi) : A.kv_lo;
     const int vis0 = (int)(jend - A.kv_lo - k0);
-    auto nvis = [&](int kb) {  // visible keys among this thread's KPT keys of block kb
-        return max(0, min(KPT, vis0 - kb * kKB));
-    };
-    // The tile's scores through a buffer resource based at its first row: key
-    // kv_lo + j of row r at byte (r W + j) 4.  A lane's offset is fixed and the
-    // block step is the scalar offset, so a load needs no address registers.
-    // Keys past a row's end read the next row or, past the scores array, zero
-    // (buffer bounds); those keys are invisible and their weights discarded.
-    const int64_t row_first = bh * A.ni + (T.it0 - A.i0);
-    const int64_t bytes_left = ((int64_t)gridDim.y * A.ni - row_first) * A.W * 4;
-    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A.scores + row_first * A.W), (short)0, (int)min64(bytes_left, INT32_MAX), 0x00020000);
-    const int voff = (r * (int)A.W + k0) * 4;
-    auto load_scores = [&](int kb, float (&x)[KPT]) {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u)
-            x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, voff + 4 * u, kb * kKB * 4, 0));
-    };
-    float *my0 = &S.sc[0][r][k0], *my1 = &S.sc[1][r][k0];
-    // this thread's sum of W: whi 2^32 + wsum; wsum grows by at most KPT 2^46
-    // per block and is folded into whi every kCarryEvery blocks (< 2^57 between)
+    auto nvis = [&](int kb) { return max(0, min(4, vis0 - kb * kKB)); };
+    const int dofs = ((r + 32 * (k0 >> 4)) * 16) + (k0 & 15);  // this lane's bytes in a W digit plane
+    // this lane's sum of W: whi 2^32 + wsum; wsum grows by at most 4 2^46 per
+    // block and is folded into whi every kCarryEvery blocks (< 2^57 between)
     int64_t wsum = 0, whi = 0;
     bool bad = false;
-    // Scores travel three blocks ahead of their use: loaded into registers,
-    // parked in this thread's LDS slots one block later, read the block after.
-    float pend[KPT];
-    if (T.nblk > 0) {
-        float sc[KPT], s1[KPT];
-        load_scores(0, sc);
-        load_scores(1, s1);
-        load_scores(2, pend);
-        const uint32_t nz = wave_or_mask(block_weights<KPT>(sc, m, nvis(0), S.dig[0] + dofs, wsum, bad));
-        if (lane == 0) S.mask[0][pw] = nz;
+
+    // ---- score sources
+    PvQRow<ND> P;
+    P.slot = -1;
+    P.slots = false;
+    const uint8_t *kbase = nullptr;
+    v4i kst[CPT];
+    int4 kist = int4{0, 0, 0, 0};
+    if constexpr (ND > 0) {
+        const int64_t qrow = bh * A.src.ni_pad + (T.it0 - A.i0) + r;
+        P.qi = A.src.qinfo[qrow];
+        P.slot = A.src.qslot ? A.src.qslot[qrow] : -1;
+        P.slots = __ballot(P.slot >= 0) != 0;
+        // (rows past the end are padding rows: one digit, bound 0; rows with a
+        // slot take their scores from it)
+        int qc = P.slot < 0 ? P.qi.y : 0, qb = P.slot < 0 ? P.qi.z : 0;
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) my1[u] = s1[u];
+        for (int off = 8; off > 0; off >>= 1) {
+            qc = max(qc, __shfl_xor(qc, off, 64));
+            qb = max(qb, __shfl_xor(qb, off, 64));
+        }
+        P.qcnt = __builtin_amdgcn_readfirstlane(qc);
+        P.qbnd = __builtin_amdgcn_readfirstlane(qb);
+        const int8_t *qd = A.src.qdig + qrow * RB + 16 * (lane >> 4);
+#pragma unroll
+        for (int a = 0; a < kQKmax; ++a)
+#pragma unroll
+            for (int n = 0; n < ND; ++n) P.Bq[a][n] = *(const v4i *)(qd + a * 64 * ND + 64 * n);
+        kbase = (const uint8_t *)A.src.kdig + T.bhk * A.src.kv_pad * (int64_t)RB;
     }
-    __syncthreads();
-    // One block step: weights of block kb+1 into the digit buffer the consumers
-    // read next, scores of block kb+3 into `load`, block kb+2's scores (`park`,
-    // loaded one step earlier) into this thread's LDS slots.  The loop is
-    // unrolled by two so that the two register sets swap roles without copies
-    // (a copy of a register still being loaded would wait for the load).
-    auto step = [&](int kb, float (&park)[KPT], float (&load)[KPT]) {
-        const int nb = (kb & 1) ^ 1;
-        if (kb + 1 < T.nblk) {
-            float sc[KPT];
-            load_scores(kb + 3, load);
-            const float *cur = nb ? my1 : my0;
+    // K digit rows of block kb: chunk c = ptid + 256 t is bytes 16 (c % (RB/16)) of key c / (RB/16)
+    auto k_load = [&](int kb) {
+        if constexpr (ND > 0) {
+            const uint8_t *src = kbase + (int64_t)kb * 32 * RB;
 #pragma unroll
-            for (int u = 0; u < KPT; ++u) sc[u] = cur[u];
-            const uint32_t nz = wave_or_mask(block_weights<KPT>(sc, m, nvis(kb + 1), S.dig[nb] + dofs, wsum, bad));
-            if (lane == 0) S.mask[nb][pw] = nz;
-            if (((kb + 1) % kCarryEvery) == 0) {
+            for (int t = 0; t < CPT; ++t) kst[t] = *(const v4i *)(src + (int64_t)(ptid + 256 * t) * 16);
+            if (ptid < 32) kist = A.src.kinfo[T.bhk * A.src.kv_pad + kb * 32 + ptid];
+        }
+    };
+    auto k_store = [&](int buf) {
+        if constexpr (ND > 0) {
+#pragma unroll
+            for (int t = 0; t < CPT; ++t) {
+                const int c = ptid + 256 * t;
+                *(v4i *)(S.kd[buf] + (c / (RB / 16)) * KROW + (c % (RB / 16)) * 16) = kst[t];
+            }
+            // the block's 32 key statistics are in lanes 0..31 of producer wave 0:
+            // their grids, and per 16-key half the largest digit count and bound
+            if (pw == 0) {
+                int kc = kist.y, kb = kist.z;
+#pragma unroll
+                for (int off = 8; off > 0; off >>= 1) {
+                    kc = max(kc, __shfl_xor(kc, off, 64));
+                    kb = max(kb, __shfl_xor(kb, off, 64));
+                }
+                if (lane < 32) {
+                    S.ki[buf][lane] = kist;
+                    S.kg[buf][lane] = kist.x;
+                    if ((lane & 15) == 0) S.kh[buf][lane >> 4] = int2{kc, kb};
+                }
+            }
+        }
+    };
+    // stored scores (f32 inputs): the lane's four scores of block kb through a
+    // buffer resource based at the tile's first row (key kv_lo + j of row r at
+    // byte (r W + j) 4): a lane's offset is fixed and the block step is the
+    // scalar offset; keys past a row's end read the next row or, past the
+    // scores array, zero (buffer bounds): those keys are invisible
+    // Recomputed scores: the same for the score slots of rows that have one
+    // (slot s at byte (s kv_pad + j) 4, key kv_lo + j); the block step is again
+    // the scalar offset.
+    const int64_t row_first = bh * A.ni + (T.it0 - A.i0);
+    const int64_t bytes_left = ND == 0 ? ((int64_t)gridDim.y * A.ni - row_first) * A.src.W * 4 : A.src.slot_bytes;
+    const bool sload = ND == 0 || P.slots;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(ND == 0 ? A.src.scores + row_first * A.src.W : A.src.slots), (short)0,
+        (int)min64(bytes_left, INT32_MAX), 0x00020000);
+    const int voff = ND == 0 ? (r * (int)A.src.W + k0) * 4 : (P.slot >= 0 ? (P.slot * (int)A.src.kv_pad + k0) * 4 : 0);
+    auto s_load = [&](int kb, float (&x)[4]) {
+        if (sload) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                x[u] = __builtin_bit_cast(float,
+                                          __builtin_amdgcn_raw_buffer_load_b32(srs, voff + 4 * u, kb * kKB * 4, 0));
+        }
+    };
+    // the weights of block kb into digit buffer kb & 1 (its K rows are in the
+    // K buffer of the same parity)
+    auto produce = [&](int kb, const float (&stored)[4]) {
+        float sc[4];
+        const int nv = nvis(kb), db = kb & 1;
+        if constexpr (ND > 0) {
+            if (!pv_block_scores<ND>(A, P, S, db, par, r, kb * kKB + k0, nv, lane, kc0, sc)) bad = true;
+            if (P.slots && P.slot >= 0) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) sc[u] = stored[u];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sc[u] = stored[u];
+        }
+        const uint32_t nz = wave_or_mask(block_weights<4>(sc, m, nv, S.dig[db] + dofs, wsum, bad));
+        if (lane == 0) S.mask[db][pw] = nz;
+    };
+
+    // prologue: K blocks 0 and 1 in LDS ([A] makes them visible), block 2 in
+    // registers; block 0's weights ([B] hands them to the consumers).  Stored
+    // scores: blocks 0 and 1 in the two register sets.
+    float s0[4] = {}, s1[4] = {};
+    if (T.nblk > 0) {
+        k_load(0);
+        k_store(0);
+        s_load(0, s0);
+        if (T.nblk > 1) {
+            k_load(1);
+            k_store(1);
+            s_load(1, s1);
+        }
+    }
+    if constexpr (ND > 0) {
+        // the Q row is needed from here on: waiting for it now (it was loaded
+        // before K's blocks 0 and 1, which the stores have waited for) keeps
+        // the block loop free of waits for it, which would also wait for the
+        // prefetched K rows
+#pragma unroll
+        for (int a = 0; a < kQKmax; ++a)
+#pragma unroll
+            for (int n = 0; n < ND; ++n) asm volatile("" ::"v"(P.Bq[a][n]));
+    }
+    __syncthreads();  // [A]
+    if (T.nblk > 2) k_load(2);
+    if (T.nblk > 0) {
+        produce(0, s0);
+        if (T.nblk > 2) s_load(2, s0);
+    }
+    __syncthreads();  // [B]
+    // One block step, while the consumers multiply block kb: block kb+2's K
+    // rows (in registers) into K buffer kb & 1 (block kb's, done with) and
+    // block kb+3's into registers; the weights of block kb+1.  Stored scores of
+    // block kb+1 sit in register set (kb+1) & 1, which then takes block kb+3's
+    // (the loop is unrolled by two so the sets keep their roles without copies).
+    auto step = [&](int kb, float (&set)[4]) {
+        if (kb + 1 < T.nblk) {
+            if constexpr (ND > 0) {
+                if (kb + 2 < T.nblk) {
+                    k_store(kb & 1);
+                    if (kb + 3 < T.nblk) k_load(kb + 3);
+                }
+            }
+            produce(kb + 1, set);
+            if (kb + 3 < T.nblk) s_load(kb + 3, set);
+            if (((kb + 2) % kCarryEvery) == 0) {
                 whi += wsum >> 32;
                 wsum &= 0xffffffffll;
             }
-            float *nxt = nb ? my0 : my1;  // block kb+2 uses buffer (kb+2)&1
-#pragma unroll
-            for (int u = 0; u < KPT; ++u) nxt[u] = park[u];
         }
         __syncthreads();
     };
-    float pend2[KPT];
     for (int kb = 0; kb < T.nblk; kb += 2) {
-        step(kb, pend, pend2);
-        if (kb + 1 < T.nblk) step(kb + 1, pend2, pend);
+        step(kb, s1);
+        if (kb + 1 < T.nblk) step(kb + 1, s0);
     }
-    // exact row sums of W: the TPR threads of a row are consecutive lanes
-    // (each wsum < 2^57, so their sum fits; whi counts units of 2^32)
+    // The deferred pairs (final after the last block's barrier), 32 at a time
+    // as the virtual keys of extra blocks.  Per extra block: their q and k
+    // rows into the K digit buffers (free after the last block; [E0]), their
+    // scores by the rule itself, one lane per pair ([E1] hands them to every
+    // producer lane), the weights of those whose row is the lane's ([E2] hands
+    // them to the consumers, who form the V digits of the pairs' keys).  The
+    // block count and the carry schedule continue those of the tile's keys.
+    if constexpr (ND > 0) {
+        const int ndef = min(S.dn[par], kDeferCap);
+        const int D = (int)A.D;
+        const bf16_t *qb = (const bf16_t *)A.src.q + T.b * A.src.qsB + T.hq * A.src.qsH;
+        const bf16_t *kb0 = (const bf16_t *)A.src.k + T.b * A.src.ksB + (T.hq / A.group) * A.src.ksH;
+        uint16_t *qs = (uint16_t *)S.kd[0], *ks = (uint16_t *)S.kd[1];
+        for (int x = 0; x < (ndef + 31) / 32; ++x) {
+            for (int t = ptid; t < 32 * D; t += 64 * kPW) {
+                const int ee = t / D, d = t - ee * D, e = 32 * x + ee;
+                const int2 E = e < ndef ? S.dl[par][e] : int2{0, 0};  // (padding: the tile's first row and key)
+                qs[t] = qb[(T.it0 + E.x) * A.src.qsS + d].bits;
+                ks[t] = kb0[(A.kv_lo + E.y) * A.src.ksS + d].bits;
+            }
+            __syncthreads();  // [E0]
+            if (ptid < 32) {
+                const int e = 32 * x + ptid;
+                double acc = 0.0;
+#pragma unroll 8
+                for (int d = 0; d < D; ++d)
+                    acc = fma((double)__uint_as_float((uint32_t)qs[ptid * D + d] << 16),
+                              (double)__uint_as_float((uint32_t)ks[ptid * D + d] << 16), acc);
+                S.dsc[ptid] = e < ndef ? (float)(A.src.scale * acc) : -__builtin_inff();
+            }
+            __syncthreads();  // [E1]
+            const int kbv = T.nblk + x, db = kbv & 1;
+            float sc[4];
 #pragma unroll
-    for (int off = 1; off < TPR; off <<= 1) {
+            for (int u = 0; u < 4; ++u) {
+                const int e = 32 * x + k0 + u;
+                sc[u] = (e < ndef && S.dl[par][e].x == r) ? S.dsc[k0 + u] : -__builtin_inff();
+            }
+            const uint32_t nz = wave_or_mask(block_weights<4>(sc, m, 4, S.dig[db] + dofs, wsum, bad));
+            if (lane == 0) S.mask[db][pw] = nz;
+            if (((kbv + 1) % kCarryEvery) == 0) {
+                whi += wsum >> 32;
+                wsum &= 0xffffffffll;
+            }
+            __syncthreads();  // [E2]
+        }
+    }
+    // exact row sums of W: the four lanes of a row (l, l^16, l^32, l^48), then
+    // the two waves of a row half add theirs in LDS (each wsum < 2^57, so four
+    // fit; whi counts units of 2^32)
+#pragma unroll
+    for (int off = 16; off < 64; off <<= 1) {
         wsum += __shfl_xor(wsum, off, 64);
         whi += __shfl_xor(whi, off, 64);
     }
-    if (ptid % TPR == 0) {
-        const int64_t hi = whi + (wsum >> 32), lo = wsum & 0xffffffffll;  // DEN 2^46 = hi 2^32 + lo
-        S.den_hi[par][r] = hi;
-        S.den_lo[par][r] = lo;
-        // correctly rounded RN64(DEN): the 128-bit value (hi >> 32) 2^64 + ((hi << 32) | lo)
-        S.d64[par][r] = i128_to_f64(hi >> 32, ((uint64_t)hi << 32) | (uint64_t)lo, -kSw);
+    if (lane < 16) {
+        const int64_t hi = whi + (wsum >> 32), lo = wsum & 0xffffffffll;
+        atomicAdd(&S.den_hi[par][r], (unsigned long long)hi);
+        atomicAdd(&S.den_lo[par][r], (unsigned long long)lo);
     }
     if (bad) S.bad[par] = 1;
-    __syncthreads();
+    __syncthreads();  // [C]
     const bool generic = S.bad[par] != 0;
-    if (A.stat_den && !generic && rowok && ptid % TPR == 0) {  // (generic tiles write theirs there)
-        A.stat_den[bh * A.stat_rows + i] = S.d64[par][r];
-        A.stat_m[bh * A.stat_rows + i] = m;
+    if (pw < 2 && lane < 16) {
+        // DEN 2^46 = hi 2^32 + lo; RN64(DEN) correctly rounded from its 128 bits
+        const int64_t hi = (int64_t)S.den_hi[par][r] + (int64_t)(S.den_lo[par][r] >> 32);
+        const uint64_t lo = S.den_lo[par][r] & 0xffffffffull;
+        const double d64 = i128_to_f64(hi >> 32, ((uint64_t)hi << 32) | lo, -kSw);
+        S.d64[par][r] = d64;
+        if (A.stat_den && !generic && rowok) {  // (generic tiles write theirs in k_pv_fix)
+            A.stat_den[bh * A.stat_rows + i] = d64;
+            A.stat_m[bh * A.stat_rows + i] = m;
+        }
     }
+    __syncthreads();  // [D]
     return generic;
 }
 
+// ---------------------------------------------------------------- consumers
+
 // The consumer's block loop for a wave whose group has BV V digits (0: no
 // group, barriers only).  Per block: the six W digit fragments of the block
-// are read from LDS up front, the next block's V digits are fetched into the
-// other register set (the loop is unrolled by two so the sets swap roles
-// without copies), and the class sums C_(a+b) += W_a x V_b run on the matrix
-// cores for the W digit planes the producers marked nonzero.
-template <int BV>
-__device__ __forceinline__ void pv_consume_loop(const PvTile &T, const v4i *vb, int lane, int wave, v16i (&C)[kNC],
-                                                PvShared &S) {
+// are read from LDS, the next block's V digits are fetched into the other
+// register set (the loop is unrolled by two so the sets swap roles without
+// copies), and the class sums C_(a+b) += W_a x V_b run on the matrix cores for
+// the W digit planes the producers marked nonzero.
+template <int BV, int ND>
+__device__ __forceinline__ void pv_consume_loop(const PvArgs &A, const PvTile &T, int G, const v4i *vb, int lane, int wave,
+                                                v16i (&C)[kNC], PvShared<ND> &S, int par) {
     v4i VA[BV > 0 ? BV : 1], VB[BV > 0 ? BV : 1];
+    __syncthreads();  // [A]
     if (BV > 0 && T.nblk > 0) {
 #pragma unroll
         for (int s = 0; s < BV; ++s) VA[s] = vb[s * 64];
     }
-    __syncthreads();
+    __syncthreads();  // [B]
     auto step = [&](int kb, const v4i (&cur)[BV > 0 ? BV : 1], v4i (&nxt)[BV > 0 ? BV : 1]) {
         if (BV > 0) {
             const int buf = kb & 1;
@@ -388,21 +712,95 @@ __device__ __forceinline__ void pv_consume_loop(const PvTile &T, const v4i *vb, 
         step(kb, VA, VB);
         if (kb + 1 < T.nblk) step(kb + 1, VB, VA);
     }
+    // extra blocks of deferred pairs (the producers' side says how they are
+    // made): lane l supplies virtual keys 16 (l / 32) + p, p = 0..15, of its
+    // column, whose V digits it forms from V itself as the slices do (the
+    // value toward zero onto the column's grid; entries with bits below it
+    // are the remainders added elsewhere)
+    if constexpr (ND > 0) {
+        const int ndef = min(S.dn[par], kDeferCap);
+        for (int x = 0; x < (ndef + 31) / 32; ++x) {
+            if (BV > 0) {
+                const int64_t d = (int64_t)G * 32 + (lane & 31);
+                const bool dok = d < A.D;
+                const int g = dok ? A.colgrid[T.bhk * A.Dp32 + d] : 0;
+                const int64_t vbase = T.b * A.vsB + (T.bhk % A.Hkv) * A.vsH + (dok ? d : 0);
+                uint64_t U[16];
+#pragma unroll
+                for (int p = 0; p < 16; ++p) {
+                    const int e = 32 * x + 16 * (lane >> 5) + p;
+                    const int64_t j = A.kv_lo + (e < ndef ? S.dl[par][e].y : 0);
+                    const double v = A.vdtype == 0 ? (double)((const float *)A.v)[vbase + j * A.vsS]
+                                                   : (double)elem<bf16_t>::to_f32(((const bf16_t *)A.v)[vbase + j * A.vsS]);
+                    U[p] = (uint64_t)((int64_t)ldexp(dok ? v : 0.0, -g) + 0x8080808080ll);
+                }
+#pragma unroll
+                for (int bb = 0; bb < BV; ++bb) {
+                    uint32_t w4[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        uint32_t pack = 0;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) pack |= ((uint32_t)(U[4 * q + u] >> (8 * bb)) & 255u) << (8 * u);
+                        w4[q] = pack ^ 0x80808080u;
+                    }
+                    VA[bb] = v4i{(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]};
+                }
+            }
+            __syncthreads();  // [E0]
+            __syncthreads();  // [E1]
+            __syncthreads();  // [E2]
+            if (BV > 0) {
+                const int kbv = T.nblk + x, buf = kbv & 1;
+                const uint8_t *dg = S.dig[buf] + lane * 16;
+                uint32_t mask = 0;
+#pragma unroll
+                for (int w = 0; w < kPW; ++w) mask |= S.mask[buf][w];
+                mask = __builtin_amdgcn_readfirstlane(mask);
+#pragma unroll
+                for (int a2 = 0; a2 < kAw; ++a2) {
+                    const v4i Aw = *(const v4i *)(dg + a2 * 1024);
+                    if (mask & (1u << a2)) {
+#pragma unroll
+                        for (int bb = 0; bb < BV; ++bb)
+                            C[a2 + bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aw, VA[bb], C[a2 + bb], 0, 0, 0);
+                    }
+                }
+                if ((kbv % kCarryEvery) == kCarryEvery - 1) {
+#pragma unroll
+                    for (int c = 0; c < kNC - 1; ++c) {
+                        const v16i cc = C[c] >> 8;
+                        C[c] -= cc << 8;
+                        C[c + 1] += cc;
+                    }
+#pragma unroll
+                    for (int rr = 0; rr < 16; ++rr) S.top[wave][rr][lane] += C[kNC - 1][rr];
+                    C[kNC - 1] = v16i{0};
+                }
+            }
+        }
+    }
 }
 
 // Consumer side of one tile: wave `wave` (< NG) owns 32-dim group G0 + wave.
 // Returns whether the tile needs the generic path.
-template <bool FUSED, int NG>
+template <bool FUSED, int NG, int ND>
 __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, int64_t tile, int wave, int par,
-                                           PvShared &S, uint32_t &rem) {
+                                           PvShared<ND> &S) {
     const int tid = threadIdx.x, lane = tid & 63;
     const PvTile T = pv_tile_of(A, bh, tile);
-    rem = T.rem;
     if (T.badv) {
-        if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
+        __syncthreads();  // [A]
+        __syncthreads();  // [B]
+        __syncthreads();  // [C]
+        __syncthreads();  // [D]
+        if (tid == 0) A.flags[bh * A.ntiles + tile] = kTileGeneric;
         return true;
     }
-    if (tid == 0) S.bad[par] = 0;
+    if (tid == 0) {  // (before [A]; the producers set them after [A])
+        S.bad[par] = 0;
+        S.dn[par] = 0;
+    }
     const int64_t G = G0 + wave;
     const bool mine = G < T.nG;
     const int Bv = mine ? A.grpB[T.bhk * T.nG + G] : 0;
@@ -411,7 +809,7 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
 #pragma unroll
     for (int s = 0; s < kNC; ++s) C[s] = v16i{0};
     // the top class's int64 part, used by tiles of kCarryEvery blocks or more
-    const bool longt = T.nblk >= kCarryEvery;
+    const bool longt = T.nblk + kDeferCap / 32 >= kCarryEvery;  // (extra blocks continue the count)
     if (longt) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) S.top[wave][rr][lane] = 0;
@@ -419,19 +817,21 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
     // the block loop with the wave's V digit count as a constant (one copy per
     // count; a wave without a group only meets the barriers)
     switch (mine ? Bv : 0) {
-        case 1: pv_consume_loop<1>(T, vb, lane, wave, C, S); break;
-        case 2: pv_consume_loop<2>(T, vb, lane, wave, C, S); break;
-        case 3: pv_consume_loop<3>(T, vb, lane, wave, C, S); break;
-        case 4: pv_consume_loop<4>(T, vb, lane, wave, C, S); break;
-        case 5: pv_consume_loop<5>(T, vb, lane, wave, C, S); break;
-        default: pv_consume_loop<0>(T, vb, lane, wave, C, S); break;
+        case 1: pv_consume_loop<1, ND>(A, T, (int)G, vb, lane, wave, C, S, par); break;
+        case 2: pv_consume_loop<2, ND>(A, T, (int)G, vb, lane, wave, C, S, par); break;
+        case 3: pv_consume_loop<3, ND>(A, T, (int)G, vb, lane, wave, C, S, par); break;
+        case 4: pv_consume_loop<4, ND>(A, T, (int)G, vb, lane, wave, C, S, par); break;
+        case 5: pv_consume_loop<5, ND>(A, T, (int)G, vb, lane, wave, C, S, par); break;
+        default: pv_consume_loop<0, ND>(A, T, (int)G, vb, lane, wave, C, S, par); break;
     }
-    __syncthreads();
-    if (S.bad[par]) {
-        if (tid == 0) A.flags[bh * A.ntiles + tile] = 1;
+    __syncthreads();  // [C]
+    const bool generic = S.bad[par] != 0;
+    __syncthreads();  // [D]: RN64(DEN) of every row is in LDS
+    if (generic) {
+        if (tid == 0) A.flags[bh * A.ntiles + tile] = kTileGeneric;
         return true;
     }
-    if (tid == 0) A.flags[bh * A.ntiles + tile] = 0;
+    if (tid == 0) A.flags[bh * A.ntiles + tile] = kTileDone;
     if (!mine) return false;
 
     // carry the classes into bytes: C_0..C_8 in [0, 256), C_9 signed, so that
@@ -443,26 +843,27 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
         C[s] &= 255;
         C[s + 1] += c;
     }
-    // the top class of accumulator register rr, with its int64 part
     auto top = [&](int rr) -> int64_t {
         return (int64_t)C[kNC - 1][rr] + (longt ? S.top[wave][rr][lane] : 0);
     };
+    auto row_of = [&](int rr) { return 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3); };
     const int64_t d = G * 32 + (lane & 31);
     const int g = A.colgrid[T.bhk * A.Dp32 + d];
     if (FUSED && ((T.rem >> G) & 1)) {
-        // this group's remainders are added later: its exact NUM goes to the
-        // tile's 32-row digit scratch (cleared here), finalized after them
+        // this group's remainders are added by k_pv_fix: its exact NUM goes to
+        // the tile's 32-row digit scratch (cleared here), with each row's
+        // RN64(DEN) beside it, and is finalized there after the remainders
         const int64_t nplane = A.ntiles * 32 * (int64_t)gridDim.y * A.D;
         int64_t *nb = A.fb_num + (bh * A.ntiles + tile) * 32 * A.D;
         for (int t = lane; t < 32 * 32 * kNumDigits; t += 64) {
-            const int k = t >> 10, r = (t >> 5) & 31, c = t & 31;
-            if (G * 32 + c < A.D) nb[k * nplane + r * A.D + G * 32 + c] = 0;
+            const int k = t >> 10, rr = (t >> 5) & 31, c = t & 31;
+            if (G * 32 + c < A.D) nb[k * nplane + rr * A.D + G * 32 + c] = 0;
         }
+        if (lane < 32) ((double *)A.fb_den)[(bh * A.ntiles + tile) * 32 + lane] = S.d64[par][lane];
         __threadfence();
         if (d < A.D) {
 #pragma unroll 1
             for (int rr = 0; rr < 16; ++rr) {
-                const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
                 const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) |
                                     ((uint32_t)C[2][rr] << 16) | ((uint32_t)C[3][rr] << 24);
                 const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) |
@@ -470,66 +871,76 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
                 const uint64_t lo = ((uint64_t)l1 << 32) | l0;
                 const int64_t hi = top(rr) * 256 + C[kNC - 2][rr];
                 const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
-                add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, nb + row * A.D + d, nplane);
+                add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, nb + row_of(rr) * A.D + d, nplane);
             }
         }
-        __threadfence();
         return false;
     }
     if (FUSED) {
-        // all 16 outputs of the lane first (no branches: their conversions and
-        // divisions interleave), then the stores of the rows that exist
+        // the lane's 16 outputs in two halves of 8 (no branches within a half:
+        // its conversions and divisions interleave), each followed by the
+        // stores of the rows that exist.
         // NUM = P_hi 2^48 + P_lo with P_lo = bytes C_0..C_5 (48 bits) and
-        // P_hi = C_9 2^24 + bytes C_8 C_7 C_6: both exact in binary64 while
+        // P_hi = top 2^24 + bytes C_8 C_7 C_6: both exact in binary64 while
         // |P_hi| < 2^53, and then fma(P_hi, 2^48, P_lo) is the correctly rounded
-        // NUM (one rounding).  A lane holding a larger P_hi redoes its outputs
+        // NUM (one rounding).  A half holding a larger P_hi redoes its outputs
         // by the 128-bit conversion.
-        float out[16];
-        bool big = false;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-            const uint64_t plo = (uint64_t)((uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) |
-                                            ((uint32_t)C[2][rr] << 16) | ((uint32_t)C[3][rr] << 24)) |
-                                 ((uint64_t)((uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8)) << 32);
-            const int64_t phi = top(rr) * (1 << 24) +
-                                (int64_t)((uint32_t)C[6][rr] | ((uint32_t)C[7][rr] << 8) | ((uint32_t)C[8][rr] << 16));
-            big |= (uint64_t)(phi + ((int64_t)1 << 53)) >= ((uint64_t)1 << 54);
-            const double n64 = ldexp(fma((double)phi, 0x1p48, (double)plo), g - kSw);
-            out[rr] = (float)(n64 / S.d64[par][row]);
-        }
-        if (big) {
-#pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-                const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) | ((uint32_t)C[2][rr] << 16) |
-                                    ((uint32_t)C[3][rr] << 24);
-                const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) | ((uint32_t)C[6][rr] << 16) |
-                                    ((uint32_t)C[7][rr] << 24);
-                const uint64_t lo = ((uint64_t)l1 << 32) | l0;
-                const int64_t hi = top(rr) * 256 + C[kNC - 2][rr];
-                out[rr] = (float)(i128_to_f64(hi, lo, g - kSw) / S.d64[par][row]);
-            }
-        }
-        // keep the arithmetic here, ahead of the guarded stores (else it is
-        // moved into each store's branch and the outputs run one after another)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) asm volatile("" ::"v"(out[rr]));
-        // the tile's output rows from a wave-uniform base, 32-bit lane offsets
-        // (the launcher bounds 32 rows of output stride)
+        // The output rows from a wave-uniform base and 32-bit lane offsets (the
+        // launcher bounds 32 rows of output stride); the stride passes through an
+        // empty asm so that no address is formed (and kept live) before here.
+        int ostride = (int)A.osS;
+        asm volatile("" : "+s"(ostride));
         float *ob = A.o + T.b * A.osB + T.hq * A.osH + T.it0 * A.osS;
-        const int nrows = (int)min64(32, T.i_end - T.it0), ostride = (int)A.osS;
+        const int nrows = (int)min64(32, T.i_end - T.it0);
         const bool dok = d < A.D;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
-            if (row < nrows && dok) ob[row * ostride + (int)d] = out[rr];
+        for (int h = 0; h < 2; ++h) {
+            float out[8];
+            bool big = false;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int rr = 8 * h + u;
+                const uint64_t plo = (uint64_t)((uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) |
+                                                ((uint32_t)C[2][rr] << 16) | ((uint32_t)C[3][rr] << 24)) |
+                                     ((uint64_t)((uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8)) << 32);
+                const int64_t phi = top(rr) * (1 << 24) + (int64_t)((uint32_t)C[6][rr] | ((uint32_t)C[7][rr] << 8) |
+                                                                    ((uint32_t)C[8][rr] << 16));
+                big |= (uint64_t)(phi + ((int64_t)1 << 53)) >= ((uint64_t)1 << 54);
+                const double n64 = ldexp(fma((double)phi, 0x1p48, (double)plo), g - kSw);
+                out[u] = (float)(n64 / S.d64[par][row_of(rr)]);
+            }
+            if (big) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int rr = 8 * h + u;
+                    const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) |
+                                        ((uint32_t)C[2][rr] << 16) | ((uint32_t)C[3][rr] << 24);
+                    const uint32_t l1 = (uint32_t)C[4][rr] | ((uint32_t)C[5][rr] << 8) |
+                                        ((uint32_t)C[6][rr] << 16) | ((uint32_t)C[7][rr] << 24);
+                    const uint64_t lo = ((uint64_t)l1 << 32) | l0;
+                    const int64_t hi = top(rr) * 256 + C[kNC - 2][rr];
+                    out[u] = (float)(i128_to_f64(hi, lo, g - kSw) / S.d64[par][row_of(rr)]);
+                }
+            }
+            // keep the arithmetic ahead of the guarded stores (else it is moved
+            // into each store's branch and the outputs run one after another)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) asm volatile("" ::"v"(out[u]));
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int row = row_of(8 * h + u);
+                if (row < nrows && dok) ob[row * ostride + (int)d] = out[u];
+            }
         }
         return false;
     }
+    // (the row base passes through an empty asm so that no address is formed
+    // and kept live before here)
+    int64_t pbase = bh * A.rows_per_bh + (T.it0 - A.row0);
+    asm volatile("" : "+s"(pbase));
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-        const int row = 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+        const int row = row_of(rr);
         const int64_t io = T.it0 + row;
         if (io >= T.i_end || d >= A.D) continue;
         const uint32_t l0 = (uint32_t)C[0][rr] | ((uint32_t)C[1][rr] << 8) | ((uint32_t)C[2][rr] << 16) |
@@ -539,11 +950,13 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
         const uint64_t lo = ((uint64_t)l1 << 32) | l0;
         const int64_t hi = top(rr) * 256 + C[kNC - 2][rr];
         const __int128 num = (__int128)(((unsigned __int128)(uint64_t)hi << 64) | lo);
-        const int64_t prow = bh * A.rows_per_bh + (io - A.row0);
+        const int64_t prow = pbase + row;
         add_i128_digits<kNumDigits>(num, g - kSw - kNumElo, A.num + prow * A.D + d, A.plane_rows * A.D);
-        if (G == 0 && (lane & 31) == 0)
-            add_i128_digits<kDenDigits>(((__int128)S.den_hi[par][row] << 32) + S.den_lo[par][row], -kSw - kDenElo,
-                                        A.den + prow, A.plane_rows);
+        if (G == 0 && (lane & 31) == 0) {
+            const int64_t hi2 = (int64_t)S.den_hi[par][row] + (int64_t)(S.den_lo[par][row] >> 32);
+            const int64_t lo2 = (int64_t)(S.den_lo[par][row] & 0xffffffffull);
+            add_i128_digits<kDenDigits>(((__int128)hi2 << 32) + lo2, -kSw - kDenElo, A.den + prow, A.plane_rows);
+        }
     }
     return false;
 }
@@ -551,126 +964,59 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
 // One workgroup per tile, or for causal attention per pair of tiles (x,
 // ntiles-1-x), whose key counts add up to the same total for every pair: the
 // whole grid then runs in one balanced round.  Both roles walk the same tiles
-// and meet at the same barriers.
-template <typename TV, bool FUSED>
-__device__ __forceinline__ void fallback_tile(const PvArgs &A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
-                              int64_t *__restrict__ num_ws, int64_t *__restrict__ den_ws, int64_t bh, int64_t tile,
-                              int64_t nbh);
-
-// A flagged tile, by the whole workgroup right after both roles learn of it
-// (the launch over the first four groups only: it covers every dimension).
-template <bool FUSED>
-__device__ __forceinline__ void pv_generic_tile(const PvArgs &A, int64_t bh, int64_t tile) {
-    if (A.vdtype == 0)
-        fallback_tile<float, FUSED>(A, (const float *)A.v, A.vsB, A.vsH, A.vsS, A.fb_num, A.fb_den, bh, tile,
-                                    (int64_t)gridDim.y);
-    else
-        fallback_tile<bf16_t, FUSED>(A, (const bf16_t *)A.v, A.vsB, A.vsH, A.vsS, A.fb_num, A.fb_den, bh, tile,
-                                     (int64_t)gridDim.y);
-}
-
-// The remainders of a tile's groups G0 .. G0+NG-1 (V entries with bits below
-// their column grid, vprep.hpp), by the whole workgroup after both roles are
-// done: each visible (row, remainder) product w V_rem is exact in binary64 and
-// is added into the row's digits (the caller's planes, or the tile's scratch,
-// where the consumers left the matrix-core part of those groups), then (fused)
-// those groups' outputs are finalized from the digits.  grp: the groups of
-// this launch that have remainders (nonzero, the same for every thread).
-template <bool FUSED, int NG>
-__device__ __forceinline__ void pv_remainder_tile(const PvArgs &A, int G0, int64_t bh, int64_t tile, int par,
-                                                  uint32_t grp, PvShared &S) {
-    const PvTile T = pv_tile_of(A, bh, tile);
-    __syncthreads();  // the consumers' scratch deposits of this tile are done (and fenced)
-    int64_t *num = FUSED ? A.fb_num : A.num;
-    const int64_t nplane_rows = FUSED ? A.ntiles * 32 * (int64_t)gridDim.y : A.plane_rows;
-    auto prow_of = [&](int64_t i) -> int64_t {
-        return FUSED ? (bh * A.ntiles + tile) * 32 + (i - T.it0) : bh * A.rows_per_bh + (i - A.row0);
-    };
-    const int n = min(*A.rare_n, kRareCap);
-    for (int t = threadIdx.x; t < n * 32; t += blockDim.x) {
-        const int4 E = A.rare[t >> 5];
-        const int64_t i = T.it0 + (t & 31), j = E.y, d = E.z;
-        const int gd = E.z / 32 - G0;  // the entry's group within this launch
-        if (E.x != T.bhk || gd < 0 || gd >= NG || !((grp >> gd) & 1) || i >= T.i_end) continue;
-        const int64_t jend = A.causal ? min64(A.kv_hi, i + 1) : A.kv_hi;
-        if (j < A.kv_lo || j >= jend) continue;
-        const float w = weight(A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)], pv_rowmax(A, bh, i));
-        if (w == 0.0f) continue;
-        const float rv = __int_as_float(E.w);
-        const int ew = f32_exp(w), ev = f32_exp(rv);
-        int64_t *dst = num + prow_of(i) * A.D + d;
-        Window win;
-        win.init();
-        win.add<kNumDigits>((double)w * (double)rv, max(ew, -126) - 23 + max(ev, -126) - 23, ew + ev + 2, kNumGcap,
-                            kNumElo, dst, nplane_rows * A.D);
-        win.flush<kNumDigits>(kNumElo, dst, nplane_rows * A.D);
-    }
-    __threadfence();
-    __syncthreads();
-    if (!FUSED) return;
-    for (int t = threadIdx.x; t < 32 * NG * 32; t += blockDim.x) {
-        const int r = t / (NG * 32), c = t % (NG * 32);
-        const int64_t d = G0 * 32 + c, i = T.it0 + r;
-        if (!((grp >> (c >> 5)) & 1) || d >= A.D || i >= T.i_end) continue;
-        const int64_t at = prow_of(i) * A.D + d;
-        int64_t nd[kNumDigits];
-        unsigned long long *np = (unsigned long long *)num;
-#pragma unroll
-        for (int k = 0; k < kNumDigits; ++k) nd[k] = (int64_t)atomicAdd(np + k * nplane_rows * A.D + at, 0ull);
-        canonicalize<kNumDigits>(nd);
-        const double n64 = digits_to_f64<kNumDigits>(nd, kNumElo);
-        A.o[T.b * A.osB + T.hq * A.osH + i * A.osS + d] = (float)(n64 / S.d64[par][r]);
-    }
-}
-
-template <bool FUSED, int NG>
+// and meet at the same barriers.  No barrier separates the two tiles beyond
+// those: the producers start the second tile while the consumers finalize the
+// first (row sums and flags are kept per tile).
+template <bool FUSED, int NG, int ND>
 __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
-    __shared__ __align__(16) PvShared S;
+    __shared__ __align__(16) PvShared<ND> S;
     const int64_t bh = blockIdx.y, x = blockIdx.x;
     const int npass = (A.causal && x != A.ntiles - 1 - x) ? 2 : 1;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // No barrier between the tiles: the producers start the second tile while
-    // the consumers finalize the first (row sums and flags are kept per tile).
-    // Both roles learn whether a tile needs the generic path; such tiles are
-    // redone at the end by the whole workgroup (from one call site).
-    bool generic[2] = {false, false};
-    uint32_t rem[2] = {0u, 0u};
     if (wave >= NG) {
         for (int pass = 0; pass < npass; ++pass)
-            generic[pass] = pv_produce<NG>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x,
-                                           threadIdx.x - 64 * NG, pass, S, rem[pass]);
+            pv_produce<NG, ND>(A, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, threadIdx.x - 64 * NG, pass,
+                               S);
     } else {
         for (int pass = 0; pass < npass; ++pass)
-            generic[pass] = pv_consume<FUSED, NG>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave,
-                                                  pass, S, rem[pass]);
-    }
-    for (int pass = 0; pass < npass; ++pass) {
-        const int64_t tile = (A.causal && pass == 0) ? A.ntiles - 1 - x : x;
-        const uint32_t grp = (rem[pass] >> G0) & ((1u << NG) - 1);
-        if (generic[pass]) {
-            if (G0 == 0) pv_generic_tile<FUSED>(A, bh, tile);
-        } else if (grp) {
-            pv_remainder_tile<FUSED, NG>(A, G0, bh, tile, pass, grp, S);
-        }
+            pv_consume<FUSED, NG, ND>(A, G0, bh, (A.causal && pass == 0) ? A.ntiles - 1 - x : x, wave, pass, S);
     }
 }
 
-// ---------------------------------------------------------------- generic exact fallback
+// ---------------------------------------------------------------- flagged tiles and remainders
 
-// One flagged tile, by the whole workgroup: the windowed exact deposit of the
-// general path over all keys of the tile's rows, then (fused) an in-kernel
-// finalize.  nbh = number of heads in the launch.
+constexpr int kFixThreads = 256;
+constexpr int kFixKeys = 64;  // keys whose weights one pass of the generic path holds in LDS
+
+// The weights of rows [it0, it0+32) against keys [j0, j0 + kFixKeys) into wl
+// (0 for invisible pairs), by the whole workgroup.
+__device__ void fix_weights(const PvArgs &A, int64_t bh, int64_t it0, int64_t i_end, int64_t j0, int64_t jhi,
+                            const float *m, float (*wl)[kFixKeys]) {
+    for (int t = threadIdx.x; t < 32 * kFixKeys; t += blockDim.x) {
+        const int r = t / kFixKeys, c = t % kFixKeys;
+        const int64_t i = it0 + r, j = j0 + c;
+        float w = 0.0f;
+        if (i < i_end && j < jhi && (!A.causal || j <= i)) w = weight(pv_score(A, bh, i, j), m[r]);
+        wl[r][c] = w;
+    }
+}
+
+// A flagged tile by the generic exact path: per pass over kFixKeys keys, the
+// tile's weights into LDS, then one binary64 window per (row, column) and per
+// row for DEN, whose terms all lie on a grid 2^g with |window| < 2^(g+53), so
+// every addition is exact; windows are flushed into digit planes by integer
+// atomics at the end of each pass.  Fused: the tile's 32-row digit scratch,
+// then the finalize; otherwise the caller's planes.
 template <typename TV, bool FUSED>
-__device__ __forceinline__ void fallback_tile(const PvArgs &A, const TV *__restrict__ vp, int64_t vsB, int64_t vsH, int64_t vsS,
-                              int64_t *__restrict__ num_ws, int64_t *__restrict__ den_ws, int64_t bh, int64_t tile,
-                              int64_t nbh) {
+__device__ void fix_generic_tile(const PvArgs &A, int64_t bh, int64_t tile, float *m, float (*wl)[kFixKeys]) {
     const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group;
     const int64_t it0 = A.i0 + tile * 32, i_end = A.i0 + A.ni;
-    const int64_t D = A.D;
+    const int64_t D = A.D, nbh = gridDim.y;
+    const int64_t jhi = A.causal ? min64(A.kv_hi, it0 + 32) : A.kv_hi;
     constexpr int VMB = elem<TV>::mant_bits;
-    // digit target: fused -> 32-row scratch of this tile (zeroed here); digits -> caller planes
-    int64_t *num = FUSED ? num_ws : A.num;
-    int64_t *den = FUSED ? den_ws : A.den;
+    const TV *vp = (const TV *)A.v;
+    int64_t *num = FUSED ? A.fb_num : A.num;
+    int64_t *den = FUSED ? A.fb_den : A.den;
     const int64_t nplane_rows = FUSED ? A.ntiles * 32 * nbh : A.plane_rows;
     auto prow_of = [&](int64_t i) -> int64_t {
         return FUSED ? (bh * A.ntiles + tile) * 32 + (i - it0) : bh * A.rows_per_bh + (i - A.row0);
@@ -682,37 +1028,41 @@ __device__ __forceinline__ void fallback_tile(const PvArgs &A, const TV *__restr
         }
         for (int64_t t = threadIdx.x; t < 32 * kDenDigits; t += blockDim.x)
             den[(t / 32) * nplane_rows + prow_of(it0) + (t % 32)] = 0;
-        __threadfence();
-        __syncthreads();
     }
-    for (int64_t t = threadIdx.x; t < 32 * (D + 1); t += blockDim.x) {
-        const int64_t r = t / (D + 1), d = t % (D + 1);  // d == D: the DEN window of row r
-        const int64_t i = it0 + r;
-        if (i >= i_end) continue;
-        const int64_t row = bh * A.ni + (i - A.i0);
-        const float m = pv_rowmax(A, bh, i);
-        const int64_t jend = A.causal ? min64(A.kv_hi, i + 1) : A.kv_hi;
-        const TV *vcol = vp + b * vsB + hk * vsH + (d < D ? d : 0);
-        const int64_t prow = prow_of(i);
-        Window win;
-        win.init();
-        for (int64_t j = A.kv_lo; j < jend; ++j) {
-            const float w = weight(A.scores[row * A.W + (j - A.kv_lo)], m);
-            if (w == 0.0f) continue;
-            const int ew = f32_exp(w);
-            const int lw = max(ew, -126) - 23;
-            if (d == D) {
-                win.add<kDenDigits>((double)w, lw, ew + 1, kDenGcap, kDenElo, den + prow, nplane_rows);
-            } else {
-                const float vf = elem<TV>::to_f32(vcol[j * vsS]);
-                if (vf == 0.0f) continue;
-                const int ev = f32_exp(vf);
-                win.add<kNumDigits>((double)w * (double)vf, lw + max(ev, -126) - VMB, ew + ev + 2, kNumGcap,
-                                    kNumElo, num + prow * D + d, nplane_rows * D);
+    if (threadIdx.x < 32) m[threadIdx.x] = it0 + threadIdx.x < i_end ? pv_rowmax(A, bh, it0 + threadIdx.x) : 0.0f;
+    __threadfence();
+    __syncthreads();
+    for (int64_t j0 = A.kv_lo; j0 < jhi; j0 += kFixKeys) {
+        fix_weights(A, bh, it0, i_end, j0, jhi, m, wl);
+        __syncthreads();
+        const int nk = (int)min64(kFixKeys, jhi - j0);
+        for (int64_t t = threadIdx.x; t < 32 * (D + 1); t += blockDim.x) {
+            const int64_t r = t / (D + 1), d = t % (D + 1);  // d == D: the DEN window of row r
+            const int64_t i = it0 + r;
+            if (i >= i_end) continue;
+            const TV *vcol = vp + b * A.vsB + hk * A.vsH + (d < D ? d : 0);
+            const int64_t prow = prow_of(i);
+            Window win;
+            win.init();
+            for (int c = 0; c < nk; ++c) {
+                const float w = wl[r][c];
+                if (w == 0.0f) continue;
+                const int ew = f32_exp(w);
+                const int lw = max(ew, -126) - 23;
+                if (d == D) {
+                    win.add<kDenDigits>((double)w, lw, ew + 1, kDenGcap, kDenElo, den + prow, nplane_rows);
+                } else {
+                    const float vf = elem<TV>::to_f32(vcol[(j0 + c) * A.vsS]);
+                    if (vf == 0.0f) continue;
+                    const int ev = f32_exp(vf);
+                    win.add<kNumDigits>((double)w * (double)vf, lw + max(ev, -126) - VMB, ew + ev + 2, kNumGcap,
+                                        kNumElo, num + prow * D + d, nplane_rows * D);
+                }
             }
+            if (d == D) win.flush<kDenDigits>(kDenElo, den + prow, nplane_rows);
+            else win.flush<kNumDigits>(kNumElo, num + prow * D + d, nplane_rows * D);
         }
-        if (d == D) win.flush<kDenDigits>(kDenElo, den + prow, nplane_rows);
-        else win.flush<kNumDigits>(kNumElo, num + prow * D + d, nplane_rows * D);
+        __syncthreads();
     }
     if (!FUSED) return;
     __threadfence();
@@ -734,9 +1084,79 @@ __device__ __forceinline__ void fallback_tile(const PvArgs &A, const TV *__restr
         A.o[b * A.osB + hq * A.osH + i * A.osS + d] = (float)(n64 / d64);
         if (A.stat_den && d == 0) {
             A.stat_den[bh * A.stat_rows + i] = d64;
-            A.stat_m[bh * A.stat_rows + i] = pv_rowmax(A, bh, i);
+            A.stat_m[bh * A.stat_rows + i] = m[r];
         }
     }
+}
+
+// The remainders of a tile's groups `grp` (V entries with bits below their
+// column grid, vprep.hpp): each visible (row, remainder) product w V_rem is
+// exact in binary64 and is added into the row's digits (the caller's planes,
+// or the tile's scratch, where the consumers left the matrix-core part of
+// those groups with each row's RN64(DEN)), then (fused) those groups' outputs
+// are finalized from the digits.
+template <bool FUSED>
+__device__ void fix_remainder_tile(const PvArgs &A, int64_t bh, int64_t tile, uint32_t grp, float *m) {
+    const PvTile T = pv_tile_of(A, bh, tile);
+    int64_t *num = FUSED ? A.fb_num : A.num;
+    const int64_t nplane_rows = FUSED ? A.ntiles * 32 * (int64_t)gridDim.y : A.plane_rows;
+    auto prow_of = [&](int64_t i) -> int64_t {
+        return FUSED ? (bh * A.ntiles + tile) * 32 + (i - T.it0) : bh * A.rows_per_bh + (i - A.row0);
+    };
+    if (threadIdx.x < 32)
+        m[threadIdx.x] = T.it0 + threadIdx.x < T.i_end ? pv_rowmax(A, bh, T.it0 + threadIdx.x) : 0.0f;
+    __syncthreads();
+    const int n = min(*A.rare_n, kRareCap);
+    for (int t = threadIdx.x; t < n * 32; t += blockDim.x) {
+        const int4 E = A.rare[t >> 5];
+        const int64_t i = T.it0 + (t & 31), j = E.y, d = E.z;
+        if (E.x != T.bhk || !((grp >> (E.z / 32)) & 1) || i >= T.i_end) continue;
+        const int64_t jend = A.causal ? min64(A.kv_hi, i + 1) : A.kv_hi;
+        if (j < A.kv_lo || j >= jend) continue;
+        const float w = weight(pv_score(A, bh, i, j), m[t & 31]);
+        if (w == 0.0f) continue;
+        const float rv = __int_as_float(E.w);
+        const int ew = f32_exp(w), ev = f32_exp(rv);
+        int64_t *dst = num + prow_of(i) * A.D + d;
+        Window win;
+        win.init();
+        win.add<kNumDigits>((double)w * (double)rv, max(ew, -126) - 23 + max(ev, -126) - 23, ew + ev + 2, kNumGcap,
+                            kNumElo, dst, nplane_rows * A.D);
+        win.flush<kNumDigits>(kNumElo, dst, nplane_rows * A.D);
+    }
+    __threadfence();
+    __syncthreads();
+    if (!FUSED) return;
+    const double *d64s = (const double *)A.fb_den + (bh * A.ntiles + tile) * 32;
+    for (int t = threadIdx.x; t < 32 * (int)T.nG * 32; t += blockDim.x) {
+        const int r = t / ((int)T.nG * 32), c = t % ((int)T.nG * 32);
+        const int64_t i = T.it0 + r;
+        if (!((grp >> (c >> 5)) & 1) || c >= A.D || i >= T.i_end) continue;
+        const int64_t at = prow_of(i) * A.D + c;
+        int64_t nd[kNumDigits];
+        unsigned long long *np = (unsigned long long *)num;
+#pragma unroll
+        for (int k = 0; k < kNumDigits; ++k) nd[k] = (int64_t)atomicAdd(np + k * nplane_rows * A.D + at, 0ull);
+        canonicalize<kNumDigits>(nd);
+        const double n64 = digits_to_f64<kNumDigits>(nd, kNumElo);
+        A.o[T.b * A.osB + T.hq * A.osH + i * A.osS + c] = (float)(n64 / d64s[r]);
+    }
+}
+
+// One workgroup per tile: the generic path for flagged tiles, the remainders
+// for the others that have any.  Most workgroups find nothing to do.
+template <bool FUSED>
+__global__ __launch_bounds__(kFixThreads) void k_pv_fix(PvArgs A) {
+    __shared__ float m[32];
+    __shared__ float wl[32][kFixKeys];
+    const int64_t tile = blockIdx.x, bh = blockIdx.y;
+    if (A.flags[bh * A.ntiles + tile] == kTileGeneric) {
+        if (A.vdtype == 0) fix_generic_tile<float, FUSED>(A, bh, tile, m, wl);
+        else fix_generic_tile<bf16_t, FUSED>(A, bh, tile, m, wl);
+        return;
+    }
+    const PvTile T = pv_tile_of(A, bh, tile);
+    if (T.rem && T.nblk > 0) fix_remainder_tile<FUSED>(A, bh, tile, T.rem, m);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -798,6 +1218,13 @@ VJob make_vjob(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi,
     return J;
 }
 
+hipError_t launch_vslice(const VJob &J, hipStream_t s) {
+    dim3 gsl((unsigned)J.nKB, (unsigned)J.nG, (unsigned)J.nbhk);
+    if (J.dtype == 0) hipLaunchKernelGGL(k_vslice<float>, gsl, dim3(64), 0, s, J);
+    else hipLaunchKernelGGL(k_vslice<bf16_t>, gsl, dim3(64), 0, s, J);
+    return hipGetLastError();
+}
+
 hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, VPrep &vp,
                         hipStream_t s) {
     ProfScope prof_("vprep", s);
@@ -807,52 +1234,69 @@ hipError_t launch_vprep(const Tensor &v, const AttnGeom &g, int64_t kv_lo, int64
     if (v.dtype == 0) hipLaunchKernelGGL(k_vstats<float>, gs, dim3(256), 0, s, J);
     else hipLaunchKernelGGL(k_vstats<bf16_t>, gs, dim3(256), 0, s, J);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    dim3 gsl((unsigned)J.nKB, (unsigned)J.nG, (unsigned)J.nbhk);
-    if (v.dtype == 0) hipLaunchKernelGGL(k_vslice<float>, gsl, dim3(64), 0, s, J);
-    else hipLaunchKernelGGL(k_vslice<bf16_t>, gsl, dim3(64), 0, s, J);
-    return hipGetLastError();
+    return launch_vslice(J, s);
 }
 
 template <bool FUSED>
-static hipError_t launch_pv_t(const Tensor &v, const AttnGeom &g, const VPrep &vp, PvArgs &a, int64_t bh,
-                              int64_t *num_ws, int64_t *den_ws, hipStream_t s) {
+static hipError_t launch_pv_t(const PvArgs &a, int64_t nG, int64_t bh, int nd, hipStream_t s) {
     hipError_t e;
     {
         ProfScope prof_("pv_mfma", s);
-        const int64_t nG = vp.Dp32 / 32;
         dim3 grid((unsigned)(a.causal ? (a.ntiles + 1) / 2 : a.ntiles), (unsigned)bh);
         // at most four groups per launch; wider heads take several launches over
         // the same tiles (the weights are recomputed, the digits are not shared)
         for (int G0 = 0; G0 < nG; G0 += 4) {
-            if (nG == 1) hipLaunchKernelGGL((k_pv<FUSED, 1>), grid, dim3(64 * (1 + kPW)), 0, s, a, G0);
-            else if (nG == 2) hipLaunchKernelGGL((k_pv<FUSED, 2>), grid, dim3(64 * (2 + kPW)), 0, s, a, G0);
-            else hipLaunchKernelGGL((k_pv<FUSED, 4>), grid, dim3(64 * (4 + kPW)), 0, s, a, G0);
+            // the score source: stored (nd = 0) or recomputed from digit rows of nd 64-dim chunks
+            if (nd == 0) {
+                if (nG == 1) hipLaunchKernelGGL((k_pv<FUSED, 1, 0>), grid, dim3(64 * (1 + kPW)), 0, s, a, G0);
+                else if (nG == 2) hipLaunchKernelGGL((k_pv<FUSED, 2, 0>), grid, dim3(64 * (2 + kPW)), 0, s, a, G0);
+                else hipLaunchKernelGGL((k_pv<FUSED, 4, 0>), grid, dim3(64 * (4 + kPW)), 0, s, a, G0);
+            } else if (nd == 1) {
+                if (nG == 1) hipLaunchKernelGGL((k_pv<FUSED, 1, 1>), grid, dim3(64 * (1 + kPW)), 0, s, a, G0);
+                else hipLaunchKernelGGL((k_pv<FUSED, 2, 1>), grid, dim3(64 * (2 + kPW)), 0, s, a, G0);
+            } else if (nd == 2) {
+                hipLaunchKernelGGL((k_pv<FUSED, 4, 2>), grid, dim3(64 * (4 + kPW)), 0, s, a, G0);
+            } else if (nd == 3) {
+                hipLaunchKernelGGL((k_pv<FUSED, 4, 3>), grid, dim3(64 * (4 + kPW)), 0, s, a, G0);
+            } else {
+                hipLaunchKernelGGL((k_pv<FUSED, 4, 4>), grid, dim3(64 * (4 + kPW)), 0, s, a, G0);
+            }
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    return hipSuccess;
+    ProfScope prof_("pv_fix", s);
+    hipLaunchKernelGGL(k_pv_fix<FUSED>, dim3((unsigned)a.ntiles, (unsigned)bh), dim3(kFixThreads), 0, s, a);
+    return hipGetLastError();
 }
 
-hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const float *scores, const float *rowmax,
-                     const uint32_t *rowmax_keys, int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1, int64_t kv_lo, int64_t kv_hi,
-                     int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o, int64_t *num, int64_t *den,
-                     int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int force_fallback, hipStream_t s,
-                     float *stat_m, double *stat_den, int64_t stat_rows) {
+hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const PvSrc &src, const float *rowmax,
+                     const uint32_t *rowmax_keys, int64_t rm_rows, int64_t rm_row0, int64_t i0, int64_t i1,
+                     int64_t kv_lo, int64_t kv_hi, int *flags, int64_t *fb_num, int64_t *fb_den, const OutView *o,
+                     int64_t *num, int64_t *den, int64_t plane_rows, int64_t rows_per_bh, int64_t row0,
+                     int force_fallback, hipStream_t s, float *stat_m, double *stat_den, int64_t stat_rows) {
     const int64_t ni = i1 - i0;
     if (ni <= 0) return hipSuccess;
     if (vp.Dp32 > 256) return hipErrorInvalidValue;
     // key offsets, and byte offsets within a 32-row tile of scores, are 32-bit in the kernel
     if ((kv_hi - kv_lo + 64) * 32 * 4 > INT32_MAX) return hipErrorInvalidValue;
+    const int64_t nG = vp.Dp32 / 32;
+    const int nd = src.scores ? 0 : (int)(src.Dp64 / 64);
+    if (!src.scores) {
+        // recomputed scores: digit rows of (D rounded up to 64) bytes per digit, whole
+        // 32-key blocks of K rows and 32-row tiles of Q rows; the kernels come in
+        // (groups, chunks) = (1, 1), (2, 1), (4, 2..4)
+        if (src.Dp64 != (g.D + 63) / 64 * 64 || src.kv_pad % 32 || src.ni_pad % 32 || src.ni_pad < ni ||
+            src.kv_pad < kv_hi - kv_lo || (nd == 1) != (nG <= 2))
+            return hipErrorInvalidValue;
+    }
     const int64_t ntiles = (ni + 31) / 32, bh = g.B * g.Hq;
     PvArgs a{};
-    a.scores = scores;
+    a.src = src;
     a.rowmax = rowmax;
     a.rowmax_keys = rowmax_keys;
     a.rm_rows = rm_rows;
     a.rm_row0 = rm_row0;
     a.ni = ni;
-    a.W = kv_hi - kv_lo;
     a.i0 = i0;
     a.kv_lo = kv_lo;
     a.kv_hi = kv_hi;
@@ -896,8 +1340,7 @@ hipError_t launch_pv(const Tensor &v, const AttnGeom &g, const VPrep &vp, const 
         a.stat_den = stat_den;
         a.stat_rows = stat_rows;
     }
-    return o ? launch_pv_t<true>(v, g, vp, a, bh, fb_num, fb_den, s)
-             : launch_pv_t<false>(v, g, vp, a, bh, fb_num, fb_den, s);
+    return o ? launch_pv_t<true>(a, nG, bh, nd, s) : launch_pv_t<false>(a, nG, bh, nd, s);
 }
 
 }  // namespace det

@@ -9,20 +9,22 @@
 // integer dot product, whatever order it is summed in.  That integer is
 // computed here from balanced int8 digits of Qi and Ki with
 // v_mfma_i32_16x16x64_i8 (exact int32 sums).  The bound is checked per
-// 16-row x 16-key item from per-row max|Qi| and per-key sum|Ki|; an item that
-// fails it (or whose rows need more than kQKmax digits) is recomputed by the
-// plain fp64 chain in k_qk_fix, so the scores are the chain's bits either way.
+// 16-row x 16-key item from per-row max|Qi| and per-key sum|Ki|; where it
+// fails, each pair takes the finer test of qkrow.hpp (whose dot products may
+// need 128 bits), and the pairs that fail that too (or whose rows need more
+// than kQKmax digits) are recomputed by the plain fp64 chain in k_qk_fix, so
+// the scores are the chain's bits either way.
 #include "dev_math.hpp"
 #include "kernels.hpp"
+#include "qkrow.hpp"
 #include "vprep.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace det {
 
 
-constexpr int kQKmax = 4;              // digits per Q or K row (32-bit integers)
-constexpr int kQKC = 2 * kQKmax - 1;   // shift classes of the product
 constexpr int kQKbad = 99;             // row needs more digits than kQKmax
 
 // Per-row statistics and digits: grid exponent g (smallest lsb), digit count,
@@ -39,6 +41,7 @@ struct QPrep {
     uint32_t *keys;  // Q only (may be null)
     int64_t key_rows, key_row0;
     int *nfix;  // Q only
+    int *slot;  // Q only: every prepared row's score slot, set to none (-1) here
     int vec;    // rows are whole 64-dim groups on 16-byte boundaries
 };
 
@@ -60,7 +63,7 @@ __device__ __forceinline__ void qkprep_rows(const QPrep &P, int64_t blk) {
     const bool live = ii < ns;
     const bf16_t *xr = x + b * sB + h * sH + (s0 + (live ? ii : 0)) * sS;
     float v[DPL];
-    int emax = INT_MIN, lmin = INT_MAX;
+    int emax = INT_MIN, lmin = INT_MAX, lmin2 = INT_MAX, pmin = 0;
     bool loaded = false;
     if constexpr (DPL % 8 == 0) {
         if (vec) {  // whole rows of D = Dp64 dims, 16-byte aligned: DPL/8 vector loads per lane
@@ -90,14 +93,21 @@ __device__ __forceinline__ void qkprep_rows(const QPrep &P, int64_t blk) {
     for (int t = 0; t < DPL; ++t) {
         if (v[t] != 0.0f) {
             const int e = f32_exp(v[t]);
+            const int l = max(e, -126) - 7;
             emax = max(emax, e);
-            lmin = min(lmin, max(e, -126) - 7);
+            // the smallest lsb exponent, a position holding it, the second smallest
+            lmin2 = min(lmin2, max(lmin, l));
+            if (l < lmin) pmin = sub * DPL + t;
+            lmin = min(lmin, l);
         }
     }
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) {
         emax = max(emax, __shfl_xor(emax, off, 64));
-        lmin = min(lmin, __shfl_xor(lmin, off, 64));
+        const int om = __shfl_xor(lmin, off, 64), om2 = __shfl_xor(lmin2, off, 64), op = __shfl_xor(pmin, off, 64);
+        lmin2 = min(min(lmin2, om2), max(lmin, om));
+        if (om < lmin || (om == lmin && op < pmin)) pmin = op;
+        lmin = min(lmin, om);
     }
     const bool zero = emax == INT_MIN;
     const int g = zero ? 0 : lmin;
@@ -121,10 +131,15 @@ __device__ __forceinline__ void qkprep_rows(const QPrep &P, int64_t blk) {
         bound = l1 ? 64 - __clzll((long long)l1) : 0;  // sum|Ki| < 2^bound
     }
     if (sub == 0) {
-        info[row] = int4{g, nd, bound, 0};
+        const int g2 = (zero || lmin2 == INT_MAX) ? kQKnoG2 : lmin2;
+        info[row] = int4{g, nd, bound, qk_row_pack(zero ? 0 : pmin, g2)};
         if (!IS_K) {
             if (keys && live) keys[bh * key_rows + (s0 + ii - key_row0)] = kKeyNegInf;
-            if (row == 0) *nfix = 0;
+            if (P.slot) P.slot[row] = -1;
+            if (row == 0) {
+                nfix[0] = 0;
+                nfix[1] = 0;  // the slot count
+            }
         }
     }
     int8_t *out = dig + row * kQKmax * Dp64 + sub * DPL;
@@ -161,8 +176,11 @@ __global__ __launch_bounds__(256) void k_qkprep(QPrep P) {
 template <int DPL>
 __global__ __launch_bounds__(256) void k_prep(QPrep K, QPrep Q, VJob J, int64_t nk, int64_t nq) {
     int64_t blk = blockIdx.x;
-    // Q's rows reset the fix count; without them the first workgroup does
-    if (nq == 0 && blk == 0 && threadIdx.x == 0) *Q.nfix = 0;
+    // Q's rows reset the fix and slot counts; without them the first workgroup does
+    if (nq == 0 && blk == 0 && threadIdx.x == 0) {
+        Q.nfix[0] = 0;
+        Q.nfix[1] = 0;
+    }
     if (blk < nk) {
         qkprep_rows<true, DPL>(K, blk);
         return;
@@ -179,7 +197,7 @@ __global__ __launch_bounds__(256) void k_prep(QPrep K, QPrep Q, VJob J, int64_t 
 
 static QPrep make_qprep(const bf16_t *x, int64_t sB, int64_t sH, int64_t sS, int64_t H, int64_t D, int64_t Dp64,
                         int64_t s0, int64_t ns, int64_t ns_pad, int64_t nrows, int4 *info, int8_t *dig,
-                        uint32_t *keys, int64_t key_rows, int64_t key_row0, int *nfix) {
+                        uint32_t *keys, int64_t key_rows, int64_t key_row0, int *nfix, int *slot) {
     QPrep P{};
     P.x = x;
     P.sB = sB;
@@ -198,6 +216,7 @@ static QPrep make_qprep(const bf16_t *x, int64_t sB, int64_t sH, int64_t sS, int
     P.key_rows = key_rows;
     P.key_row0 = key_row0;
     P.nfix = nfix;
+    P.slot = slot;
     // vector loads when every row is whole 64-dim groups starting on 16 bytes
     P.vec = D == Dp64 && ((uintptr_t)x & 15) == 0 && sS % 8 == 0 && sH % 8 == 0 && sB % 8 == 0;
     return P;
@@ -247,9 +266,14 @@ struct QkArgs {
     const int4 *qinfo, *kinfo;
     float *scores;  // [bh][ni][W] or null
     uint32_t *keys;  // rowmax keys, [bh*key_rows + i - key_row0], or null
-    int *nfix;       // number of items left (in whole or in part) to the fp64 chain
+    int *nfix;       // number of items left (in whole or in part) to the fp64 chain; nfix[1]: slots taken
     int4 *fixlist;   // their (kb, tile, bh, kFixWhole or kFixPairs)
     int fixcap;      // capacity of the list: one entry per item of the launch
+    // score slots of rows with more than kQKmax digits (every pair of such a row
+    // takes the chain): qslot[bh * ni_pad + row] (-1: none), slots[slot * kv_pad + key]
+    int *qslot;
+    float *slots;
+    int slotcap;
     double scale;
     int Dp64, ni, ni_pad, i0, kv_lo, kv_hi, kv_pad;
     int Hq, Hkv, group;
@@ -325,11 +349,22 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
     }
     aq = __builtin_amdgcn_readfirstlane(aq);  // wave-uniform after the reduction
     qbt = __builtin_amdgcn_readfirstlane(qbt);
-    int gq[4], qbr[4];
+    // the grids of the four rows of the lane's result registers (their other
+    // statistics are fetched the same way where the per-pair test needs them)
+    int gq[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        gq[r] = __shfl(qi.x, 4 * lq + r, 64);
-        qbr[r] = __shfl(qi.z, 4 * lq + r, 64);
+    for (int r = 0; r < 4; ++r) gq[r] = __shfl(qi.x, 4 * lq + r, 64);
+    // rows with more digits than the digit rows hold: every pair takes the
+    // chain (in k_qk_fix); each gets a score slot for pass 2 while slots last
+    // (assigned by the first part of the group only: one writer per row)
+    if (aq > kQKmax && A.qslot && part == 0 && lq == 0 && live && qi.y > kQKmax && it0 + lr < i_end) {
+        int at = tile * kQkT + lr;
+        asm volatile("" : "+v"(at));  // (the address is formed here, not kept from the start)
+        int *sp = A.qslot + bh * A.ni_pad + at;
+        if (*sp < 0) {
+            const int n = atomicAdd(A.nfix + 1, 1);
+            if (n < A.slotcap) *sp = n;
+        }
     }
     uint32_t mkey[4] = {kKeyNegInf, kKeyNegInf, kKeyNegInf, kKeyNegInf};
     float *srow = (A.scores && live) ? A.scores + (bh * A.ni + (it0 + 4 * lq - A.i0)) * (int64_t)A.W : nullptr;
@@ -361,6 +396,14 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
         load_block(0);
         store_block(0);
     }
+    // the Q rows are needed from here on: waiting for them now (they were
+    // loaded before block 0, which store_block has waited for) keeps the
+    // block loop free of waits for them, which would also wait for the
+    // prefetched next block
+#pragma unroll
+    for (int a = 0; a < kQKmax; ++a)
+#pragma unroll
+        for (int n = 0; n < ND; ++n) asm volatile("" ::"v"(Aq[a][n]));
     __syncthreads();
     for (int n = 0; n < nb; ++n) {
         const int buf = n & 1;
@@ -384,47 +427,56 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
                 }
             } else {
                 // pairs within the bound are exact here; when the item's bound does not
-                // hold, each pair is checked against its own row and key bounds and the
-                // others are left to the chain
+                // hold, each pair takes the finer test (qkrow.hpp) and the pairs that fail
+                // it are left to the chain.  NQ digits per side: three when every row and
+                // key of the item has at most three (the fourth digit planes are zero)
                 const bool perpair = qbt + kbnd > 53;
                 const uint8_t *krow = S.k[buf] + lr * KROW + 16 * lq;
-                v4i C[kQKC];
+                auto item = [&](auto nq) {
+                    constexpr int NQ = decltype(nq)::value, NC = 2 * NQ - 1;
+                    v4i C[NC];
 #pragma unroll
-                for (int c = 0; c < kQKC; ++c) C[c] = v4i{0, 0, 0, 0};
+                    for (int c = 0; c < NC; ++c) C[c] = v4i{0, 0, 0, 0};
 #pragma unroll
-                for (int nn = 0; nn < ND; ++nn) {
-                    v4i Bk[kQKmax];
+                    for (int nn = 0; nn < ND; ++nn) {
+                        v4i Bk[NQ];
 #pragma unroll
-                    for (int c = 0; c < kQKmax; ++c) Bk[c] = *(const v4i *)(krow + c * 64 * ND + 64 * nn);
+                        for (int c = 0; c < NQ; ++c) Bk[c] = *(const v4i *)(krow + c * 64 * ND + 64 * nn);
 #pragma unroll
-                    for (int a = 0; a < kQKmax; ++a)
+                        for (int a = 0; a < NQ; ++a)
 #pragma unroll
-                        for (int c = 0; c < kQKmax; ++c)
-                            C[a + c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[a][nn], Bk[c], C[a + c], 0, 0, 0);
-                }
-                const int j = j0 + lr;
-                const bool jv = j < A.kv_hi;
-                const int gk = ki.x;
-                bool left = false;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = it0 + 4 * lq + r;
-                    int64_t dot = 0;
-#pragma unroll
-                    for (int c = kQKC - 1; c >= 0; --c) dot = dot * 256 + (int64_t)C[c][r];
-                    const double d64 = ldexp((double)dot, gq[r] + gk);  // exact: |dot| < 2^53
-                    const float sc = (float)(A.scale * d64);
-                    const bool ok = !perpair || qbr[r] + ki.z <= 53;
-                    left |= !ok;
-                    if (jv && i < i_end && ok) {
-                        if (srow) srow[(int64_t)r * A.W + (j - A.kv_lo)] = sc;
-                        if (!A.causal || j <= i) mkey[r] = max(mkey[r], order_key(sc));
+                            for (int c = 0; c < NQ; ++c)
+                                C[a + c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[a][nn], Bk[c], C[a + c], 0, 0, 0);
                     }
-                }
-                if (__ballot(left) && lane == 0) {
-                    const int at = atomicAdd(A.nfix, 1);
-                    if (at < A.fixcap) A.fixlist[at] = int4{kb, tile, (int)bh, kFixPairs};
-                }
+                    const int j = j0 + lr;
+                    const bool jv = j < A.kv_hi;
+                    const int gk = ki.x;
+                    bool ok[4] = {true, true, true, true};
+                    if (perpair) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int qbr = __shfl(qi.z, 4 * lq + r, 64), qw = __shfl(qi.w, 4 * lq + r, 64);
+                            ok[r] = qk_pair_class(int4{gq[r], 0, qbr, qw}, ki, kQKmax) != kPairChain;
+                        }
+                    }
+                    bool left = false;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = it0 + 4 * lq + r;
+                        const float sc = (float)(A.scale * qk_dot_value<NC>(C, r, gq[r] + gk));
+                        left |= !ok[r];
+                        if (jv && i < i_end && ok[r]) {
+                            if (srow) srow[(int64_t)r * A.W + (j - A.kv_lo)] = sc;
+                            if (!A.causal || j <= i) mkey[r] = max(mkey[r], order_key(sc));
+                        }
+                    }
+                    if (__ballot(left) && lane == 0) {
+                        const int at = atomicAdd(A.nfix, 1);
+                        if (at < A.fixcap) A.fixlist[at] = int4{kb, tile, (int)bh, kFixPairs};
+                    }
+                };
+                if (aq <= 3 && bk <= 3) item(std::integral_constant<int, 3>{});
+                else item(std::integral_constant<int, kQKmax>{});
             }
         }
         if (n + 1 < nb) store_block(buf ^ 1);
@@ -445,7 +497,7 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
 // workgroup takes group ngroups-1-y and then group y, whose visible key
 // counts add up alike for every y.
 template <int ND>
-__global__ __launch_bounds__(64 * kQkWaves) void k_qk_mfma(QkArgs A) {
+__global__ __launch_bounds__(64 * kQkWaves, ND <= 2 ? 3 : 2) void k_qk_mfma(QkArgs A) {
     __shared__ __align__(16) QkShared<ND> S;
     const int64_t bh = blockIdx.z, y = blockIdx.y;
     const int npass = (A.causal && y != A.ngroups - 1 - y) ? 2 : 1;
@@ -507,7 +559,8 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
         const int64_t i = it0 + r, j = j0 + c;
         bool need = i < i_end && j < A.kv_hi;
         if (need && item.w == kFixPairs)  // (read before the barrier: its latency overlaps the staging)
-            need = A.qinfo[bh * A.ni_pad + tile * kQkT + r].z + A.kinfo[bhk * A.kv_pad + kb * kQkT + c].z > 53;
+            need = qk_pair_class(A.qinfo[bh * A.ni_pad + tile * kQkT + r], A.kinfo[bhk * A.kv_pad + kb * kQkT + c],
+                                 kQKmax) == kPairChain;
         __syncthreads();
         uint32_t key = 0;  // below order_key of every number
         if (need) {
@@ -518,6 +571,10 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
             for (int d = 0; d < Di; ++d) acc = fma((double)sq[r][d], (double)sk[c][d], acc);
             const float sc = (float)(A.scale * acc);
             if (A.scores) A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)] = sc;
+            if (A.qslot) {  // the score slot of the row, if it has one
+                const int sl = A.qslot[bh * A.ni_pad + (i - A.i0)];
+                if (sl >= 0 && sl < A.slotcap) A.slots[(int64_t)sl * A.kv_pad + (j - A.kv_lo)] = sc;
+            }
             if (!A.causal || j <= i) key = order_key(sc);
         }
         // the row's max over the item's 16 keys (16 consecutive lanes), then one
@@ -537,18 +594,53 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
 // ---------------------------------------------------------------- launchers
 
 static int64_t qk_dp64(const AttnGeom &g) { return (g.D + 63) / 64 * 64; }
-static int64_t qk_pad(int64_t len) { return std::max<int64_t>((len + kQkT - 1) / kQkT, 1) * kQkT; }
+// K digit rows of a key range: whole 32-key blocks (pass 2 stages 32 keys at a time), zero past the range
+static int64_t qk_pad(int64_t len) { return std::max<int64_t>((len + 31) / 32, 1) * 32; }
 
 size_t qk_kprep_bytes(const AttnGeom &g, int64_t kv_len) {
     const int64_t rows = g.B * g.Hkv * qk_pad(kv_len);
     return align256((size_t)rows * 16) + align256((size_t)rows * kQKmax * qk_dp64(g));
 }
 
+// Score slots of a chunk: one per 1024 query rows, at least 32 and at most 1024
+// (rows with more digits than the digit rows hold are rare; rows beyond the
+// capacity are left to pass 2's other paths).
+static int64_t qk_slot_cap(int64_t rows) { return std::min<int64_t>(1024, std::max<int64_t>(32, rows / 1024)); }
+
+// The chunk's part of the workspace: Q's statistics and digit rows, the fix
+// and slot counts, the rows' slots (all four at places that do not depend on
+// the key range: Q's part is kept across the key ranges of one chunk), the
+// fix list and the slot scores.
+struct QkChunk {
+    int4 *qinfo;
+    int8_t *qdig;
+    int *nfix;
+    int4 *fixlist;
+    int *qslot;
+    float *slots;
+    int64_t slotcap, bytes;
+};
+
+static QkChunk qk_chunk(const AttnGeom &g, int64_t ni, int64_t kv_len, void *ws) {
+    const int64_t ni_pad = padded_rows(ni), bh = g.B * g.Hq, rows = bh * ni_pad;
+    const int64_t kv_pad = qk_pad(kv_len), nKB = kv_pad / kQkT;
+    QkChunk C{};
+    char *c = (char *)ws;
+    size_t at = 0;
+    auto take = [&](size_t n) { char *p = c ? c + at : nullptr; at += align256(n); return p; };
+    C.qinfo = (int4 *)take((size_t)rows * 16);
+    C.qdig = (int8_t *)take((size_t)rows * kQKmax * qk_dp64(g));
+    C.nfix = (int *)take(8);
+    C.qslot = (int *)take((size_t)rows * 4);
+    C.fixlist = (int4 *)take((size_t)bh * (ni_pad / kQkT) * nKB * 16);
+    C.slotcap = qk_slot_cap(rows);
+    C.slots = (float *)take((size_t)C.slotcap * kv_pad * 4);
+    C.bytes = (int64_t)at;
+    return C;
+}
+
 size_t qk_chunk_bytes(const AttnGeom &g, int64_t ni, int64_t kv_len) {
-    const int64_t ni_pad = padded_rows(ni), bh = g.B * g.Hq;
-    const int64_t nKB = qk_pad(kv_len) / kQkT;
-    return align256((size_t)bh * ni_pad * 16) + align256((size_t)bh * ni_pad * kQKmax * qk_dp64(g)) + 256 +
-           align256((size_t)bh * (ni_pad / kQkT) * nKB * 16);
+    return (size_t)qk_chunk(g, ni, kv_len, nullptr).bytes;
 }
 
 bool qk_uses_mfma(const Tensor &q) { return q.dtype == 1; }
@@ -559,7 +651,57 @@ static QPrep k_rows(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t k
     int4 *info = (int4 *)ws;
     int8_t *dig = (int8_t *)ws + align256((size_t)rows * 16);
     return make_qprep((const bf16_t *)k.data, k.sB, k.sH, k.sS, g.Hkv, g.D, Dp64, kv_lo, len, kv_pad, rows, info, dig,
-                      nullptr, 0, 0, nullptr);
+                      nullptr, 0, 0, nullptr, nullptr);
+}
+
+PvSrc qk_pv_src(const Tensor &q, const Tensor &k, const AttnGeom &g, void *kprep, void *chunk_ws, int64_t ni,
+                int64_t kv_len, bool slots) {
+    const int64_t Dp64 = qk_dp64(g), ni_pad = padded_rows(ni);
+    const int64_t kv_pad = qk_pad(kv_len), krows = g.B * g.Hkv * kv_pad;
+    const QkChunk C = qk_chunk(g, ni, kv_len, chunk_ws);
+    PvSrc P{};
+    P.qinfo = C.qinfo;
+    P.qdig = C.qdig;
+    if (slots) {
+        P.qslot = C.qslot;
+        P.slots = C.slots;
+        P.slot_bytes = C.slotcap * kv_pad * 4;
+    }
+    P.kinfo = (const int4 *)kprep;
+    P.kdig = (const int8_t *)kprep + align256((size_t)krows * 16);
+    P.ni_pad = ni_pad;
+    P.kv_pad = kv_pad;
+    P.Dp64 = Dp64;
+    P.scale = g.scale;
+    P.q = q.data;
+    P.k = k.data;
+    P.qsB = q.sB;
+    P.qsH = q.sH;
+    P.qsS = q.sS;
+    P.ksB = k.sB;
+    P.ksH = k.sH;
+    P.ksS = k.sS;
+    return P;
+}
+
+hipError_t launch_qkv_prep(const Tensor &q, const Tensor &k, const Tensor &v, const AttnGeom &g, void *kprep,
+                           bool prep_k, bool prep_q, VPrep *vp, void *chunk_ws, int64_t i0, int64_t i1, int64_t kv_lo,
+                           int64_t kv_hi, hipStream_t s) {
+    ProfScope prof_("qk_prep", s);
+    const int64_t ni = i1 - i0;
+    if (ni <= 0 || kv_hi <= kv_lo) return hipSuccess;
+    if (g.D > 256) return hipErrorInvalidValue;
+    const int64_t Dp64 = qk_dp64(g), ni_pad = padded_rows(ni), bh = g.B * g.Hq;
+    const QkChunk C = qk_chunk(g, ni, kv_hi - kv_lo, chunk_ws);
+    const QPrep Q = make_qprep((const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad, bh * ni_pad,
+                               C.qinfo, C.qdig, nullptr, 0, 0, C.nfix, C.qslot);
+    const QPrep K = prep_k ? k_rows(k, g, kv_lo, kv_hi, kprep) : QPrep{};
+    VJob vj{};
+    if (vp) vj = make_vjob(v, g, kv_lo, kv_hi, *vp);
+    launch_prep(prep_k ? &K : nullptr, Q, prep_q, vp ? &vj : nullptr, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !vp) return e;
+    return launch_vslice(vj, s);
 }
 
 hipError_t launch_qk_kprep(const Tensor &k, const AttnGeom &g, int64_t kv_lo, int64_t kv_hi, void *ws,
@@ -579,19 +721,16 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     const int64_t Dp64 = qk_dp64(g), ni_pad = padded_rows(ni), bh = g.B * g.Hq;
     const int64_t len = kv_hi - kv_lo, kv_pad = qk_pad(len);
     const int64_t ntiles = ni_pad / kQkT, nKB = kv_pad / kQkT;
-    char *c = (char *)chunk_ws;
-    int4 *qinfo = (int4 *)c;
-    c += align256((size_t)bh * ni_pad * 16);
-    int8_t *qdig = (int8_t *)c;
-    c += align256((size_t)bh * ni_pad * kQKmax * Dp64);
-    int *nfix = (int *)c;
-    c += 256;
-    int4 *fixlist = (int4 *)c;
+    const QkChunk C = qk_chunk(g, ni, len, chunk_ws);
+    int4 *qinfo = C.qinfo;
+    int8_t *qdig = C.qdig;
+    int *nfix = C.nfix;
+    int4 *fixlist = C.fixlist;
     const int64_t krows = g.B * g.Hkv * kv_pad;
     // every extent the kernels see must fit 32 bits (offsets are formed in 64)
     const int64_t lim = INT32_MAX;
     if (ni_pad > lim || kv_pad > lim || i0 + ni_pad > lim || kv_hi > lim || key_rows > lim || g.Hq > lim ||
-        bh * ntiles * nKB > lim)
+        bh * ntiles * nKB > lim || C.slotcap * kv_pad * 4 > lim)
         return hipErrorInvalidValue;
     hipError_t e;
     {
@@ -599,12 +738,16 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
         // also sets the rowmax keys of the chunk to "empty" and the fix count to
         // 0; with K's digit rows and V's column statistics when they are asked for
         const QPrep Q = make_qprep((const bf16_t *)q.data, q.sB, q.sH, q.sS, g.Hq, g.D, Dp64, i0, ni, ni_pad,
-                                   bh * ni_pad, qinfo, qdig, rowmax_keys, key_rows, key_row0, nfix);
+                                   bh * ni_pad, qinfo, qdig, rowmax_keys, key_rows, key_row0, nfix, C.qslot);
         if (!prep_q && !prep_k && !vj) {
-            if ((e = launch_fill_u32((uint32_t *)nfix, 1, 0u, s)) != hipSuccess) return e;  // the fix count
+            // the fix count; the rows keep no slots (their digits are kept, the key range changed)
+            if ((e = launch_fill_u32((uint32_t *)nfix, 2, 0u, s)) != hipSuccess) return e;
+            if ((e = launch_fill_u32((uint32_t *)C.qslot, bh * ni_pad, 0xffffffffu, s)) != hipSuccess) return e;
         } else if (prep_k || vj || !prep_q) {
             const QPrep K = prep_k ? k_rows(k, g, kv_lo, kv_hi, kprep) : QPrep{};
             launch_prep(prep_k ? &K : nullptr, Q, prep_q, vj, s);
+            if (!prep_q && (e = launch_fill_u32((uint32_t *)C.qslot, bh * ni_pad, 0xffffffffu, s)) != hipSuccess)
+                return e;
         } else {
             launch_qkprep<false>(Q, s);
         }
@@ -620,6 +763,9 @@ hipError_t launch_scores_qk(const Tensor &q, const Tensor &k, const AttnGeom &g,
     a.nfix = nfix;
     a.fixlist = fixlist;
     a.fixcap = (int)(bh * ntiles * nKB);  // the list region holds one entry per item
+    a.qslot = C.qslot;
+    a.slots = C.slots;
+    a.slotcap = (int)C.slotcap;
     a.scale = g.scale;
     a.Dp64 = (int)Dp64;
     a.ni = (int)ni;

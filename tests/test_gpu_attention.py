@@ -346,6 +346,24 @@ def test_bf16_scores_outlier_rows_take_the_fp64_chain(A, oracle, causal):
     assert_bits_equal(m, oracle.attn_rowmax(q, k, 0, 96, causal, 0.02), "rowmax")
 
 
+@pytest.mark.parametrize("nkeys", [40, 300])
+def test_pairs_outside_the_refined_bound_deferred_and_overflowing(A, oracle, nkeys):
+    """Query rows and keys each holding one small entry at the same position:
+    every such pair fails both the item bound and the refined per-pair bound
+    (equal positions), so its score must come from the fp64 chain.  Two rows
+    against 40 keys (80 pairs: several extra blocks of deferred pairs) and
+    against 300 keys (600 pairs: more than a tile can defer, the tile takes
+    the generic path) must both match the oracle bit for bit."""
+    q, k, v = W.attn_inputs(611, 1, 2, 1, 64, 320, 128, torch.float32)
+    for r in (5, 21):
+        q[0, 1, r, 77] = 2.0 ** -15 * 1.5
+    k[0, 0, :nkeys, 77] = 2.0 ** -18 * 1.25
+    q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    ref = oracle.det_attn(q, k, v, False, 0.05)
+    out = A.det_attn(*gpu(q, k, v), False, 0.05)
+    assert_bits_equal(out, ref, f"{nkeys} keys")
+
+
 def test_small_workspace_many_row_chunks_bit_identical(A, gqa):
     """A workspace a sixth of the default size makes the library run the query
     rows in several chunks (K and V are prepared by the first chunk's launches
