@@ -45,6 +45,7 @@ SIGNATURES = {
     "det_profile_begin": (C.c_int, []),
     "det_profile_end": (_SZ, [C.c_char_p, _SZ]),
     "det_debug_force_generic": (C.c_int, [_I32]),
+    "det_debug_pass2_layout": (C.c_int, [_I32]),
     "det_attn_workspace_size": (_SZ, [_T, _T, _T, _I32]),
     "det_attn": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _SZ, _P]),
     "det_attn_noalloc": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P]),
@@ -95,6 +96,14 @@ def force_generic(on: bool) -> None:
     """Testing aid: send every tile through the library's generic exact path
     (bit-identical results) until switched off again."""
     check(lib().det_debug_force_generic(int(bool(on))))
+
+
+def pass2_layout(mode: int) -> None:
+    """Testing aid: pick pass 2's kernel layout for bf16 head dims <= 128
+    (0: by key-range length, 1: eight waves each making weights and
+    multiplying, 2: split weight-making and multiplying waves); the outputs
+    are the same bits either way."""
+    check(lib().det_debug_pass2_layout(int(mode)))
 
 
 def profile_begin() -> None:

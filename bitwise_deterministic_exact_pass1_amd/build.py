@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdet_attn.so")
-SOURCES = ["attn.hip", "qk.hip", "pv.hip", "ce.hip", "bwd.hip", "noalloc.hip", "capi.cpp"]
+SOURCES = ["attn.hip", "qk.hip", "pv.hip", "pv2.hip", "ce.hip", "bwd.hip", "noalloc.hip", "capi.cpp"]
 ARCH = os.environ.get("DET_OFFLOAD_ARCH", "gfx950")
 
 

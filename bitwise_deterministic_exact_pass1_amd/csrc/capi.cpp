@@ -243,6 +243,9 @@ VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
 // generic exact path, so tests can check that both paths give the same bits.
 std::atomic<int> g_force_generic{0};
 int force_fallback() { return g_force_generic.load(std::memory_order_relaxed); }
+// Set by det_debug_pass2_layout (a testing aid): which pass-2 kernel takes
+// recomputed scores (0: by key-range length).
+std::atomic<int> g_pass2_layout{0};
 
 // Largest chunk (a multiple of kRowTile, or all Sq rows) whose need fits `budget`;
 // 0 if even one tile does not fit.
@@ -281,6 +284,12 @@ const char *det_last_error(void) { return g_err.c_str(); }
 
 int det_debug_force_generic(int32_t on) {
     g_force_generic.store(on ? 1 : 0, std::memory_order_relaxed);
+    return ok();
+}
+
+int det_debug_pass2_layout(int32_t mode) {
+    if (mode < 0 || mode > 2) return fail(DET_E_VALUE, "pass-2 layout %d is not 0, 1 or 2", (int)mode);
+    g_pass2_layout.store(mode, std::memory_order_relaxed);
     return ok();
 }
 
@@ -827,3 +836,7 @@ int det_ce_backward(const void *logits, int32_t dtype, int64_t N, int64_t V, int
 }
 
 }  // extern "C"
+
+namespace det {
+int pass2_layout() { return g_pass2_layout.load(std::memory_order_relaxed); }
+}  // namespace det

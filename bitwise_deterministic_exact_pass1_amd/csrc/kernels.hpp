@@ -165,6 +165,9 @@ struct PvSrc {
     const float *slots;
     int64_t slot_bytes;
 };
+// The pass-2 layout forced by the testing switch (0: by key-range length).
+int pass2_layout();
+
 // The recomputed-score source of a chunk of ni query rows against a key range
 // of kv_len keys, from the workspace parts the score path prepared; slots:
 // pass 1 ran on this chunk and key range just before, and its score slots of

@@ -594,8 +594,8 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
 // ---------------------------------------------------------------- launchers
 
 static int64_t qk_dp64(const AttnGeom &g) { return (g.D + 63) / 64 * 64; }
-// K digit rows of a key range: whole 32-key blocks (pass 2 stages 32 keys at a time), zero past the range
-static int64_t qk_pad(int64_t len) { return std::max<int64_t>((len + 31) / 32, 1) * 32; }
+// K digit rows of a key range: whole 64-key blocks (pass 2 stages 32 or 64 keys at a time), zero past the range
+static int64_t qk_pad(int64_t len) { return std::max<int64_t>((len + 63) / 64, 1) * 64; }
 
 size_t qk_kprep_bytes(const AttnGeom &g, int64_t kv_len) {
     const int64_t rows = g.B * g.Hkv * qk_pad(kv_len);

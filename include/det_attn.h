@@ -112,6 +112,14 @@ size_t det_profile_end(char *buf, size_t len);
  * switch lets tests check that.  Process-wide; returns DET_OK. */
 int det_debug_force_generic(int32_t on);
 
+/* Testing aid (results never depend on it): pass 2 of bf16 attention with
+ * head dims up to 128 has two kernel layouts with the same exact sums --
+ * weight-making and multiplying waves on 32-key blocks, or every wave doing
+ * both on 64-key blocks.  mode 0 (the default) picks by the key range's
+ * length; 1 and 2 force the eight-wave and the split layout for every later
+ * call.  Process-wide; DET_E_VALUE for another mode, else DET_OK. */
+int det_debug_pass2_layout(int32_t mode);
+
 /* ---------------------------------------------------------------- attention */
 
 /* det-attn page, "API": det_attn(Q, K, V, causal, scale) -- the whole path

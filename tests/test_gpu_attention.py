@@ -435,3 +435,70 @@ def test_v_remainder_list_overflow_takes_the_generic_path(A, oracle):
     ref = oracle.det_attn(q, k, v, True, scale)
     out = A.det_attn(*gpu(q, k, v), True, scale)
     assert_bits_equal(out, ref, "overflow")
+
+
+# ---------------------------------------------------------------- both pass-2 layouts
+
+@contextlib.contextmanager
+def pass2_layout(mode):
+    """Force one of pass 2's two kernel layouts for bf16 head dims <= 128 (the
+    library's testing switch; 0 restores the choice by key-range length)."""
+    from bitwise_deterministic_exact_pass1_amd import _lib
+    _lib.pass2_layout(mode)
+    try:
+        yield
+    finally:
+        _lib.pass2_layout(0)
+
+
+def _layout_case(case):
+    if case == "gqa_causal":
+        q, k, v = W.attn_inputs(701, 2, 4, 2, 333, 333, 128, torch.bfloat16)
+        return q, k, v, True, W.default_scale(128)
+    if case == "d64_rect":
+        q, k, v = W.attn_inputs(702, 1, 3, 1, 77, 450, 64, torch.bfloat16)
+        return q, k, v, False, W.default_scale(64)
+    if case == "d17_causal":
+        q, k, v = W.attn_inputs(703, 1, 2, 2, 130, 130, 17, torch.bfloat16)
+        return q, k, v, True, W.default_scale(17)
+    if case == "wide_v":
+        q, k, v = W.attn_inputs(704, 1, 4, 2, 300, 300, 128, torch.bfloat16)
+        return q, k, v_with_low_bits(v, 128), True, W.default_scale(128)
+    q, k, v = W.attn_inputs(705, 1, 2, 1, 64, 320, 128, torch.float32)
+    if case.startswith("deferred"):
+        nkeys = int(case.split("_")[1])
+        for r in (5, 21):
+            q[0, 1, r, 77] = 2.0 ** -15 * 1.5
+        k[0, 0, :nkeys, 77] = 2.0 ** -18 * 1.25
+    else:  # outlier rows: many binades, more than four digits
+        q[0, 1, 3, 5] = 1e-9
+        q[0, 0, 40, :7] = 3e-12
+        k[0, 0, 7, 9] = 2e-10
+        k[0, 0, 51, :] *= 1e6
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), False, 0.05
+
+
+@pytest.mark.parametrize("case", ["gqa_causal", "d64_rect", "d17_causal", "wide_v", "deferred_40",
+                                  "deferred_300", "outliers"])
+def test_pass2_layouts_bit_identical(A, oracle, case):
+    """Pass 2's two kernel layouts (split weight-making and multiplying waves,
+    or eight waves doing both) give the same bits as each other and as the
+    oracle: fused, sharded with ragged splits, and as digits."""
+    q, k, v, causal, scale = _layout_case(case)
+    say(f"pass-2 layouts: {case}")
+    Q, K, V = gpu(q, k, v)
+    S = K.shape[2]
+    splits = [S // 3, 5, S - S // 3 - 5]  # ragged, one shard shorter than a key block
+    res = {}
+    for mode in (1, 2):
+        with pass2_layout(mode):
+            out = A.det_attn(Q, K, V, causal, scale)
+            sh = A.det_attn_sharded(Q, K, V, splits, causal, scale, order=list(range(len(splits)))[::-1])
+            m = A.rowmax(Q, K, 0, S, causal, scale)
+            n, d = A.accumulate(Q, K, V, m, 0, S, causal, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(sh, out), f"layout {mode}: sharded != fused"
+        res[mode] = (out, n, d)
+    assert torch.equal(res[1][0], res[2][0])
+    assert torch.equal(res[1][1], res[2][1]) and torch.equal(res[1][2], res[2][2])
+    assert_bits_equal(res[1][0], oracle.det_attn(q, k, v, causal, scale), case)
