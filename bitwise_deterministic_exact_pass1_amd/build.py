@@ -4,10 +4,18 @@
 
 Numerics flags: ``-ffp-contract=off`` (the only fused operations are explicit
 fma calls) and packed-fp32 code generation switched off.
+
+Every build also checks the compiler's per-kernel resource report: a kernel
+that spills registers (SGPRs to VGPR lanes, or VGPRs to scratch memory) or
+uses scratch fails the build unless it is listed in ``SPILL_CEILINGS`` and
+stays within its listed counts.  The listed kernels are the pass-2 and
+fix-up kernels whose register budget is spent on exact accumulators; their
+spills sit in set-up and per-tile code, and the list only lets them shrink.
 """
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -18,6 +26,50 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdet_attn.so")
 SOURCES = ["attn.hip", "qk.hip", "pv.hip", "pv2.hip", "ce.hip", "bwd.hip", "noalloc.hip", "capi.cpp"]
 ARCH = os.environ.get("DET_OFFLOAD_ARCH", "gfx950")
+
+
+# Kernel-name pattern -> (SGPR spills, VGPR spills, scratch bytes per lane),
+# the most each kernel matching it may report.  Every other kernel must
+# report zero for all three.
+SPILL_CEILINGS = [
+    (r"^_ZN3det4k_pvILb[01]E", (130, 115, 300)),    # pass 2, split layout
+    (r"^_ZN3det5k_pv2ILb[01]E", (270, 30, 124)),    # pass 2, eight-wave layout
+    (r"^_ZN3det8k_pv_fixILb[01]E", (165, 0, 0)),   # pass 2, generic tiles
+    (r"^_ZN3det9k_qk_mfmaILi[1-4]E", (24, 0, 0)),  # pass 1 scores
+    (r"^_ZN3det8k_qk_fix", (4, 0, 0)),             # pass 1, fp64-chain scores
+    (r"^_ZN3det9k_bwd_mmaILi[0-2]E", (18, 0, 0)),  # backward, matrix-core sums
+    (r"^_ZN3det17k_ce_backward_tab", (15, 0, 0)),  # cross-entropy gradient
+]
+
+_REMARK = re.compile(r"remark:\s+(Function Name|SGPRs Spill|VGPRs Spill|ScratchSize \[bytes/lane\]):\s+(\S+)")
+
+
+def kernel_resources(log: str) -> dict:
+    """{kernel: (sgpr spills, vgpr spills, scratch bytes per lane)} from the
+    compiler's kernel-resource-usage remarks."""
+    out, name, vals = {}, None, {}
+    for m in _REMARK.finditer(log):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            name, vals = val, {}
+            continue
+        if name is None:
+            continue
+        vals[key] = int(val)
+        if len(vals) == 3:
+            out[name] = (vals["SGPRs Spill"], vals["VGPRs Spill"], vals["ScratchSize [bytes/lane]"])
+    return out
+
+
+def spill_violations(res: dict) -> list:
+    """Kernels whose spills or scratch exceed what SPILL_CEILINGS allows."""
+    bad = []
+    for name, got in sorted(res.items()):
+        lim = next((c for pat, c in SPILL_CEILINGS if re.match(pat, name)), (0, 0, 0))
+        if any(g > l for g, l in zip(got, lim)):
+            bad.append("%s: sgpr spills %d, vgpr spills %d, scratch %d B/lane (allowed %d, %d, %d)"
+                       % ((name,) + tuple(got) + tuple(lim)))
+    return bad
 
 
 def hipcc() -> str:
@@ -31,7 +83,7 @@ def command(out: str) -> list:
     return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
             "-ffp-contract=off", "-fno-fast-math",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument",
+            "-Wno-unused-command-line-argument", "-Rpass-analysis=kernel-resource-usage",
             "-I", INCLUDE, "-I", CSRC, "-o", out] + [os.path.join(CSRC, s) for s in SOURCES]
 
 
@@ -45,7 +97,16 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libdet_attn.so")
+    kernels = kernel_resources(res.stderr)
+    bad = spill_violations(kernels)
+    if not kernels or bad:
+        os.remove(tmp)
+        raise RuntimeError("register spills beyond the allowed ceilings:\n  " + "\n  ".join(bad)
+                           if bad else "hipcc printed no kernel resource report")
     os.replace(tmp, LIB)
+    if verbose:
+        spilled = sum(1 for v in kernels.values() if any(v))
+        print("%d kernels, %d with listed spills" % (len(kernels), spilled), flush=True)
     return LIB
 
 

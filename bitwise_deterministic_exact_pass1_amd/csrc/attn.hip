@@ -177,10 +177,10 @@ hipError_t launch_widen_q(const Tensor &q, const AttnGeom &g, int64_t i0, int64_
 
 // ---------------------------------------------------------------- pass 1: scores
 
-// Query rows of a tile are read at compile-time offsets r*DP*8 from one scalar
-// base address (DP = the padded head dim), so each row's slice arrives with a
-// single s_load_dwordx16 and the row loop is branch-free: the widened Q chunk
-// is padded with zero rows up to a multiple of kRowTile.
+// The widened query tile (kRowTile rows x DP doubles, zero-padded rows and
+// columns) is staged once per block in LDS; every lane of a wave reads the same
+// address there (a broadcast, no bank conflicts), so no query value is held in
+// scalar registers and the tile loop carries no spills.
 template <typename TK, int DP>
 __global__ __launch_bounds__(256) void k_scores(const double *__restrict__ q64, const TK *__restrict__ kp,
                                                 int64_t ksB, int64_t ksH, int64_t ksS, int64_t Hq, int64_t group,
@@ -189,7 +189,8 @@ __global__ __launch_bounds__(256) void k_scores(const double *__restrict__ q64, 
                                                 float *__restrict__ scores, uint32_t *__restrict__ rowmax_keys,
                                                 int64_t key_rows, int64_t key_row0) {
     constexpr int RT = kRowTile;
-    constexpr int DC = 8;  // head-dim slice per step: one s_load_dwordx16 per row
+    constexpr int DC = 8;  // head-dim slice per step
+    __shared__ double qs[RT * DP];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t bh = blockIdx.z;
@@ -200,6 +201,8 @@ __global__ __launch_bounds__(256) void k_scores(const double *__restrict__ q64, 
     const int nrows = (int)min64(RT, i1 - ir0);
     const int64_t W = kv_hi - kv_lo;
     const double *qtile = q64 + (bh * ni_pad + (ir0 - i0)) * DP;
+    for (int t = threadIdx.x; t < RT * DP; t += blockDim.x) qs[t] = qtile[t];
+    __syncthreads();
     const TK *kbase = kp + b * ksB + hk * ksH;
 
     uint32_t mkey[RT];
@@ -216,26 +219,37 @@ __global__ __launch_bounds__(256) void k_scores(const double *__restrict__ q64, 
         double acc[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = 0.0;
+#pragma unroll 1
         for (int dc = 0; dc < DP; dc += DC) {
             double kv[DC];
 #pragma unroll
             for (int u = 0; u < DC; ++u)
                 kv[u] = (jv && dc + u < D) ? (double)elem<TK>::to_f32(krow[dc + u]) : 0.0;
-            const double *qd = qtile + dc;
+            const double *qd = qs + dc;
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
 #pragma unroll
                 for (int u = 0; u < DC; ++u) acc[r] = fma(qd[r * DP + u], kv[u], acc[r]);
             }
         }
+        // one running address for the tile's score rows (a per-row address
+        // for each of the RT rows would be RT scalar pairs live at once)
+        float *srow = scores ? scores + (bh * ni + (ir0 - i0)) * W + (j - kv_lo) : nullptr;
+        // the key's offset from the tile's first row, clamped to [-1, RT]:
+        // key j is visible to row ir0 + r under the causal mask iff dj <= r
+        const int dj = (int)max64(-1, min64(RT, j - ir0));
+        // rows past the chunk's end are zero padding: their scores are not
+        // stored and their maxima never leave the kernel (a per-lane bound,
+        // so the row tests are made where they are used)
+        int nrows_v;  // (a vector copy the compiler cannot split back into 32 scalar tests)
+        asm volatile("v_mov_b32 %0, %1" : "=v"(nrows_v) : "s"(nrows));
+        const int lim = jv ? nrows_v : 0;
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-            if (r < nrows) {
-                const int64_t i = ir0 + r;
-                const float sc = (float)(scale * acc[r]);
-                if (scores && jv) scores[(bh * ni + (i - i0)) * W + (j - kv_lo)] = sc;
-                if (jv && (!causal || j <= i)) mkey[r] = max(mkey[r], order_key(sc));
-            }
+            const float sc = (float)(scale * acc[r]);
+            if (srow && r < lim) *srow = sc;
+            if (jv && (!causal || dj <= r)) mkey[r] = max(mkey[r], order_key(sc));
+            if (srow) srow += W;
         }
     }
     if (!rowmax_keys) return;
@@ -432,27 +446,32 @@ hipError_t launch_rowmax_combine(float *acc, const float *part, int64_t n, hipSt
 
 // ---------------------------------------------------------------- finalize
 
-__global__ void k_finalize(const int64_t *__restrict__ num, const int64_t *__restrict__ den, int64_t plane_rows,
-                           int64_t rows_per_bh, int64_t row0, int64_t Hq, int64_t i0, int64_t ni, int64_t D,
-                           float *__restrict__ o, int64_t osB, int64_t osH, int64_t osS, int64_t total) {
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t d = t % D;
-        const int64_t r = t / D;
-        const int64_t ii = r % ni, bh = r / ni;
-        const int64_t i = i0 + ii;
-        const int64_t prow = bh * rows_per_bh + (i - row0);
-        int64_t nd[kNumDigits], dd[kDenDigits];
-        const int64_t nplane = plane_rows * D;
+// One block of 64 threads per output row (blockIdx.x = bh * ni + ii), its
+// threads striding over the head dim: the row's indices are wave-uniform and
+// computed once, not per element.
+__global__ __launch_bounds__(64) void k_finalize(const int64_t *__restrict__ num, const int64_t *__restrict__ den,
+                                                 int64_t plane_rows, int64_t rows_per_bh, int64_t row0, int64_t Hq,
+                                                 int64_t i0, int64_t ni, int64_t D, float *__restrict__ o,
+                                                 int64_t osB, int64_t osH, int64_t osS) {
+    const int64_t r = blockIdx.x;
+    const int64_t ii = r % ni, bh = r / ni;
+    const int64_t i = i0 + ii;
+    const int64_t prow = bh * rows_per_bh + (i - row0);
+    const int64_t b = bh / Hq, h = bh % Hq;
+    int64_t dd[kDenDigits];
 #pragma unroll
-        for (int k = 0; k < kNumDigits; ++k) nd[k] = num[k * nplane + prow * D + d];
+    for (int k = 0; k < kDenDigits; ++k) dd[k] = den[k * plane_rows + prow];
+    canonicalize<kDenDigits>(dd);
+    const double d64 = digits_to_f64<kDenDigits>(dd, kDenElo);
+    const int64_t nplane = plane_rows * D;
+    const int64_t *nrow = num + prow * D;
+    float *orow = o + b * osB + h * osH + i * osS;
+    for (int64_t d = threadIdx.x; d < D; d += 64) {
+        int64_t nd[kNumDigits];
 #pragma unroll
-        for (int k = 0; k < kDenDigits; ++k) dd[k] = den[k * plane_rows + prow];
+        for (int k = 0; k < kNumDigits; ++k) nd[k] = nrow[k * nplane + d];
         canonicalize<kNumDigits>(nd);
-        canonicalize<kDenDigits>(dd);
-        const double n64 = digits_to_f64<kNumDigits>(nd, kNumElo);
-        const double d64 = digits_to_f64<kDenDigits>(dd, kDenElo);
-        const int64_t b = bh / Hq, h = bh % Hq;
-        o[b * osB + h * osH + i * osS + d] = (float)(n64 / d64);
+        orow[d] = (float)(digits_to_f64<kNumDigits>(nd, kNumElo) / d64);
     }
 }
 
@@ -460,10 +479,11 @@ hipError_t launch_finalize(const int64_t *num, const int64_t *den, int64_t plane
                            int64_t row0, int64_t B_Hq, int64_t Hq, int64_t i0, int64_t i1, int64_t D,
                            const OutView &o, hipStream_t s) {
     ProfScope prof_("finalize", s);
-    const int64_t ni = i1 - i0, total = B_Hq * ni * D;
-    if (total <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_finalize, grid_for(total), dim3(256), 0, s, num, den, plane_rows, rows_per_bh, row0, Hq,
-                       i0, ni, D, o.data, o.sB, o.sH, o.sS, total);
+    const int64_t ni = i1 - i0, rows = B_Hq * ni;
+    if (rows <= 0 || D <= 0) return hipSuccess;
+    if (rows > INT32_MAX) return hipErrorInvalidValue;  // one block per row
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)rows), dim3(64), 0, s, num, den, plane_rows, rows_per_bh, row0, Hq,
+                       i0, ni, D, o.data, o.sB, o.sH, o.sS);
     return hipGetLastError();
 }
 
