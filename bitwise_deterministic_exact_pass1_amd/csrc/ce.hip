@@ -101,6 +101,15 @@ __device__ __forceinline__ void ce_loss(const int64_t (&dd)[kDenDigits], const v
     denom[i] = d64;
 }
 
+// The same loss from a target logit already loaded (xt, exact in f32).
+__device__ __forceinline__ void ce_loss_of(const int64_t (&dd)[kDenDigits], float xt, float m, int64_t i,
+                                           float *loss, double *denom) {
+    const double d64 = digits_to_f64<kDenDigits>(dd, kDenElo);
+    const double lse = (double)m + log_det(d64);
+    loss[i] = (float)(lse - (double)xt);
+    denom[i] = d64;
+}
+
 template <typename T>
 __global__ void k_ce_finalize(const int64_t *den, const void *x, int64_t N, int64_t ld, const int64_t *targets,
                               const float *rowmax, float *loss, double *denom) {
@@ -194,6 +203,7 @@ constexpr int kTT = 512;                   // threads of a row workgroup
 constexpr int kHalf = 32 * 128;            // patterns per sign: 32 binades x 128 mantissas
 constexpr int kTab = 2 * kHalf;            // table slots
 constexpr int kSlots = kTab / kTT;         // slots per thread (16)
+constexpr int kPipe = 4;                  // vectors per thread in flight while the previous ones are binned
 constexpr int kQcap = 2048;                // out-of-window patterns kept per row
 constexpr int64_t kTabMinLen = kTab;       // shorter ranges use the per-element kernels
 constexpr int64_t kCountMax = (int64_t)1 << 29;  // count * w stays exact in binary64
@@ -226,6 +236,14 @@ struct RowSplit {
     __device__ int64_t nscalar() const { return head + (len - tail0); }
 };
 
+// Window base from each thread's largest sampled magnitude pattern: four
+// times headroom above the workgroup's largest, 32 binades down.
+__device__ __forceinline__ uint32_t window_of_sample_max(uint32_t mag, uint32_t *red) {
+    const uint32_t top = block_max_key(mag, red) >> 7;  // exponent field of the largest sample
+    const int lo = max(0, (int)top + 2 - 31);
+    return (uint32_t)lo << 7;
+}
+
 // Window base for a row: the largest magnitude among the first vector of each
 // thread (or its first scalar), reduced over the workgroup.
 __device__ __forceinline__ uint32_t pick_window(const uint16_t *p0, const RowSplit &rs, uint32_t *red) {
@@ -239,15 +257,23 @@ __device__ __forceinline__ uint32_t pick_window(const uint16_t *p0, const RowSpl
     } else if (tid < rs.nscalar()) {
         mag = p0[rs.scalar_at(tid)] & 0x7fffu;
     }
-    const uint32_t top = block_max_key(mag, red) >> 7;  // exponent field of the largest sample
-    const int lo = max(0, (int)top + 2 - 31);
-    return (uint32_t)lo << 7;
+    return window_of_sample_max(mag, red);
+}
+
+// The same placement from one vector per thread that every thread holds
+// (rows with at least 8 vectors per thread).
+__device__ __forceinline__ uint32_t window_from_sample(const uint4 u, uint32_t *red) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t mag = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mag = max(mag, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
+    return window_of_sample_max(mag, red);
 }
 
 struct HistShared {
     uint32_t hist[kTab];
     uint16_t q[kQcap];
-    int64_t sd[kDenDigits];
+    int64_t sd[kTT / 64][kDenDigits];  // one digit set per wave (fewer lanes per LDS atomic address)
     uint32_t red[kTT / 64];
     uint32_t qn;
 };
@@ -289,33 +315,62 @@ __device__ __forceinline__ void hist_put8(HistShared &S, const uint4 u, uint32_t
 // max and RN64(den) are written; otherwise the caller's max is used and the
 // digits go to den[k*N + i] (added to what is there when add_into).
 template <bool FWD>
-__global__ __launch_bounds__(kTT) void k_ce_hist(const uint16_t *x, int64_t N, int64_t ld, int64_t v_lo,
-                                                 int64_t v_hi, const int64_t *targets, const float *rowmax_in,
-                                                 float *loss, float *rowmax_out, double *denom, int64_t *den,
-                                                 int add_into) {
+__global__ __launch_bounds__(kTT, 6) void k_ce_hist(const uint16_t *x, int64_t N, int64_t ld, int64_t v_lo,
+                                                    int64_t v_hi, const int64_t *targets, const float *rowmax_in,
+                                                    float *loss, float *rowmax_out, double *denom, int64_t *den,
+                                                    int add_into) {
     __shared__ HistShared S;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int64_t i = blockIdx.x;
     const uint16_t *p0 = x + i * ld + v_lo;
     const RowSplit rs(p0, v_hi - v_lo);
-
     for (int k = tid; k < kTab / 4; k += kTT) ((uint4 *)S.hist)[k] = make_uint4(0u, 0u, 0u, 0u);
-    if (tid < kDenDigits) S.sd[tid] = 0;
+    if (tid < kDenDigits * (kTT / 64)) (&S.sd[0][0])[tid] = 0;
     if (tid == 0) S.qn = 0;
-    const uint32_t base = pick_window(p0, rs, S.red);  // synchronizes
 
+    // The first batch of loads is issued before the window is placed: the
+    // window comes from each thread's first vector, which is that batch's
+    // first element, so the placement waits for one load round trip that
+    // the rest of the batch overlaps.
     const uint4 *vp = (const uint4 *)(p0 + rs.head);
     int64_t k = tid;
-    for (; k + 7 * kTT < rs.nvec; k += 8 * kTT) {
+    uint32_t base;
+    if (8 * kTT <= rs.nvec) {  // (a workgroup-uniform test: both branches hold a barrier)
         uint4 u[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) u[j] = vp[k + j * kTT];
+        base = window_from_sample(u[0], S.red);  // synchronizes
 #pragma unroll
         for (int j = 0; j < 8; ++j) hist_put8(S, u[j], base);
+        k += 8 * kTT;
+    } else {
+        base = pick_window(p0, rs, S.red);  // synchronizes
+    }
+    // software-pipelined: the next four vectors are in flight while the
+    // current four are binned
+    if (k + (kPipe - 1) * kTT < rs.nvec) {
+        uint4 a[kPipe];
+#pragma unroll
+        for (int j = 0; j < kPipe; ++j) a[j] = vp[k + j * kTT];
+        k += kPipe * kTT;
+        for (; k + (kPipe - 1) * kTT < rs.nvec; k += kPipe * kTT) {
+            uint4 b[kPipe];
+#pragma unroll
+            for (int j = 0; j < kPipe; ++j) b[j] = vp[k + j * kTT];
+#pragma unroll
+            for (int j = 0; j < kPipe; ++j) hist_put8(S, a[j], base);
+#pragma unroll
+            for (int j = 0; j < kPipe; ++j) a[j] = b[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kPipe; ++j) hist_put8(S, a[j], base);
     }
     for (; k < rs.nvec; k += kTT) hist_put8(S, vp[k], base);
     for (int64_t j = tid; j < rs.nscalar(); j += kTT) hist_put(S, p0[rs.scalar_at(j)], base);
     __syncthreads();
+    // the target logit is loaded now and used at the very end
+    float xt = 0.0f;
+    if (FWD && tid == 0) xt = bf16_value(x[i * ld + targets[i]]);
 
     const uint32_t qn = S.qn;
     const bool over = qn > (uint32_t)kQcap;  // some outside patterns were not kept: rescan for them
@@ -349,6 +404,7 @@ __global__ __launch_bounds__(kTT) void k_ce_hist(const uint16_t *x, int64_t N, i
         m = rowmax_in[i];
     }
 
+    int64_t *sd = S.sd[wave];
     Window win;
     win.init();
 #pragma unroll
@@ -358,7 +414,7 @@ __global__ __launch_bounds__(kTT) void k_ce_hist(const uint16_t *x, int64_t N, i
             if (w != 0.0f) {
                 const double t = (double)w * (double)cnt[j];  // exact: 24 x 29 bits
                 const int ew = f32_exp(w);
-                win.add<kDenDigits>(t, max(ew, -126) - 23, f64_exp(t) + 1, kDenGcap, kDenElo, S.sd, 1);
+                win.add<kDenDigits>(t, max(ew, -126) - 23, f64_exp(t) + 1, kDenGcap, kDenElo, sd, 1);
             }
         }
     }
@@ -366,7 +422,7 @@ __global__ __launch_bounds__(kTT) void k_ce_hist(const uint16_t *x, int64_t N, i
         const float w = weight(bf16_value(c), m);
         if (w != 0.0f) {
             const int ew = f32_exp(w);
-            win.add<kDenDigits>((double)w, max(ew, -126) - 23, ew + 1, kDenGcap, kDenElo, S.sd, 1);
+            win.add<kDenDigits>((double)w, max(ew, -126) - 23, ew + 1, kDenGcap, kDenElo, sd, 1);
         }
     };
     if (!over) {
@@ -377,16 +433,22 @@ __global__ __launch_bounds__(kTT) void k_ce_hist(const uint16_t *x, int64_t N, i
             if (tab_slot(c, base) >= (uint32_t)kTab) add_one(c);
         }
     }
-    win.flush<kDenDigits>(kDenElo, S.sd, 1);
+    win.flush<kDenDigits>(kDenElo, sd, 1);
+    __syncthreads();
+    if (tid < kDenDigits) {  // the waves' digit sets, added as integers (any order gives the same sum)
+        int64_t acc = 0;
+        for (int w = 1; w < kTT / 64; ++w) acc += S.sd[w][tid];
+        S.sd[0][tid] += acc;
+    }
     __syncthreads();
     if (tid == 0) {
         int64_t d[kDenDigits];
 #pragma unroll
-        for (int q = 0; q < kDenDigits; ++q) d[q] = S.sd[q] + ((!FWD && add_into) ? den[q * N + i] : 0);
+        for (int q = 0; q < kDenDigits; ++q) d[q] = S.sd[0][q] + ((!FWD && add_into) ? den[q * N + i] : 0);
         canonicalize<kDenDigits>(d);
         if (FWD) {
             rowmax_out[i] = m;
-            ce_loss<bf16_t>(d, x, ld, i, targets[i], m, loss, denom);
+            ce_loss_of(d, xt, m, i, loss, denom);
         } else {
 #pragma unroll
             for (int q = 0; q < kDenDigits; ++q) den[q * N + i] = d[q];

@@ -37,6 +37,29 @@ constexpr int kRowTile = 32;    // query rows per score tile
 constexpr int kKeyTile = 256;   // keys per score tile (4 waves x 64 lanes)
 
 // Query rows of a chunk, padded to whole row tiles (padding rows are zero).
+// The workgroup's logical grid position (x, y, z), its linear ids dealt so
+// that each of the chip's 8 XCDs runs one contiguous range of z-major, then
+// y-major positions: workgroups are handed to the XCDs round-robin by linear
+// id, so without this every XCD would touch every head, and each XCD's L2
+// would fetch every head's data from HBM.  A bijection of the grid, so any
+// other dispatch order only loses the locality.
+struct GridPos {
+    uint32_t x, y, z;
+};
+__device__ __forceinline__ GridPos xcd_grouped_pos() {
+    constexpr uint32_t kXcds = 8;
+    // (computed by every lane and read back from the first: vector registers
+    // are free at this point, scalar ones are not)
+    uint32_t X = gridDim.x, Y = gridDim.y, N = X * Y * gridDim.z;
+    uint32_t L = (blockIdx.z * Y + blockIdx.y) * X + blockIdx.x;
+    asm volatile("" : "+v"(X), "+v"(Y), "+v"(N), "+v"(L));
+    const uint32_t xcd = L % kXcds, r = L / kXcds, q = N / kXcds, rem = N % kXcds;
+    const uint32_t M = (xcd < rem ? xcd * (q + 1) : rem * (q + 1) + (xcd - rem) * q) + r;
+    return GridPos{(uint32_t)__builtin_amdgcn_readfirstlane((int)(M % X)),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)((M / X) % Y)),
+                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(M / (X * Y)))};
+}
+
 inline int64_t padded_rows(int64_t ni) { return (ni + kRowTile - 1) / kRowTile * kRowTile; }
 inline int64_t padded_dim(int64_t D) {
     int64_t p = 16;

@@ -749,7 +749,8 @@ __device__ __forceinline__ bool pv_consume(const PvArgs &A, int G0, int64_t bh, 
 template <bool FUSED, int NG, int ND>
 __global__ __launch_bounds__(64 * (NG + kPW), 2) void k_pv(PvArgs A, int G0) {
     __shared__ __align__(16) PvShared<ND> S;
-    const int64_t bh = blockIdx.y, x = blockIdx.x;
+    const GridPos gp = xcd_grouped_pos();
+    const int64_t bh = gp.y, x = gp.x;
     const int npass = (A.causal && x != A.ntiles - 1 - x) ? 2 : 1;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (wave >= NG) {

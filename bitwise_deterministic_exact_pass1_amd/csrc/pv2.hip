@@ -576,7 +576,8 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
 template <bool FUSED, int ND>
 __global__ __launch_bounds__(64 * kW2, 2) void k_pv2(PvArgs A) {
     __shared__ __align__(16) Pv2Shared<ND> S;
-    const int64_t bh = blockIdx.y, x = blockIdx.x;
+    const GridPos gp = xcd_grouped_pos();
+    const int64_t bh = gp.y, x = gp.x;
     const int npass = (A.causal && x != A.ntiles - 1 - x) ? 2 : 1;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll 1

@@ -306,7 +306,7 @@ struct QkShared {
 // row (A) or column (B) l%16 with k = 16*(l/16) + 0..15; result register r of
 // lane l holds row 4*(l/16) + r, column l%16.
 template <int ND>
-__device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t group, QkShared<ND> &S) {
+__device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t group, int part, QkShared<ND> &S) {
     constexpr int RB = kQKmax * 64 * ND;  // digit bytes of one key (or row) in global memory
     constexpr int KROW = QkShared<ND>::kRow;
     constexpr int NCH = kQkT * RB / 16;   // 16-byte chunks of one block
@@ -314,7 +314,7 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lq = lane >> 4;
-    const int P = gridDim.x, part = blockIdx.x;
+    const int P = gridDim.x;  // (part: this workgroup's key-block phase, 0 <= part < P)
     const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
     const int tile = (int)group * kQkWaves + wave;
     const bool live = tile < A.ntiles;
@@ -499,11 +499,12 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
 template <int ND>
 __global__ __launch_bounds__(64 * kQkWaves, ND <= 2 ? 3 : 2) void k_qk_mfma(QkArgs A) {
     __shared__ __align__(16) QkShared<ND> S;
-    const int64_t bh = blockIdx.z, y = blockIdx.y;
+    const GridPos gp = xcd_grouped_pos();
+    const int64_t bh = gp.z, y = gp.y;
     const int npass = (A.causal && y != A.ngroups - 1 - y) ? 2 : 1;
     for (int pass = 0; pass < npass; ++pass) {
         if (pass) __syncthreads();  // the LDS of the first group is free again
-        qk_group<ND>(A, bh, (A.causal && pass == 0) ? A.ngroups - 1 - y : y, S);
+        qk_group<ND>(A, bh, (A.causal && pass == 0) ? A.ngroups - 1 - y : y, (int)gp.x, S);
     }
 }
 

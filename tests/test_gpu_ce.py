@@ -236,3 +236,21 @@ def test_pattern_tables_gradient_edge_rows(CE, edge, oracle):
     grad = CE.backward(X, T, m, denom, g.cuda(), "none")
     ref = oracle.ce_backward(x, t, m.cpu().numpy(), denom.cpu().numpy(), g.numpy(), "none")
     assert np.array_equal(u32(grad.cpu().numpy()), u32(ref))
+
+
+@pytest.mark.parametrize("nvec", [2004, 3584, 3585, 3700, 4000, 4095, 4096, 5000])
+def test_range_lengths_around_the_first_load_batch(CE, oracle, nvec):
+    """Ranges of 8 * nvec bf16 columns, around eight 16-byte vectors per thread
+    of a 512-thread row workgroup (where the row kernels switch between placing
+    the window from a first load batch and from a separate sample): forward and
+    denominator digits equal the oracle bit for bit."""
+    x, t = W.ce_inputs(seed=47, N=24, V=8 * nvec)
+    X, T = x.cuda(), t.cuda()
+    loss, m, denom = CE.forward(X, T)
+    rl, rm, rd = oracle.ce_forward(x, t)
+    assert np.array_equal(u32(loss), u32(rl)) and np.array_equal(denom.cpu().numpy(), rd)
+    lo = 8 * (nvec // 3)
+    d = CE.denom_digits(X, m, lo, 8 * nvec).cpu().numpy()
+    ref = oracle.ce_denom_digits(x, m.cpu().numpy(), lo, 8 * nvec)
+    val = lambda a: [sum(int(a[k, i]) << (32 * k) for k in range(a.shape[0])) for i in range(a.shape[1])]
+    assert val(d) == val(ref)
