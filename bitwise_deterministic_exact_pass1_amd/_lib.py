@@ -46,6 +46,7 @@ SIGNATURES = {
     "det_profile_end": (_SZ, [C.c_char_p, _SZ]),
     "det_debug_force_generic": (C.c_int, [_I32]),
     "det_debug_pass2_layout": (C.c_int, [_I32]),
+    "det_debug_score_source": (C.c_int, [_I32]),
     "det_attn_workspace_size": (_SZ, [_T, _T, _T, _I32]),
     "det_attn": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P, _SZ, _P]),
     "det_attn_noalloc": (C.c_int, [_T, _T, _T, _I32, _D, _O, _P]),
@@ -104,6 +105,13 @@ def pass2_layout(mode: int) -> None:
     multiplying, 2: split weight-making and multiplying waves); the outputs
     are the same bits either way."""
     check(lib().det_debug_pass2_layout(int(mode)))
+
+
+def score_source(mode: int) -> None:
+    """Testing aid: how pass 2 gets bf16 scores (0: kept when the workspace
+    allows, 1: kept, 2: recomputed from the digit rows); the outputs are the
+    same bits either way."""
+    check(lib().det_debug_score_source(int(mode)))
 
 
 def profile_begin() -> None:

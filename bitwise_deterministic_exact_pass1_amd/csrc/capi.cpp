@@ -187,36 +187,60 @@ size_t bytes_rowmax(const AttnGeom &g, bool mfma, int64_t ni, int64_t kv_len) {
     return score_fixed_bytes(g, mfma, kv_len) + score_chunk_bytes(g, mfma, ni, kv_len) + align256((size_t)bh * ni * 4);
 }
 
-// Stored scores between the passes: only the f32 path keeps them (bf16 scores
-// are recomputed in pass 2 from the digit rows pass 1 prepared).
-size_t stored_score_bytes(bool mfma, int64_t rows, int64_t W) { return mfma ? 0 : align256((size_t)rows * W * 4); }
+// Set by det_debug_score_source (a testing aid): 0 chooses by workspace size,
+// 1 keeps bf16 scores between the passes, 2 recomputes them in pass 2.
+std::atomic<int> g_score_source{0};
 
-size_t bytes_accumulate(const AttnGeom &g, bool mfma, int64_t ni, int64_t W) {
+// Scores kept between the passes (an f32 per row and key of the chunk), unless
+// pass 2 recomputes them (rc: bf16 only, from the digit rows pass 1 prepared).
+size_t stored_score_bytes(bool rc, int64_t rows, int64_t W) { return rc ? 0 : align256((size_t)rows * W * 4); }
+
+size_t bytes_accumulate(const AttnGeom &g, bool mfma, bool rc, int64_t ni, int64_t W) {
     const int64_t bh = g.B * g.Hq;
     return vprep_bytes(g, W) + score_fixed_bytes(g, mfma, W) + score_chunk_bytes(g, mfma, ni, W) +
-           stored_score_bytes(mfma, bh * ni, W) + align256((size_t)bh * ((ni + 31) / 32) * 4);
+           stored_score_bytes(rc, bh * ni, W) + align256((size_t)bh * ((ni + 31) / 32) * 4);
 }
 
-size_t bytes_fused(const AttnGeom &g, bool mfma, int64_t ni) {
+size_t bytes_fused(const AttnGeom &g, bool mfma, bool rc, int64_t ni) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, g.Skv) + score_fixed_bytes(g, mfma, g.Skv) + score_chunk_bytes(g, mfma, ni, g.Skv) +
-           align256((size_t)rows * 4) + stored_score_bytes(mfma, rows, g.Skv) + pv_fallback_bytes(g, ni);
+           align256((size_t)rows * 4) + stored_score_bytes(rc, rows, g.Skv) + pv_fallback_bytes(g, ni);
 }
 
-size_t bytes_sharded(const AttnGeom &g, bool mfma, int64_t ni, int64_t maxlen) {
+size_t bytes_sharded(const AttnGeom &g, bool mfma, bool rc, int64_t ni, int64_t maxlen) {
     const int64_t bh = g.B * g.Hq, rows = bh * ni;
     return vprep_bytes(g, maxlen) + score_fixed_bytes(g, mfma, maxlen) + score_chunk_bytes(g, mfma, ni, maxlen) +
-           align256((size_t)rows * 4) + stored_score_bytes(mfma, rows, maxlen) + align256((size_t)rows * 4) +
+           align256((size_t)rows * 4) + stored_score_bytes(rc, rows, maxlen) + align256((size_t)rows * 4) +
            align256((size_t)bh * ((ni + 31) / 32) * 4) +
            align256((size_t)kNumDigits * rows * g.D * 8) + align256((size_t)kDenDigits * rows * 8);
+}
+
+// Whether pass 2 recomputes the bf16 scores instead of reading the ones pass 1
+// kept.  Keeping them costs a round trip through HBM of 4 bytes per (row, key)
+// and an O(rows x keys) workspace per row chunk; recomputing costs the score
+// products and their exact composition a second time.  Measured on MI355X:
+// keeping is faster up to a few thousand keys per row (1024 keys: 0.11 against
+// 0.16 ms per call; 8192: 9.5 against 9.7 ms), recomputing beyond (37810
+// keys, head dim 128: 0.71 against 0.75 s).  So the scores are recomputed for
+// key ranges of kRecomputeKeys or more at head dims up to 128, or when one row
+// tile's share of the kept buffer does not fit the workspace (a small fixed
+// scratch; `need_kept_tile`: the layout's size for one tile with kept
+// scores), and kept otherwise; f32 scores are always kept.
+constexpr int64_t kRecomputeKeys = 16384;
+template <typename F>
+bool recompute_scores(bool mfma, const AttnGeom &g, int64_t kv_len, size_t ws_bytes, F need_kept_tile) {
+    if (!mfma) return false;
+    const int m = g_score_source.load(std::memory_order_relaxed);
+    if (m == 1 || m == 2) return m == 2;
+    return (kv_len >= kRecomputeKeys && g.D <= 128) || need_kept_tile() > ws_bytes;
 }
 
 // Pass 2's score source for rows [i0, i1) against [lo, hi): stored scores, or
 // the digit rows in kprep / the chunk workspace (with pass 1's score slots when
 // pass 1 ran on the same rows and range just before: `slots`).
-PvSrc pv_src(const Tensor &tq, const Tensor &tk, const AttnGeom &g, bool mfma, void *kprep, void *cws, float *sc,
+PvSrc pv_src(const Tensor &tq, const Tensor &tk, const AttnGeom &g, bool rc, void *kprep, void *cws, float *sc,
              int64_t i0, int64_t i1, int64_t lo, int64_t hi, bool slots = false) {
-    if (mfma) return qk_pv_src(tq, tk, g, kprep, cws, i1 - i0, hi - lo, slots);
+    if (rc) return qk_pv_src(tq, tk, g, kprep, cws, i1 - i0, hi - lo, slots);
     PvSrc p{};
     p.scores = sc;
     p.W = hi - lo;
@@ -284,6 +308,12 @@ const char *det_last_error(void) { return g_err.c_str(); }
 
 int det_debug_force_generic(int32_t on) {
     g_force_generic.store(on ? 1 : 0, std::memory_order_relaxed);
+    return ok();
+}
+
+int det_debug_score_source(int32_t mode) {
+    if (mode < 0 || mode > 2) return fail(DET_E_VALUE, "score source %d is not 0, 1 or 2", (int)mode);
+    g_score_source.store(mode, std::memory_order_relaxed);
     return ok();
 }
 
@@ -368,7 +398,11 @@ size_t det_attn_accumulate_workspace_size(const det_tensor *q, const det_tensor 
     if (check_qkv(q, k, v, 0) || check_qrange(q, q_lo, q_hi) || check_range(k, kv_lo, kv_hi)) return 0;
     const AttnGeom g = geom(q, k, 0, 1.0);
     const bool mf = use_mfma_scores(q);
-    return default_size(q_hi - q_lo, [&](int64_t ni) { return bytes_accumulate(g, mf, ni, kv_hi - kv_lo); });
+    const int64_t nq = q_hi - q_lo, W = kv_hi - kv_lo;
+    const bool recomp = recompute_scores(mf, g, W, kDefaultBudget, [&] {
+        return bytes_accumulate(g, mf, false, std::max<int64_t>(std::min<int64_t>(nq, kRowTile), 1), W);
+    });
+    return default_size(nq, [&](int64_t ni) { return bytes_accumulate(g, mf, recomp, ni, W); });
 }
 
 int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tensor *v, const float *rowmax,
@@ -383,7 +417,10 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     const AttnGeom g = geom(q, k, causal, scale);
     const bool mf = use_mfma_scores(q);
     const int64_t W = kv_hi - kv_lo;
-    auto need = [&](int64_t ni) { return bytes_accumulate(g, mf, ni, W); };
+    const bool recomp = recompute_scores(mf, g, W, ws_bytes, [&] {
+        return bytes_accumulate(g, mf, false, std::max<int64_t>(std::min<int64_t>(nq, kRowTile), 1), W);
+    });
+    auto need = [&](int64_t ni) { return bytes_accumulate(g, mf, recomp, ni, W); };
     if ((rc = check_ws(workspace, ws_bytes, nq > 0 ? need(std::min<int64_t>(nq, kRowTile)) : 0))) return rc;
     if (nq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
@@ -395,7 +432,7 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     void *kprep = c0.take<char>(score_fixed_bytes(g, mf, W));
     // per-chunk regions, sized for the largest chunk and reused by every chunk
     void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, W));
-    float *sc = mf ? nullptr : c0.take<float>(bh * chunk * W);
+    float *sc = recomp ? nullptr : c0.take<float>(bh * chunk * W);
     int *flags = c0.take<int>(bh * ((chunk + 31) / 32));
     if (c0.over) return fail(DET_E_WORKSPACE, "internal: workspace layout exceeds its computed size");
     // only rows [q_lo, q_hi) of each head are touched
@@ -408,7 +445,7 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
         const int64_t i1 = std::min(q_hi, i0 + chunk);
         // the first chunk's launches also prepare K and V
         const bool first = i0 == q_lo;
-        if (mf)  // the digit rows pass 2 recomputes the scores from (and V's, on the first chunk)
+        if (recomp)  // the digit rows pass 2 recomputes the scores from (and V's, on the first chunk)
             HIP_TRY(launch_qkv_prep(tq, tk, tv, g, kprep, first, true, first ? &vp : nullptr, cws, i0, i1, kv_lo, kv_hi,
                                     s),
                     "prepare");
@@ -416,7 +453,7 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
             HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, first, true, first ? &vp : nullptr, cws, i0, i1, kv_lo,
                                kv_hi, sc, nullptr, 0, 0, s),
                     "scores");
-        HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, mf, kprep, cws, sc, i0, i1, kv_lo, kv_hi), rowmax, nullptr, g.Sq,
+        HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, recomp, kprep, cws, sc, i0, i1, kv_lo, kv_hi), rowmax, nullptr, g.Sq,
                           0, i0, i1, kv_lo, kv_hi, flags, nullptr, nullptr, nullptr, num, den, rows, g.Sq, 0, ff, s),
                 "deposit");
     }
@@ -474,7 +511,10 @@ size_t det_attn_workspace_size(const det_tensor *q, const det_tensor *k, const d
     if (check_qkv(q, k, v, causal)) return 0;
     const AttnGeom g = geom(q, k, causal, 1.0);
     const bool mf = use_mfma_scores(q);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_fused(g, mf, ni); });
+    const bool recomp = recompute_scores(mf, g, g.Skv, kDefaultBudget, [&] {
+        return bytes_fused(g, mf, false, std::max<int64_t>(std::min<int64_t>(g.Sq, kRowTile), 1));
+    });
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_fused(g, mf, recomp, ni); });
 }
 
 static int fused_attn(const det_tensor *q, const det_tensor *k, const det_tensor *v, int32_t causal, double scale,
@@ -485,7 +525,10 @@ static int fused_attn(const det_tensor *q, const det_tensor *k, const det_tensor
     if (q->S > 0 && (rc = check_out(o))) return rc;
     const AttnGeom g = geom(q, k, causal, scale);
     const bool mf = use_mfma_scores(q);
-    auto need = [&](int64_t ni) { return bytes_fused(g, mf, ni); };
+    const bool recomp = recompute_scores(mf, g, g.Skv, ws_bytes, [&] {
+        return bytes_fused(g, mf, false, std::max<int64_t>(std::min<int64_t>(g.Sq, kRowTile), 1));
+    });
+    auto need = [&](int64_t ni) { return bytes_fused(g, mf, recomp, ni); };
     if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
     if (g.Sq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
@@ -499,7 +542,7 @@ static int fused_attn(const det_tensor *q, const det_tensor *k, const det_tensor
     const int64_t crows = bh * chunk, ctiles = (chunk + 31) / 32;
     void *cws = c0.take<char>(score_chunk_bytes(g, mf, chunk, g.Skv));
     uint32_t *keys = c0.take<uint32_t>(crows);
-    float *sc = mf ? nullptr : c0.take<float>(crows * g.Skv);
+    float *sc = recomp ? nullptr : c0.take<float>(crows * g.Skv);
     int *flags = c0.take<int>(bh * ctiles);
     int64_t *fnum = c0.take<int64_t>(kNumDigits * bh * ctiles * 32 * g.D);
     int64_t *fden = c0.take<int64_t>(kDenDigits * bh * ctiles * 32);
@@ -508,11 +551,11 @@ static int fused_attn(const det_tensor *q, const det_tensor *k, const det_tensor
     for (int64_t i0 = 0; i0 < g.Sq; i0 += chunk) {
         const int64_t i1 = std::min(g.Sq, i0 + chunk), ni = i1 - i0;
         // the first chunk's launches also prepare K and V
-        // pass 1 (bf16: the row maxima only; f32: the scores are kept for pass 2)
+        // pass 1: the row maxima, and the scores when they are kept for pass 2
         HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, i0 == 0, true, i0 == 0 ? &vp : nullptr, cws, i0, i1, 0, g.Skv, sc,
                            keys, ni, i0, s),
                 "scores");
-        HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, mf, kprep, cws, sc, i0, i1, 0, g.Skv, true), nullptr, keys, ni, i0, i0,
+        HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, recomp, kprep, cws, sc, i0, i1, 0, g.Skv, true), nullptr, keys, ni, i0, i0,
                           i1, 0, g.Skv, flags, fnum, fden, &ov, nullptr, nullptr, 0, 0, 0, ff, s, stat_m, stat_den,
                           g.Sq),
                 "deposit");
@@ -532,7 +575,10 @@ int det_attn_noalloc(const det_tensor *q, const det_tensor *k, const det_tensor 
     if (q->S > 0 && (rc = check_out(o))) return rc;
     const AttnGeom g = geom(q, k, causal, scale);
     const bool mf = use_mfma_scores(q);
-    const size_t need_min = g.Sq > 0 ? bytes_fused(g, mf, std::min<int64_t>(g.Sq, kRowTile)) : 0;
+    const int64_t tile_rows = std::max<int64_t>(std::min<int64_t>(g.Sq, kRowTile), 1);
+    const bool recomp =
+        recompute_scores(mf, g, g.Skv, kNoAllocBytes, [&] { return bytes_fused(g, mf, false, tile_rows); });
+    const size_t need_min = g.Sq > 0 ? bytes_fused(g, mf, recomp, tile_rows) : 0;
     if (need_min > kNoAllocBytes)
         return fail(DET_E_WORKSPACE,
                     "det_attn_noalloc: one %d-row chunk of this problem needs %zu bytes of scratch; the fixed "
@@ -656,7 +702,10 @@ size_t det_attn_sharded_workspace_size(const det_tensor *q, const det_tensor *k,
     const AttnGeom g = geom(q, k, causal, 1.0);
     const bool mf = use_mfma_scores(q);
     const int64_t ml = max_split(kv_splits, n_splits);
-    return default_size(g.Sq, [&](int64_t ni) { return bytes_sharded(g, mf, ni, ml); });
+    const bool recomp = recompute_scores(mf, g, ml, kDefaultBudget, [&] {
+        return bytes_sharded(g, mf, false, std::max<int64_t>(std::min<int64_t>(g.Sq, kRowTile), 1), ml);
+    });
+    return default_size(g.Sq, [&](int64_t ni) { return bytes_sharded(g, mf, recomp, ni, ml); });
 }
 
 int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor *v, const int64_t *kv_splits,
@@ -668,7 +717,10 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
     const AttnGeom g = geom(q, k, causal, scale);
     const bool mf = use_mfma_scores(q);
     const int64_t ml = max_split(kv_splits, n_splits);
-    auto need = [&](int64_t ni) { return bytes_sharded(g, mf, ni, ml); };
+    const bool recomp = recompute_scores(mf, g, ml, ws_bytes, [&] {
+        return bytes_sharded(g, mf, false, std::max<int64_t>(std::min<int64_t>(g.Sq, kRowTile), 1), ml);
+    });
+    auto need = [&](int64_t ni) { return bytes_sharded(g, mf, recomp, ni, ml); };
     if ((rc = check_ws(workspace, ws_bytes, g.Sq > 0 ? need(std::min<int64_t>(g.Sq, kRowTile)) : 0))) return rc;
     if (g.Sq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
@@ -689,7 +741,7 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
         void *kprep = c.take<char>(score_fixed_bytes(g, mf, ml));
         void *cws = c.take<char>(score_chunk_bytes(g, mf, ni, ml));
         uint32_t *keys = c.take<uint32_t>(rows);
-        float *sc = mf ? nullptr : c.take<float>(rows * ml);
+        float *sc = recomp ? nullptr : c.take<float>(rows * ml);
         float *rm_acc = c.take<float>(rows);
         int *flags = c.take<int>(bh * ((ni + 31) / 32));
         int64_t *num_acc = c.take<int64_t>(kNumDigits * rows * g.D);
@@ -720,12 +772,12 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
             const int32_t sh = order ? order[a] : a;
             const int64_t l = lo[sh], h = l + kv_splits[sh];
             if (h <= l) continue;
-            if (mf)  // this shard's K and V digit rows; Q's are kept from pass 1
+            if (recomp)  // this shard's K and V digit rows; Q's are kept from pass 1
                 HIP_TRY(launch_qkv_prep(tq, tk, tv, g, kprep, true, false, &vp, cws, i0, i1, l, h, s), "prepare");
             else
                 HIP_TRY(run_scores(tq, tk, tv, g, mf, kprep, true, false, &vp, cws, i0, i1, l, h, sc, nullptr, 0, 0, s),
                         "scores");
-            HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, mf, kprep, cws, sc, i0, i1, l, h), rm_acc, nullptr, ni, i0,
+            HIP_TRY(launch_pv(tv, g, vp, pv_src(tq, tk, g, recomp, kprep, cws, sc, i0, i1, l, h), rm_acc, nullptr, ni, i0,
                               i0, i1, l, h, flags, nullptr, nullptr, nullptr, num_acc, den_acc, rows, ni, i0, ff, s),
                     "deposit");
         }

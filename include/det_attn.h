@@ -120,6 +120,15 @@ int det_debug_force_generic(int32_t on);
  * call.  Process-wide; DET_E_VALUE for another mode, else DET_OK. */
 int det_debug_pass2_layout(int32_t mode);
 
+/* Testing aid (results never depend on it): pass 2 of bf16 attention reads
+ * the scores pass 1 kept in the workspace, or recomputes them from the digit
+ * rows pass 1 prepared (no O(rows x keys) buffer).  mode 0 (the default)
+ * keeps them whenever one 32-row tile's share fits the workspace; 1 keeps
+ * and 2 recomputes for every later call.  Process-wide; DET_E_VALUE for
+ * another mode, else DET_OK.  (Forcing 1 can make a small workspace fail the
+ * size check with DET_E_WORKSPACE.) */
+int det_debug_score_source(int32_t mode);
+
 /* ---------------------------------------------------------------- attention */
 
 /* det-attn page, "API": det_attn(Q, K, V, causal, scale) -- the whole path

@@ -174,14 +174,24 @@ _LAYOUT_CASES = [
 ]
 
 
+@pytest.fixture
+def score_source(lib, request):
+    """The score-source testing switch, reset to its default afterwards."""
+    assert lib.det_debug_score_source(request.param) == 0
+    yield request.param
+    assert lib.det_debug_score_source(0) == 0
+
+
 @pytest.mark.skipif(not _no_device(), reason="passes dummy device pointers: only where no device exists")
+@pytest.mark.parametrize("score_source", [0, 1, 2], indirect=True)
 @pytest.mark.parametrize("dtype", [L.DET_F32, L.DET_BF16])
 @pytest.mark.parametrize("case", _LAYOUT_CASES, ids=lambda c: "x".join(map(str, c[:5])))
-def test_workspace_layout_fits_the_reported_size(lib, case, dtype):
+def test_workspace_layout_fits_the_reported_size(lib, case, dtype, score_source):
     """Each entry point carves its workspace on the host before it launches
     anything; given exactly the size its *_workspace_size reports, it must get
     past that (and then fail at its first HIP call, there being no device)
-    rather than report that its layout outgrew the workspace."""
+    rather than report that its layout outgrew the workspace.  For each way
+    pass 2 may get bf16 scores (kept, recomputed, or chosen by size)."""
     B, Hq, Hkv, S, D, causal, splits = case
     q = _t(B=B, H=Hq, S=S, D=D, dtype=dtype, data=0x100000)
     k = _t(B=B, H=Hkv, S=S, D=D, dtype=dtype, data=0x200000)
@@ -214,3 +224,12 @@ def test_workspace_layout_fits_the_reported_size(lib, case, dtype):
     rc = lib.det_attn_backward(C.byref(q), C.byref(k), C.byref(v), C.byref(of), C.byref(of), 0x500000, 0x600000,
                                causal, 0.125, C.byref(o), C.byref(o), C.byref(o), ws, n, None)
     assert rc == -6, (rc, lib.det_last_error())
+
+
+def test_testing_switches_reject_unknown_modes(lib):
+    """The pass-2 testing switches take modes 0-2 and refuse others with
+    DET_E_VALUE, leaving the current mode as it was."""
+    for fn in (lib.det_debug_score_source, lib.det_debug_pass2_layout):
+        assert fn(3) == -7 and fn(-1) == -7  # DET_E_VALUE
+        for m in (2, 1, 0):
+            assert fn(m) == 0

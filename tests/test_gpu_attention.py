@@ -164,6 +164,11 @@ def test_cp_share_sampled_rows_bit_exact(A, oracle, name, nrows):
     ref = oracle.det_attn(wl["q"], wl["k"], wl["v"], True, wl["scale"], rows=rows)
     b, h, i = rows.T
     assert_bits_equal(out.cpu().numpy()[b, h, i], ref, name)
+    for mode in (1, 2):
+        say(f"{name}: det_attn, score source {mode}")
+        with score_source(mode):
+            o2 = A.det_attn(Q, K, V, True, wl["scale"])
+        assert torch.equal(o2, out), f"score source {mode}"
     blk = 1024 if name == "cp_share_bf16" else 256
     say(f"{name}: 8 x {blk} shards")
     sh = A.det_attn_sharded(Q, K, V, [blk] * 8, True, wl["scale"], order=W.shard_order(1003, 8))
@@ -192,6 +197,13 @@ def test_long_nhd_sampled_rows_bit_exact(A, oracle, long_nhd):
     ref = oracle.det_attn(q, k, v, False, scale, rows=rows)
     b, h, i = rows.T
     assert_bits_equal(out.cpu().numpy()[b, h, i], ref, "long nhd")
+    for mode in (1, 2):  # kept and recomputed scores, whichever the default chose
+        say(f"long: det_attn, score source {mode}")
+        with score_source(mode):
+            o2 = A.det_attn(Q, K, V, False, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, out), f"score source {mode}"
+        del o2
 
 
 def test_long_nhd_591_blocks_all_rows(A, long_nhd):
@@ -480,12 +492,53 @@ def _layout_case(case):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16), False, 0.05
 
 
-@pytest.mark.parametrize("case", ["gqa_causal", "d64_rect", "d17_causal", "wide_v", "deferred_40",
-                                  "deferred_300", "outliers"])
+@contextlib.contextmanager
+def score_source(mode):
+    """Force how pass 2 gets bf16 scores: 1 kept from pass 1, 2 recomputed
+    from the digit rows (the library's testing switch; 0 restores the choice
+    by workspace size)."""
+    from bitwise_deterministic_exact_pass1_amd import _lib
+    _lib.score_source(mode)
+    try:
+        yield
+    finally:
+        _lib.score_source(0)
+
+
+LAYOUT_CASES = ["gqa_causal", "d64_rect", "d17_causal", "wide_v", "deferred_40", "deferred_300", "outliers"]
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES)
+def test_kept_and_recomputed_scores_bit_identical(A, oracle, case):
+    """Pass 2 reading the scores pass 1 kept, or recomputing them from the
+    digit rows, gives the oracle's bits: fused, sharded with ragged splits,
+    and as digits."""
+    q, k, v, causal, scale = _layout_case(case)
+    say(f"score sources: {case}")
+    Q, K, V = gpu(q, k, v)
+    S = K.shape[2]
+    splits = [S // 3, 5, S - S // 3 - 5]
+    res = {}
+    for mode in (1, 2):
+        with score_source(mode):
+            out = A.det_attn(Q, K, V, causal, scale)
+            sh = A.det_attn_sharded(Q, K, V, splits, causal, scale, order=[2, 0, 1])
+            m = A.rowmax(Q, K, 0, S, causal, scale)
+            n, d = A.accumulate(Q, K, V, m, 0, S, causal, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(sh, out), f"source {mode}: sharded != fused"
+        res[mode] = (out, n, d)
+    assert torch.equal(res[1][0], res[2][0])
+    assert torch.equal(res[1][1], res[2][1]) and torch.equal(res[1][2], res[2][2])
+    assert_bits_equal(res[1][0], oracle.det_attn(q, k, v, causal, scale), case)
+
+
+@pytest.mark.parametrize("case", LAYOUT_CASES)
 def test_pass2_layouts_bit_identical(A, oracle, case):
-    """Pass 2's two kernel layouts (split weight-making and multiplying waves,
-    or eight waves doing both) give the same bits as each other and as the
-    oracle: fused, sharded with ragged splits, and as digits."""
+    """With recomputed scores, pass 2's two kernel layouts (split
+    weight-making and multiplying waves, or eight waves doing both) give the
+    same bits as each other and as the oracle: fused, sharded with ragged
+    splits, and as digits."""
     q, k, v, causal, scale = _layout_case(case)
     say(f"pass-2 layouts: {case}")
     Q, K, V = gpu(q, k, v)
@@ -493,7 +546,7 @@ def test_pass2_layouts_bit_identical(A, oracle, case):
     splits = [S // 3, 5, S - S // 3 - 5]  # ragged, one shard shorter than a key block
     res = {}
     for mode in (1, 2):
-        with pass2_layout(mode):
+        with pass2_layout(mode), score_source(2):
             out = A.det_attn(Q, K, V, causal, scale)
             sh = A.det_attn_sharded(Q, K, V, splits, causal, scale, order=list(range(len(splits)))[::-1])
             m = A.rowmax(Q, K, 0, S, causal, scale)
