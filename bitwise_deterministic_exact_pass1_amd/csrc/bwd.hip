@@ -558,13 +558,14 @@ __global__ __launch_bounds__(512) void k_bwd_mma(BwdArgs A) {
 #pragma unroll
     for (int s = 0; s < kXC; ++s) C[s] = v4i{0, 0, 0, 0};
     // The left operand's digits, made from the f32 ds / p of each block:
-    // thread tid holds 4 consecutive steps t0..t0+3 of operand row xa (dQ:
-    // xa = tid / 16, the 4 keys adjacent in memory; dK, dV: xa = tid % 32, the
-    // 4 query rows adjacent in the operand and each load coalesced over the
-    // lanes), converts them on the row's grid and writes its 32-bit word of
-    // every digit plane of the LDS operand image (half xa / 16, lane xa % 16 +
-    // 16 (t0 / 16), bytes t0 % 16 ..).
-    const int xa = MODE == 0 ? (tid >> 4) : (tid & 31), t0 = MODE == 0 ? 4 * (tid & 15) : 4 * (tid >> 5);
+    // thread tid holds 4 consecutive steps t0..t0+3 of operand row xa,
+    // converts them on the row's grid and writes its 32-bit word of every
+    // digit plane of the LDS operand image (half xa / 16, lane xa % 16 +
+    // 16 (t0 / 16), bytes t0 % 16 ..).  A wave takes one row half and one
+    // 16-step group (wave w: half w & 1, group w >> 1), its lane l row
+    // xa % 16 = l / 4 and word l % 4, so the wave's 64 words of a plane are
+    // consecutive (no two lanes on one LDS bank line).
+    const int xa = 16 * (wv & 1) + (lane >> 2), t0 = 16 * (wv >> 1) + 4 * (lane & 3);
     int gx;
     const float *srow;
     int64_t sstep;
