@@ -588,15 +588,21 @@ __global__ __launch_bounds__(512) void k_bwd_mma(BwdArgs A) {
         int nx_;
         grid_of(st, gx, nx_);
     }
+    // (step counts are below 2^17: 32-bit step arithmetic, one 64-bit offset per block)
+    const int tmax = (int)(MODE == 0 ? A.Skv - 1 : A.ni - 1);
+    // the operand row's visible steps: t <= tlast (dQ: keys up to the query row)
+    // and t >= tfirst (dK, dV: query rows from the key on)
+    const int tlast = (A.causal && MODE == 0) ? (int)min64(tmax, A.i0 + y * 32 + xa) : tmax;
+    const int tfirst = (A.causal && MODE != 0) ? (int)max64(0, y * 32 + xa - A.i0) : 0;
     auto fetch_a = [&](int64_t kb, float (&av)[4]) {
+        // steps tb .. tb + 3 of block kb: keys (dQ) or chunk rows (dK, dV)
+        const int tb = (int)kb * kT16 + t0;
+        const float *p = srow + (int64_t)min(tb, tmax) * sstep;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // step t of block kb: key (dQ) or chunk row (dK, dV) kb*64 + t0 + e
-            const int64_t t = kb * kT16 + t0 + e;
-            const int64_t tmax = MODE == 0 ? A.Skv - 1 : A.ni - 1;
-            const float x = srow[(t < tmax ? t : tmax) * sstep];
-            bool vis = xok && t <= tmax;
-            if (A.causal) vis = vis && (MODE == 0 ? t <= A.i0 + y * 32 + xa : y * 32 + xa <= A.i0 + t);
+            const int t = tb + e;
+            const float x = p[(min(t, tmax) - min(tb, tmax)) * (int)sstep];
+            const bool vis = xok && t >= tfirst && t <= tlast;
             av[e] = vis ? x : 0.0f;
         }
     };
