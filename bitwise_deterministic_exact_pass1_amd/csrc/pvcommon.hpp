@@ -146,21 +146,37 @@ __device__ __forceinline__ uint32_t block_weights(const float (&sc)[KPT], float 
             U[g0 + u] = Wi + 0x808080808080ull;
         }
     }
+    // Plane a's word t holds byte a of U[4t .. 4t+3]: a 4 x 6 byte transpose
+    // per group of four keys, by byte permutes (v_perm_b32 picks any four
+    // bytes of its two sources: selector byte k in 0..3 names a byte of the
+    // second source, 4..7 one of the first).
+    static_assert(kAw == 6, "six W digit planes");
+    uint32_t any[kAw] = {};
+#pragma unroll
+    for (int t = 0; t < KPT / 4; ++t) {
+        const uint32_t L0 = (uint32_t)U[4 * t], L1 = (uint32_t)U[4 * t + 1], L2 = (uint32_t)U[4 * t + 2],
+                       L3 = (uint32_t)U[4 * t + 3];
+        const uint32_t H0 = (uint32_t)(U[4 * t] >> 32), H1 = (uint32_t)(U[4 * t + 1] >> 32),
+                       H2 = (uint32_t)(U[4 * t + 2] >> 32), H3 = (uint32_t)(U[4 * t + 3] >> 32);
+        // bytes 0, 1 (resp. 2, 3) of keys 0 and 1 interleaved, likewise keys 2 and 3
+        const uint32_t x01l = __builtin_amdgcn_perm(L1, L0, 0x05010400u), x01h = __builtin_amdgcn_perm(L1, L0, 0x07030602u);
+        const uint32_t x23l = __builtin_amdgcn_perm(L3, L2, 0x05010400u), x23h = __builtin_amdgcn_perm(L3, L2, 0x07030602u);
+        const uint32_t y01 = __builtin_amdgcn_perm(H1, H0, 0x05010400u), y23 = __builtin_amdgcn_perm(H3, H2, 0x05010400u);
+        const uint32_t word[kAw] = {
+            __builtin_amdgcn_perm(x23l, x01l, 0x05040100u), __builtin_amdgcn_perm(x23l, x01l, 0x07060302u),
+            __builtin_amdgcn_perm(x23h, x01h, 0x05040100u), __builtin_amdgcn_perm(x23h, x01h, 0x07060302u),
+            __builtin_amdgcn_perm(y23, y01, 0x05040100u),   __builtin_amdgcn_perm(y23, y01, 0x07060302u)};
+#pragma unroll
+        for (int a = 0; a < kAw; ++a) {
+            const uint32_t wd = word[a] ^ 0x80808080u;
+            any[a] |= wd;
+            ((uint32_t *)(dst + a * 64 * 16))[t] = wd;
+        }
+    }
     uint32_t nzm = 0;
 #pragma unroll
-    for (int a = 0; a < kAw; ++a) {
-        uint32_t word[KPT / 4] = {};
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) word[u / 4] |= ((uint32_t)(U[u] >> (8 * a)) & 255u) << (8 * (u % 4));
-        uint32_t any = 0;
-#pragma unroll
-        for (int t = 0; t < KPT / 4; ++t) {
-            word[t] ^= 0x80808080u;
-            any |= word[t];
-            ((uint32_t *)(dst + a * 64 * 16))[t] = word[t];
-        }
-        if (any) nzm |= 1u << a;
-    }
+    for (int a = 0; a < kAw; ++a)
+        if (any[a]) nzm |= 1u << a;
     return nzm;
 }
 

@@ -238,12 +238,12 @@ def test_pattern_tables_gradient_edge_rows(CE, edge, oracle):
     assert np.array_equal(u32(grad.cpu().numpy()), u32(ref))
 
 
-@pytest.mark.parametrize("nvec", [2004, 3584, 3585, 3700, 4000, 4095, 4096, 5000])
+@pytest.mark.parametrize("nvec", [1900, 2004, 2047, 2048, 2100, 3584, 3585, 3700, 4000, 4095, 4096, 5000])
 def test_range_lengths_around_the_first_load_batch(CE, oracle, nvec):
     """Ranges of 8 * nvec bf16 columns, around eight 16-byte vectors per thread
     of a 512-thread row workgroup (where the row kernels switch between placing
-    the window from a first load batch and from a separate sample): forward and
-    denominator digits equal the oracle bit for bit."""
+    the window from a first load batch and from a separate sample), and
+    shorter ones: forward and denominator digits equal the oracle bit for bit."""
     x, t = W.ce_inputs(seed=47, N=24, V=8 * nvec)
     X, T = x.cuda(), t.cuda()
     loss, m, denom = CE.forward(X, T)
@@ -254,3 +254,33 @@ def test_range_lengths_around_the_first_load_batch(CE, oracle, nvec):
     ref = oracle.ce_denom_digits(x, m.cpu().numpy(), lo, 8 * nvec)
     val = lambda a: [sum(int(a[k, i]) << (32 * k) for k in range(a.shape[0])) for i in range(a.shape[1])]
     assert val(d) == val(ref)
+
+
+def test_pattern_counts_past_16_bits(CE, oracle):
+    """Rows where one bf16 pattern occurs more than 65535 times, beside rows of
+    two patterns of 35000 each: forward, split denominator digits and
+    gradient equal the oracle bit for bit (the pattern counts times the
+    pattern weights stay exact at any count the tables admit)."""
+    g = torch.Generator().manual_seed(48)
+    N, V = 4, 70001
+    x = (torch.randn(N, V, generator=g) * 2.0)
+    x[0] = 0.5                        # one pattern everywhere
+    x[1, :66000] = -1.25              # 66000 copies beside random values
+    x[2, :35000] = 1.0                # two patterns of 35000, no overflow
+    x[2, 35000:70000] = -1.0
+    x[3, 100:65737] = 3.0             # exactly 65637 copies, beside the row max
+    x = x.to(torch.bfloat16)
+    t = torch.tensor([5, 66001, 12, 70000], dtype=torch.int64)
+    X, T = x.cuda(), t.cuda()
+    loss, m, denom = CE.forward(X, T)
+    rl, rm, rd = oracle.ce_forward(x, t)
+    assert np.array_equal(u32(loss), u32(rl)) and np.array_equal(denom.cpu().numpy(), rd)
+    assert np.array_equal(u32(m), u32(rm))
+    for lo, hi in [(0, V), (1000, V)]:
+        d = CE.denom_digits(X, m, lo, hi).cpu().numpy()
+        ref = oracle.ce_denom_digits(x, m.cpu().numpy(), lo, hi)
+        val = lambda a: [sum(int(a[k, i]) << (32 * k) for k in range(a.shape[0])) for i in range(a.shape[1])]
+        assert val(d) == val(ref), (lo, hi)
+    gr = CE.backward(X, T, m, denom, torch.ones(1).cuda(), "sum")
+    ref = oracle.ce_backward(x, t, rm, rd, np.ones(1, np.float32), "sum")
+    assert np.array_equal(u32(gr), u32(ref))
