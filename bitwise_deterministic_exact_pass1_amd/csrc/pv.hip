@@ -1026,7 +1026,9 @@ static hipError_t launch_pv_t(const PvArgs &a, int64_t nG, int64_t bh, int nd, h
     // wave makes weights and multiplies (pv2.hip); its larger per-tile set-up
     // pays off past a few thousand keys.
     const int layout = pass2_layout();
-    if ((nd == 1 || nd == 2) && (layout == 1 || (layout == 0 && a.kv_hi - a.kv_lo >= 4096))) {
+    const bool eight = nd == 0 ? (nG <= 4 && layout == 1)
+                               : ((nd == 1 || nd == 2) && (layout == 1 || (layout == 0 && a.kv_hi - a.kv_lo >= 4096)));
+    if (eight) {
         {
             ProfScope prof_("pv_mfma", s);
             if ((e = launch_pv2_t<FUSED>(a, bh, nd, s)) != hipSuccess) return e;

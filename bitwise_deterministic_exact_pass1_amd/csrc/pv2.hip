@@ -84,12 +84,16 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
     const int dofs = (w & 1) * kAw * 1024 + ((lane & 15) + 16 * (w >> 1)) * 16 + 4 * (lane >> 4);
     int64_t wsum = 0, whi = 0;  // this lane's sum of W: whi 2^32 + wsum (wsum < 2^55 between folds)
     bool bad = false;
-    const int64_t qrow = bh * A.src.ni_pad + (T.it0 - A.i0) + r;
-    const int4 qi = A.src.qinfo[qrow];
-    const int slot = A.src.qslot ? A.src.qslot[qrow] : -1;
-    const bool slots = __ballot(slot >= 0) != 0;
-    int qcnt, qbnd;  // the largest digit count and bound of the wave's rows without a slot
-    {
+    // recomputed scores (ND > 0): the row's statistics and score slot, and the
+    // largest digit count and bound of the wave's rows without a slot
+    int4 qi = int4{0, 0, 0, 0};
+    int slot = -1, qcnt = 0, qbnd = 0;
+    bool slots = false;
+    if constexpr (ND > 0) {
+        const int64_t qrow = bh * A.src.ni_pad + (T.it0 - A.i0) + r;
+        qi = A.src.qinfo[qrow];
+        slot = A.src.qslot ? A.src.qslot[qrow] : -1;
+        slots = __ballot(slot >= 0) != 0;
         int qc = slot < 0 ? qi.y : 0, qb = slot < 0 ? qi.z : 0;
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) {
@@ -102,10 +106,11 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
     // K digit rows of the head through a buffer resource (lane offsets in one
     // register, the block in the scalar offset: no per-lane addresses to keep)
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const uint8_t *)A.src.kdig + T.bhk * A.src.kv_pad * (int64_t)RB), (short)0,
+        ND > 0 ? (void *)((const uint8_t *)A.src.kdig + T.bhk * A.src.kv_pad * (int64_t)RB) : nullptr, (short)0,
         (int)(A.src.kv_pad * RB), 0x00020000);
     const __amdgpu_buffer_rsrc_t irs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(A.src.kinfo + T.bhk * A.src.kv_pad), (short)0, (int)(A.src.kv_pad * 16), 0x00020000);
+        ND > 0 ? (void *)(A.src.kinfo + T.bhk * A.src.kv_pad) : nullptr, (short)0, (int)(A.src.kv_pad * 16),
+        0x00020000);
     // ---- multiplying role: dims 16 w .. 16 w + 15 of group G (32 dims) half h
     const int G = w >> 1, h = w & 1;
     const bool mine = 16 * w < A.D;
@@ -143,11 +148,12 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
 
     // ---- staging of K blocks and of the tile's Q rows
     struct KSet {
-        v4i d[CPT];
+        v4i d[CPT > 0 ? CPT : 1];
         int4 st;
     };
     // chunk c = tid + 512 t of a block is bytes 16 (c % (RB/16)) of key c / (RB/16)
     auto k_load = [&](int kb, KSet &K) {
+        if constexpr (ND == 0) return;
 #pragma unroll
         for (int t = 0; t < CPT; ++t)
             K.d[t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(krs, tid * 16,
@@ -156,6 +162,7 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
             K.st = __builtin_bit_cast(int4, __builtin_amdgcn_raw_buffer_load_b128(irs, lane * 16, kb * kKB2 * 16, 0));
     };
     auto k_store = [&](int buf, const KSet &K) {
+        if constexpr (ND == 0) return;
 #pragma unroll
         for (int t = 0; t < CPT; ++t) {
             const int c = tid + 64 * kW2 * t;
@@ -175,13 +182,20 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
             if ((lane & 15) == 0) S.kh[buf][q] = int2{kc, kbd};
         }
     };
-    // slot scores of rows that have one: the lane's four keys of block kb
-    // through a buffer resource at the slots (slot s at byte (s kv_pad + j) 4)
+    // kept scores (ND == 0): the lane's four scores of block kb through a
+    // buffer resource based at the tile's first row (key kv_lo + j of row r at
+    // byte (r W + j) 4; keys past a row's end read the next row or, past the
+    // array, zero: those keys are invisible).  Recomputed scores: the slot
+    // scores of rows that have one (slot s at byte (s kv_pad + j) 4).  Either
+    // way the block step is the scalar offset.
+    const int64_t row_first = bh * A.ni + (T.it0 - A.i0);
+    const int64_t bytes_left = ND == 0 ? ((int64_t)gridDim.y * A.ni - row_first) * A.src.W * 4 : A.src.slot_bytes;
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)A.src.slots, (short)0, (int)min64(A.src.slot_bytes, INT32_MAX), 0x00020000);
-    const int voff = slot >= 0 ? (slot * (int)A.src.kv_pad + k0) * 4 : 0;
+        ND == 0 ? (void *)(A.src.scores + row_first * A.src.W) : (void *)A.src.slots, (short)0,
+        (int)min64(bytes_left, INT32_MAX), 0x00020000);
+    const int voff = ND == 0 ? (r * (int)A.src.W + k0) * 4 : (slot >= 0 ? (slot * (int)A.src.kv_pad + k0) * 4 : 0);
     auto s_load = [&](int kb, float (&x)[4]) {
-        if (slots) {
+        if (ND == 0 || slots) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 x[u] = __builtin_bit_cast(float,
@@ -191,8 +205,17 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
 
     // ---- the weights of block kb (K rows in buffer kb & 1) into W buffer kb & 1
     // ---- the weights of block kb (K rows in buffer kb & 1) into W buffer kb & 1
-    auto make = [&](int kb) {
+    auto make = [&](int kb, const float (&pre)[4]) {
         const int kbuf = kb & 1, nv = nvis(kb);
+        if constexpr (ND == 0) {  // kept scores, loaded ahead into `pre`
+            const uint32_t nz = wave_or_mask(block_weights<4>(pre, m, nv, &S.dig[kb & 1][0][0][0] + dofs, wsum, bad));
+            if (lane == 0) S.mask[kb & 1][w] = nz;
+            if (((kb + 1) % kCarry2) == 0) {
+                whi += wsum >> 32;
+                wsum &= 0xffffffffll;
+            }
+            return;
+        }
         float stored[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         s_load(kb, stored);  // (rows with a score slot only: rare)
         const int2 kh = S.kh[kbuf][w >> 1];
@@ -301,14 +324,21 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
 
     // ---- prologue: the tile's Q rows and K blocks 0 and 1 in LDS ([A]), block
     // 2 in registers; block 0's weights ([B])
-    {
+    if constexpr (ND > 0) {
         const int8_t *qsrc = A.src.qdig + (bh * A.src.ni_pad + (T.it0 - A.i0)) * (int64_t)RB;
         for (int c = tid; c < 32 * RB / 16; c += 64 * kW2)
             *(v4i *)(S.qd + (c / (RB / 16)) * KROW + (c % (RB / 16)) * 16) = *(const v4i *)(qsrc + (int64_t)c * 16);
     }
     KSet kn;
+    // kept scores of blocks 0 and 1 in the two register sets (each set takes
+    // the block two further on once its weights are made)
+    float s0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, s1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (nblk > 0) {
         KSet k1;
+        if constexpr (ND == 0) {
+            s_load(0, s0);
+            if (nblk > 1) s_load(1, s1);
+        }
         k_load(0, kn);
         if (nblk > 1) k_load(1, k1);
         k_store(0, kn);
@@ -317,24 +347,40 @@ __device__ __forceinline__ bool pv2_tile(const PvArgs &A, const PvTile &T, int64
     }
     __syncthreads();  // [A]
     if (nblk > 2) k_load(2, kn);
-    if (nblk > 0) make(0);
+    if (nblk > 0) {
+        make(0, s0);
+        if constexpr (ND == 0)
+            if (nblk > 2) s_load(2, s0);
+    }
     __syncthreads();  // [B]
     // One step: block kb's products (its weights were made in the previous
     // step), then block kb+1's V digits into the same registers (they land
     // while the weights are made), block kb+1's weights, block kb+2's K rows
     // (in registers) into K buffer kb & 1 (block kb's, done with) and block
     // kb+3's into registers.
-    auto step = [&](int kb) {
+    // (kept scores: the loop is unrolled by two so the sets keep their roles)
+    auto step = [&](int kb, float (&set)[4]) {
         mult(kb, VA);
         if (mine && kb + 1 < nblk) v_load(kb + 1, VA);
-        if (kb + 1 < nblk) make(kb + 1);
+        if (kb + 1 < nblk) {
+            make(kb + 1, set);
+            if constexpr (ND == 0)
+                if (kb + 3 < nblk) s_load(kb + 3, set);
+        }
         if (kb + 2 < nblk) {
             k_store(kb & 1, kn);
             if (kb + 3 < nblk) k_load(kb + 3, kn);
         }
         __syncthreads();
     };
-    for (int kb = 0; kb < nblk; ++kb) step(kb);
+    if constexpr (ND == 0) {
+        for (int kb = 0; kb < nblk; kb += 2) {
+            step(kb, s1);
+            if (kb + 1 < nblk) step(kb + 1, s0);
+        }
+    } else {
+        for (int kb = 0; kb < nblk; ++kb) step(kb, s0);  // (no kept scores: the sets are unused)
+    }
 
     // ---- deferred pairs, 64 at a time as the virtual keys of extra blocks:
     // their q and k rows into the K buffers ([E0]), their scores by the rule
@@ -604,7 +650,8 @@ __global__ __launch_bounds__(64 * kW2, 2) void k_pv2(PvArgs A) {
 template <bool FUSED>
 hipError_t launch_pv2_t(const PvArgs &a, int64_t bh, int nd, hipStream_t s) {
     dim3 grid((unsigned)(a.causal ? (a.ntiles + 1) / 2 : a.ntiles), (unsigned)bh);
-    if (nd == 1) hipLaunchKernelGGL((k_pv2<FUSED, 1>), grid, dim3(64 * kW2), 0, s, a);
+    if (nd == 0) hipLaunchKernelGGL((k_pv2<FUSED, 0>), grid, dim3(64 * kW2), 0, s, a);
+    else if (nd == 1) hipLaunchKernelGGL((k_pv2<FUSED, 1>), grid, dim3(64 * kW2), 0, s, a);
     else hipLaunchKernelGGL((k_pv2<FUSED, 2>), grid, dim3(64 * kW2), 0, s, a);
     return hipGetLastError();
 }

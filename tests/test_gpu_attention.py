@@ -511,8 +511,8 @@ LAYOUT_CASES = ["gqa_causal", "d64_rect", "d17_causal", "wide_v", "deferred_40",
 @pytest.mark.parametrize("case", LAYOUT_CASES)
 def test_kept_and_recomputed_scores_bit_identical(A, oracle, case):
     """Pass 2 reading the scores pass 1 kept, or recomputing them from the
-    digit rows, gives the oracle's bits: fused, sharded with ragged splits,
-    and as digits."""
+    digit rows, in either kernel layout, gives the oracle's bits: fused,
+    sharded with ragged splits, and as digits."""
     q, k, v, causal, scale = _layout_case(case)
     say(f"score sources: {case}")
     Q, K, V = gpu(q, k, v)
@@ -520,17 +520,19 @@ def test_kept_and_recomputed_scores_bit_identical(A, oracle, case):
     splits = [S // 3, 5, S - S // 3 - 5]
     res = {}
     for mode in (1, 2):
-        with score_source(mode):
-            out = A.det_attn(Q, K, V, causal, scale)
-            sh = A.det_attn_sharded(Q, K, V, splits, causal, scale, order=[2, 0, 1])
-            m = A.rowmax(Q, K, 0, S, causal, scale)
-            n, d = A.accumulate(Q, K, V, m, 0, S, causal, scale)
-        torch.cuda.synchronize()
-        assert torch.equal(sh, out), f"source {mode}: sharded != fused"
-        res[mode] = (out, n, d)
-    assert torch.equal(res[1][0], res[2][0])
-    assert torch.equal(res[1][1], res[2][1]) and torch.equal(res[1][2], res[2][2])
-    assert_bits_equal(res[1][0], oracle.det_attn(q, k, v, causal, scale), case)
+        for layout in (1, 2):
+            with score_source(mode), pass2_layout(layout):
+                out = A.det_attn(Q, K, V, causal, scale)
+                sh = A.det_attn_sharded(Q, K, V, splits, causal, scale, order=[2, 0, 1])
+                m = A.rowmax(Q, K, 0, S, causal, scale)
+                n, d = A.accumulate(Q, K, V, m, 0, S, causal, scale)
+            torch.cuda.synchronize()
+            assert torch.equal(sh, out), f"source {mode} layout {layout}: sharded != fused"
+            res[mode, layout] = (out, n, d)
+    ref = res[1, 2]
+    for key, (out, n, d) in res.items():
+        assert torch.equal(out, ref[0]) and torch.equal(n, ref[1]) and torch.equal(d, ref[2]), key
+    assert_bits_equal(ref[0], oracle.det_attn(q, k, v, causal, scale), case)
 
 
 @pytest.mark.parametrize("case", LAYOUT_CASES)
