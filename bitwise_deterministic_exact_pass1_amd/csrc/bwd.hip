@@ -502,7 +502,7 @@ constexpr int kT16 = 64;                 // reduction steps per block
 constexpr int kXCarry16 = 8192 / kT16;   // blocks between class carries
 
 template <int MODE>
-__global__ __launch_bounds__(512) void k_bwd_mma(BwdArgs A) {
+__global__ __launch_bounds__(512, 4) void k_bwd_mma(BwdArgs A) {
     __shared__ v4i sA[2][kXA][2][64];  // [slot][digit][row half][lane]
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int rh = wv & 1;
@@ -611,32 +611,50 @@ __global__ __launch_bounds__(512) void k_bwd_mma(BwdArgs A) {
     // 0x80..80 +- x 256^q are 0x80 below q, the four bytes of w = 0x80808080
     // +- x at q..q+3 (no borrow: x < 0x80808080), 0x80 plus the carry of
     // that add at q+4 and 0x80 above, so the balanced digits (bytes ^ 0x80)
-    // are the bytes of w ^ 0x80808080, then the carry, and 0 elsewhere.  Each
-    // thread zeroes its own word of every digit plane and stores its entries'
-    // nonzero digits as bytes (same thread: the stores land in order).
+    // are the bytes of the 33-bit value carry:(w ^ 0x80808080) shifted up by
+    // q bytes, and 0 elsewhere.  With each entry's digit string as an 80-bit
+    // value (planes 0..9), the thread's word of plane a is byte a of its four
+    // entries: a byte transpose by permutes (v_perm_b32: selector byte k in
+    // 0..3 names a byte of the second source, 4..7 one of the first), stored
+    // as whole words into the planes the row uses.
     const int wofs = (((xa >> 4) * 64) + (xa & 15) + 16 * (t0 >> 4)) * 4 + ((t0 & 15) >> 2);  // in uint32
     auto stash_a = [&](int buf, const float (&av)[4]) {
         uint32_t *wb = (uint32_t *)&sA[buf][0][0][0] + wofs;
-        for (int a = 0; a < nat; ++a) wb[a * 512] = 0u;
-        uint8_t *bb = (uint8_t *)wb;
+        uint32_t lo[4], mid[4], hi[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t bits = __float_as_uint(av[e]);
-            if ((bits & 0x7fffffffu) == 0u) continue;
             const uint32_t be = (bits >> 23) & 0xffu;
             const uint32_t m = (bits & 0x7fffffu) | (be ? 0x800000u : 0u);
             const int sh = (int)(be ? be : 1u) - 150 - gx;  // >= 0 for every nonzero entry of the row
-            const int q = sh >> 3;
             const uint32_t x = m << (sh & 7);
             const bool neg = (bits >> 31) != 0;
             const uint32_t w = neg ? 0x80808080u - x : 0x80808080u + x;
-            const uint32_t dg = w ^ 0x80808080u;
             const bool carry = !neg && w < x;  // the add wrapped past 2^32
-#pragma unroll
-            for (int k = 0; k < 4; ++k)  // (q >= 0 by the grid; the bounds keep every store in the slot)
-                if (q + k >= 0 && q + k < nat) bb[(q + k) * 2048 + e] = (uint8_t)(dg >> (8 * k));
-            if (carry && q + 4 >= 0 && q + 4 < nat) bb[(q + 4) * 2048 + e] = 1;
+            const bool nz = (bits & 0x7fffffffu) != 0u;
+            const uint64_t dv = nz ? ((uint64_t)carry << 32) | (w ^ 0x80808080u) : 0ull;
+            const unsigned __int128 v = (unsigned __int128)dv << ((8 * (sh >> 3)) & 127);  // (q < kXA)
+            lo[e] = (uint32_t)v;
+            mid[e] = (uint32_t)(v >> 32);
+            hi[e] = (uint32_t)(v >> 64);
         }
+        uint32_t word[12];
+        auto transpose4 = [&](const uint32_t (&L)[4], int a0) {
+            const uint32_t x01l = __builtin_amdgcn_perm(L[1], L[0], 0x05010400u);
+            const uint32_t x01h = __builtin_amdgcn_perm(L[1], L[0], 0x07030602u);
+            const uint32_t x23l = __builtin_amdgcn_perm(L[3], L[2], 0x05010400u);
+            const uint32_t x23h = __builtin_amdgcn_perm(L[3], L[2], 0x07030602u);
+            word[a0] = __builtin_amdgcn_perm(x23l, x01l, 0x05040100u);
+            word[a0 + 1] = __builtin_amdgcn_perm(x23l, x01l, 0x07060302u);
+            word[a0 + 2] = __builtin_amdgcn_perm(x23h, x01h, 0x05040100u);
+            word[a0 + 3] = __builtin_amdgcn_perm(x23h, x01h, 0x07060302u);
+        };
+        transpose4(lo, 0);
+        transpose4(mid, 4);
+        transpose4(hi, 8);
+#pragma unroll
+        for (int a = 0; a < kXA; ++a)
+            if (a < nat) wb[a * 512] = word[a];
     };
     // the wave's B digits of a block are loaded at the start of its step
     // (other waves on the SIMD cover the latency: two workgroups per CU)
