@@ -530,15 +530,30 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
         return;
     }
     const int r = tid >> 4, c = tid & 15;
+    // the count and this workgroup's first entry are read together (the list
+    // holds fixcap entries; an entry at or past the count is never used), and
+    // each item's successor is fetched while the item is worked on
     const int n = min(*A.nfix, A.fixcap);
-    const int64_t i_end = A.i0 + A.ni;
+    int4 next = (int)blockIdx.x < A.fixcap ? A.fixlist[blockIdx.x] : int4{0, 0, 0, 0};
+    const int i_end = A.i0 + A.ni;
     for (int it = blockIdx.x; it < n; it += nfw) {
-        const int4 item = A.fixlist[it];
-        const int64_t kb = item.x, tile = item.y, bh = item.z;
-        const int64_t b = bh / A.Hq, hq = bh % A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
-        const int64_t it0 = A.i0 + tile * kQkT, j0 = A.kv_lo + kb * kQkT;
+        const int4 item = next;
+        if (it + nfw < n) next = A.fixlist[it + nfw];
+        const int kb = item.x, tile = item.y, bh = item.z;
+        const int b = bh / A.Hq, hq = bh - b * A.Hq, hk = hq / A.group, bhk = b * A.Hkv + hk;
+        const int it0 = A.i0 + tile * kQkT, j0 = A.kv_lo + kb * kQkT;
         const bf16_t *qb = q + b * qsB + hq * qsH, *kbp = k + b * ksB + hk * ksH;
         __syncthreads();  // the previous item's rows are no longer read
+        const int i = it0 + r, j = j0 + c;
+        // pair statistics, the row's score slot and its current key go out with
+        // the row loads below, so their latency overlaps the staging (all the
+        // indices are in range: rows and keys of a tile are padded, and the key
+        // row is clamped to the last row)
+        const int64_t qrow = (int64_t)bh * A.ni_pad + tile * kQkT + r;
+        const int4 qi = A.qinfo[qrow], ki = A.kinfo[(int64_t)bhk * A.kv_pad + kb * kQkT + c];
+        const int sl = A.qslot ? A.qslot[qrow] : -1;
+        uint32_t *kp = A.keys ? &A.keys[(int64_t)bh * A.key_rows + (min(i, i_end - 1) - A.key_row0)] : nullptr;
+        const uint32_t kcur = kp && c == 0 ? __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
         // thread tid loads dim tid (D <= 256) of the 16 rows of each side; clamped
         // indices keep every load in range, and clamped values are never used
         {
@@ -546,8 +561,8 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
             float xq[kQkT], xk[kQkT];
 #pragma unroll
             for (int rr = 0; rr < kQkT; ++rr) {
-                xq[rr] = elem<bf16_t>::to_f32(qb[min64(it0 + rr, i_end - 1) * qsS + dd]);
-                xk[rr] = elem<bf16_t>::to_f32(kbp[min64(j0 + rr, A.kv_hi - 1) * ksS + dd]);
+                xq[rr] = elem<bf16_t>::to_f32(qb[min(it0 + rr, i_end - 1) * qsS + dd]);
+                xk[rr] = elem<bf16_t>::to_f32(kbp[min(j0 + rr, A.kv_hi - 1) * ksS + dd]);
             }
             if (tid < D) {
 #pragma unroll
@@ -557,11 +572,8 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
                 }
             }
         }
-        const int64_t i = it0 + r, j = j0 + c;
         bool need = i < i_end && j < A.kv_hi;
-        if (need && item.w == kFixPairs)  // (read before the barrier: its latency overlaps the staging)
-            need = qk_pair_class(A.qinfo[bh * A.ni_pad + tile * kQkT + r], A.kinfo[bhk * A.kv_pad + kb * kQkT + c],
-                                 kQKmax) == kPairChain;
+        if (item.w == kFixPairs) need = need && qk_pair_class(qi, ki, kQKmax) == kPairChain;
         __syncthreads();
         uint32_t key = 0;  // below order_key of every number
         if (need) {
@@ -571,24 +583,18 @@ __global__ __launch_bounds__(256) void k_qk_fix(QkArgs A, const bf16_t *__restri
 #pragma unroll 16
             for (int d = 0; d < Di; ++d) acc = fma((double)sq[r][d], (double)sk[c][d], acc);
             const float sc = (float)(A.scale * acc);
-            if (A.scores) A.scores[(bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)] = sc;
-            if (A.qslot) {  // the score slot of the row, if it has one
-                const int sl = A.qslot[bh * A.ni_pad + (i - A.i0)];
-                if (sl >= 0 && sl < A.slotcap) A.slots[(int64_t)sl * A.kv_pad + (j - A.kv_lo)] = sc;
-            }
+            if (A.scores) A.scores[((int64_t)bh * A.ni + (i - A.i0)) * A.W + (j - A.kv_lo)] = sc;
+            if (sl >= 0 && sl < A.slotcap) A.slots[(int64_t)sl * A.kv_pad + (j - A.kv_lo)] = sc;  // the row's score slot
             if (!A.causal || j <= i) key = order_key(sc);
         }
         // the row's max over the item's 16 keys (16 consecutive lanes), then one
-        // atomic per row, skipped when the row's key is already at least as large
-        // (keys only grow within the launch, so a stale read only costs an atomic):
-        // a row listed for every key block would otherwise send all its pairs to
-        // one address
+        // atomic per row, skipped when the row's key read above is already at
+        // least as large (keys only grow within the launch, so a stale read only
+        // costs an atomic): a row listed for every key block would otherwise send
+        // all its pairs to one address
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) key = max(key, (uint32_t)__shfl_xor((int)key, off, 64));
-        if (A.keys && c == 0 && key != 0) {
-            uint32_t *kp = &A.keys[bh * A.key_rows + (i - A.key_row0)];
-            if (key > __hip_atomic_load(kp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(kp, key);
-        }
+        if (kp && c == 0 && key > kcur) atomicMax(kp, key);
     }
 }
 

@@ -74,6 +74,19 @@ template <typename TV>
 __device__ __forceinline__ void vslice_block(const VJob &J, int64_t kb, int64_t G, int64_t bhk, int lane) {
     const int64_t b = bhk / J.Hkv, hk = bhk % J.Hkv;
     const int64_t d = G * 32 + (lane & 31);
+    const TV *col = (const TV *)J.v + b * J.vsB + hk * J.vsH + (d < J.D ? d : 0);
+    const int64_t jb = J.kv_lo + kb * kKB + 16 * (lane >> 5);
+    // the block's 16 entries of this lane go out as one batch of loads with
+    // the column statistics, no branch between them: clamped key indices keep
+    // every load inside the range (an empty range reads the first word of the
+    // statistics instead), and entries past the range or the head dim are
+    // zeroed below
+    const bool any = J.kv_hi > J.kv_lo;
+    const TV *src = any ? col : (const TV *)J.stats;
+    const int64_t jlast = any ? J.kv_hi - 1 : 0, stride = any ? J.vsS : 0;
+    float xv[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p) xv[p] = elem<TV>::to_f32(src[min64(jb + p, jlast) * stride]);
     int emax = INT_MIN, lmin = INT_MAX;
     const int2 *cs = (const int2 *)J.stats + (bhk * J.nG + G) * kVChunks * 32 + (lane & 31);
 #pragma unroll
@@ -96,21 +109,18 @@ __device__ __forceinline__ void vslice_block(const VJob &J, int64_t kb, int64_t 
     bg = max(bg, 1);
     if (kb == 0 && lane < 32) J.colgrid[bhk * J.Dp32 + d] = g;
     if (kb == 0 && lane == 0) J.grpB[bhk * J.nG + G] = bg;
-    const TV *col = (const TV *)J.v + b * J.vsB + hk * J.vsH + (d < J.D ? d : 0);
     // the kBmax balanced digits of Vi (|Vi| < 2^38) are the bytes of
     // Vi + 0x8080808080 with their top bit flipped
     uint64_t U[16];
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
-        const int64_t j = J.kv_lo + kb * kKB + 16 * (lane >> 5) + p;
-        double x = 0.0;
-        if (d < J.D && j < J.kv_hi) x = (double)elem<TV>::to_f32(col[j * J.vsS]);
+        const double x = d < J.D && jb + p < J.kv_hi ? (double)xv[p] : 0.0;
         U[p] = (uint64_t)((int64_t)ldexp(x, -g) + 0x8080808080ll);  // toward zero onto the grid
     }
     if (__ballot(split)) {
         // the exact remainders of a split column's entries (reread: a rare path)
         for (int p = 0; p < 16; ++p) {
-            const int64_t j = J.kv_lo + kb * kKB + 16 * (lane >> 5) + p;
+            const int64_t j = jb + p;
             if (!split || d >= J.D || j >= J.kv_hi) continue;
             const double x = (double)elem<TV>::to_f32(col[j * J.vsS]);
             const double rem = x - ldexp((double)(int64_t)ldexp(x, -g), g);  // exact: the low bits of x
