@@ -423,11 +423,13 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
         const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, d = G * 16 + xr;
         if (d < A.D) st = A.st_k[bhk * A.D + d];
         const int64_t base = b * A.ksB + hk * A.ksH + (d < A.D ? d : 0);
+        float x[16];
+#pragma unroll
+        for (int p = 0; p < 16; ++p) x[p] = ld<T>(A.k, base + min64(jb * 64 + tb + p, A.Skv - 1) * A.ksS);
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
-            const int64_t j = jb * 64 + tb + p;
-            const float x = ld<T>(A.k, base + min64(j, A.Skv - 1) * A.ksS);
-            val[p] = (d < A.D && j < A.Skv) ? x : 0.0f;
+            const float xp = keep(x[p]);
+            val[p] = (d < A.D && jb * 64 + tb + p < A.Skv) ? xp : 0.0f;
         }
         kmax = kXB;
         out = A.xb[0] + u * kXB * 64;
@@ -437,12 +439,17 @@ __global__ __launch_bounds__(256) void k_bwd_slice(BwdArgs A, int64_t nunits) {
         const int64_t b = bhk / A.Hkv, hk = bhk % A.Hkv, hq = hk * A.group + g, d = G * 16 + xr;
         if (d < A.D) st = (MODE == 4 ? A.st_q : A.st_o)[bhk * A.D + d];
         const int64_t dd = d < A.D ? d : 0;
+        float x[16];
 #pragma unroll
         for (int p = 0; p < 16; ++p) {
-            const int64_t ir = ib * 64 + tb + p, i = A.i0 + min64(ir, A.ni - 1);
-            const float x = MODE == 4 ? ld<T>(A.q, b * A.qsB + hq * A.qsH + i * A.qsS + dd)
-                                      : A.dout[b * A.dsB + hq * A.dsH + i * A.dsS + dd];
-            val[p] = (d < A.D && ir < A.ni) ? x : 0.0f;
+            const int64_t i = A.i0 + min64(ib * 64 + tb + p, A.ni - 1);
+            x[p] = MODE == 4 ? ld<T>(A.q, b * A.qsB + hq * A.qsH + i * A.qsS + dd)
+                             : A.dout[b * A.dsB + hq * A.dsH + i * A.dsS + dd];
+        }
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+            const float xp = keep(x[p]);
+            val[p] = (d < A.D && ib * 64 + tb + p < A.ni) ? xp : 0.0f;
         }
         kmax = kXB;
         out = A.xb[MODE - 3] + u * kXB * 64;

@@ -133,6 +133,15 @@ __device__ __forceinline__ double log_det(double x) {
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
+// A loaded value the compiler must materialise where this stands: a load in
+// range for every lane, whose value a later select may drop, is otherwise
+// moved into that select's branch with a wait of its own, so a batch of such
+// loads would return one at a time.  Use after the whole batch is issued.
+__device__ __forceinline__ float keep(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // ---------------------------------------------------------------- total order
 
 // Monotone map of f32 onto uint32 under IEEE totalOrder (-0 < +0); NaNs are
