@@ -332,6 +332,11 @@ __global__ __launch_bounds__(kTT, 6) void k_ce_hist(const uint16_t *x, int64_t N
     // window comes from each thread's first vector, which is that batch's
     // first element, so the placement waits for one load round trip that
     // the rest of the batch overlaps.
+    // the target's column is read now and its logit once the window is
+    // placed, so both round trips overlap the streaming (the value is used at
+    // the very end)
+    int64_t tcol = 0;
+    if (FWD && tid == 0) tcol = targets[i];
     const uint4 *vp = (const uint4 *)(p0 + rs.head);
     int64_t k = tid;
     uint32_t base;
@@ -346,6 +351,8 @@ __global__ __launch_bounds__(kTT, 6) void k_ce_hist(const uint16_t *x, int64_t N
     } else {
         base = pick_window(p0, rs, S.red);  // synchronizes
     }
+    uint32_t xraw = 0;
+    if (FWD && tid == 0) xraw = x[i * ld + tcol];
     // software-pipelined: the next four vectors are in flight while the
     // current four are binned
     if (k + (kPipe - 1) * kTT < rs.nvec) {
@@ -368,29 +375,30 @@ __global__ __launch_bounds__(kTT, 6) void k_ce_hist(const uint16_t *x, int64_t N
     for (; k < rs.nvec; k += kTT) hist_put8(S, vp[k], base);
     for (int64_t j = tid; j < rs.nscalar(); j += kTT) hist_put(S, p0[rs.scalar_at(j)], base);
     __syncthreads();
-    // the target logit is loaded now and used at the very end
-    float xt = 0.0f;
-    if (FWD && tid == 0) xt = bf16_value(x[i * ld + targets[i]]);
 
     const uint32_t qn = S.qn;
     const bool over = qn > (uint32_t)kQcap;  // some outside patterns were not kept: rescan for them
+    // thread tid takes the runs of four slots 4 (tid + q kTT), q < kSlots / 4:
+    // the patterns a row holds most of (a few binades) spread over four times
+    // as many threads as whole runs of kSlots would, while each run's weights
+    // stay close in exponent for the window
     uint32_t cnt[kSlots];
 #pragma unroll
     for (int j = 0; j < kSlots / 4; ++j) {
-        const uint4 c4 = ((const uint4 *)S.hist)[tid * (kSlots / 4) + j];
+        const uint4 c4 = ((const uint4 *)S.hist)[tid + kTT * j];
         cnt[4 * j] = c4.x;
         cnt[4 * j + 1] = c4.y;
         cnt[4 * j + 2] = c4.z;
         cnt[4 * j + 3] = c4.w;
     }
-    const uint32_t s0 = (uint32_t)tid * kSlots;
+    auto slot_at = [&](int j) { return 4u * ((uint32_t)tid + (uint32_t)kTT * (uint32_t)(j >> 2)) + (uint32_t)(j & 3); };
 
     float m;
     if (FWD) {
         uint32_t key = kKeyNegInf;
 #pragma unroll
         for (int j = 0; j < kSlots; ++j)
-            if (cnt[j]) key = max(key, order_key(bf16_value(slot_code(s0 + j, base))));
+            if (cnt[j]) key = max(key, order_key(bf16_value(slot_code(slot_at(j), base))));
         if (!over) {
             for (uint32_t q = tid; q < qn; q += kTT) key = max(key, order_key(bf16_value(S.q[q])));
         } else {
@@ -410,7 +418,7 @@ __global__ __launch_bounds__(kTT, 6) void k_ce_hist(const uint16_t *x, int64_t N
 #pragma unroll
     for (int j = 0; j < kSlots; ++j) {
         if (cnt[j]) {
-            const float w = weight(bf16_value(slot_code(s0 + j, base)), m);
+            const float w = weight(bf16_value(slot_code(slot_at(j), base)), m);
             if (w != 0.0f) {
                 const double t = (double)w * (double)cnt[j];  // exact: 24 x 29 bits
                 const int ew = f32_exp(w);
@@ -448,7 +456,7 @@ __global__ __launch_bounds__(kTT, 6) void k_ce_hist(const uint16_t *x, int64_t N
         canonicalize<kDenDigits>(d);
         if (FWD) {
             rowmax_out[i] = m;
-            ce_loss_of(d, xt, m, i, loss, denom);
+            ce_loss_of(d, bf16_value(xraw), m, i, loss, denom);
         } else {
 #pragma unroll
             for (int q = 0; q < kDenDigits; ++q) den[q * N + i] = d[q];
