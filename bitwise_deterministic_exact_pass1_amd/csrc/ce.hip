@@ -288,19 +288,32 @@ __device__ __forceinline__ void hist_put(HistShared &S, uint32_t c, uint32_t bas
     }
 }
 
+// Eight patterns of one 16-byte vector.  Both patterns of a 32-bit word are
+// placed at once in 16-bit lanes: a = (c & 0x7fff) - base modulo 2^16 is below
+// kHalf exactly when the pattern lies in the window (a difference below zero
+// wraps to 2^16 - 32767 or more), so one mask of the OR over the vector decides
+// whether all eight are in it; then each lane's byte offset 4 slot =
+// 4 a + (sign << 14) is below 2^15, so both fit their halves.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void hist_put8(HistShared &S, const uint4 u, uint32_t base) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    uint32_t s[8];
-    bool out = false;
+    const u16x2 b2 = {(uint16_t)base, (uint16_t)base};
+    uint32_t a[4], any = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        s[2 * k] = tab_slot(w[k] & 0xffffu, base);
-        s[2 * k + 1] = tab_slot(w[k] >> 16, base);
-        out |= (s[2 * k] | s[2 * k + 1]) >= (uint32_t)kTab;
+        a[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w[k] & 0x7fff7fffu) - b2);
+        any |= a[k];
     }
-    if (!out) {
+    if ((any & 0xf000f000u) == 0) {
+        const u16x2 two = {2, 2};
+        char *h = (char *)S.hist;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) atomicAdd(&S.hist[s[k]], 1u);
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t o = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, a[k]) << two) |
+                               ((w[k] >> 1) & 0x40004000u);
+            atomicAdd((uint32_t *)(h + (o & 0xffffu)), 1u);
+            atomicAdd((uint32_t *)(h + (o >> 16)), 1u);
+        }
     } else {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
