@@ -45,6 +45,7 @@ SIGNATURES = {
     "det_profile_begin": (C.c_int, []),
     "det_profile_end": (_SZ, [C.c_char_p, _SZ]),
     "det_debug_force_generic": (C.c_int, [_I32]),
+    "det_debug_checks": (C.c_int, [_I32]),
     "det_debug_pass2_layout": (C.c_int, [_I32]),
     "det_debug_score_source": (C.c_int, [_I32]),
     "det_attn_workspace_size": (_SZ, [_T, _T, _T, _I32]),
@@ -97,6 +98,13 @@ def force_generic(on: bool) -> None:
     """Testing aid: send every tile through the library's generic exact path
     (bit-identical results) until switched off again."""
     check(lib().det_debug_force_generic(int(bool(on))))
+
+
+def input_checks(on: bool) -> None:
+    """Verify caller-supplied row maxima (accumulate) and targets (cross-
+    entropy) on the device; calls then wait for their stream and raise on a
+    violation.  Off by default."""
+    check(lib().det_debug_checks(int(bool(on))))
 
 
 def pass2_layout(mode: int) -> None:

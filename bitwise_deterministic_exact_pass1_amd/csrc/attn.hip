@@ -311,6 +311,23 @@ __global__ void k_keys_to_f32(const uint32_t *__restrict__ keys, float *__restri
     }
 }
 
+__global__ void k_rowmax_below(const float *__restrict__ supplied, const float *__restrict__ computed, int64_t BHq,
+                               int64_t rows, int64_t out_rows, int64_t row0, unsigned int *bad) {
+    const int64_t n = BHq * rows;
+    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t at = (t / rows) * out_rows + row0 + t % rows;
+        if (computed[at] > supplied[at]) atomicAdd(bad, 1u);
+    }
+}
+
+hipError_t launch_rowmax_below(const float *supplied, const float *computed, int64_t BHq, int64_t rows,
+                               int64_t out_rows, int64_t row0, unsigned int *bad, hipStream_t s) {
+    if (BHq * rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_rowmax_below, grid_for(BHq * rows), dim3(256), 0, s, supplied, computed, BHq, rows,
+                       out_rows, row0, bad);
+    return hipGetLastError();
+}
+
 hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t BHq, int64_t rows, int64_t out_rows,
                               int64_t out_row0, hipStream_t s) {
     ProfScope prof_("keys_to_f32", s);

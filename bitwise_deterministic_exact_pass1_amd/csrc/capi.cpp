@@ -267,6 +267,25 @@ VPrep carve_vprep(Carver &c, const AttnGeom &g, int64_t kv_len) {
 // generic exact path, so tests can check that both paths give the same bits.
 std::atomic<int> g_force_generic{0};
 int force_fallback() { return g_force_generic.load(std::memory_order_relaxed); }
+// Set by det_debug_checks: entry points that take caller-supplied row maxima
+// or targets verify them on the device and report violations (synchronizing).
+std::atomic<int> g_checks{0};
+bool checks_on() { return g_checks.load(std::memory_order_relaxed) != 0; }
+
+// The cross-entropy target check around a launch: the count is cleared before
+// and read after (both wait for the stream).
+int ce_check_begin(hipStream_t s) {
+    unsigned int c = 0;
+    HIP_TRY(ce_take_bad_targets(s, &c), "input checks");
+    return ok();
+}
+int ce_check_end(hipStream_t s) {
+    unsigned int c = 0;
+    HIP_TRY(ce_take_bad_targets(s, &c), "input checks");
+    if (c) return fail(DET_E_VALUE, "%u rows have a target outside [0, V) (their loss is NaN)", c);
+    return ok();
+}
+
 // Set by det_debug_pass2_layout (a testing aid): which pass-2 kernel takes
 // recomputed scores (0: by key-range length).
 std::atomic<int> g_pass2_layout{0};
@@ -308,6 +327,11 @@ const char *det_last_error(void) { return g_err.c_str(); }
 
 int det_debug_force_generic(int32_t on) {
     g_force_generic.store(on ? 1 : 0, std::memory_order_relaxed);
+    return ok();
+}
+
+int det_debug_checks(int32_t on) {
+    g_checks.store(on ? 1 : 0, std::memory_order_relaxed);
     return ok();
 }
 
@@ -393,6 +417,34 @@ int det_attn_rowmax(const det_tensor *q, const det_tensor *k, int64_t q_lo, int6
 
 // ------------------------------------------------------------------ accumulate
 
+// The accumulate precondition under det_debug_checks: the range's own row
+// maxima (det_attn_rowmax into scratch this check allocates) against the
+// supplied ones; DET_E_VALUE when a visible score lies above its row's value.
+static int check_rowmax_bound(const det_tensor *q, const det_tensor *k, const float *rowmax, int64_t q_lo, int64_t q_hi,
+                       int64_t kv_lo, int64_t kv_hi, int32_t causal, double scale, hipStream_t s) {
+    const AttnGeom g = geom(q, k, causal, scale);
+    const int64_t bh = g.B * g.Hq;
+    const size_t ws = det_attn_rowmax_workspace_size(q, k, q_lo, q_hi, kv_lo, kv_hi);
+    const size_t mbytes = (size_t)(bh * g.Sq) * sizeof(float);
+    char *buf = nullptr;
+    HIP_TRY(hipMalloc((void **)&buf, align256(mbytes) + align256(sizeof(unsigned int)) + ws), "input checks");
+    float *mx = (float *)buf;
+    unsigned int *bad = (unsigned int *)(buf + align256(mbytes));
+    void *wsp = buf + align256(mbytes) + align256(sizeof(unsigned int));
+    unsigned int nbad = 0;
+    hipError_t e = hipMemsetAsync(bad, 0, sizeof(unsigned int), s);
+    int rc = e == hipSuccess ? det_attn_rowmax(q, k, q_lo, q_hi, kv_lo, kv_hi, causal, scale, mx, wsp, ws, s) : 0;
+    if (e == hipSuccess && rc == 0) e = launch_rowmax_below(rowmax, mx, bh, q_hi - q_lo, g.Sq, q_lo, bad, s);
+    if (e == hipSuccess && rc == 0) e = hipMemcpyAsync(&nbad, bad, sizeof(nbad), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && rc == 0) e = hipStreamSynchronize(s);
+    const hipError_t ef = hipFree(buf);
+    if (rc) return rc;
+    if (e != hipSuccess) return hip_fail(e, "input checks");
+    if (ef != hipSuccess) return hip_fail(ef, "input checks");
+    if (nbad) return fail(DET_E_VALUE, "%u rows have a visible score above the supplied rowmax", nbad);
+    return ok();
+}
+
 size_t det_attn_accumulate_workspace_size(const det_tensor *q, const det_tensor *k, const det_tensor *v,
                                           int64_t q_lo, int64_t q_hi, int64_t kv_lo, int64_t kv_hi) {
     if (check_qkv(q, k, v, 0) || check_qrange(q, q_lo, q_hi) || check_range(k, kv_lo, kv_hi)) return 0;
@@ -424,6 +476,8 @@ int det_attn_accumulate(const det_tensor *q, const det_tensor *k, const det_tens
     if ((rc = check_ws(workspace, ws_bytes, nq > 0 ? need(std::min<int64_t>(nq, kRowTile)) : 0))) return rc;
     if (nq == 0) return ok();
     hipStream_t s = (hipStream_t)stream;
+    if (checks_on() && W > 0 && (rc = check_rowmax_bound(q, k, rowmax, q_lo, q_hi, kv_lo, kv_hi, causal, scale, s)))
+        return rc;
     const Tensor tq = to_t(q), tk = to_t(k), tv = to_t(v);
     const int64_t bh = g.B * g.Hq, rows = bh * g.Sq;
     const int64_t chunk = choose_chunk(nq, ws_bytes, need);
@@ -839,9 +893,11 @@ int det_ce_finalize(const int64_t *den, const void *logits, int32_t dtype, int64
     int rc;
     if ((rc = check_logits(logits, dtype, N, V, ld))) return rc;
     if (N > 0 && (!den || !targets || !rowmax || !loss || !denom)) return fail(DET_E_NULL, "a required pointer is NULL");
-    HIP_TRY(launch_ce_finalize(den, logits, dtype, N, ld, targets, rowmax, loss, denom, (hipStream_t)stream),
-            "ce finalize");
-    return ok();
+    hipStream_t s = (hipStream_t)stream;
+    const bool chk = checks_on() && N > 0;
+    if (chk && (rc = ce_check_begin(s))) return rc;
+    HIP_TRY(launch_ce_finalize(den, logits, dtype, N, V, ld, targets, rowmax, loss, denom, s), "ce finalize");
+    return chk ? ce_check_end(s) : ok();
 }
 
 size_t det_ce_forward_workspace_size(int64_t) { return 0; }
@@ -851,9 +907,11 @@ int det_ce_forward(const void *logits, int32_t dtype, int64_t N, int64_t V, int6
     int rc;
     if ((rc = check_logits(logits, dtype, N, V, ld))) return rc;
     if (N > 0 && (!targets || !loss || !rowmax || !denom)) return fail(DET_E_NULL, "a required pointer is NULL");
-    HIP_TRY(launch_ce_forward(logits, dtype, N, V, ld, targets, loss, rowmax, denom, (hipStream_t)stream),
-            "ce forward");
-    return ok();
+    hipStream_t s = (hipStream_t)stream;
+    const bool chk = checks_on() && N > 0;
+    if (chk && (rc = ce_check_begin(s))) return rc;
+    HIP_TRY(launch_ce_forward(logits, dtype, N, V, ld, targets, loss, rowmax, denom, s), "ce forward");
+    return chk ? ce_check_end(s) : ok();
 }
 
 size_t det_ce_reduce_workspace_size(int64_t) { return 0; }

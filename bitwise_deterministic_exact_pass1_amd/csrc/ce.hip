@@ -16,6 +16,10 @@ namespace det {
 
 constexpr int kCeThreads = 256;
 
+// Rows whose target lies outside [0, V): their logit is not read and their
+// loss is NaN.  Counted here (per device) for the library's optional checks.
+__device__ unsigned int g_ce_bad_targets;
+
 static dim3 ce_grid(int64_t n) {
     return dim3((unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1 << 20)));
 }
@@ -94,10 +98,13 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_denom(const void *x, int64_t 
 // loss_i = RN32(RN64(RN64(m + log_det(RN64(den))) - x_t)); denom_i = RN64(den).
 template <typename T>
 __device__ __forceinline__ void ce_loss(const int64_t (&dd)[kDenDigits], const void *x, int64_t ld, int64_t i,
-                                        int64_t t, float m, float *loss, double *denom) {
+                                        int64_t V, int64_t t, float m, float *loss, double *denom) {
     const double d64 = digits_to_f64<kDenDigits>(dd, kDenElo);
     const double lse = (double)m + log_det(d64);
-    loss[i] = (float)(lse - (double)ce_load<T>(x, ld, i, t));
+    double xt = __builtin_nan("");
+    if (t >= 0 && t < V) xt = (double)ce_load<T>(x, ld, i, t);
+    else atomicAdd(&g_ce_bad_targets, 1u);
+    loss[i] = (float)(lse - xt);
     denom[i] = d64;
 }
 
@@ -111,14 +118,14 @@ __device__ __forceinline__ void ce_loss_of(const int64_t (&dd)[kDenDigits], floa
 }
 
 template <typename T>
-__global__ void k_ce_finalize(const int64_t *den, const void *x, int64_t N, int64_t ld, const int64_t *targets,
-                              const float *rowmax, float *loss, double *denom) {
+__global__ void k_ce_finalize(const int64_t *den, const void *x, int64_t N, int64_t V, int64_t ld,
+                              const int64_t *targets, const float *rowmax, float *loss, double *denom) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < N; i += (int64_t)gridDim.x * blockDim.x) {
         int64_t d[kDenDigits];
 #pragma unroll
         for (int k = 0; k < kDenDigits; ++k) d[k] = den[k * N + i];
         canonicalize<kDenDigits>(d);
-        ce_loss<T>(d, x, ld, i, targets[i], rowmax[i], loss, denom);
+        ce_loss<T>(d, x, ld, i, V, targets[i], rowmax[i], loss, denom);
     }
 }
 
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(kCeThreads) void k_ce_forward(const void *x, int64_
         for (int k = 0; k < kDenDigits; ++k) d[k] = sd[k];
         canonicalize<kDenDigits>(d);
         rowmax[i] = m;
-        ce_loss<T>(d, x, ld, i, targets[i], m, loss, denom);
+        ce_loss<T>(d, x, ld, i, V, targets[i], m, loss, denom);
     }
 }
 
@@ -364,8 +371,10 @@ __global__ __launch_bounds__(kTT, 6) void k_ce_hist(const uint16_t *x, int64_t N
     } else {
         base = pick_window(p0, rs, S.red);  // synchronizes
     }
-    uint32_t xraw = 0;
-    if (FWD && tid == 0) xraw = x[i * ld + tcol];
+    // (a target outside [0, V) reads no logit: the bf16 quiet NaN stands in)
+    const bool tok = tcol >= 0 && tcol < v_hi - v_lo;
+    uint32_t xraw = 0x7fc0u;
+    if (FWD && tid == 0 && tok) xraw = x[i * ld + tcol];
     // software-pipelined: the next four vectors are in flight while the
     // current four are binned
     if (k + (kPipe - 1) * kTT < rs.nvec) {
@@ -469,6 +478,7 @@ __global__ __launch_bounds__(kTT, 6) void k_ce_hist(const uint16_t *x, int64_t N
         canonicalize<kDenDigits>(d);
         if (FWD) {
             rowmax_out[i] = m;
+            if (!tok) atomicAdd(&g_ce_bad_targets, 1u);
             ce_loss_of(d, bf16_value(xraw), m, i, loss, denom);
         } else {
 #pragma unroll
@@ -643,16 +653,16 @@ hipError_t launch_ce_denom(const void *x, int dtype, int64_t N, int64_t ld, cons
     return hipGetLastError();
 }
 
-hipError_t launch_ce_finalize(const int64_t *den, const void *x, int dtype, int64_t N, int64_t ld,
+hipError_t launch_ce_finalize(const int64_t *den, const void *x, int dtype, int64_t N, int64_t V, int64_t ld,
                               const int64_t *targets, const float *rowmax, float *loss, double *denom,
                               hipStream_t s) {
     ProfScope prof_("ce_finalize", s);
     if (N <= 0) return hipSuccess;
     if (dtype == 0)
-        hipLaunchKernelGGL(k_ce_finalize<float>, ce_grid(N), dim3(256), 0, s, den, x, N, ld, targets, rowmax, loss,
-                           denom);
+        hipLaunchKernelGGL(k_ce_finalize<float>, ce_grid(N), dim3(256), 0, s, den, x, N, V, ld, targets, rowmax,
+                           loss, denom);
     else
-        hipLaunchKernelGGL(k_ce_finalize<bf16_t>, ce_grid(N), dim3(256), 0, s, den, x, N, ld, targets, rowmax,
+        hipLaunchKernelGGL(k_ce_finalize<bf16_t>, ce_grid(N), dim3(256), 0, s, den, x, N, V, ld, targets, rowmax,
                            loss, denom);
     return hipGetLastError();
 }
@@ -694,6 +704,22 @@ hipError_t launch_ce_backward(const void *x, int dtype, int64_t N, int64_t V, in
         hipLaunchKernelGGL(k_ce_backward<bf16_t>, ce_grid(N * V), dim3(256), 0, s, x, N, V, ld, v0, targets, rowmax,
                            denom, grad_loss, reduction, grad, grad_ld);
     return hipGetLastError();
+}
+
+}  // namespace det
+
+namespace det {
+
+// The count of rows given a target outside [0, V) since the last call, then
+// cleared (waits for the stream first).
+hipError_t ce_take_bad_targets(hipStream_t s, unsigned int *count) {
+    hipError_t e;
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return e;
+    if ((e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_ce_bad_targets), sizeof(unsigned int), 0,
+                                 hipMemcpyDeviceToHost)) != hipSuccess)
+        return e;
+    const unsigned int zero = 0;
+    return hipMemcpyToSymbol(HIP_SYMBOL(g_ce_bad_targets), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
 }
 
 }  // namespace det

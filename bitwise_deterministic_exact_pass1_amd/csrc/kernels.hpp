@@ -103,6 +103,10 @@ hipError_t launch_scores(const Tensor &k, const AttnGeom &g, const double *q64, 
                          int64_t kv_lo, int64_t kv_hi, float *scores, uint32_t *rowmax_keys, int64_t key_rows,
                          int64_t key_row0, hipStream_t s);
 
+// adds to *bad the number of rows [row0, row0 + rows) of the BHq heads
+// ([BHq][out_rows] layout) whose computed max exceeds the supplied rowmax
+hipError_t launch_rowmax_below(const float *supplied, const float *computed, int64_t BHq, int64_t rows,
+                               int64_t out_rows, int64_t row0, unsigned int *bad, hipStream_t s);
 hipError_t launch_keys_to_f32(const uint32_t *keys, float *out, int64_t B_Hq, int64_t rows, int64_t out_rows,
                               int64_t out_row0, hipStream_t s);
 
@@ -262,9 +266,12 @@ hipError_t launch_ce_rowmax(const void *x, int dtype, int64_t N, int64_t ld, int
                             float *rowmax, hipStream_t s);
 hipError_t launch_ce_denom(const void *x, int dtype, int64_t N, int64_t ld, const float *rowmax, int64_t v_lo,
                            int64_t v_hi, int64_t *den, int add_into, hipStream_t s);
-hipError_t launch_ce_finalize(const int64_t *den, const void *x, int dtype, int64_t N, int64_t ld,
+hipError_t launch_ce_finalize(const int64_t *den, const void *x, int dtype, int64_t N, int64_t V, int64_t ld,
                               const int64_t *targets, const float *rowmax, float *loss, double *denom,
                               hipStream_t s);
+// rows given a target outside [0, V) since the last call (their loss is NaN),
+// then cleared; waits for the stream
+hipError_t ce_take_bad_targets(hipStream_t s, unsigned int *count);
 hipError_t launch_ce_forward(const void *x, int dtype, int64_t N, int64_t V, int64_t ld, const int64_t *targets,
                              float *loss, float *rowmax, double *denom, hipStream_t s);
 hipError_t launch_ce_reduce(const float *loss, int64_t N, int reduction, float *out, int64_t *scratch,

@@ -45,7 +45,8 @@
  *   - Q, K, V share one dtype (DET_F32 or DET_BF16); D <= 256; Hq % Hkv == 0;
  *     query head h reads KV head h / (Hq/Hkv).  Causal means key j is visible
  *     to query i iff j <= i (absolute indices) and requires Sq == Skv.
- *   - Inputs must be finite.  Debug checks are not performed.
+ *   - Inputs must be finite.  The preconditions on caller-supplied row maxima
+ *     and targets are checked only under det_debug_checks(1).
  */
 #ifndef DET_ATTN_H
 #define DET_ATTN_H
@@ -111,6 +112,17 @@ size_t det_profile_end(char *buf, size_t len);
  * paths compute the same exact sums, so the outputs are bit-identical; the
  * switch lets tests check that.  Process-wide; returns DET_OK. */
 int det_debug_force_generic(int32_t on);
+
+/* Input checks (for debugging; results never depend on it): with on != 0,
+ * every later call of det_attn_accumulate verifies on the device that no
+ * visible score of its range lies above the supplied rowmax, and every later
+ * det_ce_forward / det_ce_finalize that every target lies in [0, V).  These
+ * calls then wait for their stream and return DET_E_VALUE on a violation:
+ * det_attn_accumulate before touching num/den, the cross-entropy calls after
+ * writing their outputs.  The accumulate check computes the range's row
+ * maxima in memory it allocates (hipMalloc) for the check.  on = 0 (the
+ * default) turns the checks off.  Process-wide; returns DET_OK. */
+int det_debug_checks(int32_t on);
 
 /* Testing aid (results never depend on it): pass 2 of bf16 attention with
  * head dims up to 128 has two kernel layouts with the same exact sums --
@@ -246,7 +258,9 @@ int det_attn_sharded(const det_tensor *q, const det_tensor *k, const det_tensor 
 /* ------------------------------------------------------------ cross-entropy */
 /* det-cross-entropy page.  logits: (device) [N][V] of dtype DET_F32 or
  * DET_BF16, row i at logits + i*ld elements; targets: (device) int64 [N] in
- * [0, V).  Reduction codes: 0 none, 1 mean, 2 sum. */
+ * [0, V).  A row whose target lies outside [0, V) reads no logit for it and
+ * gets a NaN loss (det_debug_checks reports it).  Reduction codes: 0 none,
+ * 1 mean, 2 sum. */
 
 /* "API": rowmax(logits, v_lo, v_hi) -- per-token max over [v_lo, v_hi). rowmax: (device) f32 [N]. */
 int det_ce_rowmax(const void *logits, int32_t dtype, int64_t N, int64_t ld, int64_t v_lo, int64_t v_hi,
