@@ -275,11 +275,21 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
                                           __builtin_amdgcn_raw_buffer_load_b32(srs, voff + 4 * u, kb * kKB * 4, 0));
         }
     };
-    // the weights of block kb into digit buffer kb & 1 (its K rows are in the
-    // K buffer of the same parity)
+    // kept scores: the lane's four scores of blocks kb and kb + 1
+    auto s_load2 = [&](int kb, float (&x)[8]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            x[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, voff + 4 * u, kb * kKB * 4, 0));
+            x[4 + u] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(srs, voff + 4 * u, (kb + 1) * kKB * 4, 0));
+        }
+    };
+    constexpr int kRing = PvShared<ND>::kNDig - 1;
+    // the weights of block kb into digit buffer kb % kNDig (its K rows are in
+    // the K buffer of parity kb & 1)
     auto produce = [&](int kb, const float (&stored)[4]) {
         float sc[4];
-        const int nv = nvis(kb), db = kb & 1;
+        const int nv = nvis(kb), db = kb & 1, dg = kb & kRing;
         if constexpr (ND > 0) {
             if (!pv_block_scores<ND>(A, P, S, db, par, r, kb * kKB + k0, nv, lane, kc0, sc)) bad = true;
             if (P.slots && P.slot >= 0) {
@@ -290,15 +300,32 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
 #pragma unroll
             for (int u = 0; u < 4; ++u) sc[u] = stored[u];
         }
-        const uint32_t nz = wave_or_mask(block_weights<4>(sc, m, nv, S.dig[db] + dofs, wsum, bad));
-        if (lane == 0) S.mask[db][pw] = nz;
+        const uint32_t nz = wave_or_mask(block_weights<4>(sc, m, nv, S.dig[dg] + dofs, wsum, bad));
+        if (lane == 0) S.mask[dg][pw] = nz;
+    };
+    // kept scores: the weights of blocks kb and kb + 1 together (eight exp
+    // chains per lane) into digit buffers kb % kNDig and (kb + 1) % kNDig
+    auto produce2 = [&](int kb, const float (&stored)[8]) {
+        const int d0 = kb & kRing, d1 = (kb + 1) & kRing;
+        uint32_t nz0, nz1;
+        block_weights2(stored, m, nvis(kb), nvis(kb + 1), S.dig[d0] + dofs, S.dig[d1] + dofs, wsum, bad, nz0, nz1);
+        nz0 = wave_or_mask(nz0);
+        nz1 = wave_or_mask(nz1);
+        if (lane == 0) {
+            S.mask[d0][pw] = nz0;
+            S.mask[d1][pw] = nz1;
+        }
     };
 
     // prologue: K blocks 0 and 1 in LDS ([A] makes them visible), block 2 in
     // registers; block 0's weights ([B] hands them to the consumers).  Stored
     // scores: blocks 0 and 1 in the two register sets.
     float s0[4] = {}, s1[4] = {};
-    if (T.nblk > 0) {
+    float p0[8] = {}, p1[8] = {};  // kept scores: blocks 4q, 4q+1 and 4q+2, 4q+3
+    if constexpr (ND == 0) {
+        if (T.nblk > 0) s_load2(0, p0);
+        if (T.nblk > 2) s_load2(2, p1);
+    } else if (T.nblk > 0) {
         k_load(0);
         k_store(0);
         s_load(0, s0);
@@ -319,10 +346,17 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
             for (int n = 0; n < ND; ++n) asm volatile("" ::"v"(P.Bq[a][n]));
     }
     __syncthreads();  // [A]
-    if (T.nblk > 2) k_load(2);
-    if (T.nblk > 0) {
-        produce(0, s0);
-        if (T.nblk > 2) s_load(2, s0);
+    if constexpr (ND == 0) {  // blocks 0 and 1
+        if (T.nblk > 0) {
+            produce2(0, p0);
+            if (T.nblk > 4) s_load2(4, p0);
+        }
+    } else {
+        if (T.nblk > 2) k_load(2);
+        if (T.nblk > 0) {
+            produce(0, s0);
+            if (T.nblk > 2) s_load(2, s0);
+        }
     }
     __syncthreads();  // [B]
     // One block step, while the consumers multiply block kb: block kb+2's K
@@ -347,9 +381,32 @@ __device__ __forceinline__ bool pv_produce(const PvArgs &A, int64_t bh, int64_t 
         }
         __syncthreads();
     };
-    for (int kb = 0; kb < T.nblk; kb += 2) {
-        step(kb, s1);
-        if (kb + 1 < T.nblk) step(kb + 1, s0);
+    // Kept scores, per even step kb while the consumers multiply blocks kb and
+    // kb + 1: the weights of blocks kb + 2 and kb + 3 (their scores in one of
+    // the two pair sets, which then takes blocks kb + 6 and kb + 7); the roles
+    // meet after odd steps and the last one.
+    auto step2 = [&](int kb, float (&set)[8]) {
+        if (kb + 2 < T.nblk) {
+            produce2(kb + 2, set);
+            if (kb + 6 < T.nblk) s_load2(kb + 6, set);
+            if (((kb + 4) % kCarryEvery) == 0) {
+                whi += wsum >> 32;
+                wsum &= 0xffffffffll;
+            }
+        }
+        if (pv_meets<ND>(kb, T.nblk)) __syncthreads();
+        if (kb + 1 < T.nblk && pv_meets<ND>(kb + 1, T.nblk)) __syncthreads();
+    };
+    if constexpr (ND == 0) {
+        for (int kb = 0; kb < T.nblk; kb += 4) {
+            step2(kb, p1);
+            if (kb + 2 < T.nblk) step2(kb + 2, p0);
+        }
+    } else {
+        for (int kb = 0; kb < T.nblk; kb += 2) {
+            step(kb, s1);
+            if (kb + 1 < T.nblk) step(kb + 1, s0);
+        }
     }
     // The deferred pairs (final after the last block's barrier), 32 at a time
     // as the virtual keys of extra blocks.  Per extra block: their q and k
@@ -449,7 +506,7 @@ __device__ __forceinline__ void pv_consume_loop(const PvArgs &A, const PvTile &T
     __syncthreads();  // [B]
     auto step = [&](int kb, const v4i (&cur)[BV > 0 ? BV : 1], v4i (&nxt)[BV > 0 ? BV : 1]) {
         if (BV > 0) {
-            const int buf = kb & 1;
+            const int buf = kb & (PvShared<ND>::kNDig - 1);
             if (kb + 1 < T.nblk) {
 #pragma unroll
                 for (int s = 0; s < BV; ++s) nxt[s] = vb[((int64_t)(kb + 1) * kBmax + s) * 64];
@@ -485,7 +542,7 @@ __device__ __forceinline__ void pv_consume_loop(const PvArgs &A, const PvTile &T
                 C[kNC - 1] = v16i{0};
             }
         }
-        __syncthreads();
+        if (pv_meets<ND>(kb, T.nblk)) __syncthreads();
     };
     for (int kb = 0; kb < T.nblk; kb += 2) {
         step(kb, VA, VB);

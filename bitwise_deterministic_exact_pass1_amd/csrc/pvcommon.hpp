@@ -120,11 +120,12 @@ __device__ __forceinline__ float pv_score(const PvArgs &A, int64_t bh, int64_t i
 // row max is below a score, and then w > 1 sets bad either way), so the KPT
 // exp chains interleave instead of running one after another.
 // (GRP: keys whose exponentials run interleaved; fewer hold fewer registers)
-template <int KPT, int GRP = KPT>
-__device__ __forceinline__ uint32_t block_weights(const float (&sc)[KPT], float m, int nv, uint8_t *dst,
-                                                  int64_t &wsum, bool &bad) {
+// W + 0x808080808080 (U) of KPT keys, key k visible when vis(k); the exp
+// chains of GRP keys at a time run interleaved.
+template <int KPT, int GRP, class VIS>
+__device__ __forceinline__ void block_w(const float (&sc)[KPT], float m, VIS vis, uint64_t (&U)[KPT], int64_t &wsum,
+                                        bool &bad) {
     static_assert(KPT % GRP == 0, "whole groups");
-    uint64_t U[KPT];
 #pragma unroll
     for (int g0 = 0; g0 < KPT; g0 += GRP) {
         double t[GRP], n[GRP], r[GRP], p[GRP];
@@ -136,7 +137,7 @@ __device__ __forceinline__ uint32_t block_weights(const float (&sc)[KPT], float 
         exp_det_poly<GRP>(r, p, FmaVreg{});
 #pragma unroll
         for (int u = 0; u < GRP; ++u) {
-            const float w = (g0 + u < nv && t[u] >= -104.0) ? (float)ldexp(p[u], (int)n[u]) : 0.0f;
+            const float w = (vis(g0 + u) && t[u] >= -104.0) ? (float)ldexp(p[u], (int)n[u]) : 0.0f;
             const uint32_t bits = __float_as_uint(w);
             // 0x34000000 = 2^-23, 0x3f800000 = 1
             if (bits != 0 && (bits < 0x34000000u || bits > 0x3f800000u)) bad = true;
@@ -146,38 +147,67 @@ __device__ __forceinline__ uint32_t block_weights(const float (&sc)[KPT], float 
             U[g0 + u] = Wi + 0x808080808080ull;
         }
     }
-    // Plane a's word t holds byte a of U[4t .. 4t+3]: a 4 x 6 byte transpose
-    // per group of four keys, by byte permutes (v_perm_b32 picks any four
-    // bytes of its two sources: selector byte k in 0..3 names a byte of the
-    // second source, 4..7 one of the first).
+}
+
+// Plane a's word tw at dst holds byte a of four keys' U: a 4 x 6 byte
+// transpose by byte permutes (v_perm_b32 picks any four bytes of its two
+// sources: selector byte k in 0..3 names a byte of the second source, 4..7
+// one of the first); the flipped words are ORed into any[].
+__device__ __forceinline__ void pack_w4(uint64_t u0, uint64_t u1, uint64_t u2, uint64_t u3, int tw, uint8_t *dst,
+                                        uint32_t (&any)[kAw]) {
     static_assert(kAw == 6, "six W digit planes");
-    uint32_t any[kAw] = {};
+    const uint32_t L0 = (uint32_t)u0, L1 = (uint32_t)u1, L2 = (uint32_t)u2, L3 = (uint32_t)u3;
+    const uint32_t H0 = (uint32_t)(u0 >> 32), H1 = (uint32_t)(u1 >> 32), H2 = (uint32_t)(u2 >> 32),
+                   H3 = (uint32_t)(u3 >> 32);
+    // bytes 0, 1 (resp. 2, 3) of keys 0 and 1 interleaved, likewise keys 2 and 3
+    const uint32_t x01l = __builtin_amdgcn_perm(L1, L0, 0x05010400u), x01h = __builtin_amdgcn_perm(L1, L0, 0x07030602u);
+    const uint32_t x23l = __builtin_amdgcn_perm(L3, L2, 0x05010400u), x23h = __builtin_amdgcn_perm(L3, L2, 0x07030602u);
+    const uint32_t y01 = __builtin_amdgcn_perm(H1, H0, 0x05010400u), y23 = __builtin_amdgcn_perm(H3, H2, 0x05010400u);
+    const uint32_t word[kAw] = {
+        __builtin_amdgcn_perm(x23l, x01l, 0x05040100u), __builtin_amdgcn_perm(x23l, x01l, 0x07060302u),
+        __builtin_amdgcn_perm(x23h, x01h, 0x05040100u), __builtin_amdgcn_perm(x23h, x01h, 0x07060302u),
+        __builtin_amdgcn_perm(y23, y01, 0x05040100u),   __builtin_amdgcn_perm(y23, y01, 0x07060302u)};
 #pragma unroll
-    for (int t = 0; t < KPT / 4; ++t) {
-        const uint32_t L0 = (uint32_t)U[4 * t], L1 = (uint32_t)U[4 * t + 1], L2 = (uint32_t)U[4 * t + 2],
-                       L3 = (uint32_t)U[4 * t + 3];
-        const uint32_t H0 = (uint32_t)(U[4 * t] >> 32), H1 = (uint32_t)(U[4 * t + 1] >> 32),
-                       H2 = (uint32_t)(U[4 * t + 2] >> 32), H3 = (uint32_t)(U[4 * t + 3] >> 32);
-        // bytes 0, 1 (resp. 2, 3) of keys 0 and 1 interleaved, likewise keys 2 and 3
-        const uint32_t x01l = __builtin_amdgcn_perm(L1, L0, 0x05010400u), x01h = __builtin_amdgcn_perm(L1, L0, 0x07030602u);
-        const uint32_t x23l = __builtin_amdgcn_perm(L3, L2, 0x05010400u), x23h = __builtin_amdgcn_perm(L3, L2, 0x07030602u);
-        const uint32_t y01 = __builtin_amdgcn_perm(H1, H0, 0x05010400u), y23 = __builtin_amdgcn_perm(H3, H2, 0x05010400u);
-        const uint32_t word[kAw] = {
-            __builtin_amdgcn_perm(x23l, x01l, 0x05040100u), __builtin_amdgcn_perm(x23l, x01l, 0x07060302u),
-            __builtin_amdgcn_perm(x23h, x01h, 0x05040100u), __builtin_amdgcn_perm(x23h, x01h, 0x07060302u),
-            __builtin_amdgcn_perm(y23, y01, 0x05040100u),   __builtin_amdgcn_perm(y23, y01, 0x07060302u)};
-#pragma unroll
-        for (int a = 0; a < kAw; ++a) {
-            const uint32_t wd = word[a] ^ 0x80808080u;
-            any[a] |= wd;
-            ((uint32_t *)(dst + a * 64 * 16))[t] = wd;
-        }
+    for (int a = 0; a < kAw; ++a) {
+        const uint32_t wd = word[a] ^ 0x80808080u;
+        any[a] |= wd;
+        ((uint32_t *)(dst + a * 64 * 16))[tw] = wd;
     }
+}
+
+__device__ __forceinline__ uint32_t nonzero_planes(const uint32_t (&any)[kAw]) {
     uint32_t nzm = 0;
 #pragma unroll
     for (int a = 0; a < kAw; ++a)
         if (any[a]) nzm |= 1u << a;
     return nzm;
+}
+
+template <int KPT, int GRP = KPT>
+__device__ __forceinline__ uint32_t block_weights(const float (&sc)[KPT], float m, int nv, uint8_t *dst,
+                                                  int64_t &wsum, bool &bad) {
+    uint64_t U[KPT];
+    block_w<KPT, GRP>(sc, m, [&](int k) { return k < nv; }, U, wsum, bad);
+    uint32_t any[kAw] = {};
+#pragma unroll
+    for (int t = 0; t < KPT / 4; ++t) pack_w4(U[4 * t], U[4 * t + 1], U[4 * t + 2], U[4 * t + 3], t, dst, any);
+    return nonzero_planes(any);
+}
+
+// The same for the four keys of each of two blocks at once (sc[0..3] with nv0
+// visible into dst0, sc[4..7] with nv1 visible into dst1): their eight exp
+// chains interleave, which keeps a single wave per SIMD issuing its fp64
+// Horner steps closer to their rate.  The two blocks' masks go to nz0, nz1.
+__device__ __forceinline__ void block_weights2(const float (&sc)[8], float m, int nv0, int nv1, uint8_t *dst0,
+                                               uint8_t *dst1, int64_t &wsum, bool &bad, uint32_t &nz0,
+                                               uint32_t &nz1) {
+    uint64_t U[8];
+    block_w<8, 8>(sc, m, [&](int k) { return k < 4 ? k < nv0 : k - 4 < nv1; }, U, wsum, bad);
+    uint32_t a0[kAw] = {}, a1[kAw] = {};
+    pack_w4(U[0], U[1], U[2], U[3], 0, dst0, a0);
+    pack_w4(U[4], U[5], U[6], U[7], 0, dst1, a1);
+    nz0 = nonzero_planes(a0);
+    nz1 = nonzero_planes(a1);
 }
 
 // OR of a kAw-bit mask over the wave, by one ballot per bit (no LDS traffic).
@@ -197,13 +227,17 @@ template <int ND> struct PvKRow {
     static constexpr int KROW = RB + 16;
 };
 
-// LDS of the pass-2 kernel: W digits of two key blocks, K digit rows and key
-// statistics of two blocks (recomputed scores: per key its statistics and
-// grid, per 16-key half the largest digit count and bound), digit masks, row
-// sums, the bad-tile flag, and the consumers' int64 parts of the top class
-// (tiles of 8192 keys or more).
+// LDS of the pass-2 kernel: W digits of the key blocks in flight (a ring of
+// kNDig), K digit rows and key statistics of two blocks (recomputed scores:
+// per key its statistics and grid, per 16-key half the largest digit count
+// and bound), digit masks, row sums, the bad-tile flag, and the consumers'
+// int64 parts of the top class (tiles of 8192 keys or more).  With kept
+// scores the weights of two blocks are made together, two blocks ahead of
+// the products, and the roles meet every second block (four digit buffers);
+// recomputing, one block ahead and every block (two).
 template <int ND> struct PvShared {
-    uint8_t dig[2][kAw * 1024];
+    static constexpr int kNDig = ND == 0 ? 4 : 2;
+    uint8_t dig[kNDig][kAw * 1024];
     uint8_t kd[2][ND > 0 ? 32 * PvKRow<ND>::KROW : 16];
     int4 ki[2][32];
     int kg[2][32];
@@ -214,13 +248,20 @@ template <int ND> struct PvShared {
     int dn[2];
     int2 dl[2][kDeferCap];
     float dsc[32];
-    uint32_t mask[2][kPW];
+    uint32_t mask[kNDig][kPW];
     // per tile parity, so that a tile's finalize overlaps the next tile's start
     unsigned long long den_hi[2][32], den_lo[2][32];  // exact sum of W per row: hi 2^32 + lo
     double d64[2][32];                                // RN64(DEN) of the row
     int bad[2];
     int64_t top[4][16][64];  // [consumer wave][accumulator register][lane]
 };
+
+// Whether the roles of the pass-2 kernel meet (a workgroup barrier) after
+// block step kb of nblk: after every step, or with kept scores after the odd
+// steps and the last one.  Both roles take this same test.
+template <int ND> __device__ __forceinline__ bool pv_meets(int kb, int nblk) {
+    return ND > 0 || (kb & 1) != 0 || kb + 1 == nblk;
+}
 
 struct PvTile {
     int64_t b, hq, bhk, it0, i_end, nG, jhi;
