@@ -370,10 +370,19 @@ def cpu_baseline(q, k, v, causal, scale, gpu_out, seconds):
     n = int(min(len(allrows), max(64, 64 * seconds / max(dt, 1e-3))))
     if n > 64:
         sel, ref, dt, npairs = run(n)
+    passes = 1
+    if n == len(allrows) and dt < 0.5 * seconds:
+        # the whole workload takes less than the budget: time it several times over
+        passes = max(2, int(seconds / max(dt, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            oracle.det_attn(q, k, v, causal, scale, rows=sel)
+        dt = time.perf_counter() - t0
     got = gpu_out.cpu().numpy()[sel[:, 0], sel[:, 1], sel[:, 2]]
     exact = bool(np.array_equal(got.view(np.uint32), np.ascontiguousarray(ref).view(np.uint32)))
-    return {"value": npairs / dt, "unit": "pairs/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{len(sel)} random query rows of the same workload ({npairs} pairs), {dt:.1f} s",
+    what = f"all {len(sel)} query rows" if n == len(allrows) else f"{len(sel)} random query rows"
+    return {"value": npairs * passes / dt, "unit": "pairs/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{what} of the same workload ({npairs} pairs) x {passes} passes, {dt:.1f} s",
             "gpu_bit_exact_on_sample": exact}
 
 
