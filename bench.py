@@ -121,7 +121,7 @@ def main():
                          "byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
