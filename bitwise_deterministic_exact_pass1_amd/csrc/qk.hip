@@ -120,7 +120,10 @@ __device__ __forceinline__ void qkprep_rows(const QPrep &P, int64_t blk) {
     int64_t l1 = 0;
 #pragma unroll
     for (int t = 0; t < DPL; ++t) {
-        const int64_t xi = nd == kQKbad ? 0 : (int64_t)ldexp((double)v[t], -g);
+        // (an integer; |Xi| < 2^30 wherever it is used, so a 32-bit conversion of
+        // the value clamped to that range gives the same integer)
+        const double xd = fmin(fmax(ldexp((double)v[t], -g), -1073741824.0), 1073741824.0);
+        const int64_t xi = nd == kQKbad ? 0 : (int64_t)(int32_t)xd;
         l1 += xi < 0 ? -xi : xi;
         U[t] = (uint32_t)(xi + 0x80808080ll);
     }
