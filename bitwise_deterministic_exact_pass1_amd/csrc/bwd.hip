@@ -601,16 +601,23 @@ __global__ __launch_bounds__(512, 4) void k_bwd_mma(BwdArgs A) {
     // and t >= tfirst (dK, dV: query rows from the key on)
     const int tlast = (A.causal && MODE == 0) ? (int)min64(tmax, A.i0 + y * 32 + xa) : tmax;
     const int tfirst = (A.causal && MODE != 0) ? (int)max64(0, y * 32 + xa - A.i0) : 0;
+    // Steps tb .. tb + 3 of block kb: keys (dQ) or chunk rows (dK, dV).  The
+    // loads (clamped, in range) are issued here and the values masked only in
+    // stash_a, after the products: masking them here let the compiler move
+    // each load into the branch of its select, with a wait per load.
     auto fetch_a = [&](int64_t kb, float (&av)[4]) {
-        // steps tb .. tb + 3 of block kb: keys (dQ) or chunk rows (dK, dV)
+        const int tb = (int)kb * kT16 + t0, tc = min(tb, tmax);
+        const float *p = srow + (int64_t)tc * sstep;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) av[e] = p[(min(tb + e, tmax) - tc) * (int)sstep];
+    };
+    auto mask_a = [&](int64_t kb, float (&av)[4]) {
         const int tb = (int)kb * kT16 + t0;
-        const float *p = srow + (int64_t)min(tb, tmax) * sstep;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int t = tb + e;
-            const float x = p[(min(t, tmax) - min(tb, tmax)) * (int)sstep];
-            const bool vis = xok && t >= tfirst && t <= tlast;
-            av[e] = vis ? x : 0.0f;
+            const float x = keep(av[e]);
+            av[e] = (xok && t >= tfirst && t <= tlast) ? x : 0.0f;
         }
     };
     // Digits of one entry: Xi = +-x 256^q with x = m 2^r < 2^31 (m the 24-bit
@@ -681,7 +688,7 @@ __global__ __launch_bounds__(512, 4) void k_bwd_mma(BwdArgs A) {
         const int buf = (int)((kb - k0) & 1);
         const bool more = kb + 1 < nblk;
         fetch_b(kb);
-        if (more) fetch_a(kb + 1, F);
+        fetch_a(kb + 1, F);  // in range past the last block too: a fixed count of loads after B's
         if (run) {
             const v4i *sa_ = &sA[buf][0][rh][lane];
             v4i Acur = sa_[0];
@@ -705,11 +712,13 @@ __global__ __launch_bounds__(512, 4) void k_bwd_mma(BwdArgs A) {
                 }
             }
         }
+        mask_a(kb + 1, F);  // every step waits for its loads: none is in flight at the next
         if (more) stash_a(buf ^ 1, F);  // its readers passed the previous barrier
         __syncthreads();
     };
     if (k0 < nblk) {
         fetch_a(k0, F);
+        mask_a(k0, F);
         stash_a(0, F);
     }
     __syncthreads();
