@@ -687,7 +687,6 @@ __global__ __launch_bounds__(512, 4) void k_bwd_mma(BwdArgs A) {
     auto step = [&](int64_t kb) {
         const int buf = (int)((kb - k0) & 1);
         const bool more = kb + 1 < nblk;
-        fetch_b(kb);
         fetch_a(kb + 1, F);  // in range past the last block too: a fixed count of loads after B's
         if (run) {
             const v4i *sa_ = &sA[buf][0][rh][lane];
@@ -714,6 +713,7 @@ __global__ __launch_bounds__(512, 4) void k_bwd_mma(BwdArgs A) {
         }
         mask_a(kb + 1, F);  // every step waits for its loads: none is in flight at the next
         if (more) stash_a(buf ^ 1, F);  // its readers passed the previous barrier
+        fetch_b(more ? kb + 1 : kb);  // the next block's B digits load across the barrier
         __syncthreads();
     };
     if (k0 < nblk) {
@@ -721,6 +721,7 @@ __global__ __launch_bounds__(512, 4) void k_bwd_mma(BwdArgs A) {
         mask_a(k0, F);
         stash_a(0, F);
     }
+    if (k0 < nblk) fetch_b(k0);
     __syncthreads();
     for (int64_t kb = k0; kb < nblk; ++kb) step(kb);
     if (!mine || bad) return;
