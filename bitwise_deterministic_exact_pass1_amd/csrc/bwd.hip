@@ -108,29 +108,45 @@ __device__ __forceinline__ float ld(const void *base, int64_t off) {
     return elem<T>::to_f32(((const T *)base)[off]);
 }
 
-// delta_i, one thread per row; the row is read 32 dimensions at a time with
-// all 64 loads issued before the chain uses them (clamped, in range).
+// delta_i of 16 rows per 64-thread block: the rows of dO and O are read
+// into LDS by all lanes along d (coalesced), then lanes 0..15 each run one
+// row's chain over d from LDS (the row stride D + 1 keeps the 16 rows on
+// distinct banks).  D <= 256.
+constexpr int kDeltaRows = 16;
 __global__ __launch_bounds__(64) void k_bwd_delta(BwdArgs A, int64_t rows) {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= rows) return;
-    const int64_t b = r / (A.Hq * A.Sq), hq = (r / A.Sq) % A.Hq, i = r % A.Sq;
-    const float *o = A.o + b * A.osB + hq * A.osH + i * A.osS;
-    const float *g = A.dout + b * A.dsB + hq * A.dsH + i * A.dsS;
-    const int D = (int)A.D;
-    double acc = 0.0;
-    for (int d0 = 0; d0 < D; d0 += 32) {
-        float go[32], oo[32];
+    __shared__ float sg[kDeltaRows * 257 + 1], so[kDeltaRows * 257 + 1];  // + a slot for unused lanes
+    const int tid = threadIdx.x, D = (int)A.D;
+    const int64_t r0 = (int64_t)blockIdx.x * kDeltaRows;
+    const int nr = (int)min64(kDeltaRows, rows - r0);
+    int64_t gb = 0, ob = 0;  // lane l < nr: offsets of row r0 + l
+    if (tid < nr) {
+        const int64_t r = r0 + tid, b = r / (A.Hq * A.Sq), hq = (r / A.Sq) % A.Hq, i = r % A.Sq;
+        gb = b * A.dsB + hq * A.dsH + i * A.dsS;
+        ob = b * A.osB + hq * A.osH + i * A.osS;
+    }
 #pragma unroll
-        for (int u = 0; u < 32; ++u) {
-            const int d = min(d0 + u, D - 1);
-            go[u] = g[d];
-            oo[u] = o[d];
+    for (int rr = 0; rr < kDeltaRows; ++rr) {
+        const int64_t g0 = __shfl(gb, min(rr, nr - 1), 64), o0 = __shfl(ob, min(rr, nr - 1), 64);
+        float gv[4], ov[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int d = min(tid + 64 * u, D - 1);
+            gv[u] = A.dout[g0 + d];
+            ov[u] = A.o[o0 + d];
         }
 #pragma unroll
-        for (int u = 0; u < 32; ++u)
-            if (d0 + u < D) acc = fma((double)go[u], (double)oo[u], acc);
+        for (int u = 0; u < 4; ++u) {  // stores without a branch (a guarded store drew its load into the branch)
+            const int d = tid + 64 * u, at = (rr < nr && d < D) ? rr * (D + 1) + d : kDeltaRows * 257;
+            sg[at] = gv[u];
+            so[at] = ov[u];
+        }
     }
-    A.delta[r] = acc;
+    __syncthreads();
+    if (tid >= nr) return;
+    const float *g = sg + tid * (D + 1), *o = so + tid * (D + 1);
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d) acc = fma((double)g[d], (double)o[d], acc);
+    A.delta[r0 + tid] = acc;
 }
 
 // p and ds of a 64 x 64 tile of pairs (rows of the chunk x keys); with SC the
@@ -1062,7 +1078,7 @@ hipError_t launch_attn_backward(const Tensor &q, const Tensor &k, const Tensor &
     if ((e = launch_fill_i64(A.dk_dig, (int64_t)(kvdig / 8) + kvn, 0, s)) != hipSuccess) return e;
     {
         ProfScope prof_("bwd_delta", s);
-        hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((rows + 63) / 64)), dim3(64), 0, s, A, rows);
+        hipLaunchKernelGGL(k_bwd_delta, dim3((unsigned)((rows + kDeltaRows - 1) / kDeltaRows)), dim3(64), 0, s, A, rows);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const bool bf = q.dtype == 1;
