@@ -380,12 +380,11 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
     int4 sinfo = int4{0, 0, 0, 0};
     auto load_block = [&](int n) {
         const int8_t *src = block_src(n);
+        // (no branches: a load under a lane condition was issued behind a wait
+        // for every load before it; lanes past the block read its last chunk)
 #pragma unroll
-        for (int t = 0; t < CPT; ++t) {
-            const int c = tid + 256 * t;
-            if (c < NCH) stage[t] = *(const v4i *)(src + (int64_t)c * 16);
-        }
-        if (tid < kQkT) sinfo = ibase[(part + n * P) * kQkT + tid];
+        for (int t = 0; t < CPT; ++t) stage[t] = *(const v4i *)(src + (int64_t)min(tid + 256 * t, NCH - 1) * 16);
+        sinfo = ibase[(part + n * P) * kQkT + min(tid, kQkT - 1)];
     };
     auto store_block = [&](int buf) {
 #pragma unroll
@@ -483,6 +482,11 @@ __device__ __forceinline__ void qk_group(const QkArgs &A, int64_t bh, int64_t gr
             }
         }
         if (n + 1 < nb) store_block(buf ^ 1);
+        // every path waits for the staged loads here, so none is in flight when
+        // the next block's loads reuse their registers (else each waits for all)
+#pragma unroll
+        for (int t = 0; t < CPT; ++t) asm volatile("" ::"v"(stage[t]));
+        asm volatile("" ::"v"(sinfo.x), "v"(sinfo.y), "v"(sinfo.z), "v"(sinfo.w));
         __syncthreads();
     }
     if (!A.keys || !live) return;
